@@ -1,0 +1,354 @@
+"""fp64 CPU oracle for one sparse paged decode step -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline leg
+may import this module.  The HIP library never routes through it, and it shares
+no code, tables or constants with the HIP path: every function here is written
+from the definitions on the source pages, in plain numpy float64 with no
+blocking, fusion or reordering beyond what those definitions state.
+
+Inputs are the *stored* tensors (numpy arrays in their storage dtypes); fp16 and
+fp8 values are decoded exactly to float64 first.
+
+Pages and their definitions:
+  * LServe ("Hierarchical Paging" and "Key statistics storage and updating"):
+    per logical page channel-wise key min / max; page importance
+    S_j = sum_i max(q_i * kmax_i, q_i * kmin_i); top-K page selection under a
+    token budget; streaming heads read a static sink + local index table
+    ("Decoding Stage: Kernel Implementation with Two-Level Indexing").
+  * Moira (section 3.2 "The coverage rule", Eq. 3): group-mean softmax share
+    pi_bar of each page, forced {P0, Pcur}, tau_b = max tau such that the share
+    above tau reaches gamma minus the forced shares.
+  * PersistentKV (section 3.1, Eq. 1): exact decode attention over the kept
+    tokens; section 3.3: split states and their exact merge.
+
+Readings where the pages leave a step open (every one is listed in the design doc):
+  * GQA combine for top-K: score_p = max over the group's query heads of S_{g,p}.
+  * Coverage log-mass from the bound: l_{g,p} = s * S_{g,p} + ln(valid_p), s = 1/sqrt(d);
+    every page, sink and current included, is estimated the same way.
+  * The budget counts the forced pages; if the forced set alone reaches it the
+    list is the forced set.
+  * Top-K order (score desc, logical page asc); lists are ascending logical pages.
+  * Coverage threshold test in fp64 uses 1e-12 slack (the printed worked example
+    sums to 0.8999999999999999 in binary floating point).
+  * fp8 pools are OCP E4M3FN with a per-(page, head, token) fp16 scale; their key
+    min / max is stored as fp16 rounded outward (max up, min down).
+  * An empty row (no kept tokens) gives O = 0 and lse = -inf.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+PAGE = 16
+COVERAGE_SLACK = 1e-12
+
+
+# --------------------------------------------------------------------------------------
+# Storage decoding
+# --------------------------------------------------------------------------------------
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    """OCP 8-bit floating point E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+
+    exponent field 0 encodes subnormals m/8 * 2^-6; S.1111.111 is NaN; there is no
+    infinity, so S.1111.000 .. S.1111.110 are ordinary normals (up to 448).
+    """
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = sign * (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = sign * (m / 8.0) * 2.0 ** -6
+    out = np.where(e == 0, sub, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def stored_values(pool: np.ndarray, scale: np.ndarray | None, kv_dtype: str) -> np.ndarray:
+    """Exact float64 value of stored K or V entries (fp8: code value times its token scale)."""
+    if kv_dtype == "fp8":
+        return decode_e4m3fn(pool) * np.asarray(scale, dtype=np.float64)[..., None]
+    return np.asarray(pool, dtype=np.float64)
+
+
+def n_pages(seq_len: int) -> int:
+    return (int(seq_len) + PAGE - 1) // PAGE
+
+
+def valid_tokens(seq_len: int, p: int) -> int:
+    """Row-local token count of logical page p (PersistentKV section 3.3, N*_i = seq_lens[i])."""
+    return max(0, min(PAGE, int(seq_len) - PAGE * p))
+
+
+# --------------------------------------------------------------------------------------
+# a0: per-page key statistics
+# --------------------------------------------------------------------------------------
+
+def meta_dtype(kv_dtype: str):
+    return np.float32 if kv_dtype == "f32" else np.float16
+
+
+def _round_outward_f16(x: np.ndarray, up: bool) -> np.ndarray:
+    """Nearest fp16, then one fp16 step outward if rounding moved the value inward."""
+    r = x.astype(np.float16)
+    rf = r.astype(np.float64)
+    if up:
+        moved_in = rf < x
+        r = np.where(moved_in, np.nextafter(r, np.float16(np.inf)), r)
+    else:
+        moved_in = rf > x
+        r = np.where(moved_in, np.nextafter(r, np.float16(-np.inf)), r)
+    return r.astype(np.float16)
+
+
+def page_key_minmax(k_page: np.ndarray, valid: int):
+    """Channel-wise min and max of the valid keys of one page (LServe, k_min / k_max).
+
+    k_page: float64 [P, d]. Returns (kmin, kmax) float64 [d].
+    """
+    keys = k_page[:valid]
+    return keys.min(axis=0), keys.max(axis=0)
+
+
+def page_meta_build(inp, meta: np.ndarray | None = None, first_page=None) -> np.ndarray:
+    """Key min / max for every page p >= first_page[b] of every request, all KV heads.
+
+    Layout [num_pool_pages, Hkv, 2, d]: index 0 = kmin, 1 = kmax, in the meta dtype
+    (f32 pools: f32; f16 pools: f16; fp8 pools: f16 rounded outward).  Pages not
+    visited keep the values of ``meta`` (zeros when it is None).
+    """
+    w = inp.workload
+    Hkv, d = inp.k_pool.shape[1], inp.k_pool.shape[3]
+    mdt = meta_dtype(w.kv_dtype)
+    out = np.zeros((inp.k_pool.shape[0], Hkv, 2, d), dtype=mdt) if meta is None else meta.copy()
+    for b in range(len(inp.seq_lens)):
+        L = int(inp.seq_lens[b])
+        start = 0 if first_page is None else max(0, int(first_page[b]))
+        pages = list(range(start, n_pages(L)))
+        full = [p for p in pages if valid_tokens(L, p) == PAGE]
+        part = [p for p in pages if valid_tokens(L, p) < PAGE]
+        # full pages, vectorised over chunks of pages (min / max over the token axis)
+        for c in range(0, len(full), 512):
+            phys = inp.block_table[b, full[c:c + 512]].astype(np.int64)
+            scale = None if inp.k_scale is None else inp.k_scale[phys]
+            kv = stored_values(inp.k_pool[phys], scale, w.kv_dtype)  # [n, Hkv, P, d]
+            lo, hi = _to_meta(kv.min(axis=2), kv.max(axis=2), w.kv_dtype)
+            out[phys, :, 0] = lo
+            out[phys, :, 1] = hi
+        for p in part:
+            phys = int(inp.block_table[b, p])
+            valid = valid_tokens(L, p)
+            scale = None if inp.k_scale is None else inp.k_scale[phys]
+            kv = stored_values(inp.k_pool[phys], scale, w.kv_dtype)  # [Hkv, P, d]
+            for h in range(Hkv):
+                lo, hi = _to_meta(*page_key_minmax(kv[h], valid), w.kv_dtype)
+                out[phys, h, 0] = lo
+                out[phys, h, 1] = hi
+    return out
+
+
+def _to_meta(kmin: np.ndarray, kmax: np.ndarray, kv_dtype: str):
+    """Stored form of float64 min / max: exact in the pool dtype, or fp16 outward for fp8."""
+    if kv_dtype == "fp8":
+        return _round_outward_f16(kmin, up=False), _round_outward_f16(kmax, up=True)
+    mdt = meta_dtype(kv_dtype)
+    return kmin.astype(mdt), kmax.astype(mdt)  # exact: min / max of representable values
+
+
+# --------------------------------------------------------------------------------------
+# a1: page scores
+# --------------------------------------------------------------------------------------
+
+def quest_bound(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
+    """LServe page importance S = sum_i max(q_i * kmax_i, q_i * kmin_i).
+
+    q: [G, d]; kmin, kmax: [n, d] -> S: [G, n] (float64).
+    """
+    a = q[:, None, :] * kmax[None, :, :]
+    b = q[:, None, :] * kmin[None, :, :]
+    return np.maximum(a, b).sum(axis=-1)
+
+
+def row_bounds(inp, meta: np.ndarray, b: int, h: int) -> np.ndarray:
+    """S_{g,p} for the G query heads of KV head h of request b over its pages, from stored meta."""
+    w = inp.workload
+    G = w.group
+    n = n_pages(inp.seq_lens[b])
+    phys = inp.block_table[b, :n].astype(np.int64)
+    m = meta[phys, h].astype(np.float64)          # [n, 2, d]
+    q = inp.q[b, h * G:(h + 1) * G].astype(np.float64)
+    return quest_bound(q, m[:, 0], m[:, 1])
+
+
+def topk_scores(S: np.ndarray) -> np.ndarray:
+    """Per-KV-head score of each page: the largest bound over the group's query heads."""
+    return S.max(axis=0)
+
+
+def coverage_shares(S: np.ndarray, seq_len: int, sm_scale: float):
+    """Moira's group-mean share pi_bar of each page, from the bound as the page log-mass.
+
+    l_{g,p} = s * S_{g,p} + ln(valid_p);  pi_bar_p = (1/G) sum_g softmax_p(l_{g,.}).
+    Returns (pi_bar [n], lse_g [G]).
+    """
+    n = S.shape[1]
+    valid = np.array([valid_tokens(seq_len, p) for p in range(n)], dtype=np.float64)
+    ell = sm_scale * S + np.log(valid)[None, :]
+    mx = ell.max(axis=1, keepdims=True)
+    lse = mx[:, 0] + np.log(np.exp(ell - mx).sum(axis=1))
+    share = np.exp(ell - lse[:, None])
+    return share.mean(axis=0), lse
+
+
+# --------------------------------------------------------------------------------------
+# a2: page selection
+# --------------------------------------------------------------------------------------
+
+def forced_pages(n: int, n_sink: int, n_local: int) -> list:
+    """Sink pages 0..n_sink-1 and local pages n-n_local..n-1 (LServe static index table)."""
+    s = set(range(min(max(n_sink, 0), n))) | set(range(max(0, n - max(n_local, 0)), n))
+    return sorted(s)
+
+
+def select_topk(scores: np.ndarray, n: int, budget: int, forced: list) -> list:
+    """Forced pages plus the (budget - |forced|) best others by (score desc, page asc)."""
+    fset = set(forced)
+    k_rest = budget - len(forced)
+    others = [p for p in range(n) if p not in fset]
+    if k_rest <= 0:
+        return sorted(fset)
+    order = sorted(others, key=lambda p: (-float(scores[p]), p))
+    return sorted(fset | set(order[:k_rest]))
+
+
+def select_coverage(pi: np.ndarray, n: int, gamma: float, forced: list) -> list:
+    """Moira Eq. 3: forced pages plus every other page with share >= tau_b."""
+    fset = set(forced)
+    t = gamma - sum(float(pi[p]) for p in forced)
+    if t - COVERAGE_SLACK <= 0:
+        return sorted(fset)
+    others = [p for p in range(n) if p not in fset]
+    order = sorted(others, key=lambda p: (-float(pi[p]), p))
+    cum = 0.0
+    for p in order:
+        cum += float(pi[p])
+        if cum >= t - COVERAGE_SLACK:
+            tau = float(pi[p])
+            return sorted(fset | {r for r in others if float(pi[r]) >= tau})
+    return list(range(n))
+
+
+def page_select(inp, meta: np.ndarray):
+    """Scores and lists for every (request, KV head) row.
+
+    Returns dict with 'lists' {(b,h): [pages]}, 'scores' {(b,h): per-page key or None
+    for streaming rows}, 'S' {(b,h): [G, n] bounds}, 'lse' {(b,h): [G]} (coverage only).
+    """
+    w = inp.workload
+    out = {"lists": {}, "scores": {}, "S": {}, "lse": {}}
+    for b in range(len(inp.seq_lens)):
+        L = int(inp.seq_lens[b])
+        n = n_pages(L)
+        for h in range(inp.k_pool.shape[1]):
+            if inp.head_kind[h]:
+                out["lists"][(b, h)] = forced_pages(n, w.n_sink_stream, w.n_local_stream)
+                out["scores"][(b, h)] = None
+                continue
+            S = row_bounds(inp, meta, b, h)
+            out["S"][(b, h)] = S
+            forced = forced_pages(n, w.n_sink, w.n_local)
+            if w.mode == "topk":
+                sc = topk_scores(S)
+                out["scores"][(b, h)] = sc
+                out["lists"][(b, h)] = select_topk(sc, n, w.budget_pages, forced)
+            else:
+                pi, lse = coverage_shares(S, L, w.sm_scale) if n else (np.zeros(0), np.full(w.group, -np.inf))
+                out["scores"][(b, h)] = pi
+                out["lse"][(b, h)] = lse
+                out["lists"][(b, h)] = select_coverage(pi, n, w.gamma, forced) if n else []
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# a3 + a4: attention over the kept pages
+# --------------------------------------------------------------------------------------
+
+def gather_tokens(inp, b: int, h: int, pages) -> tuple:
+    """Valid keys and values (float64) of the listed logical pages of row (b, h), in list order."""
+    w = inp.workload
+    L = int(inp.seq_lens[b])
+    ks, vs = [], []
+    for p in pages:
+        phys = int(inp.block_table[b, int(p)])
+        valid = valid_tokens(L, int(p))
+        ksc = None if inp.k_scale is None else inp.k_scale[phys, h]
+        vsc = None if inp.v_scale is None else inp.v_scale[phys, h]
+        ks.append(stored_values(inp.k_pool[phys, h], ksc, w.kv_dtype)[:valid])
+        vs.append(stored_values(inp.v_pool[phys, h], vsc, w.kv_dtype)[:valid])
+    d = inp.k_pool.shape[3]
+    if not ks:
+        return np.zeros((0, d)), np.zeros((0, d))
+    return np.concatenate(ks), np.concatenate(vs)
+
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float):
+    """PersistentKV Eq. 1 for one query: O = sum_j softmax_j(s q.k_j) v_j, lse = log sum_j e^{s q.k_j}.
+
+    q [d], K/V [N, d] float64.  N = 0 gives (zeros, -inf).
+    """
+    if K.shape[0] == 0:
+        return np.zeros(K.shape[1]), -np.inf
+    x = sm_scale * (K @ q)
+    m = x.max()
+    e = np.exp(x - m)
+    lsum = e.sum()
+    return (e @ V) / lsum, m + math.log(lsum)
+
+
+def sparse_paged_decode(inp, lists: dict, sm_scale: float):
+    """O [B, Hq, d] and lse [B, Hq] of attention restricted to each row's listed pages."""
+    w = inp.workload
+    B, Hq, d = inp.q.shape
+    G = w.group
+    O = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), -np.inf)
+    for (b, h), pages in lists.items():
+        K, V = gather_tokens(inp, b, h, pages)
+        for g in range(G):
+            qh = inp.q[b, h * G + g].astype(np.float64)
+            O[b, h * G + g], lse[b, h * G + g] = attention(qh, K, V, sm_scale)
+    return O, lse
+
+
+def merge_states(states):
+    """PersistentKV section 3.3 exact merge of split states (m_s, l_s, a_s) -> (O, lse)."""
+    ms = np.array([s[0] for s in states], dtype=np.float64)
+    m = ms.max()
+    if not np.isfinite(m):
+        return np.zeros_like(states[0][2]), -np.inf
+    ell = sum(math.exp(s[0] - m) * s[1] for s in states if np.isfinite(s[0]))
+    acc = sum(math.exp(s[0] - m) * s[2] for s in states if np.isfinite(s[0]))
+    return acc / ell, m + math.log(ell)
+
+
+def split_state(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float):
+    """One split's partial state (m_s, l_s, a_s); the empty split is (-inf, 0, 0)."""
+    if K.shape[0] == 0:
+        return (-np.inf, 0.0, np.zeros(K.shape[1]))
+    x = sm_scale * (K @ q)
+    m = x.max()
+    e = np.exp(x - m)
+    return (m, e.sum(), e @ V)
+
+
+# --------------------------------------------------------------------------------------
+# Whole step
+# --------------------------------------------------------------------------------------
+
+def decode_step(inp, meta: np.ndarray | None = None):
+    """Metadata (if not given) -> scores -> lists -> attention, as the method orders them."""
+    if meta is None:
+        meta = page_meta_build(inp)
+    sel = page_select(inp, meta)
+    O, lse = sparse_paged_decode(inp, sel["lists"], inp.workload.sm_scale)
+    return {"meta": meta, **sel, "O": O, "out_lse": lse}

@@ -1,0 +1,371 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+Each test ties one oracle function to a closed form, a worked example printed on
+the pages (fixtures under tests/golden/ carry the citation), a library routine,
+an invariant, or brute force on tiny inputs, chosen so that a dropped term, a
+wrong sign or index, or a transposed operand fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import spd_oracle as O
+from sparse_paged_decode_quest_amd import workloads as W
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ fp8 decoding
+
+def test_e4m3fn_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.decode_e4m3fn(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+
+
+def test_e4m3fn_spec_values(golden_dir):
+    g = _load(golden_dir, "e4m3fn_known_values.json")
+    for item in g["values"]:
+        v = float(O.decode_e4m3fn(np.array([int(item["code"], 16)], dtype=np.uint8))[0])
+        if item["value"] == "nan":
+            assert math.isnan(v)
+        else:
+            assert v == item["value"] and math.copysign(1, v) == math.copysign(1, item["value"])
+
+
+# ------------------------------------------------------------------ key min / max
+
+def _torch_fp8_values(codes, scale):
+    t = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64)
+    return t.numpy() * scale.astype(np.float64)[..., None]
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16", "fp8"])
+def test_meta_matches_elementwise_loops(kv):
+    w = W.small(kv=kv, q="f32" if kv == "f32" else "f16", d=64, seq_lens=(70, 16, 5, 33), Hq=4, Hkv=2,
+                seed=11)
+    inp = W.generate(w)
+    meta = O.page_meta_build(inp)
+    for b, L in enumerate(w.seq_lens):
+        for p in range((L + 15) // 16):
+            phys = inp.block_table[b, p]
+            valid = min(16, L - 16 * p)
+            for h in range(w.num_kv_heads):
+                if kv == "fp8":
+                    vals = _torch_fp8_values(inp.k_pool[phys, h], inp.k_scale[phys, h])
+                else:
+                    vals = inp.k_pool[phys, h].astype(np.float64)
+                for c in range(w.head_dim):
+                    col = [vals[t, c] for t in range(valid)]
+                    lo, hi = min(col), max(col)
+                    slo, shi = float(meta[phys, h, 0, c]), float(meta[phys, h, 1, c])
+                    if kv == "fp8":
+                        # smallest fp16 >= max and largest fp16 <= min
+                        assert shi >= hi and float(np.nextafter(np.float16(shi), np.float16(-np.inf))) < hi
+                        assert slo <= lo and float(np.nextafter(np.float16(slo), np.float16(np.inf))) > lo
+                    else:
+                        assert slo == lo and shi == hi
+
+
+def test_meta_first_page_only_touches_tail():
+    w = W.small(seq_lens=(100, 40), d=64, seed=3)
+    inp = W.generate(w)
+    full = O.page_meta_build(inp)
+    sentinel = np.full_like(full, 7.0)
+    first = np.array([(100 + 15) // 16 - 1, (40 + 15) // 16 - 1])
+    tail = O.page_meta_build(inp, meta=sentinel, first_page=first)
+    for b, L in enumerate(w.seq_lens):
+        n = (L + 15) // 16
+        for p in range(n):
+            phys = inp.block_table[b, p]
+            if p >= first[b]:
+                assert np.array_equal(tail[phys], full[phys])
+            else:
+                assert np.all(tail[phys] == 7.0)
+
+
+# ------------------------------------------------------------------ the page bound
+
+def test_bound_is_max_over_box_corners():
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        d, G = 5, 3
+        q = rng.standard_normal((G, d))
+        a = rng.standard_normal((1, d))
+        b = rng.standard_normal((1, d))
+        kmin, kmax = np.minimum(a, b), np.maximum(a, b)
+        S = O.quest_bound(q, kmin, kmax)
+        for g in range(G):
+            best = max(sum(q[g, c] * (kmax[0, c] if bit else kmin[0, c]) for c, bit in enumerate(bits))
+                       for bits in itertools.product([0, 1], repeat=d))
+            assert abs(S[g, 0] - best) < 1e-12
+
+
+def test_bound_identical_keys_is_exact_dot():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((4, 64))
+    k = rng.standard_normal((1, 64))
+    S = O.quest_bound(q, k, k)
+    assert np.allclose(S[:, 0], q @ k[0], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16", "fp8"])
+def test_bound_upper_bounds_every_key(kv):
+    w = W.small(kv=kv, q="f32" if kv == "f32" else "f16", seq_lens=(300, 23, 129), Hq=8, Hkv=2,
+                planted=("fixed", 3), seed=21)
+    inp = W.generate(w)
+    meta = O.page_meta_build(inp)
+    G = w.group
+    for b, L in enumerate(w.seq_lens):
+        n = (L + 15) // 16
+        for h in range(w.num_kv_heads):
+            S = O.row_bounds(inp, meta, b, h)
+            assert S.shape == (G, n)
+            for p in range(n):
+                K, _ = O.gather_tokens(inp, b, h, [p])
+                for g in range(G):
+                    qg = inp.q[b, h * G + g].astype(np.float64)
+                    tol = 1e-12 * float(np.abs(qg) @ np.abs(K).max(axis=0))
+                    assert S[g, p] >= (K @ qg).max() - tol
+
+
+# ------------------------------------------------------------------ top-K selection
+
+def test_topk_matches_rank_counting():
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        n = int(rng.integers(0, 40))
+        scores = rng.integers(-3, 4, size=n).astype(np.float64)  # many ties
+        budget = int(rng.integers(1, 20))
+        ns, nl = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+        forced = O.forced_pages(n, ns, nl)
+        got = O.select_topk(scores, n, budget, forced)
+        fset = set(forced)
+        others = [p for p in range(n) if p not in fset]
+        k_rest = max(0, budget - len(forced))
+        want = set(forced)
+        for p in others:
+            rank = sum(1 for r in others if scores[r] > scores[p] or (scores[r] == scores[p] and r < p))
+            if rank < k_rest:
+                want.add(p)
+        assert got == sorted(want), (trial, n, budget)
+        assert got == sorted(got) and len(set(got)) == len(got)
+
+
+def test_topk_budget_covering_row_keeps_all():
+    s = np.arange(10, dtype=np.float64)[::-1]
+    assert O.select_topk(s, 10, 10, O.forced_pages(10, 1, 2)) == list(range(10))
+    assert O.select_topk(s, 10, 50, O.forced_pages(10, 1, 2)) == list(range(10))
+
+
+def test_topk_forced_exceeding_budget_is_forced_set():
+    s = np.zeros(30)
+    assert O.select_topk(s, 30, 2, O.forced_pages(30, 1, 2)) == [0, 28, 29]
+
+
+def test_streaming_table(golden_dir):
+    g = _load(golden_dir, "streaming_index_table.json")
+    for c in g["cases"]:
+        assert O.forced_pages(c["n_pages"], c["n_sink"], c["n_local"]) == c["table"]
+
+
+def test_streaming_rows_get_the_static_table():
+    w = W.small(seq_lens=(1000, 20), streaming=(1,), n_sink_stream=2, n_local_stream=5, seed=8)
+    inp = W.generate(w)
+    sel = O.page_select(inp, O.page_meta_build(inp))
+    assert sel["lists"][(0, 1)] == [0, 1] + list(range(63 - 5, 63))
+    assert sel["lists"][(1, 1)] == [0, 1]  # 20 tokens are 2 pages
+    assert sel["scores"][(0, 1)] is None
+
+
+# ------------------------------------------------------------------ coverage selection
+
+def test_coverage_worked_example(golden_dir):
+    g = _load(golden_dir, "coverage_worked_example.json")
+    pi = np.array(g["shares"])
+    for c in g["cases"]:
+        got = O.select_coverage(pi, len(pi), c["gamma"], forced=[])
+        assert len(got) == c["kept"] and got == c["pages"]
+
+
+def test_coverage_minimal_by_enumeration():
+    rng = np.random.default_rng(9)
+    for trial in range(200):
+        n = int(rng.integers(2, 13))
+        pi = rng.dirichlet(np.full(n, 0.3))
+        gamma = float(rng.uniform(0.3, 0.999))
+        forced = O.forced_pages(n, 1, 1)
+        got = O.select_coverage(pi, n, gamma, forced)
+        others = [p for p in range(n) if p not in forced]
+        t = gamma - sum(pi[p] for p in forced)
+        assert set(forced) <= set(got)
+        if t <= 0:
+            assert got == forced
+            continue
+        best = None
+        for r in range(len(others) + 1):
+            if any(sum(pi[p] for p in sub) >= t for sub in itertools.combinations(others, r)):
+                best = r
+                break
+        chosen = [p for p in got if p not in forced]
+        assert len(chosen) == best, trial
+        assert sum(pi[p] for p in chosen) >= t - 1e-12
+        # threshold set: every unchosen page has a smaller share than every chosen one
+        unchosen = [p for p in others if p not in chosen]
+        if chosen and unchosen:
+            assert max(pi[p] for p in unchosen) < min(pi[p] for p in chosen)
+
+
+def test_coverage_ties_at_threshold_are_all_kept():
+    pi = np.array([0.0, 0.4, 0.2, 0.2, 0.2, 0.0])
+    got = O.select_coverage(pi, 6, 0.55, forced=[0, 5])
+    assert got == [0, 1, 2, 3, 4, 5]  # tau = 0.2 and every page with share >= tau is kept
+
+
+def test_coverage_gamma_one_keeps_all_and_forced_mass_short_circuits():
+    rng = np.random.default_rng(10)
+    pi = rng.dirichlet(np.ones(50))
+    assert O.select_coverage(pi, 50, 1.0, O.forced_pages(50, 1, 1)) == list(range(50))
+    pi2 = np.zeros(20)
+    pi2[0], pi2[19] = 0.6, 0.4
+    assert O.select_coverage(pi2, 20, 0.99, O.forced_pages(20, 1, 1)) == [0, 19]
+
+
+def test_coverage_shares_normalise_and_lse_matches_library():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(12)
+    S = rng.standard_normal((4, 37)) * 30
+    pi, lse = O.coverage_shares(S, 37 * 16 - 5, 0.125)
+    assert abs(pi.sum() - 1.0) < 1e-12
+    valid = np.array([16] * 36 + [11], dtype=np.float64)
+    ell = 0.125 * S + np.log(valid)
+    assert np.allclose(lse, logsumexp(ell, axis=1), rtol=0, atol=1e-12)
+    # the share of a page grows with its bound (monotone in every head)
+    S2 = S.copy()
+    S2[:, 3] += 1.0
+    pi2, _ = O.coverage_shares(S2, 37 * 16 - 5, 0.125)
+    assert pi2[3] > pi[3]
+
+
+# ------------------------------------------------------------------ attention
+
+def _dense_unpaged(inp, b, h):
+    """Contiguous keys / values of request b, KV head h, read token by token."""
+    L = int(inp.seq_lens[b])
+    w = inp.workload
+    ks, vs = [], []
+    for t in range(L):
+        phys = inp.block_table[b, t // 16]
+        if w.kv_dtype == "fp8":
+            ks.append(_torch_fp8_values(inp.k_pool[phys, h, t % 16][None], inp.k_scale[phys, h, t % 16][None])[0])
+            vs.append(_torch_fp8_values(inp.v_pool[phys, h, t % 16][None], inp.v_scale[phys, h, t % 16][None])[0])
+        else:
+            ks.append(inp.k_pool[phys, h, t % 16].astype(np.float64))
+            vs.append(inp.v_pool[phys, h, t % 16].astype(np.float64))
+    return np.array(ks), np.array(vs)
+
+
+def _sdpa(q, K, V, scale):
+    qt = torch.from_numpy(q)[None, None, None, :]
+    kt = torch.from_numpy(K)[None, None]
+    vt = torch.from_numpy(V)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    lse = torch.logsumexp(torch.from_numpy(K @ q) * scale, dim=0)
+    return o[0, 0, 0].numpy(), float(lse)
+
+
+@pytest.mark.parametrize("kv,mode", [("f32", "topk"), ("f16", "topk"), ("fp8", "topk"), ("f16", "coverage")])
+def test_all_pages_equals_dense_attention(kv, mode):
+    seq = (333, 48, 17)
+    w = W.small(kv=kv, q="f32" if kv == "f32" else "f16", seq_lens=seq, Hq=8, Hkv=2,
+                mode=mode, budget=1000, gamma=1.0, seed=13)
+    inp = W.generate(w)
+    res = O.decode_step(inp)
+    G = w.group
+    for b in range(len(seq)):
+        for h in range(w.num_kv_heads):
+            assert res["lists"][(b, h)] == list(range((seq[b] + 15) // 16))
+            K, V = _dense_unpaged(inp, b, h)
+            for g in range(G):
+                qh = inp.q[b, h * G + g].astype(np.float64)
+                o_ref, lse_ref = _sdpa(qh, K, V, w.sm_scale)
+                assert np.allclose(res["O"][b, h * G + g], o_ref, rtol=0, atol=1e-12)
+                assert abs(res["out_lse"][b, h * G + g] - lse_ref) < 1e-12
+
+
+def test_streaming_attention_is_dense_over_sink_and_local_tokens():
+    w = W.small(seq_lens=(500,), streaming=(0,), n_sink_stream=2, n_local_stream=3, Hq=4, Hkv=2, seed=14)
+    inp = W.generate(w)
+    res = O.decode_step(inp)
+    K, V = _dense_unpaged(inp, 0, 0)
+    keep = list(range(32)) + list(range(29 * 16, 500))  # pages 0,1 and 29,30,31 (last partial)
+    for g in range(2):
+        qh = inp.q[0, g].astype(np.float64)
+        o_ref, lse_ref = _sdpa(qh, K[keep], V[keep], w.sm_scale)
+        assert np.allclose(res["O"][0, g], o_ref, rtol=0, atol=1e-12)
+        assert abs(res["out_lse"][0, g] - lse_ref) < 1e-12
+
+
+def test_split_merge_is_exact():
+    rng = np.random.default_rng(15)
+    q = rng.standard_normal(64)
+    K = rng.standard_normal((200, 64)) * 3
+    V = rng.standard_normal((200, 64))
+    o_ref, lse_ref = O.attention(q, K, V, 0.125)
+    for _ in range(20):
+        cuts = sorted(rng.choice(np.arange(1, 200), size=int(rng.integers(1, 8)), replace=False))
+        bounds = [0, *cuts, 200]
+        states = [O.split_state(q, K[a:b], V[a:b], 0.125) for a, b in zip(bounds[:-1], bounds[1:])]
+        states.append(O.split_state(q, K[:0], V[:0], 0.125))  # an empty split is neutral
+        o, lse = O.merge_states(states)
+        assert np.allclose(o, o_ref, rtol=0, atol=1e-12) and abs(lse - lse_ref) < 1e-12
+
+
+def test_empty_row_convention():
+    o, lse = O.attention(np.ones(8), np.zeros((0, 8)), np.zeros((0, 8)), 0.5)
+    assert np.all(o == 0) and lse == -np.inf
+
+
+# ------------------------------------------------------------------ the generator
+
+def test_generator_is_deterministic():
+    w = W.small(kv="fp8", seq_lens=(90, 31), seed=16)
+    a, b = W.generate(w), W.generate(w)
+    for name in ("q", "k_pool", "v_pool", "k_scale", "v_scale", "block_table", "seq_lens", "head_kind"):
+        x, y = getattr(a, name), getattr(b, name)
+        assert x.tobytes() == y.tobytes(), name
+    c = W.generate(w, seed=17)
+    assert c.q.tobytes() != a.q.tobytes()
+
+
+def test_partial_pages_and_holes_hold_nan_yet_results_are_finite():
+    w = W.small(seq_lens=(37, 5), hole=0.5, seed=18)
+    inp = W.generate(w)
+    assert np.isnan(inp.k_pool[inp.block_table[0, 2], :, 5:]).all()
+    res = O.decode_step(inp)
+    assert np.isfinite(res["O"]).all() and np.isfinite(res["out_lse"]).all()
+
+
+def test_tiny_workload_selects_its_planted_pages():
+    w = W.named("tiny_b1_hq8_d64_4k_f32")
+    inp = W.generate(w)
+    res = O.decode_step(inp)
+    for h in range(2):
+        lst = res["lists"][(0, h)]
+        assert len(lst) == 32
+        # a +2 sigma shift along the query direction lifts the bound by about two standard
+        # deviations of its spread over N(0, 1) pages, so most (not all) planted pages rank high
+        hit = len(set(inp.planted[(0, h)].tolist()) & set(lst))
+        assert hit >= 5, hit
