@@ -1,0 +1,249 @@
+/*
+ * spd.h -- C ABI of a sparse paged decode-attention step for AMD gfx950.
+ *
+ * One decode step, per (request b, KV head h) "row":
+ *   1. page_meta_build      per-page channel-wise key min / max
+ *                           (LServe summary, "Hierarchical Paging" -- logical page
+ *                           statistics k_min / k_max -- and "Key statistics storage and
+ *                           updating": refreshed as tokens are appended)
+ *   2. page_score           Quest-style page bound S_j = sum_i max(q_i kmax_i, q_i kmin_i)
+ *                           (LServe, "Hierarchical Paging", page importance score), combined
+ *                           over the query-head group; in coverage mode turned into Moira's
+ *                           group-mean page share pi_bar (Moira, section 3.2, Eq. 3)
+ *   3. page_select          page list per row: forced sink + local pages plus either the
+ *                           best pages under a page budget (LServe, "Token budget and
+ *                           physical page selection") or the smallest share-threshold set
+ *                           reaching gamma (Moira, section 3.2, Eq. 3 and Algorithm 1);
+ *                           streaming heads take only the static sink + local table
+ *                           (LServe, "Decoding Stage: Kernel Implementation with Two-Level
+ *                           Indexing")
+ *   4. sparse_paged_decode  grouped-query decode attention over the listed pages through the
+ *                           native block table (PersistentKV, sections 3.1-3.3), split over a
+ *                           device-side self-planned grid (Moira, section 3.3, Eq. 4 and
+ *                           Algorithm 2)
+ *   5. lse_merge            exact log-sum-exp merge of the split states (PersistentKV,
+ *                           section 3.3; Moira, section 3.3 "Merge")
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers marked (device) are device memory owned by the caller; pointers marked (host)
+ *    are host memory read during the call only.  The library never allocates, frees or
+ *    synchronises, and never reads device memory from the host, so every call can be
+ *    captured into a hipGraph.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is only
+ *    enqueued; results are ready when the stream reaches the enqueued work.
+ *  - Every call returns SPD_OK (0) or a negative spd_status.  Argument checks happen on the
+ *    host before anything is enqueued; on an error nothing is launched.  SPD_ERR_LAUNCH
+ *    reports a HIP launch failure.  No exceptions cross the ABI and there is no global
+ *    mutable state, so calls from several host threads are safe.
+ *  - Layouts are dense row-major C arrays:
+ *      q            [B, Hq, d]                 f32 or f16 (spd_desc.q_dtype)
+ *      k_pool,v_pool [num_pool_pages, Hkv, 16, d]  f32, f16 or fp8 E4M3FN bytes
+ *      k_scale,v_scale [num_pool_pages, Hkv, 16]  fp16 bits (fp8 pools only; value =
+ *                                              E4M3FN(code) * scale)
+ *      page_meta    [num_pool_pages, Hkv, 2, d] index 0 = channel min, 1 = channel max;
+ *                                              f32 for f32 pools, f16 otherwise (for fp8
+ *                                              pools rounded outward: min down, max up)
+ *      block_table  [B, max_pages_per_seq]     int32 physical page of each logical page
+ *      seq_lens     [B]                        int32 tokens of each request
+ *      head_kind    [Hkv]                      uint8 (host) SPD_HEAD_DYNAMIC or _STREAMING
+ *      scores       [B, Hkv, max_pages_per_seq] f32
+ *      page_list    [B, Hkv, max_list]         int32 logical pages, ascending
+ *      list_len     [B, Hkv]                   int32
+ *      out          [B, Hq, d]                 f32; out_lse [B, Hq] f32 (natural log of the
+ *                                              softmax denominator of the scaled logits)
+ *      part_o       [B, Hkv, J, G, d] f32 and part_lse [B, Hkv, J, G] f32, J from
+ *                                              spd_plan_grid
+ *  - Request b has n_b = ceil(seq_lens[b] / 16) logical pages; logical page p holds
+ *    min(16, seq_lens[b] - 16 p) valid tokens (PersistentKV, section 3.3: bounds follow the
+ *    row's own length).  Only valid tokens enter the statistics and the attention; the
+ *    remaining slots of a partial page may hold anything, NaN included.
+ *  - Robustness: n_b is clamped to max_pages_per_seq, negative lengths count as 0, list
+ *    entries outside [0, n_b) and block-table entries outside [0, num_pool_pages) are
+ *    treated as empty pages (never dereferenced).
+ */
+#ifndef SPD_H_
+#define SPD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPD_ABI_VERSION 1
+#define SPD_PAGE_SIZE 16
+#define SPD_MAX_KV_HEADS 64
+
+typedef enum spd_status {
+  SPD_OK = 0,
+  SPD_ERR_INVALID_ARG = -1,  /* null pointer, inconsistent sizes, bad enum value */
+  SPD_ERR_UNSUPPORTED = -2,  /* valid but not compiled: head dim, group size, dtype combo */
+  SPD_ERR_LAUNCH = -3,       /* a HIP launch failed (hipGetLastError) */
+  SPD_ERR_WORKSPACE = -4     /* workspace null or smaller than spd_workspace_bytes */
+} spd_status;
+
+typedef enum spd_dtype {
+  SPD_DTYPE_F32 = 0,
+  SPD_DTYPE_F16 = 1,
+  SPD_DTYPE_FP8_E4M3FN = 2   /* OCP 8-bit E4M3, no infinities, 0x7F / 0xFF are NaN */
+} spd_dtype;
+
+typedef enum spd_select_mode {
+  SPD_SELECT_TOPK = 0,       /* fixed page budget */
+  SPD_SELECT_COVERAGE = 1    /* smallest share-threshold set reaching gamma */
+} spd_select_mode;
+
+typedef enum spd_head_kind {
+  SPD_HEAD_DYNAMIC = 0,
+  SPD_HEAD_STREAMING = 1
+} spd_head_kind;
+
+typedef enum spd_op {
+  SPD_OP_PAGE_SCORE = 0,
+  SPD_OP_PAGE_SELECT = 1,
+  SPD_OP_PAGE_SCORE_SELECT = 2
+} spd_op;
+
+/* Shapes of one step.  Supported: page_size 16; head_dim 64 or 128; Hq / Hkv = 4;
+ * (q_dtype, kv_dtype) in {(f32, f32), (f16, f16), (f16, fp8)}.  Others return
+ * SPD_ERR_UNSUPPORTED so a caller can route them elsewhere. */
+typedef struct spd_desc {
+  int32_t batch;              /* B >= 0 */
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv, 1..SPD_MAX_KV_HEADS, divides Hq */
+  int32_t head_dim;           /* d */
+  int32_t page_size;          /* must be 16 */
+  int32_t max_pages_per_seq;  /* block-table row stride, >= 1 */
+  int32_t num_pool_pages;     /* pool pages, >= 1 */
+  int32_t max_list;           /* page_list row stride, >= 1 */
+  int32_t q_dtype;            /* spd_dtype */
+  int32_t kv_dtype;           /* spd_dtype */
+} spd_desc;
+
+/* Selection rule.  Forced pages of a dynamic row are 0..n_sink-1 and n_b-n_local..n_b-1;
+ * a streaming row keeps exactly 0..n_sink_stream-1 and n_b-n_local_stream..n_b-1 (each
+ * page once).  TOPK: the list holds the forced pages plus the best budget_pages - |forced|
+ * other pages by (score desc, page asc); all pages when n_b <= budget_pages; only the
+ * forced pages when they fill the budget.  COVERAGE: t = gamma - sum of forced shares;
+ * the list holds the forced pages plus every other page whose share is >= tau, the
+ * largest share value whose at-or-above mass reaches t (Moira, Eq. 3); t <= 0 keeps the
+ * forced pages only, and all pages are kept when the other pages cannot reach t. */
+typedef struct spd_select_params {
+  int32_t mode;               /* spd_select_mode */
+  int32_t budget_pages;       /* TOPK budget (pages, forced included), >= 1 */
+  float gamma;                /* COVERAGE target in (0, 1] */
+  float sm_scale;             /* COVERAGE log-mass scale s (usually 1/sqrt(d)), > 0 */
+  int32_t n_sink;
+  int32_t n_local;
+  int32_t n_sink_stream;
+  int32_t n_local_stream;
+} spd_select_params;
+
+/* Self-planned split (Moira, section 3.3, Eq. 4): J = max(min_blocks_per_row,
+ * ceil(min_grid_blocks / (B * Hkv))) blocks per row; row with n listed pages is cut into
+ * chunks of c = max(min_chunk, ceil(n / J)) pages, m = ceil(n / c) of them; block j >= m
+ * exits at once.  J is fixed by (B, Hkv) so a captured graph serves every list length. */
+typedef struct spd_plan_params {
+  int32_t min_chunk;          /* C >= 1 */
+  int32_t min_blocks_per_row; /* N_J >= 1 */
+  int32_t min_grid_blocks;    /* N_T >= 0 */
+} spd_plan_params;
+
+/* ------------------------------------------------------------------ entry points */
+
+/* Channel-wise min / max of the valid keys of logical pages p of each request, for every KV
+ * head, written to page_meta at the page's physical slot.  first_page (device, [B], may be
+ * NULL): when NULL every page 0..n_b-1 is built; otherwise pages first_page[b] ..
+ * min(n_b, first_page[b] + span_pages) - 1 are built (span_pages >= 1) -- the tail refresh
+ * of a decode step uses first_page = n_b - 1, span_pages = 1.  k_scale (device) is
+ * required for fp8 pools and ignored otherwise.  Other slots of page_meta are not touched. */
+int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t* k_scale,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* first_page, int32_t span_pages, void* page_meta,
+                        void* stream);
+
+/* Page scores of every dynamic row (streaming rows are skipped, their scores untouched).
+ * TOPK: scores[b,h,p] = max over the G query heads of the row of S_{g,p} (LServe page
+ * importance, computed from page_meta).  COVERAGE: l_{g,p} = sm_scale * S_{g,p} +
+ * ln(valid tokens of p); head_lse[b, h*G+g] = logsumexp_p l_{g,p}; scores[b,h,p] =
+ * (1/G) sum_g exp(l_{g,p} - head_lse) (Moira's group-mean share, Algorithm 1 line "group
+ * mean").  head_lse (device, [B, Hq]) may be NULL in TOPK mode.  workspace (device) of
+ * spd_workspace_bytes(desc, sel, SPD_OP_PAGE_SCORE) bytes (0 in TOPK mode). */
+int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const void* q,
+                   const void* page_meta, const int32_t* block_table, const int32_t* seq_lens,
+                   const uint8_t* head_kind, float* scores, float* head_lse, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Page list of every row from its scores (selection rule: spd_select_params).  Lists are
+ * ascending logical pages.  sel_scores (device, [B, Hkv, max_list], may be NULL) receives
+ * the score of each listed page of a dynamic row (streaming rows: untouched).  Returns
+ * SPD_ERR_INVALID_ARG when max_list cannot hold the longest possible list: TOPK needs
+ * max_list >= max(budget, n_sink + n_local) and >= n_sink_stream + n_local_stream;
+ * COVERAGE needs max_list >= max_pages_per_seq. */
+int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const float* scores,
+                    const int32_t* seq_lens, const uint8_t* head_kind, int32_t* page_list,
+                    int32_t* list_len, float* sel_scores, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* spd_page_score followed by spd_page_select in one launch for TOPK mode (LiteTopK,
+ * section 3.2, "Extension to Decoding": selection fused into score computation).  The
+ * scores stay in the workspace; the last block to finish a row selects its pages.
+ * workspace (device) of spd_workspace_bytes(desc, sel, SPD_OP_PAGE_SCORE_SELECT) bytes
+ * must be zero-filled before its first use; every call leaves its counters zero again.
+ * Calls that share one workspace must not overlap.  COVERAGE returns SPD_ERR_UNSUPPORTED. */
+int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, const void* q,
+                          const void* page_meta, const int32_t* block_table,
+                          const int32_t* seq_lens, const uint8_t* head_kind, int32_t* page_list,
+                          int32_t* list_len, float* sel_scores, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Grouped-query decode attention of every row over its listed pages.  Block (b, h, j)
+ * processes chunk j of row (b, h) (spd_plan_params); rows with one chunk write out /
+ * out_lse directly, rows with more write their chunk states to part_o / part_lse for
+ * spd_lse_merge.  A row with no listed pages writes out = 0 and out_lse = -inf.
+ * k_scale / v_scale (device) are required for fp8 pools. */
+int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, const void* q,
+                            const void* k_pool, const void* v_pool, const uint16_t* k_scale,
+                            const uint16_t* v_scale, const int32_t* block_table,
+                            const int32_t* seq_lens, const int32_t* page_list,
+                            const int32_t* list_len, float sm_scale, float* out, float* out_lse,
+                            float* part_o, float* part_lse, void* stream);
+
+/* Exact merge of the chunk states of every row with more than one chunk:
+ * out_lse = log sum_j exp(lse_j), out = sum_j exp(lse_j - out_lse) * o_j.  Rows with at
+ * most one chunk are left as spd_sparse_paged_decode wrote them.  Must see the same
+ * list_len and plan as the decode call it follows. */
+int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float* part_o,
+                  const float* part_lse, const int32_t* list_len, float* out, float* out_lse,
+                  void* stream);
+
+/* ------------------------------------------------------------------ host helpers */
+
+/* J, the blocks per row of spd_sparse_paged_decode (Moira, Eq. 4). */
+int spd_plan_grid(const spd_desc* desc, const spd_plan_params* plan, int32_t* blocks_per_row);
+
+/* Chunk size c and chunk count m of a row with n_pages listed pages under J blocks per
+ * row and minimum chunk min_chunk (Moira, Eq. 4 and Algorithm 2); n_pages = 0 gives 0 / 0. */
+int spd_plan_chunks(int32_t n_pages, int32_t blocks_per_row, int32_t min_chunk,
+                    int32_t* chunk_pages, int32_t* chunks);
+
+/* Element counts of part_o and part_lse for spd_sparse_paged_decode / spd_lse_merge. */
+int spd_partials_size(const spd_desc* desc, const spd_plan_params* plan, size_t* part_o_elems,
+                      size_t* part_lse_elems);
+
+/* Workspace bytes an op needs (0 when it needs none); (size_t)-1 on invalid arguments. */
+size_t spd_workspace_bytes(const spd_desc* desc, const spd_select_params* sel, int32_t op);
+
+/* Static description of a status code. */
+const char* spd_error_string(int status);
+
+/* SPD_ABI_VERSION of the built library. */
+int spd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPD_H_ */

@@ -110,18 +110,22 @@ def page_key_minmax(k_page: np.ndarray, valid: int):
     return keys.min(axis=0), keys.max(axis=0)
 
 
-def page_meta_build(inp, meta: np.ndarray | None = None, first_page=None) -> np.ndarray:
+def page_meta_build(inp, meta: np.ndarray | None = None, first_page=None, heads=None,
+                    requests=None) -> np.ndarray:
     """Key min / max for every page p >= first_page[b] of every request, all KV heads.
 
     Layout [num_pool_pages, Hkv, 2, d]: index 0 = kmin, 1 = kmax, in the meta dtype
     (f32 pools: f32; f16 pools: f16; fp8 pools: f16 rounded outward).  Pages not
-    visited keep the values of ``meta`` (zeros when it is None).
+    visited keep the values of ``meta`` (zeros when it is None).  ``heads`` and
+    ``requests`` restrict the work to some KV heads / requests (others are left as they are).
     """
     w = inp.workload
     Hkv, d = inp.k_pool.shape[1], inp.k_pool.shape[3]
     mdt = meta_dtype(w.kv_dtype)
     out = np.zeros((inp.k_pool.shape[0], Hkv, 2, d), dtype=mdt) if meta is None else meta.copy()
-    for b in range(len(inp.seq_lens)):
+    hs = list(range(Hkv)) if heads is None else [int(h) for h in heads]
+    reqs = range(len(inp.seq_lens)) if requests is None else [int(b) for b in requests]
+    for b in reqs:
         L = int(inp.seq_lens[b])
         start = 0 if first_page is None else max(0, int(first_page[b]))
         pages = list(range(start, n_pages(L)))
@@ -130,24 +134,25 @@ def page_meta_build(inp, meta: np.ndarray | None = None, first_page=None) -> np.
         # full pages, vectorised over chunks of pages (min / max over the token axis)
         for c in range(0, len(full), 512):
             phys = inp.block_table[b, full[c:c + 512]].astype(np.int64)
-            scale = None if inp.k_scale is None else inp.k_scale[phys]
-            kv = stored_values(inp.k_pool[phys], scale, w.kv_dtype)  # [n, Hkv, P, d]
-            lo, hi = _to_meta(kv.min(axis=2), kv.max(axis=2), w.kv_dtype)
-            out[phys, :, 0] = lo
-            out[phys, :, 1] = hi
+            for h in hs:
+                scale = None if inp.k_scale is None else inp.k_scale[phys, h]
+                kv = stored_values(inp.k_pool[phys, h], scale, w.kv_dtype)  # [n, P, d]
+                lo, hi = to_stored_meta(kv.min(axis=1), kv.max(axis=1), w.kv_dtype)
+                out[phys, h, 0] = lo
+                out[phys, h, 1] = hi
         for p in part:
             phys = int(inp.block_table[b, p])
             valid = valid_tokens(L, p)
-            scale = None if inp.k_scale is None else inp.k_scale[phys]
-            kv = stored_values(inp.k_pool[phys], scale, w.kv_dtype)  # [Hkv, P, d]
-            for h in range(Hkv):
-                lo, hi = _to_meta(*page_key_minmax(kv[h], valid), w.kv_dtype)
+            for h in hs:
+                scale = None if inp.k_scale is None else inp.k_scale[phys, h]
+                kv = stored_values(inp.k_pool[phys, h], scale, w.kv_dtype)  # [P, d]
+                lo, hi = to_stored_meta(*page_key_minmax(kv, valid), w.kv_dtype)
                 out[phys, h, 0] = lo
                 out[phys, h, 1] = hi
     return out
 
 
-def _to_meta(kmin: np.ndarray, kmax: np.ndarray, kv_dtype: str):
+def to_stored_meta(kmin: np.ndarray, kmax: np.ndarray, kv_dtype: str):
     """Stored form of float64 min / max: exact in the pool dtype, or fp16 outward for fp8."""
     if kv_dtype == "fp8":
         return _round_outward_f16(kmin, up=False), _round_outward_f16(kmax, up=True)

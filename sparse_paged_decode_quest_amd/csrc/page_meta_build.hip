@@ -1,0 +1,122 @@
+// Per-page channel-wise key min / max (LServe summary, "Hierarchical Paging": every
+// logical page keeps k_min and k_max over its keys; "Key statistics storage and updating":
+// the statistics of the page a new token lands in are refreshed as the token is appended).
+//
+// One wave per (request, logical page); the wave walks the KV heads.  Lane l owns channels
+// [l*CPL, (l+1)*CPL) of every token, so min / max over the page's valid tokens is
+// lane-local: no cross-lane traffic, 16 coalesced row loads per head.
+#include "spd_device.h"
+#include "spd_launch.h"
+
+namespace spd {
+
+template <int D, int KVD>
+struct MetaTraits;
+
+template <int D> struct MetaTraits<D, SPD_DTYPE_F32> {
+  static constexpr int CPL = D / kWave;
+  using Out = float;
+  __device__ static void load(const void* pool, size_t idx, float (&v)[CPL], float) {
+    const float* p = reinterpret_cast<const float*>(pool) + idx;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] = p[c];
+  }
+  __device__ static void store(void* meta, size_t idx, const float (&lo)[CPL], const float (&hi)[CPL], int d) {
+    float* m = reinterpret_cast<float*>(meta) + idx;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) { m[c] = lo[c]; m[d + c] = hi[c]; }
+  }
+};
+
+template <int D> struct MetaTraits<D, SPD_DTYPE_F16> {
+  static constexpr int CPL = D / kWave;
+  __device__ static void load(const void* pool, size_t idx, float (&v)[CPL], float) {
+    const __half* p = reinterpret_cast<const __half*>(pool) + idx;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] = __half2float(p[c]);
+  }
+  __device__ static void store(void* meta, size_t idx, const float (&lo)[CPL], const float (&hi)[CPL], int d) {
+    __half* m = reinterpret_cast<__half*>(meta) + idx;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {  // exact: min / max of fp16 values
+      m[c] = __float2half_rn(lo[c]);
+      m[d + c] = __float2half_rn(hi[c]);
+    }
+  }
+};
+
+template <int D> struct MetaTraits<D, SPD_DTYPE_FP8_E4M3FN> {
+  static constexpr int CPL = D / kWave;
+  __device__ static void load(const void* pool, size_t idx, float (&v)[CPL], float scale) {
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(pool) + idx;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] = fp8_to_float(p[c]) * scale;  // exact in fp32
+  }
+  __device__ static void store(void* meta, size_t idx, const float (&lo)[CPL], const float (&hi)[CPL], int d) {
+    uint16_t* m = reinterpret_cast<uint16_t*>(meta) + idx;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {  // outward: the stored box still contains every key
+      m[c] = f32_to_f16_round_down(lo[c]);
+      m[d + c] = f32_to_f16_round_up(hi[c]);
+    }
+  }
+};
+
+template <int D, int KVD>
+__global__ __launch_bounds__(256) void page_meta_build_kernel(MetaArgs a) {
+  using T = MetaTraits<D, KVD>;
+  constexpr int CPL = T::CPL;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int b = blockIdx.x / a.blocks_per_req;
+  const int blk = blockIdx.x % a.blocks_per_req;
+  if (b >= a.batch) return;
+  const int len = a.seq_lens[b];
+  const int n = row_pages(len, a.max_pages);
+  int start = 0, end = n;
+  if (a.first_page) {
+    start = a.first_page[b];
+    if (start < 0) start = 0;
+    end = start + a.span < n ? start + a.span : n;
+  }
+  const int p = start + blk * 4 + wave;
+  if (p >= end) return;
+  const int phys = a.block_table[(size_t)b * a.max_pages + p];
+  if (phys < 0 || phys >= a.num_pool_pages) return;
+  const int valid = valid_in_page(len, p);
+  const int c0 = lane * CPL;
+  for (int h = 0; h < a.num_kv_heads; ++h) {
+    const size_t head_base = ((size_t)phys * a.num_kv_heads + h) * kPage;
+    float lo[CPL], hi[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) { lo[c] = INFINITY; hi[c] = -INFINITY; }
+    for (int t = 0; t < valid; ++t) {
+      float scale = 1.0f;
+      if (KVD == SPD_DTYPE_FP8_E4M3FN) scale = half_bits_to_float(a.k_scale[head_base + t]);
+      float v[CPL];
+      T::load(a.k_pool, (head_base + t) * D + c0, v, scale);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) { lo[c] = fminf(lo[c], v[c]); hi[c] = fmaxf(hi[c], v[c]); }
+    }
+    T::store(a.meta, (((size_t)phys * a.num_kv_heads + h) * 2) * D + c0, lo, hi, D);
+  }
+}
+
+int launch_page_meta_build(const MetaArgs& a, int head_dim, int kv_dtype, hipStream_t stream) {
+  dim3 grid((unsigned)(a.batch * a.blocks_per_req)), block(256);
+#define SPD_META_CASE(D, K)                                                          \
+  if (head_dim == D && kv_dtype == K) {                                              \
+    hipLaunchKernelGGL((page_meta_build_kernel<D, K>), grid, block, 0, stream, a);   \
+    return 0;                                                                        \
+  }
+  SPD_META_CASE(64, SPD_DTYPE_F32)
+  SPD_META_CASE(128, SPD_DTYPE_F32)
+  SPD_META_CASE(64, SPD_DTYPE_F16)
+  SPD_META_CASE(128, SPD_DTYPE_F16)
+  SPD_META_CASE(64, SPD_DTYPE_FP8_E4M3FN)
+  SPD_META_CASE(128, SPD_DTYPE_FP8_E4M3FN)
+#undef SPD_META_CASE
+  return SPD_ERR_UNSUPPORTED;
+}
+
+}  // namespace spd

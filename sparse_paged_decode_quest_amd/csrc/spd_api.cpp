@@ -1,0 +1,391 @@
+// Host side of the C ABI: argument checks, shape / dtype dispatch, grid sizing.  Nothing
+// here allocates, synchronises or reads device memory; every entry point only enqueues
+// kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/spd.h"
+#include "spd_launch.h"
+
+namespace {
+
+constexpr int kScorePagesPerBlock = 128;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_dtype(int v) { return v == SPD_DTYPE_F32 || v == SPD_DTYPE_F16 || v == SPD_DTYPE_FP8_E4M3FN; }
+
+int meta_dtype_of(int kv) { return kv == SPD_DTYPE_F32 ? SPD_DTYPE_F32 : SPD_DTYPE_F16; }
+
+int check_desc(const spd_desc* d) {
+  if (!d) return SPD_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->num_kv_heads < 1 || d->num_kv_heads > SPD_MAX_KV_HEADS || d->num_q_heads < 1 ||
+      d->num_q_heads % d->num_kv_heads != 0 || d->head_dim < 1 || d->page_size < 1 ||
+      d->max_pages_per_seq < 1 || d->num_pool_pages < 1 || d->max_list < 1)
+    return SPD_ERR_INVALID_ARG;
+  if (!is_dtype(d->q_dtype) || !is_dtype(d->kv_dtype) || d->q_dtype == SPD_DTYPE_FP8_E4M3FN)
+    return SPD_ERR_INVALID_ARG;
+  // index arithmetic stays within 64-bit sizes; grids within 2^31 blocks
+  if ((int64_t)d->batch * d->num_kv_heads * d->max_pages_per_seq > ((int64_t)1 << 40)) return SPD_ERR_INVALID_ARG;
+  if (d->page_size != SPD_PAGE_SIZE) return SPD_ERR_UNSUPPORTED;
+  if (d->num_q_heads / d->num_kv_heads != 4) return SPD_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return SPD_ERR_UNSUPPORTED;
+  const bool ok = (d->q_dtype == SPD_DTYPE_F32 && d->kv_dtype == SPD_DTYPE_F32) ||
+                  (d->q_dtype == SPD_DTYPE_F16 && d->kv_dtype == SPD_DTYPE_F16) ||
+                  (d->q_dtype == SPD_DTYPE_F16 && d->kv_dtype == SPD_DTYPE_FP8_E4M3FN && d->head_dim == 128);
+  return ok ? SPD_OK : SPD_ERR_UNSUPPORTED;
+}
+
+int check_sel(const spd_desc* d, const spd_select_params* s) {
+  if (!s) return SPD_ERR_INVALID_ARG;
+  if (s->n_sink < 0 || s->n_local < 0 || s->n_sink_stream < 0 || s->n_local_stream < 0) return SPD_ERR_INVALID_ARG;
+  if (s->mode == SPD_SELECT_TOPK) {
+    if (s->budget_pages < 1) return SPD_ERR_INVALID_ARG;
+  } else if (s->mode == SPD_SELECT_COVERAGE) {
+    if (!(s->gamma > 0.f && s->gamma <= 1.f)) return SPD_ERR_INVALID_ARG;
+    if (!(s->sm_scale > 0.f) || !std::isfinite(s->sm_scale)) return SPD_ERR_INVALID_ARG;
+  } else {
+    return SPD_ERR_INVALID_ARG;
+  }
+  (void)d;
+  return SPD_OK;
+}
+
+// Longest list a row can produce under the rule; max_list must hold it.
+int check_list_capacity(const spd_desc* d, const spd_select_params* s) {
+  const int64_t stream_len = std::min<int64_t>((int64_t)s->n_sink_stream + s->n_local_stream, d->max_pages_per_seq);
+  int64_t dyn_len;
+  if (s->mode == SPD_SELECT_TOPK)
+    dyn_len = std::min<int64_t>(std::max<int64_t>(s->budget_pages, (int64_t)s->n_sink + s->n_local), d->max_pages_per_seq);
+  else
+    dyn_len = d->max_pages_per_seq;
+  return (d->max_list >= dyn_len && d->max_list >= stream_len) ? SPD_OK : SPD_ERR_INVALID_ARG;
+}
+
+int head_lists(const spd_desc* d, const uint8_t* head_kind, spd::HeadList& dyn, spd::HeadList& strm, uint64_t& mask) {
+  if (!head_kind) return SPD_ERR_INVALID_ARG;
+  dyn.count = strm.count = 0;
+  mask = 0;
+  for (int h = 0; h < d->num_kv_heads; ++h) {
+    if (head_kind[h] == SPD_HEAD_DYNAMIC) dyn.head[dyn.count++] = (uint8_t)h;
+    else if (head_kind[h] == SPD_HEAD_STREAMING) { strm.head[strm.count++] = (uint8_t)h; mask |= 1ull << h; }
+    else return SPD_ERR_INVALID_ARG;
+  }
+  return SPD_OK;
+}
+
+int plan_j(const spd_desc* d, const spd_plan_params* p, int32_t& J) {
+  if (!p || p->min_chunk < 1 || p->min_blocks_per_row < 1 || p->min_grid_blocks < 0) return SPD_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)d->batch * d->num_kv_heads;
+  int64_t j = p->min_blocks_per_row;
+  if (rows > 0) j = std::max<int64_t>(j, (p->min_grid_blocks + rows - 1) / rows);
+  if (j > (1 << 16) || rows * j > ((int64_t)1 << 31) - 1) return SPD_ERR_INVALID_ARG;
+  J = (int32_t)j;
+  return SPD_OK;
+}
+
+int launched(int rc) {
+  if (rc != 0) return rc;
+  return hipGetLastError() == hipSuccess ? SPD_OK : SPD_ERR_LAUNCH;
+}
+
+struct ScoreWs {
+  size_t ell_off, part_off, total;
+};
+
+ScoreWs score_ws(const spd_desc* d) {
+  const int bpr = (d->max_pages_per_seq + kScorePagesPerBlock - 1) / kScorePagesPerBlock;
+  const size_t rows = (size_t)d->batch * d->num_kv_heads;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  ScoreWs w;
+  w.ell_off = 0;
+  w.part_off = align_up(rows * d->max_pages_per_seq * G * sizeof(float));
+  w.total = w.part_off + align_up(rows * bpr * G * 2 * sizeof(float));
+  return w;
+}
+
+struct FusedWs {
+  size_t scores_off, counters_off, total;
+};
+
+FusedWs fused_ws(const spd_desc* d) {
+  const size_t rows = (size_t)d->batch * d->num_kv_heads;
+  FusedWs w;
+  w.scores_off = 0;
+  w.counters_off = align_up(rows * d->max_pages_per_seq * sizeof(float));
+  w.total = w.counters_off + align_up(rows * sizeof(uint32_t));
+  return w;
+}
+
+spd::ScoreArgs score_args(const spd_desc* d, const spd_select_params* s, const void* q, const void* meta,
+                          const int32_t* bt, const int32_t* sl, const spd::HeadList& dyn) {
+  spd::ScoreArgs a{};
+  a.q = q;
+  a.meta = meta;
+  a.block_table = bt;
+  a.seq_lens = sl;
+  a.dyn = dyn;
+  a.batch = d->batch;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.max_pages = d->max_pages_per_seq;
+  a.num_pool_pages = d->num_pool_pages;
+  a.pages_per_block = kScorePagesPerBlock;
+  a.blocks_per_row = (d->max_pages_per_seq + kScorePagesPerBlock - 1) / kScorePagesPerBlock;
+  a.sm_scale = s->sm_scale;
+  return a;
+}
+
+spd::SelectArgs select_args(const spd_desc* d, const spd_select_params* s, const int32_t* sl, int32_t* list,
+                            int32_t* len, float* sel_scores, uint64_t mask) {
+  spd::SelectArgs a{};
+  a.seq_lens = sl;
+  a.page_list = list;
+  a.list_len = len;
+  a.sel_scores = sel_scores;
+  a.streaming_mask = mask;
+  a.batch = d->batch;
+  a.num_kv_heads = d->num_kv_heads;
+  a.max_pages = d->max_pages_per_seq;
+  a.max_list = d->max_list;
+  a.mode = s->mode;
+  a.budget = s->budget_pages;
+  a.gamma_fx = (unsigned long long)std::floor((double)s->gamma * 1099511627776.0);
+  a.n_sink = s->n_sink;
+  a.n_local = s->n_local;
+  a.n_sink_stream = s->n_sink_stream;
+  a.n_local_stream = s->n_local_stream;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spd_abi_version(void) { return SPD_ABI_VERSION; }
+
+const char* spd_error_string(int status) {
+  switch (status) {
+    case SPD_OK: return "ok";
+    case SPD_ERR_INVALID_ARG: return "invalid argument";
+    case SPD_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SPD_ERR_LAUNCH: return "kernel launch failed";
+    case SPD_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int spd_plan_grid(const spd_desc* desc, const spd_plan_params* plan, int32_t* blocks_per_row) {
+  int rc = check_desc(desc);
+  if (rc == SPD_ERR_INVALID_ARG) return rc;
+  if (!blocks_per_row) return SPD_ERR_INVALID_ARG;
+  int32_t J;
+  rc = plan_j(desc, plan, J);
+  if (rc) return rc;
+  *blocks_per_row = J;
+  return SPD_OK;
+}
+
+int spd_plan_chunks(int32_t n_pages, int32_t blocks_per_row, int32_t min_chunk, int32_t* chunk_pages,
+                    int32_t* chunks) {
+  if (!chunk_pages || !chunks || n_pages < 0 || blocks_per_row < 1 || min_chunk < 1) return SPD_ERR_INVALID_ARG;
+  int c, m;
+  spd::plan_chunks(n_pages, blocks_per_row, min_chunk, c, m);
+  *chunk_pages = c;
+  *chunks = m;
+  return SPD_OK;
+}
+
+int spd_partials_size(const spd_desc* desc, const spd_plan_params* plan, size_t* part_o_elems,
+                      size_t* part_lse_elems) {
+  int rc = check_desc(desc);
+  if (rc == SPD_ERR_INVALID_ARG) return rc;
+  if (!part_o_elems || !part_lse_elems) return SPD_ERR_INVALID_ARG;
+  int32_t J;
+  rc = plan_j(desc, plan, J);
+  if (rc) return rc;
+  const size_t slots = (size_t)desc->batch * desc->num_q_heads * J;  // rows * J * G
+  *part_lse_elems = slots;
+  *part_o_elems = slots * desc->head_dim;
+  return SPD_OK;
+}
+
+size_t spd_workspace_bytes(const spd_desc* desc, const spd_select_params* sel, int32_t op) {
+  if (check_desc(desc) == SPD_ERR_INVALID_ARG || check_sel(desc, sel) != SPD_OK) return (size_t)-1;
+  switch (op) {
+    case SPD_OP_PAGE_SCORE: return sel->mode == SPD_SELECT_COVERAGE ? score_ws(desc).total : 0;
+    case SPD_OP_PAGE_SELECT: return 0;
+    case SPD_OP_PAGE_SCORE_SELECT: return fused_ws(desc).total;
+    default: return (size_t)-1;
+  }
+}
+
+int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t* k_scale,
+                        const int32_t* block_table, const int32_t* seq_lens, const int32_t* first_page,
+                        int32_t span_pages, void* page_meta, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (desc->batch == 0) return SPD_OK;
+  if (!k_pool || !block_table || !seq_lens || !page_meta) return SPD_ERR_INVALID_ARG;
+  if (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale) return SPD_ERR_INVALID_ARG;
+  if (first_page && span_pages < 1) return SPD_ERR_INVALID_ARG;
+  spd::MetaArgs a{};
+  a.k_pool = k_pool;
+  a.k_scale = k_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.first_page = first_page;
+  a.meta = page_meta;
+  a.batch = desc->batch;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.max_pages = desc->max_pages_per_seq;
+  a.num_pool_pages = desc->num_pool_pages;
+  const int span = first_page ? std::min(span_pages, desc->max_pages_per_seq) : desc->max_pages_per_seq;
+  a.span = span;
+  a.blocks_per_req = (span + 3) / 4;
+  return launched(spd::launch_page_meta_build(a, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
+}
+
+int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const void* q, const void* page_meta,
+                   const int32_t* block_table, const int32_t* seq_lens, const uint8_t* head_kind, float* scores,
+                   float* head_lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if ((rc = check_sel(desc, sel))) return rc;
+  spd::HeadList dyn, strm;
+  uint64_t mask;
+  if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
+  if (desc->batch == 0 || dyn.count == 0) return SPD_OK;
+  if (!q || !page_meta || !block_table || !seq_lens || !scores) return SPD_ERR_INVALID_ARG;
+  spd::ScoreArgs a = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn);
+  a.scores = scores;
+  const bool coverage = sel->mode == SPD_SELECT_COVERAGE;
+  if (coverage) {
+    if (!head_lse) return SPD_ERR_INVALID_ARG;
+    const ScoreWs w = score_ws(desc);
+    if (!workspace || workspace_bytes < w.total) return SPD_ERR_WORKSPACE;
+    a.ell = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.ell_off);
+    a.partials = reinterpret_cast<float2*>(static_cast<char*>(workspace) + w.part_off);
+    a.head_lse = head_lse;
+  }
+  return launched(spd::launch_page_score(a, desc->head_dim, desc->q_dtype, meta_dtype_of(desc->kv_dtype), coverage,
+                                         (hipStream_t)stream));
+}
+
+int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const float* scores,
+                    const int32_t* seq_lens, const uint8_t* head_kind, int32_t* page_list, int32_t* list_len,
+                    float* sel_scores, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if ((rc = check_sel(desc, sel))) return rc;
+  if ((rc = check_list_capacity(desc, sel))) return rc;
+  spd::HeadList dyn, strm;
+  uint64_t mask;
+  if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
+  if (desc->batch == 0) return SPD_OK;
+  if (!seq_lens || !page_list || !list_len || (dyn.count > 0 && !scores)) return SPD_ERR_INVALID_ARG;
+  spd::SelectArgs a = select_args(desc, sel, seq_lens, page_list, list_len, sel_scores, mask);
+  a.scores = scores;
+  return launched(spd::launch_page_select(a, (hipStream_t)stream));
+}
+
+int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, const void* q, const void* page_meta,
+                          const int32_t* block_table, const int32_t* seq_lens, const uint8_t* head_kind,
+                          int32_t* page_list, int32_t* list_len, float* sel_scores, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if ((rc = check_sel(desc, sel))) return rc;
+  if (sel->mode != SPD_SELECT_TOPK) return SPD_ERR_UNSUPPORTED;
+  if ((rc = check_list_capacity(desc, sel))) return rc;
+  spd::HeadList dyn, strm;
+  uint64_t mask;
+  if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
+  if (desc->batch == 0) return SPD_OK;
+  if (!seq_lens || !page_list || !list_len) return SPD_ERR_INVALID_ARG;
+  if (dyn.count > 0 && (!q || !page_meta || !block_table)) return SPD_ERR_INVALID_ARG;
+  const FusedWs w = fused_ws(desc);
+  if (!workspace || workspace_bytes < w.total) return SPD_ERR_WORKSPACE;
+  spd::FusedArgs f{};
+  f.score = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn);
+  f.score.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.scores_off);
+  f.sel = select_args(desc, sel, seq_lens, page_list, list_len, sel_scores, mask);
+  f.stream_heads = strm;
+  f.counters = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + w.counters_off);
+  return launched(spd::launch_page_score_select(f, desc->head_dim, desc->q_dtype, meta_dtype_of(desc->kv_dtype),
+                                                (hipStream_t)stream));
+}
+
+int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, const void* q, const void* k_pool,
+                            const void* v_pool, const uint16_t* k_scale, const uint16_t* v_scale,
+                            const int32_t* block_table, const int32_t* seq_lens, const int32_t* page_list,
+                            const int32_t* list_len, float sm_scale, float* out, float* out_lse, float* part_o,
+                            float* part_lse, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  int32_t J;
+  if ((rc = plan_j(desc, plan, J))) return rc;
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return SPD_ERR_INVALID_ARG;
+  if (desc->batch == 0) return SPD_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !page_list || !list_len || !out || !out_lse ||
+      !part_o || !part_lse)
+    return SPD_ERR_INVALID_ARG;
+  if (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && (!k_scale || !v_scale)) return SPD_ERR_INVALID_ARG;
+  spd::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.page_list = page_list;
+  a.list_len = list_len;
+  a.out = out;
+  a.out_lse = out_lse;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.batch = desc->batch;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.max_pages = desc->max_pages_per_seq;
+  a.num_pool_pages = desc->num_pool_pages;
+  a.max_list = desc->max_list;
+  a.blocks_per_row = J;
+  a.min_chunk = plan->min_chunk;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  return launched(spd::launch_sparse_paged_decode(a, desc->head_dim, desc->q_dtype, desc->kv_dtype,
+                                                  (hipStream_t)stream));
+}
+
+int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float* part_o, const float* part_lse,
+                  const int32_t* list_len, float* out, float* out_lse, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  int32_t J;
+  if ((rc = plan_j(desc, plan, J))) return rc;
+  if (desc->batch == 0) return SPD_OK;
+  if (!part_o || !part_lse || !list_len || !out || !out_lse) return SPD_ERR_INVALID_ARG;
+  spd::MergeArgs a{};
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.list_len = list_len;
+  a.out = out;
+  a.out_lse = out_lse;
+  a.batch = desc->batch;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.max_list = desc->max_list;
+  a.blocks_per_row = J;
+  a.min_chunk = plan->min_chunk;
+  return launched(spd::launch_lse_merge(a, desc->head_dim, (hipStream_t)stream));
+}
+
+}  // extern "C"

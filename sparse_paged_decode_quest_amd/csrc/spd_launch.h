@@ -1,0 +1,111 @@
+// Kernel argument blocks and launchers (internal to the library; the public surface is
+// include/spd.h).  Launchers return 0 or SPD_ERR_UNSUPPORTED and only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spd.h"
+
+namespace spd {
+
+struct MetaArgs {
+  const void* k_pool;
+  const uint16_t* k_scale;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* first_page;
+  void* meta;
+  int batch, num_kv_heads, max_pages, num_pool_pages;
+  int span;            // pages after first_page (when first_page is set)
+  int blocks_per_req;  // workgroups per request (4 pages each)
+};
+int launch_page_meta_build(const MetaArgs& a, int head_dim, int kv_dtype, hipStream_t stream);
+
+// KV heads of one kind, listed in ascending order (dynamic heads for the scorer).
+struct HeadList {
+  uint8_t head[SPD_MAX_KV_HEADS];
+  int count;
+};
+
+struct ScoreArgs {
+  const void* q;
+  const void* meta;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* scores;       // [B, Hkv, max_pages]
+  float* ell;          // coverage: [B, Hkv, max_pages, G] log-masses
+  float2* partials;    // coverage: [B, Hkv, blocks_per_row, G] (max, sum of exp)
+  float* head_lse;     // coverage: [B, Hq]
+  HeadList dyn;
+  int batch, num_q_heads, num_kv_heads, max_pages, num_pool_pages;
+  int blocks_per_row;  // workgroups per (request, dynamic head)
+  int pages_per_block;
+  float sm_scale;
+};
+int launch_page_score(const ScoreArgs& a, int head_dim, int q_dtype, int meta_dtype, bool coverage,
+                      hipStream_t stream);
+
+struct SelectArgs {
+  const float* scores;      // [B, Hkv, max_pages] (fused: workspace copy)
+  const int32_t* seq_lens;
+  int32_t* page_list;       // [B, Hkv, max_list]
+  int32_t* list_len;        // [B, Hkv]
+  float* sel_scores;        // nullable
+  uint64_t streaming_mask;  // bit h set: KV head h is a streaming head
+  int batch, num_kv_heads, max_pages, max_list;
+  int mode, budget;
+  unsigned long long gamma_fx;  // gamma in 2^-40 fixed point
+  int n_sink, n_local, n_sink_stream, n_local_stream;
+};
+int launch_page_select(const SelectArgs& a, hipStream_t stream);
+
+struct FusedArgs {
+  ScoreArgs score;         // score.scores -> workspace rows [B, Hkv, max_pages]
+  SelectArgs sel;          // sel.scores unused (the rows above are selected)
+  HeadList stream_heads;   // streaming heads: one extra block per (request, head)
+  unsigned int* counters;  // [B, Hkv] finished-block tickets (workspace, zero between calls)
+};
+int launch_page_score_select(const FusedArgs& a, int head_dim, int q_dtype, int meta_dtype,
+                             hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const uint16_t* k_scale;
+  const uint16_t* v_scale;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* page_list;
+  const int32_t* list_len;
+  float* out;
+  float* out_lse;
+  float* part_o;
+  float* part_lse;
+  int batch, num_q_heads, num_kv_heads, max_pages, num_pool_pages, max_list;
+  int blocks_per_row, min_chunk;
+  float sm_scale_log2;  // softmax scale times log2(e)
+};
+int launch_sparse_paged_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype,
+                               hipStream_t stream);
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* list_len;
+  float* out;
+  float* out_lse;
+  int batch, num_q_heads, num_kv_heads, max_list, blocks_per_row, min_chunk;
+};
+int launch_lse_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+
+// Moira Eq. 4: chunk size and count of a row of n listed pages.
+__host__ __device__ inline void plan_chunks(int n, int J, int C, int& c, int& m) {
+  if (n <= 0) { c = 0; m = 0; return; }
+  int per = (n + J - 1) / J;
+  c = per > C ? per : C;
+  m = (n + c - 1) / c;
+}
+
+}  // namespace spd

@@ -1,0 +1,160 @@
+"""Device buffers and the call sequence of one decode step (marshalling only).
+
+Every arithmetic step runs in the HIP library: this module allocates torch tensors for
+inputs, intermediates and outputs, fills the C descriptors, and calls the entry points of
+``include/spd.h`` in the method's order --
+
+    page_meta_build (tail page) -> page_score -> page_select -> sparse_paged_decode -> lse_merge
+
+(or page_score_select in place of the middle two) -- on one stream, so the whole step can
+be captured into one hipGraph and replayed.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+from . import _abi as A
+from .workloads import Inputs, Workload
+
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "fp8": torch.uint8}
+
+
+@dataclasses.dataclass
+class Plan:
+    """Self-planned split constants (Moira, section 3.3, Eq. 4), re-chosen for 16-token pages
+    and 256 compute units: a chunk of at least 4 pages (one per wave of a block) and at least
+    512 blocks over the grid."""
+    min_chunk: int = 4
+    min_blocks_per_row: int = 16
+    min_grid_blocks: int = 512
+
+    def params(self) -> A.PlanParams:
+        return A.PlanParams(self.min_chunk, self.min_blocks_per_row, self.min_grid_blocks)
+
+
+@dataclasses.dataclass
+class DeviceInputs:
+    q: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    k_scale: torch.Tensor | None
+    v_scale: torch.Tensor | None
+    block_table: torch.Tensor
+    seq_lens: torch.Tensor
+    head_kind: np.ndarray      # host
+    page_meta: torch.Tensor    # [Npool, Hkv, 2, d]
+
+    @property
+    def num_pool_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+
+def upload(inp: Inputs, device="cuda") -> DeviceInputs:
+    """Copy one step's stored inputs to the device and allocate the page-meta buffer."""
+    w = inp.workload
+
+    def t(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+    k_scale = None if inp.k_scale is None else t(inp.k_scale.view(np.int16))
+    v_scale = None if inp.v_scale is None else t(inp.v_scale.view(np.int16))
+    mdt = torch.float32 if w.kv_dtype == "f32" else torch.float16
+    meta = torch.zeros((inp.num_pool_pages, w.num_kv_heads, 2, w.head_dim), dtype=mdt, device=device)
+    return DeviceInputs(q=t(inp.q), k_pool=t(inp.k_pool), v_pool=t(inp.v_pool), k_scale=k_scale, v_scale=v_scale,
+                        block_table=t(inp.block_table), seq_lens=t(inp.seq_lens), head_kind=inp.head_kind.copy(),
+                        page_meta=meta)
+
+
+def make_desc(w: Workload, num_pool_pages: int) -> A.Desc:
+    return A.Desc(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                  page_size=16, max_pages_per_seq=w.pages_per_seq, num_pool_pages=num_pool_pages,
+                  max_list=w.list_capacity, q_dtype=A.DTYPE[w.q_dtype], kv_dtype=A.DTYPE[w.kv_dtype])
+
+
+def make_select(w: Workload) -> A.SelectParams:
+    return A.SelectParams(mode=A.SELECT_COVERAGE if w.mode == "coverage" else A.SELECT_TOPK,
+                          budget_pages=max(1, w.budget_pages), gamma=float(w.gamma) if w.gamma else 1.0,
+                          sm_scale=w.sm_scale, n_sink=w.n_sink, n_local=w.n_local,
+                          n_sink_stream=w.n_sink_stream, n_local_stream=w.n_local_stream)
+
+
+def build_meta(w: Workload, d: DeviceInputs, stream=None) -> None:
+    """Bulk page statistics of every page in the block tables (done once, at prefill)."""
+    desc = make_desc(w, d.num_pool_pages)
+    A.spd_page_meta_build(desc, d.k_pool, d.k_scale, d.block_table, d.seq_lens, None, 0, d.page_meta, stream)
+
+
+class DecodeStep:
+    """Buffers for one decode step of workload ``w`` over device inputs ``d``."""
+
+    def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, fused: bool | None = None,
+                 tail_refresh: bool = True):
+        self.w, self.d = w, d
+        self.plan = plan or Plan()
+        self.fused = w.fused_select if fused is None else fused
+        self.tail_refresh = tail_refresh
+        dev = d.q.device
+        self.desc = make_desc(w, d.num_pool_pages)
+        self.sel = make_select(w)
+        self.pp = self.plan.params()
+        B, Hq, Hkv, D = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.scores = torch.zeros((B, Hkv, w.pages_per_seq), **f32)
+        self.head_lse = torch.zeros((B, Hq), **f32)
+        self.page_list = torch.zeros((B, Hkv, w.list_capacity), **i32)
+        self.list_len = torch.zeros((B, Hkv), **i32)
+        self.sel_scores = torch.zeros((B, Hkv, w.list_capacity), **f32)
+        self.out = torch.zeros((B, Hq, D), **f32)
+        self.out_lse = torch.zeros((B, Hq), **f32)
+        self.J = A.spd_plan_grid(self.desc, self.pp)
+        n_po, n_pl = A.spd_partials_size(self.desc, self.pp)
+        self.part_o = torch.zeros(max(1, n_po), **f32)
+        self.part_lse = torch.zeros(max(1, n_pl), **f32)
+        op = A.OP_PAGE_SCORE_SELECT if self.fused else A.OP_PAGE_SCORE
+        self.ws_bytes = A.spd_workspace_bytes(self.desc, self.sel, op)
+        self.workspace = torch.zeros(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+        n_b = (np.asarray(w.seq_lens, dtype=np.int64) + 15) // 16
+        self.first_page = torch.from_numpy(np.maximum(n_b - 1, 0).astype(np.int32)).to(dev)
+
+    def refresh_tail(self, stream=None):
+        """page_meta_build of the page the newest token is in (one page per request)."""
+        d = self.d
+        A.spd_page_meta_build(self.desc, d.k_pool, d.k_scale, d.block_table, d.seq_lens, self.first_page, 1,
+                              d.page_meta, stream)
+
+    def select(self, stream=None):
+        d = self.d
+        if self.fused:
+            A.spd_page_score_select(self.desc, self.sel, d.q, d.page_meta, d.block_table, d.seq_lens, d.head_kind,
+                                    self.page_list, self.list_len, self.sel_scores, self.workspace, self.ws_bytes,
+                                    stream)
+        else:
+            A.spd_page_score(self.desc, self.sel, d.q, d.page_meta, d.block_table, d.seq_lens, d.head_kind,
+                             self.scores, self.head_lse, self.workspace, self.ws_bytes, stream)
+            A.spd_page_select(self.desc, self.sel, self.scores, d.seq_lens, d.head_kind, self.page_list,
+                              self.list_len, self.sel_scores, None, 0, stream)
+
+    def attend(self, stream=None):
+        d = self.d
+        A.spd_sparse_paged_decode(self.desc, self.pp, d.q, d.k_pool, d.v_pool, d.k_scale, d.v_scale, d.block_table,
+                                  d.seq_lens, self.page_list, self.list_len, self.w.sm_scale, self.out,
+                                  self.out_lse, self.part_o, self.part_lse, stream)
+        A.spd_lse_merge(self.desc, self.pp, self.part_o, self.part_lse, self.list_len, self.out, self.out_lse,
+                        stream)
+
+    def run(self, stream=None):
+        if self.tail_refresh:
+            self.refresh_tail(stream)
+        self.select(stream)
+        self.attend(stream)
+
+    def lists(self) -> dict:
+        """Host copy of the page lists: {(b, h): [pages]}."""
+        pl = self.page_list.cpu().numpy()
+        ll = self.list_len.cpu().numpy()
+        return {(b, h): pl[b, h, :ll[b, h]].tolist() for b in range(self.w.batch)
+                for h in range(self.w.num_kv_heads)}

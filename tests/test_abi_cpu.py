@@ -1,0 +1,190 @@
+"""The C ABI without a GPU: exports, host-side validation and the planning helpers.
+
+Every call here returns before anything is launched, so no device is needed (the stream
+argument is passed as 0 so that torch never initialises HIP).
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_paged_decode_quest_amd import _abi as A
+from sparse_paged_decode_quest_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return A.lib()
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "spd.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spd_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(A.EXPORTS)
+    assert A.abi_version() == 1
+
+
+def test_error_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert A.error_string(code) not in ("", "unknown status")
+    assert A.error_string(-99) == "unknown status"
+
+
+def desc_for(w, **over):
+    d = dict(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+             page_size=16, max_pages_per_seq=w.pages_per_seq, num_pool_pages=1000, max_list=w.list_capacity,
+             q_dtype=A.DTYPE[w.q_dtype], kv_dtype=A.DTYPE[w.kv_dtype])
+    d.update(over)
+    return A.Desc(**d)
+
+
+def sel_for(w, **over):
+    s = dict(mode=A.SELECT_COVERAGE if w.mode == "coverage" else A.SELECT_TOPK, budget_pages=w.budget_pages or 1,
+             gamma=w.gamma or 1.0, sm_scale=w.sm_scale, n_sink=w.n_sink, n_local=w.n_local,
+             n_sink_stream=w.n_sink_stream, n_local_stream=w.n_local_stream)
+    s.update(over)
+    return A.SelectParams(**s)
+
+
+FAKE = 0x1000  # never dereferenced: every case below fails validation first
+
+
+def score_rc(desc, sel, heads=None, ws=FAKE, ws_bytes=1 << 30, lse=FAKE):
+    heads = heads if heads is not None else [0] * max(1, desc.num_kv_heads)
+    arr = (ctypes.c_uint8 * len(heads))(*heads)
+    return A.lib().spd_page_score(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, arr, FAKE, lse,
+                                  ws, ws_bytes, 0)
+
+
+def select_rc(desc, sel, heads=None):
+    heads = heads if heads is not None else [0] * max(1, desc.num_kv_heads)
+    arr = (ctypes.c_uint8 * len(heads))(*heads)
+    return A.lib().spd_page_select(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, arr, FAKE, FAKE, None, None,
+                                   0, 0)
+
+
+def decode_rc(desc, plan, sm_scale=0.1, **null):
+    ptrs = {k: FAKE for k in ("q", "k", "v", "ks", "vs", "bt", "sl", "pl", "ll", "o", "lse", "po", "pls")}
+    ptrs.update(null)
+    return A.lib().spd_sparse_paged_decode(
+        ctypes.byref(desc), ctypes.byref(plan), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["ks"], ptrs["vs"], ptrs["bt"],
+        ptrs["sl"], ptrs["pl"], ptrs["ll"], ctypes.c_float(sm_scale), ptrs["o"], ptrs["lse"], ptrs["po"], ptrs["pls"],
+        0)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(num_q_heads=9), A.SPD_ERR_INVALID_ARG),          # Hq % Hkv != 0
+    (dict(num_kv_heads=0), A.SPD_ERR_INVALID_ARG),
+    (dict(num_kv_heads=65, num_q_heads=260), A.SPD_ERR_INVALID_ARG),
+    (dict(batch=-1), A.SPD_ERR_INVALID_ARG),
+    (dict(max_pages_per_seq=0), A.SPD_ERR_INVALID_ARG),
+    (dict(q_dtype=7), A.SPD_ERR_INVALID_ARG),
+    (dict(q_dtype=2), A.SPD_ERR_INVALID_ARG),               # fp8 queries are not an input format
+    (dict(head_dim=96), A.SPD_ERR_UNSUPPORTED),
+    (dict(page_size=32), A.SPD_ERR_UNSUPPORTED),
+    (dict(num_q_heads=16), A.SPD_ERR_UNSUPPORTED),          # G = 8
+    (dict(q_dtype=0, kv_dtype=1), A.SPD_ERR_UNSUPPORTED),   # f32 q with f16 pool
+    (dict(head_dim=64, kv_dtype=2), A.SPD_ERR_UNSUPPORTED),  # fp8 compiled for d = 128 only
+])
+def test_descriptor_validation(lib, over, code):
+    w = W.small()
+    assert score_rc(desc_for(w, **over), sel_for(w)) == code
+    assert decode_rc(desc_for(w, **over), A.PlanParams(4, 16, 512)) == code
+
+
+def test_select_param_validation(lib):
+    w = W.small()
+    d = desc_for(w)
+    assert score_rc(d, sel_for(w, budget_pages=0)) == A.SPD_ERR_INVALID_ARG
+    assert score_rc(d, sel_for(w, mode=5)) == A.SPD_ERR_INVALID_ARG
+    assert score_rc(d, sel_for(w, n_sink=-1)) == A.SPD_ERR_INVALID_ARG
+    for g in (0.0, -0.5, 1.5, float("nan")):
+        assert score_rc(d, sel_for(w, mode=A.SELECT_COVERAGE, gamma=g)) == A.SPD_ERR_INVALID_ARG
+    assert score_rc(d, sel_for(w, mode=A.SELECT_COVERAGE, sm_scale=0.0)) == A.SPD_ERR_INVALID_ARG
+    assert score_rc(d, sel_for(w), heads=[0, 2]) == A.SPD_ERR_INVALID_ARG      # unknown head kind
+
+
+def test_list_capacity_and_workspace_checks(lib):
+    w = W.small(budget=24)
+    assert select_rc(desc_for(w, max_list=23), sel_for(w)) == A.SPD_ERR_INVALID_ARG
+    assert select_rc(desc_for(w, max_list=4), sel_for(w, n_sink_stream=3, n_local_stream=3), heads=[1, 1]) \
+        == A.SPD_ERR_INVALID_ARG
+    wc = W.small(mode="coverage")
+    assert select_rc(desc_for(wc, max_list=wc.pages_per_seq - 1), sel_for(wc)) == A.SPD_ERR_INVALID_ARG
+    need = A.spd_workspace_bytes(desc_for(wc), sel_for(wc), A.OP_PAGE_SCORE)
+    assert need > 0
+    assert score_rc(desc_for(wc), sel_for(wc), ws=FAKE, ws_bytes=need - 1) == A.SPD_ERR_WORKSPACE
+    assert score_rc(desc_for(wc), sel_for(wc), ws=None, ws_bytes=need) == A.SPD_ERR_WORKSPACE
+    assert score_rc(desc_for(wc), sel_for(wc), lse=None) == A.SPD_ERR_INVALID_ARG
+    assert A.spd_workspace_bytes(desc_for(w), sel_for(w), A.OP_PAGE_SCORE) == 0
+    assert A.spd_workspace_bytes(desc_for(w), sel_for(w), A.OP_PAGE_SELECT) == 0
+    assert A.spd_workspace_bytes(desc_for(w), sel_for(w), A.OP_PAGE_SCORE_SELECT) >= 4 * w.batch * 2 * w.pages_per_seq
+    with pytest.raises(A.SpdError):
+        A.spd_workspace_bytes(desc_for(w), sel_for(w), 9)
+
+
+def test_decode_argument_checks(lib):
+    w = W.small()
+    d = desc_for(w)
+    plan = A.PlanParams(4, 16, 512)
+    assert decode_rc(d, A.PlanParams(0, 16, 512)) == A.SPD_ERR_INVALID_ARG
+    assert decode_rc(d, A.PlanParams(4, 0, 512)) == A.SPD_ERR_INVALID_ARG
+    assert decode_rc(d, plan, sm_scale=0.0) == A.SPD_ERR_INVALID_ARG
+    assert decode_rc(d, plan, sm_scale=float("inf")) == A.SPD_ERR_INVALID_ARG
+    assert decode_rc(d, plan, q=None) == A.SPD_ERR_INVALID_ARG
+    assert decode_rc(d, plan, pls=None) == A.SPD_ERR_INVALID_ARG
+    wf = W.small(kv="fp8")
+    assert decode_rc(desc_for(wf), plan, ks=None) == A.SPD_ERR_INVALID_ARG
+
+
+def test_empty_batch_launches_nothing(lib):
+    w = W.small()
+    d = desc_for(w, batch=0)
+    assert score_rc(d, sel_for(w)) == A.SPD_OK
+    assert select_rc(d, sel_for(w)) == A.SPD_OK
+    assert decode_rc(d, A.PlanParams(4, 16, 512)) == A.SPD_OK
+
+
+def test_self_planning_worked_example(lib, golden_dir):
+    with open(os.path.join(golden_dir, "self_planning_example.json")) as f:
+        g = json.load(f)
+    used = 0
+    for n, c_want, m_want in zip(g["rows"], g["chunk_pages"], g["blocks_used"]):
+        c, m = A.spd_plan_chunks(n, g["J"], g["C"])
+        assert (c, m) == (c_want, m_want)
+        used += m
+    assert g["J"] * len(g["rows"]) - used == g["blocks_idle"]
+    assert A.spd_plan_chunks(0, 4, 2) == (0, 0)
+
+
+def test_plan_grid_formula(lib):
+    w = W.small()
+    for B, Hkv, C, NJ, NT in [(1, 8, 4, 32, 4096), (4, 8, 24, 32, 4096), (8, 8, 4, 16, 512), (1, 2, 1, 1, 0)]:
+        d = desc_for(w, batch=B, num_kv_heads=Hkv, num_q_heads=4 * Hkv)
+        J = A.spd_plan_grid(d, A.PlanParams(C, NJ, NT))
+        assert J == max(NJ, -(-NT // (B * Hkv)))
+        po, pl = A.spd_partials_size(d, A.PlanParams(C, NJ, NT))
+        assert pl == B * Hkv * J * 4 and po == pl * w.head_dim
+    # chunk sizes: every chunk holds at least C pages, at most J chunks, all pages covered once
+    rng = np.random.default_rng(0)
+    for _ in range(500):
+        n, J, C = int(rng.integers(0, 5000)), int(rng.integers(1, 100)), int(rng.integers(1, 40))
+        c, m = A.spd_plan_chunks(n, J, C)
+        if n == 0:
+            assert (c, m) == (0, 0)
+            continue
+        assert c >= C and m <= J and (m - 1) * c < n <= m * c

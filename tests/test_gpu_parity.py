@@ -1,0 +1,243 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs (needs a gfx950 GPU).
+
+Small ragged workloads are compared element by element; the full-size workloads are
+compared on sampled pages and rows in the launch configuration the benchmark uses.  The
+comparison rules and tolerances are in tests/parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import spd_oracle as O
+from sparse_paged_decode_quest_amd import _abi as A
+from sparse_paged_decode_quest_amd import step as S
+from sparse_paged_decode_quest_amd import workloads as W
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible gfx950 device"
+    A.lib()  # raises when libspd.so is not built: there is no fallback
+    yield
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_case(w, plan=None, fused=None, tail=False):
+    """Generate, upload, bulk-meta, one step.  Returns (inputs, device inputs, step)."""
+    say(f"[case] {w.name} seq={w.seq_lens[:8]} kv={w.kv_dtype} mode={w.mode} seed={w.seed}")
+    inp = W.generate(w)
+    d = S.upload(inp)
+    S.build_meta(w, d)
+    st = S.DecodeStep(w, d, plan=plan, fused=fused, tail_refresh=tail)
+    st.run()
+    torch.cuda.synchronize()
+    return inp, d, st
+
+
+SMALL = {
+    "f32_d64": W.small("f32_d64", kv="f32", q="f32", d=64, seq_lens=(700, 37, 2050, 16, 17), budget=20),
+    "f16_d128": W.small("f16_d128", seq_lens=(700, 37, 2050, 1, 33, 4000), budget=24, Hkv=3, Hq=12,
+                        streaming=(1,)),
+    "f16_d64": W.small("f16_d64", d=64, seq_lens=(513, 300, 2), budget=9, n_local=3),
+    "fp8_d128": W.small("fp8_d128", kv="fp8", seq_lens=(1500, 250, 31), budget=16),
+    "cov_f16": W.small("cov_f16", mode="coverage", gamma=0.9, n_local=1, seq_lens=(1200, 333, 64),
+                       planted=("fixed", 6), delta=("nats", 6.0)),
+    "cov_f32": W.small("cov_f32", kv="f32", q="f32", d=64, mode="coverage", gamma=0.95, n_local=1,
+                       seq_lens=(900, 77), streaming=(0,)),
+}
+
+
+def oracle_row(inp, meta, b, h):
+    """Oracle scores, list and score scale of dynamic row (b, h)."""
+    w = inp.workload
+    n = O.n_pages(inp.seq_lens[b])
+    S_ = O.row_bounds(inp, meta, b, h)
+    forced = O.forced_pages(n, w.n_sink, w.n_local)
+    if w.mode == "topk":
+        sc = O.topk_scores(S_)
+        return sc, O.select_topk(sc, n, w.budget_pages, forced), forced, None
+    pi, lse = O.coverage_shares(S_, int(inp.seq_lens[b]), w.sm_scale) if n else (np.zeros(0), None)
+    return pi, (O.select_coverage(pi, n, w.gamma, forced) if n else []), forced, lse
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_meta_scores_lists_attention(name):
+    w = SMALL[name]
+    inp, d, st = run_case(w)
+    meta_ref = O.page_meta_build(inp)
+    meta_gpu = d.page_meta.cpu().numpy()
+    used = np.unique(np.concatenate([inp.block_table[b, :O.n_pages(L)] for b, L in enumerate(w.seq_lens)]))
+    assert np.array_equal(meta_gpu[used], meta_ref[used]), "page meta differs"
+
+    scores = st.scores.cpu().numpy()
+    lists = st.lists()
+    head_lse = st.head_lse.cpu().numpy()
+    oracle_lists = {}
+    for b in range(w.batch):
+        n = O.n_pages(inp.seq_lens[b])
+        for h in range(w.num_kv_heads):
+            if inp.head_kind[h]:
+                oracle_lists[(b, h)] = O.forced_pages(n, w.n_sink_stream, w.n_local_stream)
+                assert lists[(b, h)] == oracle_lists[(b, h)], (b, h)
+                continue
+            ref, lst, forced, lse = oracle_row(inp, meta_ref, b, h)
+            oracle_lists[(b, h)] = lst
+            if w.mode == "topk":
+                scale = P.bound_scale(inp, meta_ref, b, h)
+                P.check_topk_scores(scores[b, h, :n], ref, scale)
+                P.check_topk_list(lists[(b, h)], ref, n, w.budget_pages, forced, scale)
+            else:
+                P.check_coverage_shares(scores[b, h, :n], ref)
+                if n:
+                    G = w.group
+                    assert np.allclose(head_lse[b, h * G:(h + 1) * G], lse, rtol=0, atol=1e-4 * np.abs(lse).max())
+                P.check_coverage_list(lists[(b, h)], ref, n, w.gamma, forced)
+
+    # attention over the GPU's own lists where they equal the oracle's
+    o_ref, lse_ref = O.sparse_paged_decode(inp, oracle_lists, w.sm_scale)
+    out, out_lse = st.out.cpu().numpy(), st.out_lse.cpu().numpy()
+    G = w.group
+    for (b, h), lst in oracle_lists.items():
+        if lists[(b, h)] == lst:
+            sl = slice(h * G, (h + 1) * G)
+            P.check_attention(out[b, sl], out_lse[b, sl], o_ref[b, sl], lse_ref[b, sl], w.kv_dtype, f"row {b},{h}")
+
+    # decode alone, fed the oracle's lists
+    pl = torch.zeros_like(st.page_list)
+    ll = torch.zeros_like(st.list_len)
+    for (b, h), lst in oracle_lists.items():
+        pl[b, h, :len(lst)] = torch.tensor(lst, dtype=torch.int32)
+        ll[b, h] = len(lst)
+    st.page_list.copy_(pl)
+    st.list_len.copy_(ll)
+    st.attend()
+    torch.cuda.synchronize()
+    P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), o_ref, lse_ref, w.kv_dtype, "oracle lists")
+
+
+@pytest.mark.parametrize("plan", [S.Plan(1, 1, 0), S.Plan(2, 3, 0), S.Plan(4, 16, 512), S.Plan(24, 32, 4096),
+                                  S.Plan(1000, 1, 0)])
+def test_plan_invariance(plan):
+    w = SMALL["f16_d128"].replace(budget_pages=60)
+    inp, d, st = run_case(w, plan=plan)
+    lists = st.lists()
+    o_ref, lse_ref = O.sparse_paged_decode(inp, lists_from_oracle(inp), w.sm_scale)
+    # decode over oracle lists under this plan
+    set_lists(st, lists_from_oracle(inp))
+    st.attend()
+    torch.cuda.synchronize()
+    P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), o_ref, lse_ref, w.kv_dtype, str(plan))
+
+
+def lists_from_oracle(inp):
+    return O.page_select(inp, O.page_meta_build(inp))["lists"]
+
+
+def set_lists(st, lists):
+    pl = torch.zeros_like(st.page_list)
+    ll = torch.zeros_like(st.list_len)
+    for (b, h), lst in lists.items():
+        pl[b, h, :len(lst)] = torch.tensor(lst, dtype=torch.int32)
+        ll[b, h] = len(lst)
+    st.page_list.copy_(pl)
+    st.list_len.copy_(ll)
+
+
+def test_edge_cases_empty_tiny_and_degenerate_rows():
+    # lengths 0, 1, 15, 16, 17; budget larger than rows; forced pages overlapping
+    w = W.small("edges", seq_lens=(0, 1, 15, 16, 17, 48, 49, 160), budget=3, n_sink=2, n_local=2,
+                streaming=(1,), n_sink_stream=3, n_local_stream=3, Hkv=2, Hq=8, hole=0.5)
+    inp, d, st = run_case(w)
+    ref = O.decode_step(inp)
+    assert st.lists() == ref["lists"]
+    out, lse = st.out.cpu().numpy(), st.out_lse.cpu().numpy()
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))  # empty request
+    P.check_attention(out, lse, ref["O"], ref["out_lse"], w.kv_dtype, "edges")
+
+
+def test_tail_refresh_updates_only_last_pages():
+    w = W.small("tail", seq_lens=(333, 48, 1), budget=10)
+    inp = W.generate(w)
+    d = S.upload(inp)
+    st = S.DecodeStep(w, d, tail_refresh=True)
+    sentinel = 3.0
+    d.page_meta.fill_(sentinel)
+    st.refresh_tail()
+    torch.cuda.synchronize()
+    got = d.page_meta.cpu().numpy()
+    first = [max(O.n_pages(L) - 1, 0) for L in w.seq_lens]
+    ref = O.page_meta_build(inp, meta=np.full(got.shape, sentinel, dtype=got.dtype), first_page=first)
+    assert np.array_equal(got, ref)
+
+
+def test_fused_select_equals_unfused():
+    w = W.small("fused", seq_lens=(3000, 700, 37, 0), budget=40, streaming=(1,), Hkv=2, Hq=8)
+    inp, d, st = run_case(w, fused=False)
+    lists_unfused = st.lists()
+    st2 = S.DecodeStep(w, d, fused=True, tail_refresh=False)
+    for rep in range(3):  # counters must return to zero between calls
+        st2.run()
+        torch.cuda.synchronize()
+        assert st2.lists() == lists_unfused, rep
+        assert torch.equal(st2.out, st.out) and torch.equal(st2.out_lse, st.out_lse)
+    rows = w.batch * w.num_kv_heads
+    counters_off = -(-rows * w.pages_per_seq * 4 // 256) * 256
+    assert int(st2.workspace[counters_off:counters_off + 4 * rows].sum()) == 0  # tickets back at zero
+
+
+def test_deterministic_bitwise():
+    w = SMALL["cov_f16"]
+    inp, d, st = run_case(w)
+    a = [t.clone() for t in (st.scores, st.page_list, st.list_len, st.out, st.out_lse)]
+    st.run()
+    torch.cuda.synchronize()
+    b = [st.scores, st.page_list, st.list_len, st.out, st.out_lse]
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_graph_replay_equals_eager_and_follows_new_inputs():
+    w = W.small("graph", seq_lens=(2500, 900, 60), budget=32, streaming=(0,), Hkv=2, Hq=8)
+    inp, d, st = run_case(w, tail=True)
+    eager = [t.clone() for t in (st.page_list, st.list_len, st.out, st.out_lse)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        st.run()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(eager, (st.page_list, st.list_len, st.out, st.out_lse)):
+            assert torch.equal(x, y), rep
+    # new queries in the same buffer: the graph must select and attend for them
+    rng = np.random.default_rng(99)
+    q2 = rng.standard_normal(inp.q.shape).astype(np.float16)
+    d.q.copy_(torch.from_numpy(q2))
+    g.replay()
+    torch.cuda.synchronize()
+    graph_out = [t.clone() for t in (st.page_list, st.list_len, st.out, st.out_lse)]
+    st.run()
+    torch.cuda.synchronize()
+    for x, y in zip(graph_out, (st.page_list, st.list_len, st.out, st.out_lse)):
+        assert torch.equal(x, y)
+    inp.q = q2
+    ref = O.decode_step(inp)
+    lists = st.lists()
+    for key, lst in ref["lists"].items():
+        if lists[key] == lst:
+            b, h = key
+            sl = slice(h * 4, (h + 1) * 4)
+            P.check_attention(st.out.cpu().numpy()[b, sl], st.out_lse.cpu().numpy()[b, sl], ref["O"][b, sl],
+                              ref["out_lse"][b, sl], w.kv_dtype, str(key))

@@ -1,0 +1,115 @@
+"""The named full-size workloads on the GPU, in the launch configuration the benchmark
+uses, checked against the fp64 oracle on sampled pages and rows (needs a gfx950 GPU)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import spd_oracle as O
+from sparse_paged_decode_quest_amd import _abi as A
+from sparse_paged_decode_quest_amd import step as S
+from sparse_paged_decode_quest_amd import workloads as W
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("name", list(W.NAMED))
+def test_named_workload(name):
+    assert torch.cuda.is_available()
+    A.lib()
+    w = W.named(name)
+    say(f"[workload] {name} B={w.batch} seq={w.seq_lens} kv={w.kv_dtype} mode={w.mode} fused={w.fused_select}")
+    inp = W.generate(w)
+    d = S.upload(inp)
+    S.build_meta(w, d)
+    st = S.DecodeStep(w, d)  # bench configuration: default plan, the workload's fused flag, tail refresh
+    st.run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+
+    # 1. page meta on sampled pages (all heads), exact
+    meta_gpu = d.page_meta.cpu().numpy()
+    for b in range(w.batch):
+        n = O.n_pages(inp.seq_lens[b])
+        pages = sorted(set(rng.choice(n, size=min(n, 24), replace=False).tolist()) | {n - 1})
+        for p in pages:
+            phys = int(inp.block_table[b, p])
+            valid = O.valid_tokens(inp.seq_lens[b], p)
+            for h in range(w.num_kv_heads):
+                sc = None if inp.k_scale is None else inp.k_scale[phys, h]
+                lo, hi = O.to_stored_meta(*O.page_key_minmax(O.stored_values(inp.k_pool[phys, h], sc, w.kv_dtype),
+                                                             valid), w.kv_dtype)
+                assert np.array_equal(meta_gpu[phys, h, 0], lo) and np.array_equal(meta_gpu[phys, h, 1], hi), \
+                    (b, p, h)
+
+    # 2. sampled rows: scores, lists, attention
+    dyn = [h for h in range(w.num_kv_heads) if not inp.head_kind[h]]
+    strm = [h for h in range(w.num_kv_heads) if inp.head_kind[h]]
+    rows = [(int(rng.integers(w.batch)), h) for h in rng.choice(dyn, size=min(2, len(dyn)), replace=False)]
+    if w.batch > 1:
+        rows.append((int(np.argmax(w.seq_lens)), dyn[0]))
+    rows += [(0, strm[0])] if strm else []
+    gpu_lists = st.lists()
+    if st.fused:
+        rows_n = w.batch * w.num_kv_heads
+        gpu_scores = st.workspace[:rows_n * w.pages_per_seq * 4].view(torch.float32).view(
+            w.batch, w.num_kv_heads, w.pages_per_seq).cpu().numpy()
+    else:
+        gpu_scores = st.scores.cpu().numpy()
+    oracle_lists = {}
+    for b, h in rows:
+        n = O.n_pages(inp.seq_lens[b])
+        say(f"  row b={b} h={h} n={n} kind={'streaming' if inp.head_kind[h] else 'dynamic'} "
+            f"gpu_len={len(gpu_lists[(b, h)])}")
+        if inp.head_kind[h]:
+            oracle_lists[(b, h)] = O.forced_pages(n, w.n_sink_stream, w.n_local_stream)
+            assert gpu_lists[(b, h)] == oracle_lists[(b, h)]
+            continue
+        meta_ref = O.page_meta_build(inp, heads=[h], requests=[b])
+        S_ = O.row_bounds(inp, meta_ref, b, h)
+        forced = O.forced_pages(n, w.n_sink, w.n_local)
+        if w.mode == "topk":
+            ref = O.topk_scores(S_)
+            scale = P.bound_scale(inp, meta_ref, b, h)
+            P.check_topk_scores(gpu_scores[b, h, :n], ref, scale)
+            P.check_topk_list(gpu_lists[(b, h)], ref, n, w.budget_pages, forced, scale)
+            oracle_lists[(b, h)] = O.select_topk(ref, n, w.budget_pages, forced)
+        else:
+            pi, _ = O.coverage_shares(S_, int(inp.seq_lens[b]), w.sm_scale)
+            P.check_coverage_shares(gpu_scores[b, h, :n], pi)
+            P.check_coverage_list(gpu_lists[(b, h)], pi, n, w.gamma, forced)
+            oracle_lists[(b, h)] = O.select_coverage(pi, n, w.gamma, forced)
+        say(f"    oracle_len={len(oracle_lists[(b, h)])} same={gpu_lists[(b, h)] == oracle_lists[(b, h)]}")
+
+    o_ref, lse_ref = O.sparse_paged_decode(inp, oracle_lists, w.sm_scale)
+    out, out_lse = st.out.cpu().numpy(), st.out_lse.cpu().numpy()
+    G = w.group
+    for (b, h), lst in oracle_lists.items():
+        sl = slice(h * G, (h + 1) * G)
+        if gpu_lists[(b, h)] == lst:
+            P.check_attention(out[b, sl], out_lse[b, sl], o_ref[b, sl], lse_ref[b, sl], w.kv_dtype, f"step {b},{h}")
+
+    # 3. decode fed the oracle's lists on the sampled rows (the GPU's lists elsewhere)
+    pl = st.page_list.clone()
+    ll = st.list_len.clone()
+    for (b, h), lst in oracle_lists.items():
+        pl[b, h, :len(lst)] = torch.tensor(lst, dtype=torch.int32)
+        ll[b, h] = len(lst)
+    st.page_list.copy_(pl)
+    st.list_len.copy_(ll)
+    st.attend()
+    torch.cuda.synchronize()
+    out, out_lse = st.out.cpu().numpy(), st.out_lse.cpu().numpy()
+    for (b, h) in oracle_lists:
+        sl = slice(h * G, (h + 1) * G)
+        P.check_attention(out[b, sl], out_lse[b, sl], o_ref[b, sl], lse_ref[b, sl], w.kv_dtype, f"lists {b},{h}")
+
+    if w.mode == "coverage":
+        lens = st.list_len.cpu().numpy().ravel()
+        say(f"  coverage list lengths: min {lens.min()} median {int(np.median(lens))} max {lens.max()} "
+            f"hist {np.histogram(lens, bins=[0, 20, 50, 100, 200, 500, 1000, 2000, 4000, 8193])[0].tolist()}")
