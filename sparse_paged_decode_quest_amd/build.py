@@ -24,7 +24,7 @@ SOURCES = ["spd_api.cpp", "page_meta_build.hip", "page_score.hip", "page_select.
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
+         "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas", "-Rpass-analysis=kernel-resource-usage"]
 
 
 def hipcc() -> str:

@@ -2,9 +2,9 @@
 // logical page keeps k_min and k_max over its keys; "Key statistics storage and updating":
 // the statistics of the page a new token lands in are refreshed as the token is appended).
 //
-// One wave per (request, logical page); the wave walks the KV heads.  Lane l owns channels
-// [l*CPL, (l+1)*CPL) of every token, so min / max over the page's valid tokens is
-// lane-local: no cross-lane traffic, 16 coalesced row loads per head.
+// One wave per (request, logical page, KV head).  Lane l owns channels [l*CPL, (l+1)*CPL)
+// of every token, so min / max over the page's valid tokens is lane-local: no cross-lane
+// traffic, and the page's 16 token rows are 16 coalesced loads issued back to back.
 #include "spd_device.h"
 #include "spd_launch.h"
 
@@ -69,8 +69,10 @@ __global__ __launch_bounds__(256) void page_meta_build_kernel(MetaArgs a) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int b = blockIdx.x / a.blocks_per_req;
-  const int blk = blockIdx.x % a.blocks_per_req;
+  const int item = (blockIdx.x % a.blocks_per_req) * 4 + wave;  // (page offset, head) pair
   if (b >= a.batch) return;
+  const int p_off = item / a.num_kv_heads;
+  const int h = item % a.num_kv_heads;
   const int len = a.seq_lens[b];
   const int n = row_pages(len, a.max_pages);
   int start = 0, end = n;
@@ -79,27 +81,34 @@ __global__ __launch_bounds__(256) void page_meta_build_kernel(MetaArgs a) {
     if (start < 0) start = 0;
     end = start + a.span < n ? start + a.span : n;
   }
-  const int p = start + blk * 4 + wave;
+  const int p = start + p_off;
   if (p >= end) return;
   const int phys = a.block_table[(size_t)b * a.max_pages + p];
   if (phys < 0 || phys >= a.num_pool_pages) return;
   const int valid = valid_in_page(len, p);
   const int c0 = lane * CPL;
-  for (int h = 0; h < a.num_kv_heads; ++h) {
-    const size_t head_base = ((size_t)phys * a.num_kv_heads + h) * kPage;
-    float lo[CPL], hi[CPL];
+  const size_t head_base = ((size_t)phys * a.num_kv_heads + h) * kPage;
+  // every token of the page is loaded at once (slots past `valid` are read but never used)
+  float v[kPage][CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) { lo[c] = INFINITY; hi[c] = -INFINITY; }
-    for (int t = 0; t < valid; ++t) {
-      float scale = 1.0f;
-      if (KVD == SPD_DTYPE_FP8_E4M3FN) scale = half_bits_to_float(a.k_scale[head_base + t]);
-      float v[CPL];
-      T::load(a.k_pool, (head_base + t) * D + c0, v, scale);
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) { lo[c] = fminf(lo[c], v[c]); hi[c] = fmaxf(hi[c], v[c]); }
-    }
-    T::store(a.meta, (((size_t)phys * a.num_kv_heads + h) * 2) * D + c0, lo, hi, D);
+  for (int t = 0; t < kPage; ++t) {
+    float scale = 1.0f;
+    if (KVD == SPD_DTYPE_FP8_E4M3FN) scale = half_bits_to_float(a.k_scale[head_base + t]);
+    T::load(a.k_pool, (head_base + t) * D + c0, v[t], scale);
   }
+  float lo[CPL], hi[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) { lo[c] = INFINITY; hi[c] = -INFINITY; }
+#pragma unroll
+  for (int t = 0; t < kPage; ++t) {
+    const bool ok = t < valid;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      lo[c] = ok ? fminf(lo[c], v[t][c]) : lo[c];
+      hi[c] = ok ? fmaxf(hi[c], v[t][c]) : hi[c];
+    }
+  }
+  T::store(a.meta, (((size_t)phys * a.num_kv_heads + h) * 2) * D + c0, lo, hi, D);
 }
 
 int launch_page_meta_build(const MetaArgs& a, int head_dim, int kv_dtype, hipStream_t stream) {

@@ -20,7 +20,7 @@
 namespace spd {
 
 template <int D, int QD, int MD>
-__global__ __launch_bounds__(256) void page_score_topk_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreWaves * kWave) void page_score_topk_kernel(ScoreArgs a) {
   const int row_dyn = blockIdx.x / a.blocks_per_row;
   const int blk = blockIdx.x % a.blocks_per_row;
   const int b = row_dyn / a.dyn.count;
@@ -28,20 +28,16 @@ __global__ __launch_bounds__(256) void page_score_topk_kernel(ScoreArgs a) {
   const int n = row_pages(a.seq_lens[b], a.max_pages);
   const int p_begin = blk * a.pages_per_block;
   const int p_end = min(n, p_begin + a.pages_per_block);
-  score_block_topk<D, QD, MD>(a, b, h, p_begin, p_end,
+  score_block_topk<D, QD, MD, kScoreWaves, kScoreIters>(a, b, h, p_begin, p_end,
                               a.scores + ((size_t)b * a.num_kv_heads + h) * a.max_pages);
 }
 
 // Coverage, first pass: log-masses l_{g,p} and one (max, sum exp) pair per head and block.
 template <int D, int QD, int MD>
-__global__ __launch_bounds__(256) void page_score_coverage_kernel(ScoreArgs a) {
-  using T = ScoreTraits<D, QD, MD>;
-  constexpr int LPP = T::LPP;
-  constexpr int PPI = kWave / LPP;  // pages per wave iteration
+__global__ __launch_bounds__(kScoreWaves * kWave) void page_score_coverage_kernel(ScoreArgs a) {
+  constexpr int LPP = ScoreTraits<D, QD, MD>::LPP;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int sub = lane % LPP;
-  const int slot = lane / LPP;
   const int row_dyn = blockIdx.x / a.blocks_per_row;
   const int blk = blockIdx.x % a.blocks_per_row;
   const int b = row_dyn / a.dyn.count;
@@ -56,38 +52,20 @@ __global__ __launch_bounds__(256) void page_score_coverage_kernel(ScoreArgs a) {
   float lm[kG], ls[kG];  // running (max, sum exp) of this lane's pages
 #pragma unroll
   for (int g = 0; g < kG; ++g) { lm[g] = -INFINITY; ls[g] = 0.f; }
-  typename T::Q qr;
-  const int c0 = sub * T::CW;
-  T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0);
-  for (int base = p_begin + wave * PPI; base < p_end; base += 4 * PPI) {
-    const int p = base + slot;
-    float s[kG];
-    bool ok = false;
-    if (p < p_end) {
-      const int phys = a.block_table[(size_t)b * a.max_pages + p];
-      ok = phys >= 0 && phys < a.num_pool_pages;
-      if (ok) T::bound(qr, a.meta, ((size_t)phys * a.num_kv_heads + h) * 2 * D, c0, s);
-    }
-    if (!ok) {
+  score_block<D, QD, MD, kScoreWaves, kScoreIters>(a, b, h, p_begin, p_end, [&](int p, bool ok, const float (&s)[kG]) {
+    if (p >= p_end) return;
+    const int valid = valid_in_page(len, p);
+    const float lv = valid == kPage ? 2.772588722239781f : logf((float)valid);  // ln(valid)
+    float lg[kG];
 #pragma unroll
-      for (int g = 0; g < kG; ++g) s[g] = 0.f;
+    for (int g = 0; g < kG; ++g) {
+      lg[g] = ok ? fmaf(a.sm_scale, s[g], lv) : -INFINITY;
+      lse_push(lm[g], ls[g], lg[g]);
     }
-#pragma unroll
-    for (int g = 0; g < kG; ++g) s[g] = xor_sum<LPP>(s[g]);
-    if (sub == 0 && p < p_end) {
-      const int valid = valid_in_page(len, p);
-      const float lv = valid == kPage ? 2.772588722239781f : logf((float)valid);  // ln(valid)
-      float lg[kG];
-#pragma unroll
-      for (int g = 0; g < kG; ++g) {
-        lg[g] = ok ? fmaf(a.sm_scale, s[g], lv) : -INFINITY;
-        lse_push(lm[g], ls[g], lg[g]);
-      }
-      *reinterpret_cast<float4*>(a.ell + (row * a.max_pages + p) * kG) = make_float4(lg[0], lg[1], lg[2], lg[3]);
-    }
-  }
+    *reinterpret_cast<float4*>(a.ell + (row * a.max_pages + p) * kG) = make_float4(lg[0], lg[1], lg[2], lg[3]);
+  });
   // block partial: fold the lanes that own pages (sub == 0), then the four waves in order
-  __shared__ float sm[4][kG], ss[4][kG];
+  __shared__ float sm[kScoreWaves][kG], ss[kScoreWaves][kG];
 #pragma unroll
   for (int g = 0; g < kG; ++g) {
     for (int o = LPP; o < kWave; o <<= 1) {
@@ -100,13 +78,13 @@ __global__ __launch_bounds__(256) void page_score_coverage_kernel(ScoreArgs a) {
   if (threadIdx.x < kG) {
     const int g = threadIdx.x;
     float m = sm[0][g], s = ss[0][g];
-    for (int w = 1; w < 4; ++w) lse_combine(m, s, sm[w][g], ss[w][g]);
+    for (int w = 1; w < kScoreWaves; ++w) lse_combine(m, s, sm[w][g], ss[w][g]);
     a.partials[(row * a.blocks_per_row + blk) * kG + g] = make_float2(m, s);
   }
 }
 
 // Coverage, second pass: per-head log-sum-exp of the row, then the group-mean share.
-__global__ __launch_bounds__(256) void coverage_share_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreWaves * kWave) void coverage_share_kernel(ScoreArgs a) {
   const int row_dyn = blockIdx.x / a.blocks_per_row;
   const int blk = blockIdx.x % a.blocks_per_row;
   const int b = row_dyn / a.dyn.count;
@@ -158,7 +136,7 @@ __global__ __launch_bounds__(256) void coverage_share_kernel(ScoreArgs a) {
 
 int launch_page_score(const ScoreArgs& a, int head_dim, int q_dtype, int meta_dtype, bool coverage,
                       hipStream_t stream) {
-  dim3 grid((unsigned)(a.batch * a.dyn.count * a.blocks_per_row)), block(256);
+  dim3 grid((unsigned)(a.batch * a.dyn.count * a.blocks_per_row)), block(kScoreWaves * kWave);
 #define SPD_SCORE_CASE(D, QD, MD)                                                              \
   if (head_dim == D && q_dtype == QD && meta_dtype == MD) {                                    \
     if (coverage) {                                                                            \

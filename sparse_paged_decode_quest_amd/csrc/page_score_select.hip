@@ -12,8 +12,10 @@
 
 namespace spd {
 
-template <int D, int QD, int MD>
-__global__ __launch_bounds__(256) void page_score_select_kernel(FusedArgs f) {
+static_assert(kFusedWaves * kWave == kSelThreads, "the fused block selects with kSelThreads threads");
+
+template <int D, int QD, int MD, int KPT>
+__global__ __launch_bounds__(kSelThreads) void page_score_select_kernel(FusedArgs f) {
   __shared__ SelectSmem sm;
   __shared__ int last;
   const ScoreArgs& a = f.score;
@@ -23,7 +25,7 @@ __global__ __launch_bounds__(256) void page_score_select_kernel(FusedArgs f) {
     const int b = k / f.stream_heads.count;
     const int h = f.stream_heads.head[k % f.stream_heads.count];
     const size_t row = (size_t)b * a.num_kv_heads + h;
-    select_row(f.sel, nullptr, row_pages(a.seq_lens[b], a.max_pages), row, true, sm);
+    select_streaming_row(f.sel, row_pages(a.seq_lens[b], a.max_pages), row);
     return;
   }
   const int row_dyn = blockIdx.x / a.blocks_per_row;
@@ -41,24 +43,28 @@ __global__ __launch_bounds__(256) void page_score_select_kernel(FusedArgs f) {
   const int p_begin = blk * a.pages_per_block;
   const int p_end = min(n, p_begin + a.pages_per_block);
   float* row_scores = a.scores + row * a.max_pages;
-  score_block_topk<D, QD, MD>(a, b, h, p_begin, p_end, row_scores);
+  score_block_topk<D, QD, MD, kFusedWaves, kFusedIters>(a, b, h, p_begin, p_end, row_scores);
   __threadfence();  // release this block's scores device-wide
   __syncthreads();
   if (threadIdx.x == 0) last = atomicAdd(&f.counters[row], 1u) == (unsigned)(used - 1);
   __syncthreads();
   if (!last) return;
   __threadfence();  // acquire the other blocks' scores
-  select_row(f.sel, row_scores, n, row, false, sm);
+  select_dynamic_row<KPT, false>(f.sel, row_scores, n, row, sm);
   if (threadIdx.x == 0) f.counters[row] = 0u;
 }
 
 int launch_page_score_select(const FusedArgs& f, int head_dim, int q_dtype, int meta_dtype, hipStream_t stream) {
   const int blocks = f.score.batch * (f.score.dyn.count * f.score.blocks_per_row + f.stream_heads.count);
-  dim3 grid((unsigned)blocks), block(256);
-#define SPD_FUSED_CASE(D, QD, MD)                                                                 \
-  if (head_dim == D && q_dtype == QD && meta_dtype == MD) {                                       \
-    hipLaunchKernelGGL((page_score_select_kernel<D, QD, MD>), grid, block, 0, stream, f);         \
-    return 0;                                                                                     \
+  dim3 grid((unsigned)blocks), block(kSelThreads);
+#define SPD_FUSED_CASE(D, QD, MD)                                                                  \
+  if (head_dim == D && q_dtype == QD && meta_dtype == MD) {                                        \
+    switch (select_kpt(f.score.max_pages)) {                                                       \
+      case 8: hipLaunchKernelGGL((page_score_select_kernel<D, QD, MD, 8>), grid, block, 0, stream, f); break;     \
+      case 32: hipLaunchKernelGGL((page_score_select_kernel<D, QD, MD, 32>), grid, block, 0, stream, f); break;   \
+      default: hipLaunchKernelGGL((page_score_select_kernel<D, QD, MD, 0>), grid, block, 0, stream, f); break;    \
+    }                                                                                              \
+    return 0;                                                                                      \
   }
   SPD_FUSED_CASE(64, SPD_DTYPE_F16, SPD_DTYPE_F16)
   SPD_FUSED_CASE(128, SPD_DTYPE_F16, SPD_DTYPE_F16)

@@ -262,11 +262,8 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) acc[g][cc] = 0.f;
 
-  int i = i0 + wave;
-  PageRef cur = i < i1 ? resolve_page(a, list, i, b, n_b, len) : PageRef{-1, 0, 0};
-  typename T::KF kf;
-  typename T::VF vf;
-  float ks = 1.f, vs = 1.f;
+  // Pages of this wave alternate between two register stages, so the next page's K / V
+  // loads are in flight while the current page is computed.
   auto load = [&](const PageRef& r, typename T::KF& kd, typename T::VF& vd, float& ksd, float& vsd) {
     if (r.page < 0) return;
     const size_t head_page = (size_t)r.phys * a.num_kv_heads + h;
@@ -277,52 +274,43 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
       vsd = half_bits_to_float(a.v_scale[head_page * kPage + tok]) * 256.f;
     }
   };
-  load(cur, kf, vf, ks, vs);
-
-  while (i < i1) {
-    const int inext = i + 4;
-    PageRef nxt = inext < i1 ? resolve_page(a, list, inext, b, n_b, len) : PageRef{-1, 0, 0};
-    typename T::KF kn;
-    typename T::VF vn;
-    float ksn = 1.f, vsn = 1.f;
-    load(nxt, kn, vn, ksn, vsn);
-
-    if (cur.page >= 0) {
-      // logits: partial dots over this lane's channel quarter, reduce-scattered over the quad
-      float part[kGq];
-      T::dots(q, kf, part);
-      const int b0 = quarter & 1, b1 = quarter >> 1;
-      const float send0 = b0 ? part[0] : part[1];
-      const float send1 = b0 ? part[2] : part[3];
-      const float keep0 = b0 ? part[1] : part[0];
-      const float keep1 = b0 ? part[3] : part[2];
-      const float hA = keep0 + __shfl_xor(send0, 1, kWave);  // head b0
-      const float hB = keep1 + __shfl_xor(send1, 1, kWave);  // head 2 + b0
-      const float keep2 = b1 ? hB : hA;
-      const float send2 = b1 ? hA : hB;
-      const float dot = keep2 + __shfl_xor(send2, 2, kWave);  // head `quarter`, token `tok`
-      float x = dot * a.sm_scale_log2 * ks;
-      if (tok >= cur.valid) x = -INFINITY;
-      float mx = x;
+  auto process = [&](const PageRef& r, const typename T::KF& kf, const typename T::VF& vf, float ks, float vs) {
+    if (r.page < 0) return;
+    // logits: partial dots over this lane's channel quarter, reduce-scattered over the quad
+    float part[kGq];
+    T::dots(q, kf, part);
+    const int b0 = quarter & 1, b1 = quarter >> 1;
+    const float send0 = b0 ? part[0] : part[1];
+    const float send1 = b0 ? part[2] : part[3];
+    const float keep0 = b0 ? part[1] : part[0];
+    const float keep1 = b0 ? part[3] : part[2];
+    const float hA = keep0 + __shfl_xor(send0, 1, kWave);  // head b0
+    const float hB = keep1 + __shfl_xor(send1, 1, kWave);  // head 2 + b0
+    const float keep2 = b1 ? hB : hA;
+    const float send2 = b1 ? hA : hB;
+    const float dot = keep2 + __shfl_xor(send2, 2, kWave);  // head `quarter`, token `tok`
+    float x = dot * a.sm_scale_log2 * ks;
+    if (tok >= r.valid) x = -INFINITY;
+    float mx = x;
 #pragma unroll
-      for (int o = 4; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-      const float p = m_new == -INFINITY ? 0.f : exp2f(x - m_new);
-      l_run = l_run * alpha + p;
-      m_run = m_new;
-      p_lds[wave][tok][quarter] = p * vs;
-      if (lane < kGq) alpha_lds[wave][lane] = alpha;
-      wave_fence();
-      const float4 al = *reinterpret_cast<const float4*>(alpha_lds[wave]);
-      const float alv[kGq] = {al.x, al.y, al.z, al.w};
+    for (int o = 4; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    const float p = m_new == -INFINITY ? 0.f : exp2f(x - m_new);
+    l_run = l_run * alpha + p;
+    m_run = m_new;
+    p_lds[wave][tok][quarter] = p * vs;
+    if (lane < kGq) alpha_lds[wave][lane] = alpha;
+    wave_fence();
+    const float4 al = *reinterpret_cast<const float4*>(alpha_lds[wave]);
+    const float alv[kGq] = {al.x, al.y, al.z, al.w};
 #pragma unroll
-      for (int g = 0; g < kGq; ++g)
+    for (int g = 0; g < kGq; ++g)
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) acc[g][cc] *= alv[g];
+      for (int cc = 0; cc < CPL; ++cc) acc[g][cc] *= alv[g];
 #pragma unroll
-      for (int t = 0; t < kPage; ++t) {
-        if (t >= cur.valid) break;  // invalid slots may hold NaN: never touch them
+    for (int t = 0; t < kPage; ++t) {
+      if (t < r.valid) {  // invalid slots may hold NaN: never touch them
         const float4 pt = *reinterpret_cast<const float4*>(p_lds[wave][t]);
         const float pv[kGq] = {pt.x, pt.y, pt.z, pt.w};
         float v[CPL];
@@ -332,14 +320,27 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
 #pragma unroll
           for (int cc = 0; cc < CPL; ++cc) acc[g][cc] = fmaf(pv[g], v[cc], acc[g][cc]);
       }
-      wave_fence();
     }
-    cur = nxt;
-    kf = kn;
-    vf = vn;
-    ks = ksn;
-    vs = vsn;
-    i = inext;
+    wave_fence();
+  };
+
+  const PageRef none{-1, 0, 0};
+  typename T::KF ka, kb;
+  typename T::VF va, vb;
+  float ksa = 1.f, vsa = 1.f, ksb = 1.f, vsb = 1.f;
+  int i = i0 + wave;
+  PageRef ra = i < i1 ? resolve_page(a, list, i, b, n_b, len) : none;
+  load(ra, ka, va, ksa, vsa);
+  while (i < i1) {
+    const PageRef rb = i + 4 < i1 ? resolve_page(a, list, i + 4, b, n_b, len) : none;
+    load(rb, kb, vb, ksb, vsb);
+    process(ra, ka, va, ksa, vsa);
+    i += 4;
+    if (i >= i1) break;
+    ra = i + 4 < i1 ? resolve_page(a, list, i + 4, b, n_b, len) : none;
+    load(ra, ka, va, ksa, vsa);
+    process(rb, kb, vb, ksb, vsb);
+    i += 4;
   }
 
   // wave state -> LDS
@@ -385,10 +386,21 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
 }
 
 // Exact merge of a row's chunk states (PersistentKV, section 3.3; states are stored
-// normalised: o_j = a_j / l_j and lse_j = m_j + ln l_j).
+// normalised: o_j = a_j / l_j and lse_j = m_j + ln l_j).  One 1024-thread block per (row,
+// query head): chunk weights exp(lse_j - lse) go through LDS, then D channels x (1024 / D)
+// chunk partitions accumulate in parallel (every partial load of a thread is independent)
+// and the partitions are summed in a fixed order.
+constexpr int kMergeThreads = 1024;
+constexpr int kMaxChunks = 1024;
+
 template <int D>
-__global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
-  const int row = blockIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
+  constexpr int PARTS = kMergeThreads / D;
+  __shared__ float w_s[kMaxChunks];
+  __shared__ float red[kMergeThreads / kWave];
+  __shared__ float part_s[PARTS][D];
+  const int row = blockIdx.x / kGq;
+  const int g = blockIdx.x % kGq;
   const int b = row / a.num_kv_heads;
   const int h = row % a.num_kv_heads;
   int n = a.list_len[row];
@@ -396,26 +408,52 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
   int c, m;
   plan_chunks(n, a.blocks_per_row, a.min_chunk, c, m);
   if (m <= 1) return;
-  const size_t qrow = (size_t)b * a.num_q_heads + (size_t)h * kGq;
-  for (int e = threadIdx.x; e < kGq * D; e += blockDim.x) {
-    const int g = e / D, ch = e % D;
-    const size_t slot0 = (size_t)row * a.blocks_per_row * kGq + g;
-    float M = -INFINITY;
-    for (int j = 0; j < m; ++j) M = fmaxf(M, a.part_lse[slot0 + (size_t)j * kGq]);
-    float o = 0.f, lse = -INFINITY;
-    if (M != -INFINITY) {
-      float S = 0.f, A = 0.f;
-      for (int j = 0; j < m; ++j) {
-        const size_t slot = slot0 + (size_t)j * kGq;
-        const float w = expf(a.part_lse[slot] - M);
-        S += w;
-        A = fmaf(w, a.part_o[slot * D + ch], A);
-      }
-      o = A / S;
-      lse = M + logf(S);
-    }
-    a.out[(qrow + g) * D + ch] = o;
-    if (ch == 0) a.out_lse[qrow + g] = lse;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const size_t slot0 = (size_t)row * a.blocks_per_row * kGq + g;  // + j * kGq
+
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j < m; j += kMergeThreads) {
+    const float l = a.part_lse[slot0 + (size_t)j * kGq];
+    w_s[j] = l;
+    mx = fmaxf(mx, l);
+  }
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float M = red[0];
+  for (int w = 1; w < kMergeThreads / kWave; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  const size_t qrow = (size_t)b * a.num_q_heads + (size_t)h * kGq + g;
+  if (M == -INFINITY) {
+    for (int ch = threadIdx.x; ch < D; ch += kMergeThreads) a.out[qrow * D + ch] = 0.f;
+    if (threadIdx.x == 0) a.out_lse[qrow] = -INFINITY;
+    return;
+  }
+  float sum = 0.f;
+  for (int j = threadIdx.x; j < m; j += kMergeThreads) {
+    const float wj = expf(w_s[j] - M);
+    w_s[j] = wj;
+    sum += wj;
+  }
+  sum = xor_sum<kWave>(sum);
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  float S = 0.f;
+  for (int w = 0; w < kMergeThreads / kWave; ++w) S += red[w];
+
+  const int ch = threadIdx.x % D, part = threadIdx.x / D;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int j = part; j < m; j += PARTS) acc = fmaf(w_s[j], a.part_o[(slot0 + (size_t)j * kGq) * D + ch], acc);
+  part_s[part][ch] = acc;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float o = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < PARTS; ++pp) o += part_s[pp][threadIdx.x];
+    a.out[qrow * D + threadIdx.x] = o / S;
+    if (threadIdx.x == 0) a.out_lse[qrow] = M + logf(S);
   }
 }
 
@@ -436,7 +474,7 @@ int launch_sparse_paged_decode(const DecodeArgs& a, int head_dim, int q_dtype, i
 }
 
 int launch_lse_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
-  dim3 grid((unsigned)(a.batch * a.num_kv_heads)), block(256);
+  dim3 grid((unsigned)(a.batch * a.num_kv_heads * kGq)), block(kMergeThreads);
   if (head_dim == 64) hipLaunchKernelGGL(lse_merge_kernel<64>, grid, block, 0, stream, a);
   else if (head_dim == 128) hipLaunchKernelGGL(lse_merge_kernel<128>, grid, block, 0, stream, a);
   else return SPD_ERR_UNSUPPORTED;

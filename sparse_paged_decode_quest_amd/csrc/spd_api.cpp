@@ -9,11 +9,17 @@
 #include <cstring>
 
 #include "../../include/spd.h"
+#include "score_common.h"
 #include "spd_launch.h"
 
 namespace {
 
-constexpr int kScorePagesPerBlock = 128;
+// pages per scoring workgroup (fixed by the compiled work layouts)
+int score_ppb(const spd_desc* d, bool fused = false) {
+  const int mb = d->kv_dtype == SPD_DTYPE_F32 ? 4 : 2;
+  return fused ? spd::score_pages_per_block(d->head_dim, mb, spd::kFusedWaves, spd::kFusedIters)
+               : spd::score_pages_per_block(d->head_dim, mb, spd::kScoreWaves, spd::kScoreIters);
+}
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -84,7 +90,7 @@ int plan_j(const spd_desc* d, const spd_plan_params* p, int32_t& J) {
   const int64_t rows = (int64_t)d->batch * d->num_kv_heads;
   int64_t j = p->min_blocks_per_row;
   if (rows > 0) j = std::max<int64_t>(j, (p->min_grid_blocks + rows - 1) / rows);
-  if (j > (1 << 16) || rows * j > ((int64_t)1 << 31) - 1) return SPD_ERR_INVALID_ARG;
+  if (j > 1024 || rows * j > ((int64_t)1 << 31) - 1) return SPD_ERR_INVALID_ARG;  // merge holds <= 1024 chunks
   J = (int32_t)j;
   return SPD_OK;
 }
@@ -99,7 +105,7 @@ struct ScoreWs {
 };
 
 ScoreWs score_ws(const spd_desc* d) {
-  const int bpr = (d->max_pages_per_seq + kScorePagesPerBlock - 1) / kScorePagesPerBlock;
+  const int bpr = (d->max_pages_per_seq + score_ppb(d) - 1) / score_ppb(d);
   const size_t rows = (size_t)d->batch * d->num_kv_heads;
   const int G = d->num_q_heads / d->num_kv_heads;
   ScoreWs w;
@@ -123,7 +129,7 @@ FusedWs fused_ws(const spd_desc* d) {
 }
 
 spd::ScoreArgs score_args(const spd_desc* d, const spd_select_params* s, const void* q, const void* meta,
-                          const int32_t* bt, const int32_t* sl, const spd::HeadList& dyn) {
+                          const int32_t* bt, const int32_t* sl, const spd::HeadList& dyn, bool fused = false) {
   spd::ScoreArgs a{};
   a.q = q;
   a.meta = meta;
@@ -135,8 +141,8 @@ spd::ScoreArgs score_args(const spd_desc* d, const spd_select_params* s, const v
   a.num_kv_heads = d->num_kv_heads;
   a.max_pages = d->max_pages_per_seq;
   a.num_pool_pages = d->num_pool_pages;
-  a.pages_per_block = kScorePagesPerBlock;
-  a.blocks_per_row = (d->max_pages_per_seq + kScorePagesPerBlock - 1) / kScorePagesPerBlock;
+  a.pages_per_block = score_ppb(d, fused);
+  a.blocks_per_row = (d->max_pages_per_seq + a.pages_per_block - 1) / a.pages_per_block;
   a.sm_scale = s->sm_scale;
   return a;
 }
@@ -247,7 +253,7 @@ int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t
   a.num_pool_pages = desc->num_pool_pages;
   const int span = first_page ? std::min(span_pages, desc->max_pages_per_seq) : desc->max_pages_per_seq;
   a.span = span;
-  a.blocks_per_req = (span + 3) / 4;
+  a.blocks_per_req = (span * desc->num_kv_heads + 3) / 4;
   return launched(spd::launch_page_meta_build(a, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
 }
 
@@ -314,7 +320,7 @@ int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, co
   const FusedWs w = fused_ws(desc);
   if (!workspace || workspace_bytes < w.total) return SPD_ERR_WORKSPACE;
   spd::FusedArgs f{};
-  f.score = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn);
+  f.score = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, true);
   f.score.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.scores_off);
   f.sel = select_args(desc, sel, seq_lens, page_list, list_len, sel_scores, mask);
   f.stream_heads = strm;

@@ -18,7 +18,7 @@ struct MetaArgs {
   void* meta;
   int batch, num_kv_heads, max_pages, num_pool_pages;
   int span;            // pages after first_page (when first_page is set)
-  int blocks_per_req;  // workgroups per request (4 pages each)
+  int blocks_per_req;  // workgroups per request (4 (page, head) items each)
 };
 int launch_page_meta_build(const MetaArgs& a, int head_dim, int kv_dtype, hipStream_t stream);
 
