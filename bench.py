@@ -100,7 +100,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the decode step is a single-GPU "
-                                   "kernel pipeline with no collectives (see DESIGN.md for how it would shard)"}))
+                                   "kernel pipeline with no collectives; more GPUs would each run it on their own requests or KV heads"}))
         sys.exit(2)
 
     import torch

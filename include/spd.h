@@ -168,8 +168,7 @@ int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t
  * TOPK: scores[b,h,p] = max over the G query heads of the row of S_{g,p} (LServe page
  * importance, computed from page_meta).  COVERAGE: l_{g,p} = sm_scale * S_{g,p} +
  * ln(valid tokens of p); head_lse[b, h*G+g] = logsumexp_p l_{g,p}; scores[b,h,p] =
- * (1/G) sum_g exp(l_{g,p} - head_lse) (Moira's group-mean share, Algorithm 1 line "group
- * mean").  head_lse (device, [B, Hq]) may be NULL in TOPK mode.  workspace (device) of
+ * (1/G) sum_g exp(l_{g,p} - head_lse) (Moira's group-mean share, section 3.2, Eq. 3).  head_lse (device, [B, Hq]) may be NULL in TOPK mode.  workspace (device) of
  * spd_workspace_bytes(desc, sel, SPD_OP_PAGE_SCORE) bytes (0 in TOPK mode). */
 int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const void* q,
                    const void* page_meta, const int32_t* block_table, const int32_t* seq_lens,

@@ -21,7 +21,7 @@ Pages and their definitions:
   * PersistentKV (section 3.1, Eq. 1): exact decode attention over the kept
     tokens; section 3.3: split states and their exact merge.
 
-Readings where the pages leave a step open (every one is listed in the design doc):
+Readings where the pages leave a step open:
   * GQA combine for top-K: score_p = max over the group's query heads of S_{g,p}.
   * Coverage log-mass from the bound: l_{g,p} = s * S_{g,p} + ln(valid_p), s = 1/sqrt(d);
     every page, sink and current included, is estimated the same way.
