@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 1
+#define SPD_ABI_VERSION 2
 #define SPD_PAGE_SIZE 16
 #define SPD_MAX_KV_HEADS 64
 
@@ -168,7 +168,8 @@ int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t
  * TOPK: scores[b,h,p] = max over the G query heads of the row of S_{g,p} (LServe page
  * importance, computed from page_meta).  COVERAGE: l_{g,p} = sm_scale * S_{g,p} +
  * ln(valid tokens of p); head_lse[b, h*G+g] = logsumexp_p l_{g,p}; scores[b,h,p] =
- * (1/G) sum_g exp(l_{g,p} - head_lse) (Moira's group-mean share, section 3.2, Eq. 3).  head_lse (device, [B, Hq]) may be NULL in TOPK mode.  workspace (device) of
+ * (1/G) sum_g exp(l_{g,p} - head_lse) (Moira's group-mean share, section 3.2, Eq. 3).
+ * head_lse (device, [B, Hq]) may be NULL in TOPK mode.  workspace (device) of
  * spd_workspace_bytes(desc, sel, SPD_OP_PAGE_SCORE) bytes (0 in TOPK mode). */
 int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const void* q,
                    const void* page_meta, const int32_t* block_table, const int32_t* seq_lens,
@@ -176,39 +177,52 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
                    size_t workspace_bytes, void* stream);
 
 /* Page list of every row from its scores (selection rule: spd_select_params).  Lists are
- * ascending logical pages.  sel_scores (device, [B, Hkv, max_list], may be NULL) receives
- * the score of each listed page of a dynamic row (streaming rows: untouched).  Returns
- * SPD_ERR_INVALID_ARG when max_list cannot hold the longest possible list: TOPK needs
- * max_list >= max(budget, n_sink + n_local) and >= n_sink_stream + n_local_stream;
- * COVERAGE needs max_list >= max_pages_per_seq. */
+ * ascending logical pages.  page_phys (device, [B, Hkv, max_list], may be NULL) receives the
+ * physical page of each listed page, read from block_table (device, required when page_phys
+ * is set), so spd_sparse_paged_decode need not read the block table.  sel_scores (device,
+ * [B, Hkv, max_list], may be NULL) receives the score of each listed page of a dynamic row
+ * (streaming rows: untouched).  Returns SPD_ERR_INVALID_ARG when max_list cannot hold the
+ * longest possible list: TOPK needs max_list >= max(budget, n_sink + n_local) and
+ * >= n_sink_stream + n_local_stream; COVERAGE needs max_list >= max_pages_per_seq.  Rows of
+ * more than 65536 pages return SPD_ERR_UNSUPPORTED. */
 int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const float* scores,
-                    const int32_t* seq_lens, const uint8_t* head_kind, int32_t* page_list,
-                    int32_t* list_len, float* sel_scores, void* workspace,
-                    size_t workspace_bytes, void* stream);
+                    const int32_t* seq_lens, const uint8_t* head_kind, const int32_t* block_table,
+                    int32_t* page_list, int32_t* page_phys, int32_t* list_len, float* sel_scores,
+                    void* stream);
 
-/* spd_page_score followed by spd_page_select in one launch for TOPK mode (LiteTopK,
+/* spd_page_score followed by spd_page_select in one launch, for both rules (LiteTopK,
  * section 3.2, "Extension to Decoding": selection fused into score computation).  The
- * scores stay in the workspace; the last block to finish a row selects its pages.
- * workspace (device) of spd_workspace_bytes(desc, sel, SPD_OP_PAGE_SCORE_SELECT) bytes
- * must be zero-filled before its first use; every call leaves its counters zero again.
- * Calls that share one workspace must not overlap.  COVERAGE returns SPD_ERR_UNSUPPORTED. */
+ * workgroups of a row score into the workspace; the last one to finish selects the row.
+ * refresh_tail != 0 first rebuilds the key min / max of each dynamic row's last logical page
+ * from k_pool (and k_scale for fp8 pools) and writes them to page_meta (LServe, "Key
+ * statistics storage and updating"); page_meta is otherwise only read.  scores (device,
+ * [B, Hkv, max_pages_per_seq], may be NULL) receives the TOPK scores or COVERAGE shares of
+ * dynamic rows; head_lse (device, [B, Hq], may be NULL) the COVERAGE per-head log-sum-exp.
+ * page_list, page_phys, list_len, sel_scores as in spd_page_select (block_table is
+ * required).  workspace (device) of spd_workspace_bytes(desc, sel, SPD_OP_PAGE_SCORE_SELECT)
+ * bytes must be zero-filled before its first use; every call leaves its counters zero
+ * again.  Calls that share one workspace must not overlap. */
 int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, const void* q,
-                          const void* page_meta, const int32_t* block_table,
-                          const int32_t* seq_lens, const uint8_t* head_kind, int32_t* page_list,
-                          int32_t* list_len, float* sel_scores, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          void* page_meta, const void* k_pool, const uint16_t* k_scale,
+                          int32_t refresh_tail, const int32_t* block_table, const int32_t* seq_lens,
+                          const uint8_t* head_kind, int32_t* page_list, int32_t* page_phys,
+                          int32_t* list_len, float* sel_scores, float* scores, float* head_lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Grouped-query decode attention of every row over its listed pages.  Block (b, h, j)
  * processes chunk j of row (b, h) (spd_plan_params); rows with one chunk write out /
  * out_lse directly, rows with more write their chunk states to part_o / part_lse for
  * spd_lse_merge.  A row with no listed pages writes out = 0 and out_lse = -inf.
- * k_scale / v_scale (device) are required for fp8 pools. */
+ * page_phys (device, may be NULL) holds the physical page of each list entry (as written by
+ * the selectors); when NULL they are read from block_table.  k_scale / v_scale (device) are
+ * required for fp8 pools. */
 int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, const void* q,
                             const void* k_pool, const void* v_pool, const uint16_t* k_scale,
                             const uint16_t* v_scale, const int32_t* block_table,
                             const int32_t* seq_lens, const int32_t* page_list,
-                            const int32_t* list_len, float sm_scale, float* out, float* out_lse,
-                            float* part_o, float* part_lse, void* stream);
+                            const int32_t* page_phys, const int32_t* list_len, float sm_scale,
+                            float* out, float* out_lse, float* part_o, float* part_lse,
+                            void* stream);
 
 /* Exact merge of the chunk states of every row with more than one chunk:
  * out_lse = log sum_j exp(lse_j), out = sum_j exp(lse_j - out_lse) * o_j.  Rows with at

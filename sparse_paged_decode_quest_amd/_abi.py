@@ -67,9 +67,10 @@ def lib():
         v = c_void_p
         L.spd_page_meta_build.argtypes = [D, v, v, v, v, v, c_int32, v, v]
         L.spd_page_score.argtypes = [D, S, v, v, v, v, POINTER(c_uint8), v, v, v, c_size_t, v]
-        L.spd_page_select.argtypes = [D, S, v, v, POINTER(c_uint8), v, v, v, v, c_size_t, v]
-        L.spd_page_score_select.argtypes = [D, S, v, v, v, v, POINTER(c_uint8), v, v, v, v, c_size_t, v]
-        L.spd_sparse_paged_decode.argtypes = [D, P, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v]
+        L.spd_page_select.argtypes = [D, S, v, v, POINTER(c_uint8), v, v, v, v, v, v]
+        L.spd_page_score_select.argtypes = [D, S, v, v, v, v, c_int32, v, v, POINTER(c_uint8), v, v, v, v, v, v, v,
+                                            c_size_t, v]
+        L.spd_sparse_paged_decode.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v]
         L.spd_lse_merge.argtypes = [D, P, v, v, v, v, v, v]
         L.spd_plan_grid.argtypes = [D, P, POINTER(c_int32)]
         L.spd_plan_chunks.argtypes = [c_int32, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32)]
@@ -133,27 +134,29 @@ def spd_page_score(desc, sel, q, page_meta, block_table, seq_lens, head_kind, sc
                                 int(workspace_bytes), _stream(stream)), "spd_page_score")
 
 
-def spd_page_select(desc, sel, scores, seq_lens, head_kind, page_list, list_len, sel_scores, workspace,
-                    workspace_bytes, stream=None):
+def spd_page_select(desc, sel, scores, seq_lens, head_kind, block_table, page_list, page_phys, list_len, sel_scores,
+                    stream=None):
     _check(lib().spd_page_select(ctypes.byref(desc), ctypes.byref(sel), _ptr(scores), _ptr(seq_lens),
-                                 _heads(head_kind), _ptr(page_list), _ptr(list_len), _ptr(sel_scores),
-                                 _ptr(workspace), int(workspace_bytes), _stream(stream)), "spd_page_select")
+                                 _heads(head_kind), _ptr(block_table), _ptr(page_list), _ptr(page_phys),
+                                 _ptr(list_len), _ptr(sel_scores), _stream(stream)), "spd_page_select")
 
 
-def spd_page_score_select(desc, sel, q, page_meta, block_table, seq_lens, head_kind, page_list, list_len,
-                          sel_scores, workspace, workspace_bytes, stream=None):
-    _check(lib().spd_page_score_select(ctypes.byref(desc), ctypes.byref(sel), _ptr(q), _ptr(page_meta),
-                                       _ptr(block_table), _ptr(seq_lens), _heads(head_kind), _ptr(page_list),
-                                       _ptr(list_len), _ptr(sel_scores), _ptr(workspace), int(workspace_bytes),
-                                       _stream(stream)), "spd_page_score_select")
+def spd_page_score_select(desc, sel, q, page_meta, k_pool, k_scale, refresh_tail, block_table, seq_lens, head_kind,
+                          page_list, page_phys, list_len, sel_scores, scores, head_lse, workspace, workspace_bytes,
+                          stream=None):
+    _check(lib().spd_page_score_select(ctypes.byref(desc), ctypes.byref(sel), _ptr(q), _ptr(page_meta), _ptr(k_pool),
+                                       _ptr(k_scale), int(refresh_tail), _ptr(block_table), _ptr(seq_lens),
+                                       _heads(head_kind), _ptr(page_list), _ptr(page_phys), _ptr(list_len),
+                                       _ptr(sel_scores), _ptr(scores), _ptr(head_lse), _ptr(workspace),
+                                       int(workspace_bytes), _stream(stream)), "spd_page_score_select")
 
 
 def spd_sparse_paged_decode(desc, plan, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, page_list,
-                            list_len, sm_scale, out, out_lse, part_o, part_lse, stream=None):
+                            page_phys, list_len, sm_scale, out, out_lse, part_o, part_lse, stream=None):
     _check(lib().spd_sparse_paged_decode(ctypes.byref(desc), ctypes.byref(plan), _ptr(q), _ptr(k_pool),
                                          _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
-                                         _ptr(seq_lens), _ptr(page_list), _ptr(list_len), float(sm_scale),
-                                         _ptr(out), _ptr(out_lse), _ptr(part_o), _ptr(part_lse),
+                                         _ptr(seq_lens), _ptr(page_list), _ptr(page_phys), _ptr(list_len),
+                                         float(sm_scale), _ptr(out), _ptr(out_lse), _ptr(part_o), _ptr(part_lse),
                                          _stream(stream)), "spd_sparse_paged_decode")
 
 

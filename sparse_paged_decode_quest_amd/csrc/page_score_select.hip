@@ -1,22 +1,25 @@
-// Fused top-K page scoring and selection in one launch (LiteTopK, section 3.2, "Extension
-// to Decoding": in decode the score write-back is small, so selection is fused into score
-// computation and finished over the aggregated per-block results).
+// Fused page scoring and selection in one launch (LiteTopK, section 3.2, "Extension to
+// Decoding": in decode the score write-back is small, so selection is fused into score
+// computation and finished over the aggregated per-block results), for both selection rules.
 //
-// Blocks of a dynamic row score their pages into the workspace, publish them with a
-// device-scope release fence and take a ticket from the row's counter; the block that
-// takes the last ticket acquires, selects the row's pages (select_row.h) and returns the
-// counter to zero, so the workspace is ready for the next call (and for graph replay)
-// without a separate clearing step.  Extra blocks write the static lists of streaming rows.
+// The workgroups of a dynamic row score their pages into the workspace (top-K scores, or the
+// coverage log-masses and per-workgroup (max, sum exp) pairs) and publish them by taking a
+// ticket from the row's counter with a device-scope release.  The workgroup that
+// takes the last ticket acquires, builds the row's keys (coverage: the per-head log-sum-exp
+// and Moira's group-mean shares, section 3.2, Eq. 3), selects the row's pages
+// (select_row.h) and returns the counter to zero, so the workspace is ready for the next call
+// (and for graph replay) without a clearing step.  With tail refresh on, the workgroup that
+// owns a row's last page rebuilds that page's key statistics from the K pool first (LServe,
+// "Key statistics storage and updating").  Extra workgroups write the static lists of
+// streaming rows.
 #include "score_common.h"
 #include "select_row.h"
 
 namespace spd {
 
-static_assert(kFusedWaves * kWave == kSelThreads, "the fused block selects with kSelThreads threads");
-
-template <int D, int QD, int MD, int KPT>
-__global__ __launch_bounds__(kSelThreads) void page_score_select_kernel(FusedArgs f) {
-  __shared__ SelectSmem sm;
+template <int D, int KVD, int NW, int ITERS, int KPL, bool COV>
+__global__ __launch_bounds__(NW * kWave) void page_score_select_kernel(FusedArgs f) {
+  __shared__ SelectSmem<NW, KPL, COV> sm;
   __shared__ int last;
   const ScoreArgs& a = f.score;
   const int dyn_blocks = a.batch * a.dyn.count * a.blocks_per_row;
@@ -25,7 +28,7 @@ __global__ __launch_bounds__(kSelThreads) void page_score_select_kernel(FusedArg
     const int b = k / f.stream_heads.count;
     const int h = f.stream_heads.head[k % f.stream_heads.count];
     const size_t row = (size_t)b * a.num_kv_heads + h;
-    select_streaming_row(f.sel, row_pages(a.seq_lens[b], a.max_pages), row);
+    select_streaming_row(f.sel, row_pages(a.seq_lens[b], a.max_pages), row, a.block_table + (size_t)b * a.max_pages);
     return;
   }
   const int row_dyn = blockIdx.x / a.blocks_per_row;
@@ -33,44 +36,100 @@ __global__ __launch_bounds__(kSelThreads) void page_score_select_kernel(FusedArg
   const int b = row_dyn / a.dyn.count;
   const int h = a.dyn.head[row_dyn % a.dyn.count];
   const size_t row = (size_t)b * a.num_kv_heads + h;
-  const int n = row_pages(a.seq_lens[b], a.max_pages);
+  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+  const int p_begin = blk * a.pages_per_block;
+  const int len = a.seq_lens[b];
+  int raw[ITERS];
+  load_block_table<D, KVD, NW, ITERS>(bt_row, a.max_pages, p_begin, raw);
+  const int n = row_pages(len, a.max_pages);
   const int used = (n + a.pages_per_block - 1) / a.pages_per_block;
   if (n == 0) {
     if (blk == 0 && threadIdx.x == 0) f.sel.list_len[row] = 0;
+    if (COV && blk == 0 && threadIdx.x < kG && a.head_lse)
+      a.head_lse[(size_t)b * a.num_q_heads + (size_t)h * kG + threadIdx.x] = -INFINITY;
     return;
   }
   if (blk >= used) return;
-  const int p_begin = blk * a.pages_per_block;
-  const int p_end = min(n, p_begin + a.pages_per_block);
-  float* row_scores = a.scores + row * a.max_pages;
-  score_block_topk<D, QD, MD, kFusedWaves, kFusedIters>(a, b, h, p_begin, p_end, row_scores);
-  __threadfence();  // release this block's scores device-wide
+  if constexpr (COV) score_block_coverage<D, KVD, NW, ITERS>(a, raw, n, len, b, h, p_begin, blk, a.refresh_tail != 0);
+  else score_block_topk<D, KVD, NW, ITERS>(a, raw, n, len, b, h, p_begin, a.refresh_tail != 0,
+                                           a.scores + row * a.max_pages);
+  // Publish: every wave waits for its own score stores, the workgroup barrier orders them before
+  // the ticket, and the ticket is a release at device scope (one L2 write-back per workgroup;
+  // a fence in every wave would write back and invalidate the L2 once per wave).  The workgroup
+  // that takes the last ticket acquires with one fence (the L1 it invalidates is the CU's, shared
+  // by all its waves) before any wave reads the other workgroups' scores.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(&f.counters[row], 1u) == (unsigned)(used - 1);
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(&f.counters[row], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(used - 1);
   __syncthreads();
   if (!last) return;
-  __threadfence();  // acquire the other blocks' scores
-  select_dynamic_row<KPT, false>(f.sel, row_scores, n, row, sm);
+  if (threadIdx.x < kWave) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
+
+  const int wbase = (int)(threadIdx.x / kWave) * kWave * KPL + (int)(threadIdx.x % kWave);  // select_row.h slots
+  uint32_t key[KPL];
+  SlotPhys<KPL> phys;
+  phys.bt_row = f.sel.page_phys ? bt_row : nullptr;
+  if constexpr (COV) {
+    float lse[kG];
+    row_head_lse(a.partials + row * a.blocks_per_row * kG, used, lse);  // every wave, same bits
+    if (threadIdx.x < kG && a.head_lse) {
+      float v = lse[0];
+#pragma unroll
+      for (int g = 1; g < kG; ++g) v = (int)threadIdx.x == g ? lse[g] : v;
+      a.head_lse[(size_t)b * a.num_q_heads + (size_t)h * kG + threadIdx.x] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int p = wbase + i * kWave;
+      float4 l4 = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (p < n) l4 = a.ell[row * a.max_pages + p];
+      phys.load(i, p, n);
+      const float pi = p < n ? group_share(l4, lse) : 0.f;
+      key[i] = coverage_key(pi);
+      if (f.score_out && p < n) f.score_out[row * a.max_pages + p] = pi;
+    }
+  } else {
+    const float* sc = a.scores + row * a.max_pages;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int p = wbase + i * kWave;
+      key[i] = score_key(p < n ? sc[p] : 0.f);
+      phys.load(i, p, n);
+    }
+  }
+  select_row_keys<NW, KPL, COV>(f.sel, key, phys, row_shape(n, f.sel.n_sink, f.sel.n_local), row, sm);
   if (threadIdx.x == 0) f.counters[row] = 0u;
 }
 
-int launch_page_score_select(const FusedArgs& f, int head_dim, int q_dtype, int meta_dtype, hipStream_t stream) {
+int launch_page_score_select(const FusedArgs& f, int head_dim, int kv_dtype, hipStream_t stream) {
+  SelectGeometry g;
+  if (!select_geometry(f.score.max_pages, g)) return SPD_ERR_UNSUPPORTED;
   const int blocks = f.score.batch * (f.score.dyn.count * f.score.blocks_per_row + f.stream_heads.count);
-  dim3 grid((unsigned)blocks), block(kSelThreads);
-#define SPD_FUSED_CASE(D, QD, MD)                                                                  \
-  if (head_dim == D && q_dtype == QD && meta_dtype == MD) {                                        \
-    switch (select_kpt(f.score.max_pages)) {                                                       \
-      case 8: hipLaunchKernelGGL((page_score_select_kernel<D, QD, MD, 8>), grid, block, 0, stream, f); break;     \
-      case 32: hipLaunchKernelGGL((page_score_select_kernel<D, QD, MD, 32>), grid, block, 0, stream, f); break;   \
-      default: hipLaunchKernelGGL((page_score_select_kernel<D, QD, MD, 0>), grid, block, 0, stream, f); break;    \
-    }                                                                                              \
-    return 0;                                                                                      \
+  const dim3 grid((unsigned)blocks), block(g.nw * kWave);
+  const bool cov = f.sel.mode == SPD_SELECT_COVERAGE;
+#define SPD_FUSED_GEOM(D, KVD, NW, KPL, IT)                                                                     \
+  if (g.nw == NW && g.kpl == KPL) {                                                                             \
+    if (cov) hipLaunchKernelGGL((page_score_select_kernel<D, KVD, NW, IT, KPL, true>), grid, block, 0, stream, f); \
+    else hipLaunchKernelGGL((page_score_select_kernel<D, KVD, NW, IT, KPL, false>), grid, block, 0, stream, f);    \
+    return 0;                                                                                                   \
   }
-  SPD_FUSED_CASE(64, SPD_DTYPE_F16, SPD_DTYPE_F16)
-  SPD_FUSED_CASE(128, SPD_DTYPE_F16, SPD_DTYPE_F16)
-  SPD_FUSED_CASE(64, SPD_DTYPE_F32, SPD_DTYPE_F32)
-  SPD_FUSED_CASE(128, SPD_DTYPE_F32, SPD_DTYPE_F32)
+#define SPD_FUSED_CASE(D, KVD)                 \
+  if (head_dim == D && kv_dtype == KVD) {      \
+    SPD_FUSED_GEOM(D, KVD, 16, 2, 2)           \
+    SPD_FUSED_GEOM(D, KVD, 16, 8, 2)           \
+    SPD_FUSED_GEOM(D, KVD, 16, 32, 2)          \
+    SPD_FUSED_GEOM(D, KVD, 16, 64, 4)          \
+    return SPD_ERR_UNSUPPORTED;                \
+  }
+  SPD_FUSED_CASE(64, SPD_DTYPE_F16)
+  SPD_FUSED_CASE(128, SPD_DTYPE_F16)
+  SPD_FUSED_CASE(128, SPD_DTYPE_FP8_E4M3FN)
+  SPD_FUSED_CASE(64, SPD_DTYPE_F32)
+  SPD_FUSED_CASE(128, SPD_DTYPE_F32)
 #undef SPD_FUSED_CASE
+#undef SPD_FUSED_GEOM
   return SPD_ERR_UNSUPPORTED;
 }
 

@@ -1,28 +1,59 @@
-// Page lists from page scores: one kSelThreads-thread workgroup per (request, KV head) row.
-// The selection rules and their sources are described in select_row.h.
+// Page lists from page scores: one workgroup per (request, KV head) row.  The selection rules
+// and their sources are described in select_row.h.
 #include "select_row.h"
 
 namespace spd {
 
-template <int KPT>
-__global__ __launch_bounds__(kSelThreads) void page_select_kernel(SelectArgs a) {
-  __shared__ SelectSmem sm;
+// Keys (and physical pages, when the list of physical pages is wanted) of the row's pages in
+// the slot layout of select_row_keys.  `sc` holds top-K scores or coverage shares.
+template <int NW, int KPL, bool COV>
+__device__ __forceinline__ void load_row_keys(const float* sc, int n, uint32_t (&key)[KPL], SlotPhys<KPL>& phys) {
+  const int wbase = (int)(threadIdx.x / kWave) * kWave * KPL + (int)(threadIdx.x % kWave);
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int p = wbase + i * kWave;
+    const float v = p < n ? sc[p] : 0.f;
+    key[i] = COV ? coverage_key(v) : score_key(v);
+    phys.load(i, p, n);
+  }
+}
+
+template <int NW, int KPL, bool COV>
+__global__ __launch_bounds__(NW * kWave) void page_select_kernel(SelectArgs a) {
+  __shared__ SelectSmem<NW, KPL, COV> sm;
   const int b = blockIdx.x / a.num_kv_heads;
   const int h = blockIdx.x % a.num_kv_heads;
   const size_t row = (size_t)b * a.num_kv_heads + h;
   const int n = row_pages(a.seq_lens[b], a.max_pages);
-  const bool streaming = (a.streaming_mask >> h) & 1ull;
-  select_row<KPT>(a, a.scores + row * a.max_pages, n, row, streaming, sm);
+  const int32_t* bt_row = a.page_phys ? a.block_table + (size_t)b * a.max_pages : nullptr;
+  if ((a.streaming_mask >> h) & 1ull) {
+    select_streaming_row(a, n, row, bt_row);
+    return;
+  }
+  uint32_t key[KPL];
+  SlotPhys<KPL> phys;
+  phys.bt_row = bt_row;
+  load_row_keys<NW, KPL, COV>(a.scores + row * a.max_pages, n, key, phys);
+  select_row_keys<NW, KPL, COV>(a, key, phys, row_shape(n, a.n_sink, a.n_local), row, sm);
 }
 
 int launch_page_select(const SelectArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.batch * a.num_kv_heads)), block(kSelThreads);
-  switch (select_kpt(a.max_pages)) {
-    case 8: hipLaunchKernelGGL(page_select_kernel<8>, grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL(page_select_kernel<32>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(page_select_kernel<0>, grid, block, 0, stream, a); break;
+  SelectGeometry g;
+  if (!select_geometry(a.max_pages, g)) return SPD_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)(a.batch * a.num_kv_heads)), block(g.nw * kWave);
+  const bool cov = a.mode == SPD_SELECT_COVERAGE;
+#define SPD_SEL_CASE(NW, KPL)                                                                          \
+  if (g.nw == NW && g.kpl == KPL) {                                                                    \
+    if (cov) hipLaunchKernelGGL((page_select_kernel<NW, KPL, true>), grid, block, 0, stream, a);       \
+    else hipLaunchKernelGGL((page_select_kernel<NW, KPL, false>), grid, block, 0, stream, a);          \
+    return 0;                                                                                          \
   }
-  return 0;
+  SPD_SEL_CASE(16, 2)
+  SPD_SEL_CASE(16, 8)
+  SPD_SEL_CASE(16, 32)
+  SPD_SEL_CASE(16, 64)
+#undef SPD_SEL_CASE
+  return SPD_ERR_UNSUPPORTED;
 }
 
 }  // namespace spd

@@ -6,9 +6,16 @@
 //
 // Work layout: LPP lanes cover one page's [2, d] meta row with 16-byte loads (f16 d = 128:
 // 16 lanes, PPI = 4 pages per wave instruction).  A workgroup of NW waves owns
-// ITERS * NW * PPI consecutive pages; every lane first loads the block-table entries of all
-// its pages, then issues all of its meta loads, and only then computes, so each wave keeps
-// ITERS * 32 bytes per lane in flight instead of walking pages one dependent load at a time.
+// ITERS * NW * PPI consecutive pages.  The block-table entries are loaded at the same time
+// as the request's length (entries past the row end are read from inside the table row and
+// ignored), then every meta load of the lane is issued before any arithmetic, so a lane keeps
+// ITERS * 32 bytes in flight and the whole scan is two dependent memory round trips.
+//
+// Tail refresh (LServe, "Key statistics storage and updating": the statistics of the page a
+// new token lands in are updated as the token is appended): when enabled, the lanes that own
+// the row's last page rebuild its min / max from the K pool, write them to the page meta and
+// score the page from those registers -- the same two round trips, with the K page in place
+// of its meta row.
 #pragma once
 
 #include "spd_device.h"
@@ -17,22 +24,20 @@
 namespace spd {
 
 constexpr int kG = 4;  // query heads per KV head (the compiled GQA group)
-constexpr int kScoreWaves = 4, kScoreIters = 4;  // standalone scorer: 4 waves x 4 page groups
-constexpr int kFusedWaves = 16, kFusedIters = 2;  // fused scorer (its last block selects)
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
-template <int D, int QD, int MD>
+template <int D, int KVD>
 struct ScoreTraits;
 
-// f16 query, f16 meta: packed sign-select + v_dot2_f32_f16.
-template <int D>
-struct ScoreTraits<D, SPD_DTYPE_F16, SPD_DTYPE_F16> {
-  static constexpr int CW = 8;                   // channels per 16-byte load
-  static constexpr int LPP = D * 2 / 16;         // lanes per page
+// f16 query, f16 meta (f16 pools, and fp8 pools whose meta is f16 rounded outward):
+// packed sign-select + v_dot2_f32_f16.
+template <int D, int KVD>
+struct ScoreTraitsF16 {
+  static constexpr int CW = 8;            // channels per 16-byte meta load
+  static constexpr int LPP = D * 2 / 16;  // lanes per page
   struct Q {
-    uint32_t h[kG][CW / 2];    // query pairs
-    uint32_t pos[kG][CW / 2];  // 0xffff per half where q >= 0
+    uint32_t h[kG][CW / 2];  // query pairs
   };
   struct M {
     uint4 mn, mx;
@@ -40,13 +45,12 @@ struct ScoreTraits<D, SPD_DTYPE_F16, SPD_DTYPE_F16> {
   __device__ static void load_q(Q& qr, const void* q, size_t base, int c0) {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(q) + base;
 #pragma unroll
-    for (int g = 0; g < kG; ++g)
+    for (int g = 0; g < kG; ++g) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qp + (size_t)g * D + c0);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int i = 0; i < CW / 2; ++i) {
-        uint16_t lo = qp[(size_t)g * D + c0 + 2 * i], hi = qp[(size_t)g * D + c0 + 2 * i + 1];
-        qr.h[g][i] = (uint32_t)lo | ((uint32_t)hi << 16);
-        qr.pos[g][i] = ((lo & 0x8000u) ? 0u : 0xffffu) | ((hi & 0x8000u) ? 0u : 0xffff0000u);
-      }
+      for (int i = 0; i < CW / 2; ++i) qr.h[g][i] = ws[i];
+    }
   }
   __device__ static void load_m(M& m, const void* meta, size_t row, int c0) {
     const uint16_t* base = reinterpret_cast<const uint16_t*>(meta) + row + c0;
@@ -61,17 +65,93 @@ struct ScoreTraits<D, SPD_DTYPE_F16, SPD_DTYPE_F16> {
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint32_t sel = (hi[i] & qr.pos[g][i]) | (lo[i] & ~qr.pos[g][i]);
+        // per half: 0xffff where the query is >= 0 (sign bit clear), from the sign bits
+        const uint32_t neg = (qr.h[g][i] >> 15) & 0x00010001u;
+        const uint32_t pos = (neg ^ 0x00010001u) * 0xffffu;
+        const uint32_t sel = (hi[i] & pos) | (lo[i] & ~pos);
         acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, sel), __builtin_bit_cast(h2_t, qr.h[g][i]), acc, false);
       }
       s[g] = acc;
     }
   }
+  // this lane's CW channels of the page's keys -> min / max (valid tokens only), stored and kept
+  __device__ static void rebuild(M& m, const void* k_pool, const uint16_t* k_scale, size_t head_page, int valid,
+                                 int c0, void* meta, size_t row) {
+    float lo[CW], hi[CW];
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      lo[c] = INFINITY;
+      hi[c] = -INFINITY;
+    }
+    if constexpr (KVD == SPD_DTYPE_F16) {
+      const uint16_t* kp = reinterpret_cast<const uint16_t*>(k_pool) + head_page * kPage * D + c0;
+#pragma unroll
+      for (int t = 0; t < kPage; ++t) {
+        const uint4 t4 = *reinterpret_cast<const uint4*>(kp + (size_t)t * D);
+        const uint32_t w[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const __half2 h = __builtin_bit_cast(__half2, w[i]);
+          const float v0 = __low2float(h), v1 = __high2float(h);
+          if (t < valid) {
+            lo[2 * i] = fminf(lo[2 * i], v0);
+            hi[2 * i] = fmaxf(hi[2 * i], v0);
+            lo[2 * i + 1] = fminf(lo[2 * i + 1], v1);
+            hi[2 * i + 1] = fmaxf(hi[2 * i + 1], v1);
+          }
+        }
+      }
+    } else {  // fp8 codes times the token's scale, exact in fp32
+      const uint8_t* kp = reinterpret_cast<const uint8_t*>(k_pool) + head_page * kPage * D + c0;
+#pragma unroll
+      for (int t = 0; t < kPage; ++t) {
+        const uint2 t2 = *reinterpret_cast<const uint2*>(kp + (size_t)t * D);
+        const float sc = half_bits_to_float(k_scale[head_page * kPage + t]);
+        const float v[CW] = {fp8_to_float(t2.x & 0xffu) * sc,         fp8_to_float((t2.x >> 8) & 0xffu) * sc,
+                             fp8_to_float((t2.x >> 16) & 0xffu) * sc, fp8_to_float(t2.x >> 24) * sc,
+                             fp8_to_float(t2.y & 0xffu) * sc,         fp8_to_float((t2.y >> 8) & 0xffu) * sc,
+                             fp8_to_float((t2.y >> 16) & 0xffu) * sc, fp8_to_float(t2.y >> 24) * sc};
+        if (t < valid) {
+#pragma unroll
+          for (int c = 0; c < CW; ++c) {
+            lo[c] = fminf(lo[c], v[c]);
+            hi[c] = fmaxf(hi[c], v[c]);
+          }
+        }
+      }
+    }
+    uint32_t plo[4], phi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t l0, l1, h0, h1;
+      if constexpr (KVD == SPD_DTYPE_F16) {  // exact: min / max of fp16 values
+        l0 = __half_as_ushort(__float2half_rn(lo[2 * i]));
+        l1 = __half_as_ushort(__float2half_rn(lo[2 * i + 1]));
+        h0 = __half_as_ushort(__float2half_rn(hi[2 * i]));
+        h1 = __half_as_ushort(__float2half_rn(hi[2 * i + 1]));
+      } else {  // outward: the stored box still contains every key
+        l0 = f32_to_f16_round_down(lo[2 * i]);
+        l1 = f32_to_f16_round_down(lo[2 * i + 1]);
+        h0 = f32_to_f16_round_up(hi[2 * i]);
+        h1 = f32_to_f16_round_up(hi[2 * i + 1]);
+      }
+      plo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      phi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    }
+    m.mn = make_uint4(plo[0], plo[1], plo[2], plo[3]);
+    m.mx = make_uint4(phi[0], phi[1], phi[2], phi[3]);
+    uint16_t* mp = reinterpret_cast<uint16_t*>(meta) + row + c0;
+    *reinterpret_cast<uint4*>(mp) = m.mn;
+    *reinterpret_cast<uint4*>(mp + D) = m.mx;
+  }
 };
 
-// f32 query, f32 meta.
+template <int D> struct ScoreTraits<D, SPD_DTYPE_F16> : ScoreTraitsF16<D, SPD_DTYPE_F16> {};
+template <int D> struct ScoreTraits<D, SPD_DTYPE_FP8_E4M3FN> : ScoreTraitsF16<D, SPD_DTYPE_FP8_E4M3FN> {};
+
+// f32 query, f32 meta, f32 pool.
 template <int D>
-struct ScoreTraits<D, SPD_DTYPE_F32, SPD_DTYPE_F32> {
+struct ScoreTraits<D, SPD_DTYPE_F32> {
   static constexpr int CW = 4;
   static constexpr int LPP = D * 4 / 16;
   struct Q {
@@ -83,9 +163,13 @@ struct ScoreTraits<D, SPD_DTYPE_F32, SPD_DTYPE_F32> {
   __device__ static void load_q(Q& qr, const void* q, size_t base, int c0) {
     const float* qp = reinterpret_cast<const float*>(q) + base;
 #pragma unroll
-    for (int g = 0; g < kG; ++g)
-#pragma unroll
-      for (int c = 0; c < CW; ++c) qr.v[g][c] = qp[(size_t)g * D + c0 + c];
+    for (int g = 0; g < kG; ++g) {
+      const float4 w = *reinterpret_cast<const float4*>(qp + (size_t)g * D + c0);
+      qr.v[g][0] = w.x;
+      qr.v[g][1] = w.y;
+      qr.v[g][2] = w.z;
+      qr.v[g][3] = w.w;
+    }
   }
   __device__ static void load_m(M& m, const void* meta, size_t row, int c0) {
     const float* base = reinterpret_cast<const float*>(meta) + row + c0;
@@ -102,6 +186,28 @@ struct ScoreTraits<D, SPD_DTYPE_F32, SPD_DTYPE_F32> {
       for (int c = 0; c < CW; ++c) acc = fmaf(qr.v[g][c], qr.v[g][c] >= 0.f ? hi[c] : lo[c], acc);
       s[g] = acc;
     }
+  }
+  __device__ static void rebuild(M& m, const void* k_pool, const uint16_t*, size_t head_page, int valid, int c0,
+                                 void* meta, size_t row) {
+    const float* kp = reinterpret_cast<const float*>(k_pool) + head_page * kPage * D + c0;
+    float lo[4] = {INFINITY, INFINITY, INFINITY, INFINITY}, hi[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) {
+      const float4 t4 = *reinterpret_cast<const float4*>(kp + (size_t)t * D);
+      const float v[4] = {t4.x, t4.y, t4.z, t4.w};
+      if (t < valid) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          lo[c] = fminf(lo[c], v[c]);
+          hi[c] = fmaxf(hi[c], v[c]);
+        }
+      }
+    }
+    m.mn = make_float4(lo[0], lo[1], lo[2], lo[3]);
+    m.mx = make_float4(hi[0], hi[1], hi[2], hi[3]);
+    float* mp = reinterpret_cast<float*>(meta) + row + c0;
+    *reinterpret_cast<float4*>(mp) = m.mn;
+    *reinterpret_cast<float4*>(mp + D) = m.mx;
   }
 };
 
@@ -122,69 +228,181 @@ __device__ __forceinline__ void lse_push(float& m, float& s, float x) {
 
 __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
   if (m2 == -INFINITY) return;
-  if (m == -INFINITY) { m = m2; s = s2; return; }
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+    return;
+  }
   float M = fmaxf(m, m2);
   s = s * expf(m - M) + s2 * expf(m2 - M);
   m = M;
 }
 
-// Bounds S_{g,p} of the pages [p_begin, p_end) owned by this workgroup.  For each of the
-// kScoreIters page groups of the calling lane, `fn(p, ok, s)` is called on lanes with
-// sub == 0 after the LPP-lane reduction (p may be >= p_end: then ok is false and fn must
-// ignore it).  Pages whose block-table entry is outside the pool have ok = false.
-template <int D, int QD, int MD, int NW, int ITERS, typename F>
-__device__ __forceinline__ void score_block(const ScoreArgs& a, int b, int h, int p_begin, int p_end, F&& fn) {
-  using T = ScoreTraits<D, QD, MD>;
-  constexpr int LPP = T::LPP;
+// Logical page of the calling lane's page group `it` in a workgroup starting at p_begin.
+template <int D, int KVD, int NW>
+__device__ __forceinline__ int score_page(int p_begin, int it) {
+  constexpr int LPP = ScoreTraits<D, KVD>::LPP;
   constexpr int PPI = kWave / LPP;
-  const int wave = threadIdx.x / kWave;
+  return p_begin + (it * NW + (int)threadIdx.x / kWave) * PPI + ((int)threadIdx.x % kWave) / LPP;
+}
+
+// Block-table entries of the calling lane's pages, read without waiting for the request's
+// length: indices past the table row are clamped into it and the values discarded later.
+template <int D, int KVD, int NW, int ITERS>
+__device__ __forceinline__ void load_block_table(const int32_t* bt_row, int max_pages, int p_begin, int (&raw)[ITERS]) {
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) raw[it] = bt_row[min(score_page<D, KVD, NW>(p_begin, it), max_pages - 1)];
+}
+
+// Bounds S_{g,p} of the pages [p_begin, p_begin + NW * ITERS * PPI) owned by this workgroup.
+// n is the row's page count (pages >= n are not loaded); raw holds load_block_table's entries.
+// For each of the ITERS page groups of the calling lane, `fn(p, ok, s)` is called on lanes
+// with sub == 0 after the LPP-lane reduction (p may be >= n: then ok is false and fn must
+// ignore it).  Pages whose block-table entry is outside the pool have ok = false.  `tail`
+// enables the rebuild of page n - 1 from the K pool.
+template <int D, int KVD, int NW, int ITERS, typename F>
+__device__ __forceinline__ void score_block(const ScoreArgs& a, const int (&raw)[ITERS], int n, int len, int b, int h,
+                                            int p_begin, bool tail, F&& fn) {
+  using T = ScoreTraits<D, KVD>;
+  constexpr int LPP = T::LPP;
   const int lane = threadIdx.x % kWave;
   const int sub = lane % LPP;
-  const int slot = lane / LPP;
   const int c0 = sub * T::CW;
-  typename T::Q qr;
-  T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0);
   int pg[ITERS], phys[ITERS];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
-    pg[it] = p_begin + (it * NW + wave) * PPI + slot;
-    phys[it] = pg[it] < p_end ? a.block_table[(size_t)b * a.max_pages + pg[it]] : -1;
+    pg[it] = score_page<D, KVD, NW>(p_begin, it);
+    phys[it] = pg[it] < n ? raw[it] : -1;
   }
-  typename T::M m[ITERS];
+  typename T::Q qr;
+  T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0);
+  typename T::M m[ITERS], mt;
+  int tail_phys = -1;  // the row's last page, when this lane's group owns it and it is rebuilt
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
-    if (phys[it] >= 0 && phys[it] < a.num_pool_pages)
-      T::load_m(m[it], a.meta, ((size_t)phys[it] * a.num_kv_heads + h) * 2 * D, c0);
+    const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
+    if (tail && pg[it] == n - 1) tail_phys = ok ? phys[it] : -1;
+    else if (ok) T::load_m(m[it], a.meta, ((size_t)phys[it] * a.num_kv_heads + h) * 2 * D, c0);
   }
+  if (tail_phys >= 0)
+    T::rebuild(mt, a.k_pool, a.k_scale, (size_t)tail_phys * a.num_kv_heads + h, valid_in_page(len, n - 1), c0,
+               a.meta_out, ((size_t)tail_phys * a.num_kv_heads + h) * 2 * D);
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
     float s[kG];
-    if (ok) T::bound(qr, m[it], s);
+    if (ok) T::bound(qr, (tail && pg[it] == n - 1) ? mt : m[it], s);
     else {
 #pragma unroll
       for (int g = 0; g < kG; ++g) s[g] = 0.f;
     }
 #pragma unroll
     for (int g = 0; g < kG; ++g) s[g] = xor_sum<LPP>(s[g]);
-    if (sub == 0) fn(pg[it], ok && pg[it] < p_end, s);
+    if (sub == 0) fn(pg[it], ok && pg[it] < n, s);
   }
 }
 
-// Top-K scores of pages [p_begin, p_end) of row (b, h): score_p = max_g S_{g,p} (the group
-// combine keeps the score an upper bound for every query head of the group); pages whose
-// block-table entry is outside the pool score -inf.
-template <int D, int QD, int MD, int NW, int ITERS>
-__device__ __forceinline__ void score_block_topk(const ScoreArgs& a, int b, int h, int p_begin, int p_end,
-                                                 float* row_scores) {
-  if (p_begin >= p_end) return;
-  score_block<D, QD, MD, NW, ITERS>(a, b, h, p_begin, p_end, [&](int p, bool ok, const float (&s)[kG]) {
-    if (p >= p_end) return;
+// Top-K keys of the workgroup's pages: score_p = max_g S_{g,p} (the group combine keeps the
+// score an upper bound for every query head of the group); pages whose block-table entry is
+// outside the pool score -inf.
+template <int D, int KVD, int NW, int ITERS>
+__device__ __forceinline__ void score_block_topk(const ScoreArgs& a, const int (&raw)[ITERS], int n, int len, int b,
+                                                 int h, int p_begin, bool tail, float* row_scores) {
+  score_block<D, KVD, NW, ITERS>(a, raw, n, len, b, h, p_begin, tail, [&](int p, bool ok, const float (&s)[kG]) {
+    if (p >= n) return;
     float best = s[0];
 #pragma unroll
     for (int g = 1; g < kG; ++g) best = fmaxf(best, s[g]);
     row_scores[p] = ok ? best : -INFINITY;
   });
+}
+
+// Coverage, first pass over the workgroup's pages: log-masses l_{g,p} = s S_{g,p} + ln(valid_p)
+// written per page, and one (max, sum exp) pair per head for the workgroup.  Moira, section
+// 3.2: the per-head softmax over pages needs the head's log-sum-exp over the whole row.
+template <int D, int KVD, int NW, int ITERS>
+__device__ __forceinline__ void score_block_coverage(const ScoreArgs& a, const int (&raw)[ITERS], int n, int len, int b,
+                                                     int h, int p_begin, int blk, bool tail) {
+  constexpr int LPP = ScoreTraits<D, KVD>::LPP;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const size_t row = (size_t)b * a.num_kv_heads + h;
+  float lm[kG], ls[kG];  // running (max, sum exp) of this lane's pages
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    lm[g] = -INFINITY;
+    ls[g] = 0.f;
+  }
+  score_block<D, KVD, NW, ITERS>(a, raw, n, len, b, h, p_begin, tail, [&](int p, bool ok, const float (&s)[kG]) {
+    if (p >= n) return;
+    const int valid = valid_in_page(len, p);
+    const float lv = valid == kPage ? 2.772588722239781f : logf((float)valid);  // ln(valid)
+    float lg[kG];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      lg[g] = ok ? fmaf(a.sm_scale, s[g], lv) : -INFINITY;
+      lse_push(lm[g], ls[g], lg[g]);
+    }
+    a.ell[row * a.max_pages + p] = make_float4(lg[0], lg[1], lg[2], lg[3]);
+  });
+  // fold the lanes that own pages (sub == 0), then the waves in order
+  __shared__ float sm_m[NW][kG], sm_s[NW][kG];
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    for (int o = LPP; o < kWave; o <<= 1) {
+      float m2 = __shfl_xor(lm[g], o, kWave), s2 = __shfl_xor(ls[g], o, kWave);
+      lse_combine(lm[g], ls[g], m2, s2);
+    }
+    if (lane == 0) {
+      sm_m[wave][g] = lm[g];
+      sm_s[wave][g] = ls[g];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kG) {
+    const int g = threadIdx.x;
+    float m = sm_m[0][g], s = sm_s[0][g];
+    for (int w = 1; w < NW; ++w) lse_combine(m, s, sm_m[w][g], sm_s[w][g]);
+    a.partials[(row * a.blocks_per_row + blk) * kG + g] = make_float2(m, s);
+  }
+}
+
+// Per-head log-sum-exp of a row from its `used` workgroup partials, computed by one wave in a
+// fixed order (so every caller gets the same bits): lanes fold partials lane, lane + 64, ...,
+// then a fixed butterfly.  Returns lse[g] (-inf for an empty row) in every lane.
+__device__ __forceinline__ void row_head_lse(const float2* partials, int used, float (&lse)[kG]) {
+  const int lane = threadIdx.x % kWave;
+  float m[kG], s[kG];
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    m[g] = -INFINITY;
+    s[g] = 0.f;
+  }
+  for (int k = lane; k < used; k += kWave) {
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      const float2 pr = partials[(size_t)k * kG + g];
+      lse_combine(m[g], s[g], pr.x, pr.y);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    for (int o = 1; o < kWave; o <<= 1) {
+      float m2 = __shfl_xor(m[g], o, kWave), s2 = __shfl_xor(s[g], o, kWave);
+      lse_combine(m[g], s[g], m2, s2);
+    }
+    lse[g] = m[g] == -INFINITY ? -INFINITY : m[g] + logf(s[g]);
+  }
+}
+
+// Moira's group-mean share of one page from its G log-masses and the heads' log-sum-exps.
+__device__ __forceinline__ float group_share(float4 l4, const float (&lse)[kG]) {
+  const float lg[kG] = {l4.x, l4.y, l4.z, l4.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int g = 0; g < kG; ++g)
+    if (lg[g] != -INFINITY) acc += expf(lg[g] - lse[g]);
+  return acc * (1.0f / kG);
 }
 
 }  // namespace spd

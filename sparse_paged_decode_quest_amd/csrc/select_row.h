@@ -1,51 +1,59 @@
-// Page selection of one (request, KV head) row by one workgroup of NT threads.
+// Page selection of one (request, KV head) row by one workgroup of NW waves.
 //
 //  * Forced pages: sink 0..n_sink-1 and local n-n_local..n-1 (each once).  A streaming row
 //    keeps exactly its forced pages -- the static index table of the LServe summary,
 //    "Decoding Stage: Kernel Implementation with Two-Level Indexing".
 //  * Top-K (LServe, "Token budget and physical page selection"): the forced pages plus the
 //    K' = budget - |forced| best other pages by (score desc, page asc).  The K'-th largest
-//    score is found exactly by a radix select over order-preserving 32-bit keys of the fp32
-//    scores: each digit histograms only the keys sharing the digits chosen so far, so the
-//    final selection is restricted to one bin (the bit-pattern bins of LiteTopK, section
-//    3.2, "Extension to Decoding").  No sort.
-//  * Coverage (Moira, section 3.2, Eq. 3): tau = the largest share value whose at-or-above
-//    share mass reaches t = gamma - forced shares, found by the same radix walk with bins
-//    weighted by mass.  Shares are >= 0, so their IEEE bit patterns are already ordered;
-//    masses are summed as 64-bit fixed point (2^-40 units) with integer atomics, so the sums
-//    -- and tau -- do not depend on thread timing.  tau is exact in fp32 order, unlike a
-//    bisection that stops at a resolution.
+//    score is found exactly by a radix walk over order-preserving 32-bit keys of the fp32
+//    scores: each digit histograms only the keys that share the digits chosen so far, so the
+//    final choice is made inside one bin (the bit-pattern bins of LiteTopK, section 3.2,
+//    "Extension to Decoding").  No sort.
+//  * Coverage (Moira, section 3.2, Eq. 3): tau = the largest share whose at-or-above share
+//    mass reaches t = gamma - forced shares, found by the same walk with bins weighted by
+//    mass.  Shares are >= 0, so their IEEE bit patterns are already ordered; masses are
+//    summed as 64-bit fixed point (2^-40 units) with integer atomics, so sums -- and tau --
+//    do not depend on thread timing, and tau is exact in fp32 order.
 //
-// Work layout: thread t of the workgroup owns the contiguous pages [t*chunk, (t+1)*chunk)
-// and keeps their keys in registers (KPT >= chunk), or re-reads them from memory (KPT == 0,
-// very long rows).
-// The digits start below the bits shared by the smallest and the largest free key, so the
-// first histogram already spreads the (typically narrow) score range over many bins; a pass
-// that finds the crossing bin needed whole ends the walk early.  Compaction is one
-// workgroup-wide exclusive scan of the per-thread kept counts, which writes the list in
-// ascending page order.
+// Work layout.  Wave w holds the 64 KPL consecutive pages starting at 64 KPL w; its key slot
+// i holds page 64 KPL w + 64 i + lane, so every key load of a wave reads 64 consecutive scores
+// and page order is (wave, slot, lane) order.  The list is compacted with one ballot per slot
+// and scalar running counts inside a wave, plus one LDS exchange of the wave totals.  The
+// walk needs one workgroup barrier per digit: every wave then finds the crossing bin itself
+// from the shared histogram (three rotating histogram buffers make that safe), reading it
+// without LDS bank conflicts -- 64 lane sums over skewed addresses, a scan, and a second scan
+// inside the crossing lane's group of bins.  Top-K usually stops after one digit: when at
+// most kCandMax keys share the crossing bin, each wave ranks those candidates directly.  Ties
+// at the K'-th key are taken in page order.
 #pragma once
+
+#include <type_traits>
 
 #include "spd_device.h"
 #include "spd_launch.h"
 
 namespace spd {
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kSelBins = 2048;  // 11-bit digits
-constexpr double kMassOne = 1099511627776.0;  // 2^40
+// Radix digits: 11 bits (2048 count bins) for top-K, 10 bits (1024 64-bit mass bins) for coverage.
+template <bool COV>
+struct SelectDigit {
+  static constexpr int kBits = COV ? 10 : 11;
+  static constexpr int kBins = 1 << kBits;
+};
+constexpr int kCandMax = kWave;                // crossing-bin keys ranked by one wave
+constexpr int kNoLimit = 0x7fffffff;
+constexpr double kMassOne = 1099511627776.0;   // 2^40
 
+template <int NW, int KPL, bool COV>
 struct SelectSmem {
-  union {
-    uint32_t cnt[kSelBins];
-    unsigned long long mass[kSelBins];
-  } hist;
-  unsigned long long wave_tot[kSelWaves];
-  uint32_t wave_min[kSelWaves], wave_max[kSelWaves];
-  unsigned long long cross_above;
-  unsigned long long cross_val;
-  int cross_bin;
+  using H = typename std::conditional<COV, unsigned long long, uint32_t>::type;
+  H hist[3][SelectDigit<COV>::kBins];
+  unsigned long long wsum[NW];
+  uint32_t wmin[NW], wmax[NW];
+  uint32_t cand_key[kCandMax];
+  int32_t cand_page[kCandMax];
+  uint32_t cand_count;
+  uint32_t wsure[NW], weq[NW];  // per-wave counts of kept-for-sure keys and keys equal to the cut key
 };
 
 __device__ __forceinline__ unsigned long long share_fx(float pi) {
@@ -59,280 +67,288 @@ __device__ __forceinline__ float key_to_score(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-// Exclusive prefix (in thread order) of a 64-bit value over the workgroup; `total` = sum.
-__device__ __forceinline__ unsigned long long block_excl_scan(unsigned long long v, unsigned long long& total,
-                                                              SelectSmem& sm) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  unsigned long long inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    unsigned long long u = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += u;
-  }
-  if (lane == kWave - 1) sm.wave_tot[wave] = inc;
-  __syncthreads();
-  unsigned long long before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const unsigned long long t = w < (int)(blockDim.x / kWave) ? sm.wave_tot[w] : 0ull;
-    before += w < wave ? t : 0ull;
-    all += t;
-  }
-  __syncthreads();
-  total = all;
-  return before + inc - v;
-}
-
-// Workgroup min and max of a 32-bit key.
-__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, SelectSmem& sm) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-  }
-  if (lane == 0) { sm.wave_min[wave] = mn; sm.wave_max[wave] = mx; }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w)
-    if (w < (int)(blockDim.x / kWave)) { mn = min(mn, sm.wave_min[w]); mx = max(mx, sm.wave_max[w]); }
-  __syncthreads();
-}
-
-// One radix digit over nb bins (counts or fixed-point masses): the crossing bin is the first
-// bin, walking down from the top, where (what lies above it) + bin >= need.  Returns the bin
-// (or -1 when all bins together stay below `need`); `above` gets what lies strictly above
-// it and `inbin` the bin's own value.
-template <bool MASS>
-__device__ int radix_cross(int nb, unsigned long long need, unsigned long long& above, unsigned long long& inbin,
-                           SelectSmem& sm) {
-  const int per = (nb + (int)blockDim.x - 1) / (int)blockDim.x;  // thread 0 owns the top bins
-  const int top = nb - 1 - (int)threadIdx.x * per;
-  unsigned long long local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int bin = top - i;
-    if (bin >= 0) local += MASS ? sm.hist.mass[bin] : sm.hist.cnt[bin];
-  }
-  if (threadIdx.x == 0) sm.cross_bin = -1;
-  unsigned long long total;
-  unsigned long long cum = block_excl_scan(local, total, sm);  // synchronises
-  for (int i = 0; i < per; ++i) {
-    const int bin = top - i;
-    if (bin < 0) break;
-    const unsigned long long v = MASS ? sm.hist.mass[bin] : sm.hist.cnt[bin];
-    if (cum < need && cum + v >= need) {
-      sm.cross_bin = bin;
-      sm.cross_above = cum;
-      sm.cross_val = v;
-    }
-    cum += v;
-  }
-  __syncthreads();
-  const int bin = sm.cross_bin;
-  above = bin >= 0 ? sm.cross_above : 0ull;
-  inbin = bin >= 0 ? sm.cross_val : 0ull;
-  __syncthreads();
-  return bin;
-}
-
-// Keys of this thread's chunk of the row: cached in registers (KPT > 0) or re-read (KPT == 0).
-template <int KPT, bool COV>
-struct RowKeys {
-  const float* sc;
-  int base, cnt;
-  uint32_t k[KPT > 0 ? KPT : 1];
-  __device__ __forceinline__ void load(const float* s, int b, int c) {
-    sc = s;
-    base = b;
-    cnt = c;
-    if constexpr (KPT > 0) {
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const float v = i < cnt ? sc[base + i] : 0.f;
-        k[i] = COV ? coverage_key(v) : score_key(v);
-      }
-    }
-  }
-  __device__ __forceinline__ uint32_t operator[](int i) const {
-    if constexpr (KPT > 0) return k[i];
-    else return COV ? coverage_key(sc[base + i]) : score_key(sc[base + i]);
-  }
-  __device__ __forceinline__ int extent() const { return KPT > 0 ? KPT : cnt; }
+// The forced / free split of a row of n pages.
+struct RowShape {
+  int n;            // pages
+  int sink_end;     // forced: [0, sink_end) and [local_begin, n)
+  int local_begin;
 };
 
-// Select the pages of one dynamic row.  `sc` points at the row's scores (top-K: fp32
-// scores; coverage: shares); n is the row's page count.
-template <int KPT, bool COV>
-__device__ void select_dynamic_row(const SelectArgs& a, const float* sc, int n, size_t row, SelectSmem& sm) {
-  int32_t* out = a.page_list + row * a.max_list;
-  float* out_sc = a.sel_scores ? a.sel_scores + row * a.max_list : nullptr;
-  const int ns = max(0, a.n_sink), nl = max(0, a.n_local);
-  const int sink_end = min(ns, n);
-  const int local_begin = max(sink_end, n - nl);
-  const int n_forced = sink_end + (n - local_begin);
-  const int chunk = (n + (int)blockDim.x - 1) / (int)blockDim.x;
-  const int base = min(n, (int)threadIdx.x * chunk);
-  const int cnt = min(n, base + chunk) - base;
-  RowKeys<KPT, COV> rk;
-  rk.load(sc, base, cnt);
-  auto is_free = [&](int i) { const int p = base + i; return i < cnt && p >= sink_end && p < local_begin; };
+__device__ __forceinline__ RowShape row_shape(int n, int n_sink, int n_local) {
+  RowShape r;
+  r.n = n;
+  r.sink_end = min(max(0, n_sink), n);
+  r.local_begin = max(r.sink_end, n - max(0, n_local));
+  return r;
+}
 
-  // decision: 0 = forced only, 1 = all pages, 2 = threshold: take keys above `thr` (strict) or
-  // at-or-above it; with `strict`, also the first need_eq keys equal to thr in page order
-  int decision = 2;
-  uint32_t thr = 0;
-  bool strict = false;
-  unsigned long long need_eq = 0;
-  unsigned long long need;              // count (top-K) or mass (coverage) still to cover
+// Physical pages of a row's key slots: kept in registers for rows of up to 8 slots per lane,
+// read from the block table for the listed pages only otherwise (one more dependent load, in
+// exchange for KPL registers the long-row workgroups do not have).
+template <int KPL>
+struct SlotPhys {
+  static constexpr bool kInRegs = KPL <= 8;
+  int32_t v[kInRegs ? KPL : 1];
+  const int32_t* bt_row;  // nullable: no list of physical pages wanted
+  __device__ __forceinline__ void load(int i, int p, int n) {
+    if constexpr (kInRegs) v[i] = (bt_row && p < n) ? bt_row[p] : 0;
+  }
+  __device__ __forceinline__ int32_t at(int i, int p) const {
+    if constexpr (kInRegs) return v[i];
+    else return bt_row[p];
+  }
+};
+
+// Select the pages of one dynamic row from its keys (top-K: score_key of the scores;
+// coverage: coverage_key of the shares).  phys gives the physical page of each slot (written
+// to a.page_phys when that is set).  Every thread of the workgroup must call this.
+template <int NW, int KPL, bool COV>
+__device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint32_t (&key)[KPL],
+                                                const SlotPhys<KPL>& phys, const RowShape r, const size_t row,
+                                                SelectSmem<NW, KPL, COV>& sm) {
+  using H = typename SelectSmem<NW, KPL, COV>::H;
+  constexpr int STRIDE = NW * kWave;
+  constexpr int PER = SelectDigit<COV>::kBins / kWave;  // histogram bins summed by one lane
+  constexpr int kBits = SelectDigit<COV>::kBits;
+  constexpr int kBins = SelectDigit<COV>::kBins;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int n_free = r.local_begin - r.sink_end;
+  const int n_forced = r.n - n_free;
+  const int wbase = wave * kWave * KPL + lane;
+  auto page_of = [&](int i) { return wbase + i * kWave; };
+  auto free_at = [&](int i) { return (unsigned)(page_of(i) - r.sink_end) < (unsigned)n_free; };
+  auto forced_at = [&](int i) { const int p = page_of(i); return p < r.n && !free_at(i); };
+  auto mass_of = [&](uint32_t k) { return share_fx(__uint_as_float(k)); };
+
+  // ---- range of the free keys, forced mass (coverage); clear two histogram buffers
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  unsigned long long fmass = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    if (free_at(i)) {
+      mn = min(mn, key[i]);
+      mx = max(mx, key[i]);
+    } else if (COV && forced_at(i)) {
+      fmass += mass_of(key[i]);
+    }
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (COV) fmass = wave_sum(fmass);
+  if (lane == 0) {
+    sm.wmin[wave] = mn;
+    sm.wmax[wave] = mx;
+    sm.wsum[wave] = fmass;
+  }
+  for (int e = threadIdx.x; e < 2 * kBins; e += STRIDE) (&sm.hist[0][0])[e] = 0;
+  if (threadIdx.x == 0) sm.cand_count = 0;
+  __syncthreads();
+  mn = sm.wmin[0];
+  mx = sm.wmax[0];
+  fmass = sm.wsum[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    mn = min(mn, sm.wmin[w]);
+    mx = max(mx, sm.wmax[w]);
+    fmass += sm.wsum[w];
+  }
+
+  // ---- decision: 0 = forced pages only, 1 = every page, 2 = cut at key kc: keys above kc are
+  // kept, keys equal to kc are kept in page order while fewer than need_eq of them were taken.
+  int dec;
+  unsigned long long need;  // count (top-K) or mass (coverage) still to cover
   if (!COV) {
     const int kp = a.budget - n_forced;
-    if (kp <= 0) decision = 0;
-    else if (n - n_forced <= kp) decision = 1;
+    dec = kp <= 0 ? 0 : (n_free <= kp ? 1 : 2);
     need = kp > 0 ? (unsigned long long)kp : 0ull;
   } else {
-    unsigned long long fm = 0;
-#pragma unroll
-    for (int i = 0; i < rk.extent(); ++i) {
-      const int p = base + i;
-      if (i < cnt && !(p >= sink_end && p < local_begin)) fm += share_fx(__uint_as_float(rk[i]));
-    }
-    unsigned long long fm_all;
-    block_excl_scan(fm, fm_all, sm);
-    if (fm_all >= a.gamma_fx) decision = 0;
-    need = fm_all >= a.gamma_fx ? 0ull : a.gamma_fx - fm_all;
+    dec = (n_free == 0 || fmass >= a.gamma_fx) ? 0 : 2;
+    need = dec == 2 ? a.gamma_fx - fmass : 0ull;
   }
-
-  if (decision == 2) {
-    // common high bits of the free keys
-    uint32_t mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-    for (int i = 0; i < rk.extent(); ++i)
-      if (is_free(i)) { mn = min(mn, rk[i]); mx = max(mx, rk[i]); }
-    block_minmax(mn, mx, sm);
-    uint32_t prefix, pmask;
-    int hi;
-    if (mn == mx) {  // every free key is equal: one "digit" of zero width
-      prefix = mx;
-      pmask = 0xffffffffu;
-      hi = -1;
+  uint32_t kc = 0;
+  int need_eq = kNoLimit;
+  if (dec == 2) {
+    if (mn == mx) {
+      // every free key is equal: top-K takes them in page order; coverage keeps them all (they
+      // either reach t together, or nothing does and every page is kept)
+      kc = mx;
+      need_eq = COV ? kNoLimit : (int)need;
     } else {
-      hi = 31 - __clz(mn ^ mx);
-      pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
-      prefix = mx & pmask;
-    }
-    bool exact = true;  // the walk reached bit 0 (or all keys share their bits)
-    if (COV && hi < 0) {
-      // all free shares are equal: they reach t together or not at all
-      unsigned long long tot = 0;
+      int hi = 31 - __clz(mn ^ mx);  // digits start below the bits every free key shares
+      uint32_t pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+      uint32_t prefix = mx & pmask;
+      for (int pass = 0;; ++pass) {
+        const int shift = hi > kBits - 1 ? hi - (kBits - 1) : 0;
+        const int nb = 1 << (hi - shift + 1);
+        H* h = sm.hist[pass % 3];
 #pragma unroll
-      for (int i = 0; i < rk.extent(); ++i)
-        if (is_free(i)) tot += share_fx(__uint_as_float(rk[i]));
-      unsigned long long all;
-      block_excl_scan(tot, all, sm);
-      if (all < need) decision = 1;
-    }
-    while (hi >= 0 && decision == 2) {
-      const int shift = hi > 10 ? hi - 10 : 0;
-      const int nb = 1 << (hi - shift + 1);
-      for (int i = threadIdx.x; i < nb; i += blockDim.x) {
-        if (COV) sm.hist.mass[i] = 0ull;
-        else sm.hist.cnt[i] = 0u;
-      }
-      __syncthreads();
+        for (int i = 0; i < KPL; ++i) {
+          if (free_at(i) && (key[i] & pmask) == prefix) {
+            // bins are stored from the top: slot kBins - 1 - bin
+            const int rbin = kBins - 1 - (int)((key[i] >> shift) & (uint32_t)(nb - 1));
+            if (COV) atomicAdd(reinterpret_cast<unsigned long long*>(&h[rbin]), mass_of(key[i]));
+            else atomicAdd(reinterpret_cast<uint32_t*>(&h[rbin]), 1u);
+          }
+        }
+        __syncthreads();
+        {  // the buffer of pass + 2 was last read in pass - 1, which every wave finished before the barrier
+          H* hc = sm.hist[(pass + 2) % 3];
+          for (int e = threadIdx.x; e < kBins; e += STRIDE) hc[e] = 0;
+        }
+        // crossing bin, found by every wave: lane l sums slots [l PER, (l+1) PER) (the l-th group
+        // from the top), reading them in a lane-skewed order so the wave's reads hit distinct banks
+        H s = 0;
 #pragma unroll
-      for (int i = 0; i < rk.extent(); ++i) {
-        const uint32_t key = rk[i];
-        if (is_free(i) && (key & pmask) == prefix) {
-          const int bin = (int)((key >> shift) & (uint32_t)(nb - 1));
-          if (COV) atomicAdd(&sm.hist.mass[bin], share_fx(__uint_as_float(key)));
-          else atomicAdd(&sm.hist.cnt[bin], 1u);
+        for (int j = 0; j < PER; ++j) s += h[lane * PER + ((j + lane) % PER)];
+        const H incl = wave_incl_scan(s);
+        const H excl = incl - s;
+        const unsigned long long hit = __ballot(excl < need && incl >= need);
+        if (hit == 0ull) {  // coverage only: the free pages cannot reach t -- keep every page
+          dec = 1;
+          break;
+        }
+        const int owner = __ffsll((long long)hit) - 1;
+        H owner_excl;
+        if constexpr (COV) owner_excl = lane_u64(excl, owner);
+        else owner_excl = lane_u32(excl, owner);
+        // inside the owner's group: lane j < PER takes slot owner PER + j
+        const H v = lane < PER ? h[owner * PER + lane] : (H)0;
+        const H incl2 = wave_incl_scan(v) + owner_excl;
+        const unsigned long long hit2 = __ballot(lane < PER && incl2 - v < need && incl2 >= need);
+        const int jc = __ffsll((long long)hit2) - 1;
+        const int bin = kBins - 1 - (owner * PER + jc);
+        H above, inbin;
+        if constexpr (COV) {
+          above = lane_u64(incl2 - v, jc);
+          inbin = lane_u64(v, jc);
+        } else {
+          above = lane_u32(incl2 - v, jc);
+          inbin = lane_u32(v, jc);
+        }
+        need -= above;
+        prefix |= (uint32_t)bin << shift;
+        pmask |= (uint32_t)(nb - 1) << shift;
+        hi = shift - 1;
+        if (hi < 0) {  // every bit chosen: prefix is the cut key itself
+          kc = prefix;
+          need_eq = COV ? kNoLimit : (int)need;
+          break;
+        }
+        if (!COV && inbin == need) {  // the whole crossing bin is taken
+          kc = prefix;
+          need_eq = kNoLimit;
+          break;
+        }
+        if (!COV && inbin <= (H)kCandMax) {
+          // few keys left in the bin: gather them, and let each wave rank them itself
+          uint32_t c = 0;
+#pragma unroll
+          for (int i = 0; i < KPL; ++i) c += (free_at(i) && (key[i] & pmask) == prefix) ? 1u : 0u;
+          const uint32_t cincl = wave_incl_scan(c);
+          const uint32_t wtot = lane_u32(cincl, kWave - 1);
+          uint32_t base = 0;
+          if (lane == 0 && wtot) base = atomicAdd(&sm.cand_count, wtot);
+          uint32_t pos = lane_u32(base, 0) + cincl - c;
+#pragma unroll
+          for (int i = 0; i < KPL; ++i) {
+            if (free_at(i) && (key[i] & pmask) == prefix) {
+              sm.cand_key[pos] = key[i];
+              sm.cand_page[pos] = page_of(i);
+              ++pos;
+            }
+          }
+          __syncthreads();
+          const int m = (int)sm.cand_count;  // == inbin
+          const uint32_t ck = lane < m ? sm.cand_key[lane] : 0u;
+          const int cp = lane < m ? sm.cand_page[lane] : 0x7fffffff;
+          int rank = 0;
+          for (int j = 0; j < m; ++j) {
+            const uint32_t kj = sm.cand_key[j];
+            const int pj = sm.cand_page[j];
+            rank += (kj > ck || (kj == ck && pj < cp)) ? 1 : 0;
+          }
+          const unsigned long long cut = __ballot(lane < m && rank == (int)need - 1);
+          kc = lane_u32(ck, __ffsll((long long)cut) - 1);
+          const int above_cut = __popcll(__ballot(lane < m && ck > kc));
+          need_eq = (int)need - above_cut;
+          break;
         }
       }
-      __syncthreads();
-      unsigned long long above, inbin;
-      const int bin = radix_cross<COV>(nb, need, above, inbin, sm);
-      if (bin < 0) { decision = 1; break; }  // coverage: the free pages cannot reach t: keep all
-      need -= above;
-      prefix |= (uint32_t)bin << shift;
-      pmask |= (uint32_t)(nb - 1) << shift;
-      hi = shift - 1;
-      if (!COV && inbin == need && hi >= 0) {  // the whole crossing bin is taken: stop early
-        exact = false;
-        break;
-      }
-    }
-    thr = prefix;
-    if (!COV && exact) {  // prefix is the K'-th key: all keys above it, then ties in page order
-      strict = true;
-      need_eq = need;
     }
   }
 
-  // compaction: per-thread counts, one scan each for ties (rare) and kept pages
-  unsigned long long eq_before = 0;
-  if (decision == 2 && strict) {
-    unsigned long long e = 0, all;
-#pragma unroll
-    for (int i = 0; i < rk.extent(); ++i)
-      if (is_free(i) && rk[i] == thr) ++e;
-    eq_before = block_excl_scan(e, all, sm);
+  // ---- compaction in ascending page order.  Decisions 0 and 1 become cuts that no free key
+  // passes (every key is below 0xffffffff) or that every free key passes.
+  if (dec == 0) {
+    kc = 0xffffffffu;
+    need_eq = 0;
+  } else if (dec == 1) {
+    kc = 0u;
+    need_eq = kNoLimit;
   }
-  auto keep = [&](int i, unsigned long long& eq_seen) {
-    if (i >= cnt) return false;
-    if (!is_free(i)) return true;  // forced
-    if (decision == 0) return false;
-    if (decision == 1) return true;
-    const uint32_t key = rk[i];
-    if (strict ? key > thr : key >= thr) return true;
-    if (strict && key == thr) return eq_seen++ < need_eq;
-    return false;
+  auto take_sure = [&](int i) {
+    const bool fr = free_at(i);
+    return (page_of(i) < r.n && !fr) || (fr && key[i] > kc);
   };
-  unsigned long long mine = 0, total;
-  {
-    unsigned long long eq_seen = eq_before;
+  auto take_eq = [&](int i) { return free_at(i) && key[i] == kc; };
+  uint32_t sure_l = 0, eq_l = 0;  // per lane, then summed over the wave
 #pragma unroll
-    for (int i = 0; i < rk.extent(); ++i) mine += keep(i, eq_seen) ? 1ull : 0ull;
+  for (int i = 0; i < KPL; ++i) {
+    sure_l += take_sure(i) ? 1u : 0u;
+    eq_l += take_eq(i) ? 1u : 0u;
   }
-  unsigned long long pos = block_excl_scan(mine, total, sm);
-  {
-    unsigned long long eq_seen = eq_before;
+  const uint32_t sure_w = wave_sum(sure_l), eq_w = wave_sum(eq_l);
+  if (lane == 0) {
+    sm.wsure[wave] = sure_w;
+    sm.weq[wave] = eq_w;
+  }
+  __syncthreads();
+  uint32_t sure_before = 0, eq_before = 0, sure_total = 0, eq_total = 0;
 #pragma unroll
-    for (int i = 0; i < rk.extent(); ++i) {
-      if (keep(i, eq_seen)) {
-        if (pos < (unsigned long long)a.max_list) {
-          out[pos] = base + i;
-          if (out_sc) out_sc[pos] = COV ? __uint_as_float(rk[i]) : key_to_score(rk[i]);
-        }
-        ++pos;
-      }
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t sw = sm.wsure[w], ew = sm.weq[w];
+    sure_before += w < wave ? sw : 0u;
+    eq_before += w < wave ? ew : 0u;
+    sure_total += sw;
+    eq_total += ew;
+  }
+  const uint32_t ne = (uint32_t)need_eq;
+  uint32_t pos = sure_before + min(eq_before, ne);              // first list position of this wave
+  const uint32_t total = sure_total + min(eq_total, ne);
+  int eq_left = eq_before < ne ? (int)(ne - eq_before) : 0;     // equal keys this wave may take
+
+  int32_t* out = a.page_list + row * a.max_list;
+  int32_t* out_phys = a.page_phys ? a.page_phys + row * a.max_list : nullptr;
+  float* out_sc = a.sel_scores ? a.sel_scores + row * a.max_list : nullptr;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const unsigned long long eq_mask = __ballot(take_eq(i));
+    const bool take = take_sure(i) || (take_eq(i) && (int)lanes_below(eq_mask) < eq_left);
+    const unsigned long long take_mask = __ballot(take);
+    const uint32_t q = pos + lanes_below(take_mask);
+    if (take && q < (uint32_t)a.max_list) {
+      out[q] = page_of(i);
+      if (out_phys) out_phys[q] = phys.at(i, page_of(i));
+      if (out_sc) out_sc[q] = COV ? __uint_as_float(key[i]) : key_to_score(key[i]);
     }
+    pos += (uint32_t)__popcll(take_mask);
+    eq_left -= __popcll(eq_mask);
+    __builtin_amdgcn_sched_barrier(0);  // one slot at a time: keeps the slot's two ballots the only live masks
   }
-  if (threadIdx.x == 0) a.list_len[row] = (int)min(total, (unsigned long long)a.max_list);
+  if (threadIdx.x == 0) a.list_len[row] = (int)min(total, (uint32_t)a.max_list);
 }
 
 // A streaming row keeps its static sink + local table.
-__device__ __forceinline__ void select_streaming_row(const SelectArgs& a, int n, size_t row) {
+__device__ __forceinline__ void select_streaming_row(const SelectArgs& a, int n, size_t row, const int32_t* bt_row) {
   int32_t* out = a.page_list + row * a.max_list;
-  const int sink_end = min(max(0, a.n_sink_stream), n);
-  const int local_begin = max(sink_end, n - max(0, a.n_local_stream));
-  const int n_forced = sink_end + (n - local_begin);
-  for (int i = threadIdx.x; i < n_forced && i < a.max_list; i += blockDim.x)
-    out[i] = i < sink_end ? i : local_begin + (i - sink_end);
+  const RowShape r = row_shape(n, a.n_sink_stream, a.n_local_stream);
+  const int n_forced = r.sink_end + (n - r.local_begin);
+  for (int i = threadIdx.x; i < n_forced && i < a.max_list; i += blockDim.x) {
+    const int p = i < r.sink_end ? i : r.local_begin + (i - r.sink_end);
+    out[i] = p;
+    if (a.page_phys) a.page_phys[row * a.max_list + i] = bt_row[p];
+  }
   if (threadIdx.x == 0) a.list_len[row] = min(n_forced, a.max_list);
-}
-
-template <int KPT>
-__device__ __forceinline__ void select_row(const SelectArgs& a, const float* sc, int n, size_t row, bool streaming,
-                                           SelectSmem& sm) {
-  if (streaming) select_streaming_row(a, n, row);
-  else if (a.mode == SPD_SELECT_COVERAGE) select_dynamic_row<KPT, true>(a, sc, n, row, sm);
-  else select_dynamic_row<KPT, false>(a, sc, n, row, sm);
-}
-
-// Keys per thread to compile for rows of up to max_pages pages with kSelThreads threads
-// (0: re-read them from memory for every pass -- rows beyond 32768 pages).
-__host__ __device__ constexpr int select_kpt(int max_pages) {
-  return max_pages <= kSelThreads * 8 ? 8 : max_pages <= kSelThreads * 32 ? 32 : 0;
 }
 
 }  // namespace spd

@@ -202,12 +202,15 @@ struct PageRef {
   int valid;  // valid tokens
 };
 
-__device__ __forceinline__ PageRef resolve_page(const DecodeArgs& a, const int32_t* list, int i, int b, int n_b,
-                                                int len) {
+// List entry i of a row: its logical page and, from the list of physical pages when the
+// selector wrote one (no block-table read) or else from the block table, its physical page.
+__device__ __forceinline__ PageRef resolve_page(const DecodeArgs& a, const int32_t* list, const int32_t* plist, int i,
+                                                int b, int n_b, int len) {
   PageRef r{-1, 0, 0};
   const int p = list[i];
+  const int pp = plist ? plist[i] : 0;
   if (p < 0 || p >= n_b) return r;
-  const int phys = a.block_table[(size_t)b * a.max_pages + p];
+  const int phys = plist ? pp : a.block_table[(size_t)b * a.max_pages + p];
   if (phys < 0 || phys >= a.num_pool_pages) return r;
   r.page = p;
   r.phys = phys;
@@ -251,6 +254,7 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   const int len = a.seq_lens[b];
   const int n_b = row_pages(len, a.max_pages);
   const int32_t* list = a.page_list + (size_t)row * a.max_list;
+  const int32_t* plist = a.page_phys ? a.page_phys + (size_t)row * a.max_list : nullptr;
 
   typename T::Q q;
   T::load_q(q, a.q, qrow * D, quarter);
@@ -329,15 +333,15 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   typename T::VF va, vb;
   float ksa = 1.f, vsa = 1.f, ksb = 1.f, vsb = 1.f;
   int i = i0 + wave;
-  PageRef ra = i < i1 ? resolve_page(a, list, i, b, n_b, len) : none;
+  PageRef ra = i < i1 ? resolve_page(a, list, plist, i, b, n_b, len) : none;
   load(ra, ka, va, ksa, vsa);
   while (i < i1) {
-    const PageRef rb = i + 4 < i1 ? resolve_page(a, list, i + 4, b, n_b, len) : none;
+    const PageRef rb = i + 4 < i1 ? resolve_page(a, list, plist, i + 4, b, n_b, len) : none;
     load(rb, kb, vb, ksb, vsb);
     process(ra, ka, va, ksa, vsa);
     i += 4;
     if (i >= i1) break;
-    ra = i + 4 < i1 ? resolve_page(a, list, i + 4, b, n_b, len) : none;
+    ra = i + 4 < i1 ? resolve_page(a, list, plist, i + 4, b, n_b, len) : none;
     load(ra, ka, va, ksa, vsa);
     process(rb, kb, vb, ksb, vsb);
     i += 4;

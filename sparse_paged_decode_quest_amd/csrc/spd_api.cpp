@@ -15,18 +15,22 @@
 namespace {
 
 // pages per scoring workgroup (fixed by the compiled work layouts)
-int score_ppb(const spd_desc* d, bool fused = false) {
-  const int mb = d->kv_dtype == SPD_DTYPE_F32 ? 4 : 2;
-  return fused ? spd::score_pages_per_block(d->head_dim, mb, spd::kFusedWaves, spd::kFusedIters)
-               : spd::score_pages_per_block(d->head_dim, mb, spd::kScoreWaves, spd::kScoreIters);
+int meta_bytes_of(const spd_desc* d) { return d->kv_dtype == SPD_DTYPE_F32 ? 4 : 2; }
+
+int score_ppb(const spd_desc* d) {
+  return spd::score_pages_per_block(d->head_dim, meta_bytes_of(d), spd::kScoreWaves, spd::kScoreIters);
 }
+
+int fused_ppb(const spd_desc* d, const spd::SelectGeometry& g) {
+  return spd::score_pages_per_block(d->head_dim, meta_bytes_of(d), g.nw, g.iters);
+}
+
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool is_dtype(int v) { return v == SPD_DTYPE_F32 || v == SPD_DTYPE_F16 || v == SPD_DTYPE_FP8_E4M3FN; }
 
-int meta_dtype_of(int kv) { return kv == SPD_DTYPE_F32 ? SPD_DTYPE_F32 : SPD_DTYPE_F16; }
 
 int check_desc(const spd_desc* d) {
   if (!d) return SPD_ERR_INVALID_ARG;
@@ -116,20 +120,29 @@ ScoreWs score_ws(const spd_desc* d) {
 }
 
 struct FusedWs {
-  size_t scores_off, counters_off, total;
+  size_t scores_off, part_off, counters_off, total;
+  int ppb;
 };
 
-FusedWs fused_ws(const spd_desc* d) {
+// Fused workspace: top-K scores (or coverage log-masses of the G heads), coverage workgroup
+// partials, one ticket counter per row.
+bool fused_ws(const spd_desc* d, const spd_select_params* s, FusedWs& w) {
+  spd::SelectGeometry g;
+  if (!spd::select_geometry(d->max_pages_per_seq, g)) return false;
   const size_t rows = (size_t)d->batch * d->num_kv_heads;
-  FusedWs w;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const bool cov = s->mode == SPD_SELECT_COVERAGE;
+  w.ppb = fused_ppb(d, g);
+  const size_t bpr = (d->max_pages_per_seq + w.ppb - 1) / w.ppb;
   w.scores_off = 0;
-  w.counters_off = align_up(rows * d->max_pages_per_seq * sizeof(float));
+  w.part_off = align_up(rows * d->max_pages_per_seq * (cov ? G : 1) * sizeof(float));
+  w.counters_off = w.part_off + (cov ? align_up(rows * bpr * G * 2 * sizeof(float)) : 0);
   w.total = w.counters_off + align_up(rows * sizeof(uint32_t));
-  return w;
+  return true;
 }
 
 spd::ScoreArgs score_args(const spd_desc* d, const spd_select_params* s, const void* q, const void* meta,
-                          const int32_t* bt, const int32_t* sl, const spd::HeadList& dyn, bool fused = false) {
+                          const int32_t* bt, const int32_t* sl, const spd::HeadList& dyn, int ppb) {
   spd::ScoreArgs a{};
   a.q = q;
   a.meta = meta;
@@ -141,17 +154,19 @@ spd::ScoreArgs score_args(const spd_desc* d, const spd_select_params* s, const v
   a.num_kv_heads = d->num_kv_heads;
   a.max_pages = d->max_pages_per_seq;
   a.num_pool_pages = d->num_pool_pages;
-  a.pages_per_block = score_ppb(d, fused);
-  a.blocks_per_row = (d->max_pages_per_seq + a.pages_per_block - 1) / a.pages_per_block;
+  a.pages_per_block = ppb;
+  a.blocks_per_row = (d->max_pages_per_seq + ppb - 1) / ppb;
   a.sm_scale = s->sm_scale;
   return a;
 }
 
-spd::SelectArgs select_args(const spd_desc* d, const spd_select_params* s, const int32_t* sl, int32_t* list,
-                            int32_t* len, float* sel_scores, uint64_t mask) {
+spd::SelectArgs select_args(const spd_desc* d, const spd_select_params* s, const int32_t* sl, const int32_t* bt,
+                            int32_t* list, int32_t* phys, int32_t* len, float* sel_scores, uint64_t mask) {
   spd::SelectArgs a{};
   a.seq_lens = sl;
+  a.block_table = bt;
   a.page_list = list;
+  a.page_phys = phys;
   a.list_len = len;
   a.sel_scores = sel_scores;
   a.streaming_mask = mask;
@@ -226,7 +241,10 @@ size_t spd_workspace_bytes(const spd_desc* desc, const spd_select_params* sel, i
   switch (op) {
     case SPD_OP_PAGE_SCORE: return sel->mode == SPD_SELECT_COVERAGE ? score_ws(desc).total : 0;
     case SPD_OP_PAGE_SELECT: return 0;
-    case SPD_OP_PAGE_SCORE_SELECT: return fused_ws(desc).total;
+    case SPD_OP_PAGE_SCORE_SELECT: {
+      FusedWs w;
+      return fused_ws(desc, sel, w) ? w.total : (size_t)-1;
+    }
     default: return (size_t)-1;
   }
 }
@@ -268,72 +286,86 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
   if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
   if (desc->batch == 0 || dyn.count == 0) return SPD_OK;
   if (!q || !page_meta || !block_table || !seq_lens || !scores) return SPD_ERR_INVALID_ARG;
-  spd::ScoreArgs a = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn);
+  spd::ScoreArgs a = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, score_ppb(desc));
   a.scores = scores;
   const bool coverage = sel->mode == SPD_SELECT_COVERAGE;
   if (coverage) {
     if (!head_lse) return SPD_ERR_INVALID_ARG;
     const ScoreWs w = score_ws(desc);
     if (!workspace || workspace_bytes < w.total) return SPD_ERR_WORKSPACE;
-    a.ell = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.ell_off);
+    a.ell = reinterpret_cast<float4*>(static_cast<char*>(workspace) + w.ell_off);
     a.partials = reinterpret_cast<float2*>(static_cast<char*>(workspace) + w.part_off);
     a.head_lse = head_lse;
   }
-  return launched(spd::launch_page_score(a, desc->head_dim, desc->q_dtype, meta_dtype_of(desc->kv_dtype), coverage,
-                                         (hipStream_t)stream));
+  return launched(spd::launch_page_score(a, desc->head_dim, desc->kv_dtype, coverage, (hipStream_t)stream));
 }
 
 int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const float* scores,
-                    const int32_t* seq_lens, const uint8_t* head_kind, int32_t* page_list, int32_t* list_len,
-                    float* sel_scores, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+                    const int32_t* seq_lens, const uint8_t* head_kind, const int32_t* block_table,
+                    int32_t* page_list, int32_t* page_phys, int32_t* list_len, float* sel_scores, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if ((rc = check_sel(desc, sel))) return rc;
   if ((rc = check_list_capacity(desc, sel))) return rc;
+  spd::SelectGeometry g;
+  if (!spd::select_geometry(desc->max_pages_per_seq, g)) return SPD_ERR_UNSUPPORTED;
   spd::HeadList dyn, strm;
   uint64_t mask;
   if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
   if (desc->batch == 0) return SPD_OK;
   if (!seq_lens || !page_list || !list_len || (dyn.count > 0 && !scores)) return SPD_ERR_INVALID_ARG;
-  spd::SelectArgs a = select_args(desc, sel, seq_lens, page_list, list_len, sel_scores, mask);
+  if (page_phys && !block_table) return SPD_ERR_INVALID_ARG;
+  spd::SelectArgs a = select_args(desc, sel, seq_lens, block_table, page_list, page_phys, list_len, sel_scores, mask);
   a.scores = scores;
   return launched(spd::launch_page_select(a, (hipStream_t)stream));
 }
 
-int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, const void* q, const void* page_meta,
+int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, const void* q, void* page_meta,
+                          const void* k_pool, const uint16_t* k_scale, int32_t refresh_tail,
                           const int32_t* block_table, const int32_t* seq_lens, const uint8_t* head_kind,
-                          int32_t* page_list, int32_t* list_len, float* sel_scores, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          int32_t* page_list, int32_t* page_phys, int32_t* list_len, float* sel_scores, float* scores,
+                          float* head_lse, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if ((rc = check_sel(desc, sel))) return rc;
-  if (sel->mode != SPD_SELECT_TOPK) return SPD_ERR_UNSUPPORTED;
   if ((rc = check_list_capacity(desc, sel))) return rc;
+  FusedWs w;
+  if (!fused_ws(desc, sel, w)) return SPD_ERR_UNSUPPORTED;
   spd::HeadList dyn, strm;
   uint64_t mask;
   if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
   if (desc->batch == 0) return SPD_OK;
-  if (!seq_lens || !page_list || !list_len) return SPD_ERR_INVALID_ARG;
-  if (dyn.count > 0 && (!q || !page_meta || !block_table)) return SPD_ERR_INVALID_ARG;
-  const FusedWs w = fused_ws(desc);
+  if (!seq_lens || !page_list || !list_len || !block_table) return SPD_ERR_INVALID_ARG;
+  if (dyn.count > 0 && (!q || !page_meta)) return SPD_ERR_INVALID_ARG;
+  if (refresh_tail && (!k_pool || (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale))) return SPD_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < w.total) return SPD_ERR_WORKSPACE;
+  const bool cov = sel->mode == SPD_SELECT_COVERAGE;
+  char* ws = static_cast<char*>(workspace);
   spd::FusedArgs f{};
-  f.score = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, true);
-  f.score.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.scores_off);
-  f.sel = select_args(desc, sel, seq_lens, page_list, list_len, sel_scores, mask);
+  f.score = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, w.ppb);
+  f.score.meta_out = page_meta;
+  f.score.k_pool = k_pool;
+  f.score.k_scale = k_scale;
+  f.score.refresh_tail = refresh_tail ? 1 : 0;
+  if (cov) {
+    f.score.ell = reinterpret_cast<float4*>(ws + w.scores_off);
+    f.score.partials = reinterpret_cast<float2*>(ws + w.part_off);
+    f.score.head_lse = head_lse;
+    f.score_out = scores;
+  } else {
+    f.score.scores = scores ? scores : reinterpret_cast<float*>(ws + w.scores_off);
+  }
+  f.sel = select_args(desc, sel, seq_lens, block_table, page_list, page_phys, list_len, sel_scores, mask);
   f.stream_heads = strm;
-  f.counters = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + w.counters_off);
-  return launched(spd::launch_page_score_select(f, desc->head_dim, desc->q_dtype, meta_dtype_of(desc->kv_dtype),
-                                                (hipStream_t)stream));
+  f.counters = reinterpret_cast<unsigned int*>(ws + w.counters_off);
+  return launched(spd::launch_page_score_select(f, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
 }
 
 int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, const void* q, const void* k_pool,
                             const void* v_pool, const uint16_t* k_scale, const uint16_t* v_scale,
                             const int32_t* block_table, const int32_t* seq_lens, const int32_t* page_list,
-                            const int32_t* list_len, float sm_scale, float* out, float* out_lse, float* part_o,
-                            float* part_lse, void* stream) {
+                            const int32_t* page_phys, const int32_t* list_len, float sm_scale, float* out,
+                            float* out_lse, float* part_o, float* part_lse, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   int32_t J;
@@ -353,6 +385,7 @@ int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, c
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.page_list = page_list;
+  a.page_phys = page_phys;
   a.list_len = list_len;
   a.out = out;
   a.out_lse = out_lse;

@@ -76,6 +76,96 @@ __device__ __forceinline__ float xor_sum(float v) {
   return v;
 }
 
+// Cross-lane moves through DPP (data-parallel primitives of the gfx9 vector ALU): a lane reads
+// another lane's register in the same instruction, without the LDS crossbar that __shfl uses.
+// Lanes whose source is out of range, or that the row / bank masks leave unwritten, get 0.
+// Controls: quad_perm(1,0,3,2) = 0xb1, quad_perm(2,3,0,1) = 0x4e, row_shr:k = 0x110 + k,
+// row_mirror = 0x140, row_half_mirror = 0x141, row_bcast:15 = 0x142, row_bcast:31 = 0x143.
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int lane) {
+  return (unsigned long long)lane_u32((uint32_t)v, lane) | ((unsigned long long)lane_u32((uint32_t)(v >> 32), lane) << 32);
+}
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each row of 16 lanes, then the
+// row totals are carried across rows with the two row broadcasts.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp<0x111>(v);
+  v += dpp<0x112>(v);
+  v += dpp<0x114>(v);
+  v += dpp<0x118>(v);
+  v += dpp<0x142, 0xa>(v);
+  v += dpp<0x143, 0xc>(v);
+  return v;
+}
+
+// 64-bit version: the two halves move with the same control, the carry is added back.
+__device__ __forceinline__ unsigned long long add_u64_halves(unsigned long long a, uint32_t lo, uint32_t hi) {
+  const uint32_t alo = (uint32_t)a, ahi = (uint32_t)(a >> 32);
+  const uint32_t rlo = alo + lo;
+  const uint32_t rhi = ahi + hi + (rlo < alo ? 1u : 0u);
+  return (unsigned long long)rlo | ((unsigned long long)rhi << 32);
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ unsigned long long dpp_add_u64(unsigned long long v) {
+  return add_u64_halves(v, dpp<CTRL, ROW_MASK>((uint32_t)v), dpp<CTRL, ROW_MASK>((uint32_t)(v >> 32)));
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_scan(unsigned long long v) {
+  v = dpp_add_u64<0x111>(v);
+  v = dpp_add_u64<0x112>(v);
+  v = dpp_add_u64<0x114>(v);
+  v = dpp_add_u64<0x118>(v);
+  v = dpp_add_u64<0x142, 0xa>(v);
+  v = dpp_add_u64<0x143, 0xc>(v);
+  return v;
+}
+
+// Reductions whose result every lane receives: a butterfly inside each row of 16 lanes (two quad
+// permutations and two mirrors, every lane has a source), then the four row results are read as
+// scalars.  OP is an associative, commutative binary functor.
+template <typename OP>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, OP op) {
+  v = op(v, dpp<0xb1>(v));
+  v = op(v, dpp<0x4e>(v));
+  v = op(v, dpp<0x141>(v));
+  v = op(v, dpp<0x140>(v));
+  return op(op(lane_u32(v, 0), lane_u32(v, 16)), op(lane_u32(v, 32), lane_u32(v, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+__device__ __forceinline__ unsigned long long wave_sum(unsigned long long v) {
+  v = add_u64_halves(v, dpp<0xb1>((uint32_t)v), dpp<0xb1>((uint32_t)(v >> 32)));
+  v = add_u64_halves(v, dpp<0x4e>((uint32_t)v), dpp<0x4e>((uint32_t)(v >> 32)));
+  v = add_u64_halves(v, dpp<0x141>((uint32_t)v), dpp<0x141>((uint32_t)(v >> 32)));
+  v = add_u64_halves(v, dpp<0x140>((uint32_t)v), dpp<0x140>((uint32_t)(v >> 32)));
+  return lane_u64(v, 0) + lane_u64(v, 16) + lane_u64(v, 32) + lane_u64(v, 48);
+}
+
+// Lanes below this one whose bit is set in `mask` (a 64-lane ballot).
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 __device__ __forceinline__ float fmax_nan_safe(float a, float b) { return a > b ? a : b; }
 
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key); NaN -> 0.

@@ -9,6 +9,26 @@
 
 namespace spd {
 
+// Scoring workgroups: NW waves, each with ITERS groups of pages (score_common.h).
+constexpr int kScoreWaves = 4, kScoreIters = 4;  // standalone scorer
+
+// Selection workgroup shape for rows of up to max_pages pages (select_row.h): NW waves with
+// KPL key slots per lane; the fused score + select kernel scores with the same workgroup and
+// `iters` page groups per lane.  Returns false when rows are too long to select.
+struct SelectGeometry {
+  int nw, kpl, iters;
+};
+inline bool select_geometry(int max_pages, SelectGeometry& g) {
+  // 16 waves: a row's selection is a chain of short dependent steps per key slot, so four waves
+  // per SIMD hide each other's latencies; the scoring part covers 128 pages per workgroup (f16 d128)
+  if (max_pages <= 16 * 64 * 2) g = {16, 2, 2};
+  else if (max_pages <= 16 * 64 * 8) g = {16, 8, 2};
+  else if (max_pages <= 16 * 64 * 32) g = {16, 32, 2};
+  else if (max_pages <= 16 * 64 * 64) g = {16, 64, 4};
+  else return false;
+  return true;
+}
+
 struct MetaArgs {
   const void* k_pool;
   const uint16_t* k_scale;
@@ -31,25 +51,30 @@ struct HeadList {
 struct ScoreArgs {
   const void* q;
   const void* meta;
+  void* meta_out;            // tail refresh target (fused path; the same buffer as meta)
+  const void* k_pool;        // tail refresh source (fused path)
+  const uint16_t* k_scale;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* scores;       // [B, Hkv, max_pages]
-  float* ell;          // coverage: [B, Hkv, max_pages, G] log-masses
-  float2* partials;    // coverage: [B, Hkv, blocks_per_row, G] (max, sum of exp)
-  float* head_lse;     // coverage: [B, Hq]
+  float* scores;             // top-K: [B, Hkv, max_pages]; coverage: shares (nullable when fused)
+  float4* ell;               // coverage: [B, Hkv, max_pages] log-masses of the G heads
+  float2* partials;          // coverage: [B, Hkv, blocks_per_row, G] (max, sum of exp)
+  float* head_lse;           // coverage: [B, Hq] (nullable when fused)
   HeadList dyn;
   int batch, num_q_heads, num_kv_heads, max_pages, num_pool_pages;
-  int blocks_per_row;  // workgroups per (request, dynamic head)
+  int blocks_per_row;        // workgroups per (request, dynamic head)
   int pages_per_block;
   float sm_scale;
+  int refresh_tail;          // fused path: rebuild each dynamic row's last page from k_pool
 };
-int launch_page_score(const ScoreArgs& a, int head_dim, int q_dtype, int meta_dtype, bool coverage,
-                      hipStream_t stream);
+int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool coverage, hipStream_t stream);
 
 struct SelectArgs {
-  const float* scores;      // [B, Hkv, max_pages] (fused: workspace copy)
+  const float* scores;      // [B, Hkv, max_pages] (top-K scores or coverage shares)
   const int32_t* seq_lens;
+  const int32_t* block_table;  // read when page_phys is set
   int32_t* page_list;       // [B, Hkv, max_list]
+  int32_t* page_phys;       // [B, Hkv, max_list] physical pages of the list (nullable)
   int32_t* list_len;        // [B, Hkv]
   float* sel_scores;        // nullable
   uint64_t streaming_mask;  // bit h set: KV head h is a streaming head
@@ -61,13 +86,13 @@ struct SelectArgs {
 int launch_page_select(const SelectArgs& a, hipStream_t stream);
 
 struct FusedArgs {
-  ScoreArgs score;         // score.scores -> workspace rows [B, Hkv, max_pages]
-  SelectArgs sel;          // sel.scores unused (the rows above are selected)
+  ScoreArgs score;         // score.scores / score.ell / score.partials -> workspace
+  SelectArgs sel;          // sel.scores unused; shares are written to score_out when set
+  float* score_out;        // optional copy of the row scores (top-K) or shares (coverage) [B, Hkv, max_pages]
   HeadList stream_heads;   // streaming heads: one extra block per (request, head)
   unsigned int* counters;  // [B, Hkv] finished-block tickets (workspace, zero between calls)
 };
-int launch_page_score_select(const FusedArgs& a, int head_dim, int q_dtype, int meta_dtype,
-                             hipStream_t stream);
+int launch_page_score_select(const FusedArgs& a, int head_dim, int kv_dtype, hipStream_t stream);
 
 struct DecodeArgs {
   const void* q;
@@ -78,6 +103,7 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* page_list;
+  const int32_t* page_phys;  // nullable: physical pages of the lists (block_table is then not read)
   const int32_t* list_len;
   float* out;
   float* out_lse;

@@ -88,14 +88,22 @@ def build_meta(w: Workload, d: DeviceInputs, stream=None) -> None:
 
 
 class DecodeStep:
-    """Buffers for one decode step of workload ``w`` over device inputs ``d``."""
+    """Buffers for one decode step of workload ``w`` over device inputs ``d``.
 
-    def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, fused: bool | None = None,
-                 tail_refresh: bool = True):
+    ``fused`` scores and selects in one launch, refreshing the tail page's key statistics inside
+    it; otherwise (default: faster on MI355X at batch 1, where one workgroup per row selects
+    either way) the tail refresh, scoring and selection are three calls.
+    ``phys_lists`` (default) has the selector write the physical page of every list entry so
+    the decode kernel does not read the block table.
+    """
+
+    def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, fused: bool = False,
+                 tail_refresh: bool = True, phys_lists: bool = True):
         self.w, self.d = w, d
         self.plan = plan or Plan()
-        self.fused = w.fused_select if fused is None else fused
+        self.fused = fused
         self.tail_refresh = tail_refresh
+        self.phys_lists = phys_lists
         dev = d.q.device
         self.desc = make_desc(w, d.num_pool_pages)
         self.sel = make_select(w)
@@ -106,6 +114,7 @@ class DecodeStep:
         self.scores = torch.zeros((B, Hkv, w.pages_per_seq), **f32)
         self.head_lse = torch.zeros((B, Hq), **f32)
         self.page_list = torch.zeros((B, Hkv, w.list_capacity), **i32)
+        self.page_phys = torch.zeros((B, Hkv, w.list_capacity), **i32) if phys_lists else None
         self.list_len = torch.zeros((B, Hkv), **i32)
         self.sel_scores = torch.zeros((B, Hkv, w.list_capacity), **f32)
         self.out = torch.zeros((B, Hq, D), **f32)
@@ -121,33 +130,52 @@ class DecodeStep:
         self.first_page = torch.from_numpy(np.maximum(n_b - 1, 0).astype(np.int32)).to(dev)
 
     def refresh_tail(self, stream=None):
-        """page_meta_build of the page the newest token is in (one page per request)."""
+        """page_meta_build of the page the newest token is in (one page per request, all heads)."""
         d = self.d
         A.spd_page_meta_build(self.desc, d.k_pool, d.k_scale, d.block_table, d.seq_lens, self.first_page, 1,
                               d.page_meta, stream)
 
-    def select(self, stream=None):
+    def score(self, stream=None):
         d = self.d
-        if self.fused:
-            A.spd_page_score_select(self.desc, self.sel, d.q, d.page_meta, d.block_table, d.seq_lens, d.head_kind,
-                                    self.page_list, self.list_len, self.sel_scores, self.workspace, self.ws_bytes,
-                                    stream)
-        else:
-            A.spd_page_score(self.desc, self.sel, d.q, d.page_meta, d.block_table, d.seq_lens, d.head_kind,
-                             self.scores, self.head_lse, self.workspace, self.ws_bytes, stream)
-            A.spd_page_select(self.desc, self.sel, self.scores, d.seq_lens, d.head_kind, self.page_list,
-                              self.list_len, self.sel_scores, None, 0, stream)
+        A.spd_page_score(self.desc, self.sel, d.q, d.page_meta, d.block_table, d.seq_lens, d.head_kind,
+                         self.scores, self.head_lse, self.workspace, self.ws_bytes, stream)
 
-    def attend(self, stream=None):
+    def select_only(self, stream=None):
+        d = self.d
+        A.spd_page_select(self.desc, self.sel, self.scores, d.seq_lens, d.head_kind, d.block_table, self.page_list,
+                          self.page_phys, self.list_len, self.sel_scores, stream)
+
+    def score_select(self, stream=None):
+        d = self.d
+        A.spd_page_score_select(self.desc, self.sel, d.q, d.page_meta, d.k_pool, d.k_scale, int(self.tail_refresh),
+                                d.block_table, d.seq_lens, d.head_kind, self.page_list, self.page_phys,
+                                self.list_len, self.sel_scores, self.scores, self.head_lse, self.workspace,
+                                self.ws_bytes, stream)
+
+    def select(self, stream=None):
+        """Scores and page lists (the fused launch, or the scorer then the selector)."""
+        if self.fused:
+            self.score_select(stream)
+        else:
+            self.score(stream)
+            self.select_only(stream)
+
+    def decode(self, stream=None):
         d = self.d
         A.spd_sparse_paged_decode(self.desc, self.pp, d.q, d.k_pool, d.v_pool, d.k_scale, d.v_scale, d.block_table,
-                                  d.seq_lens, self.page_list, self.list_len, self.w.sm_scale, self.out,
-                                  self.out_lse, self.part_o, self.part_lse, stream)
+                                  d.seq_lens, self.page_list, self.page_phys, self.list_len, self.w.sm_scale,
+                                  self.out, self.out_lse, self.part_o, self.part_lse, stream)
+
+    def merge(self, stream=None):
         A.spd_lse_merge(self.desc, self.pp, self.part_o, self.part_lse, self.list_len, self.out, self.out_lse,
                         stream)
 
+    def attend(self, stream=None):
+        self.decode(stream)
+        self.merge(stream)
+
     def run(self, stream=None):
-        if self.tail_refresh:
+        if self.tail_refresh and not self.fused:
             self.refresh_tail(stream)
         self.select(stream)
         self.attend(stream)

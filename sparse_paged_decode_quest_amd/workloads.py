@@ -68,7 +68,6 @@ class Workload:
     max_pages_per_seq: int | None = None
     max_list: int | None = None
     shuffle_lengths: bool = False
-    fused_select: bool = False
 
     @property
     def batch(self) -> int:
@@ -177,7 +176,7 @@ def named(name: str, seed_offset: int = 0) -> Workload:
     if name == "fp8_b1_512k":
         return Workload(name=name, seq_lens=(524288,), num_q_heads=32, num_kv_heads=8, head_dim=128,
                         kv_dtype="fp8", q_dtype="f16", mode="topk", budget_pages=256,
-                        n_sink=1, n_local=2, planted=("fixed", 512), delta=2.0, fused_select=True,
+                        n_sink=1, n_local=2, planted=("fixed", 512), delta=2.0,
                         seed=BASE_SEED + 4 + seed_offset)
     raise KeyError(name)
 

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 1
+    assert A.abi_version() == 2
 
 
 def test_error_strings(lib):
@@ -70,20 +70,27 @@ def score_rc(desc, sel, heads=None, ws=FAKE, ws_bytes=1 << 30, lse=FAKE):
                                   ws, ws_bytes, 0)
 
 
-def select_rc(desc, sel, heads=None):
+def select_rc(desc, sel, heads=None, bt=FAKE, phys=None):
     heads = heads if heads is not None else [0] * max(1, desc.num_kv_heads)
     arr = (ctypes.c_uint8 * len(heads))(*heads)
-    return A.lib().spd_page_select(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, arr, FAKE, FAKE, None, None,
-                                   0, 0)
+    return A.lib().spd_page_select(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, arr, bt, FAKE, phys, FAKE, None,
+                                   0)
+
+
+def fused_rc(desc, sel, heads=None, ws=FAKE, ws_bytes=1 << 30, refresh=0, k_pool=FAKE, k_scale=FAKE, bt=FAKE):
+    heads = heads if heads is not None else [0] * max(1, desc.num_kv_heads)
+    arr = (ctypes.c_uint8 * len(heads))(*heads)
+    return A.lib().spd_page_score_select(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, k_pool, k_scale, refresh,
+                                         bt, FAKE, arr, FAKE, None, FAKE, None, None, None, ws, ws_bytes, 0)
 
 
 def decode_rc(desc, plan, sm_scale=0.1, **null):
-    ptrs = {k: FAKE for k in ("q", "k", "v", "ks", "vs", "bt", "sl", "pl", "ll", "o", "lse", "po", "pls")}
+    ptrs = {k: FAKE for k in ("q", "k", "v", "ks", "vs", "bt", "sl", "pl", "pp", "ll", "o", "lse", "po", "pls")}
     ptrs.update(null)
     return A.lib().spd_sparse_paged_decode(
         ctypes.byref(desc), ctypes.byref(plan), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["ks"], ptrs["vs"], ptrs["bt"],
-        ptrs["sl"], ptrs["pl"], ptrs["ll"], ctypes.c_float(sm_scale), ptrs["o"], ptrs["lse"], ptrs["po"], ptrs["pls"],
-        0)
+        ptrs["sl"], ptrs["pl"], ptrs["pp"], ptrs["ll"], ctypes.c_float(sm_scale), ptrs["o"], ptrs["lse"], ptrs["po"],
+        ptrs["pls"], 0)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -133,8 +140,14 @@ def test_list_capacity_and_workspace_checks(lib):
     assert A.spd_workspace_bytes(desc_for(w), sel_for(w), A.OP_PAGE_SCORE) == 0
     assert A.spd_workspace_bytes(desc_for(w), sel_for(w), A.OP_PAGE_SELECT) == 0
     assert A.spd_workspace_bytes(desc_for(w), sel_for(w), A.OP_PAGE_SCORE_SELECT) >= 4 * w.batch * 2 * w.pages_per_seq
+    # coverage keeps G log-masses per page in the fused workspace
+    assert A.spd_workspace_bytes(desc_for(wc), sel_for(wc), A.OP_PAGE_SCORE_SELECT) >= \
+        16 * wc.batch * 2 * wc.pages_per_seq
     with pytest.raises(A.SpdError):
         A.spd_workspace_bytes(desc_for(w), sel_for(w), 9)
+    fneed = A.spd_workspace_bytes(desc_for(wc), sel_for(wc), A.OP_PAGE_SCORE_SELECT)
+    assert fused_rc(desc_for(wc), sel_for(wc), ws_bytes=fneed - 1) == A.SPD_ERR_WORKSPACE
+    assert fused_rc(desc_for(wc), sel_for(wc), ws=None, ws_bytes=fneed) == A.SPD_ERR_WORKSPACE
 
 
 def test_decode_argument_checks(lib):
@@ -151,11 +164,28 @@ def test_decode_argument_checks(lib):
     assert decode_rc(desc_for(wf), plan, ks=None) == A.SPD_ERR_INVALID_ARG
 
 
+def test_select_and_fused_argument_checks(lib):
+    w = W.small()
+    d = desc_for(w)
+    assert select_rc(d, sel_for(w), bt=None, phys=FAKE) == A.SPD_ERR_INVALID_ARG   # physical pages need the table
+    assert fused_rc(d, sel_for(w), bt=None) == A.SPD_ERR_INVALID_ARG
+    assert fused_rc(d, sel_for(w), refresh=1, k_pool=None) == A.SPD_ERR_INVALID_ARG  # tail refresh reads K
+    wf = W.small(kv="fp8")
+    assert fused_rc(desc_for(wf), sel_for(wf), refresh=1, k_scale=None) == A.SPD_ERR_INVALID_ARG
+    # rows longer than the longest compiled selection workgroup (65536 pages) are routed elsewhere
+    long = desc_for(w, max_pages_per_seq=65537, max_list=65537)
+    assert select_rc(long, sel_for(w)) == A.SPD_ERR_UNSUPPORTED
+    assert fused_rc(long, sel_for(w)) == A.SPD_ERR_UNSUPPORTED
+    with pytest.raises(A.SpdError):
+        A.spd_workspace_bytes(long, sel_for(w), A.OP_PAGE_SCORE_SELECT)
+
+
 def test_empty_batch_launches_nothing(lib):
     w = W.small()
     d = desc_for(w, batch=0)
     assert score_rc(d, sel_for(w)) == A.SPD_OK
     assert select_rc(d, sel_for(w)) == A.SPD_OK
+    assert fused_rc(d, sel_for(w)) == A.SPD_OK
     assert decode_rc(d, A.PlanParams(4, 16, 512)) == A.SPD_OK
 
 

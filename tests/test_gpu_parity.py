@@ -29,9 +29,9 @@ def say(*a):
     print(*a, flush=True)
 
 
-def run_case(w, plan=None, fused=None, tail=False):
+def run_case(w, plan=None, fused=True, tail=False):
     """Generate, upload, bulk-meta, one step.  Returns (inputs, device inputs, step)."""
-    say(f"[case] {w.name} seq={w.seq_lens[:8]} kv={w.kv_dtype} mode={w.mode} seed={w.seed}")
+    say(f"[case] {w.name} seq={w.seq_lens[:8]} kv={w.kv_dtype} mode={w.mode} seed={w.seed} fused={fused}")
     inp = W.generate(w)
     d = S.upload(inp)
     S.build_meta(w, d)
@@ -67,10 +67,11 @@ def oracle_row(inp, meta, b, h):
     return pi, (O.select_coverage(pi, n, w.gamma, forced) if n else []), forced, lse
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_small_meta_scores_lists_attention(name):
+def test_small_meta_scores_lists_attention(name, fused):
     w = SMALL[name]
-    inp, d, st = run_case(w)
+    inp, d, st = run_case(w, fused=fused)
     meta_ref = O.page_meta_build(inp)
     meta_gpu = d.page_meta.cpu().numpy()
     used = np.unique(np.concatenate([inp.block_table[b, :O.n_pages(L)] for b, L in enumerate(w.seq_lens)]))
@@ -99,6 +100,11 @@ def test_small_meta_scores_lists_attention(name):
                     G = w.group
                     assert np.allclose(head_lse[b, h * G:(h + 1) * G], lse, rtol=0, atol=1e-4 * np.abs(lse).max())
                 P.check_coverage_list(lists[(b, h)], ref, n, w.gamma, forced)
+
+    # the physical pages written beside the lists are the block-table entries of the listed pages
+    pp = st.page_phys.cpu().numpy()
+    for (b, h), lst in lists.items():
+        assert pp[b, h, :len(lst)].tolist() == inp.block_table[b, lst].tolist(), (b, h)
 
     # attention over the GPU's own lists where they equal the oracle's
     o_ref, lse_ref = O.sparse_paged_decode(inp, oracle_lists, w.sm_scale)
@@ -166,7 +172,7 @@ def test_tail_refresh_updates_only_last_pages():
     w = W.small("tail", seq_lens=(333, 48, 1), budget=10)
     inp = W.generate(w)
     d = S.upload(inp)
-    st = S.DecodeStep(w, d, tail_refresh=True)
+    st = S.DecodeStep(w, d, fused=False, tail_refresh=True)
     sentinel = 3.0
     d.page_meta.fill_(sentinel)
     st.refresh_tail()
@@ -177,8 +183,11 @@ def test_tail_refresh_updates_only_last_pages():
     assert np.array_equal(got, ref)
 
 
-def test_fused_select_equals_unfused():
-    w = W.small("fused", seq_lens=(3000, 700, 37, 0), budget=40, streaming=(1,), Hkv=2, Hq=8)
+@pytest.mark.parametrize("mode", ["topk", "coverage"])
+def test_fused_select_equals_unfused(mode):
+    kw = dict(budget=40) if mode == "topk" else dict(mode="coverage", gamma=0.9, n_local=1, planted=("fixed", 6),
+                                                     delta=("nats", 6.0))
+    w = W.small("fused_" + mode, seq_lens=(3000, 700, 37, 0), streaming=(1,), Hkv=2, Hq=8, **kw)
     inp, d, st = run_case(w, fused=False)
     lists_unfused = st.lists()
     st2 = S.DecodeStep(w, d, fused=True, tail_refresh=False)
@@ -187,9 +196,40 @@ def test_fused_select_equals_unfused():
         torch.cuda.synchronize()
         assert st2.lists() == lists_unfused, rep
         assert torch.equal(st2.out, st.out) and torch.equal(st2.out_lse, st.out_lse)
+        assert torch.equal(st2.page_phys, st.page_phys) and torch.equal(st2.sel_scores, st.sel_scores)
+        for b in range(w.batch):
+            n = O.n_pages(w.seq_lens[b])
+            assert torch.equal(st2.scores[b, 0, :n], st.scores[b, 0, :n]), (rep, b)  # dynamic head 0
+        if mode == "coverage":
+            assert torch.equal(st2.head_lse[:, :4], st.head_lse[:, :4])
     rows = w.batch * w.num_kv_heads
-    counters_off = -(-rows * w.pages_per_seq * 4 // 256) * 256
-    assert int(st2.workspace[counters_off:counters_off + 4 * rows].sum()) == 0  # tickets back at zero
+    counters = st2.workspace[st2.ws_bytes - (-(-rows * 4 // 256) * 256):].view(torch.int32)
+    assert int(counters.abs().sum()) == 0  # tickets back at zero
+
+
+def test_fused_tail_refresh_rebuilds_the_last_page_of_dynamic_rows():
+    for kv in ("f16", "fp8", "f32"):
+        w = W.small("tail_" + kv, kv=kv, q="f32" if kv == "f32" else "f16", d=64 if kv == "f32" else 128,
+                    seq_lens=(333, 48, 1, 0), budget=10, streaming=(1,), Hkv=2, Hq=8)
+        inp = W.generate(w)
+        d = S.upload(inp)
+        S.build_meta(w, d)
+        ref_full = d.page_meta.clone()
+        d.page_meta.fill_(3.0)  # sentinel everywhere
+        st = S.DecodeStep(w, d, fused=True, tail_refresh=True)
+        st.select()
+        torch.cuda.synchronize()
+        got = d.page_meta.cpu().numpy()
+        full = ref_full.cpu().numpy()
+        for b, L in enumerate(w.seq_lens):
+            n = O.n_pages(L)
+            for p in range(n):
+                phys = int(inp.block_table[b, p])
+                for h in range(w.num_kv_heads):
+                    if p == n - 1 and not inp.head_kind[h]:
+                        assert np.array_equal(got[phys, h], full[phys, h]), (kv, b, p, h)
+                    else:
+                        assert np.all(got[phys, h] == 3.0), (kv, b, p, h)
 
 
 def test_deterministic_bitwise():

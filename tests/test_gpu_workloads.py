@@ -23,11 +23,11 @@ def test_named_workload(name):
     assert torch.cuda.is_available()
     A.lib()
     w = W.named(name)
-    say(f"[workload] {name} B={w.batch} seq={w.seq_lens} kv={w.kv_dtype} mode={w.mode} fused={w.fused_select}")
+    say(f"[workload] {name} B={w.batch} seq={w.seq_lens} kv={w.kv_dtype} mode={w.mode}")
     inp = W.generate(w)
     d = S.upload(inp)
     S.build_meta(w, d)
-    st = S.DecodeStep(w, d)  # bench configuration: default plan, the workload's fused flag, tail refresh
+    st = S.DecodeStep(w, d)  # bench configuration: default plan, fused score + select with tail refresh
     st.run()
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
@@ -55,12 +55,7 @@ def test_named_workload(name):
         rows.append((int(np.argmax(w.seq_lens)), dyn[0]))
     rows += [(0, strm[0])] if strm else []
     gpu_lists = st.lists()
-    if st.fused:
-        rows_n = w.batch * w.num_kv_heads
-        gpu_scores = st.workspace[:rows_n * w.pages_per_seq * 4].view(torch.float32).view(
-            w.batch, w.num_kv_heads, w.pages_per_seq).cpu().numpy()
-    else:
-        gpu_scores = st.scores.cpu().numpy()
+    gpu_scores = st.scores.cpu().numpy()
     oracle_lists = {}
     for b, h in rows:
         n = O.n_pages(inp.seq_lens[b])
