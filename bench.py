@@ -4,9 +4,9 @@ Default workload: the Llama-3-8B-shaped attention layer at 128k context (batch 1
 Hkv 8, d 128, 16-token fp16 pages; KV heads 0-3 streaming with 4 sink + 16 local pages, heads
 4-7 top-K 256 pages with 1 sink + 2 local pages forced; 64 planted pages per head).
 
-A step is the whole hot path, captured in a hipGraph: tail-page key statistics refresh -> page
-scores -> page selection (or those three in one launch with --fused) -> split-K decode
-attention -> log-sum-exp merge.
+A step is the whole hot path, captured in a hipGraph: page scores (the scorer first rebuilds the
+key statistics of each dynamic row's last page) -> page selection (or both in one launch with
+--fused) -> split-K decode attention -> log-sum-exp merge.
 To measure HBM rather than the 256 MB Infinity Cache, the bench keeps R independent copies
 ("layers") of every input and output and rotates through them, so one rotation touches
 well over 1 GB.
@@ -65,18 +65,23 @@ def algorithmic_bytes(w, list_len: np.ndarray, head_kind: np.ndarray) -> dict:
     return {"meta": meta, "kv": kv, "q": q, "o": o, "tables": tables, "tail": tail, "total": total}
 
 
-def scorer_bytes(w, head_kind: np.ndarray) -> int:
-    """Algorithmic bytes of one fused score + select launch: the dynamic rows' meta, their
-    block-table entries, the group queries and the tail pages (the list write-back is small)."""
+def scorer_bytes(w, head_kind: np.ndarray, tail: str) -> int:
+    """Algorithmic bytes of one scorer launch (or fused score + select launch): the meta rows
+    and block-table entries of the dynamic rows' scanned pages, the group queries, the scores
+    written, and -- when the scorer rebuilds the last page -- that page's keys (the list
+    write-back of a fused launch is small).  A skipping scorer ("side") leaves out the last
+    page; a rebuilding one ("rebuild") reads its keys instead of its meta."""
     d = w.head_dim
     meta_bytes = 4 if w.kv_dtype == "f32" else 2
     kv_bytes = {"f32": 4, "f16": 2, "fp8": 1}[w.kv_dtype]
     dyn_heads = int((head_kind == 0).sum())
-    pages = int(w.n_pages.sum())
-    per_page_head = 2 * d * meta_bytes + 4  # meta row + block-table entry
-    q = w.batch * dyn_heads * 4 * d * (4 if w.q_dtype == "f32" else 2)
-    tail = w.batch * dyn_heads * 16 * d * kv_bytes
-    return pages * dyn_heads * per_page_head + q + tail
+    rows = int((w.n_pages > 0).sum()) * dyn_heads
+    scanned = int(w.n_pages.sum()) * dyn_heads - (rows if tail in ("side", "rebuild") else 0)
+    per_page_head = 2 * d * meta_bytes + 4 + 4  # meta row + block-table entry + score
+    q = w.batch * dyn_heads * w.group * d * (4 if w.q_dtype == "f32" else 2)
+    rebuilt = rows * (16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0) + 2 * d * meta_bytes + 4 + 4) \
+        if tail == "rebuild" else 0
+    return scanned * per_page_head + q + rebuilt
 
 
 def cpu_baseline(w, inp, seconds: float) -> dict:
@@ -109,9 +114,10 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="independent input copies rotated per step (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--fused", action="store_true", help="tail refresh, scorer and selector in one launch")
+    ap.add_argument("--fused", action="store_true", help="scorer and selector in one launch")
+    ap.add_argument("--plan", default=None, help="self-planning constants C,N_J,N_T (default: the library's)")
     ap.add_argument("--phase-only", default=None,
-                    help="time only one phase per step (select|decode|merge|score|select_only|tail)")
+                    help="time only one phase per step (select|decode|merge|score|select_only)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -146,7 +152,8 @@ def main():
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
 
-    probe = S.DecodeStep(w, base, fused=args.fused)
+    plan = S.Plan(*[int(x) for x in args.plan.split(",")]) if args.plan else None
+    probe = S.DecodeStep(w, base, plan=plan, fused=args.fused)
     probe.run()
     torch.cuda.synchronize()
     ab0 = algorithmic_bytes(w, probe.list_len.cpu().numpy(), inp.head_kind)
@@ -162,7 +169,7 @@ def main():
                                       block_table=clone(base.block_table), seq_lens=clone(base.seq_lens),
                                       head_kind=base.head_kind.copy(), page_meta=clone(base.page_meta))
                        for _ in range(R - 1)]
-    steps = [probe] + [S.DecodeStep(w, d, fused=args.fused) for d in layers[1:]]
+    steps = [probe] + [S.DecodeStep(w, d, plan=plan, fused=args.fused) for d in layers[1:]]
     for st in steps:
         st.run()
     torch.cuda.synchronize()
@@ -171,8 +178,10 @@ def main():
         assert st.lists() == ref_lists and torch.equal(st.out, steps[0].out), "layer copies disagree"
 
     phases = {"decode": lambda st, s: st.decode(s), "merge": lambda st, s: st.merge(s)}
+    if probe.tail in ("side", "serial"):
+        phases["tail"] = lambda st, s: st.refresh_tail(s)
     if not args.fused:
-        phases.update({"tail": lambda st, s: st.refresh_tail(s), "score": lambda st, s: st.score(s),
+        phases.update({"score": lambda st, s: st.score(s),
                        "select_only": lambda st, s: st.select_only(s)})
     else:
         phases["select"] = lambda st, s: st.score_select(s)
@@ -232,8 +241,8 @@ def main():
     tbs = ab["total"] / step_s / 1e12
 
     dom_name = "select" if args.fused else "score"
-    dom_kernel = "page_score_select_kernel" if args.fused else "page_score_topk_kernel"
-    dom_bytes = scorer_bytes(w, inp.head_kind)
+    dom_kernel = "page_score_select_kernel" if args.fused else "page_score_kernel"
+    dom_bytes = scorer_bytes(w, inp.head_kind, probe.tail)
     dom_us = phase_us[dom_name]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     traffic = None
@@ -270,7 +279,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "context": int(max(w.seq_lens)), "heads": heads,
                    "head_dim": w.head_dim, "page": 16, "kv_dtype": w.kv_dtype, "mode": w.mode,
                    "budget_pages": w.budget_pages, "gamma": w.gamma, "streaming_kv_heads": len(w.streaming_heads),
-                   "layers_rotated": R, "graph": True, "fused_select": args.fused},
+                   "layers_rotated": R, "graph": True, "fused_select": args.fused,
+                   "plan": [probe.plan.min_chunk, probe.plan.min_blocks_per_row, probe.plan.min_grid_blocks]},
         "step_us": round(step_us, 3), "tokens_per_s": round(w.batch / step_s, 1),
         "bytes_per_step": ab, "frac_of_peak": round(tbs / PEAK_HBM_TBS, 4),
         "phase_us": {k: round(v, 3) for k, v in phase_us.items()},

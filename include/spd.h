@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 2
+#define SPD_ABI_VERSION 3
 #define SPD_PAGE_SIZE 16
 #define SPD_MAX_KV_HEADS 64
 
@@ -99,6 +99,18 @@ typedef enum spd_head_kind {
   SPD_HEAD_DYNAMIC = 0,
   SPD_HEAD_STREAMING = 1
 } spd_head_kind;
+
+/* What the scorers do with the last logical page of each dynamic row (the page the newest
+ * token is in): */
+typedef enum spd_tail_mode {
+  SPD_TAIL_NONE = 0,     /* score it from page_meta like every other page */
+  SPD_TAIL_REBUILD = 1,  /* rebuild its key min / max from k_pool first (written to page_meta),
+                          * then score it (LServe, "Key statistics storage and updating") */
+  SPD_TAIL_SKIP = 2      /* do not score it: TOPK with n_local >= 1 only (the local window keeps
+                          * the page whatever its score); its score (and its sel_scores entry) is
+                          * written as -inf and page_meta is not read for it, so
+                          * spd_page_meta_build may refresh it concurrently */
+} spd_tail_mode;
 
 typedef enum spd_op {
   SPD_OP_PAGE_SCORE = 0,
@@ -169,17 +181,26 @@ int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t
  * importance, computed from page_meta).  COVERAGE: l_{g,p} = sm_scale * S_{g,p} +
  * ln(valid tokens of p); head_lse[b, h*G+g] = logsumexp_p l_{g,p}; scores[b,h,p] =
  * (1/G) sum_g exp(l_{g,p} - head_lse) (Moira's group-mean share, section 3.2, Eq. 3).
- * head_lse (device, [B, Hq]) may be NULL in TOPK mode.  workspace (device) of
- * spd_workspace_bytes(desc, sel, SPD_OP_PAGE_SCORE) bytes (0 in TOPK mode). */
+ * tail_mode (spd_tail_mode) says how each dynamic row's last logical page is treated;
+ * SPD_TAIL_REBUILD reads k_pool (and k_scale for fp8 pools) and writes that page's entries of
+ * page_meta, which is otherwise only read; SPD_TAIL_SKIP is valid in TOPK mode only.  head_lse
+ * (device, [B, Hq]) may be NULL in TOPK mode.  workspace (device) of spd_workspace_bytes(desc,
+ * sel, SPD_OP_PAGE_SCORE) bytes (0 in TOPK mode). */
 int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const void* q,
-                   const void* page_meta, const int32_t* block_table, const int32_t* seq_lens,
+                   void* page_meta, const void* k_pool, const uint16_t* k_scale,
+                   int32_t tail_mode, const int32_t* block_table, const int32_t* seq_lens,
                    const uint8_t* head_kind, float* scores, float* head_lse, void* workspace,
                    size_t workspace_bytes, void* stream);
 
 /* Page list of every row from its scores (selection rule: spd_select_params).  Lists are
  * ascending logical pages.  page_phys (device, [B, Hkv, max_list], may be NULL) receives the
  * physical page of each listed page, read from block_table (device, required when page_phys
- * is set), so spd_sparse_paged_decode need not read the block table.  sel_scores (device,
+ * is set), so spd_sparse_paged_decode need not read the block table.  When page_meta (device,
+ * may be NULL) is set, workgroups beside the selection also rebuild the key min / max of each
+ * request's last logical page, every KV head, from k_pool (and k_scale for fp8 pools) into
+ * page_meta -- what spd_page_meta_build does with first_page = that page and span 1 (LServe,
+ * "Key statistics storage and updating"); block_table is then required, and the scores must
+ * not depend on those statistics (the scorer ran with SPD_TAIL_SKIP).  sel_scores (device,
  * [B, Hkv, max_list], may be NULL) receives the score of each listed page of a dynamic row
  * (streaming rows: untouched).  Returns SPD_ERR_INVALID_ARG when max_list cannot hold the
  * longest possible list: TOPK needs max_list >= max(budget, n_sink + n_local) and
@@ -187,15 +208,13 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
  * more than 65536 pages return SPD_ERR_UNSUPPORTED. */
 int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const float* scores,
                     const int32_t* seq_lens, const uint8_t* head_kind, const int32_t* block_table,
-                    int32_t* page_list, int32_t* page_phys, int32_t* list_len, float* sel_scores,
-                    void* stream);
+                    const void* k_pool, const uint16_t* k_scale, void* page_meta, int32_t* page_list,
+                    int32_t* page_phys, int32_t* list_len, float* sel_scores, void* stream);
 
 /* spd_page_score followed by spd_page_select in one launch, for both rules (LiteTopK,
  * section 3.2, "Extension to Decoding": selection fused into score computation).  The
  * workgroups of a row score into the workspace; the last one to finish selects the row.
- * refresh_tail != 0 first rebuilds the key min / max of each dynamic row's last logical page
- * from k_pool (and k_scale for fp8 pools) and writes them to page_meta (LServe, "Key
- * statistics storage and updating"); page_meta is otherwise only read.  scores (device,
+ * tail_mode as in spd_page_score.  scores (device,
  * [B, Hkv, max_pages_per_seq], may be NULL) receives the TOPK scores or COVERAGE shares of
  * dynamic rows; head_lse (device, [B, Hq], may be NULL) the COVERAGE per-head log-sum-exp.
  * page_list, page_phys, list_len, sel_scores as in spd_page_select (block_table is
@@ -204,7 +223,7 @@ int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const fl
  * again.  Calls that share one workspace must not overlap. */
 int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, const void* q,
                           void* page_meta, const void* k_pool, const uint16_t* k_scale,
-                          int32_t refresh_tail, const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t tail_mode, const int32_t* block_table, const int32_t* seq_lens,
                           const uint8_t* head_kind, int32_t* page_list, int32_t* page_phys,
                           int32_t* list_len, float* sel_scores, float* scores, float* head_lse,
                           void* workspace, size_t workspace_bytes, void* stream);

@@ -24,6 +24,7 @@ DTYPE = {"f32": 0, "f16": 1, "fp8": 2}
 SELECT_TOPK, SELECT_COVERAGE = 0, 1
 HEAD_DYNAMIC, HEAD_STREAMING = 0, 1
 OP_PAGE_SCORE, OP_PAGE_SELECT, OP_PAGE_SCORE_SELECT = 0, 1, 2
+TAIL_NONE, TAIL_REBUILD, TAIL_SKIP = 0, 1, 2
 
 EXPORTS = ("spd_page_meta_build", "spd_page_score", "spd_page_select", "spd_page_score_select",
            "spd_sparse_paged_decode", "spd_lse_merge", "spd_plan_grid", "spd_plan_chunks",
@@ -66,8 +67,8 @@ def lib():
         D, S, P = POINTER(Desc), POINTER(SelectParams), POINTER(PlanParams)
         v = c_void_p
         L.spd_page_meta_build.argtypes = [D, v, v, v, v, v, c_int32, v, v]
-        L.spd_page_score.argtypes = [D, S, v, v, v, v, POINTER(c_uint8), v, v, v, c_size_t, v]
-        L.spd_page_select.argtypes = [D, S, v, v, POINTER(c_uint8), v, v, v, v, v, v]
+        L.spd_page_score.argtypes = [D, S, v, v, v, v, c_int32, v, v, POINTER(c_uint8), v, v, v, c_size_t, v]
+        L.spd_page_select.argtypes = [D, S, v, v, POINTER(c_uint8), v, v, v, v, v, v, v, v, v]
         L.spd_page_score_select.argtypes = [D, S, v, v, v, v, c_int32, v, v, POINTER(c_uint8), v, v, v, v, v, v, v,
                                             c_size_t, v]
         L.spd_sparse_paged_decode.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v]
@@ -127,25 +128,27 @@ def spd_page_meta_build(desc, k_pool, k_scale, block_table, seq_lens, first_page
                                      _stream(stream)), "spd_page_meta_build")
 
 
-def spd_page_score(desc, sel, q, page_meta, block_table, seq_lens, head_kind, scores, head_lse, workspace,
-                   workspace_bytes, stream=None):
-    _check(lib().spd_page_score(ctypes.byref(desc), ctypes.byref(sel), _ptr(q), _ptr(page_meta), _ptr(block_table),
-                                _ptr(seq_lens), _heads(head_kind), _ptr(scores), _ptr(head_lse), _ptr(workspace),
-                                int(workspace_bytes), _stream(stream)), "spd_page_score")
+def spd_page_score(desc, sel, q, page_meta, k_pool, k_scale, tail_mode, block_table, seq_lens, head_kind, scores,
+                   head_lse, workspace, workspace_bytes, stream=None):
+    _check(lib().spd_page_score(ctypes.byref(desc), ctypes.byref(sel), _ptr(q), _ptr(page_meta), _ptr(k_pool),
+                                _ptr(k_scale), int(tail_mode), _ptr(block_table), _ptr(seq_lens), _heads(head_kind),
+                                _ptr(scores), _ptr(head_lse), _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "spd_page_score")
 
 
-def spd_page_select(desc, sel, scores, seq_lens, head_kind, block_table, page_list, page_phys, list_len, sel_scores,
-                    stream=None):
+def spd_page_select(desc, sel, scores, seq_lens, head_kind, block_table, k_pool, k_scale, page_meta, page_list,
+                    page_phys, list_len, sel_scores, stream=None):
     _check(lib().spd_page_select(ctypes.byref(desc), ctypes.byref(sel), _ptr(scores), _ptr(seq_lens),
-                                 _heads(head_kind), _ptr(block_table), _ptr(page_list), _ptr(page_phys),
-                                 _ptr(list_len), _ptr(sel_scores), _stream(stream)), "spd_page_select")
+                                 _heads(head_kind), _ptr(block_table), _ptr(k_pool), _ptr(k_scale), _ptr(page_meta),
+                                 _ptr(page_list), _ptr(page_phys), _ptr(list_len), _ptr(sel_scores),
+                                 _stream(stream)), "spd_page_select")
 
 
-def spd_page_score_select(desc, sel, q, page_meta, k_pool, k_scale, refresh_tail, block_table, seq_lens, head_kind,
+def spd_page_score_select(desc, sel, q, page_meta, k_pool, k_scale, tail_mode, block_table, seq_lens, head_kind,
                           page_list, page_phys, list_len, sel_scores, scores, head_lse, workspace, workspace_bytes,
                           stream=None):
     _check(lib().spd_page_score_select(ctypes.byref(desc), ctypes.byref(sel), _ptr(q), _ptr(page_meta), _ptr(k_pool),
-                                       _ptr(k_scale), int(refresh_tail), _ptr(block_table), _ptr(seq_lens),
+                                       _ptr(k_scale), int(tail_mode), _ptr(block_table), _ptr(seq_lens),
                                        _heads(head_kind), _ptr(page_list), _ptr(page_phys), _ptr(list_len),
                                        _ptr(sel_scores), _ptr(scores), _ptr(head_lse), _ptr(workspace),
                                        int(workspace_bytes), _stream(stream)), "spd_page_score_select")

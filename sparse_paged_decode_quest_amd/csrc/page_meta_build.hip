@@ -1,73 +1,12 @@
-// Per-page channel-wise key min / max (LServe summary, "Hierarchical Paging": every
-// logical page keeps k_min and k_max over its keys; "Key statistics storage and updating":
-// the statistics of the page a new token lands in are refreshed as the token is appended).
-//
-// One wave per (request, logical page, KV head).  Lane l owns channels [l*CPL, (l+1)*CPL)
-// of every token, so min / max over the page's valid tokens is lane-local: no cross-lane
-// traffic, and the page's 16 token rows are 16 coalesced loads issued back to back.
-#include "spd_device.h"
-#include "spd_launch.h"
+// Bulk statistics (every page of every request, at prefill) or the pages [first_page,
+// first_page + span) of each request (the page the newest token is in, during decode).
+#include "meta_build.h"
 
 namespace spd {
 
 template <int D, int KVD>
-struct MetaTraits;
-
-template <int D> struct MetaTraits<D, SPD_DTYPE_F32> {
-  static constexpr int CPL = D / kWave;
-  using Out = float;
-  __device__ static void load(const void* pool, size_t idx, float (&v)[CPL], float) {
-    const float* p = reinterpret_cast<const float*>(pool) + idx;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = p[c];
-  }
-  __device__ static void store(void* meta, size_t idx, const float (&lo)[CPL], const float (&hi)[CPL], int d) {
-    float* m = reinterpret_cast<float*>(meta) + idx;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) { m[c] = lo[c]; m[d + c] = hi[c]; }
-  }
-};
-
-template <int D> struct MetaTraits<D, SPD_DTYPE_F16> {
-  static constexpr int CPL = D / kWave;
-  __device__ static void load(const void* pool, size_t idx, float (&v)[CPL], float) {
-    const __half* p = reinterpret_cast<const __half*>(pool) + idx;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = __half2float(p[c]);
-  }
-  __device__ static void store(void* meta, size_t idx, const float (&lo)[CPL], const float (&hi)[CPL], int d) {
-    __half* m = reinterpret_cast<__half*>(meta) + idx;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {  // exact: min / max of fp16 values
-      m[c] = __float2half_rn(lo[c]);
-      m[d + c] = __float2half_rn(hi[c]);
-    }
-  }
-};
-
-template <int D> struct MetaTraits<D, SPD_DTYPE_FP8_E4M3FN> {
-  static constexpr int CPL = D / kWave;
-  __device__ static void load(const void* pool, size_t idx, float (&v)[CPL], float scale) {
-    const uint8_t* p = reinterpret_cast<const uint8_t*>(pool) + idx;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = fp8_to_float(p[c]) * scale;  // exact in fp32
-  }
-  __device__ static void store(void* meta, size_t idx, const float (&lo)[CPL], const float (&hi)[CPL], int d) {
-    uint16_t* m = reinterpret_cast<uint16_t*>(meta) + idx;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {  // outward: the stored box still contains every key
-      m[c] = f32_to_f16_round_down(lo[c]);
-      m[d + c] = f32_to_f16_round_up(hi[c]);
-    }
-  }
-};
-
-template <int D, int KVD>
 __global__ __launch_bounds__(256) void page_meta_build_kernel(MetaArgs a) {
-  using T = MetaTraits<D, KVD>;
-  constexpr int CPL = T::CPL;
   const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
   const int b = blockIdx.x / a.blocks_per_req;
   const int item = (blockIdx.x % a.blocks_per_req) * 4 + wave;  // (page offset, head) pair
   if (b >= a.batch) return;
@@ -83,32 +22,7 @@ __global__ __launch_bounds__(256) void page_meta_build_kernel(MetaArgs a) {
   }
   const int p = start + p_off;
   if (p >= end) return;
-  const int phys = a.block_table[(size_t)b * a.max_pages + p];
-  if (phys < 0 || phys >= a.num_pool_pages) return;
-  const int valid = valid_in_page(len, p);
-  const int c0 = lane * CPL;
-  const size_t head_base = ((size_t)phys * a.num_kv_heads + h) * kPage;
-  // every token of the page is loaded at once (slots past `valid` are read but never used)
-  float v[kPage][CPL];
-#pragma unroll
-  for (int t = 0; t < kPage; ++t) {
-    float scale = 1.0f;
-    if (KVD == SPD_DTYPE_FP8_E4M3FN) scale = half_bits_to_float(a.k_scale[head_base + t]);
-    T::load(a.k_pool, (head_base + t) * D + c0, v[t], scale);
-  }
-  float lo[CPL], hi[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) { lo[c] = INFINITY; hi[c] = -INFINITY; }
-#pragma unroll
-  for (int t = 0; t < kPage; ++t) {
-    const bool ok = t < valid;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      lo[c] = ok ? fminf(lo[c], v[t][c]) : lo[c];
-      hi[c] = ok ? fmaxf(hi[c], v[t][c]) : hi[c];
-    }
-  }
-  T::store(a.meta, (((size_t)phys * a.num_kv_heads + h) * 2) * D + c0, lo, hi, D);
+  build_page_meta<D, KVD>(a, b, p, h, len);
 }
 
 int launch_page_meta_build(const MetaArgs& a, int head_dim, int kv_dtype, hipStream_t stream) {

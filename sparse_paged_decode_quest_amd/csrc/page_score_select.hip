@@ -8,10 +8,11 @@
 // takes the last ticket acquires, builds the row's keys (coverage: the per-head log-sum-exp
 // and Moira's group-mean shares, section 3.2, Eq. 3), selects the row's pages
 // (select_row.h) and returns the counter to zero, so the workspace is ready for the next call
-// (and for graph replay) without a clearing step.  With tail refresh on, the workgroup that
-// owns a row's last page rebuilds that page's key statistics from the K pool first (LServe,
-// "Key statistics storage and updating").  Extra workgroups write the static lists of
-// streaming rows.
+// (and for graph replay) without a clearing step.  With SPD_TAIL_REBUILD one more workgroup per
+// dynamic row rebuilds the key statistics of the row's last page from the K pool and scores it
+// (LServe, "Key statistics storage and updating"); it takes a ticket like the others.  With
+// SPD_TAIL_SKIP (top-K) that page is not scored: the local window keeps it.  Extra workgroups
+// write the static lists of streaming rows.
 #include "score_common.h"
 #include "select_row.h"
 
@@ -22,7 +23,8 @@ __global__ __launch_bounds__(NW * kWave) void page_score_select_kernel(FusedArgs
   __shared__ SelectSmem<NW, KPL, COV> sm;
   __shared__ int last;
   const ScoreArgs& a = f.score;
-  const int dyn_blocks = a.batch * a.dyn.count * a.blocks_per_row;
+  const int per_row = a.blocks_per_row + tail_blocks(a);  // + the tail workgroup
+  const int dyn_blocks = a.batch * a.dyn.count * per_row;
   if ((int)blockIdx.x >= dyn_blocks) {
     const int k = blockIdx.x - dyn_blocks;
     const int b = k / f.stream_heads.count;
@@ -31,8 +33,9 @@ __global__ __launch_bounds__(NW * kWave) void page_score_select_kernel(FusedArgs
     select_streaming_row(f.sel, row_pages(a.seq_lens[b], a.max_pages), row, a.block_table + (size_t)b * a.max_pages);
     return;
   }
-  const int row_dyn = blockIdx.x / a.blocks_per_row;
-  const int blk = blockIdx.x % a.blocks_per_row;
+  const int row_dyn = blockIdx.x / per_row;
+  const int blk = blockIdx.x % per_row;
+  const bool tail_block = blk == a.blocks_per_row;
   const int b = row_dyn / a.dyn.count;
   const int h = a.dyn.head[row_dyn % a.dyn.count];
   const size_t row = (size_t)b * a.num_kv_heads + h;
@@ -40,19 +43,30 @@ __global__ __launch_bounds__(NW * kWave) void page_score_select_kernel(FusedArgs
   const int p_begin = blk * a.pages_per_block;
   const int len = a.seq_lens[b];
   int raw[ITERS];
-  load_block_table<D, KVD, NW, ITERS>(bt_row, a.max_pages, p_begin, raw);
+  if (!tail_block) load_block_table<D, KVD, NW, ITERS>(bt_row, a.max_pages, p_begin, raw);
   const int n = row_pages(len, a.max_pages);
-  const int used = (n + a.pages_per_block - 1) / a.pages_per_block;
   if (n == 0) {
     if (blk == 0 && threadIdx.x == 0) f.sel.list_len[row] = 0;
     if (COV && blk == 0 && threadIdx.x < kG && a.head_lse)
       a.head_lse[(size_t)b * a.num_q_heads + (size_t)h * kG + threadIdx.x] = -INFINITY;
     return;
   }
-  if (blk >= used) return;
-  if constexpr (COV) score_block_coverage<D, KVD, NW, ITERS>(a, raw, n, len, b, h, p_begin, blk, a.refresh_tail != 0);
-  else score_block_topk<D, KVD, NW, ITERS>(a, raw, n, len, b, h, p_begin, a.refresh_tail != 0,
-                                           a.scores + row * a.max_pages);
+  const int n_scan = scan_pages(a, n);
+  // Page-scanning workgroups, then the tail workgroup; when the only page is a skipped last
+  // page, workgroup 0 still takes the one ticket.
+  int used = (n_scan + a.pages_per_block - 1) / a.pages_per_block;
+  if (used + tail_blocks(a) == 0) used = 1;
+  const int tickets = used + tail_blocks(a);
+  if (tail_block) {
+    score_tail<D, KVD, COV>(a, bt_row, n, len, b, h, used);
+  } else {
+    if (blk >= used) return;
+    if (!COV && a.tail_mode == SPD_TAIL_SKIP && blk == 0 && threadIdx.x == 0) a.scores[row * a.max_pages + n - 1] = -INFINITY;
+    if (p_begin < n_scan) {
+      if constexpr (COV) score_block_coverage<D, KVD, NW, ITERS>(a, raw, n_scan, len, b, h, p_begin, blk);
+      else score_block_topk<D, KVD, NW, ITERS>(a, raw, n_scan, b, h, p_begin, a.scores + row * a.max_pages);
+    }
+  }
   // Publish: every wave waits for its own score stores, the workgroup barrier orders them before
   // the ticket, and the ticket is a release at device scope (one L2 write-back per workgroup;
   // a fence in every wave would write back and invalidate the L2 once per wave).  The workgroup
@@ -61,7 +75,7 @@ __global__ __launch_bounds__(NW * kWave) void page_score_select_kernel(FusedArgs
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(&f.counters[row], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(used - 1);
+    last = __hip_atomic_fetch_add(&f.counters[row], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(tickets - 1);
   __syncthreads();
   if (!last) return;
   if (threadIdx.x < kWave) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -73,7 +87,7 @@ __global__ __launch_bounds__(NW * kWave) void page_score_select_kernel(FusedArgs
   phys.bt_row = f.sel.page_phys ? bt_row : nullptr;
   if constexpr (COV) {
     float lse[kG];
-    row_head_lse(a.partials + row * a.blocks_per_row * kG, used, lse);  // every wave, same bits
+    row_head_lse(a.partials + row * a.partial_stride * kG, tickets, lse);  // every wave, same bits
     if (threadIdx.x < kG && a.head_lse) {
       float v = lse[0];
 #pragma unroll
@@ -106,7 +120,8 @@ __global__ __launch_bounds__(NW * kWave) void page_score_select_kernel(FusedArgs
 int launch_page_score_select(const FusedArgs& f, int head_dim, int kv_dtype, hipStream_t stream) {
   SelectGeometry g;
   if (!select_geometry(f.score.max_pages, g)) return SPD_ERR_UNSUPPORTED;
-  const int blocks = f.score.batch * (f.score.dyn.count * f.score.blocks_per_row + f.stream_heads.count);
+  const int per_row = f.score.blocks_per_row + tail_blocks(f.score);
+  const int blocks = f.score.batch * (f.score.dyn.count * per_row + f.stream_heads.count);
   const dim3 grid((unsigned)blocks), block(g.nw * kWave);
   const bool cov = f.sel.mode == SPD_SELECT_COVERAGE;
 #define SPD_FUSED_GEOM(D, KVD, NW, KPL, IT)                                                                     \

@@ -1,5 +1,9 @@
 // Page lists from page scores: one workgroup per (request, KV head) row.  The selection rules
-// and their sources are described in select_row.h.
+// and their sources are described in select_row.h.  Optionally, workgroups after the rows
+// rebuild the key statistics of each request's last page, one wave per KV head (LServe, "Key
+// statistics storage and updating"), beside the selection: where the scorer skipped that page
+// (the local window keeps it), the rebuild leaves the critical path of the step.
+#include "meta_build.h"
 #include "select_row.h"
 
 namespace spd {
@@ -18,9 +22,25 @@ __device__ __forceinline__ void load_row_keys(const float* sc, int n, uint32_t (
   }
 }
 
+// Tail workgroup k: wave w rebuilds (request, KV head) item k * NW + w.
+template <int NW>
+__device__ __forceinline__ void rebuild_tail_pages(const SelectArgs& a, int k) {
+  const int item = k * NW + (int)(threadIdx.x / kWave);
+  if (item >= a.batch * a.num_kv_heads) return;
+  const int b = item / a.num_kv_heads, h = item % a.num_kv_heads;
+  const int len = a.seq_lens[b];
+  const int n = row_pages(len, a.max_pages);
+  if (n > 0) build_page_meta_rt(a.tail, b, n - 1, h, len);
+}
+
 template <int NW, int KPL, bool COV>
 __global__ __launch_bounds__(NW * kWave) void page_select_kernel(SelectArgs a) {
   __shared__ SelectSmem<NW, KPL, COV> sm;
+  const int rows = a.batch * a.num_kv_heads;
+  if ((int)blockIdx.x >= rows) {
+    rebuild_tail_pages<NW>(a, blockIdx.x - rows);
+    return;
+  }
   const int b = blockIdx.x / a.num_kv_heads;
   const int h = blockIdx.x % a.num_kv_heads;
   const size_t row = (size_t)b * a.num_kv_heads + h;
@@ -40,7 +60,9 @@ __global__ __launch_bounds__(NW * kWave) void page_select_kernel(SelectArgs a) {
 int launch_page_select(const SelectArgs& a, hipStream_t stream) {
   SelectGeometry g;
   if (!select_geometry(a.max_pages, g)) return SPD_ERR_UNSUPPORTED;
-  const dim3 grid((unsigned)(a.batch * a.num_kv_heads)), block(g.nw * kWave);
+  const int rows = a.batch * a.num_kv_heads;
+  const int tail_blocks = a.tail.meta ? (rows + g.nw - 1) / g.nw : 0;
+  const dim3 grid((unsigned)(rows + tail_blocks)), block(g.nw * kWave);
   const bool cov = a.mode == SPD_SELECT_COVERAGE;
 #define SPD_SEL_CASE(NW, KPL)                                                                          \
   if (g.nw == NW && g.kpl == KPL) {                                                                    \

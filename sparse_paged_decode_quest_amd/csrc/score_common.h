@@ -11,11 +11,12 @@
 // ignored), then every meta load of the lane is issued before any arithmetic, so a lane keeps
 // ITERS * 32 bytes in flight and the whole scan is two dependent memory round trips.
 //
-// Tail refresh (LServe, "Key statistics storage and updating": the statistics of the page a
-// new token lands in are updated as the token is appended): when enabled, the lanes that own
-// the row's last page rebuild its min / max from the K pool, write them to the page meta and
-// score the page from those registers -- the same two round trips, with the K page in place
-// of its meta row.
+// The last page (LServe, "Key statistics storage and updating": the statistics of the page a
+// new token lands in are updated as the token is appended).  With SPD_TAIL_REBUILD each dynamic
+// row gets one more workgroup, which rebuilds the min / max of the row's last page from the K
+// pool, writes them to the page meta and scores the page from those registers, while the
+// regular workgroups score every other page.  With SPD_TAIL_SKIP (top-K) the page is not scored
+// and its meta is not read, so a separate rebuild may run concurrently with the scorer.
 #pragma once
 
 #include "spd_device.h"
@@ -211,6 +212,12 @@ struct ScoreTraits<D, SPD_DTYPE_F32> {
   }
 };
 
+// Extra workgroups per dynamic row for the tail mode, and the pages the scan covers.
+__host__ __device__ __forceinline__ int tail_blocks(const ScoreArgs& a) { return a.tail_mode == SPD_TAIL_REBUILD ? 1 : 0; }
+__device__ __forceinline__ int scan_pages(const ScoreArgs& a, int n) {
+  return a.tail_mode != SPD_TAIL_NONE && n > 0 ? n - 1 : n;
+}
+
 // Pages per workgroup of NW waves with ITERS page groups each.
 __host__ __device__ constexpr int score_pages_per_block(int d, int meta_bytes, int nw, int iters) {
   return iters * nw * (kWave / (d * meta_bytes / 16));
@@ -255,14 +262,13 @@ __device__ __forceinline__ void load_block_table(const int32_t* bt_row, int max_
 }
 
 // Bounds S_{g,p} of the pages [p_begin, p_begin + NW * ITERS * PPI) owned by this workgroup.
-// n is the row's page count (pages >= n are not loaded); raw holds load_block_table's entries.
+// Pages >= n are not loaded (n is the scan limit); raw holds load_block_table's entries.
 // For each of the ITERS page groups of the calling lane, `fn(p, ok, s)` is called on lanes
 // with sub == 0 after the LPP-lane reduction (p may be >= n: then ok is false and fn must
-// ignore it).  Pages whose block-table entry is outside the pool have ok = false.  `tail`
-// enables the rebuild of page n - 1 from the K pool.
+// ignore it).  Pages whose block-table entry is outside the pool have ok = false.
 template <int D, int KVD, int NW, int ITERS, typename F>
-__device__ __forceinline__ void score_block(const ScoreArgs& a, const int (&raw)[ITERS], int n, int len, int b, int h,
-                                            int p_begin, bool tail, F&& fn) {
+__device__ __forceinline__ void score_block(const ScoreArgs& a, const int (&raw)[ITERS], int n, int b, int h,
+                                            int p_begin, F&& fn) {
   using T = ScoreTraits<D, KVD>;
   constexpr int LPP = T::LPP;
   const int lane = threadIdx.x % kWave;
@@ -276,53 +282,84 @@ __device__ __forceinline__ void score_block(const ScoreArgs& a, const int (&raw)
   }
   typename T::Q qr;
   T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0);
-  typename T::M m[ITERS], mt;
-  int tail_phys = -1;  // the row's last page, when this lane's group owns it and it is rebuilt
+  typename T::M m[ITERS];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
-    if (tail && pg[it] == n - 1) tail_phys = ok ? phys[it] : -1;
-    else if (ok) T::load_m(m[it], a.meta, ((size_t)phys[it] * a.num_kv_heads + h) * 2 * D, c0);
+    if (ok) T::load_m(m[it], a.meta, ((size_t)phys[it] * a.num_kv_heads + h) * 2 * D, c0);
   }
-  if (tail_phys >= 0)
-    T::rebuild(mt, a.k_pool, a.k_scale, (size_t)tail_phys * a.num_kv_heads + h, valid_in_page(len, n - 1), c0,
-               a.meta_out, ((size_t)tail_phys * a.num_kv_heads + h) * 2 * D);
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
     float s[kG];
-    if (ok) T::bound(qr, (tail && pg[it] == n - 1) ? mt : m[it], s);
+    if (ok) T::bound(qr, m[it], s);
     else {
 #pragma unroll
       for (int g = 0; g < kG; ++g) s[g] = 0.f;
     }
 #pragma unroll
-    for (int g = 0; g < kG; ++g) s[g] = xor_sum<LPP>(s[g]);
+    for (int g = 0; g < kG; ++g) s[g] = group_sum<LPP>(s[g]);
     if (sub == 0) fn(pg[it], ok && pg[it] < n, s);
   }
+}
+
+// The tail workgroup of a dynamic row: lanes 0..LPP-1 of wave 0 rebuild the key statistics of
+// the row's last page (n - 1) from the K pool, store them, and bound it; `fn(s)` gets the
+// bounds on lane 0 (not called when the page's block-table entry is outside the pool).
+template <int D, int KVD, typename F>
+__device__ __forceinline__ void score_tail_page(const ScoreArgs& a, const int32_t* bt_row, int n, int len, int b,
+                                                int h, F&& fn) {
+  using T = ScoreTraits<D, KVD>;
+  constexpr int LPP = T::LPP;
+  if (threadIdx.x >= LPP) return;
+  const int c0 = (int)threadIdx.x * T::CW;
+  const int phys = bt_row[n - 1];
+  typename T::Q qr;
+  T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0);
+  if (phys < 0 || phys >= a.num_pool_pages) return;
+  const size_t head_page = (size_t)phys * a.num_kv_heads + h;
+  typename T::M m;
+  T::rebuild(m, a.k_pool, a.k_scale, head_page, valid_in_page(len, n - 1), c0, a.meta_out, head_page * 2 * D);
+  float s[kG];
+  T::bound(qr, m, s);
+#pragma unroll
+  for (int g = 0; g < kG; ++g) s[g] = group_sum<LPP>(s[g]);
+  if (threadIdx.x == 0) fn(s);
 }
 
 // Top-K keys of the workgroup's pages: score_p = max_g S_{g,p} (the group combine keeps the
 // score an upper bound for every query head of the group); pages whose block-table entry is
 // outside the pool score -inf.
-template <int D, int KVD, int NW, int ITERS>
-__device__ __forceinline__ void score_block_topk(const ScoreArgs& a, const int (&raw)[ITERS], int n, int len, int b,
-                                                 int h, int p_begin, bool tail, float* row_scores) {
-  score_block<D, KVD, NW, ITERS>(a, raw, n, len, b, h, p_begin, tail, [&](int p, bool ok, const float (&s)[kG]) {
-    if (p >= n) return;
-    float best = s[0];
+__device__ __forceinline__ float topk_score(const float (&s)[kG]) {
+  float best = s[0];
 #pragma unroll
-    for (int g = 1; g < kG; ++g) best = fmaxf(best, s[g]);
-    row_scores[p] = ok ? best : -INFINITY;
+  for (int g = 1; g < kG; ++g) best = fmaxf(best, s[g]);
+  return best;
+}
+
+template <int D, int KVD, int NW, int ITERS>
+__device__ __forceinline__ void score_block_topk(const ScoreArgs& a, const int (&raw)[ITERS], int n, int b, int h,
+                                                 int p_begin, float* row_scores) {
+  score_block<D, KVD, NW, ITERS>(a, raw, n, b, h, p_begin, [&](int p, bool ok, const float (&s)[kG]) {
+    if (p >= n) return;
+    row_scores[p] = ok ? topk_score(s) : -INFINITY;
   });
 }
 
-// Coverage, first pass over the workgroup's pages: log-masses l_{g,p} = s S_{g,p} + ln(valid_p)
-// written per page, and one (max, sum exp) pair per head for the workgroup.  Moira, section
-// 3.2: the per-head softmax over pages needs the head's log-sum-exp over the whole row.
+// Coverage log-mass of a page: l_{g,p} = s S_{g,p} + ln(valid_p).
+__device__ __forceinline__ void coverage_logmass(const ScoreArgs& a, int valid, bool ok, const float (&s)[kG],
+                                                 float (&lg)[kG]) {
+  const float lv = valid == kPage ? 2.772588722239781f : logf((float)valid);  // ln(valid)
+#pragma unroll
+  for (int g = 0; g < kG; ++g) lg[g] = ok ? fmaf(a.sm_scale, s[g], lv) : -INFINITY;
+}
+
+// Coverage, first pass over the workgroup's pages [.., n): log-masses written per page, and one
+// (max, sum exp) pair per head for the workgroup in partial slot `slot`.  Moira, section 3.2: the
+// per-head softmax over pages needs the head's log-sum-exp over the whole row.
 template <int D, int KVD, int NW, int ITERS>
 __device__ __forceinline__ void score_block_coverage(const ScoreArgs& a, const int (&raw)[ITERS], int n, int len, int b,
-                                                     int h, int p_begin, int blk, bool tail) {
+                                                     int h, int p_begin, int slot) {
   constexpr int LPP = ScoreTraits<D, KVD>::LPP;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -333,16 +370,12 @@ __device__ __forceinline__ void score_block_coverage(const ScoreArgs& a, const i
     lm[g] = -INFINITY;
     ls[g] = 0.f;
   }
-  score_block<D, KVD, NW, ITERS>(a, raw, n, len, b, h, p_begin, tail, [&](int p, bool ok, const float (&s)[kG]) {
+  score_block<D, KVD, NW, ITERS>(a, raw, n, b, h, p_begin, [&](int p, bool ok, const float (&s)[kG]) {
     if (p >= n) return;
-    const int valid = valid_in_page(len, p);
-    const float lv = valid == kPage ? 2.772588722239781f : logf((float)valid);  // ln(valid)
     float lg[kG];
+    coverage_logmass(a, valid_in_page(len, p), ok, s, lg);
 #pragma unroll
-    for (int g = 0; g < kG; ++g) {
-      lg[g] = ok ? fmaf(a.sm_scale, s[g], lv) : -INFINITY;
-      lse_push(lm[g], ls[g], lg[g]);
-    }
+    for (int g = 0; g < kG; ++g) lse_push(lm[g], ls[g], lg[g]);
     a.ell[row * a.max_pages + p] = make_float4(lg[0], lg[1], lg[2], lg[3]);
   });
   // fold the lanes that own pages (sub == 0), then the waves in order
@@ -363,7 +396,38 @@ __device__ __forceinline__ void score_block_coverage(const ScoreArgs& a, const i
     const int g = threadIdx.x;
     float m = sm_m[0][g], s = sm_s[0][g];
     for (int w = 1; w < NW; ++w) lse_combine(m, s, sm_m[w][g], sm_s[w][g]);
-    a.partials[(row * a.blocks_per_row + blk) * kG + g] = make_float2(m, s);
+    a.partials[(row * a.partial_stride + slot) * kG + g] = make_float2(m, s);
+  }
+}
+
+// The tail workgroup's work for either rule: the last page's top-K score, or its log-masses and
+// the (max, 1) pair of that single page in partial slot `slot`.
+template <int D, int KVD, bool COV>
+__device__ __forceinline__ void score_tail(const ScoreArgs& a, const int32_t* bt_row, int n, int len, int b, int h,
+                                           int slot) {
+  const size_t row = (size_t)b * a.num_kv_heads + h;
+  if constexpr (COV) {
+    bool wrote = false;
+    score_tail_page<D, KVD>(a, bt_row, n, len, b, h, [&](const float (&s)[kG]) {
+      float lg[kG];
+      coverage_logmass(a, valid_in_page(len, n - 1), true, s, lg);
+      a.ell[row * a.max_pages + n - 1] = make_float4(lg[0], lg[1], lg[2], lg[3]);
+#pragma unroll
+      for (int g = 0; g < kG; ++g) a.partials[(row * a.partial_stride + slot) * kG + g] = make_float2(lg[g], 1.f);
+      wrote = true;
+    });
+    if (threadIdx.x == 0 && !wrote) {  // page outside the pool: no mass
+      a.ell[row * a.max_pages + n - 1] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+#pragma unroll
+      for (int g = 0; g < kG; ++g) a.partials[(row * a.partial_stride + slot) * kG + g] = make_float2(-INFINITY, 0.f);
+    }
+  } else {
+    bool wrote = false;
+    score_tail_page<D, KVD>(a, bt_row, n, len, b, h, [&](const float (&s)[kG]) {
+      a.scores[row * a.max_pages + n - 1] = topk_score(s);
+      wrote = true;
+    });
+    if (threadIdx.x == 0 && !wrote) a.scores[row * a.max_pages + n - 1] = -INFINITY;
   }
 }
 

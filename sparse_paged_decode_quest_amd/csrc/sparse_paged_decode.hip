@@ -11,13 +11,15 @@
 // Two-Level Indexing" (loop over a per-head index table of pages).
 //
 // Block (row, j) with 4 waves: wave w takes pages j*c + w, j*c + w + 4, ... of the chunk.
-// For one 16-token page a wave needs no LDS staging: lane l reads token l/4, channel
-// quarter l%4 of K (16-byte loads, 64 contiguous bytes per token per instruction), and
-// channels [l*d/64, (l+1)*d/64) of V for all 16 tokens (one 256-byte row per instruction).
-// The G = 4 partial dot products of a lane are reduce-scattered over its quad so that lane
-// l ends with the full logit of head l%4 and token l/4 -- one logit per lane.  Softmax
-// max / sum run on those, the 64 probabilities go through 1 KiB of LDS so every lane can
-// apply all of them to its V channels.  The waves' states are merged in LDS at the end.
+// For one 16-token page a wave needs no LDS staging: lane l = 16 q + t reads token t, channel
+// quarter q of K (16-byte loads), and channels [l*d/64, (l+1)*d/64) of V for all 16 tokens
+// (one 256-byte row per instruction).  The G = 4 partial dot products of a lane are
+// reduce-scattered over the four lanes of its token (gfx950's permlane16 / permlane32 swaps
+// exchange rows of 16 lanes in one VALU instruction) so that lane 16 h + t ends with the full
+// logit of head h and token t: each 16-lane row is one head, and the softmax max / sum over
+// the page's tokens are row reductions through DPP.  The 64 probabilities go through 1 KiB of
+// LDS so every lane can apply all of them to its V channels; the waves' states are merged in
+// LDS at the end.
 #include <type_traits>
 
 #include "spd_device.h"
@@ -196,22 +198,45 @@ struct DecTraits<D, SPD_DTYPE_F32, SPD_DTYPE_F32> {
   static constexpr bool kScaled = false;
 };
 
+// Value of the lane 16 rows away (lane ^ 16) and 32 lanes away (lane ^ 32): gfx950's row swaps.
+__device__ __forceinline__ float xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Max / sum over the 16 lanes of a row (every lane of the row receives it), through DPP.
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp<0xb1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<0x4e>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<0x141>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(dpp<0x140>(__float_as_uint(v))));
+}
+
+__device__ __forceinline__ float row_sum(float v) {
+  v += __uint_as_float(dpp<0xb1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<0x4e>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<0x141>(__float_as_uint(v)));
+  return v + __uint_as_float(dpp<0x140>(__float_as_uint(v)));
+}
+
 struct PageRef {
   int page;   // logical page, -1 when the entry is not a usable page
   int phys;
   int valid;  // valid tokens
 };
 
-// List entry i of a row: its logical page and, from the list of physical pages when the
-// selector wrote one (no block-table read) or else from the block table, its physical page.
-__device__ __forceinline__ PageRef resolve_page(const DecodeArgs& a, const int32_t* list, const int32_t* plist, int i,
-                                                int b, int n_b, int len) {
+// Page i of this wave's batch: its logical page (lane i of `lp`), its physical page (lane i of
+// `lph`) and valid token count, broadcast to the whole wave (uniform values, scalar addresses).
+__device__ __forceinline__ PageRef batch_page(int lp, int lph, int i, int n_b, int len, int num_pool_pages) {
   PageRef r{-1, 0, 0};
-  const int p = list[i];
-  const int pp = plist ? plist[i] : 0;
-  if (p < 0 || p >= n_b) return r;
-  const int phys = plist ? pp : a.block_table[(size_t)b * a.max_pages + p];
-  if (phys < 0 || phys >= a.num_pool_pages) return r;
+  const int p = __builtin_amdgcn_readlane(lp, i);
+  const int phys = __builtin_amdgcn_readlane(lph, i);
+  if (p < 0 || p >= n_b || phys < 0 || phys >= num_pool_pages) return r;
   r.page = p;
   r.phys = phys;
   r.valid = valid_in_page(len, p);
@@ -223,20 +248,35 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   using T = DecTraits<D, QD, KVD>;
   constexpr int CPL = T::CPL;
   __shared__ float p_lds[4][kPage][kGq];
-  __shared__ float alpha_lds[4][kGq];
   __shared__ float ws_m[4][kGq], ws_l[4][kGq];
   __shared__ float ws_acc[4][kGq][D];
 
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int tok = lane >> 2;      // QK role: token of the page
-  const int quarter = lane & 3;   // QK role: channel quarter, and after the reduce-scatter the head
+  const int tok = lane & (kPage - 1);  // QK role: token of the page
+  const int quarter = lane >> 4;       // QK role: channel quarter, and after the reduce-scatter the head
   const int row = blockIdx.x / a.blocks_per_row;
   const int j = blockIdx.x % a.blocks_per_row;
   const int b = row / a.num_kv_heads;
   const int h = row % a.num_kv_heads;
   const size_t qrow = (size_t)b * a.num_q_heads + (size_t)h * kGq;  // first query head of the group
 
+  const int32_t* list = a.page_list + (size_t)row * a.max_list;
+  const int32_t* plist = a.page_phys ? a.page_phys + (size_t)row * a.max_list : nullptr;
+  // The list entries of this wave's first 64 pages are requested together with the row's list
+  // length, assuming the chunk starts at j * min_chunk -- true whenever the row fits in
+  // J * min_chunk pages, where the chunk size is the minimum; otherwise they are read again.
+  const int spec_i0 = j * a.min_chunk;
+  int spec_lp = -1, spec_lph = -1;
+  {
+    const int idx = spec_i0 + wave + 4 * lane;
+    if (idx < a.max_list) {
+      spec_lp = list[idx];
+      if (plist) spec_lph = plist[idx];
+    }
+  }
+  typename T::Q q;
+  T::load_q(q, a.q, qrow * D, quarter);
   int n = a.list_len[row];
   n = n < 0 ? 0 : (n > a.max_list ? a.max_list : n);
   if (n == 0) {
@@ -253,11 +293,6 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   const int i1 = min(n, i0 + c);
   const int len = a.seq_lens[b];
   const int n_b = row_pages(len, a.max_pages);
-  const int32_t* list = a.page_list + (size_t)row * a.max_list;
-  const int32_t* plist = a.page_phys ? a.page_phys + (size_t)row * a.max_list : nullptr;
-
-  typename T::Q q;
-  T::load_q(q, a.q, qrow * D, quarter);
 
   float m_run = -INFINITY, l_run = 0.f;
   float acc[kGq][CPL];
@@ -288,71 +323,91 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
     const float send1 = b0 ? part[2] : part[3];
     const float keep0 = b0 ? part[1] : part[0];
     const float keep1 = b0 ? part[3] : part[2];
-    const float hA = keep0 + __shfl_xor(send0, 1, kWave);  // head b0
-    const float hB = keep1 + __shfl_xor(send1, 1, kWave);  // head 2 + b0
+    const float hA = keep0 + xor16(send0);  // head b0
+    const float hB = keep1 + xor16(send1);  // head 2 + b0
     const float keep2 = b1 ? hB : hA;
     const float send2 = b1 ? hA : hB;
-    const float dot = keep2 + __shfl_xor(send2, 2, kWave);  // head `quarter`, token `tok`
+    const float dot = keep2 + xor32(send2);  // head `quarter`, token `tok`
     float x = dot * a.sm_scale_log2 * ks;
     if (tok >= r.valid) x = -INFINITY;
-    float mx = x;
-#pragma unroll
-    for (int o = 4; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    const float mx = row_max(x);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
     const float p = m_new == -INFINITY ? 0.f : exp2f(x - m_new);
     l_run = l_run * alpha + p;
     m_run = m_new;
-    p_lds[wave][tok][quarter] = p * vs;
-    if (lane < kGq) alpha_lds[wave][lane] = alpha;
+    p_lds[wave][tok][quarter] = tok < r.valid ? p * vs : 0.f;  // invalid slots' scales may be NaN
+    float alv[kGq];  // each head's rescale, read from its row
+#pragma unroll
+    for (int g = 0; g < kGq; ++g) alv[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), g * 16));
     wave_fence();
-    const float4 al = *reinterpret_cast<const float4*>(alpha_lds[wave]);
-    const float alv[kGq] = {al.x, al.y, al.z, al.w};
 #pragma unroll
     for (int g = 0; g < kGq; ++g)
 #pragma unroll
       for (int cc = 0; cc < CPL; ++cc) acc[g][cc] *= alv[g];
+    float4 pt[kPage];  // every probability of the page, read in one batch
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) pt[t] = *reinterpret_cast<const float4*>(p_lds[wave][t]);
 #pragma unroll
     for (int t = 0; t < kPage; ++t) {
-      if (t < r.valid) {  // invalid slots may hold NaN: never touch them
-        const float4 pt = *reinterpret_cast<const float4*>(p_lds[wave][t]);
-        const float pv[kGq] = {pt.x, pt.y, pt.z, pt.w};
-        float v[CPL];
-        T::v_values(vf, t, v);
+      const float pv[kGq] = {pt[t].x, pt[t].y, pt[t].z, pt[t].w};
+      float v[CPL];
+      T::v_values(vf, t, v);
 #pragma unroll
-        for (int g = 0; g < kGq; ++g)
+      for (int cc = 0; cc < CPL; ++cc) v[cc] = t < r.valid ? v[cc] : 0.f;  // invalid slots may hold NaN
 #pragma unroll
-          for (int cc = 0; cc < CPL; ++cc) acc[g][cc] = fmaf(pv[g], v[cc], acc[g][cc]);
-      }
+      for (int g = 0; g < kGq; ++g)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) acc[g][cc] = fmaf(pv[g], v[cc], acc[g][cc]);
     }
     wave_fence();
   };
 
-  const PageRef none{-1, 0, 0};
+  // This wave's pages are i0 + wave, i0 + wave + 4, ...  Their list entries (and physical pages)
+  // are read 64 at a time, one per lane, before any K / V load is issued: a list read issued
+  // behind K / V loads would have to wait for them (loads retire in order).  Pages then
+  // alternate between two register stages, so the next page's K / V loads are in flight while
+  // the current page is computed.
+  const int my_pages = i1 - i0 > wave ? (i1 - i0 - wave + 3) / 4 : 0;
   typename T::KF ka, kb;
   typename T::VF va, vb;
   float ksa = 1.f, vsa = 1.f, ksb = 1.f, vsb = 1.f;
-  int i = i0 + wave;
-  PageRef ra = i < i1 ? resolve_page(a, list, plist, i, b, n_b, len) : none;
-  load(ra, ka, va, ksa, vsa);
-  while (i < i1) {
-    const PageRef rb = i + 4 < i1 ? resolve_page(a, list, plist, i + 4, b, n_b, len) : none;
-    load(rb, kb, vb, ksb, vsb);
-    process(ra, ka, va, ksa, vsa);
-    i += 4;
-    if (i >= i1) break;
-    ra = i + 4 < i1 ? resolve_page(a, list, plist, i + 4, b, n_b, len) : none;
+  for (int bb = 0; bb < my_pages; bb += kWave) {
+    const int cnt = min(kWave, my_pages - bb);
+    const int idx = i0 + wave + 4 * (bb + lane);
+    int lp = -1, lph = -1;
+    if (bb == 0 && i0 == spec_i0) {  // the speculative read covered this batch
+      if (lane < cnt) {
+        lp = spec_lp;
+        lph = spec_lph;
+      }
+    } else if (lane < cnt) {
+      lp = list[idx];
+      if (plist) lph = plist[idx];
+    }
+    if (!plist && lane < cnt && lp >= 0 && lp < n_b) lph = a.block_table[(size_t)b * a.max_pages + lp];
+    PageRef ra = batch_page(lp, lph, 0, n_b, len, a.num_pool_pages), rb;
     load(ra, ka, va, ksa, vsa);
-    process(rb, kb, vb, ksb, vsb);
-    i += 4;
+    for (int u = 0; u < cnt; u += 2) {
+      if (u + 1 < cnt) {
+        rb = batch_page(lp, lph, u + 1, n_b, len, a.num_pool_pages);
+        load(rb, kb, vb, ksb, vsb);
+      }
+      process(ra, ka, va, ksa, vsa);
+      if (u + 1 >= cnt) break;
+      if (u + 2 < cnt) {
+        ra = batch_page(lp, lph, u + 2, n_b, len, a.num_pool_pages);
+        load(ra, ka, va, ksa, vsa);
+      }
+      process(rb, kb, vb, ksb, vsb);
+    }
   }
 
   // wave state -> LDS
-#pragma unroll
-  for (int o = 4; o < kWave; o <<= 1) l_run += __shfl_xor(l_run, o, kWave);
-  if (lane < kGq) {
-    ws_m[wave][lane] = m_run;
-    ws_l[wave][lane] = l_run;
+  l_run = row_sum(l_run);
+  if (tok == 0) {
+    ws_m[wave][quarter] = m_run;
+    ws_l[wave][quarter] = l_run;
   }
 #pragma unroll
   for (int g = 0; g < kGq; ++g)
@@ -391,15 +446,18 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
 
 // Exact merge of a row's chunk states (PersistentKV, section 3.3; states are stored
 // normalised: o_j = a_j / l_j and lse_j = m_j + ln l_j).  One 1024-thread block per (row,
-// query head): chunk weights exp(lse_j - lse) go through LDS, then D channels x (1024 / D)
-// chunk partitions accumulate in parallel (every partial load of a thread is independent)
-// and the partitions are summed in a fixed order.
+// query head).  The row's list length, the chunk log-sum-exps and the first kPre chunk outputs
+// of every thread are all requested at once -- entries past the row's chunk count are read
+// (they lie inside the partial buffers) and never used -- so the merge costs one memory round
+// trip.  Chunk weights exp(lse_j - lse) go through LDS; D channels x (1024 / D) chunk
+// partitions accumulate in parallel and the partitions are summed in a fixed order.
 constexpr int kMergeThreads = 1024;
 constexpr int kMaxChunks = 1024;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
   constexpr int PARTS = kMergeThreads / D;
+  constexpr int kPre = 8;  // chunk outputs per thread loaded up front (J <= kPre * PARTS needs no more)
   __shared__ float w_s[kMaxChunks];
   __shared__ float red[kMergeThreads / kWave];
   __shared__ float part_s[PARTS][D];
@@ -407,19 +465,38 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
   const int g = blockIdx.x % kGq;
   const int b = row / a.num_kv_heads;
   const int h = row % a.num_kv_heads;
+  const int J = a.blocks_per_row;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int ch = threadIdx.x % D, part = threadIdx.x / D;
+  const size_t slot0 = (size_t)row * J * kGq + g;  // + j * kGq
+
+  // speculative loads: list length, chunk lse values, first chunk outputs
   int n = a.list_len[row];
+  float lse_j[(kMaxChunks + kMergeThreads - 1) / kMergeThreads];
+#pragma unroll
+  for (int k = 0; k < (kMaxChunks + kMergeThreads - 1) / kMergeThreads; ++k) {
+    const int jj = (int)threadIdx.x + k * kMergeThreads;
+    lse_j[k] = jj < J ? a.part_lse[slot0 + (size_t)jj * kGq] : -INFINITY;
+  }
+  float pre[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int jj = part + u * PARTS;
+    pre[u] = jj < J ? a.part_o[(slot0 + (size_t)jj * kGq) * D + ch] : 0.f;
+  }
   n = n < 0 ? 0 : (n > a.max_list ? a.max_list : n);
   int c, m;
-  plan_chunks(n, a.blocks_per_row, a.min_chunk, c, m);
+  plan_chunks(n, J, a.min_chunk, c, m);
   if (m <= 1) return;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const size_t slot0 = (size_t)row * a.blocks_per_row * kGq + g;  // + j * kGq
 
   float mx = -INFINITY;
-  for (int j = threadIdx.x; j < m; j += kMergeThreads) {
-    const float l = a.part_lse[slot0 + (size_t)j * kGq];
-    w_s[j] = l;
-    mx = fmaxf(mx, l);
+#pragma unroll
+  for (int k = 0; k < (kMaxChunks + kMergeThreads - 1) / kMergeThreads; ++k) {
+    const int jj = (int)threadIdx.x + k * kMergeThreads;
+    if (jj < m) {
+      w_s[jj] = lse_j[k];
+      mx = fmaxf(mx, lse_j[k]);
+    }
   }
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
@@ -430,14 +507,14 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
   __syncthreads();
   const size_t qrow = (size_t)b * a.num_q_heads + (size_t)h * kGq + g;
   if (M == -INFINITY) {
-    for (int ch = threadIdx.x; ch < D; ch += kMergeThreads) a.out[qrow * D + ch] = 0.f;
+    for (int e = threadIdx.x; e < D; e += kMergeThreads) a.out[qrow * D + e] = 0.f;
     if (threadIdx.x == 0) a.out_lse[qrow] = -INFINITY;
     return;
   }
   float sum = 0.f;
-  for (int j = threadIdx.x; j < m; j += kMergeThreads) {
-    const float wj = expf(w_s[j] - M);
-    w_s[j] = wj;
+  for (int jj = threadIdx.x; jj < m; jj += kMergeThreads) {
+    const float wj = expf(w_s[jj] - M);
+    w_s[jj] = wj;
     sum += wj;
   }
   sum = xor_sum<kWave>(sum);
@@ -446,10 +523,14 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
   float S = 0.f;
   for (int w = 0; w < kMergeThreads / kWave; ++w) S += red[w];
 
-  const int ch = threadIdx.x % D, part = threadIdx.x / D;
   float acc = 0.f;
-#pragma unroll 8
-  for (int j = part; j < m; j += PARTS) acc = fmaf(w_s[j], a.part_o[(slot0 + (size_t)j * kGq) * D + ch], acc);
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int jj = part + u * PARTS;
+    if (jj < m) acc = fmaf(w_s[jj], pre[u], acc);
+  }
+  for (int jj = part + kPre * PARTS; jj < m; jj += PARTS)
+    acc = fmaf(w_s[jj], a.part_o[(slot0 + (size_t)jj * kGq) * D + ch], acc);
   part_s[part][ch] = acc;
   __syncthreads();
   if (threadIdx.x < D) {

@@ -66,6 +66,17 @@ int check_sel(const spd_desc* d, const spd_select_params* s) {
   return SPD_OK;
 }
 
+// Tail mode: a known value; a rebuild needs the K pool (and its scales for fp8); skipping the
+// last page is only for TOPK with a local window, which always keeps that page.
+int check_tail(const spd_desc* d, const spd_select_params* s, int32_t mode, const void* k_pool,
+               const uint16_t* k_scale) {
+  if (mode != SPD_TAIL_NONE && mode != SPD_TAIL_REBUILD && mode != SPD_TAIL_SKIP) return SPD_ERR_INVALID_ARG;
+  if (mode == SPD_TAIL_REBUILD && (!k_pool || (d->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale)))
+    return SPD_ERR_INVALID_ARG;
+  if (mode == SPD_TAIL_SKIP && (s->mode != SPD_SELECT_TOPK || s->n_local < 1)) return SPD_ERR_INVALID_ARG;
+  return SPD_OK;
+}
+
 // Longest list a row can produce under the rule; max_list must hold it.
 int check_list_capacity(const spd_desc* d, const spd_select_params* s) {
   const int64_t stream_len = std::min<int64_t>((int64_t)s->n_sink_stream + s->n_local_stream, d->max_pages_per_seq);
@@ -115,7 +126,7 @@ ScoreWs score_ws(const spd_desc* d) {
   ScoreWs w;
   w.ell_off = 0;
   w.part_off = align_up(rows * d->max_pages_per_seq * G * sizeof(float));
-  w.total = w.part_off + align_up(rows * bpr * G * 2 * sizeof(float));
+  w.total = w.part_off + align_up(rows * (bpr + 1) * G * 2 * sizeof(float));  // + the tail workgroup's slot
   return w;
 }
 
@@ -136,7 +147,7 @@ bool fused_ws(const spd_desc* d, const spd_select_params* s, FusedWs& w) {
   const size_t bpr = (d->max_pages_per_seq + w.ppb - 1) / w.ppb;
   w.scores_off = 0;
   w.part_off = align_up(rows * d->max_pages_per_seq * (cov ? G : 1) * sizeof(float));
-  w.counters_off = w.part_off + (cov ? align_up(rows * bpr * G * 2 * sizeof(float)) : 0);
+  w.counters_off = w.part_off + (cov ? align_up(rows * (bpr + 1) * G * 2 * sizeof(float)) : 0);
   w.total = w.counters_off + align_up(rows * sizeof(uint32_t));
   return true;
 }
@@ -156,6 +167,7 @@ spd::ScoreArgs score_args(const spd_desc* d, const spd_select_params* s, const v
   a.num_pool_pages = d->num_pool_pages;
   a.pages_per_block = ppb;
   a.blocks_per_row = (d->max_pages_per_seq + ppb - 1) / ppb;
+  a.partial_stride = a.blocks_per_row + 1;
   a.sm_scale = s->sm_scale;
   return a;
 }
@@ -181,6 +193,23 @@ spd::SelectArgs select_args(const spd_desc* d, const spd_select_params* s, const
   a.n_local = s->n_local;
   a.n_sink_stream = s->n_sink_stream;
   a.n_local_stream = s->n_local_stream;
+  return a;
+}
+
+spd::MetaArgs meta_args(const spd_desc* d, const void* k_pool, const uint16_t* k_scale, const int32_t* bt,
+                        const int32_t* sl, void* meta) {
+  spd::MetaArgs a{};
+  a.k_pool = k_pool;
+  a.k_scale = k_scale;
+  a.block_table = bt;
+  a.seq_lens = sl;
+  a.meta = meta;
+  a.batch = d->batch;
+  a.num_kv_heads = d->num_kv_heads;
+  a.max_pages = d->max_pages_per_seq;
+  a.num_pool_pages = d->num_pool_pages;
+  a.head_dim = d->head_dim;
+  a.kv_dtype = d->kv_dtype;
   return a;
 }
 
@@ -258,26 +287,18 @@ int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t
   if (!k_pool || !block_table || !seq_lens || !page_meta) return SPD_ERR_INVALID_ARG;
   if (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale) return SPD_ERR_INVALID_ARG;
   if (first_page && span_pages < 1) return SPD_ERR_INVALID_ARG;
-  spd::MetaArgs a{};
-  a.k_pool = k_pool;
-  a.k_scale = k_scale;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
+  spd::MetaArgs a = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
   a.first_page = first_page;
-  a.meta = page_meta;
-  a.batch = desc->batch;
-  a.num_kv_heads = desc->num_kv_heads;
-  a.max_pages = desc->max_pages_per_seq;
-  a.num_pool_pages = desc->num_pool_pages;
   const int span = first_page ? std::min(span_pages, desc->max_pages_per_seq) : desc->max_pages_per_seq;
   a.span = span;
   a.blocks_per_req = (span * desc->num_kv_heads + 3) / 4;
   return launched(spd::launch_page_meta_build(a, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
 }
 
-int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const void* q, const void* page_meta,
-                   const int32_t* block_table, const int32_t* seq_lens, const uint8_t* head_kind, float* scores,
-                   float* head_lse, void* workspace, size_t workspace_bytes, void* stream) {
+int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const void* q, void* page_meta,
+                   const void* k_pool, const uint16_t* k_scale, int32_t tail_mode, const int32_t* block_table,
+                   const int32_t* seq_lens, const uint8_t* head_kind, float* scores, float* head_lse,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if ((rc = check_sel(desc, sel))) return rc;
@@ -286,8 +307,13 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
   if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
   if (desc->batch == 0 || dyn.count == 0) return SPD_OK;
   if (!q || !page_meta || !block_table || !seq_lens || !scores) return SPD_ERR_INVALID_ARG;
+  if ((rc = check_tail(desc, sel, tail_mode, k_pool, k_scale))) return rc;
   spd::ScoreArgs a = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, score_ppb(desc));
   a.scores = scores;
+  a.meta_out = page_meta;
+  a.k_pool = k_pool;
+  a.k_scale = k_scale;
+  a.tail_mode = tail_mode;
   const bool coverage = sel->mode == SPD_SELECT_COVERAGE;
   if (coverage) {
     if (!head_lse) return SPD_ERR_INVALID_ARG;
@@ -302,7 +328,8 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
 
 int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const float* scores,
                     const int32_t* seq_lens, const uint8_t* head_kind, const int32_t* block_table,
-                    int32_t* page_list, int32_t* page_phys, int32_t* list_len, float* sel_scores, void* stream) {
+                    const void* k_pool, const uint16_t* k_scale, void* page_meta, int32_t* page_list,
+                    int32_t* page_phys, int32_t* list_len, float* sel_scores, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if ((rc = check_sel(desc, sel))) return rc;
@@ -315,13 +342,16 @@ int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const fl
   if (desc->batch == 0) return SPD_OK;
   if (!seq_lens || !page_list || !list_len || (dyn.count > 0 && !scores)) return SPD_ERR_INVALID_ARG;
   if (page_phys && !block_table) return SPD_ERR_INVALID_ARG;
+  if (page_meta && (!block_table || !k_pool || (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale)))
+    return SPD_ERR_INVALID_ARG;
   spd::SelectArgs a = select_args(desc, sel, seq_lens, block_table, page_list, page_phys, list_len, sel_scores, mask);
   a.scores = scores;
+  if (page_meta) a.tail = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
   return launched(spd::launch_page_select(a, (hipStream_t)stream));
 }
 
 int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, const void* q, void* page_meta,
-                          const void* k_pool, const uint16_t* k_scale, int32_t refresh_tail,
+                          const void* k_pool, const uint16_t* k_scale, int32_t tail_mode,
                           const int32_t* block_table, const int32_t* seq_lens, const uint8_t* head_kind,
                           int32_t* page_list, int32_t* page_phys, int32_t* list_len, float* sel_scores, float* scores,
                           float* head_lse, void* workspace, size_t workspace_bytes, void* stream) {
@@ -337,7 +367,7 @@ int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, co
   if (desc->batch == 0) return SPD_OK;
   if (!seq_lens || !page_list || !list_len || !block_table) return SPD_ERR_INVALID_ARG;
   if (dyn.count > 0 && (!q || !page_meta)) return SPD_ERR_INVALID_ARG;
-  if (refresh_tail && (!k_pool || (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale))) return SPD_ERR_INVALID_ARG;
+  if ((rc = check_tail(desc, sel, tail_mode, k_pool, k_scale))) return rc;
   if (!workspace || workspace_bytes < w.total) return SPD_ERR_WORKSPACE;
   const bool cov = sel->mode == SPD_SELECT_COVERAGE;
   char* ws = static_cast<char*>(workspace);
@@ -346,7 +376,7 @@ int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, co
   f.score.meta_out = page_meta;
   f.score.k_pool = k_pool;
   f.score.k_scale = k_scale;
-  f.score.refresh_tail = refresh_tail ? 1 : 0;
+  f.score.tail_mode = tail_mode;
   if (cov) {
     f.score.ell = reinterpret_cast<float4*>(ws + w.scores_off);
     f.score.partials = reinterpret_cast<float2*>(ws + w.part_off);

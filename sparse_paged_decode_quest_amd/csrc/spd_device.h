@@ -161,6 +161,23 @@ __device__ __forceinline__ unsigned long long wave_sum(unsigned long long v) {
   return lane_u64(v, 0) + lane_u64(v, 16) + lane_u64(v, 32) + lane_u64(v, 48);
 }
 
+// Sum over aligned groups of WIDTH lanes (8, 16 or 32); every lane of a group receives its sum.
+// Half-row / row mirrors and quad permutations stay inside the group, and gfx950's permlane16
+// swap pairs the two rows of a 32-lane group.
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(WIDTH == 8 || WIDTH == 16 || WIDTH == 32, "group of 8, 16 or 32 lanes");
+  v += __uint_as_float(dpp<0xb1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<0x4e>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<0x141>(__float_as_uint(v)));
+  if constexpr (WIDTH >= 16) v += __uint_as_float(dpp<0x140>(__float_as_uint(v)));
+  if constexpr (WIDTH == 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v += __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+  }
+  return v;
+}
+
 // Lanes below this one whose bit is set in `mask` (a 64-lane ballot).
 __device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

@@ -10,7 +10,7 @@
 namespace spd {
 
 // Scoring workgroups: NW waves, each with ITERS groups of pages (score_common.h).
-constexpr int kScoreWaves = 4, kScoreIters = 4;  // standalone scorer
+constexpr int kScoreWaves = 4, kScoreIters = 2;  // standalone scorer
 
 // Selection workgroup shape for rows of up to max_pages pages (select_row.h): NW waves with
 // KPL key slots per lane; the fused score + select kernel scores with the same workgroup and
@@ -39,6 +39,7 @@ struct MetaArgs {
   int batch, num_kv_heads, max_pages, num_pool_pages;
   int span;            // pages after first_page (when first_page is set)
   int blocks_per_req;  // workgroups per request (4 (page, head) items each)
+  int head_dim, kv_dtype;
 };
 int launch_page_meta_build(const MetaArgs& a, int head_dim, int kv_dtype, hipStream_t stream);
 
@@ -51,21 +52,22 @@ struct HeadList {
 struct ScoreArgs {
   const void* q;
   const void* meta;
-  void* meta_out;            // tail refresh target (fused path; the same buffer as meta)
-  const void* k_pool;        // tail refresh source (fused path)
+  void* meta_out;            // tail refresh target (the same buffer as meta)
+  const void* k_pool;        // tail refresh source
   const uint16_t* k_scale;
   const int32_t* block_table;
   const int32_t* seq_lens;
   float* scores;             // top-K: [B, Hkv, max_pages]; coverage: shares (nullable when fused)
   float4* ell;               // coverage: [B, Hkv, max_pages] log-masses of the G heads
-  float2* partials;          // coverage: [B, Hkv, blocks_per_row, G] (max, sum of exp)
+  float2* partials;          // coverage: [B, Hkv, partial_stride, G] (max, sum of exp)
   float* head_lse;           // coverage: [B, Hq] (nullable when fused)
   HeadList dyn;
   int batch, num_q_heads, num_kv_heads, max_pages, num_pool_pages;
-  int blocks_per_row;        // workgroups per (request, dynamic head)
+  int blocks_per_row;        // page-scanning workgroups per (request, dynamic head)
+  int partial_stride;        // partial slots per row: blocks_per_row + 1 (the tail workgroup's)
   int pages_per_block;
   float sm_scale;
-  int refresh_tail;          // fused path: rebuild each dynamic row's last page from k_pool
+  int tail_mode;             // spd_tail_mode: last page of each dynamic row scored / rebuilt / skipped
 };
 int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool coverage, hipStream_t stream);
 
@@ -82,6 +84,7 @@ struct SelectArgs {
   int mode, budget;
   unsigned long long gamma_fx;  // gamma in 2^-40 fixed point
   int n_sink, n_local, n_sink_stream, n_local_stream;
+  MetaArgs tail;            // tail.meta set: also rebuild each request's last page, all KV heads
 };
 int launch_page_select(const SelectArgs& a, hipStream_t stream);
 

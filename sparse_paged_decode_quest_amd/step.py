@@ -6,8 +6,10 @@ inputs, intermediates and outputs, fills the C descriptors, and calls the entry 
 
     page_meta_build (tail page) -> page_score -> page_select -> sparse_paged_decode -> lse_merge
 
-(or page_score_select in place of the middle two) -- on one stream, so the whole step can
-be captured into one hipGraph and replayed.
+(or page_score_select in place of the middle two), so the whole step can be captured into
+one hipGraph and replayed.  In top-K mode the last page of a row is always kept by the local
+window, so its score is not needed in the step that appends to it: by default the scorer
+skips it and the selector's spare workgroups rebuild its statistics beside the selection.
 """
 from __future__ import annotations
 
@@ -87,22 +89,48 @@ def build_meta(w: Workload, d: DeviceInputs, stream=None) -> None:
     A.spd_page_meta_build(desc, d.k_pool, d.k_scale, d.block_table, d.seq_lens, None, 0, d.page_meta, stream)
 
 
+TAILS = ("auto", "none", "select", "side", "serial", "rebuild")
+
+
 class DecodeStep:
     """Buffers for one decode step of workload ``w`` over device inputs ``d``.
 
-    ``fused`` scores and selects in one launch, refreshing the tail page's key statistics inside
-    it; otherwise (default: faster on MI355X at batch 1, where one workgroup per row selects
-    either way) the tail refresh, scoring and selection are three calls.
+    ``fused`` scores and selects in one launch; otherwise (default: faster on MI355X, where one
+    workgroup per row selects either way) scoring and selection are two calls.  ``tail`` says
+    how the key statistics of the page each request's newest token is in are rebuilt:
+
+    * ``"none"``: not at all (the statistics are current);
+    * ``"select"``: by the selector's spare workgroups (all heads), after a scorer that skips
+      that page (top-K with a local window, unfused);
+    * ``"side"``: the all-heads rebuild (``refresh_tail``) on a second stream, concurrent with a
+      scorer that skips that page (top-K with a local window);
+    * ``"serial"``: the all-heads rebuild, then a scorer that reads the rebuilt statistics;
+    * ``"rebuild"``: inside the scorer, by one extra workgroup per dynamic row;
+    * ``"auto"`` (default): ``"select"`` where it applies, ``"rebuild"`` for a fused top-K step,
+      else ``"serial"``.
+
     ``phys_lists`` (default) has the selector write the physical page of every list entry so
     the decode kernel does not read the block table.
     """
 
     def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, fused: bool = False,
-                 tail_refresh: bool = True, phys_lists: bool = True):
+                 tail: str = "auto", phys_lists: bool = True):
+        if tail not in TAILS:
+            raise ValueError(f"tail must be one of {TAILS}")
+        skippable = w.mode == "topk" and w.n_local >= 1
+        if tail == "auto":
+            tail = ("rebuild" if fused else "select") if skippable else "serial"
+        if tail in ("select", "side") and not skippable:
+            raise ValueError(f"tail={tail!r} skips the last page: top-K with a local window only")
+        if tail == "select" and fused:
+            raise ValueError("tail='select' needs the separate selector (fused=False)")
         self.w, self.d = w, d
         self.plan = plan or Plan()
         self.fused = fused
-        self.tail_refresh = tail_refresh
+        self.tail = tail
+        self.tail_mode = {"none": A.TAIL_NONE, "select": A.TAIL_SKIP, "side": A.TAIL_SKIP, "serial": A.TAIL_NONE,
+                          "rebuild": A.TAIL_REBUILD}[tail]
+        self.side = torch.cuda.Stream(device=d.q.device) if tail == "side" else None
         self.phys_lists = phys_lists
         dev = d.q.device
         self.desc = make_desc(w, d.num_pool_pages)
@@ -135,19 +163,25 @@ class DecodeStep:
         A.spd_page_meta_build(self.desc, d.k_pool, d.k_scale, d.block_table, d.seq_lens, self.first_page, 1,
                               d.page_meta, stream)
 
-    def score(self, stream=None):
+    def score(self, stream=None, tail_mode=None):
+        """Page scores, treating each dynamic row's last page by the step's tail mode."""
         d = self.d
-        A.spd_page_score(self.desc, self.sel, d.q, d.page_meta, d.block_table, d.seq_lens, d.head_kind,
-                         self.scores, self.head_lse, self.workspace, self.ws_bytes, stream)
+        tm = self.tail_mode if tail_mode is None else tail_mode
+        A.spd_page_score(self.desc, self.sel, d.q, d.page_meta, d.k_pool, d.k_scale, tm, d.block_table,
+                         d.seq_lens, d.head_kind, self.scores, self.head_lse, self.workspace, self.ws_bytes, stream)
 
     def select_only(self, stream=None):
+        """Page lists from the scores (and, with tail="select", the last pages' statistics)."""
         d = self.d
-        A.spd_page_select(self.desc, self.sel, self.scores, d.seq_lens, d.head_kind, d.block_table, self.page_list,
-                          self.page_phys, self.list_len, self.sel_scores, stream)
+        rebuild = self.tail == "select"
+        A.spd_page_select(self.desc, self.sel, self.scores, d.seq_lens, d.head_kind, d.block_table,
+                          d.k_pool if rebuild else None, d.k_scale if rebuild else None,
+                          d.page_meta if rebuild else None, self.page_list, self.page_phys, self.list_len,
+                          self.sel_scores, stream)
 
     def score_select(self, stream=None):
         d = self.d
-        A.spd_page_score_select(self.desc, self.sel, d.q, d.page_meta, d.k_pool, d.k_scale, int(self.tail_refresh),
+        A.spd_page_score_select(self.desc, self.sel, d.q, d.page_meta, d.k_pool, d.k_scale, self.tail_mode,
                                 d.block_table, d.seq_lens, d.head_kind, self.page_list, self.page_phys,
                                 self.list_len, self.sel_scores, self.scores, self.head_lse, self.workspace,
                                 self.ws_bytes, stream)
@@ -175,10 +209,25 @@ class DecodeStep:
         self.merge(stream)
 
     def run(self, stream=None):
-        if self.tail_refresh and not self.fused:
+        """One whole step on `stream` (a torch stream or a raw HIP stream handle; None: torch's
+        current stream)."""
+        if self.tail == "serial":
             self.refresh_tail(stream)
+        if self.tail != "side":
+            self.select(stream)
+            self.attend(stream)
+            return
+        if stream is None:
+            main = torch.cuda.current_stream()
+        elif isinstance(stream, int):
+            main = torch.cuda.ExternalStream(stream, device=self.d.q.device)
+        else:
+            main = stream
+        self.side.wait_stream(main)  # fork: the rebuild starts after what `stream` already holds
+        self.refresh_tail(self.side.cuda_stream)
         self.select(stream)
         self.attend(stream)
+        main.wait_stream(self.side)  # join
 
     def lists(self) -> dict:
         """Host copy of the page lists: {(b, h): [pages]}."""

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 2
+    assert A.abi_version() == 3
 
 
 def test_error_strings(lib):
@@ -63,24 +63,24 @@ def sel_for(w, **over):
 FAKE = 0x1000  # never dereferenced: every case below fails validation first
 
 
-def score_rc(desc, sel, heads=None, ws=FAKE, ws_bytes=1 << 30, lse=FAKE):
+def score_rc(desc, sel, heads=None, ws=FAKE, ws_bytes=1 << 30, lse=FAKE, tail=0, k_pool=FAKE, k_scale=FAKE):
     heads = heads if heads is not None else [0] * max(1, desc.num_kv_heads)
     arr = (ctypes.c_uint8 * len(heads))(*heads)
-    return A.lib().spd_page_score(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, arr, FAKE, lse,
-                                  ws, ws_bytes, 0)
+    return A.lib().spd_page_score(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, k_pool, k_scale, tail, FAKE,
+                                  FAKE, arr, FAKE, lse, ws, ws_bytes, 0)
 
 
-def select_rc(desc, sel, heads=None, bt=FAKE, phys=None):
+def select_rc(desc, sel, heads=None, bt=FAKE, phys=None, k_pool=FAKE, k_scale=FAKE, meta=None):
     heads = heads if heads is not None else [0] * max(1, desc.num_kv_heads)
     arr = (ctypes.c_uint8 * len(heads))(*heads)
-    return A.lib().spd_page_select(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, arr, bt, FAKE, phys, FAKE, None,
-                                   0)
+    return A.lib().spd_page_select(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, arr, bt, k_pool, k_scale, meta,
+                                   FAKE, phys, FAKE, None, 0)
 
 
-def fused_rc(desc, sel, heads=None, ws=FAKE, ws_bytes=1 << 30, refresh=0, k_pool=FAKE, k_scale=FAKE, bt=FAKE):
+def fused_rc(desc, sel, heads=None, ws=FAKE, ws_bytes=1 << 30, tail=0, k_pool=FAKE, k_scale=FAKE, bt=FAKE):
     heads = heads if heads is not None else [0] * max(1, desc.num_kv_heads)
     arr = (ctypes.c_uint8 * len(heads))(*heads)
-    return A.lib().spd_page_score_select(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, k_pool, k_scale, refresh,
+    return A.lib().spd_page_score_select(ctypes.byref(desc), ctypes.byref(sel), FAKE, FAKE, k_pool, k_scale, tail,
                                          bt, FAKE, arr, FAKE, None, FAKE, None, None, None, ws, ws_bytes, 0)
 
 
@@ -168,10 +168,26 @@ def test_select_and_fused_argument_checks(lib):
     w = W.small()
     d = desc_for(w)
     assert select_rc(d, sel_for(w), bt=None, phys=FAKE) == A.SPD_ERR_INVALID_ARG   # physical pages need the table
+    assert select_rc(d, sel_for(w), bt=None, meta=FAKE) == A.SPD_ERR_INVALID_ARG   # so does the tail rebuild
+    assert select_rc(d, sel_for(w), k_pool=None, meta=FAKE) == A.SPD_ERR_INVALID_ARG  # which reads K
+    assert select_rc(desc_for(W.small(kv="fp8")), sel_for(w), k_scale=None, meta=FAKE) == A.SPD_ERR_INVALID_ARG
     assert fused_rc(d, sel_for(w), bt=None) == A.SPD_ERR_INVALID_ARG
-    assert fused_rc(d, sel_for(w), refresh=1, k_pool=None) == A.SPD_ERR_INVALID_ARG  # tail refresh reads K
+    assert fused_rc(d, sel_for(w), tail=A.TAIL_REBUILD, k_pool=None) == A.SPD_ERR_INVALID_ARG  # a rebuild reads K
+    assert score_rc(d, sel_for(w), tail=A.TAIL_REBUILD, k_pool=None) == A.SPD_ERR_INVALID_ARG
     wf = W.small(kv="fp8")
-    assert fused_rc(desc_for(wf), sel_for(wf), refresh=1, k_scale=None) == A.SPD_ERR_INVALID_ARG
+    assert fused_rc(desc_for(wf), sel_for(wf), tail=A.TAIL_REBUILD, k_scale=None) == A.SPD_ERR_INVALID_ARG
+    for bad in (-1, 3):
+        assert score_rc(d, sel_for(w), tail=bad) == A.SPD_ERR_INVALID_ARG
+        assert fused_rc(d, sel_for(w), tail=bad) == A.SPD_ERR_INVALID_ARG
+    # skipping the last page needs top-K with a local window (which keeps that page)
+    assert fused_rc(d, sel_for(w), tail=A.TAIL_SKIP, k_pool=None, ws=None) == A.SPD_ERR_WORKSPACE  # passes the tail check
+    no_local = sel_for(w)
+    no_local.n_local = 0
+    assert score_rc(d, no_local, tail=A.TAIL_SKIP) == A.SPD_ERR_INVALID_ARG
+    assert fused_rc(d, no_local, tail=A.TAIL_SKIP) == A.SPD_ERR_INVALID_ARG
+    wc = W.small(mode="coverage", gamma=0.9)
+    assert score_rc(desc_for(wc), sel_for(wc), tail=A.TAIL_SKIP) == A.SPD_ERR_INVALID_ARG
+    assert fused_rc(desc_for(wc), sel_for(wc), tail=A.TAIL_SKIP) == A.SPD_ERR_INVALID_ARG
     # rows longer than the longest compiled selection workgroup (65536 pages) are routed elsewhere
     long = desc_for(w, max_pages_per_seq=65537, max_list=65537)
     assert select_rc(long, sel_for(w)) == A.SPD_ERR_UNSUPPORTED

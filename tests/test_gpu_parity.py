@@ -29,13 +29,14 @@ def say(*a):
     print(*a, flush=True)
 
 
-def run_case(w, plan=None, fused=True, tail=False):
+def run_case(w, plan=None, fused=True, tail="none"):
     """Generate, upload, bulk-meta, one step.  Returns (inputs, device inputs, step)."""
-    say(f"[case] {w.name} seq={w.seq_lens[:8]} kv={w.kv_dtype} mode={w.mode} seed={w.seed} fused={fused}")
+    say(f"[case] {w.name} seq={w.seq_lens[:8]} kv={w.kv_dtype} mode={w.mode} seed={w.seed} fused={fused} "
+        f"tail={tail}")
     inp = W.generate(w)
     d = S.upload(inp)
     S.build_meta(w, d)
-    st = S.DecodeStep(w, d, plan=plan, fused=fused, tail_refresh=tail)
+    st = S.DecodeStep(w, d, plan=plan, fused=fused, tail=tail)
     st.run()
     torch.cuda.synchronize()
     return inp, d, st
@@ -168,11 +169,11 @@ def test_edge_cases_empty_tiny_and_degenerate_rows():
     P.check_attention(out, lse, ref["O"], ref["out_lse"], w.kv_dtype, "edges")
 
 
-def test_tail_refresh_updates_only_last_pages():
+def test_all_heads_tail_rebuild_updates_only_last_pages():
     w = W.small("tail", seq_lens=(333, 48, 1), budget=10)
     inp = W.generate(w)
     d = S.upload(inp)
-    st = S.DecodeStep(w, d, fused=False, tail_refresh=True)
+    st = S.DecodeStep(w, d, fused=False, tail="serial")
     sentinel = 3.0
     d.page_meta.fill_(sentinel)
     st.refresh_tail()
@@ -190,7 +191,7 @@ def test_fused_select_equals_unfused(mode):
     w = W.small("fused_" + mode, seq_lens=(3000, 700, 37, 0), streaming=(1,), Hkv=2, Hq=8, **kw)
     inp, d, st = run_case(w, fused=False)
     lists_unfused = st.lists()
-    st2 = S.DecodeStep(w, d, fused=True, tail_refresh=False)
+    st2 = S.DecodeStep(w, d, fused=True, tail="none")
     for rep in range(3):  # counters must return to zero between calls
         st2.run()
         torch.cuda.synchronize()
@@ -207,17 +208,23 @@ def test_fused_select_equals_unfused(mode):
     assert int(counters.abs().sum()) == 0  # tickets back at zero
 
 
-def test_fused_tail_refresh_rebuilds_the_last_page_of_dynamic_rows():
+@pytest.mark.parametrize("fused,tail", [(True, "rebuild"), (True, "side"), (True, "serial"), (False, "rebuild"),
+                                        (False, "side"), (False, "serial"), (False, "select")])
+def test_step_tail_modes_rebuild_the_last_page(fused, tail):
+    """A step rebuilds the statistics of each request's last page and of no other page: in the
+    scorer ("rebuild": dynamic heads only), or for all heads by the meta-build kernel ("side",
+    "serial") or the selector's spare workgroups ("select")."""
     for kv in ("f16", "fp8", "f32"):
         w = W.small("tail_" + kv, kv=kv, q="f32" if kv == "f32" else "f16", d=64 if kv == "f32" else 128,
                     seq_lens=(333, 48, 1, 0), budget=10, streaming=(1,), Hkv=2, Hq=8)
+        say(f"[case] tail={tail} fused={fused} kv={kv}")
         inp = W.generate(w)
         d = S.upload(inp)
         S.build_meta(w, d)
         ref_full = d.page_meta.clone()
         d.page_meta.fill_(3.0)  # sentinel everywhere
-        st = S.DecodeStep(w, d, fused=True, tail_refresh=True)
-        st.select()
+        st = S.DecodeStep(w, d, fused=fused, tail=tail)
+        st.run()
         torch.cuda.synchronize()
         got = d.page_meta.cpu().numpy()
         full = ref_full.cpu().numpy()
@@ -226,10 +233,42 @@ def test_fused_tail_refresh_rebuilds_the_last_page_of_dynamic_rows():
             for p in range(n):
                 phys = int(inp.block_table[b, p])
                 for h in range(w.num_kv_heads):
-                    if p == n - 1 and not inp.head_kind[h]:
+                    if p == n - 1 and (tail != "rebuild" or not inp.head_kind[h]):
                         assert np.array_equal(got[phys, h], full[phys, h]), (kv, b, p, h)
                     else:
                         assert np.all(got[phys, h] == 3.0), (kv, b, p, h)
+
+
+@pytest.mark.parametrize("mode", ["topk", "coverage"])
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
+def test_tail_modes_agree_on_current_statistics(mode, fused):
+    """With statistics already current, every tail mode gives the lists, physical pages and
+    outputs of the plain step bit for bit; the scores too, except that a skipping scorer
+    writes -inf for each dynamic row's last page."""
+    kw = dict(budget=40) if mode == "topk" else dict(mode="coverage", gamma=0.9, n_local=1, planted=("fixed", 6),
+                                                     delta=("nats", 6.0))
+    w = W.small("tails_" + mode, seq_lens=(3000, 700, 37, 1, 0, 16, 17), streaming=(1,), Hkv=2, Hq=8, **kw)
+    inp, d, ref = run_case(w, fused=fused, tail="none")
+    tails = ["rebuild", "serial"] + (["side"] if mode == "topk" else []) + \
+        (["select"] if mode == "topk" and not fused else [])
+    for tail in tails:
+        say(f"  tail={tail}")
+        st = S.DecodeStep(w, d, fused=fused, tail=tail)
+        for rep in range(2):
+            st.run()
+            torch.cuda.synchronize()
+            assert st.lists() == ref.lists(), (tail, rep)
+            for name in ("page_phys", "out", "out_lse"):
+                assert torch.equal(getattr(st, name), getattr(ref, name)), (tail, rep, name)
+            for b in range(w.batch):
+                n = O.n_pages(w.seq_lens[b])
+                got, want = st.scores[b, 0, :n].clone(), ref.scores[b, 0, :n]  # dynamic head 0
+                if tail in ("side", "select") and n:
+                    assert got[n - 1].item() == -np.inf, (tail, b)
+                    got[n - 1] = want[n - 1]
+                assert torch.equal(got, want), (tail, rep, b)
+            if mode == "coverage":
+                assert torch.equal(st.head_lse[:, :4], ref.head_lse[:, :4]), tail
 
 
 def test_deterministic_bitwise():
@@ -245,7 +284,7 @@ def test_deterministic_bitwise():
 
 def test_graph_replay_equals_eager_and_follows_new_inputs():
     w = W.small("graph", seq_lens=(2500, 900, 60), budget=32, streaming=(0,), Hkv=2, Hq=8)
-    inp, d, st = run_case(w, tail=True)
+    inp, d, st = run_case(w, fused=False, tail="side")  # the step's second stream is captured too
     eager = [t.clone() for t in (st.page_list, st.list_len, st.out, st.out_lse)]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
