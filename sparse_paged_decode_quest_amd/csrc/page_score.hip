@@ -7,9 +7,9 @@
 // (SPD_TAIL_SKIP, top-K: the local window keeps it whatever its score).
 //
 // Top-K mode writes score_p = max_g S_{g,p}.  Coverage mode (Moira, section 3.2, Eq. 3,
-// group-mean share) writes the log-mass l_{g,p} = s S_{g,p} + ln(valid_p) and per-block
-// (max, sum exp) pairs; a second kernel merges the pairs of the row into the per-head
-// log-sum-exp and writes pi_bar_p = (1/G) sum_g exp(l_{g,p} - lse_g).
+// group-mean share) writes the log-mass l_{g,p} = s S_{g,p} + ln(valid_p); a second kernel,
+// one workgroup per row, takes the per-head log-sum-exp over the row's log-masses and writes
+// pi_bar_p = (1/G) sum_g exp(l_{g,p} - lse_g).
 #include "score_common.h"
 #include "spd_launch.h"
 
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreAr
   const int len = a.seq_lens[r.b];
   if (r.tail) {
     const int n = row_pages(len, a.max_pages);
-    if (n > 0) score_tail<D, KVD, COV>(a, bt_row, n, len, r.b, r.h, (n - 1 + a.pages_per_block - 1) / a.pages_per_block);
+    if (n > 0) score_tail<D, KVD, COV>(a, bt_row, n, len, r.b, r.h, -1);
     return;
   }
   const int p_begin = r.blk * a.pages_per_block;
@@ -52,48 +52,82 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreAr
   float* sc_row = a.scores + ((size_t)r.b * a.num_kv_heads + r.h) * a.max_pages;
   if (!COV && a.tail_mode == SPD_TAIL_SKIP && r.blk == 0 && n > 0 && threadIdx.x == 0) sc_row[n - 1] = -INFINITY;
   if (p_begin >= n_scan) return;  // uniform over the block
-  if constexpr (COV) score_block_coverage<D, KVD, kScoreWaves, kScoreIters>(a, raw, n_scan, len, r.b, r.h, p_begin, r.blk);
+  if constexpr (COV) score_block_ell<D, KVD, kScoreWaves, kScoreIters>(a, raw, n_scan, len, r.b, r.h, p_begin);
   else score_block_topk<D, KVD, kScoreWaves, kScoreIters>(a, raw, n_scan, r.b, r.h, p_begin, sc_row);
 }
 
-// Partial slots a row's coverage pass filled: the scanning workgroups', then the tail's.
-__device__ __forceinline__ int coverage_slots(const ScoreArgs& a, int n) {
-  if (n == 0) return 0;
-  return (scan_pages(a, n) + a.pages_per_block - 1) / a.pages_per_block + tail_blocks(a);
-}
+// Coverage, second pass: one workgroup per dynamic row.  Every thread folds the log-masses of
+// its pages into a running (max, sum exp) per head, the workgroup combines those in a fixed
+// order into lse_g, and the shares are written from a second (cached) read of the log-masses.
+constexpr int kShareThreads = 1024;
+constexpr int kShareBatch = 8;  // pages per thread requested together
 
-// Coverage, second pass: per-head log-sum-exp of the row, then the group-mean share.
-__global__ __launch_bounds__(kScoreWaves * kWave) void coverage_share_kernel(ScoreArgs a) {
-  const int row_dyn = blockIdx.x / a.blocks_per_row;
-  const int blk = blockIdx.x % a.blocks_per_row;
-  const int b = row_dyn / a.dyn.count;
-  const int h = a.dyn.head[row_dyn % a.dyn.count];
+__global__ __launch_bounds__(kShareThreads) void coverage_share_kernel(ScoreArgs a) {
+  __shared__ float wm[kShareThreads / kWave][kG], ws[kShareThreads / kWave][kG];
+  __shared__ float lse_s[kG];
+  const int b = blockIdx.x / a.dyn.count;
+  const int h = a.dyn.head[blockIdx.x % a.dyn.count];
   const int n = row_pages(a.seq_lens[b], a.max_pages);
-  const int p_begin = blk * a.pages_per_block;
-  const int p_end = min(n, p_begin + a.pages_per_block);
-  if (p_begin >= p_end && blk != 0) return;  // block 0 of an empty row still writes head_lse
   const size_t row = (size_t)b * a.num_kv_heads + h;
-  float lse[kG];
-  row_head_lse(a.partials + row * a.partial_stride * kG, coverage_slots(a, n), lse);  // every wave, same bits
-  if (blk == 0 && threadIdx.x < kG && a.head_lse) {
-    float v = lse[0];
+  const float4* ell = a.ell + row * a.max_pages;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  float m[kG], s[kG];
 #pragma unroll
-    for (int g = 1; g < kG; ++g) v = (int)threadIdx.x == g ? lse[g] : v;
-    a.head_lse[(size_t)b * a.num_q_heads + (size_t)h * kG + threadIdx.x] = v;
+  for (int g = 0; g < kG; ++g) {
+    m[g] = -INFINITY;
+    s[g] = 0.f;
   }
-  for (int p = p_begin + threadIdx.x; p < p_end; p += blockDim.x)
-    a.scores[row * a.max_pages + p] = group_share(a.ell[row * a.max_pages + p], lse);
+  for (int p0 = 0; p0 < n; p0 += kShareThreads * kShareBatch) {
+    float4 v[kShareBatch];
+#pragma unroll
+    for (int k = 0; k < kShareBatch; ++k) {
+      const int p = p0 + k * kShareThreads + (int)threadIdx.x;
+      v[k] = p < n ? ell[p] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+#pragma unroll
+    for (int k = 0; k < kShareBatch; ++k) {
+      lse_push(m[0], s[0], v[k].x);
+      lse_push(m[1], s[1], v[k].y);
+      lse_push(m[2], s[2], v[k].z);
+      lse_push(m[3], s[3], v[k].w);
+    }
+  }
+  // wave: common max, then the rescaled sums; waves are folded in order by four threads
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const float M = wave_max_f(m[g]);
+    const float sc = m[g] == -INFINITY ? 0.f : s[g] * expf(m[g] - M);
+    const float S = wave_sum_f(sc);
+    if (lane == 0) {
+      wm[wave][g] = M;
+      ws[wave][g] = S;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kG) {
+    const int g = threadIdx.x;
+    float M = wm[0][g], S = ws[0][g];
+    for (int w = 1; w < kShareThreads / kWave; ++w) lse_combine(M, S, wm[w][g], ws[w][g]);
+    const float lse = M == -INFINITY ? -INFINITY : M + logf(S);
+    lse_s[g] = lse;
+    if (a.head_lse) a.head_lse[(size_t)b * a.num_q_heads + (size_t)h * kG + g] = lse;
+  }
+  __syncthreads();
+  float lse[kG];
+#pragma unroll
+  for (int g = 0; g < kG; ++g) lse[g] = lse_s[g];
+  for (int p = threadIdx.x; p < n; p += kShareThreads) a.scores[row * a.max_pages + p] = group_share(ell[p], lse);
 }
 
 int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool coverage, hipStream_t stream) {
   const unsigned rows = (unsigned)(a.batch * a.dyn.count);
   const dim3 grid(rows * (unsigned)(a.blocks_per_row + tail_blocks(a))), block(kScoreWaves * kWave);
-  const dim3 share_grid(rows * (unsigned)a.blocks_per_row);
+  const dim3 share_grid(rows), share_block(kShareThreads);
 #define SPD_SCORE_CASE(D, KVD)                                                                  \
   if (head_dim == D && kv_dtype == KVD) {                                                       \
     if (coverage) {                                                                             \
       hipLaunchKernelGGL((page_score_kernel<D, KVD, true>), grid, block, 0, stream, a);         \
-      hipLaunchKernelGGL(coverage_share_kernel, share_grid, block, 0, stream, a);               \
+      hipLaunchKernelGGL(coverage_share_kernel, share_grid, share_block, 0, stream, a);         \
     } else {                                                                                    \
       hipLaunchKernelGGL((page_score_kernel<D, KVD, false>), grid, block, 0, stream, a);        \
     }                                                                                           \

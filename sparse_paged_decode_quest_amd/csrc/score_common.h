@@ -354,6 +354,20 @@ __device__ __forceinline__ void coverage_logmass(const ScoreArgs& a, int valid, 
   for (int g = 0; g < kG; ++g) lg[g] = ok ? fmaf(a.sm_scale, s[g], lv) : -INFINITY;
 }
 
+// Coverage log-masses of the workgroup's pages [.., n), written per page (the scorer's first
+// pass; the row's per-head log-sum-exp is taken afterwards over these values).
+template <int D, int KVD, int NW, int ITERS>
+__device__ __forceinline__ void score_block_ell(const ScoreArgs& a, const int (&raw)[ITERS], int n, int len, int b,
+                                                int h, int p_begin) {
+  const size_t row = (size_t)b * a.num_kv_heads + h;
+  score_block<D, KVD, NW, ITERS>(a, raw, n, b, h, p_begin, [&](int p, bool ok, const float (&s)[kG]) {
+    if (p >= n) return;
+    float lg[kG];
+    coverage_logmass(a, valid_in_page(len, p), ok, s, lg);
+    a.ell[row * a.max_pages + p] = make_float4(lg[0], lg[1], lg[2], lg[3]);
+  });
+}
+
 // Coverage, first pass over the workgroup's pages [.., n): log-masses written per page, and one
 // (max, sum exp) pair per head for the workgroup in partial slot `slot`.  Moira, section 3.2: the
 // per-head softmax over pages needs the head's log-sum-exp over the whole row.
@@ -401,7 +415,7 @@ __device__ __forceinline__ void score_block_coverage(const ScoreArgs& a, const i
 }
 
 // The tail workgroup's work for either rule: the last page's top-K score, or its log-masses and
-// the (max, 1) pair of that single page in partial slot `slot`.
+// (slot >= 0, the fused kernel) the (max, 1) pair of that single page in partial slot `slot`.
 template <int D, int KVD, bool COV>
 __device__ __forceinline__ void score_tail(const ScoreArgs& a, const int32_t* bt_row, int n, int len, int b, int h,
                                            int slot) {
@@ -412,14 +426,18 @@ __device__ __forceinline__ void score_tail(const ScoreArgs& a, const int32_t* bt
       float lg[kG];
       coverage_logmass(a, valid_in_page(len, n - 1), true, s, lg);
       a.ell[row * a.max_pages + n - 1] = make_float4(lg[0], lg[1], lg[2], lg[3]);
+      if (slot >= 0) {
 #pragma unroll
-      for (int g = 0; g < kG; ++g) a.partials[(row * a.partial_stride + slot) * kG + g] = make_float2(lg[g], 1.f);
+        for (int g = 0; g < kG; ++g) a.partials[(row * a.partial_stride + slot) * kG + g] = make_float2(lg[g], 1.f);
+      }
       wrote = true;
     });
     if (threadIdx.x == 0 && !wrote) {  // page outside the pool: no mass
       a.ell[row * a.max_pages + n - 1] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (slot >= 0) {
 #pragma unroll
-      for (int g = 0; g < kG; ++g) a.partials[(row * a.partial_stride + slot) * kG + g] = make_float2(-INFINITY, 0.f);
+        for (int g = 0; g < kG; ++g) a.partials[(row * a.partial_stride + slot) * kG + g] = make_float2(-INFINITY, 0.f);
+      }
     }
   } else {
     bool wrote = false;

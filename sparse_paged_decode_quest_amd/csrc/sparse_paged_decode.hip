@@ -198,32 +198,6 @@ struct DecTraits<D, SPD_DTYPE_F32, SPD_DTYPE_F32> {
   static constexpr bool kScaled = false;
 };
 
-// Value of the lane 16 rows away (lane ^ 16) and 32 lanes away (lane ^ 32): gfx950's row swaps.
-__device__ __forceinline__ float xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
-}
-
-__device__ __forceinline__ float xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-}
-
-// Max / sum over the 16 lanes of a row (every lane of the row receives it), through DPP.
-__device__ __forceinline__ float row_max(float v) {
-  v = fmaxf(v, __uint_as_float(dpp<0xb1>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp<0x4e>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp<0x141>(__float_as_uint(v))));
-  return fmaxf(v, __uint_as_float(dpp<0x140>(__float_as_uint(v))));
-}
-
-__device__ __forceinline__ float row_sum(float v) {
-  v += __uint_as_float(dpp<0xb1>(__float_as_uint(v)));
-  v += __uint_as_float(dpp<0x4e>(__float_as_uint(v)));
-  v += __uint_as_float(dpp<0x141>(__float_as_uint(v)));
-  return v + __uint_as_float(dpp<0x140>(__float_as_uint(v)));
-}
-
 struct PageRef {
   int page;   // logical page, -1 when the entry is not a usable page
   int phys;

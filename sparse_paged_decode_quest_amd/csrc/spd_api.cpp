@@ -115,18 +115,17 @@ int launched(int rc) {
   return hipGetLastError() == hipSuccess ? SPD_OK : SPD_ERR_LAUNCH;
 }
 
+// Standalone coverage scorer: the per-page log-masses [B, Hkv, max_pages, G] between its two kernels.
 struct ScoreWs {
-  size_t ell_off, part_off, total;
+  size_t ell_off, total;
 };
 
 ScoreWs score_ws(const spd_desc* d) {
-  const int bpr = (d->max_pages_per_seq + score_ppb(d) - 1) / score_ppb(d);
   const size_t rows = (size_t)d->batch * d->num_kv_heads;
   const int G = d->num_q_heads / d->num_kv_heads;
   ScoreWs w;
   w.ell_off = 0;
-  w.part_off = align_up(rows * d->max_pages_per_seq * G * sizeof(float));
-  w.total = w.part_off + align_up(rows * (bpr + 1) * G * 2 * sizeof(float));  // + the tail workgroup's slot
+  w.total = align_up(rows * d->max_pages_per_seq * G * sizeof(float));
   return w;
 }
 
@@ -320,7 +319,6 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
     const ScoreWs w = score_ws(desc);
     if (!workspace || workspace_bytes < w.total) return SPD_ERR_WORKSPACE;
     a.ell = reinterpret_cast<float4*>(static_cast<char*>(workspace) + w.ell_off);
-    a.partials = reinterpret_cast<float2*>(static_cast<char*>(workspace) + w.part_off);
     a.head_lse = head_lse;
   }
   return launched(spd::launch_page_score(a, desc->head_dim, desc->kv_dtype, coverage, (hipStream_t)stream));

@@ -94,6 +94,45 @@ __device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int
   return (unsigned long long)lane_u32((uint32_t)v, lane) | ((unsigned long long)lane_u32((uint32_t)(v >> 32), lane) << 32);
 }
 
+// Value of the lane 16 rows away (lane ^ 16) and 32 lanes away (lane ^ 32): gfx950's row swaps.
+__device__ __forceinline__ float xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Max / sum over the 16 lanes of a row (every lane of the row receives it), through DPP.
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp<0xb1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<0x4e>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<0x141>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(dpp<0x140>(__float_as_uint(v))));
+}
+
+__device__ __forceinline__ float row_sum(float v) {
+  v += __uint_as_float(dpp<0xb1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<0x4e>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<0x141>(__float_as_uint(v)));
+  return v + __uint_as_float(dpp<0x140>(__float_as_uint(v)));
+}
+
+// Max / sum over the whole wave (every lane receives it).
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = row_max(v);
+  v = fmaxf(v, xor16(v));
+  return fmaxf(v, xor32(v));
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v = row_sum(v);
+  v += xor16(v);
+  return v + xor32(v);
+}
+
 // Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each row of 16 lanes, then the
 // row totals are carried across rows with the two row broadcasts.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
