@@ -18,13 +18,16 @@
 // Work layout.  Wave w holds the 64 KPL consecutive pages starting at 64 KPL w; its key slot
 // i holds page 64 KPL w + 64 i + lane, so every key load of a wave reads 64 consecutive scores
 // and page order is (wave, slot, lane) order.  The list is compacted with one ballot per slot
-// and scalar running counts inside a wave, plus one LDS exchange of the wave totals.  The
-// walk needs one workgroup barrier per digit: every wave then finds the crossing bin itself
-// from the shared histogram (three rotating histogram buffers make that safe), reading it
-// without LDS bank conflicts -- 64 lane sums over skewed addresses, a scan, and a second scan
-// inside the crossing lane's group of bins.  Top-K usually stops after one digit: when at
-// most kCandMax keys share the crossing bin, each wave ranks those candidates directly.  Ties
-// at the K'-th key are taken in page order.
+// and scalar running counts inside a wave, plus one LDS exchange of the wave totals.  Each
+// digit of the walk takes two workgroup barriers: after the histogram, and after wave 0 has
+// found the crossing bin in it (three rotating histogram buffers let the next digit's
+// histogram start at once) -- 64 lane sums over skewed addresses (no LDS bank conflicts), a
+// scan, and a second scan inside the crossing lane's group of bins.  Top-K usually stops after
+// one digit: when at most kCandMax keys share the crossing bin, wave 0 ranks those candidates
+// directly.  Ties at the K'-th key are taken in page order.  Values every wave needs from the
+// others (ranges, counts) are read one per lane and combined with DPP reductions and scans:
+// one LDS read per wave instead of one per wave entry, since sixteen waves reading the same
+// LDS words one by one were the bulk of the selection time.
 #pragma once
 
 #include <type_traits>
@@ -54,6 +57,12 @@ struct SelectSmem {
   int32_t cand_page[kCandMax];
   uint32_t cand_count;
   uint32_t wsure[NW], weq[NW];  // per-wave counts of kept-for-sure keys and keys equal to the cut key
+  struct {
+    int bin;       // crossing bin of the current digit (-1: coverage target out of reach)
+    H above, inbin;  // count / mass above the bin and inside it
+    uint32_t kc;     // top-K cut key found by ranking the crossing bin's keys
+    int need_eq;     // keys equal to kc still to take
+  } cross;
 };
 
 __device__ __forceinline__ unsigned long long share_fx(float pi) {
@@ -143,15 +152,10 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
   for (int e = threadIdx.x; e < 2 * kBins; e += STRIDE) (&sm.hist[0][0])[e] = 0;
   if (threadIdx.x == 0) sm.cand_count = 0;
   __syncthreads();
-  mn = sm.wmin[0];
-  mx = sm.wmax[0];
-  fmass = sm.wsum[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    mn = min(mn, sm.wmin[w]);
-    mx = max(mx, sm.wmax[w]);
-    fmass += sm.wsum[w];
-  }
+  // lane w < NW reads wave w's entries; DPP reductions give every lane the workgroup's values
+  mn = wave_min(lane < NW ? sm.wmin[lane] : 0xffffffffu);
+  mx = wave_max(lane < NW ? sm.wmax[lane] : 0u);
+  if (COV) fmass = wave_sum(lane < NW ? sm.wsum[lane] : 0ull);
 
   // ---- decision: 0 = forced pages only, 1 = every page, 2 = cut at key kc: keys above kc are
   // kept, keys equal to kc are kept in page order while fewer than need_eq of them were taken.
@@ -195,36 +199,43 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
           H* hc = sm.hist[(pass + 2) % 3];
           for (int e = threadIdx.x; e < kBins; e += STRIDE) hc[e] = 0;
         }
-        // crossing bin, found by every wave: lane l sums slots [l PER, (l+1) PER) (the l-th group
-        // from the top), reading them in a lane-skewed order so the wave's reads hit distinct banks
-        H s = 0;
+        // Crossing bin, found by wave 0 alone (one wave's histogram reads instead of every
+        // wave's): lane l sums slots [l PER, (l+1) PER) (the l-th group from the top), reading
+        // them in a lane-skewed order so the reads hit distinct banks; a scan finds the group,
+        // a second scan inside it the bin.  The others wait at the barrier and read the result.
+        if (wave == 0) {
+          H s = 0;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) s += h[lane * PER + ((j + lane) % PER)];
-        const H incl = wave_incl_scan(s);
-        const H excl = incl - s;
-        const unsigned long long hit = __ballot(excl < need && incl >= need);
-        if (hit == 0ull) {  // coverage only: the free pages cannot reach t -- keep every page
+          for (int j = 0; j < PER; ++j) s += h[lane * PER + ((j + lane) % PER)];
+          const H incl = wave_incl_scan(s);
+          const H excl = incl - s;
+          const unsigned long long hit = __ballot(excl < need && incl >= need);
+          if (hit == 0ull) {  // coverage only: the free pages cannot reach t -- keep every page
+            if (lane == 0) sm.cross.bin = -1;
+          } else {
+            const int owner = __ffsll((long long)hit) - 1;
+            H owner_excl;
+            if constexpr (COV) owner_excl = lane_u64(excl, owner);
+            else owner_excl = lane_u32(excl, owner);
+            // inside the owner's group: lane j < PER takes slot owner PER + j
+            const H v = lane < PER ? h[owner * PER + lane] : (H)0;
+            const H incl2 = wave_incl_scan(v) + owner_excl;
+            const unsigned long long hit2 = __ballot(lane < PER && incl2 - v < need && incl2 >= need);
+            const int jc = __ffsll((long long)hit2) - 1;
+            if (lane == jc) {
+              sm.cross.bin = kBins - 1 - (owner * PER + jc);
+              sm.cross.above = incl2 - v;
+              sm.cross.inbin = v;
+            }
+          }
+        }
+        __syncthreads();
+        const int bin = sm.cross.bin;
+        if (bin < 0) {
           dec = 1;
           break;
         }
-        const int owner = __ffsll((long long)hit) - 1;
-        H owner_excl;
-        if constexpr (COV) owner_excl = lane_u64(excl, owner);
-        else owner_excl = lane_u32(excl, owner);
-        // inside the owner's group: lane j < PER takes slot owner PER + j
-        const H v = lane < PER ? h[owner * PER + lane] : (H)0;
-        const H incl2 = wave_incl_scan(v) + owner_excl;
-        const unsigned long long hit2 = __ballot(lane < PER && incl2 - v < need && incl2 >= need);
-        const int jc = __ffsll((long long)hit2) - 1;
-        const int bin = kBins - 1 - (owner * PER + jc);
-        H above, inbin;
-        if constexpr (COV) {
-          above = lane_u64(incl2 - v, jc);
-          inbin = lane_u64(v, jc);
-        } else {
-          above = lane_u32(incl2 - v, jc);
-          inbin = lane_u32(v, jc);
-        }
+        const H above = sm.cross.above, inbin = sm.cross.inbin;
         need -= above;
         prefix |= (uint32_t)bin << shift;
         pmask |= (uint32_t)(nb - 1) << shift;
@@ -240,7 +251,8 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
           break;
         }
         if (!COV && inbin <= (H)kCandMax) {
-          // few keys left in the bin: gather them, and let each wave rank them itself
+          // few keys left in the bin: gather them; wave 0 ranks them (one candidate per lane,
+          // compared against every other through lane reads) and publishes the cut
           uint32_t c = 0;
 #pragma unroll
           for (int i = 0; i < KPL; ++i) c += (free_at(i) && (key[i] & pmask) == prefix) ? 1u : 0u;
@@ -258,19 +270,27 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
             }
           }
           __syncthreads();
-          const int m = (int)sm.cand_count;  // == inbin
-          const uint32_t ck = lane < m ? sm.cand_key[lane] : 0u;
-          const int cp = lane < m ? sm.cand_page[lane] : 0x7fffffff;
-          int rank = 0;
-          for (int j = 0; j < m; ++j) {
-            const uint32_t kj = sm.cand_key[j];
-            const int pj = sm.cand_page[j];
-            rank += (kj > ck || (kj == ck && pj < cp)) ? 1 : 0;
+          if (wave == 0) {
+            const int m = (int)sm.cand_count;  // == inbin
+            const uint32_t ck = lane < m ? sm.cand_key[lane] : 0u;
+            const int cp = lane < m ? sm.cand_page[lane] : 0x7fffffff;
+            int rank = 0;
+            for (int j = 0; j < m; ++j) {
+              const uint32_t kj = lane_u32(ck, j);
+              const int pj = (int)lane_u32((uint32_t)cp, j);
+              rank += (kj > ck || (kj == ck && pj < cp)) ? 1 : 0;
+            }
+            const unsigned long long cut = __ballot(lane < m && rank == (int)need - 1);
+            const uint32_t kcut = lane_u32(ck, __ffsll((long long)cut) - 1);
+            const int above_cut = __popcll(__ballot(lane < m && ck > kcut));
+            if (lane == 0) {
+              sm.cross.kc = kcut;
+              sm.cross.need_eq = (int)need - above_cut;
+            }
           }
-          const unsigned long long cut = __ballot(lane < m && rank == (int)need - 1);
-          kc = lane_u32(ck, __ffsll((long long)cut) - 1);
-          const int above_cut = __popcll(__ballot(lane < m && ck > kc));
-          need_eq = (int)need - above_cut;
+          __syncthreads();
+          kc = sm.cross.kc;
+          need_eq = sm.cross.need_eq;
           break;
         }
       }
@@ -303,15 +323,11 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
     sm.weq[wave] = eq_w;
   }
   __syncthreads();
-  uint32_t sure_before = 0, eq_before = 0, sure_total = 0, eq_total = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t sw = sm.wsure[w], ew = sm.weq[w];
-    sure_before += w < wave ? sw : 0u;
-    eq_before += w < wave ? ew : 0u;
-    sure_total += sw;
-    eq_total += ew;
-  }
+  // lane w < NW reads wave w's counts; inclusive scans give this wave's offsets and the totals
+  const uint32_t sw_l = lane < NW ? sm.wsure[lane] : 0u, ew_l = lane < NW ? sm.weq[lane] : 0u;
+  const uint32_t sw_incl = wave_incl_scan(sw_l), ew_incl = wave_incl_scan(ew_l);
+  const uint32_t sure_before = lane_u32(sw_incl - sw_l, wave), eq_before = lane_u32(ew_incl - ew_l, wave);
+  const uint32_t sure_total = lane_u32(sw_incl, NW - 1), eq_total = lane_u32(ew_incl, NW - 1);
   const uint32_t ne = (uint32_t)need_eq;
   uint32_t pos = sure_before + min(eq_before, ne);              // first list position of this wave
   const uint32_t total = sure_total + min(eq_total, ne);
