@@ -115,7 +115,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--fused", action="store_true", help="scorer and selector in one launch")
-    ap.add_argument("--plan", default=None, help="self-planning constants C,N_J,N_T (default: the library's)")
+    ap.add_argument("--plan", default=None,
+                    help="self-planning constants C,N_J,N_T[,balanced] (default: the step's for the workload)")
     ap.add_argument("--phase-only", default=None,
                     help="time only one phase per step (select|decode|merge|score|select_only)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -152,7 +153,10 @@ def main():
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
 
-    plan = S.Plan(*[int(x) for x in args.plan.split(",")]) if args.plan else None
+    plan = None
+    if args.plan:
+        v = [int(x) for x in args.plan.split(",")]
+        plan = S.Plan(*v[:3], balanced=bool(v[3]) if len(v) > 3 else False)
     probe = S.DecodeStep(w, base, plan=plan, fused=args.fused)
     probe.run()
     torch.cuda.synchronize()
@@ -280,7 +284,8 @@ def main():
                    "head_dim": w.head_dim, "page": 16, "kv_dtype": w.kv_dtype, "mode": w.mode,
                    "budget_pages": w.budget_pages, "gamma": w.gamma, "streaming_kv_heads": len(w.streaming_heads),
                    "layers_rotated": R, "graph": True, "fused_select": args.fused,
-                   "plan": [probe.plan.min_chunk, probe.plan.min_blocks_per_row, probe.plan.min_grid_blocks]},
+                   "plan": [probe.plan.min_chunk, probe.plan.min_blocks_per_row, probe.plan.min_grid_blocks,
+                            int(probe.plan.balanced)]},
         "step_us": round(step_us, 3), "tokens_per_s": round(w.batch / step_s, 1),
         "bytes_per_step": ab, "frac_of_peak": round(tbs / PEAK_HBM_TBS, 4),
         "phase_us": {k: round(v, 3) for k, v in phase_us.items()},

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 3
+#define SPD_ABI_VERSION 4
 #define SPD_PAGE_SIZE 16
 #define SPD_MAX_KV_HEADS 64
 
@@ -156,11 +156,20 @@ typedef struct spd_select_params {
 /* Self-planned split (Moira, section 3.3, Eq. 4): J = max(min_blocks_per_row,
  * ceil(min_grid_blocks / (B * Hkv))) blocks per row; row with n listed pages is cut into
  * chunks of c = max(min_chunk, ceil(n / J)) pages, m = ceil(n / c) of them; block j >= m
- * exits at once.  J is fixed by (B, Hkv) so a captured graph serves every list length. */
+ * exits at once.  J is fixed by (B, Hkv) so a captured graph serves every list length.
+ *
+ * balanced != 0 plans the whole step at once instead (for skewed list lengths): with T the
+ * total listed pages of all rows and n_max the longest list, every chunk holds
+ * c = max(min_chunk, ceil(T / N_T), ceil(n_max / 1024)) pages, row r has m_r = ceil(n_r / c)
+ * chunks, chunks are numbered row by row, and block k of the N_T + B * Hkv blocks processes
+ * chunk k (sum m_r <= N_T + B * Hkv).  Every block derives the plan from the list lengths on
+ * the device, so a captured graph still serves every list length.  min_blocks_per_row is
+ * not used; N_T >= 1. */
 typedef struct spd_plan_params {
   int32_t min_chunk;          /* C >= 1 */
   int32_t min_blocks_per_row; /* N_J >= 1 */
-  int32_t min_grid_blocks;    /* N_T >= 0 */
+  int32_t min_grid_blocks;    /* N_T >= 0 (>= 1 when balanced) */
+  int32_t balanced;           /* 0: per-row split (Eq. 4); 1: step-wide split */
 } spd_plan_params;
 
 /* ------------------------------------------------------------------ entry points */
@@ -253,7 +262,8 @@ int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float
 
 /* ------------------------------------------------------------------ host helpers */
 
-/* J, the blocks per row of spd_sparse_paged_decode (Moira, Eq. 4). */
+/* J, the blocks per row of spd_sparse_paged_decode (Moira, Eq. 4); for a balanced plan, the
+ * decode grid N_T + B * Hkv. */
 int spd_plan_grid(const spd_desc* desc, const spd_plan_params* plan, int32_t* blocks_per_row);
 
 /* Chunk size c and chunk count m of a row with n_pages listed pages under J blocks per

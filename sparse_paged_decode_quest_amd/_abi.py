@@ -51,7 +51,8 @@ class SelectParams(ctypes.Structure):
 
 
 class PlanParams(ctypes.Structure):
-    _fields_ = [("min_chunk", c_int32), ("min_blocks_per_row", c_int32), ("min_grid_blocks", c_int32)]
+    _fields_ = [("min_chunk", c_int32), ("min_blocks_per_row", c_int32), ("min_grid_blocks", c_int32),
+                ("balanced", c_int32)]
 
 
 _lib = None

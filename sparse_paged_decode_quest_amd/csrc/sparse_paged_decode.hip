@@ -198,6 +198,83 @@ struct DecTraits<D, SPD_DTYPE_F32, SPD_DTYPE_F32> {
   static constexpr bool kScaled = false;
 };
 
+// ------------------------------------------------------------ step-wide (balanced) split
+constexpr int kMaxChunks = 1024;  // chunks of one row the merge holds
+
+__device__ __forceinline__ int clamp_len(int n, int max_list) { return n < 0 ? 0 : (n > max_list ? max_list : n); }
+
+// Chunk size of the balanced plan, c = max(C, ceil(T / N_T), ceil(n_max / kMaxChunks)), from
+// every row's list length (computed by the calling wave; every lane receives it).
+__device__ __forceinline__ int balanced_chunk(const int32_t* list_len, int rows, int max_list, int C, int NT) {
+  const int lane = threadIdx.x % kWave;
+  unsigned long long tot = 0;
+  uint32_t nmax = 0;
+  for (int r0 = 0; r0 < rows; r0 += kWave) {
+    const int r = r0 + lane;
+    const int n = r < rows ? clamp_len(list_len[r], max_list) : 0;
+    tot += (unsigned long long)n;
+    nmax = max(nmax, (uint32_t)n);
+  }
+  tot = wave_sum(tot);
+  nmax = wave_max(nmax);
+  unsigned long long c = (unsigned long long)C;
+  c = max(c, (tot + (unsigned long long)NT - 1) / (unsigned long long)NT);
+  c = max(c, (unsigned long long)((nmax + kMaxChunks - 1) / kMaxChunks));
+  return (int)c;
+}
+
+// Chunk k of the balanced plan: its row, its index j in the row, the row's chunk count m, the
+// number of the row's first chunk and the row's list length.  False when k is past the last chunk.
+struct ChunkPos {
+  int row, j, m, first, n;
+};
+
+__device__ __forceinline__ bool balanced_locate(const int32_t* list_len, int rows, int max_list, int c, int k,
+                                                ChunkPos& cp) {
+  const int lane = threadIdx.x % kWave;
+  uint32_t base = 0;
+  for (int r0 = 0; r0 < rows; r0 += kWave) {
+    const int r = r0 + lane;
+    const int n = r < rows ? clamp_len(list_len[r], max_list) : 0;
+    const uint32_t m = (uint32_t)((n + c - 1) / c);
+    const uint32_t incl = wave_incl_scan(m) + base;
+    const unsigned long long hit = __ballot(m > 0 && incl > (uint32_t)k && incl - m <= (uint32_t)k);
+    if (hit) {
+      const int l = __ffsll((long long)hit) - 1;
+      cp.row = r0 + l;
+      cp.m = (int)lane_u32(m, l);
+      cp.first = (int)(lane_u32(incl, l) - (uint32_t)cp.m);
+      cp.j = k - cp.first;
+      cp.n = (int)lane_u32((uint32_t)n, l);
+      return true;
+    }
+    base = lane_u32(incl, kWave - 1);
+  }
+  return false;
+}
+
+// First chunk number and chunk count of row `row` in the balanced plan.
+__device__ __forceinline__ void balanced_row(const int32_t* list_len, int rows, int max_list, int c, int row,
+                                             int& first, int& m) {
+  const int lane = threadIdx.x % kWave;
+  uint32_t base = 0;
+  for (int r0 = 0; r0 < rows; r0 += kWave) {
+    const int r = r0 + lane;
+    const int n = r < rows ? clamp_len(list_len[r], max_list) : 0;
+    const uint32_t mm = (uint32_t)((n + c - 1) / c);
+    const uint32_t incl = wave_incl_scan(mm) + base;
+    if (row < r0 + kWave) {
+      const int l = row - r0;
+      m = (int)lane_u32(mm, l);
+      first = (int)(lane_u32(incl, l) - (uint32_t)m);
+      return;
+    }
+    base = lane_u32(incl, kWave - 1);
+  }
+  first = 0;
+  m = 0;
+}
+
 struct PageRef {
   int page;   // logical page, -1 when the entry is not a usable page
   int phys;
@@ -229,20 +306,43 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   const int lane = threadIdx.x % kWave;
   const int tok = lane & (kPage - 1);  // QK role: token of the page
   const int quarter = lane >> 4;       // QK role: channel quarter, and after the reduce-scatter the head
-  const int row = blockIdx.x / a.blocks_per_row;
-  const int j = blockIdx.x % a.blocks_per_row;
+  // Which chunk of which row this block processes: per-row plan (Moira Eq. 4, block (row, j)),
+  // or the step-wide plan (block k takes chunk k of the row-by-row numbering).
+  int row, j, c = 0, m = 0, n = 0;
+  size_t slot_row;  // partial-state slot of chunk 0 of the row: row * J, or the row's first chunk number
+  if (a.balanced) {
+    const int rows = a.batch * a.num_kv_heads;
+    c = balanced_chunk(a.list_len, rows, a.max_list, a.min_chunk, a.grid_target);
+    if ((int)blockIdx.x < rows && clamp_len(a.list_len[blockIdx.x], a.max_list) == 0) {
+      // row blockIdx.x has no chunk: this block writes its empty result
+      const size_t q0 = (size_t)(blockIdx.x / a.num_kv_heads) * a.num_q_heads + (size_t)(blockIdx.x % a.num_kv_heads) * kGq;
+      for (int e = threadIdx.x; e < kGq * D; e += blockDim.x) a.out[q0 * D + e] = 0.f;
+      if (threadIdx.x < kGq) a.out_lse[q0 + threadIdx.x] = -INFINITY;
+    }
+    ChunkPos cp;
+    if (!balanced_locate(a.list_len, rows, a.max_list, c, (int)blockIdx.x, cp)) return;
+    row = cp.row;
+    j = cp.j;
+    m = cp.m;
+    n = cp.n;
+    slot_row = (size_t)cp.first;
+  } else {
+    row = blockIdx.x / a.blocks_per_row;
+    j = blockIdx.x % a.blocks_per_row;
+    slot_row = (size_t)row * a.blocks_per_row;
+  }
   const int b = row / a.num_kv_heads;
   const int h = row % a.num_kv_heads;
   const size_t qrow = (size_t)b * a.num_q_heads + (size_t)h * kGq;  // first query head of the group
 
   const int32_t* list = a.page_list + (size_t)row * a.max_list;
   const int32_t* plist = a.page_phys ? a.page_phys + (size_t)row * a.max_list : nullptr;
-  // The list entries of this wave's first 64 pages are requested together with the row's list
-  // length, assuming the chunk starts at j * min_chunk -- true whenever the row fits in
+  // Per-row plan: the list entries of this wave's first 64 pages are requested together with the
+  // row's list length, assuming the chunk starts at j * min_chunk -- true whenever the row fits in
   // J * min_chunk pages, where the chunk size is the minimum; otherwise they are read again.
-  const int spec_i0 = j * a.min_chunk;
+  const int spec_i0 = a.balanced ? -1 : j * a.min_chunk;
   int spec_lp = -1, spec_lph = -1;
-  {
+  if (!a.balanced) {
     const int idx = spec_i0 + wave + 4 * lane;
     if (idx < a.max_list) {
       spec_lp = list[idx];
@@ -251,18 +351,18 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   }
   typename T::Q q;
   T::load_q(q, a.q, qrow * D, quarter);
-  int n = a.list_len[row];
-  n = n < 0 ? 0 : (n > a.max_list ? a.max_list : n);
-  if (n == 0) {
-    if (j == 0) {
-      for (int e = threadIdx.x; e < kGq * D; e += blockDim.x) a.out[qrow * D + e] = 0.f;
-      if (threadIdx.x < kGq) a.out_lse[qrow + threadIdx.x] = -INFINITY;
+  if (!a.balanced) {
+    n = clamp_len(a.list_len[row], a.max_list);
+    if (n == 0) {
+      if (j == 0) {
+        for (int e = threadIdx.x; e < kGq * D; e += blockDim.x) a.out[qrow * D + e] = 0.f;
+        if (threadIdx.x < kGq) a.out_lse[qrow + threadIdx.x] = -INFINITY;
+      }
+      return;
     }
-    return;
+    plan_chunks(n, a.blocks_per_row, a.min_chunk, c, m);
+    if (j >= m) return;
   }
-  int c, m;
-  plan_chunks(n, a.blocks_per_row, a.min_chunk, c, m);
-  if (j >= m) return;
   const int i0 = j * c;
   const int i1 = min(n, i0 + c);
   const int len = a.seq_lens[b];
@@ -411,7 +511,7 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
       a.out[(qrow + g) * D + ch] = o;
       if (ch == 0) a.out_lse[qrow + g] = lse;
     } else {
-      const size_t slot = ((size_t)row * a.blocks_per_row + j) * kGq + g;
+      const size_t slot = (slot_row + j) * kGq + g;
       a.part_o[slot * D + ch] = o;
       if (ch == 0) a.part_lse[slot] = lse;
     }
@@ -426,7 +526,6 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
 // trip.  Chunk weights exp(lse_j - lse) go through LDS; D channels x (1024 / D) chunk
 // partitions accumulate in parallel and the partitions are summed in a fixed order.
 constexpr int kMergeThreads = 1024;
-constexpr int kMaxChunks = 1024;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
@@ -442,25 +541,33 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
   const int J = a.blocks_per_row;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int ch = threadIdx.x % D, part = threadIdx.x / D;
-  const size_t slot0 = (size_t)row * J * kGq + g;  // + j * kGq
-
-  // speculative loads: list length, chunk lse values, first chunk outputs
+  // Balanced plan: the row's chunk count and first chunk number come from every row's list length
+  // (one more dependent read before the chunk states).
+  int c, m, first = 0;
   int n = a.list_len[row];
+  if (a.balanced) {
+    const int rows = a.batch * a.num_kv_heads;
+    c = balanced_chunk(a.list_len, rows, a.max_list, a.min_chunk, a.grid_target);
+    balanced_row(a.list_len, rows, a.max_list, c, row, first, m);
+  }
+  const size_t slot0 = (a.balanced ? (size_t)first : (size_t)row * J) * kGq + g;  // + j * kGq
+  const int J_read = a.balanced ? m : J;  // chunk slots of the row that may be read
+
+  // speculative loads (per-row plan: before the row's chunk count is known): chunk lse values,
+  // first chunk outputs
   float lse_j[(kMaxChunks + kMergeThreads - 1) / kMergeThreads];
 #pragma unroll
   for (int k = 0; k < (kMaxChunks + kMergeThreads - 1) / kMergeThreads; ++k) {
     const int jj = (int)threadIdx.x + k * kMergeThreads;
-    lse_j[k] = jj < J ? a.part_lse[slot0 + (size_t)jj * kGq] : -INFINITY;
+    lse_j[k] = jj < J_read ? a.part_lse[slot0 + (size_t)jj * kGq] : -INFINITY;
   }
   float pre[kPre];
 #pragma unroll
   for (int u = 0; u < kPre; ++u) {
     const int jj = part + u * PARTS;
-    pre[u] = jj < J ? a.part_o[(slot0 + (size_t)jj * kGq) * D + ch] : 0.f;
+    pre[u] = jj < J_read ? a.part_o[(slot0 + (size_t)jj * kGq) * D + ch] : 0.f;
   }
-  n = n < 0 ? 0 : (n > a.max_list ? a.max_list : n);
-  int c, m;
-  plan_chunks(n, J, a.min_chunk, c, m);
+  if (!a.balanced) plan_chunks(clamp_len(n, a.max_list), J, a.min_chunk, c, m);
   if (m <= 1) return;
 
   float mx = -INFINITY;
@@ -517,7 +624,8 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
 }
 
 int launch_sparse_paged_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype, hipStream_t stream) {
-  dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.blocks_per_row)), block(256);
+  // per-row plan: rows x J blocks; balanced plan: blocks_per_row holds the whole grid N_T + rows
+  dim3 grid((unsigned)(a.balanced ? a.blocks_per_row : a.batch * a.num_kv_heads * a.blocks_per_row)), block(256);
 #define SPD_DEC_CASE(D, QD, KVD)                                                                 \
   if (head_dim == D && q_dtype == QD && kv_dtype == KVD) {                                       \
     hipLaunchKernelGGL((sparse_paged_decode_kernel<D, QD, KVD>), grid, block, 0, stream, a);     \

@@ -100,9 +100,18 @@ int head_lists(const spd_desc* d, const uint8_t* head_kind, spd::HeadList& dyn, 
   return SPD_OK;
 }
 
+// J of the per-row plan (blocks per row), or the grid N_T + rows of the balanced plan.
 int plan_j(const spd_desc* d, const spd_plan_params* p, int32_t& J) {
   if (!p || p->min_chunk < 1 || p->min_blocks_per_row < 1 || p->min_grid_blocks < 0) return SPD_ERR_INVALID_ARG;
+  if (p->balanced != 0 && p->balanced != 1) return SPD_ERR_INVALID_ARG;
   const int64_t rows = (int64_t)d->batch * d->num_kv_heads;
+  if (p->balanced) {
+    if (p->min_grid_blocks < 1) return SPD_ERR_INVALID_ARG;
+    const int64_t grid = (int64_t)p->min_grid_blocks + rows;
+    if (grid > ((int64_t)1 << 31) - 1) return SPD_ERR_INVALID_ARG;
+    J = (int32_t)grid;
+    return SPD_OK;
+  }
   int64_t j = p->min_blocks_per_row;
   if (rows > 0) j = std::max<int64_t>(j, (p->min_grid_blocks + rows - 1) / rows);
   if (j > 1024 || rows * j > ((int64_t)1 << 31) - 1) return SPD_ERR_INVALID_ARG;  // merge holds <= 1024 chunks
@@ -258,7 +267,9 @@ int spd_partials_size(const spd_desc* desc, const spd_plan_params* plan, size_t*
   int32_t J;
   rc = plan_j(desc, plan, J);
   if (rc) return rc;
-  const size_t slots = (size_t)desc->batch * desc->num_q_heads * J;  // rows * J * G
+  // rows * J * G chunk states, or (balanced) one per chunk of the N_T + rows grid, times G
+  const size_t slots = plan->balanced ? (size_t)J * (desc->num_q_heads / desc->num_kv_heads)
+                                      : (size_t)desc->batch * desc->num_q_heads * J;
   *part_lse_elems = slots;
   *part_o_elems = slots * desc->head_dim;
   return SPD_OK;
@@ -427,6 +438,8 @@ int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, c
   a.max_list = desc->max_list;
   a.blocks_per_row = J;
   a.min_chunk = plan->min_chunk;
+  a.balanced = plan->balanced;
+  a.grid_target = plan->min_grid_blocks;
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   return launched(spd::launch_sparse_paged_decode(a, desc->head_dim, desc->q_dtype, desc->kv_dtype,
                                                   (hipStream_t)stream));
@@ -452,6 +465,8 @@ int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float
   a.max_list = desc->max_list;
   a.blocks_per_row = J;
   a.min_chunk = plan->min_chunk;
+  a.balanced = plan->balanced;
+  a.grid_target = plan->min_grid_blocks;
   return launched(spd::launch_lse_merge(a, desc->head_dim, (hipStream_t)stream));
 }
 

@@ -114,6 +114,7 @@ struct DecodeArgs {
   float* part_lse;
   int batch, num_q_heads, num_kv_heads, max_pages, num_pool_pages, max_list;
   int blocks_per_row, min_chunk;
+  int balanced, grid_target;  // step-wide split over grid_target (N_T) + rows blocks
   float sm_scale_log2;  // softmax scale times log2(e)
 };
 int launch_sparse_paged_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype,
@@ -126,6 +127,7 @@ struct MergeArgs {
   float* out;
   float* out_lse;
   int batch, num_q_heads, num_kv_heads, max_list, blocks_per_row, min_chunk;
+  int balanced, grid_target;
 };
 int launch_lse_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 

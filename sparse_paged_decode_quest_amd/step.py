@@ -28,13 +28,15 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "fp8": torch.uint8}
 class Plan:
     """Self-planned split constants (Moira, section 3.3, Eq. 4), re-chosen for 16-token pages
     and 256 compute units: a chunk of at least 4 pages (one per wave of a block) and at least
-    512 blocks over the grid."""
+    512 blocks over the grid.  ``balanced`` splits the step's total listed pages evenly instead
+    of each row into J chunks (for skewed list lengths; see spd_plan_params)."""
     min_chunk: int = 4
     min_blocks_per_row: int = 16
     min_grid_blocks: int = 512
+    balanced: bool = False
 
     def params(self) -> A.PlanParams:
-        return A.PlanParams(self.min_chunk, self.min_blocks_per_row, self.min_grid_blocks)
+        return A.PlanParams(self.min_chunk, self.min_blocks_per_row, self.min_grid_blocks, int(self.balanced))
 
 
 @dataclasses.dataclass
@@ -125,7 +127,8 @@ class DecodeStep:
         if tail == "select" and fused:
             raise ValueError("tail='select' needs the separate selector (fused=False)")
         self.w, self.d = w, d
-        self.plan = plan or Plan()
+        # coverage lists range from the forced pages to the whole row: split the step evenly
+        self.plan = plan or (Plan(balanced=True, min_grid_blocks=1024) if w.mode == "coverage" else Plan())
         self.fused = fused
         self.tail = tail
         self.tail_mode = {"none": A.TAIL_NONE, "select": A.TAIL_SKIP, "side": A.TAIL_SKIP, "serial": A.TAIL_NONE,

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 3
+    assert A.abi_version() == 4
 
 
 def test_error_strings(lib):
@@ -225,6 +225,25 @@ def test_plan_grid_formula(lib):
         assert J == max(NJ, -(-NT // (B * Hkv)))
         po, pl = A.spd_partials_size(d, A.PlanParams(C, NJ, NT))
         assert pl == B * Hkv * J * 4 and po == pl * w.head_dim
+    # balanced plan: the grid is N_T + rows and holds one chunk state per block
+    for B, Hkv, NT in [(1, 8, 512), (4, 8, 1024), (2, 2, 1)]:
+        d = desc_for(w, batch=B, num_kv_heads=Hkv, num_q_heads=4 * Hkv)
+        assert A.spd_plan_grid(d, A.PlanParams(4, 16, NT, 1)) == NT + B * Hkv
+        po, pl = A.spd_partials_size(d, A.PlanParams(4, 16, NT, 1))
+        assert pl == (NT + B * Hkv) * 4 and po == pl * w.head_dim
+    d = desc_for(w)
+    for bad in (A.PlanParams(4, 16, 0, 1), A.PlanParams(4, 16, 512, 2), A.PlanParams(0, 16, 512, 1)):
+        with pytest.raises(A.SpdError):
+            A.spd_plan_grid(d, bad)
+    # ... and the chunk count it documents never exceeds that grid, nor 1024 chunks in a row
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        rows, NT, C = int(rng.integers(1, 200)), int(rng.integers(1, 5000)), int(rng.integers(1, 40))
+        n = rng.integers(0, 70000, size=rows) * (rng.random(rows) < 0.8)
+        T, nmax = int(n.sum()), int(n.max())
+        c = max(C, -(-T // NT), -(-nmax // 1024))
+        m = -(-n // c)
+        assert int(m.sum()) <= NT + rows and int(m.max()) <= 1024
     # chunk sizes: every chunk holds at least C pages, at most J chunks, all pages covered once
     rng = np.random.default_rng(0)
     for _ in range(500):

@@ -117,20 +117,22 @@ def test_small_meta_scores_lists_attention(name, fused):
             P.check_attention(out[b, sl], out_lse[b, sl], o_ref[b, sl], lse_ref[b, sl], w.kv_dtype, f"row {b},{h}")
 
     # decode alone, fed the oracle's lists
-    pl = torch.zeros_like(st.page_list)
-    ll = torch.zeros_like(st.list_len)
-    for (b, h), lst in oracle_lists.items():
-        pl[b, h, :len(lst)] = torch.tensor(lst, dtype=torch.int32)
-        ll[b, h] = len(lst)
-    st.page_list.copy_(pl)
-    st.list_len.copy_(ll)
+    set_lists(st, oracle_lists)
+    poison_outputs(st)
     st.attend()
     torch.cuda.synchronize()
     P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), o_ref, lse_ref, w.kv_dtype, "oracle lists")
 
 
+def poison_outputs(st):
+    """NaN in every output, so a row the decode or merge fails to write cannot pass."""
+    st.out.fill_(float("nan"))
+    st.out_lse.fill_(float("nan"))
+
+
 @pytest.mark.parametrize("plan", [S.Plan(1, 1, 0), S.Plan(2, 3, 0), S.Plan(4, 16, 512), S.Plan(24, 32, 4096),
-                                  S.Plan(1000, 1, 0)])
+                                  S.Plan(1000, 1, 0), S.Plan(1, 1, 1, True), S.Plan(2, 1, 3, True),
+                                  S.Plan(4, 16, 16, True), S.Plan(4, 16, 1024, True)])
 def test_plan_invariance(plan):
     w = SMALL["f16_d128"].replace(budget_pages=60)
     inp, d, st = run_case(w, plan=plan)
@@ -138,6 +140,7 @@ def test_plan_invariance(plan):
     o_ref, lse_ref = O.sparse_paged_decode(inp, lists_from_oracle(inp), w.sm_scale)
     # decode over oracle lists under this plan
     set_lists(st, lists_from_oracle(inp))
+    poison_outputs(st)
     st.attend()
     torch.cuda.synchronize()
     P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), o_ref, lse_ref, w.kv_dtype, str(plan))
@@ -148,22 +151,33 @@ def lists_from_oracle(inp):
 
 
 def set_lists(st, lists):
+    """Page lists (and, when the step keeps them, their physical pages) written by the host."""
     pl = torch.zeros_like(st.page_list)
     ll = torch.zeros_like(st.list_len)
+    bt = st.d.block_table.cpu()
+    pp = torch.zeros_like(pl)
     for (b, h), lst in lists.items():
         pl[b, h, :len(lst)] = torch.tensor(lst, dtype=torch.int32)
+        pp[b, h, :len(lst)] = bt[b, lst] if lst else pp[b, h, :0]
         ll[b, h] = len(lst)
     st.page_list.copy_(pl)
     st.list_len.copy_(ll)
+    if st.page_phys is not None:
+        st.page_phys.copy_(pp)
 
 
-def test_edge_cases_empty_tiny_and_degenerate_rows():
+@pytest.mark.parametrize("plan", [None, S.Plan(1, 1, 2, True), S.Plan(4, 16, 512, True)],
+                         ids=["per_row", "balanced_tiny_grid", "balanced"])
+def test_edge_cases_empty_tiny_and_degenerate_rows(plan):
     # lengths 0, 1, 15, 16, 17; budget larger than rows; forced pages overlapping
     w = W.small("edges", seq_lens=(0, 1, 15, 16, 17, 48, 49, 160), budget=3, n_sink=2, n_local=2,
                 streaming=(1,), n_sink_stream=3, n_local_stream=3, Hkv=2, Hq=8, hole=0.5)
-    inp, d, st = run_case(w)
+    inp, d, st = run_case(w, plan=plan)
     ref = O.decode_step(inp)
     assert st.lists() == ref["lists"]
+    poison_outputs(st)
+    st.attend()
+    torch.cuda.synchronize()
     out, lse = st.out.cpu().numpy(), st.out_lse.cpu().numpy()
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))  # empty request
     P.check_attention(out, lse, ref["O"], ref["out_lse"], w.kv_dtype, "edges")
@@ -269,6 +283,24 @@ def test_tail_modes_agree_on_current_statistics(mode, fused):
                 assert torch.equal(got, want), (tail, rep, b)
             if mode == "coverage":
                 assert torch.equal(st.head_lse[:, :4], ref.head_lse[:, :4]), tail
+
+
+def test_balanced_plan_on_skewed_coverage_lists():
+    """Coverage lists from the forced pages up to whole rows, decoded under the step-wide split
+    and under the per-row split: both match the oracle over the GPU's lists."""
+    w = W.small("skew", mode="coverage", gamma=0.97, n_local=1, seq_lens=(16000, 40, 0, 5000, 17, 9000),
+                planted=("fixed", 6), delta=("nats", 6.0), Hkv=2, Hq=8)
+    inp, d, st = run_case(w, plan=S.Plan(4, 16, 64, True))
+    lists = st.lists()
+    o_ref, lse_ref = O.sparse_paged_decode(inp, lists, w.sm_scale)
+    P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), o_ref, lse_ref, w.kv_dtype, "balanced")
+    for plan in (S.Plan(), S.Plan(1, 1, 1, True), S.Plan(4, 16, 4096, True)):
+        st2 = S.DecodeStep(w, d, plan=plan)
+        set_lists(st2, lists)
+        poison_outputs(st2)
+        st2.attend()
+        torch.cuda.synchronize()
+        P.check_attention(st2.out.cpu().numpy(), st2.out_lse.cpu().numpy(), o_ref, lse_ref, w.kv_dtype, str(plan))
 
 
 def test_deterministic_bitwise():

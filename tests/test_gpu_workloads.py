@@ -96,11 +96,15 @@ def test_named_workload(name):
     # 3. decode fed the oracle's lists on the sampled rows (the GPU's lists elsewhere)
     pl = st.page_list.clone()
     ll = st.list_len.clone()
+    pp = st.page_phys.clone()
     for (b, h), lst in oracle_lists.items():
         pl[b, h, :len(lst)] = torch.tensor(lst, dtype=torch.int32)
+        pp[b, h, :len(lst)] = torch.from_numpy(inp.block_table[b, lst].astype(np.int32))
         ll[b, h] = len(lst)
     st.page_list.copy_(pl)
     st.list_len.copy_(ll)
+    st.page_phys.copy_(pp)
+    st.out.fill_(float("nan"))
     st.attend()
     torch.cuda.synchronize()
     out, out_lse = st.out.cpu().numpy(), st.out_lse.cpu().numpy()
