@@ -7,8 +7,8 @@
 // (SPD_TAIL_SKIP, top-K: the local window keeps it whatever its score).
 //
 // Top-K mode writes score_p = max_g S_{g,p}.  Coverage mode (Moira, section 3.2, Eq. 3,
-// group-mean share) writes the log-mass l_{g,p} = s S_{g,p} + ln(valid_p); a second kernel,
-// one workgroup per row, takes the per-head log-sum-exp over the row's log-masses and writes
+// group-mean share) writes the log-mass l_{g,p} = s S_{g,p} + ln(valid_p); two more kernels
+// take the per-head log-sum-exp over the row's log-masses and write
 // pi_bar_p = (1/G) sum_g exp(l_{g,p} - lse_g).
 #include "score_common.h"
 #include "spd_launch.h"
@@ -56,77 +56,129 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreAr
   else score_block_topk<D, KVD, kScoreWaves, kScoreIters>(a, raw, n_scan, r.b, r.h, p_begin, sc_row);
 }
 
-// Coverage, second pass: one workgroup per dynamic row.  Every thread folds the log-masses of
-// its pages into a running (max, sum exp) per head, the workgroup combines those in a fixed
-// order into lse_g, and the shares are written from a second (cached) read of the log-masses.
+// Coverage, second and third passes, over blocks of kSharePages pages of a row (one page per
+// thread, so the exponentials of a row are spread over many workgroups):
+//  * coverage_part_kernel: each block's (max, sum exp) of the log-masses, per head;
+//  * coverage_share_kernel: wave 0 folds the row's block pairs into lse_g (fixed order) while
+//    every thread reads its page's log-masses; then pi_bar_p = (1/G) sum_g exp(l_{g,p} - lse_g).
 constexpr int kShareThreads = 1024;
-constexpr int kShareBatch = 8;  // pages per thread requested together
+constexpr int kSharePages = kShareThreads;
+constexpr int kShareWaves = kShareThreads / kWave;
+
+__host__ __device__ inline int share_blocks_per_row(int max_pages) { return (max_pages + kSharePages - 1) / kSharePages; }
+
+// Workgroup max and sum over kShareThreads lanes of four values per lane (every thread receives
+// them); `red` holds one entry per wave and head.
+__device__ __forceinline__ float block_max_f(float v, float (&red)[kShareWaves]) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  v = wave_max_f(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float r = wave_max_f(lane < kShareWaves ? red[lane] : -INFINITY);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_sum_f(float v, float (&red)[kShareWaves]) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  v = wave_sum_f(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float r = wave_sum_f(lane < kShareWaves ? red[lane] : 0.f);
+  __syncthreads();
+  return r;
+}
+
+struct ShareRole {
+  int b, h, part, n;
+  size_t row;
+};
+
+__device__ __forceinline__ ShareRole share_role(const ScoreArgs& a) {
+  const int bpr = share_blocks_per_row(a.max_pages);
+  const int row_dyn = blockIdx.x / bpr;
+  ShareRole r;
+  r.part = blockIdx.x % bpr;
+  r.b = row_dyn / a.dyn.count;
+  r.h = a.dyn.head[row_dyn % a.dyn.count];
+  r.n = row_pages(a.seq_lens[r.b], a.max_pages);
+  r.row = (size_t)r.b * a.num_kv_heads + r.h;
+  return r;
+}
+
+__global__ __launch_bounds__(kShareThreads) void coverage_part_kernel(ScoreArgs a) {
+  __shared__ float red[kG][kShareWaves];
+  const ShareRole r = share_role(a);
+  if (r.part * kSharePages >= r.n) return;  // uniform: the block is past the row
+  const int p = r.part * kSharePages + (int)threadIdx.x;
+  const float4 l4 = p < r.n ? a.ell[r.row * a.max_pages + p]
+                            : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  const float lg[kG] = {l4.x, l4.y, l4.z, l4.w};
+  float2 out[kG];
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const float M = block_max_f(lg[g], red[g]);
+    const float e = (M == -INFINITY || lg[g] == -INFINITY) ? 0.f : expf(lg[g] - M);
+    out[g] = make_float2(M, block_sum_f(e, red[g]));
+  }
+  if (threadIdx.x < kG) {
+    float2 v = out[0];
+#pragma unroll
+    for (int g = 1; g < kG; ++g) v = (int)threadIdx.x == g ? out[g] : v;
+    a.partials[(r.row * share_blocks_per_row(a.max_pages) + r.part) * kG + threadIdx.x] = v;
+  }
+}
 
 __global__ __launch_bounds__(kShareThreads) void coverage_share_kernel(ScoreArgs a) {
-  __shared__ float wm[kShareThreads / kWave][kG], ws[kShareThreads / kWave][kG];
   __shared__ float lse_s[kG];
-  const int b = blockIdx.x / a.dyn.count;
-  const int h = a.dyn.head[blockIdx.x % a.dyn.count];
-  const int n = row_pages(a.seq_lens[b], a.max_pages);
-  const size_t row = (size_t)b * a.num_kv_heads + h;
-  const float4* ell = a.ell + row * a.max_pages;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  float m[kG], s[kG];
+  const ShareRole r = share_role(a);
+  const int lane = threadIdx.x % kWave;
+  if (r.part * kSharePages >= r.n && r.part != 0) return;  // block 0 of an empty row still writes head_lse
+  const int p = r.part * kSharePages + (int)threadIdx.x;
+  float4 l4 = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  if (p < r.n) l4 = a.ell[r.row * a.max_pages + p];
+  if (threadIdx.x < kWave) {
+    // the row's block pairs, lane k holding pair k (k, k + 64, ... folded in order first)
+    const int nparts = (r.n + kSharePages - 1) / kSharePages;
+    const float2* pr = a.partials + r.row * share_blocks_per_row(a.max_pages) * kG;
+    float m[kG], s[kG];
 #pragma unroll
-  for (int g = 0; g < kG; ++g) {
-    m[g] = -INFINITY;
-    s[g] = 0.f;
-  }
-  for (int p0 = 0; p0 < n; p0 += kShareThreads * kShareBatch) {
-    float4 v[kShareBatch];
+    for (int g = 0; g < kG; ++g) {
+      m[g] = -INFINITY;
+      s[g] = 0.f;
+    }
+    for (int k = lane; k < nparts; k += kWave) {
 #pragma unroll
-    for (int k = 0; k < kShareBatch; ++k) {
-      const int p = p0 + k * kShareThreads + (int)threadIdx.x;
-      v[k] = p < n ? ell[p] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      for (int g = 0; g < kG; ++g) {
+        const float2 v = pr[(size_t)k * kG + g];
+        lse_combine(m[g], s[g], v.x, v.y);
+      }
     }
 #pragma unroll
-    for (int k = 0; k < kShareBatch; ++k) {
-      lse_push(m[0], s[0], v[k].x);
-      lse_push(m[1], s[1], v[k].y);
-      lse_push(m[2], s[2], v[k].z);
-      lse_push(m[3], s[3], v[k].w);
-    }
-  }
-  // wave: common max, then the rescaled sums; waves are folded in order by four threads
-#pragma unroll
-  for (int g = 0; g < kG; ++g) {
-    const float M = wave_max_f(m[g]);
-    const float sc = m[g] == -INFINITY ? 0.f : s[g] * expf(m[g] - M);
-    const float S = wave_sum_f(sc);
-    if (lane == 0) {
-      wm[wave][g] = M;
-      ws[wave][g] = S;
+    for (int g = 0; g < kG; ++g) {
+      const float M = wave_max_f(m[g]);
+      const float S = wave_sum_f(m[g] == -INFINITY ? 0.f : s[g] * expf(m[g] - M));
+      const float lse = M == -INFINITY ? -INFINITY : M + logf(S);
+      if (lane == g) {
+        lse_s[g] = lse;
+        if (r.part == 0 && a.head_lse) a.head_lse[(size_t)r.b * a.num_q_heads + (size_t)r.h * kG + g] = lse;
+      }
     }
   }
   __syncthreads();
-  if (threadIdx.x < kG) {
-    const int g = threadIdx.x;
-    float M = wm[0][g], S = ws[0][g];
-    for (int w = 1; w < kShareThreads / kWave; ++w) lse_combine(M, S, wm[w][g], ws[w][g]);
-    const float lse = M == -INFINITY ? -INFINITY : M + logf(S);
-    lse_s[g] = lse;
-    if (a.head_lse) a.head_lse[(size_t)b * a.num_q_heads + (size_t)h * kG + g] = lse;
-  }
-  __syncthreads();
-  float lse[kG];
-#pragma unroll
-  for (int g = 0; g < kG; ++g) lse[g] = lse_s[g];
-  for (int p = threadIdx.x; p < n; p += kShareThreads) a.scores[row * a.max_pages + p] = group_share(ell[p], lse);
+  const float lse[kG] = {lse_s[0], lse_s[1], lse_s[2], lse_s[3]};
+  if (p < r.n) a.scores[r.row * a.max_pages + p] = group_share(l4, lse);
 }
 
 int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool coverage, hipStream_t stream) {
   const unsigned rows = (unsigned)(a.batch * a.dyn.count);
   const dim3 grid(rows * (unsigned)(a.blocks_per_row + tail_blocks(a))), block(kScoreWaves * kWave);
-  const dim3 share_grid(rows), share_block(kShareThreads);
+  const dim3 share_grid(rows * (unsigned)share_blocks_per_row(a.max_pages)), share_block(kShareThreads);
 #define SPD_SCORE_CASE(D, KVD)                                                                  \
   if (head_dim == D && kv_dtype == KVD) {                                                       \
     if (coverage) {                                                                             \
       hipLaunchKernelGGL((page_score_kernel<D, KVD, true>), grid, block, 0, stream, a);         \
+      hipLaunchKernelGGL(coverage_part_kernel, share_grid, share_block, 0, stream, a);          \
       hipLaunchKernelGGL(coverage_share_kernel, share_grid, share_block, 0, stream, a);         \
     } else {                                                                                    \
       hipLaunchKernelGGL((page_score_kernel<D, KVD, false>), grid, block, 0, stream, a);        \

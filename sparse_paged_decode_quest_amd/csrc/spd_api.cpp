@@ -124,17 +124,20 @@ int launched(int rc) {
   return hipGetLastError() == hipSuccess ? SPD_OK : SPD_ERR_LAUNCH;
 }
 
-// Standalone coverage scorer: the per-page log-masses [B, Hkv, max_pages, G] between its two kernels.
+// Standalone coverage scorer: the per-page log-masses [B, Hkv, max_pages, G] and the per-block
+// (max, sum exp) pairs [B, Hkv, ceil(max_pages / 1024), G] between its kernels.
 struct ScoreWs {
-  size_t ell_off, total;
+  size_t ell_off, part_off, total;
 };
 
 ScoreWs score_ws(const spd_desc* d) {
   const size_t rows = (size_t)d->batch * d->num_kv_heads;
   const int G = d->num_q_heads / d->num_kv_heads;
+  const size_t parts = ((size_t)d->max_pages_per_seq + 1023) / 1024;
   ScoreWs w;
   w.ell_off = 0;
-  w.total = align_up(rows * d->max_pages_per_seq * G * sizeof(float));
+  w.part_off = align_up(rows * d->max_pages_per_seq * G * sizeof(float));
+  w.total = w.part_off + align_up(rows * parts * G * 2 * sizeof(float));
   return w;
 }
 
@@ -330,6 +333,7 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
     const ScoreWs w = score_ws(desc);
     if (!workspace || workspace_bytes < w.total) return SPD_ERR_WORKSPACE;
     a.ell = reinterpret_cast<float4*>(static_cast<char*>(workspace) + w.ell_off);
+    a.partials = reinterpret_cast<float2*>(static_cast<char*>(workspace) + w.part_off);
     a.head_lse = head_lse;
   }
   return launched(spd::launch_page_score(a, desc->head_dim, desc->kv_dtype, coverage, (hipStream_t)stream));
