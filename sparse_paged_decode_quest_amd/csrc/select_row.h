@@ -336,6 +336,7 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
   int32_t* out = a.page_list + row * a.max_list;
   int32_t* out_phys = a.page_phys ? a.page_phys + row * a.max_list : nullptr;
   float* out_sc = a.sel_scores ? a.sel_scores + row * a.max_list : nullptr;
+  const uint32_t pos0 = pos;
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const unsigned long long eq_mask = __ballot(take_eq(i));
@@ -344,12 +345,23 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
     const uint32_t q = pos + lanes_below(take_mask);
     if (take && q < (uint32_t)a.max_list) {
       out[q] = page_of(i);
-      if (out_phys) out_phys[q] = phys.at(i, page_of(i));
+      if (SlotPhys<KPL>::kInRegs && out_phys) out_phys[q] = phys.at(i, page_of(i));
       if (out_sc) out_sc[q] = COV ? __uint_as_float(key[i]) : key_to_score(key[i]);
     }
     pos += (uint32_t)__popcll(take_mask);
     eq_left -= __popcll(eq_mask);
     __builtin_amdgcn_sched_barrier(0);  // one slot at a time: keeps the slot's two ballots the only live masks
+  }
+  if constexpr (!SlotPhys<KPL>::kInRegs) {
+    // Long rows keep no physical pages in registers: this wave reads back the list entries it
+    // wrote, 64 at a time, and looks their physical pages up in the block table -- two reads
+    // per wave, instead of a block-table read waited for in every slot that took a page.
+    if (out_phys) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      const uint32_t end = min(pos, (uint32_t)a.max_list);
+      for (uint32_t q = pos0 + lane; q < end; q += kWave) out_phys[q] = phys.bt_row[out[q]];
+    }
   }
   if (threadIdx.x == 0) a.list_len[row] = (int)min(total, (uint32_t)a.max_list);
 }
