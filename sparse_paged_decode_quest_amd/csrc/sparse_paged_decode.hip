@@ -422,17 +422,30 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
     float4 pt[kPage];  // every probability of the page, read in one batch
 #pragma unroll
     for (int t = 0; t < kPage; ++t) pt[t] = *reinterpret_cast<const float4*>(p_lds[wave][t]);
+    if (r.valid == kPage) {  // full page (every page but a request's last): no masking
 #pragma unroll
-    for (int t = 0; t < kPage; ++t) {
-      const float pv[kGq] = {pt[t].x, pt[t].y, pt[t].z, pt[t].w};
-      float v[CPL];
-      T::v_values(vf, t, v);
+      for (int t = 0; t < kPage; ++t) {
+        const float pv[kGq] = {pt[t].x, pt[t].y, pt[t].z, pt[t].w};
+        float v[CPL];
+        T::v_values(vf, t, v);
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) v[cc] = t < r.valid ? v[cc] : 0.f;  // invalid slots may hold NaN
+        for (int g = 0; g < kGq; ++g)
 #pragma unroll
-      for (int g = 0; g < kGq; ++g)
+          for (int cc = 0; cc < CPL; ++cc) acc[g][cc] = fmaf(pv[g], v[cc], acc[g][cc]);
+      }
+    } else {
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) acc[g][cc] = fmaf(pv[g], v[cc], acc[g][cc]);
+      for (int t = 0; t < kPage; ++t) {
+        const float pv[kGq] = {pt[t].x, pt[t].y, pt[t].z, pt[t].w};
+        float v[CPL];
+        T::v_values(vf, t, v);
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) v[cc] = t < r.valid ? v[cc] : 0.f;  // invalid slots may hold NaN
+#pragma unroll
+        for (int g = 0; g < kGq; ++g)
+#pragma unroll
+          for (int cc = 0; cc < CPL; ++cc) acc[g][cc] = fmaf(pv[g], v[cc], acc[g][cc]);
+      }
     }
     wave_fence();
   };
