@@ -35,7 +35,7 @@ METRIC = "sparse paged decode step us + achieved HBM TB/s (128k ctx, Hq32/Hkv8/d
 DEFAULT_WORKLOAD = "llama3_8b_b1_128k_f16"
 PEAK_HBM_TBS = 8.0
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-KERNEL_SOURCES = ["score_common.h", "page_score.hip", "select_row.h", "page_score_select.hip", "spd_device.h", "spd_launch.h"]
+KERNEL_SOURCES = ["score_common.h", "page_score.hip", "spd_device.h", "spd_launch.h"]  # what page_score_kernel is built from
 
 
 def kernel_hash(files=KERNEL_SOURCES) -> str:

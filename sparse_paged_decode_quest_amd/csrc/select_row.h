@@ -337,11 +337,7 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
   int32_t* out_phys = a.page_phys ? a.page_phys + row * a.max_list : nullptr;
   float* out_sc = a.sel_scores ? a.sel_scores + row * a.max_list : nullptr;
   const uint32_t pos0 = pos;
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    const unsigned long long eq_mask = __ballot(take_eq(i));
-    const bool take = take_sure(i) || (take_eq(i) && (int)lanes_below(eq_mask) < eq_left);
-    const unsigned long long take_mask = __ballot(take);
+  auto write = [&](int i, bool take, unsigned long long take_mask) {
     const uint32_t q = pos + lanes_below(take_mask);
     if (take && q < (uint32_t)a.max_list) {
       out[q] = page_of(i);
@@ -349,8 +345,25 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
       if (out_sc) out_sc[q] = COV ? __uint_as_float(key[i]) : key_to_score(key[i]);
     }
     pos += (uint32_t)__popcll(take_mask);
-    eq_left -= __popcll(eq_mask);
-    __builtin_amdgcn_sched_barrier(0);  // one slot at a time: keeps the slot's two ballots the only live masks
+  };
+  if (eq_w <= (uint32_t)eq_left) {
+    // every key of this wave equal to the cut is taken (the usual case): one ballot per slot
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const bool take = take_sure(i) || take_eq(i);
+      const unsigned long long take_mask = __ballot(take);
+      if (take_mask) write(i, take, take_mask);
+    }
+  } else {
+    // the wave holds the last keys equal to the cut that are taken: rank them in page order
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const unsigned long long eq_mask = __ballot(take_eq(i));
+      const bool take = take_sure(i) || (take_eq(i) && (int)lanes_below(eq_mask) < eq_left);
+      write(i, take, __ballot(take));
+      eq_left -= __popcll(eq_mask);
+      __builtin_amdgcn_sched_barrier(0);  // one slot at a time: keeps the slot's two ballots the only live masks
+    }
   }
   if constexpr (!SlotPhys<KPL>::kInRegs) {
     // Long rows keep no physical pages in registers: this wave reads back the list entries it

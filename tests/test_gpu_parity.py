@@ -303,6 +303,28 @@ def test_balanced_plan_on_skewed_coverage_lists():
         P.check_attention(st2.out.cpu().numpy(), st2.out_lse.cpu().numpy(), o_ref, lse_ref, w.kv_dtype, str(plan))
 
 
+@pytest.mark.parametrize("seq", [40000, 131072 + 5], ids=["2500_pages", "8193_pages"])
+def test_equal_scores_are_taken_in_page_order(seq):
+    """All free pages score the same (every page's key box is the same), so the cut key is shared by
+    thousands of pages spread over every wave of the selecting workgroup: the list must be the forced
+    pages plus the lowest-numbered free pages."""
+    w = W.small("ties", seq_lens=(seq, 3000), budget=300, n_sink=2, n_local=3, Hkv=2, Hq=8)
+    inp = W.generate(w)
+    d = S.upload(inp)
+    d.page_meta.fill_(0.25)  # identical statistics everywhere
+    st = S.DecodeStep(w, d, fused=False, tail="none")
+    st.run()
+    torch.cuda.synchronize()
+    lists = st.lists()
+    for b, L in enumerate(w.seq_lens):
+        n = O.n_pages(L)
+        forced = O.forced_pages(n, w.n_sink, w.n_local)
+        free = [p for p in range(n) if p not in set(forced)]
+        want = sorted(set(forced) | set(free[:w.budget_pages - len(forced)]))
+        for h in range(w.num_kv_heads):
+            assert lists[(b, h)] == want, (b, h)
+
+
 def test_deterministic_bitwise():
     w = SMALL["cov_f16"]
     inp, d, st = run_case(w)
