@@ -592,12 +592,10 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
       mx = fmaxf(mx, lse_j[k]);
     }
   }
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  mx = wave_max_f(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
-  float M = red[0];
-  for (int w = 1; w < kMergeThreads / kWave; ++w) M = fmaxf(M, red[w]);
+  const float M = wave_max_f(lane < kMergeThreads / kWave ? red[lane] : -INFINITY);  // one read per lane
   __syncthreads();
   const size_t qrow = (size_t)b * a.num_q_heads + (size_t)h * kGq + g;
   if (M == -INFINITY) {
@@ -611,11 +609,10 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
     w_s[jj] = wj;
     sum += wj;
   }
-  sum = xor_sum<kWave>(sum);
+  sum = wave_sum_f(sum);
   if (lane == 0) red[wave] = sum;
   __syncthreads();
-  float S = 0.f;
-  for (int w = 0; w < kMergeThreads / kWave; ++w) S += red[w];
+  const float S = wave_sum_f(lane < kMergeThreads / kWave ? red[lane] : 0.f);
 
   float acc = 0.f;
 #pragma unroll
