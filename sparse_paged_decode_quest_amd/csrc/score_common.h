@@ -55,8 +55,8 @@ struct ScoreTraitsF16 {
   }
   __device__ static void load_m(M& m, const void* meta, size_t row, int c0) {
     const uint16_t* base = reinterpret_cast<const uint16_t*>(meta) + row + c0;
-    m.mn = *reinterpret_cast<const uint4*>(base);
-    m.mx = *reinterpret_cast<const uint4*>(base + D);
+    m.mn = ld_stream(reinterpret_cast<const uint4*>(base));
+    m.mx = ld_stream(reinterpret_cast<const uint4*>(base + D));
   }
   __device__ static void bound(const Q& qr, const M& m, float (&s)[kG]) {
     const uint32_t lo[4] = {m.mn.x, m.mn.y, m.mn.z, m.mn.w};
@@ -174,8 +174,8 @@ struct ScoreTraits<D, SPD_DTYPE_F32> {
   }
   __device__ static void load_m(M& m, const void* meta, size_t row, int c0) {
     const float* base = reinterpret_cast<const float*>(meta) + row + c0;
-    m.mn = *reinterpret_cast<const float4*>(base);
-    m.mx = *reinterpret_cast<const float4*>(base + D);
+    m.mn = ld_stream(reinterpret_cast<const float4*>(base));
+    m.mx = ld_stream(reinterpret_cast<const float4*>(base + D));
   }
   __device__ static void bound(const Q& qr, const M& m, float (&s)[kG]) {
     const float lo[4] = {m.mn.x, m.mn.y, m.mn.z, m.mn.w};

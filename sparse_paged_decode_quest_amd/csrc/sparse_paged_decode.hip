@@ -56,12 +56,12 @@ struct DecTraits<D, SPD_DTYPE_F16, SPD_DTYPE_F16> {
   __device__ static void load_k(KF& f, const void* pool, size_t tok_base, int quarter) {
     const uint16_t* p = reinterpret_cast<const uint16_t*>(pool) + tok_base;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) f.k[s] = *reinterpret_cast<const uint4*>(p + s * 32 + quarter * 8);
+    for (int s = 0; s < NS; ++s) f.k[s] = ld_stream(reinterpret_cast<const uint4*>(p + s * 32 + quarter * 8));
   }
   __device__ static void load_v(VF& f, const void* pool, size_t page_base, int lane) {
     const VW* p = reinterpret_cast<const VW*>(reinterpret_cast<const uint16_t*>(pool) + page_base + lane * CPL);
 #pragma unroll
-    for (int t = 0; t < kPage; ++t) f.v[t] = p[t * (D / CPL)];
+    for (int t = 0; t < kPage; ++t) f.v[t] = ld_stream(p + t * (D / CPL));
   }
   __device__ static void dots(const Q& q, const KF& f, float (&part)[kGq]) {
 #pragma unroll
@@ -111,12 +111,12 @@ struct DecTraits<D, SPD_DTYPE_F16, SPD_DTYPE_FP8_E4M3FN> {
   __device__ static void load_k(KF& f, const void* pool, size_t tok_base, int quarter) {
     const uint8_t* p = reinterpret_cast<const uint8_t*>(pool) + tok_base;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) f.k[s] = *reinterpret_cast<const uint4*>(p + s * 64 + quarter * 16);
+    for (int s = 0; s < NS; ++s) f.k[s] = ld_stream(reinterpret_cast<const uint4*>(p + s * 64 + quarter * 16));
   }
   __device__ static void load_v(VF& f, const void* pool, size_t page_base, int lane) {
     const uint16_t* p = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(pool) + page_base + lane * CPL);
 #pragma unroll
-    for (int t = 0; t < kPage; ++t) f.v[t] = p[t * (D / 2)];
+    for (int t = 0; t < kPage; ++t) f.v[t] = ld_stream(p + t * (D / 2));
   }
   // dot products of the codes' values times 2^-8 (the token scale and 2^8 are applied later)
   __device__ static void dots(const Q& q, const KF& f, float (&part)[kGq]) {
@@ -168,14 +168,14 @@ struct DecTraits<D, SPD_DTYPE_F32, SPD_DTYPE_F32> {
   __device__ static void load_k(KF& f, const void* pool, size_t tok_base, int quarter) {
     const float* p = reinterpret_cast<const float*>(pool) + tok_base;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) f.k[s] = *reinterpret_cast<const float4*>(p + s * 16 + quarter * 4);
+    for (int s = 0; s < NS; ++s) f.k[s] = ld_stream(reinterpret_cast<const float4*>(p + s * 16 + quarter * 4));
   }
   __device__ static void load_v(VF& f, const void* pool, size_t page_base, int lane) {
     const float* p = reinterpret_cast<const float*>(pool) + page_base + lane * CPL;
 #pragma unroll
     for (int t = 0; t < kPage; ++t)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) f.v[t][c] = p[t * D + c];
+      for (int c = 0; c < CPL; ++c) f.v[t][c] = ld_stream(p + t * D + c);
   }
   __device__ static void dots(const Q& q, const KF& f, float (&part)[kGq]) {
 #pragma unroll

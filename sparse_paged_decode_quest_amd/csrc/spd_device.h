@@ -67,6 +67,26 @@ __device__ __forceinline__ uint16_t f32_to_f16_round_down(float x) {
   return bits;
 }
 
+// ------------------------------------------------------------------ streaming loads
+
+// Loads of data read once per step (page meta in the scorer, K / V pages in decode), marked
+// non-temporal: they stream past the caches instead of displacing what is reused.
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  const nt_f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // ------------------------------------------------------------------ wave reductions
 
 template <int WIDTH>
