@@ -34,7 +34,7 @@ __device__ __forceinline__ RowRole row_role(const ScoreArgs& a) {
   return r;
 }
 
-template <int D, int KVD, bool COV>
+template <int D, int KVD, bool COV, int ITERS>
 __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreArgs a) {
   const RowRole r = row_role(a);
   const int32_t* bt_row = a.block_table + (size_t)r.b * a.max_pages;
@@ -45,15 +45,15 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreAr
     return;
   }
   const int p_begin = r.blk * a.pages_per_block;
-  int raw[kScoreIters];
-  load_block_table<D, KVD, kScoreWaves, kScoreIters>(bt_row, a.max_pages, p_begin, raw);
+  int raw[ITERS];
+  load_block_table<D, KVD, kScoreWaves, ITERS>(bt_row, a.max_pages, p_begin, raw);
   const int n = row_pages(len, a.max_pages);
   const int n_scan = scan_pages(a, n);
   float* sc_row = a.scores + ((size_t)r.b * a.num_kv_heads + r.h) * a.max_pages;
   if (!COV && a.tail_mode == SPD_TAIL_SKIP && r.blk == 0 && n > 0 && threadIdx.x == 0) sc_row[n - 1] = -INFINITY;
   if (p_begin >= n_scan) return;  // uniform over the block
-  if constexpr (COV) score_block_ell<D, KVD, kScoreWaves, kScoreIters>(a, raw, n_scan, len, r.b, r.h, p_begin);
-  else score_block_topk<D, KVD, kScoreWaves, kScoreIters>(a, raw, n_scan, r.b, r.h, p_begin, sc_row);
+  if constexpr (COV) score_block_ell<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, len, r.b, r.h, p_begin);
+  else score_block_topk<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, r.b, r.h, p_begin, sc_row);
 }
 
 // Coverage, second and third passes, over blocks of kSharePages pages of a row (one page per
@@ -174,14 +174,18 @@ int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool cover
   const unsigned rows = (unsigned)(a.batch * a.dyn.count);
   const dim3 grid(rows * (unsigned)(a.blocks_per_row + tail_blocks(a))), block(kScoreWaves * kWave);
   const dim3 share_grid(rows * (unsigned)share_blocks_per_row(a.max_pages)), share_block(kShareThreads);
+  const bool long_scan = score_iters((long long)rows * a.max_pages) == kScoreItersLong;
+#define SPD_SCORE_LAUNCH(D, KVD, COV)                                                                           \
+  if (long_scan) hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, kScoreItersLong>), grid, block, 0, stream, a); \
+  else hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, kScoreItersShort>), grid, block, 0, stream, a);
 #define SPD_SCORE_CASE(D, KVD)                                                                  \
   if (head_dim == D && kv_dtype == KVD) {                                                       \
     if (coverage) {                                                                             \
-      hipLaunchKernelGGL((page_score_kernel<D, KVD, true>), grid, block, 0, stream, a);         \
+      SPD_SCORE_LAUNCH(D, KVD, true)                                                            \
       hipLaunchKernelGGL(coverage_part_kernel, share_grid, share_block, 0, stream, a);          \
       hipLaunchKernelGGL(coverage_share_kernel, share_grid, share_block, 0, stream, a);         \
     } else {                                                                                    \
-      hipLaunchKernelGGL((page_score_kernel<D, KVD, false>), grid, block, 0, stream, a);        \
+      SPD_SCORE_LAUNCH(D, KVD, false)                                                           \
     }                                                                                           \
     return 0;                                                                                   \
   }
@@ -191,6 +195,7 @@ int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool cover
   SPD_SCORE_CASE(64, SPD_DTYPE_F32)
   SPD_SCORE_CASE(128, SPD_DTYPE_F32)
 #undef SPD_SCORE_CASE
+#undef SPD_SCORE_LAUNCH
   return SPD_ERR_UNSUPPORTED;
 }
 

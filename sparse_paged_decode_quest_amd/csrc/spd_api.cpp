@@ -17,8 +17,10 @@ namespace {
 // pages per scoring workgroup (fixed by the compiled work layouts)
 int meta_bytes_of(const spd_desc* d) { return d->kv_dtype == SPD_DTYPE_F32 ? 4 : 2; }
 
-int score_ppb(const spd_desc* d) {
-  return spd::score_pages_per_block(d->head_dim, meta_bytes_of(d), spd::kScoreWaves, spd::kScoreIters);
+// Pages per scorer workgroup (the standalone scorer's page groups per lane depend on the scan's size).
+int score_ppb(const spd_desc* d, int dyn_heads) {
+  const int iters = spd::score_iters((long long)d->batch * dyn_heads * d->max_pages_per_seq);
+  return spd::score_pages_per_block(d->head_dim, meta_bytes_of(d), spd::kScoreWaves, iters);
 }
 
 int fused_ppb(const spd_desc* d, const spd::SelectGeometry& g) {
@@ -321,7 +323,7 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
   if (desc->batch == 0 || dyn.count == 0) return SPD_OK;
   if (!q || !page_meta || !block_table || !seq_lens || !scores) return SPD_ERR_INVALID_ARG;
   if ((rc = check_tail(desc, sel, tail_mode, k_pool, k_scale))) return rc;
-  spd::ScoreArgs a = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, score_ppb(desc));
+  spd::ScoreArgs a = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, score_ppb(desc, dyn.count));
   a.scores = scores;
   a.meta_out = page_meta;
   a.k_pool = k_pool;

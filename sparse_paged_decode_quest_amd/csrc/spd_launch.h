@@ -10,7 +10,13 @@
 namespace spd {
 
 // Scoring workgroups: NW waves, each with ITERS groups of pages (score_common.h).
-constexpr int kScoreWaves = 4, kScoreIters = 2;  // standalone scorer
+constexpr int kScoreWaves = 4;  // standalone scorer
+// Page groups per lane of the standalone scorer: 2 for short scans, 4 once the step scans at least
+// kScoreLongItems (page, dynamic head) pairs -- more meta bytes in flight per lane pays off only
+// when the scan is long enough to be bandwidth- rather than latency-bound.
+constexpr int kScoreItersShort = 2, kScoreItersLong = 4;
+constexpr long long kScoreLongItems = 65536;
+inline int score_iters(long long items) { return items >= kScoreLongItems ? kScoreItersLong : kScoreItersShort; }
 
 // Selection workgroup shape for rows of up to max_pages pages (select_row.h): NW waves with
 // KPL key slots per lane; the fused score + select kernel scores with the same workgroup and
