@@ -316,6 +316,7 @@ def test_equal_scores_are_taken_in_page_order(seq):
     st.run()
     torch.cuda.synchronize()
     lists = st.lists()
+    pp = st.page_phys.cpu().numpy()
     for b, L in enumerate(w.seq_lens):
         n = O.n_pages(L)
         forced = O.forced_pages(n, w.n_sink, w.n_local)
@@ -323,6 +324,7 @@ def test_equal_scores_are_taken_in_page_order(seq):
         want = sorted(set(forced) | set(free[:w.budget_pages - len(forced)]))
         for h in range(w.num_kv_heads):
             assert lists[(b, h)] == want, (b, h)
+            assert pp[b, h, :len(want)].tolist() == inp.block_table[b, want].tolist(), (b, h)  # physical pages
 
 
 def test_deterministic_bitwise():

@@ -56,6 +56,10 @@ def test_named_workload(name):
     rows += [(0, strm[0])] if strm else []
     gpu_lists = st.lists()
     gpu_scores = st.scores.cpu().numpy()
+    gpu_phys = st.page_phys.cpu().numpy()
+    for b, h in rows:  # the physical page written beside every list entry
+        lst = gpu_lists[(b, h)]
+        assert gpu_phys[b, h, :len(lst)].tolist() == inp.block_table[b, lst].tolist(), (b, h)
     oracle_lists = {}
     for b, h in rows:
         n = O.n_pages(inp.seq_lens[b])
