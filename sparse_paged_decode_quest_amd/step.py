@@ -112,11 +112,12 @@ class DecodeStep:
       else ``"serial"``.
 
     ``phys_lists`` (default) has the selector write the physical page of every list entry so
-    the decode kernel does not read the block table.
+    the decode kernel does not read the block table.  ``keep_sel_scores`` has it also write the
+    score of every listed page (``sel_scores``); the step itself does not need them.
     """
 
     def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, fused: bool = False,
-                 tail: str = "auto", phys_lists: bool = True):
+                 tail: str = "auto", phys_lists: bool = True, keep_sel_scores: bool = False):
         if tail not in TAILS:
             raise ValueError(f"tail must be one of {TAILS}")
         skippable = w.mode == "topk" and w.n_local >= 1
@@ -147,7 +148,7 @@ class DecodeStep:
         self.page_list = torch.zeros((B, Hkv, w.list_capacity), **i32)
         self.page_phys = torch.zeros((B, Hkv, w.list_capacity), **i32) if phys_lists else None
         self.list_len = torch.zeros((B, Hkv), **i32)
-        self.sel_scores = torch.zeros((B, Hkv, w.list_capacity), **f32)
+        self.sel_scores = torch.zeros((B, Hkv, w.list_capacity), **f32) if keep_sel_scores else None
         self.out = torch.zeros((B, Hq, D), **f32)
         self.out_lse = torch.zeros((B, Hq), **f32)
         self.J = A.spd_plan_grid(self.desc, self.pp)

@@ -203,9 +203,17 @@ def test_fused_select_equals_unfused(mode):
     kw = dict(budget=40) if mode == "topk" else dict(mode="coverage", gamma=0.9, n_local=1, planted=("fixed", 6),
                                                      delta=("nats", 6.0))
     w = W.small("fused_" + mode, seq_lens=(3000, 700, 37, 0), streaming=(1,), Hkv=2, Hq=8, **kw)
-    inp, d, st = run_case(w, fused=False)
+    inp, d, _ = run_case(w, fused=False)
+    st = S.DecodeStep(w, d, fused=False, tail="none", keep_sel_scores=True)
+    st.run()
+    torch.cuda.synchronize()
     lists_unfused = st.lists()
-    st2 = S.DecodeStep(w, d, fused=True, tail="none")
+    # the score written beside each listed page of a dynamic row is that page's score
+    sc, ss = st.scores.cpu().numpy(), st.sel_scores.cpu().numpy()
+    for (b, h), lst in lists_unfused.items():
+        if not inp.head_kind[h]:
+            assert np.array_equal(ss[b, h, :len(lst)], sc[b, h, lst]), (b, h)
+    st2 = S.DecodeStep(w, d, fused=True, tail="none", keep_sel_scores=True)
     for rep in range(3):  # counters must return to zero between calls
         st2.run()
         torch.cuda.synchronize()
