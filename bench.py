@@ -4,9 +4,10 @@ Default workload: the Llama-3-8B-shaped attention layer at 128k context (batch 1
 Hkv 8, d 128, 16-token fp16 pages; KV heads 0-3 streaming with 4 sink + 16 local pages, heads
 4-7 top-K 256 pages with 1 sink + 2 local pages forced; 64 planted pages per head).
 
-A step is the whole hot path, captured in a hipGraph: page scores (the scorer first rebuilds the
-key statistics of each dynamic row's last page) -> page selection (or both in one launch with
---fused) -> split-K decode attention -> log-sum-exp merge.
+A step is the whole hot path, captured in a hipGraph: page scores -> page selection (or both in
+one launch with --fused), with the key statistics of the page each request's newest token is in
+rebuilt on the way (top-K: by the selector beside the selection; coverage: before scoring) ->
+split-K decode attention -> log-sum-exp merge.
 To measure HBM rather than the 256 MB Infinity Cache, the bench keeps R independent copies
 ("layers") of every input and output and rotates through them, so one rotation touches
 well over 1 GB.
@@ -14,7 +15,9 @@ well over 1 GB.
 Prints one JSON line: value = achieved HBM TB/s on the algorithmic bytes of a step (page meta
 scanned + the selected K/V pages + Q + O + block table + the tail page), ms_per_step = step
 time.  The roofline object is for the kernel that moves the most bytes (the page scorer),
-timed alone with HIP events on the stream its graph replays on.
+timed alone with HIP events on the stream its graph replays on.  step_us_spread gives the
+per-step time of single replays of the rotation graph, and beta_copy_TBs a plain device copy's
+bandwidth on the same GPU (read + write bytes), the practical streaming ceiling.
 """
 from __future__ import annotations
 
@@ -82,6 +85,25 @@ def scorer_bytes(w, head_kind: np.ndarray, tail: str) -> int:
     rebuilt = rows * (16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0) + 2 * d * meta_bytes + 4 + 4) \
         if tail == "rebuild" else 0
     return scanned * per_page_head + q + rebuilt
+
+
+def copy_bandwidth(stream, mib: int = 1024, reps: int = 10) -> float:
+    """Measured streaming bandwidth of this GPU (TB/s, read + write bytes): a plain device copy."""
+    import torch
+
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    return 2 * (mib << 20) / sec / 1e12
 
 
 def cpu_baseline(w, inp, seconds: float) -> dict:
@@ -234,6 +256,22 @@ def main():
     timed(whole, max(args.warmup, 1), R)              # warm-up: W untimed steps
     torch.cuda.synchronize()
     step_s = timed(whole, args.steps, R) / args.steps  # exactly K timed steps
+
+    # spread: the R-step graph replayed on its own, one pair of events per replay
+    g_all = capture(whole, R)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(20, args.steps // R))]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for e0, e1 in evs:
+            e0.record(stream)
+            g_all.replay()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([e0.elapsed_time(e1) * 1e3 / R for e0, e1 in evs])
+    spread = {"p10": round(float(np.percentile(per_step, 10)), 3), "p50": round(float(np.median(per_step)), 3),
+              "p90": round(float(np.percentile(per_step, 90)), 3), "replays": len(evs), "steps_per_replay": R}
+    beta = copy_bandwidth(stream)
     phase_us = {}
     for name, fn in phases.items():                   # each phase alone, rotated over the same layers
         reps = max(R, args.steps // 4)
@@ -258,7 +296,8 @@ def main():
             traffic = rec.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_TBS * 1000, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4),
-                "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3)}
+                "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3),
+                "frac_of_beta_copy": round(achieved / (beta * 1000), 4)}
 
     cpu = None
     if not args.no_cpu:
@@ -286,8 +325,9 @@ def main():
                    "layers_rotated": R, "graph": True, "fused_select": args.fused,
                    "plan": [probe.plan.min_chunk, probe.plan.min_blocks_per_row, probe.plan.min_grid_blocks,
                             int(probe.plan.balanced)]},
-        "step_us": round(step_us, 3), "tokens_per_s": round(w.batch / step_s, 1),
+        "step_us": round(step_us, 3), "step_us_spread": spread, "tokens_per_s": round(w.batch / step_s, 1),
         "bytes_per_step": ab, "frac_of_peak": round(tbs / PEAK_HBM_TBS, 4),
+        "beta_copy_TBs": round(beta, 3), "frac_of_beta": round(tbs / beta, 4),
         "phase_us": {k: round(v, 3) for k, v in phase_us.items()},
         "selection_overhead": sel_over,
         "list_len": {"min": int(list_len.min()), "median": int(np.median(list_len)), "max": int(list_len.max())},
