@@ -141,6 +141,8 @@ def main():
                     help="self-planning constants C,N_J,N_T[,balanced] (default: the step's for the workload)")
     ap.add_argument("--phase-only", default=None,
                     help="time only one phase per step (select|decode|merge|score|select_only)")
+    ap.add_argument("--reuse", type=int, default=4,
+                    help="also time chunks of this many steps that reuse one page selection (1: off)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -272,6 +274,34 @@ def main():
     spread = {"p10": round(float(np.percentile(per_step, 10)), 3), "p50": round(float(np.median(per_step)), 3),
               "p90": round(float(np.percentile(per_step, 90)), 3), "replays": len(evs), "steps_per_replay": R}
     beta = copy_bandwidth(stream)
+
+    # Reusable page selection (LServe, "Reusable Page Selection"), top-K only: chunks of C steps, the
+    # first selecting, the others one token longer each and reusing its lists.  The lengths are
+    # rewound by C - 1 tokens first (the pools hold those keys), advanced inside the chunk and
+    # restored at its end, so every replay is the same chunk.
+    reuse = None
+    if w.mode == "topk" and not args.fused and args.reuse > 1:
+        C = args.reuse
+        rsteps = [S.DecodeStep(w, d, plan=plan, reuse=C) for d in layers]
+        for d in layers:
+            d.seq_lens.sub_(C - 1)
+        torch.cuda.synchronize()
+
+        def chunk(st, s_, _r={id(a): b for a, b in zip(steps, rsteps)}):
+            r = _r[id(st)]
+            r.run(s_)
+            for _ in range(C - 1):
+                r.d.seq_lens.add_(1)
+                r.reuse_step(s_)
+            r.d.seq_lens.sub_(C - 1)
+
+        timed(chunk, R, R)
+        reps = max(R, args.steps // C)
+        chunk_s = timed(chunk, reps, R) / reps
+        for d in layers:
+            d.seq_lens.add_(C - 1)
+        torch.cuda.synchronize()
+        reuse = {"C": C, "us_per_token": round(chunk_s / C * 1e6, 3), "chunk_us": round(chunk_s * 1e6, 3)}
     phase_us = {}
     for name, fn in phases.items():                   # each phase alone, rotated over the same layers
         reps = max(R, args.steps // 4)
@@ -329,7 +359,7 @@ def main():
         "bytes_per_step": ab, "frac_of_peak": round(tbs / PEAK_HBM_TBS, 4),
         "beta_copy_TBs": round(beta, 3), "frac_of_beta": round(tbs / beta, 4),
         "phase_us": {k: round(v, 3) for k, v in phase_us.items()},
-        "selection_overhead": sel_over,
+        "selection_overhead": sel_over, "reuse": reuse,
         "list_len": {"min": int(list_len.min()), "median": int(np.median(list_len)), "max": int(list_len.max())},
         "roofline": roofline, "cpu_baseline": cpu,
         "setup_s": round(gen_s, 1), "kernel_hash": kernel_hash(),

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 4
+#define SPD_ABI_VERSION 5
 #define SPD_PAGE_SIZE 16
 #define SPD_MAX_KV_HEADS 64
 
@@ -176,10 +176,12 @@ typedef struct spd_plan_params {
 
 /* Channel-wise min / max of the valid keys of logical pages p of each request, for every KV
  * head, written to page_meta at the page's physical slot.  first_page (device, [B], may be
- * NULL): when NULL every page 0..n_b-1 is built; otherwise pages first_page[b] ..
- * min(n_b, first_page[b] + span_pages) - 1 are built (span_pages >= 1) -- the tail refresh
- * of a decode step uses first_page = n_b - 1, span_pages = 1.  k_scale (device) is
- * required for fp8 pools and ignored otherwise.  Other slots of page_meta are not touched. */
+ * NULL): when set, pages first_page[b] .. min(n_b, first_page[b] + span_pages) - 1 are built
+ * (span_pages >= 1).  When NULL, span_pages = 0 builds every page 0..n_b-1 (the bulk build at
+ * prefill) and span_pages >= 1 builds the last span_pages pages of each request, read from
+ * seq_lens on the device -- span_pages = 1 is the refresh of the page the newest token is in.
+ * k_scale (device) is required for fp8 pools and ignored otherwise.  Other slots of page_meta
+ * are not touched. */
 int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t* k_scale,
                         const int32_t* block_table, const int32_t* seq_lens,
                         const int32_t* first_page, int32_t span_pages, void* page_meta,
@@ -236,6 +238,22 @@ int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, co
                           const uint8_t* head_kind, int32_t* page_list, int32_t* page_phys,
                           int32_t* list_len, float* sel_scores, float* scores, float* head_lse,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Reusable page selection (LServe, "Reusable Page Selection": the selector runs on the first
+ * step of each chunk of decoding steps and its lists serve the rest of the chunk).  Called on
+ * each later step of a chunk, after the requests have grown: a dynamic row keeps its list and
+ * gets the pages of the current forced set (n_sink sink pages, n_local local pages) that lie past
+ * its last entry appended in ascending order; a streaming row's list is rewritten as its static
+ * sink + local table for the current length.  Lengths must not shrink between the selection and
+ * this call.  max_list must leave room for the pages a chunk can add (one per 16 tokens
+ * appended, plus one); entries that do not fit are dropped.  page_phys (device, may be NULL)
+ * receives the physical page of every appended entry; block_table is required.  When page_meta is
+ * set, workgroups beside the rows also rebuild the key min / max of each request's last page, as in
+ * spd_page_select.  Same ownership and errors as spd_page_select. */
+int spd_page_list_refresh(const spd_desc* desc, const spd_select_params* sel, const int32_t* seq_lens,
+                          const uint8_t* head_kind, const int32_t* block_table, const void* k_pool,
+                          const uint16_t* k_scale, void* page_meta, int32_t* page_list,
+                          int32_t* page_phys, int32_t* list_len, void* stream);
 
 /* Grouped-query decode attention of every row over its listed pages.  Block (b, h, j)
  * processes chunk j of row (b, h) (spd_plan_params); rows with one chunk write out /

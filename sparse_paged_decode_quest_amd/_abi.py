@@ -27,7 +27,7 @@ OP_PAGE_SCORE, OP_PAGE_SELECT, OP_PAGE_SCORE_SELECT = 0, 1, 2
 TAIL_NONE, TAIL_REBUILD, TAIL_SKIP = 0, 1, 2
 
 EXPORTS = ("spd_page_meta_build", "spd_page_score", "spd_page_select", "spd_page_score_select",
-           "spd_sparse_paged_decode", "spd_lse_merge", "spd_plan_grid", "spd_plan_chunks",
+           "spd_sparse_paged_decode", "spd_lse_merge", "spd_plan_grid", "spd_plan_chunks", "spd_page_list_refresh",
            "spd_partials_size", "spd_workspace_bytes", "spd_error_string", "spd_abi_version")
 
 
@@ -70,6 +70,7 @@ def lib():
         L.spd_page_meta_build.argtypes = [D, v, v, v, v, v, c_int32, v, v]
         L.spd_page_score.argtypes = [D, S, v, v, v, v, c_int32, v, v, POINTER(c_uint8), v, v, v, c_size_t, v]
         L.spd_page_select.argtypes = [D, S, v, v, POINTER(c_uint8), v, v, v, v, v, v, v, v, v]
+        L.spd_page_list_refresh.argtypes = [D, S, v, POINTER(c_uint8), v, v, v, v, v, v, v, v]
         L.spd_page_score_select.argtypes = [D, S, v, v, v, v, c_int32, v, v, POINTER(c_uint8), v, v, v, v, v, v, v,
                                             c_size_t, v]
         L.spd_sparse_paged_decode.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v]
@@ -143,6 +144,14 @@ def spd_page_select(desc, sel, scores, seq_lens, head_kind, block_table, k_pool,
                                  _heads(head_kind), _ptr(block_table), _ptr(k_pool), _ptr(k_scale), _ptr(page_meta),
                                  _ptr(page_list), _ptr(page_phys), _ptr(list_len), _ptr(sel_scores),
                                  _stream(stream)), "spd_page_select")
+
+
+def spd_page_list_refresh(desc, sel, seq_lens, head_kind, block_table, k_pool, k_scale, page_meta, page_list,
+                          page_phys, list_len, stream=None):
+    _check(lib().spd_page_list_refresh(ctypes.byref(desc), ctypes.byref(sel), _ptr(seq_lens), _heads(head_kind),
+                                       _ptr(block_table), _ptr(k_pool), _ptr(k_scale), _ptr(page_meta),
+                                       _ptr(page_list), _ptr(page_phys), _ptr(list_len), _stream(stream)),
+           "spd_page_list_refresh")
 
 
 def spd_page_score_select(desc, sel, q, page_meta, k_pool, k_scale, tail_mode, block_table, seq_lens, head_kind,

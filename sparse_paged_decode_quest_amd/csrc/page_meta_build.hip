@@ -1,5 +1,6 @@
-// Bulk statistics (every page of every request, at prefill) or the pages [first_page,
-// first_page + span) of each request (the page the newest token is in, during decode).
+// Bulk statistics (every page of every request, at prefill), the pages [first_page, first_page
+// + span) of each request, or its last `span` pages (the page the newest token is in, during
+// decode).
 #include "meta_build.h"
 
 namespace spd {
@@ -19,6 +20,8 @@ __global__ __launch_bounds__(256) void page_meta_build_kernel(MetaArgs a) {
     start = a.first_page[b];
     if (start < 0) start = 0;
     end = start + a.span < n ? start + a.span : n;
+  } else if (a.span < a.max_pages) {  // the last `span` pages of the request
+    start = n - a.span > 0 ? n - a.span : 0;
   }
   const int p = start + p_off;
   if (p >= end) return;

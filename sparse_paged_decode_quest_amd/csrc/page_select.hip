@@ -57,6 +57,55 @@ __global__ __launch_bounds__(NW * kWave) void page_select_kernel(SelectArgs a) {
   select_row_keys<NW, KPL, COV>(a, key, phys, row_shape(n, a.n_sink, a.n_local), row, sm);
 }
 
+// Reusable page selection (LServe, "Reusable Page Selection"): between two selections the lists
+// of the chunk's first step are reused, while the requests grow.  A dynamic row keeps its list
+// and gets every page of the current forced set (sink + local window) that lies past its last
+// entry appended in order -- the local window only moves right, so the list stays ascending; a
+// streaming row's static table is rewritten for the current length.  Workgroups after the rows
+// rebuild each request's newest page statistics, as in the selector.
+constexpr int kRefreshThreads = 256;
+
+__global__ __launch_bounds__(kRefreshThreads) void page_list_refresh_kernel(SelectArgs a) {
+  const int rows = a.batch * a.num_kv_heads;
+  if ((int)blockIdx.x >= rows) {
+    rebuild_tail_pages<kRefreshThreads / kWave>(a, blockIdx.x - rows);
+    return;
+  }
+  const int b = blockIdx.x / a.num_kv_heads;
+  const int h = blockIdx.x % a.num_kv_heads;
+  const size_t row = (size_t)b * a.num_kv_heads + h;
+  const int n = row_pages(a.seq_lens[b], a.max_pages);
+  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+  if ((a.streaming_mask >> h) & 1ull) {
+    select_streaming_row(a, n, row, bt_row);
+    return;
+  }
+  int32_t* out = a.page_list + row * a.max_list;
+  const int len = min(max(a.list_len[row], 0), a.max_list);
+  const int last = len > 0 ? out[len - 1] : -1;
+  const RowShape r = row_shape(n, a.n_sink, a.n_local);
+  // forced pages past `last`: sinks [last + 1, sink_end), then locals [max(last + 1, local_begin), n)
+  const int s0 = last + 1;
+  const int n_sink_new = max(0, r.sink_end - s0);
+  const int l0 = max(s0, r.local_begin);
+  const int n_local_new = max(0, n - l0);
+  const int add = n_sink_new + n_local_new;
+  for (int i = threadIdx.x; i < add && len + i < a.max_list; i += blockDim.x) {
+    const int p = i < n_sink_new ? s0 + i : l0 + (i - n_sink_new);
+    out[len + i] = p;
+    if (a.page_phys) a.page_phys[row * a.max_list + len + i] = bt_row[p];
+  }
+  if (threadIdx.x == 0) a.list_len[row] = min(len + add, a.max_list);
+}
+
+int launch_page_list_refresh(const SelectArgs& a, hipStream_t stream) {
+  const int rows = a.batch * a.num_kv_heads;
+  const int waves = kRefreshThreads / kWave;
+  const int tail_blocks = a.tail.meta ? (rows + waves - 1) / waves : 0;
+  hipLaunchKernelGGL(page_list_refresh_kernel, dim3((unsigned)(rows + tail_blocks)), dim3(kRefreshThreads), 0, stream, a);
+  return 0;
+}
+
 int launch_page_select(const SelectArgs& a, hipStream_t stream) {
   SelectGeometry g;
   if (!select_geometry(a.max_pages, g)) return SPD_ERR_UNSUPPORTED;

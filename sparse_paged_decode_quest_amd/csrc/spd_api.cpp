@@ -301,10 +301,12 @@ int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t
   if (desc->batch == 0) return SPD_OK;
   if (!k_pool || !block_table || !seq_lens || !page_meta) return SPD_ERR_INVALID_ARG;
   if (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale) return SPD_ERR_INVALID_ARG;
-  if (first_page && span_pages < 1) return SPD_ERR_INVALID_ARG;
+  if ((first_page && span_pages < 1) || span_pages < 0) return SPD_ERR_INVALID_ARG;
   spd::MetaArgs a = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
   a.first_page = first_page;
-  const int span = first_page ? std::min(span_pages, desc->max_pages_per_seq) : desc->max_pages_per_seq;
+  // pages per request: the span (from first_page, or the last span pages), or every page
+  const int span = (first_page || span_pages > 0) ? std::min(span_pages, desc->max_pages_per_seq)
+                                                  : desc->max_pages_per_seq;
   a.span = span;
   a.blocks_per_req = (span * desc->num_kv_heads + 3) / 4;
   return launched(spd::launch_page_meta_build(a, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
@@ -363,6 +365,25 @@ int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const fl
   a.scores = scores;
   if (page_meta) a.tail = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
   return launched(spd::launch_page_select(a, (hipStream_t)stream));
+}
+
+int spd_page_list_refresh(const spd_desc* desc, const spd_select_params* sel, const int32_t* seq_lens,
+                          const uint8_t* head_kind, const int32_t* block_table, const void* k_pool,
+                          const uint16_t* k_scale, void* page_meta, int32_t* page_list, int32_t* page_phys,
+                          int32_t* list_len, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if ((rc = check_sel(desc, sel))) return rc;
+  if ((rc = check_list_capacity(desc, sel))) return rc;
+  spd::HeadList dyn, strm;
+  uint64_t mask;
+  if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
+  if (desc->batch == 0) return SPD_OK;
+  if (!seq_lens || !page_list || !list_len || !block_table) return SPD_ERR_INVALID_ARG;
+  if (page_meta && (!k_pool || (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale))) return SPD_ERR_INVALID_ARG;
+  spd::SelectArgs a = select_args(desc, sel, seq_lens, block_table, page_list, page_phys, list_len, nullptr, mask);
+  if (page_meta) a.tail = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
+  return launched(spd::launch_page_list_refresh(a, (hipStream_t)stream));
 }
 
 int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, const void* q, void* page_meta,

@@ -93,6 +93,7 @@ struct SelectArgs {
   MetaArgs tail;            // tail.meta set: also rebuild each request's last page, all KV heads
 };
 int launch_page_select(const SelectArgs& a, hipStream_t stream);
+int launch_page_list_refresh(const SelectArgs& a, hipStream_t stream);
 
 struct FusedArgs {
   ScoreArgs score;         // score.scores / score.ell / score.partials -> workspace

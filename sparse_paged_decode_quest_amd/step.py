@@ -72,10 +72,16 @@ def upload(inp: Inputs, device="cuda") -> DeviceInputs:
                         page_meta=meta)
 
 
-def make_desc(w: Workload, num_pool_pages: int) -> A.Desc:
+def make_desc(w: Workload, num_pool_pages: int, max_list: int | None = None) -> A.Desc:
     return A.Desc(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                   page_size=16, max_pages_per_seq=w.pages_per_seq, num_pool_pages=num_pool_pages,
-                  max_list=w.list_capacity, q_dtype=A.DTYPE[w.q_dtype], kv_dtype=A.DTYPE[w.kv_dtype])
+                  max_list=max_list or w.list_capacity, q_dtype=A.DTYPE[w.q_dtype], kv_dtype=A.DTYPE[w.kv_dtype])
+
+
+def reuse_slack(reuse: int) -> int:
+    """List entries a chunk of `reuse` steps can append to a selection: one page per 16 tokens
+    appended, plus the page a step may open."""
+    return 0 if reuse <= 1 else (reuse - 1) // 16 + 2
 
 
 def make_select(w: Workload) -> A.SelectParams:
@@ -114,10 +120,15 @@ class DecodeStep:
     ``phys_lists`` (default) has the selector write the physical page of every list entry so
     the decode kernel does not read the block table.  ``keep_sel_scores`` has it also write the
     score of every listed page (``sel_scores``); the step itself does not need them.
+
+    ``reuse`` = C > 1 sizes the lists for reusable page selection (LServe, "Reusable Page
+    Selection"): ``run`` selects on the first step of a chunk of C steps and ``reuse_step`` serves
+    the other C - 1, after the requests have grown, with the chunk's lists plus the current sink and
+    local pages.
     """
 
     def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, fused: bool = False,
-                 tail: str = "auto", phys_lists: bool = True, keep_sel_scores: bool = False):
+                 tail: str = "auto", phys_lists: bool = True, keep_sel_scores: bool = False, reuse: int = 1):
         if tail not in TAILS:
             raise ValueError(f"tail must be one of {TAILS}")
         skippable = w.mode == "topk" and w.n_local >= 1
@@ -137,7 +148,9 @@ class DecodeStep:
         self.side = torch.cuda.Stream(device=d.q.device) if tail == "side" else None
         self.phys_lists = phys_lists
         dev = d.q.device
-        self.desc = make_desc(w, d.num_pool_pages)
+        self.reuse = reuse
+        self.max_list = w.list_capacity + reuse_slack(reuse)
+        self.desc = make_desc(w, d.num_pool_pages, self.max_list)
         self.sel = make_select(w)
         self.pp = self.plan.params()
         B, Hq, Hkv, D = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
@@ -145,10 +158,10 @@ class DecodeStep:
         i32 = dict(dtype=torch.int32, device=dev)
         self.scores = torch.zeros((B, Hkv, w.pages_per_seq), **f32)
         self.head_lse = torch.zeros((B, Hq), **f32)
-        self.page_list = torch.zeros((B, Hkv, w.list_capacity), **i32)
-        self.page_phys = torch.zeros((B, Hkv, w.list_capacity), **i32) if phys_lists else None
+        self.page_list = torch.zeros((B, Hkv, self.max_list), **i32)
+        self.page_phys = torch.zeros((B, Hkv, self.max_list), **i32) if phys_lists else None
         self.list_len = torch.zeros((B, Hkv), **i32)
-        self.sel_scores = torch.zeros((B, Hkv, w.list_capacity), **f32) if keep_sel_scores else None
+        self.sel_scores = torch.zeros((B, Hkv, self.max_list), **f32) if keep_sel_scores else None
         self.out = torch.zeros((B, Hq, D), **f32)
         self.out_lse = torch.zeros((B, Hq), **f32)
         self.J = A.spd_plan_grid(self.desc, self.pp)
@@ -158,14 +171,11 @@ class DecodeStep:
         op = A.OP_PAGE_SCORE_SELECT if self.fused else A.OP_PAGE_SCORE
         self.ws_bytes = A.spd_workspace_bytes(self.desc, self.sel, op)
         self.workspace = torch.zeros(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
-        n_b = (np.asarray(w.seq_lens, dtype=np.int64) + 15) // 16
-        self.first_page = torch.from_numpy(np.maximum(n_b - 1, 0).astype(np.int32)).to(dev)
 
     def refresh_tail(self, stream=None):
         """page_meta_build of the page the newest token is in (one page per request, all heads)."""
         d = self.d
-        A.spd_page_meta_build(self.desc, d.k_pool, d.k_scale, d.block_table, d.seq_lens, self.first_page, 1,
-                              d.page_meta, stream)
+        A.spd_page_meta_build(self.desc, d.k_pool, d.k_scale, d.block_table, d.seq_lens, None, 1, d.page_meta, stream)
 
     def score(self, stream=None, tail_mode=None):
         """Page scores, treating each dynamic row's last page by the step's tail mode."""
@@ -211,6 +221,17 @@ class DecodeStep:
     def attend(self, stream=None):
         self.decode(stream)
         self.merge(stream)
+
+    def reuse_step(self, stream=None):
+        """A later step of a reuse chunk: the chunk's lists plus the current forced pages (and the
+        newest pages' statistics rebuilt beside them), then attention."""
+        d = self.d
+        rebuild = self.tail != "none"
+        A.spd_page_list_refresh(self.desc, self.sel, d.seq_lens, d.head_kind, d.block_table,
+                                d.k_pool if rebuild else None, d.k_scale if rebuild else None,
+                                d.page_meta if rebuild else None, self.page_list, self.page_phys, self.list_len,
+                                stream)
+        self.attend(stream)
 
     def run(self, stream=None):
         """One whole step on `stream` (a torch stream or a raw HIP stream handle; None: torch's

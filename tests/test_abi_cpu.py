@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 4
+    assert A.abi_version() == 5
 
 
 def test_error_strings(lib):
@@ -162,6 +162,22 @@ def test_decode_argument_checks(lib):
     assert decode_rc(d, plan, pls=None) == A.SPD_ERR_INVALID_ARG
     wf = W.small(kv="fp8")
     assert decode_rc(desc_for(wf), plan, ks=None) == A.SPD_ERR_INVALID_ARG
+
+
+def test_list_refresh_argument_checks(lib):
+    w = W.small()
+    d = desc_for(w)
+    heads = (ctypes.c_uint8 * d.num_kv_heads)(*([0] * d.num_kv_heads))
+
+    def rc(sl=FAKE, bt=FAKE, k_pool=FAKE, meta=None, pl=FAKE, ll=FAKE, desc=d):
+        return A.lib().spd_page_list_refresh(ctypes.byref(desc), ctypes.byref(sel_for(w)), sl, heads, bt, k_pool, FAKE,
+                                             meta, pl, None, ll, 0)
+
+    for kw in (dict(sl=None), dict(bt=None), dict(pl=None), dict(ll=None)):
+        assert rc(**kw) == A.SPD_ERR_INVALID_ARG, kw
+    assert rc(k_pool=None, meta=FAKE) == A.SPD_ERR_INVALID_ARG  # the newest-page rebuild reads K
+    assert rc(desc=desc_for(w, max_list=2)) == A.SPD_ERR_INVALID_ARG  # lists must hold a selection
+    assert rc(desc=desc_for(w, batch=0)) == A.SPD_OK  # nothing to do, nothing launched
 
 
 def test_select_and_fused_argument_checks(lib):

@@ -335,6 +335,59 @@ def test_equal_scores_are_taken_in_page_order(seq):
             assert pp[b, h, :len(want)].tolist() == inp.block_table[b, want].tolist(), (b, h)  # physical pages
 
 
+@pytest.mark.parametrize("reuse", [4, 20])
+def test_reusable_selection_serves_a_chunk_of_growing_steps(reuse):
+    """LServe's reusable page selection: the first step of a chunk selects; each later step, one
+    token longer, keeps those lists plus the current sink and local pages (a page opened during the
+    chunk is appended) and rebuilds the newest page's statistics.  Lists, physical pages and
+    attention are checked against the oracle at every length."""
+    import copy
+
+    full = (16 * 40 + 2, 16 * 12 + 9, 16 * 3 + 1 + reuse, 700)  # the pools hold keys up to these lengths
+    w = W.small("reuse", seq_lens=full, budget=12, n_sink=1, n_local=2, streaming=(1,), n_sink_stream=2,
+                n_local_stream=2, Hkv=2, Hq=8)
+    inp = W.generate(w)
+    d = S.upload(inp)
+    S.build_meta(w, d)
+    L = np.array(full, dtype=np.int64) - (reuse - 1)
+    d.seq_lens.copy_(torch.from_numpy(L.astype(np.int32)))
+    st = S.DecodeStep(w, d, fused=False, reuse=reuse)
+    st.run()
+    torch.cuda.synchronize()
+    expect = st.lists()
+    for i in range(1, reuse):
+        L = L + 1
+        d.seq_lens.add_(1)
+        poison_outputs(st)
+        st.reuse_step()
+        torch.cuda.synchronize()
+        for (b, h), lst in expect.items():
+            n = O.n_pages(int(L[b]))
+            if inp.head_kind[h]:
+                expect[(b, h)] = O.forced_pages(n, w.n_sink_stream, w.n_local_stream)
+            else:
+                last = lst[-1] if lst else -1
+                expect[(b, h)] = lst + [p for p in O.forced_pages(n, w.n_sink, w.n_local) if p > last]
+        got = st.lists()
+        assert got == expect, i
+        pp = st.page_phys.cpu().numpy()
+        for (b, h), lst in got.items():
+            assert pp[b, h, :len(lst)].tolist() == inp.block_table[b, lst].tolist(), (i, b, h)
+        at = copy.copy(inp)
+        at.seq_lens = L.astype(inp.seq_lens.dtype)
+        o_ref, lse_ref = O.sparse_paged_decode(at, expect, w.sm_scale)
+        P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), o_ref, lse_ref, w.kv_dtype, f"step {i}")
+    # the newest page of every request holds the statistics of its tokens at the final length
+    at = copy.copy(inp)
+    at.seq_lens = L.astype(inp.seq_lens.dtype)
+    last = [max(O.n_pages(int(x)) - 1, 0) for x in L]
+    ref = O.page_meta_build(at, first_page=last)
+    got = d.page_meta.cpu().numpy()
+    for b, x in enumerate(L):
+        phys = int(inp.block_table[b, last[b]])
+        assert np.array_equal(got[phys], ref[phys]), b
+
+
 def test_deterministic_bitwise():
     w = SMALL["cov_f16"]
     inp, d, st = run_case(w)
