@@ -20,6 +20,11 @@ Pages and their definitions:
     above tau reaches gamma minus the forced shares.
   * PersistentKV (section 3.1, Eq. 1): exact decode attention over the kept
     tokens; section 3.3: split states and their exact merge.
+  * Moira (section 3.1 "Page summaries and the mvar estimate", Eq. 2): per page
+    and KV head the channel-wise mean and variance of the keys; the page's
+    estimated attention mass for query head g is
+    log m_{g,P} = s q_g . mu_P + (1/2) (s q_g)^2 . sigma^2_P + log(tokens); the
+    first page and the current page are computed exactly.
 
 Readings where the pages leave a step open:
   * GQA combine for top-K: score_p = max over the group's query heads of S_{g,p}.
@@ -33,6 +38,10 @@ Readings where the pages leave a step open:
   * fp8 pools are OCP E4M3FN with a per-(page, head, token) fp16 scale; their key
     min / max is stored as fp16 rounded outward (max up, min down).
   * An empty row (no kept tokens) gives O = 0 and lse = -inf.
+  * mvar: the variance is the population variance over the page's valid tokens
+    (divided by their count), and the token count in Eq. 2 is the page's valid
+    token count; mean and variance are stored rounded to bf16 (nearest, ties to even)
+    and Eq. 2 is evaluated on the stored values.
 """
 from __future__ import annotations
 
@@ -198,11 +207,104 @@ def coverage_shares(S: np.ndarray, seq_len: int, sm_scale: float):
     """
     n = S.shape[1]
     valid = np.array([valid_tokens(seq_len, p) for p in range(n)], dtype=np.float64)
-    ell = sm_scale * S + np.log(valid)[None, :]
+    return shares_from_logmass(sm_scale * S + np.log(valid)[None, :])
+
+
+def shares_from_logmass(ell: np.ndarray):
+    """Group-mean share of each page from page log-masses ell [G, n] (Moira section 3.2, Eq. 3):
+    pi_bar_p = (1/G) sum_g exp(ell_{g,p} - lse_g), lse_g = log sum_p exp(ell_{g,p})."""
     mx = ell.max(axis=1, keepdims=True)
     lse = mx[:, 0] + np.log(np.exp(ell - mx).sum(axis=1))
     share = np.exp(ell - lse[:, None])
     return share.mean(axis=0), lse
+
+
+# --------------------------------------------------------------------------------------
+# a0 / a1, second estimator: Moira's page summaries and the mvar estimate
+# --------------------------------------------------------------------------------------
+
+def page_mean_var(k_page: np.ndarray, valid: int):
+    """Channel-wise mean and population variance of the valid keys of one page ([P, d] float64)."""
+    keys = k_page[:valid]
+    mu = keys.sum(axis=0) / valid
+    var = ((keys - mu[None, :]) ** 2).sum(axis=0) / valid
+    return mu, var
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> nearest bfloat16 value (8 significant bits, ties to even), returned as float64.
+
+    bfloat16 keeps float32's exponent range: normal exponents down to -126, subnormal steps of
+    2^-133, largest finite (2 - 2^-7) * 2^127; values rounding past it become +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                                # x = m 2^e, 0.5 <= |m| < 1
+    step = np.exp2(np.maximum(e - 8, -133).astype(np.float64))
+    r = np.round(x / step) * step                     # numpy rounds halves to even
+    big = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    return np.where(np.abs(r) > big, np.copysign(np.inf, x), np.where(x == 0, x, r))
+
+
+def page_stats_build(inp, first_page=None, heads=None, requests=None) -> np.ndarray:
+    """Stored page summaries: mean and variance of the keys of every page p >= first_page[b]
+    of every request, rounded to bfloat16 (Moira, "Memory for page summaries": the summaries
+    are kept in bf16).
+
+    Layout [num_pool_pages, Hkv, 2, d] float64 holding bf16 values: index 0 = mean,
+    1 = variance; pages not visited are NaN.
+    """
+    w = inp.workload
+    Hkv, d = inp.k_pool.shape[1], inp.k_pool.shape[3]
+    out = np.full((inp.k_pool.shape[0], Hkv, 2, d), np.nan)
+    hs = list(range(Hkv)) if heads is None else [int(h) for h in heads]
+    reqs = range(len(inp.seq_lens)) if requests is None else [int(b) for b in requests]
+    for b in reqs:
+        L = int(inp.seq_lens[b])
+        start = 0 if first_page is None else max(0, int(first_page[b]))
+        for p in range(start, n_pages(L)):
+            phys = int(inp.block_table[b, p])
+            for h in hs:
+                scale = None if inp.k_scale is None else inp.k_scale[phys, h]
+                kv = stored_values(inp.k_pool[phys, h], scale, w.kv_dtype)
+                mu, var = page_mean_var(kv, valid_tokens(L, p))
+                out[phys, h, 0], out[phys, h, 1] = round_bf16(mu), round_bf16(var)
+    return out
+
+
+def mvar_logmass(q: np.ndarray, mu: np.ndarray, var: np.ndarray, valid: np.ndarray, sm_scale: float) -> np.ndarray:
+    """Moira Eq. 2: log m_{g,P} = s q_g . mu_P + 0.5 (s q_g)^2 . sigma^2_P + log(tokens).
+
+    q: [G, d]; mu, var: [n, d]; valid: [n] -> [G, n].
+    """
+    sq = sm_scale * q
+    return sq @ mu.T + 0.5 * ((sq * sq) @ var.T) + np.log(valid)[None, :]
+
+
+def exact_logmass(q: np.ndarray, keys: np.ndarray, sm_scale: float) -> np.ndarray:
+    """log sum_{k in page} exp(s q_g . k) for each query head: q [G, d], keys [valid, d] -> [G]."""
+    x = sm_scale * (q @ keys.T)
+    mx = x.max(axis=1)
+    return mx + np.log(np.exp(x - mx[:, None]).sum(axis=1))
+
+
+def row_logmass_mvar(inp, stats: np.ndarray, b: int, h: int) -> np.ndarray:
+    """Page log-masses of dynamic row (b, h) under the mvar estimator, [G, n]: Eq. 2 from the
+    page summaries, except the first page and the current (last) page, computed exactly."""
+    w = inp.workload
+    G = w.group
+    L = int(inp.seq_lens[b])
+    n = n_pages(L)
+    q = inp.q[b, h * G:(h + 1) * G].astype(np.float64)
+    phys = inp.block_table[b, :n].astype(np.int64)
+    st = stats[phys, h]
+    valid = np.array([valid_tokens(L, p) for p in range(n)], dtype=np.float64)
+    ell = mvar_logmass(q, st[:, 0], st[:, 1], valid, w.sm_scale)
+    for p in sorted({0, n - 1}):
+        ph = int(phys[p])
+        scale = None if inp.k_scale is None else inp.k_scale[ph, h]
+        keys = stored_values(inp.k_pool[ph, h], scale, w.kv_dtype)[:valid_tokens(L, p)]
+        ell[:, p] = exact_logmass(q, keys, w.sm_scale)
+    return ell
 
 
 # --------------------------------------------------------------------------------------
@@ -243,13 +345,16 @@ def select_coverage(pi: np.ndarray, n: int, gamma: float, forced: list) -> list:
     return list(range(n))
 
 
-def page_select(inp, meta: np.ndarray):
+def page_select(inp, meta: np.ndarray, stats: np.ndarray | None = None):
     """Scores and lists for every (request, KV head) row.
 
     Returns dict with 'lists' {(b,h): [pages]}, 'scores' {(b,h): per-page key or None
     for streaming rows}, 'S' {(b,h): [G, n] bounds}, 'lse' {(b,h): [G]} (coverage only).
+    With the mvar estimator the page log-masses come from ``stats`` (page_stats_build).
     """
     w = inp.workload
+    if w.estimator == "mvar":
+        return _page_select_mvar(inp, page_stats_build(inp) if stats is None else stats)
     out = {"lists": {}, "scores": {}, "S": {}, "lse": {}}
     for b in range(len(inp.seq_lens)):
         L = int(inp.seq_lens[b])
@@ -271,6 +376,28 @@ def page_select(inp, meta: np.ndarray):
                 out["scores"][(b, h)] = pi
                 out["lse"][(b, h)] = lse
                 out["lists"][(b, h)] = select_coverage(pi, n, w.gamma, forced) if n else []
+    return out
+
+
+def _page_select_mvar(inp, stats: np.ndarray):
+    """page_select for coverage rows whose page log-masses come from the mvar estimate."""
+    w = inp.workload
+    out = {"lists": {}, "scores": {}, "S": {}, "lse": {}}
+    for b in range(len(inp.seq_lens)):
+        L = int(inp.seq_lens[b])
+        n = n_pages(L)
+        for h in range(inp.k_pool.shape[1]):
+            if inp.head_kind[h]:
+                out["lists"][(b, h)] = forced_pages(n, w.n_sink_stream, w.n_local_stream)
+                out["scores"][(b, h)] = None
+                continue
+            if n == 0:
+                out["scores"][(b, h)], out["lse"][(b, h)], out["lists"][(b, h)] = np.zeros(0), np.full(w.group, -np.inf), []
+                continue
+            pi, lse = shares_from_logmass(row_logmass_mvar(inp, stats, b, h))
+            out["scores"][(b, h)] = pi
+            out["lse"][(b, h)] = lse
+            out["lists"][(b, h)] = select_coverage(pi, n, w.gamma, forced_pages(n, w.n_sink, w.n_local))
     return out
 
 

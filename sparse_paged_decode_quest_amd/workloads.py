@@ -54,6 +54,7 @@ class Workload:
     kv_dtype: str
     q_dtype: str
     mode: str  # "topk" | "coverage"
+    estimator: str = "bound"  # coverage page mass: "bound" (Quest key box) | "mvar" (Moira mean / variance)
     budget_pages: int = 0
     gamma: float = 0.0
     n_sink: int = 1

@@ -259,6 +259,106 @@ def test_coverage_shares_normalise_and_lse_matches_library():
     assert pi2[3] > pi[3]
 
 
+# ------------------------------------------------------------------ mvar (Moira Eq. 2)
+
+def test_mean_var_hand_example():
+    keys = np.array([[1.0, 2.0], [3.0, 6.0], [9.0, 9.0]])
+    mu, var = O.page_mean_var(keys, 2)  # the third row is not a valid token
+    assert mu.tolist() == [2.0, 4.0]
+    assert var.tolist() == [1.0, 4.0]  # population variance: ((1-2)^2 + (3-2)^2) / 2
+
+
+def test_bf16_rounding_matches_library():
+    import torch
+    rng = np.random.default_rng(26)
+    x32 = np.concatenate([rng.standard_normal(20000) * np.exp2(rng.integers(-140, 120, 20000)),
+                          # exact halfway cases between neighbouring bf16 values, both parities
+                          (np.arange(1, 2000) * 2 + 1) * 2.0 ** -8, -(np.arange(1, 2000) * 2 + 1) * 2.0 ** -8,
+                          [0.0, -0.0, 2.0 ** -133, 3 * 2.0 ** -134, 3.3e38]]).astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_bf16(x32.astype(np.float64))
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_stored_stats_are_the_rounded_mean_and_variance():
+    w = W.small(mode="coverage", estimator="mvar", gamma=0.9, seq_lens=(40,), Hq=4, Hkv=1, seed=27)
+    inp = W.generate(w)
+    st = O.page_stats_build(inp)
+    for p, valid in ((0, 16), (2, 8)):
+        phys = int(inp.block_table[0, p])
+        keys = inp.k_pool[phys, 0, :valid].astype(np.float64)
+        assert np.array_equal(st[phys, 0, 0], O.round_bf16(keys.mean(axis=0)))
+        assert np.array_equal(st[phys, 0, 1], O.round_bf16(keys.var(axis=0)))  # numpy's var: population
+
+
+def test_mvar_identical_keys_is_the_exact_page_mass():
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal(64)
+    q = rng.standard_normal((4, 64))
+    keys = np.repeat(k[None, :], 11, axis=0)
+    mu, var = O.page_mean_var(keys, 11)
+    ell = O.mvar_logmass(q, mu[None], var[None], np.array([11.0]), 0.125)[:, 0]
+    assert np.allclose(ell, O.exact_logmass(q, keys, 0.125), rtol=0, atol=1e-12)
+    assert np.allclose(ell, 0.125 * q @ k + np.log(11.0), rtol=0, atol=1e-12)  # closed form
+
+
+def test_mvar_is_the_gaussian_expectation():
+    """Eq. 2 is log(S * E[exp(s q.k)]) for keys independent Gaussian per channel: check it against a
+    Monte Carlo average over many drawn keys (seeded)."""
+    rng = np.random.default_rng(22)
+    d, S, s = 16, 16.0, 0.25
+    mu = rng.standard_normal(d) * 0.5
+    var = rng.uniform(0.1, 0.6, d)
+    q = rng.standard_normal((3, d))
+    keys = mu[None, :] + rng.standard_normal((400_000, d)) * np.sqrt(var)[None, :]
+    mc = np.log(S * np.exp(s * keys @ q.T).mean(axis=0))
+    ell = O.mvar_logmass(q, mu[None], var[None], np.array([S]), s)[:, 0]
+    assert np.allclose(ell, mc, rtol=0, atol=0.01), (ell, mc)
+    # dropping the variance term is off by far more than the sampling error
+    assert np.abs(ell - (s * q @ mu + np.log(S))).max() > 0.05
+
+
+def test_exact_logmass_matches_library():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(23)
+    q, keys = rng.standard_normal((4, 32)), rng.standard_normal((13, 32)) * 3
+    assert np.allclose(O.exact_logmass(q, keys, 0.2), logsumexp(0.2 * keys @ q.T, axis=0), rtol=0, atol=1e-12)
+
+
+def test_mvar_two_page_rows_give_the_exact_page_shares():
+    """With one or two pages, the first and current pages are exact, so the shares equal the
+    dense softmax mass of each page's tokens, averaged over the group."""
+    w = W.small(mode="coverage", estimator="mvar", gamma=0.9, seq_lens=(31, 9, 16), Hq=8, Hkv=2, seed=24)
+    inp = W.generate(w)
+    stats = O.page_stats_build(inp)
+    G = w.group
+    for b, L in enumerate(w.seq_lens):
+        n = O.n_pages(L)
+        for h in range(w.num_kv_heads):
+            pi, lse = O.shares_from_logmass(O.row_logmass_mvar(inp, stats, b, h))
+            K, _ = _dense_unpaged(inp, b, h)
+            q = inp.q[b, h * G:(h + 1) * G].astype(np.float64)
+            x = w.sm_scale * q @ K.T  # [G, L]
+            prob = np.exp(x - x.max(axis=1, keepdims=True))
+            prob /= prob.sum(axis=1, keepdims=True)
+            want = np.array([prob[:, 16 * p:16 * (p + 1)].sum(axis=1).mean() for p in range(n)])
+            assert np.allclose(pi, want, rtol=0, atol=1e-12), (b, h)
+
+
+def test_mvar_selection_runs_the_coverage_rule():
+    w = W.small(mode="coverage", estimator="mvar", gamma=0.9, n_local=1, seq_lens=(1200, 333, 40), Hq=8, Hkv=2,
+                planted=("fixed", 6), delta=("nats", 6.0), seed=25)
+    inp = W.generate(w)
+    stats = O.page_stats_build(inp)
+    sel = O.page_select(inp, O.page_meta_build(inp), stats)
+    for (b, h), lst in sel["lists"].items():
+        n = O.n_pages(w.seq_lens[b])
+        pi, _ = O.shares_from_logmass(O.row_logmass_mvar(inp, stats, b, h))
+        assert lst == O.select_coverage(pi, n, w.gamma, O.forced_pages(n, w.n_sink, w.n_local))
+        assert abs(pi.sum() - 1) < 1e-12
+
+
 # ------------------------------------------------------------------ attention
 
 def _dense_unpaged(inp, b, h):
