@@ -39,6 +39,7 @@ DEFAULT_WORKLOAD = "llama3_8b_b1_128k_f16"
 PEAK_HBM_TBS = 8.0
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SOURCES = ["score_common.h", "page_score.hip", "spd_device.h", "spd_launch.h"]  # what page_score_kernel is built from
+MVAR_SOURCES = KERNEL_SOURCES + ["page_score_mvar.hip", "meta_build.h"]  # page_score_mvar_kernel
 
 
 def kernel_hash(files=KERNEL_SOURCES) -> str:
@@ -58,12 +59,16 @@ def algorithmic_bytes(w, list_len: np.ndarray, head_kind: np.ndarray) -> dict:
     n_pages = w.n_pages
     dyn_heads = int((head_kind == 0).sum())
     meta = int(n_pages.sum()) * dyn_heads * 2 * d * meta_bytes
+    key_page = 16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0)
+    tail = w.batch * dyn_heads * (key_page + 2 * d * meta_bytes)
+    if w.estimator == "mvar":  # bf16 summaries; the first and current pages read as keys, one summary written
+        meta = int(np.maximum(n_pages - 2, 0).sum()) * dyn_heads * 2 * d * 2
+        tail = dyn_heads * int(np.minimum(n_pages, 2).sum()) * key_page + w.batch * dyn_heads * 2 * d * 2
     page_kv = 16 * d * kv_bytes * 2 + (16 * 2 * 2 if w.kv_dtype == "fp8" else 0)
     kv = int(list_len.sum()) * page_kv
     q = w.batch * w.num_q_heads * d * (4 if w.q_dtype == "f32" else 2)
     o = w.batch * w.num_q_heads * (d + 1) * 4
     tables = int(n_pages.sum()) * 4 + w.batch * 4
-    tail = w.batch * dyn_heads * (16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0) + 2 * d * meta_bytes)
     total = meta + kv + q + o + tables + tail
     return {"meta": meta, "kv": kv, "q": q, "o": o, "tables": tables, "tail": tail, "total": total}
 
@@ -78,10 +83,18 @@ def scorer_bytes(w, head_kind: np.ndarray, tail: str) -> int:
     meta_bytes = 4 if w.kv_dtype == "f32" else 2
     kv_bytes = {"f32": 4, "f16": 2, "fp8": 1}[w.kv_dtype]
     dyn_heads = int((head_kind == 0).sum())
+    q = w.batch * dyn_heads * w.group * d * (4 if w.q_dtype == "f32" else 2)
+    if w.estimator == "mvar":
+        # summaries + block-table entries + G log-masses of the estimated pages; keys of the first and
+        # current pages and their log-masses; the rebuilt summary of the current page
+        est = int(np.maximum(w.n_pages - 2, 0).sum()) * dyn_heads
+        exact = int(np.minimum(w.n_pages, 2).sum()) * dyn_heads
+        key_page = 16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0)
+        rebuilt = int((w.n_pages > 0).sum()) * dyn_heads * 2 * d * 2 if tail == "rebuild" else 0
+        return est * (2 * d * 2 + 4 + 4 * w.group) + exact * (key_page + 4 * w.group) + q + rebuilt
     rows = int((w.n_pages > 0).sum()) * dyn_heads
     scanned = int(w.n_pages.sum()) * dyn_heads - (rows if tail in ("side", "rebuild") else 0)
     per_page_head = 2 * d * meta_bytes + 4 + 4  # meta row + block-table entry + score
-    q = w.batch * dyn_heads * w.group * d * (4 if w.q_dtype == "f32" else 2)
     rebuilt = rows * (16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0) + 2 * d * meta_bytes + 4 + 4) \
         if tail == "rebuild" else 0
     return scanned * per_page_head + q + rebuilt
@@ -112,13 +125,17 @@ def cpu_baseline(w, inp, seconds: float) -> dict:
 
     from oracle import spd_oracle as O
 
+    mvar = w.estimator == "mvar"
     with threadpool_limits(limits=1):
-        meta = O.page_meta_build(inp)  # setup (the GPU builds it once before timing too)
+        # setup (the GPU builds the page summaries once before timing too)
+        meta = O.page_stats_build(inp) if mvar else O.page_meta_build(inp)
         first = [max(O.n_pages(L) - 1, 0) for L in inp.seq_lens]
         steps, t0 = 0, time.perf_counter()
         while True:
-            m2 = O.page_meta_build(inp, meta=meta, first_page=first)
-            sel = O.page_select(inp, m2)
+            if mvar:
+                sel = O.page_select(inp, None, O.page_stats_build(inp, first_page=first, stats=meta))
+            else:
+                sel = O.page_select(inp, O.page_meta_build(inp, meta=meta, first_page=first))
             O.sparse_paged_decode(inp, sel["lists"], w.sm_scale)
             steps += 1
             el = time.perf_counter() - t0
@@ -313,7 +330,9 @@ def main():
     tbs = ab["total"] / step_s / 1e12
 
     dom_name = "select" if args.fused else "score"
-    dom_kernel = "page_score_select_kernel" if args.fused else "page_score_kernel"
+    mvar = w.estimator == "mvar"
+    dom_kernel = "page_score_select_kernel" if args.fused else "page_score_mvar_kernel" if mvar else "page_score_kernel"
+    dom_hash = kernel_hash(MVAR_SOURCES if mvar else KERNEL_SOURCES)
     dom_bytes = scorer_bytes(w, inp.head_kind, probe.tail)
     dom_us = phase_us[dom_name]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
@@ -322,7 +341,7 @@ def main():
         with open(PMC_FILE) as f:
             pmc = json.load(f)
         rec = pmc.get(w.name, {})
-        if rec.get("kernel_hash") == kernel_hash() and rec.get("kernel") == dom_kernel:
+        if rec.get("kernel_hash") == dom_hash and rec.get("kernel") == dom_kernel:
             traffic = rec.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_TBS * 1000, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4),
@@ -351,6 +370,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "context": int(max(w.seq_lens)), "heads": heads,
                    "head_dim": w.head_dim, "page": 16, "kv_dtype": w.kv_dtype, "mode": w.mode,
+                   "estimator": w.estimator,
                    "budget_pages": w.budget_pages, "gamma": w.gamma, "streaming_kv_heads": len(w.streaming_heads),
                    "layers_rotated": R, "graph": True, "fused_select": args.fused,
                    "plan": [probe.plan.min_chunk, probe.plan.min_blocks_per_row, probe.plan.min_grid_blocks,
@@ -362,7 +382,7 @@ def main():
         "selection_overhead": sel_over, "reuse": reuse,
         "list_len": {"min": int(list_len.min()), "median": int(np.median(list_len)), "max": int(list_len.max())},
         "roofline": roofline, "cpu_baseline": cpu,
-        "setup_s": round(gen_s, 1), "kernel_hash": kernel_hash(),
+        "setup_s": round(gen_s, 1), "kernel_hash": dom_hash,
     }
     print(json.dumps(line))
 

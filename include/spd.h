@@ -5,11 +5,13 @@
  *   1. page_meta_build      per-page channel-wise key min / max
  *                           (LServe summary, "Hierarchical Paging" -- logical page
  *                           statistics k_min / k_max -- and "Key statistics storage and
- *                           updating": refreshed as tokens are appended)
+ *                           updating": refreshed as tokens are appended); or
+ *      page_stats_build     per-page channel-wise key mean / variance (Moira, section 3.1)
  *   2. page_score           Quest-style page bound S_j = sum_i max(q_i kmax_i, q_i kmin_i)
  *                           (LServe, "Hierarchical Paging", page importance score), combined
  *                           over the query-head group; in coverage mode turned into Moira's
- *                           group-mean page share pi_bar (Moira, section 3.2, Eq. 3)
+ *                           group-mean page share pi_bar (Moira, section 3.2, Eq. 3), from the
+ *                           bound or from the mvar estimate of each page's mass (Eq. 2)
  *   3. page_select          page list per row: forced sink + local pages plus either the
  *                           best pages under a page budget (LServe, "Token budget and
  *                           physical page selection") or the smallest share-threshold set
@@ -44,6 +46,13 @@
  *      page_meta    [num_pool_pages, Hkv, 2, d] index 0 = channel min, 1 = channel max;
  *                                              f32 for f32 pools, f16 otherwise (for fp8
  *                                              pools rounded outward: min down, max up)
+ *      page_stats   [num_pool_pages, Hkv, 2, d] bf16 bits: index 0 = channel mean, 1 =
+ *                                              channel variance (mean squared deviation) of
+ *                                              the page's valid keys, each rounded to nearest
+ *                                              even (Moira, section 3.1 "Page summaries and the
+ *                                              mvar estimate"; bf16 as in "Memory for page
+ *                                              summaries").  Scorers with the MVAR estimator
+ *                                              take it in the page_meta argument.
  *      block_table  [B, max_pages_per_seq]     int32 physical page of each logical page
  *      seq_lens     [B]                        int32 tokens of each request
  *      head_kind    [Hkv]                      uint8 (host) SPD_HEAD_DYNAMIC or _STREAMING
@@ -72,7 +81,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 5
+#define SPD_ABI_VERSION 6
 #define SPD_PAGE_SIZE 16
 #define SPD_MAX_KV_HEADS 64
 
@@ -94,6 +103,16 @@ typedef enum spd_select_mode {
   SPD_SELECT_TOPK = 0,       /* fixed page budget */
   SPD_SELECT_COVERAGE = 1    /* smallest share-threshold set reaching gamma */
 } spd_select_mode;
+
+/* How COVERAGE estimates the attention mass of a page: */
+typedef enum spd_estimator {
+  SPD_ESTIMATOR_BOUND = 0,   /* from the key box: l = sm_scale * S + ln(valid tokens) */
+  SPD_ESTIMATOR_MVAR = 1     /* from the page summary (Moira, section 3.1, Eq. 2):
+                              * l_g = s q_g . mu + (1/2) (s q_g)^2 . sigma^2 + ln(valid tokens),
+                              * s = sm_scale; the row's first page and its last page are not
+                              * estimated but computed exactly, l_g = log sum_k exp(s q_g . k)
+                              * over their valid keys read from k_pool */
+} spd_estimator;
 
 typedef enum spd_head_kind {
   SPD_HEAD_DYNAMIC = 0,
@@ -151,6 +170,7 @@ typedef struct spd_select_params {
   int32_t n_local;
   int32_t n_sink_stream;
   int32_t n_local_stream;
+  int32_t estimator;          /* spd_estimator; MVAR needs COVERAGE */
 } spd_select_params;
 
 /* Self-planned split (Moira, section 3.3, Eq. 4): J = max(min_blocks_per_row,
@@ -187,6 +207,15 @@ int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t
                         const int32_t* first_page, int32_t span_pages, void* page_meta,
                         void* stream);
 
+/* Moira page summaries (section 3.1, "Page summaries and the mvar estimate"): channel mean and
+ * variance of the valid keys of logical pages of each request, every KV head, written to
+ * page_stats (bf16, layout above) at the page's physical slot.  Pages, arguments and errors as
+ * in spd_page_meta_build. */
+int spd_page_stats_build(const spd_desc* desc, const void* k_pool, const uint16_t* k_scale,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* first_page, int32_t span_pages, void* page_stats,
+                         void* stream);
+
 /* Page scores of every dynamic row (streaming rows are skipped, their scores untouched).
  * TOPK: scores[b,h,p] = max over the G query heads of the row of S_{g,p} (LServe page
  * importance, computed from page_meta).  COVERAGE: l_{g,p} = sm_scale * S_{g,p} +
@@ -196,7 +225,11 @@ int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t
  * SPD_TAIL_REBUILD reads k_pool (and k_scale for fp8 pools) and writes that page's entries of
  * page_meta, which is otherwise only read; SPD_TAIL_SKIP is valid in TOPK mode only.  head_lse
  * (device, [B, Hq]) may be NULL in TOPK mode.  workspace (device) of spd_workspace_bytes(desc,
- * sel, SPD_OP_PAGE_SCORE) bytes (0 in TOPK mode). */
+ * sel, SPD_OP_PAGE_SCORE) bytes (0 in TOPK mode).
+ * With the MVAR estimator page_meta holds page_stats; k_pool (and k_scale for fp8 pools) is
+ * always read, for the exact first and last pages; SPD_TAIL_NONE leaves page_stats untouched and
+ * SPD_TAIL_REBUILD also writes the last page's summary (what spd_page_stats_build does for that
+ * page), for the steps after this one -- the page itself is computed exactly either way. */
 int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const void* q,
                    void* page_meta, const void* k_pool, const uint16_t* k_scale,
                    int32_t tail_mode, const int32_t* block_table, const int32_t* seq_lens,
@@ -213,7 +246,9 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
  * "Key statistics storage and updating"); block_table is then required, and the scores must
  * not depend on those statistics (the scorer ran with SPD_TAIL_SKIP).  sel_scores (device,
  * [B, Hkv, max_list], may be NULL) receives the score of each listed page of a dynamic row
- * (streaming rows: untouched).  Returns SPD_ERR_INVALID_ARG when max_list cannot hold the
+ * (streaming rows: untouched).  With the MVAR estimator page_meta is page_stats and the last
+ * page's summary is rebuilt by a second launch on the same stream, after the selection.  Returns
+ * SPD_ERR_INVALID_ARG when max_list cannot hold the
  * longest possible list: TOPK needs max_list >= max(budget, n_sink + n_local) and
  * >= n_sink_stream + n_local_stream; COVERAGE needs max_list >= max_pages_per_seq.  Rows of
  * more than 65536 pages return SPD_ERR_UNSUPPORTED. */
@@ -231,7 +266,8 @@ int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const fl
  * page_list, page_phys, list_len, sel_scores as in spd_page_select (block_table is
  * required).  workspace (device) of spd_workspace_bytes(desc, sel, SPD_OP_PAGE_SCORE_SELECT)
  * bytes must be zero-filled before its first use; every call leaves its counters zero
- * again.  Calls that share one workspace must not overlap. */
+ * again.  Calls that share one workspace must not overlap.  The MVAR estimator returns
+ * SPD_ERR_UNSUPPORTED. */
 int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, const void* q,
                           void* page_meta, const void* k_pool, const uint16_t* k_scale,
                           int32_t tail_mode, const int32_t* block_table, const int32_t* seq_lens,
@@ -248,8 +284,9 @@ int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, co
  * this call.  max_list must leave room for the pages a chunk can add (one per 16 tokens
  * appended, plus one); entries that do not fit are dropped.  page_phys (device, may be NULL)
  * receives the physical page of every appended entry; block_table is required.  When page_meta is
- * set, workgroups beside the rows also rebuild the key min / max of each request's last page, as in
- * spd_page_select.  Same ownership and errors as spd_page_select. */
+ * set, workgroups beside the rows also rebuild the key min / max of each request's last page (with
+ * the MVAR estimator: its summary), as in spd_page_select.  Same ownership and errors as
+ * spd_page_select. */
 int spd_page_list_refresh(const spd_desc* desc, const spd_select_params* sel, const int32_t* seq_lens,
                           const uint8_t* head_kind, const int32_t* block_table, const void* k_pool,
                           const uint16_t* k_scale, void* page_meta, int32_t* page_list,
@@ -293,7 +330,8 @@ int spd_plan_chunks(int32_t n_pages, int32_t blocks_per_row, int32_t min_chunk,
 int spd_partials_size(const spd_desc* desc, const spd_plan_params* plan, size_t* part_o_elems,
                       size_t* part_lse_elems);
 
-/* Workspace bytes an op needs (0 when it needs none); (size_t)-1 on invalid arguments. */
+/* Workspace bytes an op needs (0 when it needs none); (size_t)-1 on invalid arguments or an
+ * op that the arguments do not support. */
 size_t spd_workspace_bytes(const spd_desc* desc, const spd_select_params* sel, int32_t op);
 
 /* Static description of a status code. */

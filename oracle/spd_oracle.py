@@ -245,17 +245,17 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return np.where(np.abs(r) > big, np.copysign(np.inf, x), np.where(x == 0, x, r))
 
 
-def page_stats_build(inp, first_page=None, heads=None, requests=None) -> np.ndarray:
+def page_stats_build(inp, first_page=None, heads=None, requests=None, stats=None) -> np.ndarray:
     """Stored page summaries: mean and variance of the keys of every page p >= first_page[b]
     of every request, rounded to bfloat16 (Moira, "Memory for page summaries": the summaries
     are kept in bf16).
 
     Layout [num_pool_pages, Hkv, 2, d] float64 holding bf16 values: index 0 = mean,
-    1 = variance; pages not visited are NaN.
+    1 = variance; pages not visited are NaN, or keep their values in ``stats`` when given.
     """
     w = inp.workload
     Hkv, d = inp.k_pool.shape[1], inp.k_pool.shape[3]
-    out = np.full((inp.k_pool.shape[0], Hkv, 2, d), np.nan)
+    out = np.full((inp.k_pool.shape[0], Hkv, 2, d), np.nan) if stats is None else np.array(stats, dtype=np.float64)
     hs = list(range(Hkv)) if heads is None else [int(h) for h in heads]
     reqs = range(len(inp.seq_lens)) if requests is None else [int(b) for b in requests]
     for b in reqs:

@@ -25,8 +25,9 @@ SELECT_TOPK, SELECT_COVERAGE = 0, 1
 HEAD_DYNAMIC, HEAD_STREAMING = 0, 1
 OP_PAGE_SCORE, OP_PAGE_SELECT, OP_PAGE_SCORE_SELECT = 0, 1, 2
 TAIL_NONE, TAIL_REBUILD, TAIL_SKIP = 0, 1, 2
+ESTIMATOR_BOUND, ESTIMATOR_MVAR = 0, 1
 
-EXPORTS = ("spd_page_meta_build", "spd_page_score", "spd_page_select", "spd_page_score_select",
+EXPORTS = ("spd_page_meta_build", "spd_page_stats_build", "spd_page_score", "spd_page_select", "spd_page_score_select",
            "spd_sparse_paged_decode", "spd_lse_merge", "spd_plan_grid", "spd_plan_chunks", "spd_page_list_refresh",
            "spd_partials_size", "spd_workspace_bytes", "spd_error_string", "spd_abi_version")
 
@@ -47,7 +48,7 @@ class Desc(ctypes.Structure):
 class SelectParams(ctypes.Structure):
     _fields_ = [("mode", c_int32), ("budget_pages", c_int32), ("gamma", c_float), ("sm_scale", c_float),
                 ("n_sink", c_int32), ("n_local", c_int32), ("n_sink_stream", c_int32),
-                ("n_local_stream", c_int32)]
+                ("n_local_stream", c_int32), ("estimator", c_int32)]
 
 
 class PlanParams(ctypes.Structure):
@@ -68,6 +69,7 @@ def lib():
         D, S, P = POINTER(Desc), POINTER(SelectParams), POINTER(PlanParams)
         v = c_void_p
         L.spd_page_meta_build.argtypes = [D, v, v, v, v, v, c_int32, v, v]
+        L.spd_page_stats_build.argtypes = [D, v, v, v, v, v, c_int32, v, v]
         L.spd_page_score.argtypes = [D, S, v, v, v, v, c_int32, v, v, POINTER(c_uint8), v, v, v, c_size_t, v]
         L.spd_page_select.argtypes = [D, S, v, v, POINTER(c_uint8), v, v, v, v, v, v, v, v, v]
         L.spd_page_list_refresh.argtypes = [D, S, v, POINTER(c_uint8), v, v, v, v, v, v, v, v]
@@ -128,6 +130,13 @@ def spd_page_meta_build(desc, k_pool, k_scale, block_table, seq_lens, first_page
     _check(lib().spd_page_meta_build(ctypes.byref(desc), _ptr(k_pool), _ptr(k_scale), _ptr(block_table),
                                      _ptr(seq_lens), _ptr(first_page), int(span_pages), _ptr(page_meta),
                                      _stream(stream)), "spd_page_meta_build")
+
+
+def spd_page_stats_build(desc, k_pool, k_scale, block_table, seq_lens, first_page, span_pages, page_stats,
+                         stream=None):
+    _check(lib().spd_page_stats_build(ctypes.byref(desc), _ptr(k_pool), _ptr(k_scale), _ptr(block_table),
+                                      _ptr(seq_lens), _ptr(first_page), int(span_pages), _ptr(page_stats),
+                                      _stream(stream)), "spd_page_stats_build")
 
 
 def spd_page_score(desc, sel, q, page_meta, k_pool, k_scale, tail_mode, block_table, seq_lens, head_kind, scores,

@@ -100,6 +100,60 @@ __device__ __forceinline__ void build_page_meta(const MetaArgs& a, int b, int p,
   T::store(a.meta, (((size_t)phys * a.num_kv_heads + h) * 2) * D + c0, lo, hi, D);
 }
 
+// Moira page summary ("Page summaries and the mvar estimate"): channel-wise mean and variance of
+// the page's valid keys, stored as bf16 ("Memory for page summaries").  Same work layout as the
+// min / max: lane-local over the page's token rows, loaded at once.  The arithmetic is fp64 --
+// the sum of up to 16 stored keys is exact there, so the mean is the correctly rounded mean, and
+// the variance (mean squared deviation from it) carries only fp64 rounding -- and each value is
+// rounded once, straight from fp64 to bf16: the stored summary is the exact statistic rounded to
+// bf16, with no double rounding through fp32.
+__device__ __forceinline__ uint16_t f64_to_bf16_rn(double x) {
+  if (x != x) return 0x7fc0u;
+  if (x == 0.0) return (uint16_t)(__double_as_longlong(x) >> 48);  // keeps the sign of zero
+  int e;
+  (void)frexp(x, &e);                         // x = m 2^e, 0.5 <= |m| < 1
+  const double step = ldexp(1.0, max(e - 8, -133));  // 8 significant bits; bf16 subnormal step 2^-133
+  const double r = rint(x / step) * step;     // ties to even
+  if (fabs(r) > 3.3895313892515355e38) return x > 0 ? 0x7f80u : 0xff80u;  // past the largest finite bf16
+  return (uint16_t)(__float_as_uint((float)r) >> 16);  // r is exact in bf16, hence in fp32
+}
+
+template <int D, int KVD>
+__device__ __forceinline__ void build_page_stats(const MetaArgs& a, int b, int p, int h, int len) {
+  using T = MetaTraits<D, KVD>;
+  constexpr int CPL = T::CPL;
+  const int lane = threadIdx.x % kWave;
+  const int phys = a.block_table[(size_t)b * a.max_pages + p];
+  if (phys < 0 || phys >= a.num_pool_pages) return;
+  const int valid = valid_in_page(len, p);
+  if (valid <= 0) return;
+  const int c0 = lane * CPL;
+  const size_t head_base = ((size_t)phys * a.num_kv_heads + h) * kPage;
+  float v[kPage][CPL];
+#pragma unroll
+  for (int t = 0; t < kPage; ++t) {
+    float scale = 1.0f;
+    if (KVD == SPD_DTYPE_FP8_E4M3FN) scale = half_bits_to_float(a.k_scale[head_base + t]);
+    T::load(a.k_pool, (head_base + t) * D + c0, v[t], scale);
+  }
+  uint16_t* m = reinterpret_cast<uint16_t*>(a.meta) + (((size_t)phys * a.num_kv_heads + h) * 2) * D + c0;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    double sum = 0.0;
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) sum += t < valid ? (double)v[t][c] : 0.0;
+    const double mu = sum / valid;
+    double sq = 0.0;
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) {
+      const double dv = (double)v[t][c] - mu;
+      sq += t < valid ? dv * dv : 0.0;
+    }
+    m[c] = f64_to_bf16_rn(mu);
+    m[D + c] = f64_to_bf16_rn(sq / valid);
+  }
+}
+
 // build_page_meta for the head size and pool type given at run time (a.head_dim, a.kv_dtype).
 __device__ __forceinline__ void build_page_meta_rt(const MetaArgs& a, int b, int p, int h, int len) {
 #define SPD_META_RT(D, K) \

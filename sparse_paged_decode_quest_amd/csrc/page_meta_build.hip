@@ -1,11 +1,11 @@
 // Bulk statistics (every page of every request, at prefill), the pages [first_page, first_page
 // + span) of each request, or its last `span` pages (the page the newest token is in, during
-// decode).
+// decode): key min / max (page meta) or key mean / variance (page summaries).
 #include "meta_build.h"
 
 namespace spd {
 
-template <int D, int KVD>
+template <int D, int KVD, bool STATS>
 __global__ __launch_bounds__(256) void page_meta_build_kernel(MetaArgs a) {
   const int wave = threadIdx.x / kWave;
   const int b = blockIdx.x / a.blocks_per_req;
@@ -25,14 +25,16 @@ __global__ __launch_bounds__(256) void page_meta_build_kernel(MetaArgs a) {
   }
   const int p = start + p_off;
   if (p >= end) return;
-  build_page_meta<D, KVD>(a, b, p, h, len);
+  if constexpr (STATS) build_page_stats<D, KVD>(a, b, p, h, len);
+  else build_page_meta<D, KVD>(a, b, p, h, len);
 }
 
 int launch_page_meta_build(const MetaArgs& a, int head_dim, int kv_dtype, hipStream_t stream) {
   dim3 grid((unsigned)(a.batch * a.blocks_per_req)), block(256);
 #define SPD_META_CASE(D, K)                                                          \
   if (head_dim == D && kv_dtype == K) {                                              \
-    hipLaunchKernelGGL((page_meta_build_kernel<D, K>), grid, block, 0, stream, a);   \
+    if (a.stats) hipLaunchKernelGGL((page_meta_build_kernel<D, K, true>), grid, block, 0, stream, a);  \
+    else hipLaunchKernelGGL((page_meta_build_kernel<D, K, false>), grid, block, 0, stream, a);     \
     return 0;                                                                        \
   }
   SPD_META_CASE(64, SPD_DTYPE_F32)

@@ -170,10 +170,16 @@ __global__ __launch_bounds__(kShareThreads) void coverage_share_kernel(ScoreArgs
   if (p < r.n) a.scores[r.row * a.max_pages + p] = group_share(l4, lse);
 }
 
+void launch_coverage_shares(const ScoreArgs& a, hipStream_t stream) {
+  const unsigned rows = (unsigned)(a.batch * a.dyn.count);
+  const dim3 share_grid(rows * (unsigned)share_blocks_per_row(a.max_pages)), share_block(kShareThreads);
+  hipLaunchKernelGGL(coverage_part_kernel, share_grid, share_block, 0, stream, a);
+  hipLaunchKernelGGL(coverage_share_kernel, share_grid, share_block, 0, stream, a);
+}
+
 int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool coverage, hipStream_t stream) {
   const unsigned rows = (unsigned)(a.batch * a.dyn.count);
   const dim3 grid(rows * (unsigned)(a.blocks_per_row + tail_blocks(a))), block(kScoreWaves * kWave);
-  const dim3 share_grid(rows * (unsigned)share_blocks_per_row(a.max_pages)), share_block(kShareThreads);
   const bool long_scan = score_iters((long long)rows * a.max_pages) == kScoreItersLong;
 #define SPD_SCORE_LAUNCH(D, KVD, COV)                                                                           \
   if (long_scan) hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, kScoreItersLong>), grid, block, 0, stream, a); \
@@ -182,8 +188,7 @@ int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool cover
   if (head_dim == D && kv_dtype == KVD) {                                                       \
     if (coverage) {                                                                             \
       SPD_SCORE_LAUNCH(D, KVD, true)                                                            \
-      hipLaunchKernelGGL(coverage_part_kernel, share_grid, share_block, 0, stream, a);          \
-      hipLaunchKernelGGL(coverage_share_kernel, share_grid, share_block, 0, stream, a);         \
+      launch_coverage_shares(a, stream);                                                        \
     } else {                                                                                    \
       SPD_SCORE_LAUNCH(D, KVD, false)                                                           \
     }                                                                                           \

@@ -17,10 +17,13 @@ namespace {
 // pages per scoring workgroup (fixed by the compiled work layouts)
 int meta_bytes_of(const spd_desc* d) { return d->kv_dtype == SPD_DTYPE_F32 ? 4 : 2; }
 
-// Pages per scorer workgroup (the standalone scorer's page groups per lane depend on the scan's size).
-int score_ppb(const spd_desc* d, int dyn_heads) {
+bool is_mvar(const spd_select_params* s) { return s->estimator == SPD_ESTIMATOR_MVAR; }
+
+// Pages per scorer workgroup (the standalone scorer's page groups per lane depend on the scan's size;
+// the mvar page summaries are bf16 whatever the pool type).
+int score_ppb(const spd_desc* d, const spd_select_params* s, int dyn_heads) {
   const int iters = spd::score_iters((long long)d->batch * dyn_heads * d->max_pages_per_seq);
-  return spd::score_pages_per_block(d->head_dim, meta_bytes_of(d), spd::kScoreWaves, iters);
+  return spd::score_pages_per_block(d->head_dim, is_mvar(s) ? 2 : meta_bytes_of(d), spd::kScoreWaves, iters);
 }
 
 int fused_ppb(const spd_desc* d, const spd::SelectGeometry& g) {
@@ -64,6 +67,8 @@ int check_sel(const spd_desc* d, const spd_select_params* s) {
   } else {
     return SPD_ERR_INVALID_ARG;
   }
+  if (s->estimator != SPD_ESTIMATOR_BOUND && s->estimator != SPD_ESTIMATOR_MVAR) return SPD_ERR_INVALID_ARG;
+  if (s->estimator == SPD_ESTIMATOR_MVAR && s->mode != SPD_SELECT_COVERAGE) return SPD_ERR_INVALID_ARG;
   (void)d;
   return SPD_OK;
 }
@@ -226,6 +231,27 @@ spd::MetaArgs meta_args(const spd_desc* d, const void* k_pool, const uint16_t* k
   return a;
 }
 
+// spd_page_meta_build and spd_page_stats_build: the pages to build and the launch.
+int build_summaries(const spd_desc* desc, const void* k_pool, const uint16_t* k_scale, const int32_t* block_table,
+                    const int32_t* seq_lens, const int32_t* first_page, int32_t span_pages, void* out, int stats,
+                    void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (desc->batch == 0) return SPD_OK;
+  if (!k_pool || !block_table || !seq_lens || !out) return SPD_ERR_INVALID_ARG;
+  if (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale) return SPD_ERR_INVALID_ARG;
+  if ((first_page && span_pages < 1) || span_pages < 0) return SPD_ERR_INVALID_ARG;
+  spd::MetaArgs a = meta_args(desc, k_pool, k_scale, block_table, seq_lens, out);
+  a.first_page = first_page;
+  a.stats = stats;
+  // pages per request: the span (from first_page, or the last span pages), or every page
+  const int span = (first_page || span_pages > 0) ? std::min(span_pages, desc->max_pages_per_seq)
+                                                  : desc->max_pages_per_seq;
+  a.span = span;
+  a.blocks_per_req = (span * desc->num_kv_heads + 3) / 4;
+  return launched(spd::launch_page_meta_build(a, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -287,7 +313,7 @@ size_t spd_workspace_bytes(const spd_desc* desc, const spd_select_params* sel, i
     case SPD_OP_PAGE_SELECT: return 0;
     case SPD_OP_PAGE_SCORE_SELECT: {
       FusedWs w;
-      return fused_ws(desc, sel, w) ? w.total : (size_t)-1;
+      return !is_mvar(sel) && fused_ws(desc, sel, w) ? w.total : (size_t)-1;
     }
     default: return (size_t)-1;
   }
@@ -296,20 +322,14 @@ size_t spd_workspace_bytes(const spd_desc* desc, const spd_select_params* sel, i
 int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t* k_scale,
                         const int32_t* block_table, const int32_t* seq_lens, const int32_t* first_page,
                         int32_t span_pages, void* page_meta, void* stream) {
-  int rc = check_desc(desc);
-  if (rc) return rc;
-  if (desc->batch == 0) return SPD_OK;
-  if (!k_pool || !block_table || !seq_lens || !page_meta) return SPD_ERR_INVALID_ARG;
-  if (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale) return SPD_ERR_INVALID_ARG;
-  if ((first_page && span_pages < 1) || span_pages < 0) return SPD_ERR_INVALID_ARG;
-  spd::MetaArgs a = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
-  a.first_page = first_page;
-  // pages per request: the span (from first_page, or the last span pages), or every page
-  const int span = (first_page || span_pages > 0) ? std::min(span_pages, desc->max_pages_per_seq)
-                                                  : desc->max_pages_per_seq;
-  a.span = span;
-  a.blocks_per_req = (span * desc->num_kv_heads + 3) / 4;
-  return launched(spd::launch_page_meta_build(a, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
+  return build_summaries(desc, k_pool, k_scale, block_table, seq_lens, first_page, span_pages, page_meta, 0, stream);
+}
+
+int spd_page_stats_build(const spd_desc* desc, const void* k_pool, const uint16_t* k_scale,
+                         const int32_t* block_table, const int32_t* seq_lens, const int32_t* first_page,
+                         int32_t span_pages, void* page_stats, void* stream) {
+  return build_summaries(desc, k_pool, k_scale, block_table, seq_lens, first_page, span_pages, page_stats, 1,
+                         stream);
 }
 
 int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const void* q, void* page_meta,
@@ -325,7 +345,9 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
   if (desc->batch == 0 || dyn.count == 0) return SPD_OK;
   if (!q || !page_meta || !block_table || !seq_lens || !scores) return SPD_ERR_INVALID_ARG;
   if ((rc = check_tail(desc, sel, tail_mode, k_pool, k_scale))) return rc;
-  spd::ScoreArgs a = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, score_ppb(desc, dyn.count));
+  // the mvar estimator computes the first and current pages exactly, from the K pool
+  if (is_mvar(sel) && (!k_pool || (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale))) return SPD_ERR_INVALID_ARG;
+  spd::ScoreArgs a = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, score_ppb(desc, sel, dyn.count));
   a.scores = scores;
   a.meta_out = page_meta;
   a.k_pool = k_pool;
@@ -340,6 +362,7 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
     a.partials = reinterpret_cast<float2*>(static_cast<char*>(workspace) + w.part_off);
     a.head_lse = head_lse;
   }
+  if (is_mvar(sel)) return launched(spd::launch_page_score_mvar(a, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
   return launched(spd::launch_page_score(a, desc->head_dim, desc->kv_dtype, coverage, (hipStream_t)stream));
 }
 
@@ -363,8 +386,12 @@ int spd_page_select(const spd_desc* desc, const spd_select_params* sel, const fl
     return SPD_ERR_INVALID_ARG;
   spd::SelectArgs a = select_args(desc, sel, seq_lens, block_table, page_list, page_phys, list_len, sel_scores, mask);
   a.scores = scores;
-  if (page_meta) a.tail = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
-  return launched(spd::launch_page_select(a, (hipStream_t)stream));
+  if (page_meta && !is_mvar(sel)) a.tail = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
+  if ((rc = launched(spd::launch_page_select(a, (hipStream_t)stream)))) return rc;
+  // page summaries (mvar): a launch of their own, which keeps the selector's registers unchanged
+  if (page_meta && is_mvar(sel))
+    return build_summaries(desc, k_pool, k_scale, block_table, seq_lens, nullptr, 1, page_meta, 1, stream);
+  return SPD_OK;
 }
 
 int spd_page_list_refresh(const spd_desc* desc, const spd_select_params* sel, const int32_t* seq_lens,
@@ -382,8 +409,11 @@ int spd_page_list_refresh(const spd_desc* desc, const spd_select_params* sel, co
   if (!seq_lens || !page_list || !list_len || !block_table) return SPD_ERR_INVALID_ARG;
   if (page_meta && (!k_pool || (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale))) return SPD_ERR_INVALID_ARG;
   spd::SelectArgs a = select_args(desc, sel, seq_lens, block_table, page_list, page_phys, list_len, nullptr, mask);
-  if (page_meta) a.tail = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
-  return launched(spd::launch_page_list_refresh(a, (hipStream_t)stream));
+  if (page_meta && !is_mvar(sel)) a.tail = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
+  if ((rc = launched(spd::launch_page_list_refresh(a, (hipStream_t)stream)))) return rc;
+  if (page_meta && is_mvar(sel))
+    return build_summaries(desc, k_pool, k_scale, block_table, seq_lens, nullptr, 1, page_meta, 1, stream);
+  return SPD_OK;
 }
 
 int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, const void* q, void* page_meta,
@@ -396,7 +426,7 @@ int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, co
   if ((rc = check_sel(desc, sel))) return rc;
   if ((rc = check_list_capacity(desc, sel))) return rc;
   FusedWs w;
-  if (!fused_ws(desc, sel, w)) return SPD_ERR_UNSUPPORTED;
+  if (is_mvar(sel) || !fused_ws(desc, sel, w)) return SPD_ERR_UNSUPPORTED;
   spd::HeadList dyn, strm;
   uint64_t mask;
   if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;

@@ -67,6 +67,18 @@ __device__ __forceinline__ uint16_t f32_to_f16_round_down(float x) {
   return bits;
 }
 
+// bfloat16 (the top 16 bits of an fp32): nearest, ties to even; NaN stays a quiet NaN and values
+// past the largest finite bf16 round to infinity.
+__device__ __forceinline__ uint16_t f32_to_bf16_rn(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// The two bf16 values packed in a 32-bit word, as fp32 (exact: a shift).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 // ------------------------------------------------------------------ streaming loads
 
 // Loads of data read once per step (page meta in the scorer, K / V pages in decode), marked

@@ -46,6 +46,7 @@ struct MetaArgs {
   int span;            // pages after first_page (when first_page is set)
   int blocks_per_req;  // workgroups per request (4 (page, head) items each)
   int head_dim, kv_dtype;
+  int stats;           // 0: key min / max (page meta); 1: key mean / variance, bf16 (page summaries)
 };
 int launch_page_meta_build(const MetaArgs& a, int head_dim, int kv_dtype, hipStream_t stream);
 
@@ -76,6 +77,10 @@ struct ScoreArgs {
   int tail_mode;             // spd_tail_mode: last page of each dynamic row scored / rebuilt / skipped
 };
 int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool coverage, hipStream_t stream);
+// Coverage shares from the log-masses in a.ell (the scorers' second and third kernels).
+void launch_coverage_shares(const ScoreArgs& a, hipStream_t stream);
+// Coverage log-masses from the Moira page summaries (mvar), then the shares.
+int launch_page_score_mvar(const ScoreArgs& a, int head_dim, int kv_dtype, hipStream_t stream);
 
 struct SelectArgs {
   const float* scores;      // [B, Hkv, max_pages] (top-K scores or coverage shares)

@@ -49,7 +49,7 @@ class DeviceInputs:
     block_table: torch.Tensor
     seq_lens: torch.Tensor
     head_kind: np.ndarray      # host
-    page_meta: torch.Tensor    # [Npool, Hkv, 2, d]
+    page_meta: torch.Tensor    # [Npool, Hkv, 2, d]: key min / max, or (mvar) key mean / variance in bf16
 
     @property
     def num_pool_pages(self) -> int:
@@ -57,7 +57,7 @@ class DeviceInputs:
 
 
 def upload(inp: Inputs, device="cuda") -> DeviceInputs:
-    """Copy one step's stored inputs to the device and allocate the page-meta buffer."""
+    """Copy one step's stored inputs to the device and allocate the page-summary buffer."""
     w = inp.workload
 
     def t(x):
@@ -65,7 +65,7 @@ def upload(inp: Inputs, device="cuda") -> DeviceInputs:
 
     k_scale = None if inp.k_scale is None else t(inp.k_scale.view(np.int16))
     v_scale = None if inp.v_scale is None else t(inp.v_scale.view(np.int16))
-    mdt = torch.float32 if w.kv_dtype == "f32" else torch.float16
+    mdt = torch.bfloat16 if w.estimator == "mvar" else torch.float32 if w.kv_dtype == "f32" else torch.float16
     meta = torch.zeros((inp.num_pool_pages, w.num_kv_heads, 2, w.head_dim), dtype=mdt, device=device)
     return DeviceInputs(q=t(inp.q), k_pool=t(inp.k_pool), v_pool=t(inp.v_pool), k_scale=k_scale, v_scale=v_scale,
                         block_table=t(inp.block_table), seq_lens=t(inp.seq_lens), head_kind=inp.head_kind.copy(),
@@ -88,13 +88,20 @@ def make_select(w: Workload) -> A.SelectParams:
     return A.SelectParams(mode=A.SELECT_COVERAGE if w.mode == "coverage" else A.SELECT_TOPK,
                           budget_pages=max(1, w.budget_pages), gamma=float(w.gamma) if w.gamma else 1.0,
                           sm_scale=w.sm_scale, n_sink=w.n_sink, n_local=w.n_local,
-                          n_sink_stream=w.n_sink_stream, n_local_stream=w.n_local_stream)
+                          n_sink_stream=w.n_sink_stream, n_local_stream=w.n_local_stream,
+                          estimator=A.ESTIMATOR_MVAR if w.estimator == "mvar" else A.ESTIMATOR_BOUND)
+
+
+def build_summaries(w: Workload, d: DeviceInputs, first_page, span: int, stream=None) -> None:
+    """Page summaries of the workload's estimator: key min / max, or key mean / variance (mvar)."""
+    fn = A.spd_page_stats_build if w.estimator == "mvar" else A.spd_page_meta_build
+    fn(make_desc(w, d.num_pool_pages), d.k_pool, d.k_scale, d.block_table, d.seq_lens, first_page, span, d.page_meta,
+       stream)
 
 
 def build_meta(w: Workload, d: DeviceInputs, stream=None) -> None:
     """Bulk page statistics of every page in the block tables (done once, at prefill)."""
-    desc = make_desc(w, d.num_pool_pages)
-    A.spd_page_meta_build(desc, d.k_pool, d.k_scale, d.block_table, d.seq_lens, None, 0, d.page_meta, stream)
+    build_summaries(w, d, None, 0, stream)
 
 
 TAILS = ("auto", "none", "select", "side", "serial", "rebuild")
@@ -114,8 +121,12 @@ class DecodeStep:
       scorer that skips that page (top-K with a local window);
     * ``"serial"``: the all-heads rebuild, then a scorer that reads the rebuilt statistics;
     * ``"rebuild"``: inside the scorer, by one extra workgroup per dynamic row;
-    * ``"auto"`` (default): ``"select"`` where it applies, ``"rebuild"`` for a fused top-K step,
-      else ``"serial"``.
+    * ``"auto"`` (default): ``"select"`` where it applies, ``"rebuild"`` for a fused top-K step
+      and for the mvar estimator (whose scorer reads that page's keys anyway), else ``"serial"``.
+
+    With the mvar estimator (Moira, section 3.1) ``d.page_meta`` holds the bf16 page summaries
+    and the scorer computes each row's first and current pages exactly; scoring and selection are
+    then two calls.
 
     ``phys_lists`` (default) has the selector write the physical page of every list entry so
     the decode kernel does not read the block table.  ``keep_sel_scores`` has it also write the
@@ -132,8 +143,10 @@ class DecodeStep:
         if tail not in TAILS:
             raise ValueError(f"tail must be one of {TAILS}")
         skippable = w.mode == "topk" and w.n_local >= 1
+        if fused and w.estimator == "mvar":
+            raise ValueError("the fused score + select launch has no mvar estimator")
         if tail == "auto":
-            tail = ("rebuild" if fused else "select") if skippable else "serial"
+            tail = ("rebuild" if fused else "select") if skippable else "rebuild" if w.estimator == "mvar" else "serial"
         if tail in ("select", "side") and not skippable:
             raise ValueError(f"tail={tail!r} skips the last page: top-K with a local window only")
         if tail == "select" and fused:
@@ -173,9 +186,8 @@ class DecodeStep:
         self.workspace = torch.zeros(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
 
     def refresh_tail(self, stream=None):
-        """page_meta_build of the page the newest token is in (one page per request, all heads)."""
-        d = self.d
-        A.spd_page_meta_build(self.desc, d.k_pool, d.k_scale, d.block_table, d.seq_lens, None, 1, d.page_meta, stream)
+        """Summary of the page the newest token is in (one page per request, all heads)."""
+        build_summaries(self.w, self.d, None, 1, stream)
 
     def score(self, stream=None, tail_mode=None):
         """Page scores, treating each dynamic row's last page by the step's tail mode."""

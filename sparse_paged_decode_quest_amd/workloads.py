@@ -186,11 +186,18 @@ def named(name: str, seed_offset: int = 0) -> Workload:
                         kv_dtype="f16", q_dtype="f16", mode="topk", budget_pages=8192,
                         n_sink=1, n_local=2, planted=("fixed", 64), delta=2.0,
                         seed=BASE_SEED + 5 + seed_offset)
+    if name == "coverage_mvar_b4_128k_f16":
+        # the coverage step with Moira's mvar page estimate (section 3.1) in place of the key box
+        return Workload(name=name, seq_lens=(131072,) * 4, num_q_heads=32, num_kv_heads=8,
+                        head_dim=128, kv_dtype="f16", q_dtype="f16", mode="coverage", estimator="mvar",
+                        gamma=0.99, n_sink=1, n_local=1, planted=("loguniform", 20, 2000),
+                        delta=("nats", 12.0), seed=BASE_SEED + 6 + seed_offset)
     raise KeyError(name)
 
 
 NAMED = ("tiny_b1_hq8_d64_4k_f32", "llama3_8b_b1_128k_f16", "mixed_b8_bimodal_f16",
-         "mixed_b8_powerlaw_f16", "coverage_b4_128k_f16", "fp8_b1_512k", "llama3_8b_b1_128k_f16_dense")
+         "mixed_b8_powerlaw_f16", "coverage_b4_128k_f16", "fp8_b1_512k", "llama3_8b_b1_128k_f16_dense",
+         "coverage_mvar_b4_128k_f16")
 
 
 # --------------------------------------------------------------------------------------

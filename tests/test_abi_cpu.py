@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 5
+    assert A.abi_version() == 6
 
 
 def test_error_strings(lib):
@@ -210,6 +210,33 @@ def test_select_and_fused_argument_checks(lib):
     assert fused_rc(long, sel_for(w)) == A.SPD_ERR_UNSUPPORTED
     with pytest.raises(A.SpdError):
         A.spd_workspace_bytes(long, sel_for(w), A.OP_PAGE_SCORE_SELECT)
+
+
+def test_mvar_estimator_argument_checks(lib):
+    wc = W.small(mode="coverage", gamma=0.9, estimator="mvar")
+    d = desc_for(wc)
+    mv = sel_for(wc, estimator=A.ESTIMATOR_MVAR)
+    assert score_rc(d, sel_for(wc, estimator=2)) == A.SPD_ERR_INVALID_ARG           # unknown estimator
+    w = W.small()
+    assert score_rc(desc_for(w), sel_for(w, estimator=A.ESTIMATOR_MVAR)) == A.SPD_ERR_INVALID_ARG  # top-K
+    assert score_rc(d, mv, k_pool=None) == A.SPD_ERR_INVALID_ARG   # the first and last pages read K
+    wf = W.small(mode="coverage", gamma=0.9, kv="fp8", estimator="mvar")
+    assert score_rc(desc_for(wf), sel_for(wf, estimator=A.ESTIMATOR_MVAR), k_scale=None) == A.SPD_ERR_INVALID_ARG
+    assert score_rc(d, mv, tail=A.TAIL_SKIP) == A.SPD_ERR_INVALID_ARG
+    need = A.spd_workspace_bytes(d, mv, A.OP_PAGE_SCORE)
+    assert need == A.spd_workspace_bytes(d, sel_for(wc), A.OP_PAGE_SCORE) > 0
+    assert score_rc(d, mv, ws_bytes=need - 1) == A.SPD_ERR_WORKSPACE
+    # the fused launch has no mvar estimator
+    assert fused_rc(d, mv) == A.SPD_ERR_UNSUPPORTED
+    with pytest.raises(A.SpdError):
+        A.spd_workspace_bytes(d, mv, A.OP_PAGE_SCORE_SELECT)
+    # summary builds: same checks as the key-box build
+    stats = A.lib().spd_page_stats_build
+    assert stats(ctypes.byref(d), None, None, FAKE, FAKE, None, 0, FAKE, 0) == A.SPD_ERR_INVALID_ARG
+    assert stats(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, 0, FAKE, 0) == A.SPD_ERR_INVALID_ARG  # span >= 1
+    assert stats(ctypes.byref(d), FAKE, None, FAKE, FAKE, None, -1, FAKE, 0) == A.SPD_ERR_INVALID_ARG
+    assert stats(ctypes.byref(desc_for(wf)), FAKE, None, FAKE, FAKE, None, 0, FAKE, 0) == A.SPD_ERR_INVALID_ARG
+    assert stats(ctypes.byref(desc_for(wc, batch=0)), None, None, None, None, None, 0, None, 0) == A.SPD_OK
 
 
 def test_empty_batch_launches_nothing(lib):

@@ -32,8 +32,9 @@ def test_named_workload(name):
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
 
-    # 1. page meta on sampled pages (all heads), exact
-    meta_gpu = d.page_meta.cpu().numpy()
+    # 1. page meta (or mvar summaries) on sampled pages (all heads), exact
+    mvar = w.estimator == "mvar"
+    meta_gpu = (d.page_meta.float() if mvar else d.page_meta).cpu().numpy()
     for b in range(w.batch):
         n = O.n_pages(inp.seq_lens[b])
         pages = sorted(set(rng.choice(n, size=min(n, 24), replace=False).tolist()) | {n - 1})
@@ -42,8 +43,12 @@ def test_named_workload(name):
             valid = O.valid_tokens(inp.seq_lens[b], p)
             for h in range(w.num_kv_heads):
                 sc = None if inp.k_scale is None else inp.k_scale[phys, h]
-                lo, hi = O.to_stored_meta(*O.page_key_minmax(O.stored_values(inp.k_pool[phys, h], sc, w.kv_dtype),
-                                                             valid), w.kv_dtype)
+                keys = O.stored_values(inp.k_pool[phys, h], sc, w.kv_dtype)
+                if mvar:
+                    mu, var = O.page_mean_var(keys, valid)
+                    lo, hi = O.round_bf16(mu), O.round_bf16(var)
+                else:
+                    lo, hi = O.to_stored_meta(*O.page_key_minmax(keys, valid), w.kv_dtype)
                 assert np.array_equal(meta_gpu[phys, h, 0], lo) and np.array_equal(meta_gpu[phys, h, 1], hi), \
                     (b, p, h)
 
@@ -69,8 +74,8 @@ def test_named_workload(name):
             oracle_lists[(b, h)] = O.forced_pages(n, w.n_sink_stream, w.n_local_stream)
             assert gpu_lists[(b, h)] == oracle_lists[(b, h)]
             continue
-        meta_ref = O.page_meta_build(inp, heads=[h], requests=[b])
-        S_ = O.row_bounds(inp, meta_ref, b, h)
+        meta_ref = None if mvar else O.page_meta_build(inp, heads=[h], requests=[b])
+        S_ = None if mvar else O.row_bounds(inp, meta_ref, b, h)
         forced = O.forced_pages(n, w.n_sink, w.n_local)
         if w.mode == "topk":
             ref = O.topk_scores(S_)
@@ -82,6 +87,12 @@ def test_named_workload(name):
                 P.check_topk_scores(gpu_scores[b, h, :n], ref, scale)
             P.check_topk_list(gpu_lists[(b, h)], ref, n, w.budget_pages, forced, scale)
             oracle_lists[(b, h)] = O.select_topk(ref, n, w.budget_pages, forced)
+        elif mvar:
+            stats = O.page_stats_build(inp, heads=[h], requests=[b])
+            pi, _ = O.shares_from_logmass(O.row_logmass_mvar(inp, stats, b, h))
+            P.check_coverage_shares(gpu_scores[b, h, :n], pi)
+            P.check_coverage_list(gpu_lists[(b, h)], pi, n, w.gamma, forced)
+            oracle_lists[(b, h)] = O.select_coverage(pi, n, w.gamma, forced)
         else:
             pi, _ = O.coverage_shares(S_, int(inp.seq_lens[b]), w.sm_scale)
             P.check_coverage_shares(gpu_scores[b, h, :n], pi)
