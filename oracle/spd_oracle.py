@@ -20,6 +20,11 @@ Pages and their definitions:
     above tau reaches gamma minus the forced shares.
   * PersistentKV (section 3.1, Eq. 1): exact decode attention over the kept
     tokens; section 3.3: split states and their exact merge.
+  * LServe ("Hierarchical Paging", "Token budget and physical page selection"):
+    physical pages of N_P = g * N_L tokens hold g logical pages of N_L = 16
+    tokens; each logical page keeps its own key min / max, and a physical page's
+    importance is the largest importance of its logical pages; the top-K runs
+    over physical pages and attention reads whole physical pages.
   * Moira (section 3.1 "Page summaries and the mvar estimate", Eq. 2): per page
     and KV head the channel-wise mean and variance of the keys; the page's
     estimated attention mass for query head g is
@@ -38,6 +43,9 @@ Readings where the pages leave a step open:
   * fp8 pools are OCP E4M3FN with a per-(page, head, token) fp16 scale; their key
     min / max is stored as fp16 rounded outward (max up, min down).
   * An empty row (no kept tokens) gives O = 0 and lse = -inf.
+  * Hierarchical paging: the GQA group is combined as above (max over query heads)
+    after the max over logical pages; logical pages with no valid token do not
+    enter the max; the budget, the sink and the local window count physical pages.
   * mvar: the variance is the population variance over the page's valid tokens
     (divided by their count), and the token count in Eq. 2 is the page's valid
     token count; mean and variance are stored rounded to bf16 (nearest, ties to even)
@@ -474,11 +482,144 @@ def split_state(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float):
 
 
 # --------------------------------------------------------------------------------------
+# Hierarchical paging: N_P-token physical pages over N_L = 16-token logical pages
+# --------------------------------------------------------------------------------------
+
+def physical_page_tokens(inp) -> int:
+    """N_P, the tokens of one physical page: the pool's third axis."""
+    return int(inp.k_pool.shape[2])
+
+
+def hier_n_physical(seq_len: int, page_tokens: int) -> int:
+    return (int(seq_len) + page_tokens - 1) // page_tokens
+
+
+def hier_logical_keys(inp, b: int, h: int, lp: int) -> np.ndarray:
+    """Valid keys (float64 [valid, d]) of logical page lp of request b, KV head h.
+
+    Logical page lp covers tokens [16 lp, 16 lp + 16) of the request; they sit in physical page
+    block_table[b, lp // g] at token slots 16 (lp % g) ... 16 (lp % g) + 15.
+    """
+    w = inp.workload
+    g = physical_page_tokens(inp) // PAGE
+    phys = int(inp.block_table[b, lp // g])
+    sl = slice(PAGE * (lp % g), PAGE * (lp % g) + PAGE)
+    scale = None if inp.k_scale is None else inp.k_scale[phys, h, sl]
+    return stored_values(inp.k_pool[phys, h, sl], scale, w.kv_dtype)[:valid_tokens(inp.seq_lens[b], lp)]
+
+
+def hier_meta_build(inp) -> np.ndarray:
+    """Key min / max of every logical page of every request, all KV heads (LServe: statistics
+    on N_L-token logical pages, stored with the physical page that holds them).
+
+    Layout [num_pool_pages, Hkv, g, 2, d]: entry [P, h, i] is logical sub-page i of physical page
+    P; 0 = kmin, 1 = kmax, in the meta dtype (fp8 pools: fp16 rounded outward).  Sub-pages past a
+    request's end are left at zero.
+    """
+    w = inp.workload
+    Npool, Hkv, NP, d = inp.k_pool.shape
+    g = NP // PAGE
+    out = np.zeros((Npool, Hkv, g, 2, d), dtype=meta_dtype(w.kv_dtype))
+    for b in range(len(inp.seq_lens)):
+        for lp in range(n_pages(inp.seq_lens[b])):
+            phys = int(inp.block_table[b, lp // g])
+            for h in range(Hkv):
+                keys = hier_logical_keys(inp, b, h, lp)
+                lo, hi = to_stored_meta(keys.min(axis=0), keys.max(axis=0), w.kv_dtype)
+                out[phys, h, lp % g, 0] = lo
+                out[phys, h, lp % g, 1] = hi
+    return out
+
+
+def hier_row_scores(inp, meta: np.ndarray, b: int, h: int):
+    """Physical page scores of dynamic row (b, h) (LServe, "Physical page importance
+    aggregation"): each logical page's bound S_{g,lp} from its stored key box, then the largest
+    over the logical pages of each physical page and over the group's query heads.
+
+    Returns (scores [n_physical], S [G, n_logical]).
+    """
+    w = inp.workload
+    G = w.group
+    NP = physical_page_tokens(inp)
+    g = NP // PAGE
+    L = int(inp.seq_lens[b])
+    n_log = n_pages(L)
+    lps = np.arange(n_log)
+    phys = inp.block_table[b, lps // g].astype(np.int64)
+    m = meta[phys, h, lps % g].astype(np.float64)            # [n_log, 2, d]
+    q = inp.q[b, h * G:(h + 1) * G].astype(np.float64)
+    S = quest_bound(q, m[:, 0], m[:, 1])                      # [G, n_log]
+    per_logical = S.max(axis=0) if n_log else np.zeros(0)
+    scores = np.array([per_logical[j * g:(j + 1) * g].max() for j in range(hier_n_physical(L, NP))])
+    return scores, S
+
+
+def hier_page_select(inp, meta: np.ndarray):
+    """Lists of physical pages for every row: streaming rows keep their sink + local physical
+    pages; dynamic rows the forced physical pages plus the best others under the physical page
+    budget (top-K by (score desc, page asc)).  Same dict as page_select."""
+    w = inp.workload
+    assert w.mode == "topk", "hierarchical paging is defined for the top-K rule"
+    NP = physical_page_tokens(inp)
+    out = {"lists": {}, "scores": {}, "S": {}, "lse": {}}
+    for b in range(len(inp.seq_lens)):
+        n = hier_n_physical(inp.seq_lens[b], NP)
+        for h in range(inp.k_pool.shape[1]):
+            if inp.head_kind[h]:
+                out["lists"][(b, h)] = forced_pages(n, w.n_sink_stream, w.n_local_stream)
+                out["scores"][(b, h)] = None
+                continue
+            sc, S = hier_row_scores(inp, meta, b, h)
+            out["scores"][(b, h)], out["S"][(b, h)] = sc, S
+            out["lists"][(b, h)] = select_topk(sc, n, w.budget_pages, forced_pages(n, w.n_sink, w.n_local))
+    return out
+
+
+def hier_gather_tokens(inp, b: int, h: int, pages) -> tuple:
+    """Valid keys and values (float64) of the listed physical pages of row (b, h), in list order."""
+    w = inp.workload
+    NP = physical_page_tokens(inp)
+    L = int(inp.seq_lens[b])
+    ks, vs = [], []
+    for j in pages:
+        phys = int(inp.block_table[b, int(j)])
+        valid = max(0, min(NP, L - NP * int(j)))
+        ksc = None if inp.k_scale is None else inp.k_scale[phys, h]
+        vsc = None if inp.v_scale is None else inp.v_scale[phys, h]
+        ks.append(stored_values(inp.k_pool[phys, h], ksc, w.kv_dtype)[:valid])
+        vs.append(stored_values(inp.v_pool[phys, h], vsc, w.kv_dtype)[:valid])
+    d = inp.k_pool.shape[3]
+    if not ks:
+        return np.zeros((0, d)), np.zeros((0, d))
+    return np.concatenate(ks), np.concatenate(vs)
+
+
+def hier_sparse_paged_decode(inp, lists: dict, sm_scale: float):
+    """O [B, Hq, d] and lse [B, Hq] of attention over every valid token of the listed physical pages."""
+    w = inp.workload
+    B, Hq, d = inp.q.shape
+    G = w.group
+    O = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), -np.inf)
+    for (b, h), pages in lists.items():
+        K, V = hier_gather_tokens(inp, b, h, pages)
+        for g in range(G):
+            O[b, h * G + g], lse[b, h * G + g] = attention(inp.q[b, h * G + g].astype(np.float64), K, V, sm_scale)
+    return O, lse
+
+
+# --------------------------------------------------------------------------------------
 # Whole step
 # --------------------------------------------------------------------------------------
 
 def decode_step(inp, meta: np.ndarray | None = None):
     """Metadata (if not given) -> scores -> lists -> attention, as the method orders them."""
+    if physical_page_tokens(inp) != PAGE:  # hierarchical paging
+        if meta is None:
+            meta = hier_meta_build(inp)
+        sel = hier_page_select(inp, meta)
+        O, lse = hier_sparse_paged_decode(inp, sel["lists"], inp.workload.sm_scale)
+        return {"meta": meta, **sel, "O": O, "out_lse": lse}
     if meta is None:
         meta = page_meta_build(inp)
     sel = page_select(inp, meta)

@@ -18,6 +18,12 @@ request a consecutive slice.
 "Planted" pages give the selectors something real to find: for KV head h of
 request b, every key of a planted page is ``z + delta * u`` where ``z`` is the
 N(0, 1) draw and ``u`` is the unit vector along the sum of the group's queries.
+
+Physical pages hold ``page_size`` tokens: 16 (one logical page each), or 64 for
+the hierarchical layout of the LServe page ("Hierarchical Paging", N_P = 64
+physical tokens over N_L = 16-token logical pages).  Planted pages are always
+16-token logical pages, so a physical page of 64 tokens may hold one planted
+logical page among three ordinary ones.
 """
 from __future__ import annotations
 
@@ -27,7 +33,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-PAGE_SIZE = 16
+PAGE_SIZE = 16      # logical page (N_L), and the default physical page
+LOGICAL_PAGE = 16
 BASE_SEED = 20261202
 
 KV_DTYPES = ("f32", "f16", "fp8")
@@ -69,6 +76,7 @@ class Workload:
     max_pages_per_seq: int | None = None
     max_list: int | None = None
     shuffle_lengths: bool = False
+    page_size: int = PAGE_SIZE  # physical page tokens (N_P): 16, or 64 over 16-token logical pages
 
     @property
     def batch(self) -> int:
@@ -80,7 +88,14 @@ class Workload:
 
     @property
     def n_pages(self) -> np.ndarray:
-        return np.array([(int(L) + PAGE_SIZE - 1) // PAGE_SIZE for L in self.seq_lens], dtype=np.int64)
+        """Physical pages of each request (ceil(len / page_size))."""
+        P = self.page_size
+        return np.array([(int(L) + P - 1) // P for L in self.seq_lens], dtype=np.int64)
+
+    @property
+    def n_logical(self) -> np.ndarray:
+        """16-token logical pages of each request."""
+        return np.array([(int(L) + LOGICAL_PAGE - 1) // LOGICAL_PAGE for L in self.seq_lens], dtype=np.int64)
 
     @property
     def pages_per_seq(self) -> int:
@@ -192,12 +207,22 @@ def named(name: str, seed_offset: int = 0) -> Workload:
                         head_dim=128, kv_dtype="f16", q_dtype="f16", mode="coverage", estimator="mvar",
                         gamma=0.99, n_sink=1, n_local=1, planted=("loguniform", 20, 2000),
                         delta=("nats", 12.0), seed=BASE_SEED + 6 + seed_offset)
+    if name == "llama3_8b_b1_128k_f16_hier64":
+        # the 128k layer with 64-token physical pages scored through 16-token logical pages (LServe,
+        # "Hierarchical Paging", N_P = 64, N_L = 16): token budget 4096 = 64 physical pages
+        # ("Token budget and physical page selection", K = ceil(B / N_P)); one sink and one local
+        # physical page per dynamic head; streaming heads keep the same 64 + 256 tokens (1 + 4 pages)
+        return Workload(name=name, seq_lens=(131072,), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        kv_dtype="f16", q_dtype="f16", mode="topk", page_size=64,
+                        budget_pages=-(-4096 // 64), n_sink=1, n_local=1, n_sink_stream=1, n_local_stream=4,
+                        streaming_heads=(0, 1, 2, 3), planted=("fixed", 64), delta=2.0,
+                        seed=BASE_SEED + 7 + seed_offset)
     raise KeyError(name)
 
 
 NAMED = ("tiny_b1_hq8_d64_4k_f32", "llama3_8b_b1_128k_f16", "mixed_b8_bimodal_f16",
          "mixed_b8_powerlaw_f16", "coverage_b4_128k_f16", "fp8_b1_512k", "llama3_8b_b1_128k_f16_dense",
-         "coverage_mvar_b4_128k_f16")
+         "coverage_mvar_b4_128k_f16", "llama3_8b_b1_128k_f16_hier64")
 
 
 # --------------------------------------------------------------------------------------
@@ -235,7 +260,9 @@ def generate(w: Workload, seed: int | None = None) -> Inputs:
     B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
     assert Hq % Hkv == 0 and w.kv_dtype in KV_DTYPES and w.q_dtype in Q_DTYPES
     G = Hq // Hkv
-    P = PAGE_SIZE
+    P = w.page_size
+    assert P % LOGICAL_PAGE == 0
+    g = P // LOGICAL_PAGE  # logical pages per physical page
     n_pages = w.n_pages
     maxp = w.pages_per_seq
 
@@ -268,7 +295,8 @@ def generate(w: Workload, seed: int | None = None) -> Inputs:
     for b in range(B):
         nb = int(n_pages[b])
         forced = set(range(min(w.n_sink, nb))) | set(range(max(0, nb - w.n_local), nb))
-        candidates = np.array([p for p in range(nb) if p not in forced], dtype=np.int64)
+        # logical pages outside the forced physical pages (g = 1: the non-forced pages)
+        candidates = np.array([p for p in range(int(w.n_logical[b])) if p // g not in forced], dtype=np.int64)
         for h in range(Hkv):
             kind, *args = w.planted
             if kind == "fixed":
@@ -293,8 +321,14 @@ def generate(w: Workload, seed: int | None = None) -> Inputs:
                 delta = nats / (w.sm_scale * proj) if proj > 0 else 0.0
             else:
                 delta = float(w.delta)
-            phys = torch.from_numpy(block_table[b, pages].astype(np.int64))
-            kz[phys, h] += torch.from_numpy((delta * u).astype(np.float32))[None, None, :]
+            shift = torch.from_numpy((delta * u).astype(np.float32))
+            if g == 1:
+                phys = torch.from_numpy(block_table[b, pages].astype(np.int64))
+                kz[phys, h] += shift[None, None, :]
+            else:  # the 16 token slots of each planted logical page inside its physical page
+                phys = np.repeat(block_table[b, pages // g].astype(np.int64), LOGICAL_PAGE)
+                slot = ((pages % g) * LOGICAL_PAGE)[:, None] + np.arange(LOGICAL_PAGE)[None, :]
+                kz[torch.from_numpy(phys), h, torch.from_numpy(slot.reshape(-1))] += shift[None, :]
             planted[(b, h)] = pages
             deltas[(b, h)] = delta
 

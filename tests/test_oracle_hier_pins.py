@@ -1,0 +1,178 @@
+"""Pins of the oracle's hierarchical paging (CPU only).
+
+LServe, "Hierarchical Paging": physical pages of N_P = g * N_L tokens (here 64 = 4 * 16)
+keep key min / max per 16-token logical page; a physical page's importance is the largest
+importance of its logical pages; the top-K runs over physical pages ("Token budget and
+physical page selection") and attention loads whole physical pages.  Each test ties the
+oracle's hierarchical functions to something other than themselves: dense attention read
+token by token, brute-force dot products, the box of a whole physical page, the flat
+(16-token) oracle on the same tokens re-laid out, and a closed form.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import spd_oracle as O
+from sparse_paged_decode_quest_amd import workloads as W
+
+NP = 64
+
+
+def _hier(**kw):
+    base = dict(seq_lens=(333, 48, 1000, 64), Hq=8, Hkv=2, page_size=NP, budget=5, n_sink=1, n_local=1,
+                planted=("fixed", 3), seed=71)
+    base.update(kw)
+    return W.small("hier", **base)
+
+
+def _token_values(inp, pool, scale, phys, h, slot):
+    w = inp.workload
+    if w.kv_dtype == "fp8":  # torch's E4M3FN decode times the token scale, independent of the oracle
+        code = torch.tensor([int(pool[phys, h, slot, c]) for c in range(pool.shape[3])], dtype=torch.uint8)
+        return code.view(torch.float8_e4m3fn).to(torch.float64).numpy() * float(scale[phys, h, slot])
+    return pool[phys, h, slot].astype(np.float64)
+
+
+def _dense_unpaged(inp, b, h, tokens=None):
+    """Keys / values of request b, KV head h, read token by token through the block table."""
+    L = int(inp.seq_lens[b])
+    ks, vs = [], []
+    for t in (range(L) if tokens is None else tokens):
+        phys, slot = int(inp.block_table[b, t // NP]), t % NP
+        ks.append(_token_values(inp, inp.k_pool, inp.k_scale, phys, h, slot))
+        vs.append(_token_values(inp, inp.v_pool, inp.v_scale, phys, h, slot))
+    return np.array(ks), np.array(vs)
+
+
+def _sdpa(q, K, V, scale):
+    qt = torch.from_numpy(q)[None, None, None, :]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, torch.from_numpy(K)[None, None],
+                                                         torch.from_numpy(V)[None, None], scale=scale)
+    return o[0, 0, 0].numpy(), float(torch.logsumexp(torch.from_numpy(K @ q) * scale, dim=0))
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16", "fp8"])
+def test_every_physical_page_listed_equals_dense_attention(kv):
+    w = _hier(kv=kv, q="f32" if kv == "f32" else "f16", d=64, budget=1000)
+    inp = W.generate(w)
+    res = O.decode_step(inp)
+    G = w.group
+    for b, L in enumerate(w.seq_lens):
+        for h in range(w.num_kv_heads):
+            assert res["lists"][(b, h)] == list(range(-(-L // NP)))
+            K, V = _dense_unpaged(inp, b, h)
+            for g in range(G):
+                o_ref, lse_ref = _sdpa(inp.q[b, h * G + g].astype(np.float64), K, V, w.sm_scale)
+                assert np.allclose(res["O"][b, h * G + g], o_ref, rtol=0, atol=1e-12)
+                assert abs(res["out_lse"][b, h * G + g] - lse_ref) < 1e-12
+
+
+def test_streaming_row_attends_to_its_sink_and_local_physical_pages():
+    w = _hier(seq_lens=(1000,), streaming=(0,), n_sink_stream=1, n_local_stream=2, Hq=4, Hkv=2)
+    inp = W.generate(w)
+    res = O.decode_step(inp)
+    assert res["lists"][(0, 0)] == [0, 14, 15]  # 1000 tokens: physical pages 0..15, the last holds 40
+    keep = list(range(64)) + list(range(14 * 64, 1000))
+    K, V = _dense_unpaged(inp, 0, 0, keep)
+    for g in range(2):
+        o_ref, lse_ref = _sdpa(inp.q[0, g].astype(np.float64), K, V, w.sm_scale)
+        assert np.allclose(res["O"][0, g], o_ref, rtol=0, atol=1e-12)
+        assert abs(res["out_lse"][0, g] - lse_ref) < 1e-12
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8"])
+def test_physical_score_bounds_every_key_of_the_page(kv):
+    w = _hier(kv=kv)
+    inp = W.generate(w)
+    meta = O.hier_meta_build(inp)
+    G = w.group
+    for b, L in enumerate(w.seq_lens):
+        for h in range(w.num_kv_heads):
+            sc, _ = O.hier_row_scores(inp, meta, b, h)
+            q = inp.q[b, h * G:(h + 1) * G].astype(np.float64)
+            for j in range(len(sc)):
+                K, _ = _dense_unpaged(inp, b, h, range(j * NP, min(L, (j + 1) * NP)))
+                best = (q @ K.T).max()
+                assert sc[j] >= best - 1e-9 * (1 + abs(best))
+
+
+def test_max_over_logical_pages_is_tighter_than_one_box_per_physical_page():
+    w = _hier(seq_lens=(2048,), planted=("fixed", 0))
+    inp = W.generate(w)
+    meta = O.hier_meta_build(inp)
+    G = w.group
+    tighter = 0
+    for h in range(w.num_kv_heads):
+        sc, _ = O.hier_row_scores(inp, meta, 0, h)
+        q = inp.q[0, h * G:(h + 1) * G].astype(np.float64)
+        for j in range(len(sc)):
+            K, _ = _dense_unpaged(inp, 0, h, range(j * NP, (j + 1) * NP))
+            lo, hi = K.min(axis=0), K.max(axis=0)
+            whole = np.maximum(q * hi, q * lo).sum(axis=1).max()  # the bound of one 64-token box
+            assert sc[j] <= whole + 1e-9 * abs(whole)
+            tighter += sc[j] < whole - 1e-6
+    assert tighter >= len(sc)  # most pages: four small boxes bound q.k more tightly than one big box
+
+
+def _flat_relayout(inp):
+    """The same tokens in a pool of 16-token pages: logical page lp of request b goes to flat page
+    block_table[b, lp // 4] * 4 + lp % 4 (a reshape of the pool, no arithmetic)."""
+    g = NP // 16
+    Np, Hkv, _, d = inp.k_pool.shape
+
+    def pool(x):
+        return None if x is None else np.ascontiguousarray(
+            x.reshape(Np, Hkv, g, 16, *x.shape[3:]).swapaxes(1, 2).reshape(Np * g, Hkv, 16, *x.shape[3:]))
+    w = inp.workload
+    nl = w.n_logical
+    bt = np.zeros((len(nl), max(1, int(nl.max()))), dtype=np.int32)
+    for b, n in enumerate(nl):
+        lp = np.arange(n)
+        bt[b, :n] = inp.block_table[b, lp // g] * g + lp % g
+    return W.Inputs(workload=w.replace(page_size=16, max_pages_per_seq=None), q=inp.q, k_pool=pool(inp.k_pool),
+                    v_pool=pool(inp.v_pool), k_scale=pool(inp.k_scale), v_scale=pool(inp.v_scale),
+                    block_table=bt, seq_lens=inp.seq_lens, head_kind=inp.head_kind)
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16", "fp8"])
+def test_logical_bounds_equal_the_flat_oracle_on_the_same_tokens(kv):
+    w = _hier(kv=kv, q="f32" if kv == "f32" else "f16", d=64)
+    inp = W.generate(w)
+    flat = _flat_relayout(inp)
+    meta_h = O.hier_meta_build(inp)
+    meta_f = O.page_meta_build(flat)
+    for b, L in enumerate(w.seq_lens):
+        for h in range(w.num_kv_heads):
+            sc, S = O.hier_row_scores(inp, meta_h, b, h)
+            S_flat = O.row_bounds(flat, meta_f, b, h)
+            assert np.array_equal(S, S_flat)
+            per_logical = O.topk_scores(S_flat)
+            assert np.array_equal(sc, [per_logical[4 * j:4 * j + 4].max() for j in range(-(-L // NP))])
+
+
+def test_page_of_identical_keys_scores_the_exact_dot_product():
+    w = _hier(kv="f32", q="f32", seq_lens=(256,), planted=("fixed", 0))
+    inp = W.generate(w)
+    k = np.linspace(-1.5, 2.0, w.head_dim).astype(np.float32)
+    phys = int(inp.block_table[0, 2])
+    inp.k_pool[phys, 1] = k[None, :]
+    meta = O.hier_meta_build(inp)
+    sc, _ = O.hier_row_scores(inp, meta, 0, 1)
+    q = inp.q[0, 4:8].astype(np.float64)
+    assert abs(sc[2] - (q @ k.astype(np.float64)).max()) < 1e-12
+
+
+def test_topk_keeps_the_physical_pages_of_strongly_planted_logical_pages():
+    w = _hier(seq_lens=(4096,), budget=12, planted=("fixed", 6), delta=8.0, hole=0.0)
+    inp = W.generate(w)
+    res = O.decode_step(inp)
+    for h in range(w.num_kv_heads):
+        want = {int(p) // 4 for p in inp.planted[(0, h)]}
+        assert want <= set(res["lists"][(0, h)])
+        assert len(res["lists"][(0, h)]) == 12
+
+
+def test_named_workload_budget_is_the_token_budget_over_the_physical_page():
+    w = W.named("llama3_8b_b1_128k_f16_hier64")
+    assert w.page_size == 64 and w.budget_pages == 4096 // 64  # K = ceil(B / N_P)
+    assert int(w.n_pages[0]) == 2048 and int(w.n_logical[0]) == 8192
