@@ -26,6 +26,13 @@
  *   5. lse_merge            exact log-sum-exp merge of the split states (PersistentKV,
  *                           section 3.3; Moira, section 3.3 "Merge")
  *
+ * Hierarchical paging (LServe summary, "Hierarchical Paging"; spd_desc.page_size = 64): physical
+ * pages of N_P = 64 tokens hold 4 logical pages of N_L = 16 tokens.  Key statistics are kept per
+ * logical page; a physical page's score is the largest score of its logical pages ("Physical page
+ * importance aggregation"); the budget, the sink and local windows and the lists count physical
+ * pages ("Token budget and physical page selection": K = ceil(token budget / N_P)), and
+ * attention reads every valid token of each listed physical page.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Pointers marked (device) are device memory owned by the caller; pointers marked (host)
@@ -40,12 +47,15 @@
  *    mutable state, so calls from several host threads are safe.
  *  - Layouts are dense row-major C arrays:
  *      q            [B, Hq, d]                 f32 or f16 (spd_desc.q_dtype)
- *      k_pool,v_pool [num_pool_pages, Hkv, 16, d]  f32, f16 or fp8 E4M3FN bytes
- *      k_scale,v_scale [num_pool_pages, Hkv, 16]  fp16 bits (fp8 pools only; value =
+ *    P = spd_desc.page_size (tokens of a physical page), g = P / 16 (logical pages per
+ *    physical page: 1, or 4 with hierarchical paging)
+ *      k_pool,v_pool [num_pool_pages, Hkv, P, d]  f32, f16 or fp8 E4M3FN bytes
+ *      k_scale,v_scale [num_pool_pages, Hkv, P]  fp16 bits (fp8 pools only; value =
  *                                              E4M3FN(code) * scale)
- *      page_meta    [num_pool_pages, Hkv, 2, d] index 0 = channel min, 1 = channel max;
- *                                              f32 for f32 pools, f16 otherwise (for fp8
- *                                              pools rounded outward: min down, max up)
+ *      page_meta    [num_pool_pages, Hkv, g, 2, d] per logical page (sub-page i of the
+ *                                              physical page): index 0 = channel min, 1 =
+ *                                              channel max; f32 for f32 pools, f16 otherwise
+ *                                              (for fp8 pools rounded outward: min down, max up)
  *      page_stats   [num_pool_pages, Hkv, 2, d] bf16 bits: index 0 = channel mean, 1 =
  *                                              channel variance (mean squared deviation) of
  *                                              the page's valid keys, each rounded to nearest
@@ -53,20 +63,25 @@
  *                                              mvar estimate"; bf16 as in "Memory for page
  *                                              summaries").  Scorers with the MVAR estimator
  *                                              take it in the page_meta argument.
- *      block_table  [B, max_pages_per_seq]     int32 physical page of each logical page
+ *      block_table  [B, max_pages_per_seq]     int32 physical page holding tokens
+ *                                              [P j, P j + P) of the request, j = 0, 1, ...
  *      seq_lens     [B]                        int32 tokens of each request
  *      head_kind    [Hkv]                      uint8 (host) SPD_HEAD_DYNAMIC or _STREAMING
- *      scores       [B, Hkv, max_pages_per_seq] f32
- *      page_list    [B, Hkv, max_list]         int32 logical pages, ascending
+ *      scores       [B, Hkv, max_pages_per_seq] f32, per block-table slot j
+ *      page_list    [B, Hkv, max_list]         int32 block-table slots j, ascending
  *      list_len     [B, Hkv]                   int32
  *      out          [B, Hq, d]                 f32; out_lse [B, Hq] f32 (natural log of the
  *                                              softmax denominator of the scaled logits)
  *      part_o       [B, Hkv, J, G, d] f32 and part_lse [B, Hkv, J, G] f32, J from
  *                                              spd_plan_grid
- *  - Request b has n_b = ceil(seq_lens[b] / 16) logical pages; logical page p holds
- *    min(16, seq_lens[b] - 16 p) valid tokens (PersistentKV, section 3.3: bounds follow the
- *    row's own length).  Only valid tokens enter the statistics and the attention; the
- *    remaining slots of a partial page may hold anything, NaN included.
+ *  - Request b has n_b = ceil(seq_lens[b] / P) pages (block-table slots) and ceil(seq_lens[b] /
+ *    16) logical pages; logical page p holds min(16, seq_lens[b] - 16 p) valid tokens, in
+ *    physical page block_table[b, p / g] at token slots 16 (p mod g) .. 16 (p mod g) + 15
+ *    (PersistentKV, section 3.3: bounds follow the row's own length).  With P = 16 a page and a
+ *    logical page are the same thing, and "page" below means either; otherwise rows, scores,
+ *    budgets, forced windows and lists count pages (slots of P tokens) and statistics count
+ *    logical pages.  Only valid tokens enter the statistics and the attention; the remaining
+ *    slots of a partial page may hold anything, NaN included.
  *  - Robustness: n_b is clamped to max_pages_per_seq, negative lengths count as 0, list
  *    entries outside [0, n_b) and block-table entries outside [0, num_pool_pages) are
  *    treated as empty pages (never dereferenced).
@@ -81,8 +96,9 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 6
-#define SPD_PAGE_SIZE 16
+#define SPD_ABI_VERSION 7
+#define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
+#define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
 
 typedef enum spd_status {
@@ -137,15 +153,17 @@ typedef enum spd_op {
   SPD_OP_PAGE_SCORE_SELECT = 2
 } spd_op;
 
-/* Shapes of one step.  Supported: page_size 16; head_dim 64 or 128; Hq / Hkv = 4;
- * (q_dtype, kv_dtype) in {(f32, f32), (f16, f16), (f16, fp8)}.  Others return
- * SPD_ERR_UNSUPPORTED so a caller can route them elsewhere. */
+/* Shapes of one step.  Supported: page_size 16 or 64; head_dim 64 or 128; Hq / Hkv = 4;
+ * (q_dtype, kv_dtype) in {(f32, f32), (f16, f16), (f16, fp8)}.  page_size 64 (hierarchical
+ * paging) supports the TOPK rule with the BOUND estimator, tail modes NONE and SKIP, and the
+ * unfused entry points; f32 pools need head_dim 64 there.  Others return SPD_ERR_UNSUPPORTED so
+ * a caller can route them elsewhere. */
 typedef struct spd_desc {
   int32_t batch;              /* B >= 0 */
   int32_t num_q_heads;        /* Hq */
   int32_t num_kv_heads;       /* Hkv, 1..SPD_MAX_KV_HEADS, divides Hq */
   int32_t head_dim;           /* d */
-  int32_t page_size;          /* must be 16 */
+  int32_t page_size;          /* 16, or 64 (hierarchical paging) */
   int32_t max_pages_per_seq;  /* block-table row stride, >= 1 */
   int32_t num_pool_pages;     /* pool pages, >= 1 */
   int32_t max_list;           /* page_list row stride, >= 1 */
@@ -195,7 +213,8 @@ typedef struct spd_plan_params {
 /* ------------------------------------------------------------------ entry points */
 
 /* Channel-wise min / max of the valid keys of logical pages p of each request, for every KV
- * head, written to page_meta at the page's physical slot.  first_page (device, [B], may be
+ * head, written to page_meta at the logical page's place in its physical page.  first_page and
+ * span_pages count logical pages.  first_page (device, [B], may be
  * NULL): when set, pages first_page[b] .. min(n_b, first_page[b] + span_pages) - 1 are built
  * (span_pages >= 1).  When NULL, span_pages = 0 builds every page 0..n_b-1 (the bulk build at
  * prefill) and span_pages >= 1 builds the last span_pages pages of each request, read from
@@ -218,7 +237,9 @@ int spd_page_stats_build(const spd_desc* desc, const void* k_pool, const uint16_
 
 /* Page scores of every dynamic row (streaming rows are skipped, their scores untouched).
  * TOPK: scores[b,h,p] = max over the G query heads of the row of S_{g,p} (LServe page
- * importance, computed from page_meta).  COVERAGE: l_{g,p} = sm_scale * S_{g,p} +
+ * importance, computed from page_meta); with page_size 64, the largest of these over the logical
+ * pages of page p that hold valid tokens (LServe, "Physical page importance aggregation"), and
+ * SPD_TAIL_SKIP skips the row's last page (all its logical pages).  COVERAGE: l_{g,p} = sm_scale * S_{g,p} +
  * ln(valid tokens of p); head_lse[b, h*G+g] = logsumexp_p l_{g,p}; scores[b,h,p] =
  * (1/G) sum_g exp(l_{g,p} - head_lse) (Moira's group-mean share, section 3.2, Eq. 3).
  * tail_mode (spd_tail_mode) says how each dynamic row's last logical page is treated;
@@ -237,11 +258,11 @@ int spd_page_score(const spd_desc* desc, const spd_select_params* sel, const voi
                    size_t workspace_bytes, void* stream);
 
 /* Page list of every row from its scores (selection rule: spd_select_params).  Lists are
- * ascending logical pages.  page_phys (device, [B, Hkv, max_list], may be NULL) receives the
+ * ascending pages (block-table slots).  page_phys (device, [B, Hkv, max_list], may be NULL) receives the
  * physical page of each listed page, read from block_table (device, required when page_phys
  * is set), so spd_sparse_paged_decode need not read the block table.  When page_meta (device,
  * may be NULL) is set, workgroups beside the selection also rebuild the key min / max of each
- * request's last logical page, every KV head, from k_pool (and k_scale for fp8 pools) into
+ * request's last logical page (the one the newest token is in), every KV head, from k_pool (and k_scale for fp8 pools) into
  * page_meta -- what spd_page_meta_build does with first_page = that page and span 1 (LServe,
  * "Key statistics storage and updating"); block_table is then required, and the scores must
  * not depend on those statistics (the scorer ran with SPD_TAIL_SKIP).  sel_scores (device,
@@ -293,7 +314,8 @@ int spd_page_list_refresh(const spd_desc* desc, const spd_select_params* sel, co
                           int32_t* page_phys, int32_t* list_len, void* stream);
 
 /* Grouped-query decode attention of every row over its listed pages.  Block (b, h, j)
- * processes chunk j of row (b, h) (spd_plan_params); rows with one chunk write out /
+ * processes chunk j of row (b, h) (spd_plan_params; with page_size 64 the plan counts 16-token
+ * units, four per listed page, so list_len n plans as 4 n); rows with one chunk write out /
  * out_lse directly, rows with more write their chunk states to part_o / part_lse for
  * spd_lse_merge.  A row with no listed pages writes out = 0 and out_lse = -inf.
  * page_phys (device, may be NULL) holds the physical page of each list entry (as written by

@@ -65,18 +65,20 @@ template <int D> struct MetaTraits<D, SPD_DTYPE_FP8_E4M3FN> {
   }
 };
 
-// Statistics of logical page p of request b (len tokens), KV head h, by the calling wave.
+// Statistics of logical page p of request b (len tokens), KV head h, by the calling wave, stored
+// with the physical page that holds it (sub-page p mod 2^lgs of block-table slot p >> lgs).
 // Pages whose block-table entry is outside the pool are left alone.
 template <int D, int KVD>
 __device__ __forceinline__ void build_page_meta(const MetaArgs& a, int b, int p, int h, int len) {
   using T = MetaTraits<D, KVD>;
   constexpr int CPL = T::CPL;
   const int lane = threadIdx.x % kWave;
-  const int phys = a.block_table[(size_t)b * a.max_pages + p];
+  const int phys = a.block_table[(size_t)b * a.max_pages + (p >> a.lgs)];
   if (phys < 0 || phys >= a.num_pool_pages) return;
   const int valid = valid_in_page(len, p);
   const int c0 = lane * CPL;
-  const size_t head_base = ((size_t)phys * a.num_kv_heads + h) * kPage;
+  const size_t unit = head_unit(phys, a.num_kv_heads, h, a.lgs, p & ((1 << a.lgs) - 1));
+  const size_t head_base = unit * kPage;
   // every token of the page is loaded at once (slots past `valid` are read but never used)
   float v[kPage][CPL];
 #pragma unroll
@@ -97,7 +99,7 @@ __device__ __forceinline__ void build_page_meta(const MetaArgs& a, int b, int p,
       hi[c] = ok ? fmaxf(hi[c], v[t][c]) : hi[c];
     }
   }
-  T::store(a.meta, (((size_t)phys * a.num_kv_heads + h) * 2) * D + c0, lo, hi, D);
+  T::store(a.meta, unit * 2 * D + c0, lo, hi, D);
 }
 
 // Moira page summary ("Page summaries and the mvar estimate"): channel-wise mean and variance of
@@ -123,12 +125,13 @@ __device__ __forceinline__ void build_page_stats(const MetaArgs& a, int b, int p
   using T = MetaTraits<D, KVD>;
   constexpr int CPL = T::CPL;
   const int lane = threadIdx.x % kWave;
-  const int phys = a.block_table[(size_t)b * a.max_pages + p];
+  const int phys = a.block_table[(size_t)b * a.max_pages + (p >> a.lgs)];
   if (phys < 0 || phys >= a.num_pool_pages) return;
   const int valid = valid_in_page(len, p);
   if (valid <= 0) return;
   const int c0 = lane * CPL;
-  const size_t head_base = ((size_t)phys * a.num_kv_heads + h) * kPage;
+  const size_t unit = head_unit(phys, a.num_kv_heads, h, a.lgs, p & ((1 << a.lgs) - 1));
+  const size_t head_base = unit * kPage;
   float v[kPage][CPL];
 #pragma unroll
   for (int t = 0; t < kPage; ++t) {
@@ -136,7 +139,7 @@ __device__ __forceinline__ void build_page_stats(const MetaArgs& a, int b, int p
     if (KVD == SPD_DTYPE_FP8_E4M3FN) scale = half_bits_to_float(a.k_scale[head_base + t]);
     T::load(a.k_pool, (head_base + t) * D + c0, v[t], scale);
   }
-  uint16_t* m = reinterpret_cast<uint16_t*>(a.meta) + (((size_t)phys * a.num_kv_heads + h) * 2) * D + c0;
+  uint16_t* m = reinterpret_cast<uint16_t*>(a.meta) + unit * 2 * D + c0;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     double sum = 0.0;

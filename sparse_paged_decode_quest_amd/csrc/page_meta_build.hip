@@ -1,6 +1,7 @@
 // Bulk statistics (every page of every request, at prefill), the pages [first_page, first_page
 // + span) of each request, or its last `span` pages (the page the newest token is in, during
-// decode): key min / max (page meta) or key mean / variance (page summaries).
+// decode): key min / max (page meta) or key mean / variance (page summaries).  Pages here are
+// 16-token logical pages, also when physical pages hold several (hierarchical paging).
 #include "meta_build.h"
 
 namespace spd {
@@ -14,13 +15,13 @@ __global__ __launch_bounds__(256) void page_meta_build_kernel(MetaArgs a) {
   const int p_off = item / a.num_kv_heads;
   const int h = item % a.num_kv_heads;
   const int len = a.seq_lens[b];
-  const int n = row_pages(len, a.max_pages);
+  const int n = row_logical_pages(len, a.max_pages, a.lgs);  // logical pages (hierarchical paging)
   int start = 0, end = n;
   if (a.first_page) {
     start = a.first_page[b];
     if (start < 0) start = 0;
     end = start + a.span < n ? start + a.span : n;
-  } else if (a.span < a.max_pages) {  // the last `span` pages of the request
+  } else if (a.span < (a.max_pages << a.lgs)) {  // the last `span` pages of the request
     start = n - a.span > 0 ? n - a.span : 0;
   }
   const int p = start + p_off;

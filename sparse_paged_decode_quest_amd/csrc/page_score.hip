@@ -34,7 +34,10 @@ __device__ __forceinline__ RowRole row_role(const ScoreArgs& a) {
   return r;
 }
 
-template <int D, int KVD, bool COV, int ITERS>
+// HIER: top-K over physical pages of 2^lgs logical pages (hierarchical paging): the workgroups scan
+// logical pages and write each physical page's largest key; SPD_TAIL_SKIP skips the row's last
+// physical page (the local window keeps it).
+template <int D, int KVD, bool COV, int ITERS, bool HIER>
 __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreArgs a) {
   const RowRole r = row_role(a);
   const int32_t* bt_row = a.block_table + (size_t)r.b * a.max_pages;
@@ -46,14 +49,23 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreAr
   }
   const int p_begin = r.blk * a.pages_per_block;
   int raw[ITERS];
-  load_block_table<D, KVD, kScoreWaves, ITERS>(bt_row, a.max_pages, p_begin, raw);
-  const int n = row_pages(len, a.max_pages);
-  const int n_scan = scan_pages(a, n);
+  load_block_table<D, KVD, kScoreWaves, ITERS>(bt_row, a.max_pages, p_begin, raw, HIER ? a.lgs : 0);
   float* sc_row = a.scores + ((size_t)r.b * a.num_kv_heads + r.h) * a.max_pages;
-  if (!COV && a.tail_mode == SPD_TAIL_SKIP && r.blk == 0 && n > 0 && threadIdx.x == 0) sc_row[n - 1] = -INFINITY;
-  if (p_begin >= n_scan) return;  // uniform over the block
-  if constexpr (COV) score_block_ell<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, len, r.b, r.h, p_begin);
-  else score_block_topk<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, r.b, r.h, p_begin, sc_row);
+  if constexpr (HIER) {
+    const int n_phys = row_phys_pages(len, a.max_pages, a.lgs);
+    const int phys_scan = a.tail_mode == SPD_TAIL_SKIP && n_phys > 0 ? n_phys - 1 : n_phys;
+    const int n_scan = min(row_logical_pages(len, a.max_pages, a.lgs), phys_scan << a.lgs);
+    if (a.tail_mode == SPD_TAIL_SKIP && r.blk == 0 && n_phys > 0 && threadIdx.x == 0) sc_row[n_phys - 1] = -INFINITY;
+    if (p_begin >= n_scan) return;  // uniform over the block
+    score_block_topk_hier<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, phys_scan, r.b, r.h, p_begin, sc_row);
+  } else {
+    const int n = row_pages(len, a.max_pages);
+    const int n_scan = scan_pages(a, n);
+    if (!COV && a.tail_mode == SPD_TAIL_SKIP && r.blk == 0 && n > 0 && threadIdx.x == 0) sc_row[n - 1] = -INFINITY;
+    if (p_begin >= n_scan) return;  // uniform over the block
+    if constexpr (COV) score_block_ell<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, len, r.b, r.h, p_begin);
+    else score_block_topk<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, r.b, r.h, p_begin, sc_row);
+  }
 }
 
 // Coverage, second and third passes, over blocks of kSharePages pages of a row (one page per
@@ -180,15 +192,20 @@ void launch_coverage_shares(const ScoreArgs& a, hipStream_t stream) {
 int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool coverage, hipStream_t stream) {
   const unsigned rows = (unsigned)(a.batch * a.dyn.count);
   const dim3 grid(rows * (unsigned)(a.blocks_per_row + tail_blocks(a))), block(kScoreWaves * kWave);
-  const bool long_scan = score_iters((long long)rows * a.max_pages) == kScoreItersLong;
-#define SPD_SCORE_LAUNCH(D, KVD, COV)                                                                           \
-  if (long_scan) hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, kScoreItersLong>), grid, block, 0, stream, a); \
-  else hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, kScoreItersShort>), grid, block, 0, stream, a);
+  const bool long_scan = score_iters((long long)rows * ((long long)a.max_pages << a.lgs)) == kScoreItersLong;
+#define SPD_SCORE_LAUNCH(D, KVD, COV)                                                                                       \
+  if (long_scan) hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, kScoreItersLong, false>), grid, block, 0, stream, a);   \
+  else hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, kScoreItersShort, false>), grid, block, 0, stream, a);
+#define SPD_SCORE_LAUNCH_HIER(D, KVD)                                                                                       \
+  if (long_scan) hipLaunchKernelGGL((page_score_kernel<D, KVD, false, kScoreItersLong, true>), grid, block, 0, stream, a);  \
+  else hipLaunchKernelGGL((page_score_kernel<D, KVD, false, kScoreItersShort, true>), grid, block, 0, stream, a);
 #define SPD_SCORE_CASE(D, KVD)                                                                  \
   if (head_dim == D && kv_dtype == KVD) {                                                       \
     if (coverage) {                                                                             \
       SPD_SCORE_LAUNCH(D, KVD, true)                                                            \
       launch_coverage_shares(a, stream);                                                        \
+    } else if (a.lgs > 0) {                                                                     \
+      SPD_SCORE_LAUNCH_HIER(D, KVD)                                                             \
     } else {                                                                                    \
       SPD_SCORE_LAUNCH(D, KVD, false)                                                           \
     }                                                                                           \
@@ -201,6 +218,7 @@ int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool cover
   SPD_SCORE_CASE(128, SPD_DTYPE_F32)
 #undef SPD_SCORE_CASE
 #undef SPD_SCORE_LAUNCH
+#undef SPD_SCORE_LAUNCH_HIER
   return SPD_ERR_UNSUPPORTED;
 }
 

@@ -1,5 +1,7 @@
 // Page lists from page scores: one workgroup per (request, KV head) row.  The selection rules
-// and their sources are described in select_row.h.  Optionally, workgroups after the rows
+// and their sources are described in select_row.h.  With hierarchical paging the rows, scores,
+// forced pages, budget and lists are physical pages, and the rebuilt statistics those of the
+// newest token's 16-token logical page.  Optionally, workgroups after the rows
 // rebuild the key statistics of each request's last page, one wave per KV head (LServe, "Key
 // statistics storage and updating"), beside the selection: where the scorer skipped that page
 // (the local window keeps it), the rebuild leaves the critical path of the step.
@@ -29,7 +31,7 @@ __device__ __forceinline__ void rebuild_tail_pages(const SelectArgs& a, int k) {
   if (item >= a.batch * a.num_kv_heads) return;
   const int b = item / a.num_kv_heads, h = item % a.num_kv_heads;
   const int len = a.seq_lens[b];
-  const int n = row_pages(len, a.max_pages);
+  const int n = row_logical_pages(len, a.max_pages, a.tail.lgs);  // the newest token's logical page
   if (n > 0) build_page_meta_rt(a.tail, b, n - 1, h, len);
 }
 
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(NW * kWave) void page_select_kernel(SelectArgs a) {
   const int b = blockIdx.x / a.num_kv_heads;
   const int h = blockIdx.x % a.num_kv_heads;
   const size_t row = (size_t)b * a.num_kv_heads + h;
-  const int n = row_pages(a.seq_lens[b], a.max_pages);
+  const int n = row_phys_pages(a.seq_lens[b], a.max_pages, a.lgs);  // physical pages (hierarchical paging)
   const int32_t* bt_row = a.page_phys ? a.block_table + (size_t)b * a.max_pages : nullptr;
   if ((a.streaming_mask >> h) & 1ull) {
     select_streaming_row(a, n, row, bt_row);
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(kRefreshThreads) void page_list_refresh_kernel(Sele
   const int b = blockIdx.x / a.num_kv_heads;
   const int h = blockIdx.x % a.num_kv_heads;
   const size_t row = (size_t)b * a.num_kv_heads + h;
-  const int n = row_pages(a.seq_lens[b], a.max_pages);
+  const int n = row_phys_pages(a.seq_lens[b], a.max_pages, a.lgs);
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
   if ((a.streaming_mask >> h) & 1ull) {
     select_streaming_row(a, n, row, bt_row);

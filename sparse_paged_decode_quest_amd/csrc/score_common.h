@@ -255,10 +255,13 @@ __device__ __forceinline__ int score_page(int p_begin, int it) {
 
 // Block-table entries of the calling lane's pages, read without waiting for the request's
 // length: indices past the table row are clamped into it and the values discarded later.
+// Pages are logical pages; with hierarchical paging (lgs > 0) the entry is that of the physical page
+// holding the logical page.
 template <int D, int KVD, int NW, int ITERS>
-__device__ __forceinline__ void load_block_table(const int32_t* bt_row, int max_pages, int p_begin, int (&raw)[ITERS]) {
+__device__ __forceinline__ void load_block_table(const int32_t* bt_row, int max_pages, int p_begin, int (&raw)[ITERS],
+                                                 int lgs = 0) {
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) raw[it] = bt_row[min(score_page<D, KVD, NW>(p_begin, it), max_pages - 1)];
+  for (int it = 0; it < ITERS; ++it) raw[it] = bt_row[min(score_page<D, KVD, NW>(p_begin, it) >> lgs, max_pages - 1)];
 }
 
 // Bounds S_{g,p} of the pages [p_begin, p_begin + NW * ITERS * PPI) owned by this workgroup.
@@ -286,7 +289,7 @@ __device__ __forceinline__ void score_block(const ScoreArgs& a, const int (&raw)
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
-    if (ok) T::load_m(m[it], a.meta, ((size_t)phys[it] * a.num_kv_heads + h) * 2 * D, c0);
+    if (ok) T::load_m(m[it], a.meta, head_unit(phys[it], a.num_kv_heads, h, a.lgs, pg[it] & ((1 << a.lgs) - 1)) * 2 * D, c0);
   }
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
@@ -344,6 +347,54 @@ __device__ __forceinline__ void score_block_topk(const ScoreArgs& a, const int (
     if (p >= n) return;
     row_scores[p] = ok ? topk_score(s) : -INFINITY;
   });
+}
+
+// Hierarchical paging (LServe summary, "Hierarchical Paging", physical page importance): the
+// workgroup's pages are logical pages, and physical page j's score is the largest top-K key of
+// its 2^lgs logical pages.  A wave instruction covers PPI consecutive logical pages (PPI a
+// multiple of 2^lgs, and workgroups start on a physical page), so the logical pages of one
+// physical page sit in lane groups LPP apart and one xor-shuffle per level folds them.  Logical
+// pages >= n (past the request or the scan) do not count; physical pages >= n_phys are not
+// written.
+template <int D, int KVD, int NW, int ITERS>
+__device__ __forceinline__ void score_block_topk_hier(const ScoreArgs& a, const int (&raw)[ITERS], int n, int n_phys,
+                                                      int b, int h, int p_begin, float* row_scores) {
+  using T = ScoreTraits<D, KVD>;
+  constexpr int LPP = T::LPP;
+  const int lane = threadIdx.x % kWave;
+  const int sub = lane % LPP;
+  const int c0 = sub * T::CW;
+  const int span = LPP << a.lgs;  // lanes of one physical page
+  int pg[ITERS], phys[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    pg[it] = score_page<D, KVD, NW>(p_begin, it);
+    phys[it] = pg[it] < n ? raw[it] : -1;
+  }
+  typename T::Q qr;
+  T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0);
+  typename T::M m[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
+    if (ok) T::load_m(m[it], a.meta, head_unit(phys[it], a.num_kv_heads, h, a.lgs, pg[it] & ((1 << a.lgs) - 1)) * 2 * D, c0);
+  }
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
+    float s[kG];
+    if (ok) T::bound(qr, m[it], s);
+    else {
+#pragma unroll
+      for (int g = 0; g < kG; ++g) s[g] = 0.f;
+    }
+#pragma unroll
+    for (int g = 0; g < kG; ++g) s[g] = group_sum<LPP>(s[g]);  // every lane of the group holds the sums
+    float v = ok ? topk_score(s) : -INFINITY;
+    for (int o = LPP; o < span; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    const int j = pg[it] >> a.lgs;
+    if (lane % span == 0 && j < n_phys) row_scores[j] = v;
+  }
 }
 
 // Coverage log-mass of a page: l_{g,p} = s S_{g,p} + ln(valid_p).

@@ -203,15 +203,21 @@ constexpr int kMaxChunks = 1024;  // chunks of one row the merge holds
 
 __device__ __forceinline__ int clamp_len(int n, int max_list) { return n < 0 ? 0 : (n > max_list ? max_list : n); }
 
+// Work units of a row: its list entries, 2^lgs 16-token units per entry (hierarchical paging: an
+// entry is a physical page of 2^lgs logical pages, each processed like a 16-token page).
+__device__ __forceinline__ int row_units(const int32_t* list_len, int r, int max_list, int lgs) {
+  return clamp_len(list_len[r], max_list) << lgs;
+}
+
 // Chunk size of the balanced plan, c = max(C, ceil(T / N_T), ceil(n_max / kMaxChunks)), from
 // every row's list length (computed by the calling wave; every lane receives it).
-__device__ __forceinline__ int balanced_chunk(const int32_t* list_len, int rows, int max_list, int C, int NT) {
+__device__ __forceinline__ int balanced_chunk(const int32_t* list_len, int rows, int max_list, int C, int NT, int lgs) {
   const int lane = threadIdx.x % kWave;
   unsigned long long tot = 0;
   uint32_t nmax = 0;
   for (int r0 = 0; r0 < rows; r0 += kWave) {
     const int r = r0 + lane;
-    const int n = r < rows ? clamp_len(list_len[r], max_list) : 0;
+    const int n = r < rows ? row_units(list_len, r, max_list, lgs) : 0;
     tot += (unsigned long long)n;
     nmax = max(nmax, (uint32_t)n);
   }
@@ -230,12 +236,12 @@ struct ChunkPos {
 };
 
 __device__ __forceinline__ bool balanced_locate(const int32_t* list_len, int rows, int max_list, int c, int k,
-                                                ChunkPos& cp) {
+                                                ChunkPos& cp, int lgs) {
   const int lane = threadIdx.x % kWave;
   uint32_t base = 0;
   for (int r0 = 0; r0 < rows; r0 += kWave) {
     const int r = r0 + lane;
-    const int n = r < rows ? clamp_len(list_len[r], max_list) : 0;
+    const int n = r < rows ? row_units(list_len, r, max_list, lgs) : 0;
     const uint32_t m = (uint32_t)((n + c - 1) / c);
     const uint32_t incl = wave_incl_scan(m) + base;
     const unsigned long long hit = __ballot(m > 0 && incl > (uint32_t)k && incl - m <= (uint32_t)k);
@@ -255,12 +261,12 @@ __device__ __forceinline__ bool balanced_locate(const int32_t* list_len, int row
 
 // First chunk number and chunk count of row `row` in the balanced plan.
 __device__ __forceinline__ void balanced_row(const int32_t* list_len, int rows, int max_list, int c, int row,
-                                             int& first, int& m) {
+                                             int& first, int& m, int lgs) {
   const int lane = threadIdx.x % kWave;
   uint32_t base = 0;
   for (int r0 = 0; r0 < rows; r0 += kWave) {
     const int r = r0 + lane;
-    const int n = r < rows ? clamp_len(list_len[r], max_list) : 0;
+    const int n = r < rows ? row_units(list_len, r, max_list, lgs) : 0;
     const uint32_t mm = (uint32_t)((n + c - 1) / c);
     const uint32_t incl = wave_incl_scan(mm) + base;
     if (row < r0 + kWave) {
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   size_t slot_row;  // partial-state slot of chunk 0 of the row: row * J, or the row's first chunk number
   if (a.balanced) {
     const int rows = a.batch * a.num_kv_heads;
-    c = balanced_chunk(a.list_len, rows, a.max_list, a.min_chunk, a.grid_target);
+    c = balanced_chunk(a.list_len, rows, a.max_list, a.min_chunk, a.grid_target, a.lgs);
     if ((int)blockIdx.x < rows && clamp_len(a.list_len[blockIdx.x], a.max_list) == 0) {
       // row blockIdx.x has no chunk: this block writes its empty result
       const size_t q0 = (size_t)(blockIdx.x / a.num_kv_heads) * a.num_q_heads + (size_t)(blockIdx.x % a.num_kv_heads) * kGq;
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
       if (threadIdx.x < kGq) a.out_lse[q0 + threadIdx.x] = -INFINITY;
     }
     ChunkPos cp;
-    if (!balanced_locate(a.list_len, rows, a.max_list, c, (int)blockIdx.x, cp)) return;
+    if (!balanced_locate(a.list_len, rows, a.max_list, c, (int)blockIdx.x, cp, a.lgs)) return;
     row = cp.row;
     j = cp.j;
     m = cp.m;
@@ -341,18 +347,18 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   // row's list length, assuming the chunk starts at j * min_chunk -- true whenever the row fits in
   // J * min_chunk pages, where the chunk size is the minimum; otherwise they are read again.
   const int spec_i0 = a.balanced ? -1 : j * a.min_chunk;
-  int spec_lp = -1, spec_lph = -1;
+  int spec_lp = -1, spec_lph = -1;  // list entry (physical page slot when lgs > 0) and physical page of the unit
   if (!a.balanced) {
-    const int idx = spec_i0 + wave + 4 * lane;
-    if (idx < a.max_list) {
-      spec_lp = list[idx];
-      if (plist) spec_lph = plist[idx];
+    const int e = (spec_i0 + wave + 4 * lane) >> a.lgs;
+    if (e < a.max_list) {
+      spec_lp = list[e];
+      if (plist) spec_lph = plist[e];
     }
   }
   typename T::Q q;
   T::load_q(q, a.q, qrow * D, quarter);
   if (!a.balanced) {
-    n = clamp_len(a.list_len[row], a.max_list);
+    n = row_units(a.list_len, row, a.max_list, a.lgs);
     if (n == 0) {
       if (j == 0) {
         for (int e = threadIdx.x; e < kGq * D; e += blockDim.x) a.out[qrow * D + e] = 0.f;
@@ -366,7 +372,9 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   const int i0 = j * c;
   const int i1 = min(n, i0 + c);
   const int len = a.seq_lens[b];
-  const int n_b = row_pages(len, a.max_pages);
+  const int n_b = row_logical_pages(len, a.max_pages, a.lgs);   // 16-token pages of the request
+  const int n_phys = row_phys_pages(len, a.max_pages, a.lgs);   // list entries must be below this
+  const int sub_mask = (1 << a.lgs) - 1;
 
   float m_run = -INFINITY, l_run = 0.f;
   float acc[kGq][CPL];
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   // loads are in flight while the current page is computed.
   auto load = [&](const PageRef& r, typename T::KF& kd, typename T::VF& vd, float& ksd, float& vsd) {
     if (r.page < 0) return;
-    const size_t head_page = (size_t)r.phys * a.num_kv_heads + h;
+    const size_t head_page = head_unit(r.phys, a.num_kv_heads, h, a.lgs, r.page & sub_mask);
     T::load_k(kd, a.k_pool, (head_page * kPage + tok) * D, quarter);
     T::load_v(vd, a.v_pool, head_page * kPage * D, lane);
     if (T::kScaled) {
@@ -469,10 +477,13 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
         lph = spec_lph;
       }
     } else if (lane < cnt) {
-      lp = list[idx];
-      if (plist) lph = plist[idx];
+      lp = list[idx >> a.lgs];
+      if (plist) lph = plist[idx >> a.lgs];
     }
-    if (!plist && lane < cnt && lp >= 0 && lp < n_b) lph = a.block_table[(size_t)b * a.max_pages + lp];
+    // unit idx of entry lp is its logical page (lp << lgs) + (idx mod 2^lgs); entries outside the
+    // request are not usable (checked before the shift, so no entry can wrap into range)
+    if (lane < cnt) lp = (lp >= 0 && lp < n_phys) ? (lp << a.lgs) | (idx & sub_mask) : -1;
+    if (!plist && lane < cnt && lp >= 0 && lp < n_b) lph = a.block_table[(size_t)b * a.max_pages + (lp >> a.lgs)];
     PageRef ra = batch_page(lp, lph, 0, n_b, len, a.num_pool_pages), rb;
     load(ra, ka, va, ksa, vsa);
     for (int u = 0; u < cnt; u += 2) {
@@ -560,8 +571,8 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
   int n = a.list_len[row];
   if (a.balanced) {
     const int rows = a.batch * a.num_kv_heads;
-    c = balanced_chunk(a.list_len, rows, a.max_list, a.min_chunk, a.grid_target);
-    balanced_row(a.list_len, rows, a.max_list, c, row, first, m);
+    c = balanced_chunk(a.list_len, rows, a.max_list, a.min_chunk, a.grid_target, a.lgs);
+    balanced_row(a.list_len, rows, a.max_list, c, row, first, m, a.lgs);
   }
   const size_t slot0 = (a.balanced ? (size_t)first : (size_t)row * J) * kGq + g;  // + j * kGq
   const int J_read = a.balanced ? m : J;  // chunk slots of the row that may be read
@@ -580,7 +591,7 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
     const int jj = part + u * PARTS;
     pre[u] = jj < J_read ? a.part_o[(slot0 + (size_t)jj * kGq) * D + ch] : 0.f;
   }
-  if (!a.balanced) plan_chunks(clamp_len(n, a.max_list), J, a.min_chunk, c, m);
+  if (!a.balanced) plan_chunks(clamp_len(n, a.max_list) << a.lgs, J, a.min_chunk, c, m);
   if (m <= 1) return;
 
   float mx = -INFINITY;

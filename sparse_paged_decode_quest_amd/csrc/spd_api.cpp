@@ -19,10 +19,14 @@ int meta_bytes_of(const spd_desc* d) { return d->kv_dtype == SPD_DTYPE_F32 ? 4 :
 
 bool is_mvar(const spd_select_params* s) { return s->estimator == SPD_ESTIMATOR_MVAR; }
 
+// log2 of the 16-token logical pages per physical page (hierarchical paging): 0 for 16-token pages, 2 for 64.
+int lgs_of(const spd_desc* d) { return d->page_size == 64 ? 2 : 0; }
+bool is_hier(const spd_desc* d) { return lgs_of(d) > 0; }
+
 // Pages per scorer workgroup (the standalone scorer's page groups per lane depend on the scan's size;
 // the mvar page summaries are bf16 whatever the pool type).
 int score_ppb(const spd_desc* d, const spd_select_params* s, int dyn_heads) {
-  const int iters = spd::score_iters((long long)d->batch * dyn_heads * d->max_pages_per_seq);
+  const int iters = spd::score_iters((long long)d->batch * dyn_heads * ((long long)d->max_pages_per_seq << lgs_of(d)));
   return spd::score_pages_per_block(d->head_dim, is_mvar(s) ? 2 : meta_bytes_of(d), spd::kScoreWaves, iters);
 }
 
@@ -46,8 +50,13 @@ int check_desc(const spd_desc* d) {
   if (!is_dtype(d->q_dtype) || !is_dtype(d->kv_dtype) || d->q_dtype == SPD_DTYPE_FP8_E4M3FN)
     return SPD_ERR_INVALID_ARG;
   // index arithmetic stays within 64-bit sizes; grids within 2^31 blocks
-  if ((int64_t)d->batch * d->num_kv_heads * d->max_pages_per_seq > ((int64_t)1 << 40)) return SPD_ERR_INVALID_ARG;
-  if (d->page_size != SPD_PAGE_SIZE) return SPD_ERR_UNSUPPORTED;
+  if (((int64_t)d->batch * d->num_kv_heads * d->max_pages_per_seq << lgs_of(d)) > ((int64_t)1 << 40)) return SPD_ERR_INVALID_ARG;
+  // logical pages and decode work units (4 per list entry) fit in int32
+  if (is_hier(d) && (d->max_pages_per_seq > (1 << 28) || d->max_list > (1 << 28))) return SPD_ERR_INVALID_ARG;
+  if (d->page_size != SPD_PAGE_SIZE && d->page_size != SPD_HIER_PAGE_SIZE) return SPD_ERR_UNSUPPORTED;
+  // hierarchical scoring folds a physical page's logical pages inside one wave instruction: a
+  // logical page's key box may span at most 16 lanes of 16 bytes (f32 at d = 128 spans 32)
+  if (d->page_size == SPD_HIER_PAGE_SIZE && d->kv_dtype == SPD_DTYPE_F32 && d->head_dim > 64) return SPD_ERR_UNSUPPORTED;
   if (d->num_q_heads / d->num_kv_heads != 4) return SPD_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return SPD_ERR_UNSUPPORTED;
   const bool ok = (d->q_dtype == SPD_DTYPE_F32 && d->kv_dtype == SPD_DTYPE_F32) ||
@@ -69,7 +78,7 @@ int check_sel(const spd_desc* d, const spd_select_params* s) {
   }
   if (s->estimator != SPD_ESTIMATOR_BOUND && s->estimator != SPD_ESTIMATOR_MVAR) return SPD_ERR_INVALID_ARG;
   if (s->estimator == SPD_ESTIMATOR_MVAR && s->mode != SPD_SELECT_COVERAGE) return SPD_ERR_INVALID_ARG;
-  (void)d;
+  if (is_hier(d) && s->mode != SPD_SELECT_TOPK) return SPD_ERR_UNSUPPORTED;  // physical pages: top-K only
   return SPD_OK;
 }
 
@@ -81,6 +90,7 @@ int check_tail(const spd_desc* d, const spd_select_params* s, int32_t mode, cons
   if (mode == SPD_TAIL_REBUILD && (!k_pool || (d->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale)))
     return SPD_ERR_INVALID_ARG;
   if (mode == SPD_TAIL_SKIP && (s->mode != SPD_SELECT_TOPK || s->n_local < 1)) return SPD_ERR_INVALID_ARG;
+  if (mode == SPD_TAIL_REBUILD && is_hier(d)) return SPD_ERR_UNSUPPORTED;
   return SPD_OK;
 }
 
@@ -184,7 +194,8 @@ spd::ScoreArgs score_args(const spd_desc* d, const spd_select_params* s, const v
   a.max_pages = d->max_pages_per_seq;
   a.num_pool_pages = d->num_pool_pages;
   a.pages_per_block = ppb;
-  a.blocks_per_row = (d->max_pages_per_seq + ppb - 1) / ppb;
+  a.lgs = lgs_of(d);
+  a.blocks_per_row = (int)((((int64_t)d->max_pages_per_seq << a.lgs) + ppb - 1) / ppb);
   a.partial_stride = a.blocks_per_row + 1;
   a.sm_scale = s->sm_scale;
   return a;
@@ -211,6 +222,7 @@ spd::SelectArgs select_args(const spd_desc* d, const spd_select_params* s, const
   a.n_local = s->n_local;
   a.n_sink_stream = s->n_sink_stream;
   a.n_local_stream = s->n_local_stream;
+  a.lgs = lgs_of(d);
   return a;
 }
 
@@ -228,6 +240,7 @@ spd::MetaArgs meta_args(const spd_desc* d, const void* k_pool, const uint16_t* k
   a.num_pool_pages = d->num_pool_pages;
   a.head_dim = d->head_dim;
   a.kv_dtype = d->kv_dtype;
+  a.lgs = lgs_of(d);
   return a;
 }
 
@@ -241,12 +254,13 @@ int build_summaries(const spd_desc* desc, const void* k_pool, const uint16_t* k_
   if (!k_pool || !block_table || !seq_lens || !out) return SPD_ERR_INVALID_ARG;
   if (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale) return SPD_ERR_INVALID_ARG;
   if ((first_page && span_pages < 1) || span_pages < 0) return SPD_ERR_INVALID_ARG;
+  if (stats && is_hier(desc)) return SPD_ERR_UNSUPPORTED;
   spd::MetaArgs a = meta_args(desc, k_pool, k_scale, block_table, seq_lens, out);
   a.first_page = first_page;
   a.stats = stats;
-  // pages per request: the span (from first_page, or the last span pages), or every page
-  const int span = (first_page || span_pages > 0) ? std::min(span_pages, desc->max_pages_per_seq)
-                                                  : desc->max_pages_per_seq;
+  // logical pages per request: the span (from first_page, or the last span pages), or every page
+  const int max_logical = desc->max_pages_per_seq << lgs_of(desc);
+  const int span = (first_page || span_pages > 0) ? std::min(span_pages, max_logical) : max_logical;
   a.span = span;
   a.blocks_per_req = (span * desc->num_kv_heads + 3) / 4;
   return launched(spd::launch_page_meta_build(a, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
@@ -313,7 +327,7 @@ size_t spd_workspace_bytes(const spd_desc* desc, const spd_select_params* sel, i
     case SPD_OP_PAGE_SELECT: return 0;
     case SPD_OP_PAGE_SCORE_SELECT: {
       FusedWs w;
-      return !is_mvar(sel) && fused_ws(desc, sel, w) ? w.total : (size_t)-1;
+      return !is_mvar(sel) && !is_hier(desc) && fused_ws(desc, sel, w) ? w.total : (size_t)-1;
     }
     default: return (size_t)-1;
   }
@@ -426,7 +440,7 @@ int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, co
   if ((rc = check_sel(desc, sel))) return rc;
   if ((rc = check_list_capacity(desc, sel))) return rc;
   FusedWs w;
-  if (is_mvar(sel) || !fused_ws(desc, sel, w)) return SPD_ERR_UNSUPPORTED;
+  if (is_mvar(sel) || is_hier(desc) || !fused_ws(desc, sel, w)) return SPD_ERR_UNSUPPORTED;
   spd::HeadList dyn, strm;
   uint64_t mask;
   if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
@@ -498,6 +512,7 @@ int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, c
   a.balanced = plan->balanced;
   a.grid_target = plan->min_grid_blocks;
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.lgs = lgs_of(desc);
   return launched(spd::launch_sparse_paged_decode(a, desc->head_dim, desc->q_dtype, desc->kv_dtype,
                                                   (hipStream_t)stream));
 }
@@ -524,6 +539,7 @@ int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float
   a.min_chunk = plan->min_chunk;
   a.balanced = plan->balanced;
   a.grid_target = plan->min_grid_blocks;
+  a.lgs = lgs_of(desc);
   return launched(spd::launch_lse_merge(a, desc->head_dim, (hipStream_t)stream));
 }
 

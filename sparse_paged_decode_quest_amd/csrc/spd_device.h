@@ -279,4 +279,25 @@ __device__ __forceinline__ int valid_in_page(int len, int p) {
   return v < 0 ? 0 : (v > kPage ? kPage : v);
 }
 
+// Hierarchical paging (LServe summary, "Hierarchical Paging"): a physical page of kPage << lgs
+// tokens holds 2^lgs logical pages of kPage tokens.  Logical page lp of a request lives in the
+// physical page of block-table slot lp >> lgs, as sub-page lp & (2^lgs - 1).  With lgs = 0 the two
+// coincide.
+__device__ __forceinline__ int row_logical_pages(int len, int max_pages, int lgs) {
+  return row_pages(len, max_pages << lgs);
+}
+
+__device__ __forceinline__ int row_phys_pages(int len, int max_pages, int lgs) {
+  const int P = kPage << lgs;
+  const int n = len > 0 ? (len + P - 1) / P : 0;
+  return n < max_pages ? n : max_pages;
+}
+
+// Index of the kPage-token unit holding sub-page `sub` of physical page `phys`, KV head h, in the
+// pools ([pages, Hkv, kPage << lgs, d]): its keys start at element unit * kPage * d, its scales at
+// unit * kPage, and its key statistics at unit * 2 * d of the page meta ([pages, Hkv, 2^lgs, 2, d]).
+__device__ __forceinline__ size_t head_unit(int phys, int num_kv_heads, int h, int lgs, int sub) {
+  return (((size_t)phys * num_kv_heads + h) << lgs) + (size_t)sub;
+}
+
 }  // namespace spd

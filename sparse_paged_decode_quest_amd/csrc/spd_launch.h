@@ -47,6 +47,7 @@ struct MetaArgs {
   int blocks_per_req;  // workgroups per request (4 (page, head) items each)
   int head_dim, kv_dtype;
   int stats;           // 0: key min / max (page meta); 1: key mean / variance, bf16 (page summaries)
+  int lgs;             // log2 of logical pages per physical page (hierarchical paging; 0: 16-token pages)
 };
 int launch_page_meta_build(const MetaArgs& a, int head_dim, int kv_dtype, hipStream_t stream);
 
@@ -75,6 +76,7 @@ struct ScoreArgs {
   int pages_per_block;
   float sm_scale;
   int tail_mode;             // spd_tail_mode: last page of each dynamic row scored / rebuilt / skipped
+  int lgs;                   // log2 of logical pages per physical page; > 0: scores are per physical page
 };
 int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool coverage, hipStream_t stream);
 // Coverage shares from the log-masses in a.ell (the scorers' second and third kernels).
@@ -95,7 +97,8 @@ struct SelectArgs {
   int mode, budget;
   unsigned long long gamma_fx;  // gamma in 2^-40 fixed point
   int n_sink, n_local, n_sink_stream, n_local_stream;
-  MetaArgs tail;            // tail.meta set: also rebuild each request's last page, all KV heads
+  int lgs;                  // log2 of logical pages per physical page: rows, lists and budget count physical pages
+  MetaArgs tail;            // tail.meta set: also rebuild each request's last logical page, all KV heads
 };
 int launch_page_select(const SelectArgs& a, hipStream_t stream);
 int launch_page_list_refresh(const SelectArgs& a, hipStream_t stream);
@@ -128,6 +131,7 @@ struct DecodeArgs {
   int blocks_per_row, min_chunk;
   int balanced, grid_target;  // step-wide split over grid_target (N_T) + rows blocks
   float sm_scale_log2;  // softmax scale times log2(e)
+  int lgs;              // log2 of logical pages per physical page: each list entry is 2^lgs work units
 };
 int launch_sparse_paged_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype,
                                hipStream_t stream);
@@ -140,6 +144,7 @@ struct MergeArgs {
   float* out_lse;
   int batch, num_q_heads, num_kv_heads, max_list, blocks_per_row, min_chunk;
   int balanced, grid_target;
+  int lgs;  // as in DecodeArgs
 };
 int launch_lse_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 

@@ -66,7 +66,9 @@ def upload(inp: Inputs, device="cuda") -> DeviceInputs:
     k_scale = None if inp.k_scale is None else t(inp.k_scale.view(np.int16))
     v_scale = None if inp.v_scale is None else t(inp.v_scale.view(np.int16))
     mdt = torch.bfloat16 if w.estimator == "mvar" else torch.float32 if w.kv_dtype == "f32" else torch.float16
-    meta = torch.zeros((inp.num_pool_pages, w.num_kv_heads, 2, w.head_dim), dtype=mdt, device=device)
+    g = w.page_size // 16  # logical pages per physical page (hierarchical paging)
+    shape = (inp.num_pool_pages, w.num_kv_heads) + ((g,) if g > 1 else ()) + (2, w.head_dim)
+    meta = torch.zeros(shape, dtype=mdt, device=device)
     return DeviceInputs(q=t(inp.q), k_pool=t(inp.k_pool), v_pool=t(inp.v_pool), k_scale=k_scale, v_scale=v_scale,
                         block_table=t(inp.block_table), seq_lens=t(inp.seq_lens), head_kind=inp.head_kind.copy(),
                         page_meta=meta)
@@ -74,14 +76,14 @@ def upload(inp: Inputs, device="cuda") -> DeviceInputs:
 
 def make_desc(w: Workload, num_pool_pages: int, max_list: int | None = None) -> A.Desc:
     return A.Desc(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
-                  page_size=16, max_pages_per_seq=w.pages_per_seq, num_pool_pages=num_pool_pages,
+                  page_size=w.page_size, max_pages_per_seq=w.pages_per_seq, num_pool_pages=num_pool_pages,
                   max_list=max_list or w.list_capacity, q_dtype=A.DTYPE[w.q_dtype], kv_dtype=A.DTYPE[w.kv_dtype])
 
 
-def reuse_slack(reuse: int) -> int:
-    """List entries a chunk of `reuse` steps can append to a selection: one page per 16 tokens
-    appended, plus the page a step may open."""
-    return 0 if reuse <= 1 else (reuse - 1) // 16 + 2
+def reuse_slack(reuse: int, page_size: int = 16) -> int:
+    """List entries a chunk of `reuse` steps can append to a selection: one page per page_size
+    tokens appended, plus the page a step may open."""
+    return 0 if reuse <= 1 else (reuse - 1) // page_size + 2
 
 
 def make_select(w: Workload) -> A.SelectParams:
@@ -162,7 +164,7 @@ class DecodeStep:
         self.phys_lists = phys_lists
         dev = d.q.device
         self.reuse = reuse
-        self.max_list = w.list_capacity + reuse_slack(reuse)
+        self.max_list = w.list_capacity + reuse_slack(reuse, w.page_size)
         self.desc = make_desc(w, d.num_pool_pages, self.max_list)
         self.sel = make_select(w)
         self.pp = self.plan.params()

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 6
+    assert A.abi_version() == 7
 
 
 def test_error_strings(lib):
@@ -296,3 +296,27 @@ def test_plan_grid_formula(lib):
             assert (c, m) == (0, 0)
             continue
         assert c >= C and m <= J and (m - 1) * c < n <= m * c
+
+
+def test_hierarchical_paging_argument_checks(lib):
+    """64-token physical pages (LServe, "Hierarchical Paging"): the top-K rule with the bound, the
+    unfused entry points and tail modes NONE / SKIP; everything else is reported unsupported."""
+    w = W.small(page_size=64, budget=6, n_local=1)
+    d = desc_for(w, page_size=64)
+    cov = sel_for(w, mode=A.SELECT_COVERAGE, gamma=0.9)
+    assert score_rc(d, cov) == A.SPD_ERR_UNSUPPORTED
+    assert score_rc(d, sel_for(w, mode=A.SELECT_COVERAGE, gamma=0.9, estimator=A.ESTIMATOR_MVAR)) == A.SPD_ERR_UNSUPPORTED
+    assert select_rc(desc_for(w, page_size=64, max_list=w.pages_per_seq), cov) == A.SPD_ERR_UNSUPPORTED
+    assert score_rc(d, sel_for(w), tail=A.TAIL_REBUILD) == A.SPD_ERR_UNSUPPORTED
+    assert fused_rc(d, sel_for(w)) == A.SPD_ERR_UNSUPPORTED
+    assert A.lib().spd_workspace_bytes(ctypes.byref(d), ctypes.byref(sel_for(w)), A.OP_PAGE_SCORE_SELECT) == \
+        ctypes.c_size_t(-1).value
+    rc = A.lib().spd_page_stats_build(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 0)
+    assert rc == A.SPD_ERR_UNSUPPORTED
+    # f32 pools at d = 128: a logical page's key box spans 32 lanes, more than hierarchical scoring folds
+    w32 = W.small(page_size=64, kv="f32", q="f32", d=128, budget=6, n_local=1)
+    assert score_rc(desc_for(w32, page_size=64), sel_for(w32)) == A.SPD_ERR_UNSUPPORTED
+    assert decode_rc(desc_for(w32, page_size=64), A.PlanParams(4, 16, 512)) == A.SPD_ERR_UNSUPPORTED
+    # argument errors are still found first on the supported shapes
+    assert score_rc(d, sel_for(w, budget_pages=0)) == A.SPD_ERR_INVALID_ARG
+    assert decode_rc(d, A.PlanParams(4, 16, 512), q=None) == A.SPD_ERR_INVALID_ARG
