@@ -56,15 +56,16 @@ def algorithmic_bytes(w, list_len: np.ndarray, head_kind: np.ndarray) -> dict:
     d = w.head_dim
     kv_bytes = {"f32": 4, "f16": 2, "fp8": 1}[w.kv_dtype]
     meta_bytes = 4 if w.kv_dtype == "f32" else 2
-    n_pages = w.n_pages
+    n_pages = w.n_pages  # physical pages (block-table slots)
     dyn_heads = int((head_kind == 0).sum())
-    meta = int(n_pages.sum()) * dyn_heads * 2 * d * meta_bytes
+    meta = int(w.n_logical.sum()) * dyn_heads * 2 * d * meta_bytes  # one key box per 16-token logical page
     key_page = 16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0)
     tail = w.batch * dyn_heads * (key_page + 2 * d * meta_bytes)
     if w.estimator == "mvar":  # bf16 summaries; the first and current pages read as keys, one summary written
         meta = int(np.maximum(n_pages - 2, 0).sum()) * dyn_heads * 2 * d * 2
         tail = dyn_heads * int(np.minimum(n_pages, 2).sum()) * key_page + w.batch * dyn_heads * 2 * d * 2
-    page_kv = 16 * d * kv_bytes * 2 + (16 * 2 * 2 if w.kv_dtype == "fp8" else 0)
+    P = w.page_size  # a listed page is read whole: K and V (+ their fp16 scales) of P tokens
+    page_kv = P * d * kv_bytes * 2 + (P * 2 * 2 if w.kv_dtype == "fp8" else 0)
     kv = int(list_len.sum()) * page_kv
     q = w.batch * w.num_q_heads * d * (4 if w.q_dtype == "f32" else 2)
     o = w.batch * w.num_q_heads * (d + 1) * 4
@@ -92,6 +93,13 @@ def scorer_bytes(w, head_kind: np.ndarray, tail: str) -> int:
         key_page = 16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0)
         rebuilt = int((w.n_pages > 0).sum()) * dyn_heads * 2 * d * 2 if tail == "rebuild" else 0
         return est * (2 * d * 2 + 4 + 4 * w.group) + exact * (key_page + 4 * w.group) + q + rebuilt
+    if w.page_size != 16:
+        # hierarchical paging: the key boxes of the scanned logical pages (the skipping scorer leaves out
+        # the last physical page), one block-table entry and one score per physical page
+        g = w.page_size // 16
+        skip = 1 if tail in ("side", "select") else 0
+        logical = sum(min(int(nl), g * max(int(npg) - skip, 0)) for nl, npg in zip(w.n_logical, w.n_pages))
+        return dyn_heads * (logical * 2 * d * meta_bytes + int(w.n_pages.sum()) * 8) + q
     rows = int((w.n_pages > 0).sum()) * dyn_heads
     scanned = int(w.n_pages.sum()) * dyn_heads - (rows if tail in ("side", "rebuild") else 0)
     per_page_head = 2 * d * meta_bytes + 4 + 4  # meta row + block-table entry + score
@@ -126,17 +134,23 @@ def cpu_baseline(w, inp, seconds: float) -> dict:
     from oracle import spd_oracle as O
 
     mvar = w.estimator == "mvar"
+    hier = w.page_size != 16
     with threadpool_limits(limits=1):
         # setup (the GPU builds the page summaries once before timing too)
-        meta = O.page_stats_build(inp) if mvar else O.page_meta_build(inp)
-        first = [max(O.n_pages(L) - 1, 0) for L in inp.seq_lens]
+        meta = O.page_stats_build(inp) if mvar else O.hier_meta_build(inp) if hier else O.page_meta_build(inp)
+        first = [max(O.n_pages(L) - 1, 0) for L in inp.seq_lens]  # the newest token's (logical) page
         steps, t0 = 0, time.perf_counter()
         while True:
             if mvar:
                 sel = O.page_select(inp, None, O.page_stats_build(inp, first_page=first, stats=meta))
+            elif hier:
+                sel = O.hier_page_select(inp, O.hier_meta_build(inp, meta=meta, first_page=first))
             else:
                 sel = O.page_select(inp, O.page_meta_build(inp, meta=meta, first_page=first))
-            O.sparse_paged_decode(inp, sel["lists"], w.sm_scale)
+            if hier:
+                O.hier_sparse_paged_decode(inp, sel["lists"], w.sm_scale)
+            else:
+                O.sparse_paged_decode(inp, sel["lists"], w.sm_scale)
             steps += 1
             el = time.perf_counter() - t0
             if el >= seconds:
@@ -369,7 +383,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "context": int(max(w.seq_lens)), "heads": heads,
-                   "head_dim": w.head_dim, "page": 16, "kv_dtype": w.kv_dtype, "mode": w.mode,
+                   "head_dim": w.head_dim, "page": w.page_size, "logical_page": 16, "kv_dtype": w.kv_dtype, "mode": w.mode,
                    "estimator": w.estimator,
                    "budget_pages": w.budget_pages, "gamma": w.gamma, "streaming_kv_heads": len(w.streaming_heads),
                    "layers_rotated": R, "graph": True, "fused_select": args.fused,

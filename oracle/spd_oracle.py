@@ -508,20 +508,21 @@ def hier_logical_keys(inp, b: int, h: int, lp: int) -> np.ndarray:
     return stored_values(inp.k_pool[phys, h, sl], scale, w.kv_dtype)[:valid_tokens(inp.seq_lens[b], lp)]
 
 
-def hier_meta_build(inp) -> np.ndarray:
-    """Key min / max of every logical page of every request, all KV heads (LServe: statistics
-    on N_L-token logical pages, stored with the physical page that holds them).
+def hier_meta_build(inp, meta: np.ndarray | None = None, first_page=None) -> np.ndarray:
+    """Key min / max of every logical page lp >= first_page[b] of every request, all KV heads
+    (LServe: statistics on N_L-token logical pages, stored with the physical page that holds them).
 
     Layout [num_pool_pages, Hkv, g, 2, d]: entry [P, h, i] is logical sub-page i of physical page
-    P; 0 = kmin, 1 = kmax, in the meta dtype (fp8 pools: fp16 rounded outward).  Sub-pages past a
-    request's end are left at zero.
+    P; 0 = kmin, 1 = kmax, in the meta dtype (fp8 pools: fp16 rounded outward).  Entries not
+    visited keep the values of ``meta`` (zeros when it is None).
     """
     w = inp.workload
     Npool, Hkv, NP, d = inp.k_pool.shape
     g = NP // PAGE
-    out = np.zeros((Npool, Hkv, g, 2, d), dtype=meta_dtype(w.kv_dtype))
+    out = np.zeros((Npool, Hkv, g, 2, d), dtype=meta_dtype(w.kv_dtype)) if meta is None else meta.copy()
     for b in range(len(inp.seq_lens)):
-        for lp in range(n_pages(inp.seq_lens[b])):
+        start = 0 if first_page is None else max(0, int(first_page[b]))
+        for lp in range(start, n_pages(inp.seq_lens[b])):
             phys = int(inp.block_table[b, lp // g])
             for h in range(Hkv):
                 keys = hier_logical_keys(inp, b, h, lp)
