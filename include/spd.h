@@ -29,9 +29,10 @@
  * Hierarchical paging (LServe summary, "Hierarchical Paging"; spd_desc.page_size = 64): physical
  * pages of N_P = 64 tokens hold 4 logical pages of N_L = 16 tokens.  Key statistics are kept per
  * logical page; a physical page's score is the largest score of its logical pages ("Physical page
- * importance aggregation"); the budget, the sink and local windows and the lists count physical
- * pages ("Token budget and physical page selection": K = ceil(token budget / N_P)), and
- * attention reads every valid token of each listed physical page.
+ * importance aggregation"); under the coverage rule a physical page's share is the sum of its
+ * logical pages' shares (mass is additive); the budget, the sink and local windows and the lists
+ * count physical pages ("Token budget and physical page selection": K = ceil(token budget / N_P)),
+ * and attention reads every valid token of each listed physical page.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -155,7 +156,7 @@ typedef enum spd_op {
 
 /* Shapes of one step.  Supported: page_size 16 or 64; head_dim 64 or 128; Hq / Hkv = 4;
  * (q_dtype, kv_dtype) in {(f32, f32), (f16, f16), (f16, fp8)}.  page_size 64 (hierarchical
- * paging) supports the TOPK rule with the BOUND estimator, tail modes NONE and SKIP, and the
+ * paging) supports both rules with the BOUND estimator, tail modes NONE and SKIP, and the
  * unfused entry points; f32 pools need head_dim 64 there.  Others return SPD_ERR_UNSUPPORTED so
  * a caller can route them elsewhere. */
 typedef struct spd_desc {
@@ -239,7 +240,9 @@ int spd_page_stats_build(const spd_desc* desc, const void* k_pool, const uint16_
  * TOPK: scores[b,h,p] = max over the G query heads of the row of S_{g,p} (LServe page
  * importance, computed from page_meta); with page_size 64, the largest of these over the logical
  * pages of page p that hold valid tokens (LServe, "Physical page importance aggregation"), and
- * SPD_TAIL_SKIP skips the row's last page (all its logical pages).  COVERAGE: l_{g,p} = sm_scale * S_{g,p} +
+ * SPD_TAIL_SKIP skips the row's last page (all its logical pages); COVERAGE takes l, head_lse and
+ * the shares over logical pages and writes scores[b,h,p] = the sum of the shares of page p's
+ * logical pages.  COVERAGE: l_{g,p} = sm_scale * S_{g,p} +
  * ln(valid tokens of p); head_lse[b, h*G+g] = logsumexp_p l_{g,p}; scores[b,h,p] =
  * (1/G) sum_g exp(l_{g,p} - head_lse) (Moira's group-mean share, section 3.2, Eq. 3).
  * tail_mode (spd_tail_mode) says how each dynamic row's last logical page is treated;

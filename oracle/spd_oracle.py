@@ -46,6 +46,10 @@ Readings where the pages leave a step open:
   * Hierarchical paging: the GQA group is combined as above (max over query heads)
     after the max over logical pages; logical pages with no valid token do not
     enter the max; the budget, the sink and the local window count physical pages.
+    Under the coverage rule the shares are taken over logical pages (each logical
+    page's log-mass from its own box and valid tokens) and a physical page's share
+    is the sum of its logical pages' shares: mass is additive, where the top-K
+    importance bound takes the max.
   * mvar: the variance is the population variance over the page's valid tokens
     (divided by their count), and the token count in Eq. 2 is the page's valid
     token count; mean and variance are stored rounded to bf16 (nearest, ties to even)
@@ -555,12 +559,30 @@ def hier_row_scores(inp, meta: np.ndarray, b: int, h: int):
     return scores, S
 
 
+def hier_row_shares(inp, meta: np.ndarray, b: int, h: int):
+    """Coverage shares of the physical pages of dynamic row (b, h): Moira's group-mean share of
+    every logical page (log-mass s * S_{g,lp} + ln(valid_lp) from its own key box, softmax over
+    the row's logical pages per query head, mean over the group; section 3.2, Eq. 3), summed over
+    the logical pages of each physical page.
+
+    Returns (shares [n_physical], lse_g [G]).
+    """
+    w = inp.workload
+    NP = physical_page_tokens(inp)
+    g = NP // PAGE
+    L = int(inp.seq_lens[b])
+    _, S = hier_row_scores(inp, meta, b, h)
+    pi_log, lse = coverage_shares(S, L, w.sm_scale)
+    return np.array([pi_log[j * g:(j + 1) * g].sum() for j in range(hier_n_physical(L, NP))]), lse
+
+
 def hier_page_select(inp, meta: np.ndarray):
     """Lists of physical pages for every row: streaming rows keep their sink + local physical
     pages; dynamic rows the forced physical pages plus the best others under the physical page
-    budget (top-K by (score desc, page asc)).  Same dict as page_select."""
+    budget (top-K by (score desc, page asc)), or the coverage rule over physical shares.  Same
+    dict as page_select."""
     w = inp.workload
-    assert w.mode == "topk", "hierarchical paging is defined for the top-K rule"
+    assert w.estimator == "bound", "hierarchical paging scores pages from their key boxes"
     NP = physical_page_tokens(inp)
     out = {"lists": {}, "scores": {}, "S": {}, "lse": {}}
     for b in range(len(inp.seq_lens)):
@@ -570,9 +592,17 @@ def hier_page_select(inp, meta: np.ndarray):
                 out["lists"][(b, h)] = forced_pages(n, w.n_sink_stream, w.n_local_stream)
                 out["scores"][(b, h)] = None
                 continue
-            sc, S = hier_row_scores(inp, meta, b, h)
-            out["scores"][(b, h)], out["S"][(b, h)] = sc, S
-            out["lists"][(b, h)] = select_topk(sc, n, w.budget_pages, forced_pages(n, w.n_sink, w.n_local))
+            forced = forced_pages(n, w.n_sink, w.n_local)
+            if w.mode == "topk":
+                sc, S = hier_row_scores(inp, meta, b, h)
+                out["scores"][(b, h)], out["S"][(b, h)] = sc, S
+                out["lists"][(b, h)] = select_topk(sc, n, w.budget_pages, forced)
+            elif n == 0:
+                out["scores"][(b, h)], out["lse"][(b, h)], out["lists"][(b, h)] = np.zeros(0), np.full(w.group, -np.inf), []
+            else:
+                pi, lse = hier_row_shares(inp, meta, b, h)
+                out["scores"][(b, h)], out["lse"][(b, h)] = pi, lse
+                out["lists"][(b, h)] = select_coverage(pi, n, w.gamma, forced)
     return out
 
 

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreAr
   }
   const int p_begin = r.blk * a.pages_per_block;
   int raw[ITERS];
-  load_block_table<D, KVD, kScoreWaves, ITERS>(bt_row, a.max_pages, p_begin, raw, HIER ? a.lgs : 0);
+  load_block_table<D, KVD, kScoreWaves, ITERS>(bt_row, a.max_pages, p_begin, raw, HIER || COV ? a.lgs : 0);
   float* sc_row = a.scores + ((size_t)r.b * a.num_kv_heads + r.h) * a.max_pages;
   if constexpr (HIER) {
     const int n_phys = row_phys_pages(len, a.max_pages, a.lgs);
@@ -59,7 +59,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreAr
     if (p_begin >= n_scan) return;  // uniform over the block
     score_block_topk_hier<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, phys_scan, r.b, r.h, p_begin, sc_row);
   } else {
-    const int n = row_pages(len, a.max_pages);
+    // coverage over 64-token pages scans logical pages too (their shares are summed per page later)
+    const int n = COV ? row_logical_pages(len, a.max_pages, a.lgs) : row_pages(len, a.max_pages);
     const int n_scan = scan_pages(a, n);
     if (!COV && a.tail_mode == SPD_TAIL_SKIP && r.blk == 0 && n > 0 && threadIdx.x == 0) sc_row[n - 1] = -INFINITY;
     if (p_begin >= n_scan) return;  // uniform over the block
@@ -68,8 +69,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreAr
   }
 }
 
-// Coverage, second and third passes, over blocks of kSharePages pages of a row (one page per
-// thread, so the exponentials of a row are spread over many workgroups):
+// Coverage, second and third passes, over blocks of kSharePages (logical) pages of a row (one page
+// per thread, so the exponentials of a row are spread over many workgroups):
 //  * coverage_part_kernel: each block's (max, sum exp) of the log-masses, per head;
 //  * coverage_share_kernel: wave 0 folds the row's block pairs into lse_g (fixed order) while
 //    every thread reads its page's log-masses; then pi_bar_p = (1/G) sum_g exp(l_{g,p} - lse_g).
@@ -78,6 +79,8 @@ constexpr int kSharePages = kShareThreads;
 constexpr int kShareWaves = kShareThreads / kWave;
 
 __host__ __device__ inline int share_blocks_per_row(int max_pages) { return (max_pages + kSharePages - 1) / kSharePages; }
+// ... of a row of logical pages (hierarchical paging: 2^lgs per block-table slot)
+__host__ __device__ inline int share_blocks_per_row(const ScoreArgs& a) { return share_blocks_per_row(a.max_pages << a.lgs); }
 
 // Workgroup max and sum over kShareThreads lanes of four values per lane (every thread receives
 // them); `red` holds one entry per wave and head.
@@ -107,13 +110,13 @@ struct ShareRole {
 };
 
 __device__ __forceinline__ ShareRole share_role(const ScoreArgs& a) {
-  const int bpr = share_blocks_per_row(a.max_pages);
+  const int bpr = share_blocks_per_row(a);
   const int row_dyn = blockIdx.x / bpr;
   ShareRole r;
   r.part = blockIdx.x % bpr;
   r.b = row_dyn / a.dyn.count;
   r.h = a.dyn.head[row_dyn % a.dyn.count];
-  r.n = row_pages(a.seq_lens[r.b], a.max_pages);
+  r.n = row_logical_pages(a.seq_lens[r.b], a.max_pages, a.lgs);
   r.row = (size_t)r.b * a.num_kv_heads + r.h;
   return r;
 }
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(kShareThreads) void coverage_part_kernel(ScoreArgs 
   const ShareRole r = share_role(a);
   if (r.part * kSharePages >= r.n) return;  // uniform: the block is past the row
   const int p = r.part * kSharePages + (int)threadIdx.x;
-  const float4 l4 = p < r.n ? a.ell[r.row * a.max_pages + p]
+  const float4 l4 = p < r.n ? a.ell[r.row * ell_stride(a) + p]
                             : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
   const float lg[kG] = {l4.x, l4.y, l4.z, l4.w};
   float2 out[kG];
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(kShareThreads) void coverage_part_kernel(ScoreArgs 
     float2 v = out[0];
 #pragma unroll
     for (int g = 1; g < kG; ++g) v = (int)threadIdx.x == g ? out[g] : v;
-    a.partials[(r.row * share_blocks_per_row(a.max_pages) + r.part) * kG + threadIdx.x] = v;
+    a.partials[(r.row * share_blocks_per_row(a) + r.part) * kG + threadIdx.x] = v;
   }
 }
 
@@ -148,11 +151,11 @@ __global__ __launch_bounds__(kShareThreads) void coverage_share_kernel(ScoreArgs
   if (r.part * kSharePages >= r.n && r.part != 0) return;  // block 0 of an empty row still writes head_lse
   const int p = r.part * kSharePages + (int)threadIdx.x;
   float4 l4 = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-  if (p < r.n) l4 = a.ell[r.row * a.max_pages + p];
+  if (p < r.n) l4 = a.ell[r.row * ell_stride(a) + p];
   if (threadIdx.x < kWave) {
     // the row's block pairs, lane k holding pair k (k, k + 64, ... folded in order first)
     const int nparts = (r.n + kSharePages - 1) / kSharePages;
-    const float2* pr = a.partials + r.row * share_blocks_per_row(a.max_pages) * kG;
+    const float2* pr = a.partials + r.row * share_blocks_per_row(a) * kG;
     float m[kG], s[kG];
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
@@ -179,12 +182,22 @@ __global__ __launch_bounds__(kShareThreads) void coverage_share_kernel(ScoreArgs
   }
   __syncthreads();
   const float lse[kG] = {lse_s[0], lse_s[1], lse_s[2], lse_s[3]};
-  if (p < r.n) a.scores[r.row * a.max_pages + p] = group_share(l4, lse);
+  if (a.lgs == 0) {
+    if (p < r.n) a.scores[r.row * a.max_pages + p] = group_share(l4, lse);
+    return;
+  }
+  // hierarchical paging: a page's share is the sum of its logical pages' shares (mass is additive);
+  // the 2^lgs logical pages of a page are consecutive threads of one wave
+  float v = p < r.n ? group_share(l4, lse) : 0.f;
+  for (int o = 1; o < (1 << a.lgs); o <<= 1) v += __shfl_xor(v, o, kWave);
+  const int j = p >> a.lgs;
+  if ((p & ((1 << a.lgs) - 1)) == 0 && j < row_phys_pages(a.seq_lens[r.b], a.max_pages, a.lgs))
+    a.scores[r.row * a.max_pages + j] = v;
 }
 
 void launch_coverage_shares(const ScoreArgs& a, hipStream_t stream) {
   const unsigned rows = (unsigned)(a.batch * a.dyn.count);
-  const dim3 share_grid(rows * (unsigned)share_blocks_per_row(a.max_pages)), share_block(kShareThreads);
+  const dim3 share_grid(rows * (unsigned)share_blocks_per_row(a)), share_block(kShareThreads);
   hipLaunchKernelGGL(coverage_part_kernel, share_grid, share_block, 0, stream, a);
   hipLaunchKernelGGL(coverage_share_kernel, share_grid, share_block, 0, stream, a);
 }

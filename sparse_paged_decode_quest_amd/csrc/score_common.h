@@ -397,6 +397,9 @@ __device__ __forceinline__ void score_block_topk_hier(const ScoreArgs& a, const 
   }
 }
 
+// Row stride of the coverage log-masses: one entry per logical page.
+__host__ __device__ __forceinline__ size_t ell_stride(const ScoreArgs& a) { return (size_t)a.max_pages << a.lgs; }
+
 // Coverage log-mass of a page: l_{g,p} = s S_{g,p} + ln(valid_p).
 __device__ __forceinline__ void coverage_logmass(const ScoreArgs& a, int valid, bool ok, const float (&s)[kG],
                                                  float (&lg)[kG]) {
@@ -415,7 +418,7 @@ __device__ __forceinline__ void score_block_ell(const ScoreArgs& a, const int (&
     if (p >= n) return;
     float lg[kG];
     coverage_logmass(a, valid_in_page(len, p), ok, s, lg);
-    a.ell[row * a.max_pages + p] = make_float4(lg[0], lg[1], lg[2], lg[3]);
+    a.ell[row * ell_stride(a) + p] = make_float4(lg[0], lg[1], lg[2], lg[3]);
   });
 }
 
@@ -441,7 +444,7 @@ __device__ __forceinline__ void score_block_coverage(const ScoreArgs& a, const i
     coverage_logmass(a, valid_in_page(len, p), ok, s, lg);
 #pragma unroll
     for (int g = 0; g < kG; ++g) lse_push(lm[g], ls[g], lg[g]);
-    a.ell[row * a.max_pages + p] = make_float4(lg[0], lg[1], lg[2], lg[3]);
+    a.ell[row * ell_stride(a) + p] = make_float4(lg[0], lg[1], lg[2], lg[3]);
   });
   // fold the lanes that own pages (sub == 0), then the waves in order
   __shared__ float sm_m[NW][kG], sm_s[NW][kG];

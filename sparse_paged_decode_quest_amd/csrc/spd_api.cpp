@@ -78,7 +78,7 @@ int check_sel(const spd_desc* d, const spd_select_params* s) {
   }
   if (s->estimator != SPD_ESTIMATOR_BOUND && s->estimator != SPD_ESTIMATOR_MVAR) return SPD_ERR_INVALID_ARG;
   if (s->estimator == SPD_ESTIMATOR_MVAR && s->mode != SPD_SELECT_COVERAGE) return SPD_ERR_INVALID_ARG;
-  if (is_hier(d) && s->mode != SPD_SELECT_TOPK) return SPD_ERR_UNSUPPORTED;  // physical pages: top-K only
+  if (is_hier(d) && is_mvar(s)) return SPD_ERR_UNSUPPORTED;  // 64-token pages: key-box estimates only
   return SPD_OK;
 }
 
@@ -150,10 +150,11 @@ struct ScoreWs {
 ScoreWs score_ws(const spd_desc* d) {
   const size_t rows = (size_t)d->batch * d->num_kv_heads;
   const int G = d->num_q_heads / d->num_kv_heads;
-  const size_t parts = ((size_t)d->max_pages_per_seq + 1023) / 1024;
+  const size_t logical = (size_t)d->max_pages_per_seq << lgs_of(d);  // log-masses per logical page
+  const size_t parts = (logical + 1023) / 1024;
   ScoreWs w;
   w.ell_off = 0;
-  w.part_off = align_up(rows * d->max_pages_per_seq * G * sizeof(float));
+  w.part_off = align_up(rows * logical * G * sizeof(float));
   w.total = w.part_off + align_up(rows * parts * G * 2 * sizeof(float));
   return w;
 }

@@ -299,14 +299,17 @@ def test_plan_grid_formula(lib):
 
 
 def test_hierarchical_paging_argument_checks(lib):
-    """64-token physical pages (LServe, "Hierarchical Paging"): the top-K rule with the bound, the
-    unfused entry points and tail modes NONE / SKIP; everything else is reported unsupported."""
+    """64-token physical pages (LServe, "Hierarchical Paging"): both rules with the key-box bound,
+    the unfused entry points and tail modes NONE / SKIP; everything else is reported unsupported."""
     w = W.small(page_size=64, budget=6, n_local=1)
     d = desc_for(w, page_size=64)
     cov = sel_for(w, mode=A.SELECT_COVERAGE, gamma=0.9)
-    assert score_rc(d, cov) == A.SPD_ERR_UNSUPPORTED
     assert score_rc(d, sel_for(w, mode=A.SELECT_COVERAGE, gamma=0.9, estimator=A.ESTIMATOR_MVAR)) == A.SPD_ERR_UNSUPPORTED
-    assert select_rc(desc_for(w, page_size=64, max_list=w.pages_per_seq), cov) == A.SPD_ERR_UNSUPPORTED
+    assert select_rc(desc_for(w, page_size=64, max_list=w.pages_per_seq - 1), cov) == A.SPD_ERR_INVALID_ARG
+    assert score_rc(d, cov, ws_bytes=A.spd_workspace_bytes(d, cov, A.OP_PAGE_SCORE) - 1) == A.SPD_ERR_WORKSPACE
+    # the coverage log-masses are kept per logical page: four times the 16-token layout's workspace
+    flat = desc_for(w, page_size=16, max_pages_per_seq=w.pages_per_seq * 4)
+    assert A.spd_workspace_bytes(d, cov, A.OP_PAGE_SCORE) == A.spd_workspace_bytes(flat, cov, A.OP_PAGE_SCORE)
     assert score_rc(d, sel_for(w), tail=A.TAIL_REBUILD) == A.SPD_ERR_UNSUPPORTED
     assert fused_rc(d, sel_for(w)) == A.SPD_ERR_UNSUPPORTED
     assert A.lib().spd_workspace_bytes(ctypes.byref(d), ctypes.byref(sel_for(w)), A.OP_PAGE_SCORE_SELECT) == \

@@ -41,7 +41,17 @@ HSMALL = {
     "h_fp8_d128": W.small("h_fp8_d128", page_size=NP, kv="fp8", seq_lens=(1500, 250, 31), budget=5, n_local=1),
     "h_f32_d64": W.small("h_f32_d64", page_size=NP, kv="f32", q="f32", d=64, seq_lens=(700, 37, 2050, 16, 17),
                          budget=5, n_local=1),
+    # the coverage rule over physical pages: shares of logical pages summed per page
+    "h_cov_f16": W.small("h_cov_f16", page_size=NP, mode="coverage", gamma=0.9, n_local=1, seq_lens=(1200, 333, 64, 1),
+                         planted=("fixed", 6), delta=("nats", 6.0)),
+    "h_cov_f32_d64": W.small("h_cov_f32_d64", page_size=NP, kv="f32", q="f32", d=64, mode="coverage", gamma=0.95,
+                             n_local=1, seq_lens=(900, 77), streaming=(0,), n_sink_stream=1, n_local_stream=1),
+    # more than 1024 logical pages: the share passes take several workgroups per row
+    "h_cov_long": W.small("h_cov_long", page_size=NP, mode="coverage", gamma=0.99, n_local=1, seq_lens=(20000, 5000),
+                          Hq=4, Hkv=1, planted=("fixed", 40), delta=("nats", 9.0)),
 }
+TOPK_SMALL = [k for k in HSMALL if HSMALL[k].mode == "topk"]
+COV_SMALL = [k for k in HSMALL if HSMALL[k].mode == "coverage"]
 
 
 def run_case(w, plan=None, tail="auto"):
@@ -97,6 +107,20 @@ def check_rows(inp, st, meta_ref, rows):
             oracle_lists[(b, h)] = O.forced_pages(n, w.n_sink_stream, w.n_local_stream)
             assert lst == oracle_lists[(b, h)], (b, h)
             continue
+        forced = O.forced_pages(n, w.n_sink, w.n_local)
+        if w.mode == "coverage":
+            if n == 0:
+                oracle_lists[(b, h)] = []
+                assert lst == []
+                continue
+            pi, lse = O.hier_row_shares(inp, meta_ref, b, h)
+            P.check_coverage_shares(scores[b, h, :n], pi)
+            G = w.group
+            head_lse = st.head_lse.cpu().numpy()[b, h * G:(h + 1) * G]
+            assert np.allclose(head_lse, lse, rtol=0, atol=1e-4 * np.abs(lse).max()), (b, h)
+            P.check_coverage_list(lst, pi, n, w.gamma, forced)
+            oracle_lists[(b, h)] = O.select_coverage(pi, n, w.gamma, forced)
+            continue
         ref, _ = O.hier_row_scores(inp, meta_ref, b, h)
         scale = phys_scale(inp, meta_ref, b, h)
         if st.tail == "select" and n > 0:  # the scorer skips the last physical page (the local window keeps it)
@@ -104,16 +128,17 @@ def check_rows(inp, st, meta_ref, rows):
             P.check_topk_scores(scores[b, h, :n - 1], ref[:n - 1], scale[:n - 1])
         else:
             P.check_topk_scores(scores[b, h, :n], ref, scale)
-        forced = O.forced_pages(n, w.n_sink, w.n_local)
         P.check_topk_list(lst, ref, n, w.budget_pages, forced, scale)
         oracle_lists[(b, h)] = O.select_topk(ref, n, w.budget_pages, forced)
     return oracle_lists
 
 
 @pytest.mark.parametrize("tail", ["none", "select"])
-@pytest.mark.parametrize("name", list(HSMALL))
+@pytest.mark.parametrize("name", TOPK_SMALL + COV_SMALL)
 def test_hier_small_meta_scores_lists_attention(name, tail):
     w = HSMALL[name]
+    if w.mode == "coverage" and tail == "select":
+        tail = "serial"  # coverage counts the forced pages' shares: their statistics are rebuilt first
     inp, d, st = run_case(w, tail=tail)
     meta_ref = O.hier_meta_build(inp)
     assert np.array_equal(d.page_meta.cpu().numpy(), meta_ref), "logical page meta differs"

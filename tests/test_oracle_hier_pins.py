@@ -176,3 +176,54 @@ def test_named_workload_budget_is_the_token_budget_over_the_physical_page():
     w = W.named("llama3_8b_b1_128k_f16_hier64")
     assert w.page_size == 64 and w.budget_pages == 4096 // 64  # K = ceil(B / N_P)
     assert int(w.n_pages[0]) == 2048 and int(w.n_logical[0]) == 8192
+
+
+def test_coverage_shares_are_the_flat_logical_shares_summed_per_physical_page():
+    w = _hier(mode="coverage", gamma=0.9, n_local=1, planted=("fixed", 5), delta=("nats", 6.0))
+    inp = W.generate(w)
+    flat = _flat_relayout(inp)
+    meta_h = O.hier_meta_build(inp)
+    meta_f = O.page_meta_build(flat)
+    for b, L in enumerate(w.seq_lens):
+        for h in range(w.num_kv_heads):
+            pi, lse = O.hier_row_shares(inp, meta_h, b, h)
+            pi_f, lse_f = O.coverage_shares(O.row_bounds(flat, meta_f, b, h), L, w.sm_scale)
+            assert np.array_equal(lse, lse_f)
+            assert np.allclose(pi, [pi_f[4 * j:4 * j + 4].sum() for j in range(-(-L // NP))], rtol=0, atol=1e-15)
+            assert abs(pi.sum() - 1.0) < 1e-12
+
+
+def test_coverage_share_of_a_physical_page_is_its_estimated_mass_fraction():
+    # one request, one KV head: the share of physical page j is sum over its logical pages and the
+    # group of exp(l) / exp(lse_g), with l = s * bound + ln(valid), computed here from the tokens
+    w = _hier(mode="coverage", gamma=0.9, n_local=1, seq_lens=(300,), Hq=4, Hkv=1, kv="f32", q="f32", d=64,
+              planted=("fixed", 0))
+    inp = W.generate(w)
+    meta = O.hier_meta_build(inp)
+    pi, lse = O.hier_row_shares(inp, meta, 0, 0)
+    q = inp.q[0].astype(np.float64)
+    ell = []
+    for lp in range(-(-300 // 16)):
+        K, _ = _dense_unpaged(inp, 0, 0, range(16 * lp, min(300, 16 * lp + 16)))
+        lo, hi = K.min(axis=0), K.max(axis=0)
+        ell.append(w.sm_scale * np.maximum(q * hi, q * lo).sum(axis=1) + np.log(len(K)))
+    ell = np.array(ell).T                                   # [G, n_logical]
+    tot = np.log(np.exp(ell).sum(axis=1))
+    assert np.allclose(lse, tot, rtol=0, atol=1e-12)
+    share_log = (np.exp(ell - tot[:, None])).mean(axis=0)
+    want = [share_log[4 * j:4 * j + 4].sum() for j in range(len(pi))]
+    assert np.allclose(pi, want, rtol=0, atol=1e-14)
+
+
+def test_coverage_gamma_one_lists_every_physical_page_and_equals_dense():
+    w = _hier(mode="coverage", gamma=1.0, n_local=1, seq_lens=(333, 64, 17))
+    inp = W.generate(w)
+    res = O.decode_step(inp)
+    G = w.group
+    for b, L in enumerate(w.seq_lens):
+        for h in range(w.num_kv_heads):
+            assert res["lists"][(b, h)] == list(range(-(-L // NP)))
+            K, V = _dense_unpaged(inp, b, h)
+            for g in range(G):
+                o_ref, lse_ref = _sdpa(inp.q[b, h * G + g].astype(np.float64), K, V, w.sm_scale)
+                assert np.allclose(res["O"][b, h * G + g], o_ref, rtol=0, atol=1e-12)
