@@ -288,8 +288,8 @@ __device__ __forceinline__ int row_logical_pages(int len, int max_pages, int lgs
 }
 
 __device__ __forceinline__ int row_phys_pages(int len, int max_pages, int lgs) {
-  const int P = kPage << lgs;
-  const int n = len > 0 ? (len + P - 1) / P : 0;
+  static_assert(kPage == 16, "pages are 2^4 tokens");
+  const int n = len > 0 ? (int)(((unsigned)len + (kPage << lgs) - 1) >> (4 + lgs)) : 0;  // shifts, no division
   return n < max_pages ? n : max_pages;
 }
 
