@@ -25,6 +25,10 @@ Pages and their definitions:
     tokens; each logical page keeps its own key min / max, and a physical page's
     importance is the largest importance of its logical pages; the top-K runs
     over physical pages and attention reads whole physical pages.
+  * LiteTopK (section 3.4, LiteDSA): several query tokens take their own top-k
+    lists, whose union is scanned once; a per-query membership mask keeps each
+    query's attention on exactly its own list.  Here the query tokens are the T
+    draft tokens of one decode step, each attending causally.
   * Moira (section 3.1 "Page summaries and the mvar estimate", Eq. 2): per page
     and KV head the channel-wise mean and variance of the keys; the page's
     estimated attention mass for query head g is
@@ -43,6 +47,10 @@ Readings where the pages leave a step open:
   * fp8 pools are OCP E4M3FN with a per-(page, head, token) fp16 scale; their key
     min / max is stored as fp16 rounded outward (max up, min down).
   * An empty row (no kept tokens) gives O = 0 and lse = -inf.
+  * Several query tokens per request (T draft tokens at positions L-T .. L-1 of a
+    request whose cache holds L keys): query t attends to positions < L - T + 1 + t
+    and selects its pages as a single query with that length would, from key
+    statistics that cover every cached key (the draft tokens' included).
   * Hierarchical paging: the GQA group is combined as above (max over query heads)
     after the max over logical pages; logical pages with no valid token do not
     enter the max; the budget, the sink and the local window count physical pages.
@@ -656,3 +664,54 @@ def decode_step(inp, meta: np.ndarray | None = None):
     sel = page_select(inp, meta)
     O, lse = sparse_paged_decode(inp, sel["lists"], inp.workload.sm_scale)
     return {"meta": meta, **sel, "O": O, "out_lse": lse}
+
+
+# --------------------------------------------------------------------------------------
+# Several query tokens per request (LiteDSA union with per-query membership masks)
+# --------------------------------------------------------------------------------------
+
+def mq_lengths(seq_len: int, T: int) -> list:
+    """Causal length of each of the T query tokens of a request whose cache holds seq_len keys."""
+    return [int(seq_len) - T + 1 + t for t in range(T)]
+
+
+def mq_token_inputs(inp, t: int):
+    """The single-query view of query token t: its queries and its causal lengths."""
+    import copy
+    T = inp.q.shape[1]
+    one = copy.copy(inp)
+    one.workload = inp.workload.replace(num_queries=1)
+    one.q = np.ascontiguousarray(inp.q[:, t])
+    one.seq_lens = np.array([mq_lengths(L, T)[t] for L in inp.seq_lens], dtype=inp.seq_lens.dtype)
+    return one
+
+
+def union_lists(lists_by_token: list) -> dict:
+    """LiteDSA candidate union: {(b, h): (ascending union of the T lists, mask per entry with bit t
+    set when the page is in token t's list)}."""
+    out = {}
+    for key in lists_by_token[0]:
+        pages = sorted(set().union(*[set(lt[key]) for lt in lists_by_token]))
+        masks = [sum(1 << t for t, lt in enumerate(lists_by_token) if p in set(lt[key])) for p in pages]
+        out[key] = (pages, masks)
+    return out
+
+
+def mq_decode_step(inp, meta: np.ndarray | None = None):
+    """Several query tokens per request: key statistics over every cached key, each token's own
+    selection over its causal prefix, the union of the lists, and each token's attention over its
+    own list (the union and masks change which pages are read, not what a query attends to).
+
+    Returns dict with 'lists_by_token' [T] of {(b,h): pages}, 'union' {(b,h): (pages, masks)},
+    'O' [B, T, Hq, d] and 'out_lse' [B, T, Hq]."""
+    if meta is None:
+        meta = page_meta_build(inp)
+    B, T, Hq, d = inp.q.shape
+    lists_by_token, O, lse = [], np.zeros((B, T, Hq, d)), np.full((B, T, Hq), -np.inf)
+    for t in range(T):
+        one = mq_token_inputs(inp, t)
+        sel = page_select(one, meta)
+        lists_by_token.append(sel["lists"])
+        O[:, t], lse[:, t] = sparse_paged_decode(one, sel["lists"], inp.workload.sm_scale)
+    return {"meta": meta, "lists_by_token": lists_by_token, "union": union_lists(lists_by_token), "O": O,
+            "out_lse": lse}

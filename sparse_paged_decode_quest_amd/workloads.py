@@ -77,6 +77,7 @@ class Workload:
     max_list: int | None = None
     shuffle_lengths: bool = False
     page_size: int = PAGE_SIZE  # physical page tokens (N_P): 16, or 64 over 16-token logical pages
+    num_queries: int = 1        # query tokens per request (T > 1: draft tokens verified in one step)
 
     @property
     def batch(self) -> int:
@@ -207,6 +208,15 @@ def named(name: str, seed_offset: int = 0) -> Workload:
                         head_dim=128, kv_dtype="f16", q_dtype="f16", mode="coverage", estimator="mvar",
                         gamma=0.99, n_sink=1, n_local=1, planted=("loguniform", 20, 2000),
                         delta=("nats", 12.0), seed=BASE_SEED + 6 + seed_offset)
+    if name == "mtp4_b1_128k_f16":
+        # the 128k layer verifying 4 draft tokens in one step (speculative decoding): each query token
+        # selects its own 256 pages over its causal prefix, and the four lists share one scan (LiteDSA
+        # union with per-query membership masks)
+        return Workload(name=name, seq_lens=(131072,), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        kv_dtype="f16", q_dtype="f16", mode="topk", budget_pages=256, num_queries=4,
+                        n_sink=1, n_local=2, n_sink_stream=4, n_local_stream=16,
+                        streaming_heads=(0, 1, 2, 3), planted=("fixed", 64), delta=2.0,
+                        seed=BASE_SEED + 8 + seed_offset)
     if name == "llama3_8b_b1_128k_f16_hier64":
         # the 128k layer with 64-token physical pages scored through 16-token logical pages (LServe,
         # "Hierarchical Paging", N_P = 64, N_L = 16): token budget 4096 = 64 physical pages
@@ -222,7 +232,7 @@ def named(name: str, seed_offset: int = 0) -> Workload:
 
 NAMED = ("tiny_b1_hq8_d64_4k_f32", "llama3_8b_b1_128k_f16", "mixed_b8_bimodal_f16",
          "mixed_b8_powerlaw_f16", "coverage_b4_128k_f16", "fp8_b1_512k", "llama3_8b_b1_128k_f16_dense",
-         "coverage_mvar_b4_128k_f16", "llama3_8b_b1_128k_f16_hier64")
+         "coverage_mvar_b4_128k_f16", "llama3_8b_b1_128k_f16_hier64", "mtp4_b1_128k_f16")
 
 
 # --------------------------------------------------------------------------------------
@@ -266,8 +276,9 @@ def generate(w: Workload, seed: int | None = None) -> Inputs:
     n_pages = w.n_pages
     maxp = w.pages_per_seq
 
-    # queries: float64 draw, stored in the query dtype
-    q = rng.standard_normal((B, Hq, d)).astype(_np_dtype(w.q_dtype))
+    # queries: float64 draw, stored in the query dtype; T > 1 query tokens per request: [B, T, Hq, d]
+    T = w.num_queries
+    q = rng.standard_normal((B, Hq, d) if T == 1 else (B, T, Hq, d)).astype(_np_dtype(w.q_dtype))
 
     # block table: seeded permutation of the physical universe, consecutive slices
     total = int(n_pages.sum())
@@ -312,7 +323,7 @@ def generate(w: Workload, seed: int | None = None) -> Inputs:
                 planted[(b, h)] = np.zeros(0, dtype=np.int64)
                 continue
             pages = np.sort(rng.choice(candidates, size=n_plant, replace=False))
-            qs = qf[b, h * G:(h + 1) * G]
+            qs = qf[b, h * G:(h + 1) * G] if T == 1 else qf[b, :, h * G:(h + 1) * G].reshape(T * G, d)
             u = qs.sum(axis=0)
             u = u / np.linalg.norm(u)
             if isinstance(w.delta, tuple):

@@ -18,7 +18,8 @@ def say(*a):
     print(*a, flush=True)
 
 
-@pytest.mark.parametrize("name", [n for n in W.NAMED if W.named(n).page_size == 16])  # 64-token pages: test_gpu_hier.py
+# 64-token pages: test_gpu_hier.py; several query tokens per request: test_gpu_mq.py
+@pytest.mark.parametrize("name", [n for n in W.NAMED if W.named(n).page_size == 16 and W.named(n).num_queries == 1])
 def test_named_workload(name):
     assert torch.cuda.is_available()
     A.lib()
