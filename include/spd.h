@@ -97,7 +97,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 7
+#define SPD_ABI_VERSION 8
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
@@ -339,6 +339,56 @@ int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, c
 int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float* part_o,
                   const float* part_lse, const int32_t* list_len, float* out, float* out_lse,
                   void* stream);
+
+/* ------------------------------------------------------------------ several query tokens per request
+ *
+ * One step for T <= SPD_MQ_MAX_TOKENS query tokens per request -- the draft tokens that
+ * speculative decoding verifies at once -- with their page lists shared as one scan (LiteTopK,
+ * section 3.4, LiteDSA: "Candidate Union and Membership Masks", "Grouped Sparse Attention").
+ * Request b's cache holds seq_lens[b] = L keys, the draft tokens' included; query token t sits at
+ * position L - T + t and attends to positions < L - T + 1 + t.  The caller selects each token's
+ * pages with spd_page_score / spd_page_select on a descriptor of B * T rows (row b T + t: token t's
+ * queries, request b's block-table row, seq_lens L - T + 1 + t, key statistics covering all L
+ * keys), then merges them with spd_page_list_union and attends with spd_sparse_paged_decode_mq
+ * and spd_lse_merge_mq.  Supported: page_size 16, max_pages_per_seq <= SPD_MQ_MAX_PAGES; decode
+ * and merge need f16 queries and pools, head_dim 128 and the per-row plan (balanced = 0). */
+#define SPD_MQ_MAX_TOKENS 4
+#define SPD_MQ_ROWS 16          /* chunk-state rows per (request, KV head): 4 tokens x G = 4 */
+#define SPD_MQ_MAX_PAGES 32768
+
+/* Union of the T token lists of every (request, KV head) row (LiteDSA's candidate union).
+ * desc describes the B requests (max_list: the union's capacity, at least
+ * min(T * token_max_list, max_pages_per_seq)).  token_list (device, [B * T, Hkv, token_max_list])
+ * and token_len (device, [B * T, Hkv]) are the tokens' lists as spd_page_select writes them; entries
+ * outside [0, n_b) of the request are ignored.  Writes page_list (device, [B, Hkv, max_list]) in
+ * ascending page order, page_mask (device, same shape, uint32: bit t set when token t listed the
+ * page), list_len (device, [B, Hkv]) and, when page_phys (device, may be NULL) is set, the
+ * physical page of each entry from block_table.  Errors as elsewhere; num_tokens outside
+ * [1, SPD_MQ_MAX_TOKENS] is SPD_ERR_INVALID_ARG. */
+int spd_page_list_union(const spd_desc* desc, int32_t num_tokens, int32_t token_max_list,
+                        const int32_t* token_list, const int32_t* token_len, const int32_t* block_table,
+                        const int32_t* seq_lens, int32_t* page_list, int32_t* page_phys,
+                        uint32_t* page_mask, int32_t* list_len, void* stream);
+
+/* Decode attention of the T query tokens of every row over the union list: q (device,
+ * [B, T, Hq, d] f16), out (device, [B, T, Hq, d] f32), out_lse (device, [B, T, Hq] f32).  Each
+ * union page is read once for all T x G query rows; row (t, g) keeps the page only when bit t of
+ * its mask is set, and only positions < L - T + 1 + t.  Split as spd_sparse_paged_decode's per-row
+ * plan over the union lengths; rows with more than one chunk write part_o (device,
+ * [B, Hkv, J, SPD_MQ_ROWS, d] f32) and part_lse ([B, Hkv, J, SPD_MQ_ROWS] f32) for
+ * spd_lse_merge_mq.  A row with an empty union, or a token with no kept key, writes out = 0 and
+ * out_lse = -inf.  page_phys may be NULL (then block_table is read). */
+int spd_sparse_paged_decode_mq(const spd_desc* desc, int32_t num_tokens, const spd_plan_params* plan,
+                               const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* page_list, const int32_t* page_phys,
+                               const uint32_t* page_mask, const int32_t* list_len, float sm_scale,
+                               float* out, float* out_lse, float* part_o, float* part_lse, void* stream);
+
+/* spd_lse_merge for spd_sparse_paged_decode_mq's chunk states (same plan and list_len). */
+int spd_lse_merge_mq(const spd_desc* desc, int32_t num_tokens, const spd_plan_params* plan,
+                     const float* part_o, const float* part_lse, const int32_t* list_len, float* out,
+                     float* out_lse, void* stream);
 
 /* ------------------------------------------------------------------ host helpers */
 

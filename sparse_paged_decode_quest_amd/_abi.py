@@ -29,7 +29,9 @@ ESTIMATOR_BOUND, ESTIMATOR_MVAR = 0, 1
 
 EXPORTS = ("spd_page_meta_build", "spd_page_stats_build", "spd_page_score", "spd_page_select", "spd_page_score_select",
            "spd_sparse_paged_decode", "spd_lse_merge", "spd_plan_grid", "spd_plan_chunks", "spd_page_list_refresh",
-           "spd_partials_size", "spd_workspace_bytes", "spd_error_string", "spd_abi_version")
+           "spd_partials_size", "spd_workspace_bytes", "spd_error_string", "spd_abi_version",
+           "spd_page_list_union", "spd_sparse_paged_decode_mq", "spd_lse_merge_mq")
+MQ_ROWS = 16  # chunk-state rows per (request, KV head) of the several-query decode
 
 
 class SpdError(RuntimeError):
@@ -77,6 +79,9 @@ def lib():
                                             c_size_t, v]
         L.spd_sparse_paged_decode.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v]
         L.spd_lse_merge.argtypes = [D, P, v, v, v, v, v, v]
+        L.spd_page_list_union.argtypes = [D, c_int32, c_int32, v, v, v, v, v, v, v, v, v]
+        L.spd_sparse_paged_decode_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v]
+        L.spd_lse_merge_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v]
         L.spd_plan_grid.argtypes = [D, P, POINTER(c_int32)]
         L.spd_plan_chunks.argtypes = [c_int32, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32)]
         L.spd_partials_size.argtypes = [D, P, POINTER(c_size_t), POINTER(c_size_t)]
@@ -185,6 +190,29 @@ def spd_sparse_paged_decode(desc, plan, q, k_pool, v_pool, k_scale, v_scale, blo
 def spd_lse_merge(desc, plan, part_o, part_lse, list_len, out, out_lse, stream=None):
     _check(lib().spd_lse_merge(ctypes.byref(desc), ctypes.byref(plan), _ptr(part_o), _ptr(part_lse),
                                _ptr(list_len), _ptr(out), _ptr(out_lse), _stream(stream)), "spd_lse_merge")
+
+
+def spd_page_list_union(desc, num_tokens, token_max_list, token_list, token_len, block_table, seq_lens, page_list,
+                        page_phys, page_mask, list_len, stream=None):
+    _check(lib().spd_page_list_union(ctypes.byref(desc), int(num_tokens), int(token_max_list), _ptr(token_list),
+                                     _ptr(token_len), _ptr(block_table), _ptr(seq_lens), _ptr(page_list),
+                                     _ptr(page_phys), _ptr(page_mask), _ptr(list_len), _stream(stream)),
+           "spd_page_list_union")
+
+
+def spd_sparse_paged_decode_mq(desc, num_tokens, plan, q, k_pool, v_pool, block_table, seq_lens, page_list,
+                               page_phys, page_mask, list_len, sm_scale, out, out_lse, part_o, part_lse, stream=None):
+    _check(lib().spd_sparse_paged_decode_mq(ctypes.byref(desc), int(num_tokens), ctypes.byref(plan), _ptr(q),
+                                            _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                                            _ptr(page_list), _ptr(page_phys), _ptr(page_mask), _ptr(list_len),
+                                            float(sm_scale), _ptr(out), _ptr(out_lse), _ptr(part_o), _ptr(part_lse),
+                                            _stream(stream)), "spd_sparse_paged_decode_mq")
+
+
+def spd_lse_merge_mq(desc, num_tokens, plan, part_o, part_lse, list_len, out, out_lse, stream=None):
+    _check(lib().spd_lse_merge_mq(ctypes.byref(desc), int(num_tokens), ctypes.byref(plan), _ptr(part_o),
+                                  _ptr(part_lse), _ptr(list_len), _ptr(out), _ptr(out_lse), _stream(stream)),
+           "spd_lse_merge_mq")
 
 
 def spd_plan_grid(desc, plan) -> int:

@@ -1,0 +1,335 @@
+// Several query tokens per request in one decode step (the T <= 4 draft tokens of speculative
+// decoding), with the lists of the tokens shared as one scan: LiteTopK, section 3.4 (LiteDSA,
+// "Candidate Union and Membership Masks", "Grouped Sparse Attention").  Each query token t has
+// its own page list (selected as a single query with its causal length); the lists of a
+// (request, KV head) row are merged into one ascending union with a bit mask per entry (bit t:
+// the page is in token t's list), and attention reads each union page once for all T x G query
+// rows, masking out the rows whose token did not select the page.
+//
+// Decode work layout (one 16-token page per wave, four waves per workgroup, Moira Eq. 4 split):
+//  * logits: the page's 16 x 16 tile S[row = 4 t + g][token] is one chain of eight
+//    v_mfma_f32_16x16x16_f16 over the 128 channels.  The channel order inside the chain is
+//    permuted so that every lane's operands are contiguous: lane l holds channels
+//    32 (l / 16) .. 32 (l / 16) + 31 of query row l % 16 (A) and of key l % 16 (B), and step s
+//    takes channels 32 (l / 16) + 4 s .. + 3 of both.  The result puts rows 4 q .. 4 q + 3 (token
+//    t = q) of key l % 16 in lane l, so each query token's rows sit in one 16-lane DPP row;
+//  * masks: bit t of the page's mask, the token's causal limit (positions < len - T + 1 + t)
+//    and the request's length, before the online softmax (fp32, base 2);
+//  * PV on the VALU: probabilities go through LDS (1 KiB per wave) and every lane accumulates
+//    its two channels for all 16 rows from the page's V rows (16 coalesced 256-byte rows).
+#include "spd_device.h"
+#include "spd_launch.h"
+
+namespace spd {
+
+constexpr int kMqG = 4;      // query heads per KV head
+constexpr int kMqRows = 16;  // 4 query tokens x G = 4 heads
+constexpr int kUnionThreads = 1024;
+
+__device__ __forceinline__ int mq_clamp(int n, int hi) { return n < 0 ? 0 : (n > hi ? hi : n); }
+
+// One workgroup per (request, KV head): a byte per page of the request in LDS collects the
+// tokens' bits (atomicOr on the word holding it), then an ordered compaction writes the union.
+__global__ __launch_bounds__(kUnionThreads) void page_list_union_kernel(UnionArgs a) {
+  extern __shared__ uint32_t bits[];  // ceil(max_pages / 4) words
+  __shared__ uint32_t wsum[kUnionThreads / kWave];
+  const int row = blockIdx.x;
+  const int b = row / a.num_kv_heads, h = row % a.num_kv_heads;
+  const int n = row_pages(a.seq_lens[b], a.max_pages);
+  for (int i = threadIdx.x; i < (n + 3) / 4; i += kUnionThreads) bits[i] = 0u;
+  __syncthreads();
+  for (int t = 0; t < a.num_tokens; ++t) {
+    const size_t trow = ((size_t)b * a.num_tokens + t) * a.num_kv_heads + h;
+    const int len = mq_clamp(a.token_len[trow], a.token_max_list);
+    const int32_t* lst = a.token_list + trow * a.token_max_list;
+    for (int i = threadIdx.x; i < len; i += kUnionThreads) {
+      const int p = lst[i];
+      if (p >= 0 && p < n) atomicOr(&bits[p >> 2], 1u << ((p & 3) * 8 + t));
+    }
+  }
+  __syncthreads();
+  // thread k owns pages [k per, (k + 1) per): count, block scan, write in page order
+  const int per = (n + kUnionThreads - 1) / kUnionThreads;
+  const int p0 = (int)threadIdx.x * per;
+  uint32_t cnt = 0;
+  for (int i = 0; i < per; ++i) {
+    const int p = p0 + i;
+    if (p < n && ((bits[p >> 2] >> ((p & 3) * 8)) & 0xffu)) ++cnt;
+  }
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const uint32_t incl = wave_incl_scan(cnt);
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  uint32_t pos = base + incl - cnt;
+  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+  const size_t out_row = (size_t)row * a.max_list;
+  for (int i = 0; i < per; ++i) {
+    const int p = p0 + i;
+    if (p >= n) break;
+    const uint32_t m = (bits[p >> 2] >> ((p & 3) * 8)) & 0xffu;
+    if (!m) continue;
+    if (pos < (uint32_t)a.max_list) {
+      a.page_list[out_row + pos] = p;
+      a.page_mask[out_row + pos] = m;
+      if (a.page_phys) a.page_phys[out_row + pos] = bt_row[p];
+    }
+    ++pos;
+  }
+  if (threadIdx.x == kUnionThreads - 1) a.list_len[row] = (int)min(base + incl, (uint32_t)a.max_list);
+}
+
+typedef _Float16 mq_half4 __attribute__((ext_vector_type(4)));
+typedef float mq_float4 __attribute__((ext_vector_type(4)));
+
+struct MqPage {
+  int page;  // logical page, -1 when the entry is not usable
+  int phys;
+  uint32_t mask;
+  int valid;
+};
+
+// One page's K operand (lane: key l % 16, channels 32 (l / 16) .. + 31) and V rows (lane: channels
+// 2 l, 2 l + 1 of every key).
+struct MqKV {
+  uint4 k[4];
+  uint32_t v[kPage];
+};
+
+template <int D>
+__device__ __forceinline__ void mq_load(const MqDecodeArgs& a, const MqPage& r, int h, MqKV& kv) {
+  if (r.page < 0) return;
+  const int lane = threadIdx.x % kWave;
+  const size_t head_page = (size_t)r.phys * a.num_kv_heads + h;
+  const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.k_pool) +
+                                                   (head_page * kPage + (lane & 15)) * D + 32 * (lane >> 4));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kv.k[i] = ld_stream(kp + i);
+  const uint32_t* vp = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(a.v_pool) +
+                                                         head_page * kPage * D) + lane;
+#pragma unroll
+  for (int t = 0; t < kPage; ++t) kv.v[t] = ld_stream(vp + t * (D / 2));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
+  static_assert(D == 128, "the logit tile covers 128 channels: 4 lane groups x 32");
+  __shared__ float p_lds[4][kPage][kMqRows];
+  __shared__ float ws_m[4][kMqRows], ws_l[4][kMqRows];
+  __shared__ float ws_acc[4][kMqRows][D];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int tok = lane & 15;  // logit role: key of the page
+  const int q4 = lane >> 4;   // logit role: query token of rows 4 q4 .. 4 q4 + 3
+  const int row = blockIdx.x / a.blocks_per_row;
+  const int j = blockIdx.x % a.blocks_per_row;
+  const int b = row / a.num_kv_heads;
+  const int h = row % a.num_kv_heads;
+  const int T = a.num_tokens;
+  auto out_row = [&](int t, int g) { return ((size_t)b * T + t) * a.num_q_heads + (size_t)h * kMqG + g; };
+
+  const int n = mq_clamp(a.list_len[row], a.max_list);
+  if (n == 0) {
+    if (j == 0) {
+      for (int e = threadIdx.x; e < T * kMqG * D; e += blockDim.x)
+        a.out[out_row(e / (kMqG * D), (e / D) % kMqG) * D + e % D] = 0.f;
+      if ((int)threadIdx.x < T * kMqG) a.out_lse[out_row(threadIdx.x / kMqG, threadIdx.x % kMqG)] = -INFINITY;
+    }
+    return;
+  }
+  int c, m;
+  plan_chunks(n, a.blocks_per_row, a.min_chunk, c, m);
+  if (j >= m) return;
+  const int i0 = j * c;
+  const int i1 = min(n, i0 + c);
+  const int len = a.seq_lens[b];
+  const int n_b = row_pages(len, a.max_pages);
+  const int lim = len - T + 1 + q4;  // keys this lane's query token may see: positions < lim
+
+  // A operand: query row l % 16 = (t_a, g_a), channels 32 q4 .. 32 q4 + 31
+  const int t_a = tok >> 2, g_a = tok & 3;
+  mq_half4 qa[8];
+  {
+    uint4 w[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    if (t_a < T) {
+      const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + out_row(t_a, g_a) * D +
+                                                       32 * q4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = qp[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qa[2 * i] = __builtin_bit_cast(mq_half4, make_uint2(w[i].x, w[i].y));
+      qa[2 * i + 1] = __builtin_bit_cast(mq_half4, make_uint2(w[i].z, w[i].w));
+    }
+  }
+
+  float m_run[4], l_run[4];
+  float acc[kMqRows][2];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    m_run[jj] = -INFINITY;
+    l_run[jj] = 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < kMqRows; ++r) acc[r][0] = acc[r][1] = 0.f;
+
+  auto process = [&](const MqPage& r, const MqKV& kv) {
+    if (r.page < 0) return;
+    mq_float4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[2 * i], __builtin_bit_cast(mq_half4, make_uint2(kv.k[i].x, kv.k[i].y)),
+                                                s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[2 * i + 1],
+                                                __builtin_bit_cast(mq_half4, make_uint2(kv.k[i].z, kv.k[i].w)), s, 0, 0, 0);
+    }
+    const bool ok = q4 < T && ((r.mask >> q4) & 1u) && r.page * kPage + tok < lim && tok < r.valid;
+    float p[4], alpha[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float x = ok ? s[jj] * a.sm_scale_log2 : -INFINITY;
+      const float m_new = fmaxf(m_run[jj], row_max(x));
+      alpha[jj] = m_new == -INFINITY ? 1.f : exp2f(m_run[jj] - m_new);
+      p[jj] = m_new == -INFINITY ? 0.f : exp2f(x - m_new);
+      l_run[jj] = l_run[jj] * alpha[jj] + p[jj];
+      m_run[jj] = m_new;
+    }
+    *reinterpret_cast<float4*>(&p_lds[wave][tok][4 * q4]) = make_float4(p[0], p[1], p[2], p[3]);
+    float al[kMqRows];  // every row's rescale, read from the lane group that owns the row
+#pragma unroll
+    for (int rr = 0; rr < kMqRows; ++rr)
+      al[rr] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[rr & 3]), 16 * (rr >> 2)));
+    wave_fence();
+#pragma unroll
+    for (int rr = 0; rr < kMqRows; ++rr) {
+      acc[rr][0] *= al[rr];
+      acc[rr][1] *= al[rr];
+    }
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) {
+      const float4* pr = reinterpret_cast<const float4*>(p_lds[wave][t]);
+      const float4 p0 = pr[0], p1 = pr[1], p2 = pr[2], p3 = pr[3];
+      const float pv[kMqRows] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w,
+                                 p2.x, p2.y, p2.z, p2.w, p3.x, p3.y, p3.z, p3.w};
+      const __half2 vh = __builtin_bit_cast(__half2, kv.v[t]);
+      const float v0 = t < r.valid ? __low2float(vh) : 0.f;  // slots past the request's end may hold NaN
+      const float v1 = t < r.valid ? __high2float(vh) : 0.f;
+#pragma unroll
+      for (int rr = 0; rr < kMqRows; ++rr) {
+        acc[rr][0] = fmaf(pv[rr], v0, acc[rr][0]);
+        acc[rr][1] = fmaf(pv[rr], v1, acc[rr][1]);
+      }
+    }
+    wave_fence();
+  };
+
+  // This wave's entries are i0 + wave, i0 + wave + 4, ...; their list entries, masks and physical
+  // pages are read 64 at a time (one per lane) before the K / V loads; pages alternate between two
+  // register stages so the next page's loads are in flight while the current one is computed.
+  const int32_t* list = a.page_list + (size_t)row * a.max_list;
+  const uint32_t* mlist = a.page_mask + (size_t)row * a.max_list;
+  const int32_t* plist = a.page_phys ? a.page_phys + (size_t)row * a.max_list : nullptr;
+  const int my_pages = i1 - i0 > wave ? (i1 - i0 - wave + 3) / 4 : 0;
+  auto page_at = [&](int lp, int lph, uint32_t lm, int u) {
+    MqPage r{-1, 0, 0u, 0};
+    const int p = __builtin_amdgcn_readlane(lp, u);
+    const int phys = __builtin_amdgcn_readlane(lph, u);
+    if (p < 0 || p >= n_b || phys < 0 || phys >= a.num_pool_pages) return r;
+    r.page = p;
+    r.phys = phys;
+    r.mask = (uint32_t)__builtin_amdgcn_readlane((int)lm, u);
+    r.valid = valid_in_page(len, p);
+    return r;
+  };
+  MqKV ka, kb;
+  for (int bb = 0; bb < my_pages; bb += kWave) {
+    const int cnt = min(kWave, my_pages - bb);
+    const int idx = i0 + wave + 4 * (bb + lane);
+    int lp = -1, lph = -1;
+    uint32_t lm = 0u;
+    if (lane < cnt) {
+      lp = list[idx];
+      lm = mlist[idx];
+      if (plist) lph = plist[idx];
+      else if (lp >= 0 && lp < n_b) lph = a.block_table[(size_t)b * a.max_pages + lp];
+    }
+    MqPage ra = page_at(lp, lph, lm, 0), rb;
+    mq_load<D>(a, ra, h, ka);
+    for (int u = 0; u < cnt; u += 2) {
+      if (u + 1 < cnt) {
+        rb = page_at(lp, lph, lm, u + 1);
+        mq_load<D>(a, rb, h, kb);
+      }
+      process(ra, ka);
+      if (u + 1 >= cnt) break;
+      if (u + 2 < cnt) {
+        ra = page_at(lp, lph, lm, u + 2);
+        mq_load<D>(a, ra, h, ka);
+      }
+      process(rb, kb);
+    }
+  }
+
+  // wave states -> LDS (row 4 q4 + jj is held by lane group q4; its sum spans the group's 16 lanes)
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const float lt = row_sum(l_run[jj]);
+    if (tok == 0) {
+      ws_m[wave][4 * q4 + jj] = m_run[jj];
+      ws_l[wave][4 * q4 + jj] = lt;
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < kMqRows; ++rr) {
+    ws_acc[wave][rr][2 * lane] = acc[rr][0];
+    ws_acc[wave][rr][2 * lane + 1] = acc[rr][1];
+  }
+  __syncthreads();
+
+  // merge the four wave states (fixed order); write the chunk result of the rows of tokens < T
+  for (int e = threadIdx.x; e < T * kMqG * D; e += blockDim.x) {
+    const int rr = e / D, ch = e % D;
+    float M = ws_m[0][rr];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, ws_m[w][rr]);
+    float o = 0.f, lse = -INFINITY;
+    if (M != -INFINITY) {
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sc = exp2f(ws_m[w][rr] - M);
+        L = fmaf(ws_l[w][rr], sc, L);
+        A = fmaf(ws_acc[w][rr][ch], sc, A);
+      }
+      o = A / L;
+      lse = (M + log2f(L)) * kLn2;
+    }
+    if (m == 1) {
+      const size_t orow = out_row(rr / kMqG, rr % kMqG);
+      a.out[orow * D + ch] = o;
+      if (ch == 0) a.out_lse[orow] = lse;
+    } else {
+      const size_t slot = ((size_t)row * a.blocks_per_row + j) * kMqRows + rr;
+      a.part_o[slot * D + ch] = o;
+      if (ch == 0) a.part_lse[slot] = lse;
+    }
+  }
+}
+
+int launch_page_list_union(const UnionArgs& a, hipStream_t stream) {
+  const size_t lds = (size_t)((a.max_pages + 3) / 4) * sizeof(uint32_t);
+  hipLaunchKernelGGL(page_list_union_kernel, dim3((unsigned)(a.batch * a.num_kv_heads)), dim3(kUnionThreads), lds,
+                     stream, a);
+  return 0;
+}
+
+int launch_mq_decode(const MqDecodeArgs& a, int head_dim, hipStream_t stream) {
+  if (head_dim != 128) return SPD_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(mq_decode_kernel<128>, dim3((unsigned)(a.batch * a.num_kv_heads * a.blocks_per_row)), dim3(256),
+                     0, stream, a);
+  return 0;
+}
+
+}  // namespace spd

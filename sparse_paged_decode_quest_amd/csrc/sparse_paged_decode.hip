@@ -558,10 +558,14 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
   __shared__ float w_s[kMaxChunks];
   __shared__ float red[kMergeThreads / kWave];
   __shared__ float part_s[PARTS][D];
-  const int row = blockIdx.x / kGq;
-  const int g = blockIdx.x % kGq;
+  // block (row, r): chunk-state row r of (request, KV head) row `row`; with several query tokens per
+  // request r = t G + g (token t, head g of the group) and the output is [B, T, Hq, d]
+  const int R = a.rows_per_head;
+  const int row = blockIdx.x / R;
+  const int r = blockIdx.x % R;
   const int b = row / a.num_kv_heads;
   const int h = row % a.num_kv_heads;
+  if (r >= a.num_tokens * kGq) return;  // rows of absent query tokens (uniform over the block)
   const int J = a.blocks_per_row;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int ch = threadIdx.x % D, part = threadIdx.x / D;
@@ -574,7 +578,7 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
     c = balanced_chunk(a.list_len, rows, a.max_list, a.min_chunk, a.grid_target, a.lgs);
     balanced_row(a.list_len, rows, a.max_list, c, row, first, m, a.lgs);
   }
-  const size_t slot0 = (a.balanced ? (size_t)first : (size_t)row * J) * kGq + g;  // + j * kGq
+  const size_t slot0 = (a.balanced ? (size_t)first : (size_t)row * J) * R + r;  // + j * R
   const int J_read = a.balanced ? m : J;  // chunk slots of the row that may be read
 
   // speculative loads (per-row plan: before the row's chunk count is known): chunk lse values,
@@ -583,13 +587,13 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int k = 0; k < (kMaxChunks + kMergeThreads - 1) / kMergeThreads; ++k) {
     const int jj = (int)threadIdx.x + k * kMergeThreads;
-    lse_j[k] = jj < J_read ? a.part_lse[slot0 + (size_t)jj * kGq] : -INFINITY;
+    lse_j[k] = jj < J_read ? a.part_lse[slot0 + (size_t)jj * R] : -INFINITY;
   }
   float pre[kPre];
 #pragma unroll
   for (int u = 0; u < kPre; ++u) {
     const int jj = part + u * PARTS;
-    pre[u] = jj < J_read ? a.part_o[(slot0 + (size_t)jj * kGq) * D + ch] : 0.f;
+    pre[u] = jj < J_read ? a.part_o[(slot0 + (size_t)jj * R) * D + ch] : 0.f;
   }
   if (!a.balanced) plan_chunks(clamp_len(n, a.max_list) << a.lgs, J, a.min_chunk, c, m);
   if (m <= 1) return;
@@ -608,7 +612,7 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
   __syncthreads();
   const float M = wave_max_f(lane < kMergeThreads / kWave ? red[lane] : -INFINITY);  // one read per lane
   __syncthreads();
-  const size_t qrow = (size_t)b * a.num_q_heads + (size_t)h * kGq + g;
+  const size_t qrow = ((size_t)b * a.num_tokens + r / kGq) * a.num_q_heads + (size_t)h * kGq + r % kGq;
   if (M == -INFINITY) {
     for (int e = threadIdx.x; e < D; e += kMergeThreads) a.out[qrow * D + e] = 0.f;
     if (threadIdx.x == 0) a.out_lse[qrow] = -INFINITY;
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
     if (jj < m) acc = fmaf(w_s[jj], pre[u], acc);
   }
   for (int jj = part + kPre * PARTS; jj < m; jj += PARTS)
-    acc = fmaf(w_s[jj], a.part_o[(slot0 + (size_t)jj * kGq) * D + ch], acc);
+    acc = fmaf(w_s[jj], a.part_o[(slot0 + (size_t)jj * R) * D + ch], acc);
   part_s[part][ch] = acc;
   __syncthreads();
   if (threadIdx.x < D) {
@@ -662,7 +666,7 @@ int launch_sparse_paged_decode(const DecodeArgs& a, int head_dim, int q_dtype, i
 }
 
 int launch_lse_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
-  dim3 grid((unsigned)(a.batch * a.num_kv_heads * kGq)), block(kMergeThreads);
+  dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.rows_per_head)), block(kMergeThreads);
   if (head_dim == 64) hipLaunchKernelGGL(lse_merge_kernel<64>, grid, block, 0, stream, a);
   else if (head_dim == 128) hipLaunchKernelGGL(lse_merge_kernel<128>, grid, block, 0, stream, a);
   else return SPD_ERR_UNSUPPORTED;

@@ -541,6 +541,119 @@ int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float
   a.balanced = plan->balanced;
   a.grid_target = plan->min_grid_blocks;
   a.lgs = lgs_of(desc);
+  a.rows_per_head = desc->num_q_heads / desc->num_kv_heads;
+  a.num_tokens = 1;
+  return launched(spd::launch_lse_merge(a, desc->head_dim, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ several query tokens per request
+
+static int check_mq(const spd_desc* d, int32_t num_tokens) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (num_tokens < 1 || num_tokens > SPD_MQ_MAX_TOKENS) return SPD_ERR_INVALID_ARG;
+  if (is_hier(d) || d->max_pages_per_seq > SPD_MQ_MAX_PAGES) return SPD_ERR_UNSUPPORTED;
+  return SPD_OK;
+}
+
+int spd_page_list_union(const spd_desc* desc, int32_t num_tokens, int32_t token_max_list, const int32_t* token_list,
+                        const int32_t* token_len, const int32_t* block_table, const int32_t* seq_lens,
+                        int32_t* page_list, int32_t* page_phys, uint32_t* page_mask, int32_t* list_len,
+                        void* stream) {
+  int rc = check_mq(desc, num_tokens);
+  if (rc) return rc;
+  if (token_max_list < 1) return SPD_ERR_INVALID_ARG;
+  // the union of T lists of at most token_max_list pages each, within the request's pages
+  if ((int64_t)desc->max_list < std::min<int64_t>((int64_t)num_tokens * token_max_list, desc->max_pages_per_seq))
+    return SPD_ERR_INVALID_ARG;
+  if (desc->batch == 0) return SPD_OK;
+  if (!token_list || !token_len || !seq_lens || !page_list || !page_mask || !list_len) return SPD_ERR_INVALID_ARG;
+  if (page_phys && !block_table) return SPD_ERR_INVALID_ARG;
+  spd::UnionArgs a{};
+  a.token_list = token_list;
+  a.token_len = token_len;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.page_list = page_list;
+  a.page_phys = page_phys;
+  a.page_mask = page_mask;
+  a.list_len = list_len;
+  a.batch = desc->batch;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.max_pages = desc->max_pages_per_seq;
+  a.max_list = desc->max_list;
+  a.num_tokens = num_tokens;
+  a.token_max_list = token_max_list;
+  return launched(spd::launch_page_list_union(a, (hipStream_t)stream));
+}
+
+int spd_sparse_paged_decode_mq(const spd_desc* desc, int32_t num_tokens, const spd_plan_params* plan, const void* q,
+                               const void* k_pool, const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* page_list, const int32_t* page_phys,
+                               const uint32_t* page_mask, const int32_t* list_len, float sm_scale, float* out,
+                               float* out_lse, float* part_o, float* part_lse, void* stream) {
+  int rc = check_mq(desc, num_tokens);
+  if (rc) return rc;
+  int32_t J;
+  if ((rc = plan_j(desc, plan, J))) return rc;
+  if (plan->balanced) return SPD_ERR_UNSUPPORTED;
+  if (desc->kv_dtype != SPD_DTYPE_F16 || desc->head_dim != 128) return SPD_ERR_UNSUPPORTED;
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return SPD_ERR_INVALID_ARG;
+  if (desc->batch == 0) return SPD_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !page_list || !page_mask || !list_len || !out ||
+      !out_lse || !part_o || !part_lse)
+    return SPD_ERR_INVALID_ARG;
+  spd::MqDecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.page_list = page_list;
+  a.page_phys = page_phys;
+  a.page_mask = page_mask;
+  a.list_len = list_len;
+  a.out = out;
+  a.out_lse = out_lse;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.batch = desc->batch;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.max_pages = desc->max_pages_per_seq;
+  a.num_pool_pages = desc->num_pool_pages;
+  a.max_list = desc->max_list;
+  a.num_tokens = num_tokens;
+  a.blocks_per_row = J;
+  a.min_chunk = plan->min_chunk;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  return launched(spd::launch_mq_decode(a, desc->head_dim, (hipStream_t)stream));
+}
+
+int spd_lse_merge_mq(const spd_desc* desc, int32_t num_tokens, const spd_plan_params* plan, const float* part_o,
+                     const float* part_lse, const int32_t* list_len, float* out, float* out_lse, void* stream) {
+  int rc = check_mq(desc, num_tokens);
+  if (rc) return rc;
+  int32_t J;
+  if ((rc = plan_j(desc, plan, J))) return rc;
+  if (plan->balanced) return SPD_ERR_UNSUPPORTED;
+  if (desc->head_dim != 128) return SPD_ERR_UNSUPPORTED;
+  if (desc->batch == 0) return SPD_OK;
+  if (!part_o || !part_lse || !list_len || !out || !out_lse) return SPD_ERR_INVALID_ARG;
+  spd::MergeArgs a{};
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.list_len = list_len;
+  a.out = out;
+  a.out_lse = out_lse;
+  a.batch = desc->batch;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.max_list = desc->max_list;
+  a.blocks_per_row = J;
+  a.min_chunk = plan->min_chunk;
+  a.rows_per_head = SPD_MQ_ROWS;
+  a.num_tokens = num_tokens;
   return launched(spd::launch_lse_merge(a, desc->head_dim, (hipStream_t)stream));
 }
 

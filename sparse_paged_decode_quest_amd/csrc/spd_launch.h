@@ -145,8 +145,44 @@ struct MergeArgs {
   int batch, num_q_heads, num_kv_heads, max_list, blocks_per_row, min_chunk;
   int balanced, grid_target;
   int lgs;  // as in DecodeArgs
+  int rows_per_head;  // chunk-state rows per (request, KV head): G, or 16 for several query tokens
+  int num_tokens;     // query tokens per request (outputs [B, T, Hq, d]); rows r >= T * G are not merged
 };
 int launch_lse_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+
+// Several query tokens per request (mq_decode.hip).
+struct UnionArgs {
+  const int32_t* token_list;  // [B * T, Hkv, token_max_list]
+  const int32_t* token_len;   // [B * T, Hkv]
+  const int32_t* block_table;
+  const int32_t* seq_lens;    // [B] keys in each request's cache
+  int32_t* page_list;         // [B, Hkv, max_list]
+  int32_t* page_phys;         // nullable
+  uint32_t* page_mask;        // [B, Hkv, max_list]
+  int32_t* list_len;          // [B, Hkv]
+  int batch, num_kv_heads, max_pages, max_list, num_tokens, token_max_list;
+};
+int launch_page_list_union(const UnionArgs& a, hipStream_t stream);
+
+struct MqDecodeArgs {
+  const void* q;              // [B, T, Hq, d]
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* page_list;
+  const int32_t* page_phys;   // nullable
+  const uint32_t* page_mask;
+  const int32_t* list_len;
+  float* out;                 // [B, T, Hq, d]
+  float* out_lse;             // [B, T, Hq]
+  float* part_o;              // [B, Hkv, J, 16, d]
+  float* part_lse;            // [B, Hkv, J, 16]
+  int batch, num_q_heads, num_kv_heads, max_pages, num_pool_pages, max_list, num_tokens;
+  int blocks_per_row, min_chunk;
+  float sm_scale_log2;
+};
+int launch_mq_decode(const MqDecodeArgs& a, int head_dim, hipStream_t stream);
 
 // Moira Eq. 4: chunk size and count of a row of n listed pages.
 __host__ __device__ inline void plan_chunks(int n, int J, int C, int& c, int& m) {

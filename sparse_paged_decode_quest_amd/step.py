@@ -274,3 +274,106 @@ class DecodeStep:
         ll = self.list_len.cpu().numpy()
         return {(b, h): pl[b, h, :ll[b, h]].tolist() for b in range(self.w.batch)
                 for h in range(self.w.num_kv_heads)}
+
+
+class MQDecodeStep:
+    """One decode step for T > 1 query tokens per request (the draft tokens speculative decoding
+    verifies at once), with the tokens' page lists scanned as one union (LiteTopK, section 3.4).
+
+    Request b's cache holds ``seq_lens[b]`` = L keys, the draft tokens' included; token t attends to
+    positions < L - T + 1 + t.  Each token selects its pages as a single query of that length: the
+    scorer and the selector run over B * T rows that share their request's block-table row.  The
+    rows' lists are merged per (request, KV head) with a membership mask per entry, and the
+    several-query decode reads each union page once for all T x G query rows.  ``d.q`` is
+    [B, T, Hq, d]; ``out`` is [B, T, Hq, d] and ``out_lse`` [B, T, Hq].
+    """
+
+    def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None):
+        T = w.num_queries
+        if T < 2 or w.mode != "topk" or w.page_size != 16:
+            raise ValueError("several query tokens: top-K over 16-token pages, T >= 2")
+        self.w, self.d, self.T = w, d, T
+        self.plan = plan or Plan()
+        self.pp = self.plan.params()
+        dev = d.q.device
+        B, Hq, Hkv, D = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.token_cap = w.list_capacity
+        self.union_cap = min(T * self.token_cap, w.pages_per_seq)
+        self.desc = make_desc(w, d.num_pool_pages, self.union_cap)                 # the B requests
+        self.desc_x = make_desc(w.replace(seq_lens=tuple(w.seq_lens) * T), d.num_pool_pages, self.token_cap)
+        self.sel = make_select(w)
+        # the B * T token rows: queries, block-table rows and causal lengths
+        self.q_x = d.q.view(B * T, Hq, D)
+        self.bt_x = d.block_table.repeat_interleave(T, dim=0).contiguous()
+        self.seq_x = torch.zeros(B * T, **i32)
+        self.steps_t = torch.arange(T, dtype=torch.int32, device=dev)
+        self.set_lengths()
+        self.scores = torch.zeros((B * T, Hkv, w.pages_per_seq), **f32)
+        self.head_lse = torch.zeros((B * T, Hq), **f32)
+        self.token_list = torch.zeros((B * T, Hkv, self.token_cap), **i32)
+        self.token_len = torch.zeros((B * T, Hkv), **i32)
+        self.page_list = torch.zeros((B, Hkv, self.union_cap), **i32)
+        self.page_phys = torch.zeros((B, Hkv, self.union_cap), **i32)
+        self.page_mask = torch.zeros((B, Hkv, self.union_cap), **i32)  # uint32 bits
+        self.list_len = torch.zeros((B, Hkv), **i32)
+        self.out = torch.zeros((B, T, Hq, D), **f32)
+        self.out_lse = torch.zeros((B, T, Hq), **f32)
+        self.J = A.spd_plan_grid(self.desc, self.pp)
+        self.part_o = torch.zeros(B * Hkv * self.J * A.MQ_ROWS * D, **f32)
+        self.part_lse = torch.zeros(B * Hkv * self.J * A.MQ_ROWS, **f32)
+        self.ws_bytes = A.spd_workspace_bytes(self.desc_x, self.sel, A.OP_PAGE_SCORE)
+        self.workspace = torch.zeros(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+
+    def set_lengths(self):
+        """Causal length of every token row from the requests' lengths (a device op, capturable)."""
+        L = self.d.seq_lens.to(torch.int32)
+        self.seq_x.copy_((L[:, None] - self.T + 1 + self.steps_t[None, :]).reshape(-1))
+
+    def refresh_tail(self, stream=None):
+        """Key statistics of the pages the draft tokens are in (the last two pages of each request)."""
+        A.spd_page_meta_build(self.desc, self.d.k_pool, self.d.k_scale, self.d.block_table, self.d.seq_lens, None, 2,
+                              self.d.page_meta, stream)
+
+    def select(self, stream=None):
+        d = self.d
+        A.spd_page_score(self.desc_x, self.sel, self.q_x, d.page_meta, d.k_pool, d.k_scale, A.TAIL_NONE, self.bt_x,
+                         self.seq_x, d.head_kind, self.scores, self.head_lse, self.workspace, self.ws_bytes, stream)
+        A.spd_page_select(self.desc_x, self.sel, self.scores, self.seq_x, d.head_kind, self.bt_x, None, None, None,
+                          self.token_list, None, self.token_len, None, stream)
+
+    def union(self, stream=None):
+        d = self.d
+        A.spd_page_list_union(self.desc, self.T, self.token_cap, self.token_list, self.token_len, d.block_table,
+                              d.seq_lens, self.page_list, self.page_phys, self.page_mask, self.list_len, stream)
+
+    def attend(self, stream=None):
+        d = self.d
+        A.spd_sparse_paged_decode_mq(self.desc, self.T, self.pp, d.q, d.k_pool, d.v_pool, d.block_table, d.seq_lens,
+                                     self.page_list, self.page_phys, self.page_mask, self.list_len, self.w.sm_scale,
+                                     self.out, self.out_lse, self.part_o, self.part_lse, stream)
+        A.spd_lse_merge_mq(self.desc, self.T, self.pp, self.part_o, self.part_lse, self.list_len, self.out,
+                           self.out_lse, stream)
+
+    def run(self, stream=None):
+        self.refresh_tail(stream)
+        self.select(stream)
+        self.union(stream)
+        self.attend(stream)
+
+    def token_lists(self) -> list:
+        """Host copy of each token's lists: [T] of {(b, h): [pages]}."""
+        pl = self.token_list.cpu().numpy()
+        ll = self.token_len.cpu().numpy()
+        B, T = self.w.batch, self.T
+        return [{(b, h): pl[b * T + t, h, :ll[b * T + t, h]].tolist() for b in range(B)
+                 for h in range(self.w.num_kv_heads)} for t in range(T)]
+
+    def union_lists(self) -> dict:
+        """Host copy of the union lists: {(b, h): (pages, masks)}."""
+        pl = self.page_list.cpu().numpy()
+        pm = self.page_mask.cpu().numpy().astype(np.int64) & 0xffffffff
+        ll = self.list_len.cpu().numpy()
+        return {(b, h): (pl[b, h, :ll[b, h]].tolist(), pm[b, h, :ll[b, h]].tolist()) for b in range(self.w.batch)
+                for h in range(self.w.num_kv_heads)}

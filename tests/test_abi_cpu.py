@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 7
+    assert A.abi_version() == 8
 
 
 def test_error_strings(lib):
@@ -323,3 +323,39 @@ def test_hierarchical_paging_argument_checks(lib):
     # argument errors are still found first on the supported shapes
     assert score_rc(d, sel_for(w, budget_pages=0)) == A.SPD_ERR_INVALID_ARG
     assert decode_rc(d, A.PlanParams(4, 16, 512), q=None) == A.SPD_ERR_INVALID_ARG
+
+
+def test_several_query_tokens_argument_checks(lib):
+    w = W.small(num_queries=4, budget=6)
+    d = desc_for(w, max_list=24)
+    plan = A.PlanParams(4, 16, 512)
+    L = A.lib()
+
+    def union_rc(desc, T=4, tml=6, **null):
+        p = {k: FAKE for k in ("tl", "tn", "bt", "sl", "pl", "pp", "pm", "ll")}
+        p.update(null)
+        return L.spd_page_list_union(ctypes.byref(desc), T, tml, p["tl"], p["tn"], p["bt"], p["sl"], p["pl"], p["pp"],
+                                     p["pm"], p["ll"], 0)
+
+    def dec_rc(desc, T=4, pl=plan, **null):
+        p = {k: FAKE for k in ("q", "k", "v", "bt", "sl", "pl", "pp", "pm", "ll", "o", "lse", "po", "pls")}
+        p.update(null)
+        return L.spd_sparse_paged_decode_mq(ctypes.byref(desc), T, ctypes.byref(pl), p["q"], p["k"], p["v"], p["bt"],
+                                            p["sl"], p["pl"], p["pp"], p["pm"], p["ll"], ctypes.c_float(0.1), p["o"],
+                                            p["lse"], p["po"], p["pls"], 0)
+
+    for T in (0, 5):
+        assert union_rc(d, T=T) == A.SPD_ERR_INVALID_ARG
+        assert dec_rc(d, T=T) == A.SPD_ERR_INVALID_ARG
+    assert union_rc(desc_for(w, max_list=23)) == A.SPD_ERR_INVALID_ARG      # cannot hold 4 lists of 6
+    assert union_rc(d, tml=0) == A.SPD_ERR_INVALID_ARG
+    assert union_rc(d, pm=None) == A.SPD_ERR_INVALID_ARG
+    assert union_rc(d, bt=None) == A.SPD_ERR_INVALID_ARG                    # physical pages wanted
+    assert union_rc(desc_for(w, max_list=24, page_size=64)) == A.SPD_ERR_UNSUPPORTED
+    assert union_rc(desc_for(w, max_list=24, max_pages_per_seq=40000)) == A.SPD_ERR_UNSUPPORTED
+    assert dec_rc(d, pl=A.PlanParams(4, 16, 512, 1)) == A.SPD_ERR_UNSUPPORTED  # per-row plan only
+    assert dec_rc(desc_for(W.small(num_queries=4, d=64), max_list=24)) == A.SPD_ERR_UNSUPPORTED
+    assert dec_rc(desc_for(W.small(num_queries=4, kv="fp8"), max_list=24)) == A.SPD_ERR_UNSUPPORTED
+    assert dec_rc(d, pm=None) == A.SPD_ERR_INVALID_ARG
+    rc = L.spd_lse_merge_mq(ctypes.byref(d), 4, ctypes.byref(plan), FAKE, None, FAKE, FAKE, FAKE, 0)
+    assert rc == A.SPD_ERR_INVALID_ARG

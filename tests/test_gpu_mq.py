@@ -1,0 +1,172 @@
+"""Several query tokens per request on the GPU against the fp64 oracle (needs a gfx950 GPU).
+
+LiteTopK, section 3.4 (LiteDSA): each draft token selects its own pages; the tokens' lists are
+scanned as one union with a membership mask per entry, and each token attends to exactly its own
+list over its causal prefix.  Every call goes through the C ABI; rules and tolerances are those of
+tests/parity.py.
+"""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import spd_oracle as O
+from sparse_paged_decode_quest_amd import _abi as A
+from sparse_paged_decode_quest_amd import step as S
+from sparse_paged_decode_quest_amd import workloads as W
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible gfx950 device"
+    A.lib()
+    yield
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+MQ_SMALL = {
+    "t4": W.small("mq_t4", num_queries=4, seq_lens=(700, 37, 2050, 3, 17, 4000), budget=12, Hkv=3, Hq=12,
+                  streaming=(1,), n_sink_stream=1, n_local_stream=2),
+    "t2": W.small("mq_t2", num_queries=2, seq_lens=(513, 300, 2, 129), budget=9, n_local=3),
+    "t3_planted": W.small("mq_t3", num_queries=3, seq_lens=(1500, 250, 31), budget=16, planted=("fixed", 8),
+                          delta=3.0),
+}
+
+
+def run_case(w, plan=None):
+    say(f"[case] {w.name} T={w.num_queries} seq={w.seq_lens[:8]} seed={w.seed} plan={plan}")
+    inp = W.generate(w)
+    d = S.upload(inp)
+    S.build_meta(w, d)
+    st = S.MQDecodeStep(w, d, plan=plan)
+    st.run()
+    torch.cuda.synchronize()
+    return inp, d, st
+
+
+def check_token_lists(inp, st, meta_ref):
+    """Each token's lists against the oracle's (tie rule of parity.py); returns the oracle's lists."""
+    w = inp.workload
+    T = w.num_queries
+    gpu = st.token_lists()
+    want = []
+    for t in range(T):
+        one = O.mq_token_inputs(inp, t)
+        ref = {}
+        for b in range(w.batch):
+            n = O.n_pages(one.seq_lens[b])
+            for h in range(w.num_kv_heads):
+                if inp.head_kind[h]:
+                    ref[(b, h)] = O.forced_pages(n, w.n_sink_stream, w.n_local_stream)
+                    assert gpu[t][(b, h)] == ref[(b, h)], (t, b, h)
+                    continue
+                S_ = O.row_bounds(one, meta_ref, b, h)
+                sc = O.topk_scores(S_)
+                forced = O.forced_pages(n, w.n_sink, w.n_local)
+                P.check_topk_list(gpu[t][(b, h)], sc, n, w.budget_pages, forced, P.bound_scale(one, meta_ref, b, h))
+                ref[(b, h)] = O.select_topk(sc, n, w.budget_pages, forced)
+        want.append(ref)
+    return gpu, want
+
+
+def set_union(st, union):
+    pl = torch.zeros_like(st.page_list)
+    pp = torch.zeros_like(st.page_phys)
+    pm = torch.zeros_like(st.page_mask)
+    ll = torch.zeros_like(st.list_len)
+    bt = st.d.block_table.cpu()
+    for (b, h), (pages, masks) in union.items():
+        if pages:
+            pl[b, h, :len(pages)] = torch.tensor(pages, dtype=torch.int32)
+            pp[b, h, :len(pages)] = bt[b, pages]
+            pm[b, h, :len(pages)] = torch.tensor(masks, dtype=torch.int32)
+        ll[b, h] = len(pages)
+    for dst, src in ((st.page_list, pl), (st.page_phys, pp), (st.page_mask, pm), (st.list_len, ll)):
+        dst.copy_(src)
+
+
+@pytest.mark.parametrize("name", list(MQ_SMALL))
+def test_mq_lists_union_attention(name):
+    w = MQ_SMALL[name]
+    inp, d, st = run_case(w)
+    meta_ref = O.page_meta_build(inp)
+    assert np.array_equal(d.page_meta.cpu().numpy()[np.unique(inp.block_table)], meta_ref[np.unique(inp.block_table)])
+    gpu_lists, ref_lists = check_token_lists(inp, st, meta_ref)
+    # the union is exact integer work: it must be the union of the GPU's own token lists
+    union = st.union_lists()
+    assert union == O.union_lists(gpu_lists)
+    pp = st.page_phys.cpu().numpy()
+    for (b, h), (pages, _) in union.items():
+        assert pp[b, h, :len(pages)].tolist() == inp.block_table[b, pages].tolist()
+    # attention of every token over its own list, where the GPU's lists equal the oracle's
+    res = O.mq_decode_step(inp, meta_ref)
+    out, lse = st.out.cpu().numpy(), st.out_lse.cpu().numpy()
+    G = w.group
+    same = 0
+    for t in range(w.num_queries):
+        for (b, h), lst in ref_lists[t].items():
+            if gpu_lists[t][(b, h)] == lst:
+                sl = slice(h * G, (h + 1) * G)
+                P.check_attention(out[b, t, sl], lse[b, t, sl], res["O"][b, t, sl], res["out_lse"][b, t, sl],
+                                  w.kv_dtype, f"token {t} row {b},{h}")
+                same += 1
+    assert same >= w.num_queries * w.batch * w.num_kv_heads - 2
+    # decode fed the oracle's union
+    set_union(st, res["union"])
+    st.out.fill_(float("nan"))
+    st.out_lse.fill_(float("nan"))
+    st.attend()
+    torch.cuda.synchronize()
+    P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), res["O"], res["out_lse"], w.kv_dtype,
+                      "oracle union")
+
+
+@pytest.mark.parametrize("plan", [S.Plan(1, 1, 0), S.Plan(2, 3, 0), S.Plan(4, 16, 512), S.Plan(1000, 1, 0)])
+def test_mq_plan_invariance(plan):
+    w = MQ_SMALL["t4"].replace(budget_pages=40)
+    inp, d, st = run_case(w, plan=plan)
+    res = O.mq_decode_step(inp)
+    set_union(st, res["union"])
+    st.out.fill_(float("nan"))
+    st.out_lse.fill_(float("nan"))
+    st.attend()
+    torch.cuda.synchronize()
+    P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), res["O"], res["out_lse"], w.kv_dtype, str(plan))
+
+
+def test_mq_every_page_listed_is_dense_causal_attention():
+    # budget above every row: each token attends to its whole causal prefix
+    w = W.small("mq_dense", num_queries=4, seq_lens=(333, 48, 17, 5, 2), budget=1000, Hkv=2, Hq=8)
+    inp, d, st = run_case(w)
+    res = O.mq_decode_step(inp)
+    assert st.union_lists() == res["union"]
+    P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), res["O"], res["out_lse"], w.kv_dtype, "dense")
+    out = st.out.cpu().numpy()
+    assert np.all(out[4, :2] == 0)  # two keys, four draft tokens: the first two tokens see no key
+
+
+def test_mq_named_workload_in_the_bench_configuration():
+    w = W.named("mtp4_b1_128k_f16")
+    inp, d, st = run_case(w)
+    meta_ref = O.page_meta_build(inp)
+    gpu_lists, ref_lists = check_token_lists(inp, st, meta_ref)
+    union = st.union_lists()
+    assert union == O.union_lists(gpu_lists)
+    for h in range(w.num_kv_heads):
+        say(f"  head {h}: union {len(union[(0, h)][0])} pages, token lists "
+            f"{[len(gpu_lists[t][(0, h)]) for t in range(w.num_queries)]}")
+    res = O.mq_decode_step(inp, meta_ref)
+    set_union(st, res["union"])
+    st.out.fill_(float("nan"))
+    st.attend()
+    torch.cuda.synchronize()
+    P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), res["O"], res["out_lse"], w.kv_dtype,
+                      "oracle union")
