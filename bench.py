@@ -212,6 +212,8 @@ def main():
     if args.plan:
         v = [int(x) for x in args.plan.split(",")]
         plan = S.Plan(*v[:3], balanced=bool(v[3]) if len(v) > 3 else False)
+    if w.num_queries > 1:
+        return bench_mq(args, w, inp, base, plan, gen_s)
     probe = S.DecodeStep(w, base, plan=plan, fused=args.fused)
     probe.run()
     torch.cuda.synchronize()
@@ -397,6 +399,121 @@ def main():
         "list_len": {"min": int(list_len.min()), "median": int(np.median(list_len)), "max": int(list_len.max())},
         "roofline": roofline, "cpu_baseline": cpu,
         "setup_s": round(gen_s, 1), "kernel_hash": dom_hash,
+    }
+    print(json.dumps(line))
+
+
+def bench_mq(args, w, inp, base, plan, gen_s):
+    """Several query tokens per request (LiteDSA union): same timing protocol as the single-query
+    step -- rotated layer copies, graph replays, HIP events on the replay stream."""
+    import torch
+
+    from sparse_paged_decode_quest_amd import step as S
+
+    T = w.num_queries
+    probe = S.MQDecodeStep(w, base, plan=plan)
+    probe.run()
+    torch.cuda.synchronize()
+    d = w.head_dim
+    dyn = int((inp.head_kind == 0).sum())
+    union_len = probe.list_len.cpu().numpy()
+    token_len = probe.token_len.cpu().numpy()
+    # algorithmic bytes: every token scans the dynamic rows' key boxes; the union pages' K / V are read
+    # once for the T tokens; queries, outputs, block-table rows; the rebuilt last two pages
+    meta = T * int(w.n_pages.sum()) * dyn * 2 * d * 2
+    kv = int(union_len.sum()) * 16 * d * 2 * 2
+    per_token_kv = int(token_len.sum()) * 16 * d * 2 * 2  # what T independent decodes would read
+    q = w.batch * T * w.num_q_heads * d * 2
+    o = w.batch * T * w.num_q_heads * (d + 1) * 4
+    tables = T * int(w.n_pages.sum()) * 4
+    tail = w.batch * w.num_kv_heads * 2 * (16 * d * 2 + 2 * d * 2)
+    ab = {"meta": meta, "kv": kv, "q": q, "o": o, "tables": tables, "tail": tail,
+          "total": meta + kv + q + o + tables + tail}
+    layer_bytes = sum(t.numel() * t.element_size() for t in (base.k_pool, base.v_pool, base.page_meta))
+    R = args.layers or int(min(64, max(4, math.ceil((1 << 30) / ab["total"]))))
+    R = max(1, min(R, int(100e9 // max(layer_bytes, 1))))
+    layers = [base] + [S.DeviceInputs(q=base.q.clone(), k_pool=base.k_pool.clone(), v_pool=base.v_pool.clone(),
+                                      k_scale=None, v_scale=None, block_table=base.block_table.clone(),
+                                      seq_lens=base.seq_lens.clone(), head_kind=base.head_kind.copy(),
+                                      page_meta=base.page_meta.clone()) for _ in range(R - 1)]
+    steps = [probe] + [S.MQDecodeStep(w, x, plan=plan) for x in layers[1:]]
+    for st in steps:
+        st.run()
+    torch.cuda.synchronize()
+    assert steps[-1].union_lists() == probe.union_lists() and torch.equal(steps[-1].out, probe.out)
+    stream = torch.cuda.Stream()
+
+    def timed(fn, total):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for i in range(R):
+                fn(steps[i], stream.cuda_stream)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(R):
+                fn(steps[i], stream.cuda_stream)
+        reps = max(1, total // R)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / (reps * R)
+
+    whole = (lambda st, s: st.run(s))
+    timed(whole, max(args.warmup, R))
+    step_s = timed(whole, args.steps)
+    phases = {"tail": lambda st, s: st.refresh_tail(s), "score": lambda st, s: st.score(s),
+              "select_only": lambda st, s: st.select_only(s), "union": lambda st, s: st.union(s),
+              "attend": lambda st, s: st.attend(s)}
+    phase_us = {}
+    for name, fn in phases.items():
+        timed(fn, R)
+        phase_us[name] = timed(fn, max(R, args.steps // 4)) * 1e6
+    beta = copy_bandwidth(stream)
+    cpu = None
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import spd_oracle as O
+
+        with threadpool_limits(limits=1):
+            m0 = O.page_meta_build(inp)
+            last = [max(O.n_pages(L) - 2, 0) for L in inp.seq_lens]
+            n, t0 = 0, time.perf_counter()
+            while True:
+                O.mq_decode_step(inp, O.page_meta_build(inp, meta=m0, first_page=last))
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds:
+                    break
+        cpu = {"value": round(ab["total"] / (el / n) / 1e12, 8), "unit": "TB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} whole steps of {w.name} ({T} query tokens: last-page statistics, each token's "
+                         f"scores and selection, attention; fp64 numpy, 1 thread) in {el:.1f} s",
+               "step_ms": round(el / n * 1e3, 2)}
+    # the scan of T token rows is the kernel that moves the most bytes
+    sc_bytes = meta + tables + q + T * int(w.n_pages.sum()) * dyn * 4
+    line = {
+        "metric": METRIC, "value": round(ab["total"] / step_s / 1e12, 4), "unit": "TB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "query_tokens": T, "context": int(max(w.seq_lens)),
+                   "heads": f"Hq{w.num_q_heads}/Hkv{w.num_kv_heads}", "head_dim": d, "page": w.page_size,
+                   "kv_dtype": w.kv_dtype, "mode": w.mode, "budget_pages": w.budget_pages,
+                   "streaming_kv_heads": len(w.streaming_heads), "layers_rotated": R, "graph": True,
+                   "plan": [probe.plan.min_chunk, probe.plan.min_blocks_per_row, probe.plan.min_grid_blocks, 0]},
+        "step_us": round(step_s * 1e6, 3), "tokens_per_s": round(w.batch * T / step_s, 1),
+        "bytes_per_step": ab, "kv_bytes_without_union": per_token_kv, "frac_of_peak": round(ab["total"] / step_s / 1e12 / PEAK_HBM_TBS, 4),
+        "beta_copy_TBs": round(beta, 3), "phase_us": {k: round(v, 3) for k, v in phase_us.items()},
+        "union_len": {"min": int(union_len.min()), "median": int(np.median(union_len)), "max": int(union_len.max())},
+        "roofline": {"bound": "hbm", "kernel": "page_score_kernel (B x T token rows)",
+                     "achieved": round(sc_bytes / (phase_us["score"] * 1e-6) / 1e9, 1), "peak": PEAK_HBM_TBS * 1000,
+                     "unit": "GB/s", "frac": round(sc_bytes / (phase_us["score"] * 1e-6) / 1e9 / (PEAK_HBM_TBS * 1000), 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": sc_bytes, "avg_launch_us": round(phase_us["score"], 3)},
+        "cpu_baseline": cpu, "setup_s": round(gen_s, 1),
     }
     print(json.dumps(line))
 

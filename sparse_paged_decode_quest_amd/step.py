@@ -336,12 +336,21 @@ class MQDecodeStep:
         A.spd_page_meta_build(self.desc, self.d.k_pool, self.d.k_scale, self.d.block_table, self.d.seq_lens, None, 2,
                               self.d.page_meta, stream)
 
-    def select(self, stream=None):
+    def score(self, stream=None):
+        """Page scores of every token row (statistics over all cached keys)."""
         d = self.d
         A.spd_page_score(self.desc_x, self.sel, self.q_x, d.page_meta, d.k_pool, d.k_scale, A.TAIL_NONE, self.bt_x,
                          self.seq_x, d.head_kind, self.scores, self.head_lse, self.workspace, self.ws_bytes, stream)
+
+    def select_only(self, stream=None):
+        """Each token row's page list from its scores."""
+        d = self.d
         A.spd_page_select(self.desc_x, self.sel, self.scores, self.seq_x, d.head_kind, self.bt_x, None, None, None,
                           self.token_list, None, self.token_len, None, stream)
+
+    def select(self, stream=None):
+        self.score(stream)
+        self.select_only(stream)
 
     def union(self, stream=None):
         d = self.d
