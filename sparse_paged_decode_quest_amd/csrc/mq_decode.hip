@@ -15,8 +15,10 @@
 //    t = q) of key l % 16 in lane l, so each query token's rows sit in one 16-lane DPP row;
 //  * masks: bit t of the page's mask, the token's causal limit (positions < len - T + 1 + t)
 //    and the request's length, before the online softmax (fp32, base 2);
-//  * PV on the VALU: probabilities go through LDS (1 KiB per wave) and every lane accumulates
-//    its two channels for all 16 rows from the page's V rows (16 coalesced 256-byte rows).
+//  * PV on MFMA too, as O^T = V^T P^T in eight 16 x 16 x 16 tiles of channels: the wave writes
+//    its page's V transposed into LDS (each lane packs its two channels' 16 keys into two 32-byte
+//    rows) and P as fp16 in [row][key] order, then every lane reads four keys of one channel (A)
+//    and four keys of one row (B) per tile with 8-byte LDS reads.
 #include "spd_device.h"
 #include "spd_launch.h"
 
@@ -25,6 +27,10 @@ namespace spd {
 constexpr int kMqG = 4;      // query heads per KV head
 constexpr int kMqRows = 16;  // 4 query tokens x G = 4 heads
 constexpr int kUnionThreads = 1024;
+#ifndef SPD_MQ_STAGES
+#define SPD_MQ_STAGES 2
+#endif
+constexpr int kMqStages = SPD_MQ_STAGES;  // pages of a wave in flight: one computed, the rest loading
 
 __device__ __forceinline__ int mq_clamp(int n, int hi) { return n < 0 ? 0 : (n > hi ? hi : n); }
 
@@ -115,7 +121,9 @@ __device__ __forceinline__ void mq_load(const MqDecodeArgs& a, const MqPage& r, 
 template <int D>
 __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
   static_assert(D == 128, "the logit tile covers 128 channels: 4 lane groups x 32");
-  __shared__ float p_lds[4][kPage][kMqRows];
+  __shared__ _Float16 p16[4][kMqRows][kPage];  // P of the wave's page, [row][key]
+  __shared__ float al_lds[4][kMqRows];           // each row's rescale of the page
+  __shared__ uint4 vt[4][D][2];                  // V^T of the wave's page: channel c's 16 keys (fp16)
   __shared__ float ws_m[4][kMqRows], ws_l[4][kMqRows];
   __shared__ float ws_acc[4][kMqRows][D];
   const int wave = threadIdx.x / kWave;
@@ -166,14 +174,14 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
   }
 
   float m_run[4], l_run[4];
-  float acc[kMqRows][2];
+  mq_float4 acc[D / 16];  // O^T tile s: lane l holds channels 16 s + 4 (l / 16) .. + 3 of row l % 16
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     m_run[jj] = -INFINITY;
     l_run[jj] = 0.f;
   }
 #pragma unroll
-  for (int r = 0; r < kMqRows; ++r) acc[r][0] = acc[r][1] = 0.f;
+  for (int t = 0; t < D / 16; ++t) acc[t] = mq_float4{0.f, 0.f, 0.f, 0.f};
 
   auto process = [&](const MqPage& r, const MqKV& kv) {
     if (r.page < 0) return;
@@ -196,31 +204,32 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
       l_run[jj] = l_run[jj] * alpha[jj] + p[jj];
       m_run[jj] = m_new;
     }
-    *reinterpret_cast<float4*>(&p_lds[wave][tok][4 * q4]) = make_float4(p[0], p[1], p[2], p[3]);
-    float al[kMqRows];  // every row's rescale, read from the lane group that owns the row
 #pragma unroll
-    for (int rr = 0; rr < kMqRows; ++rr)
-      al[rr] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[rr & 3]), 16 * (rr >> 2)));
-    wave_fence();
+    for (int jj = 0; jj < 4; ++jj) p16[wave][4 * q4 + jj][tok] = (_Float16)p[jj];
+    if (tok == 0) *reinterpret_cast<float4*>(&al_lds[wave][4 * q4]) = make_float4(alpha[0], alpha[1], alpha[2], alpha[3]);
+    // V^T: this lane's channels 2 l (low halves) and 2 l + 1 (high halves) of the 16 keys, keys past
+    // the request's end zeroed (their slots may hold NaN, and 0 x NaN would reach every row)
+    uint32_t v[kPage];
 #pragma unroll
-    for (int rr = 0; rr < kMqRows; ++rr) {
-      acc[rr][0] *= al[rr];
-      acc[rr][1] *= al[rr];
+    for (int t = 0; t < kPage; ++t) v[t] = t < r.valid ? kv.v[t] : 0u;
+    uint32_t lo[kPage / 2], hi[kPage / 2];
+#pragma unroll
+    for (int i = 0; i < kPage / 2; ++i) {
+      lo[i] = __builtin_amdgcn_perm(v[2 * i + 1], v[2 * i], 0x05040100u);  // low halves of keys 2 i, 2 i + 1
+      hi[i] = __builtin_amdgcn_perm(v[2 * i + 1], v[2 * i], 0x07060302u);  // high halves
     }
+    vt[wave][2 * lane][0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    vt[wave][2 * lane][1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+    vt[wave][2 * lane + 1][0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    vt[wave][2 * lane + 1][1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+    wave_fence();
+    // B = P^T: row l % 16, keys 4 q4 .. 4 q4 + 3; A = V^T tile s: channel 16 s + l % 16, the same keys
+    const mq_half4 pb = *reinterpret_cast<const mq_half4*>(&p16[wave][tok][4 * q4]);
+    const float al = al_lds[wave][tok];
 #pragma unroll
-    for (int t = 0; t < kPage; ++t) {
-      const float4* pr = reinterpret_cast<const float4*>(p_lds[wave][t]);
-      const float4 p0 = pr[0], p1 = pr[1], p2 = pr[2], p3 = pr[3];
-      const float pv[kMqRows] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w,
-                                 p2.x, p2.y, p2.z, p2.w, p3.x, p3.y, p3.z, p3.w};
-      const __half2 vh = __builtin_bit_cast(__half2, kv.v[t]);
-      const float v0 = t < r.valid ? __low2float(vh) : 0.f;  // slots past the request's end may hold NaN
-      const float v1 = t < r.valid ? __high2float(vh) : 0.f;
-#pragma unroll
-      for (int rr = 0; rr < kMqRows; ++rr) {
-        acc[rr][0] = fmaf(pv[rr], v0, acc[rr][0]);
-        acc[rr][1] = fmaf(pv[rr], v1, acc[rr][1]);
-      }
+    for (int t = 0; t < D / 16; ++t) {
+      const uint2 va = reinterpret_cast<const uint2*>(&vt[wave][16 * t + tok][0])[q4];
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(mq_half4, va), pb, acc[t] * al, 0, 0, 0);
     }
     wave_fence();
   };
@@ -243,7 +252,8 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
     r.valid = valid_in_page(len, p);
     return r;
   };
-  MqKV ka, kb;
+  MqKV kv[kMqStages];  // ring of page buffers: page u lives in slot u mod kMqStages
+  MqPage rp[kMqStages];
   for (int bb = 0; bb < my_pages; bb += kWave) {
     const int cnt = min(kWave, my_pages - bb);
     const int idx = i0 + wave + 4 * (bb + lane);
@@ -255,20 +265,22 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
       if (plist) lph = plist[idx];
       else if (lp >= 0 && lp < n_b) lph = a.block_table[(size_t)b * a.max_pages + lp];
     }
-    MqPage ra = page_at(lp, lph, lm, 0), rb;
-    mq_load<D>(a, ra, h, ka);
-    for (int u = 0; u < cnt; u += 2) {
-      if (u + 1 < cnt) {
-        rb = page_at(lp, lph, lm, u + 1);
-        mq_load<D>(a, rb, h, kb);
+#pragma unroll
+    for (int k = 0; k < kMqStages - 1; ++k) {  // the first kMqStages - 1 pages' loads go out at once
+      rp[k] = k < cnt ? page_at(lp, lph, lm, k) : MqPage{-1, 0, 0u, 0};
+      mq_load<D>(a, rp[k], h, kv[k]);
+    }
+    for (int u0 = 0; u0 < cnt; u0 += kMqStages) {
+#pragma unroll
+      for (int k = 0; k < kMqStages; ++k) {
+        const int u = u0 + k;
+        if (u >= cnt) break;  // uniform over the wave
+        const int un = u + kMqStages - 1;
+        MqPage& rn = rp[(k + kMqStages - 1) % kMqStages];
+        rn = un < cnt ? page_at(lp, lph, lm, un) : MqPage{-1, 0, 0u, 0};
+        mq_load<D>(a, rn, h, kv[(k + kMqStages - 1) % kMqStages]);
+        process(rp[k], kv[k]);
       }
-      process(ra, ka);
-      if (u + 1 >= cnt) break;
-      if (u + 2 < cnt) {
-        ra = page_at(lp, lph, lm, u + 2);
-        mq_load<D>(a, ra, h, ka);
-      }
-      process(rb, kb);
     }
   }
 
@@ -282,10 +294,8 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
     }
   }
 #pragma unroll
-  for (int rr = 0; rr < kMqRows; ++rr) {
-    ws_acc[wave][rr][2 * lane] = acc[rr][0];
-    ws_acc[wave][rr][2 * lane + 1] = acc[rr][1];
-  }
+  for (int t = 0; t < D / 16; ++t)
+    *reinterpret_cast<float4*>(&ws_acc[wave][tok][16 * t + 4 * q4]) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
   __syncthreads();
 
   // merge the four wave states (fixed order); write the chunk result of the rows of tokens < T
