@@ -27,10 +27,9 @@ namespace spd {
 constexpr int kMqG = 4;      // query heads per KV head
 constexpr int kMqRows = 16;  // 4 query tokens x G = 4 heads
 constexpr int kUnionThreads = 1024;
-#ifndef SPD_MQ_STAGES
-#define SPD_MQ_STAGES 2
-#endif
-constexpr int kMqStages = SPD_MQ_STAGES;  // pages of a wave in flight: one computed, the rest loading
+// Pages of a wave in flight: one computed while the next one loads (three or four were measured
+// slower: the kernel is bound by its per-page instructions, not by load latency).
+constexpr int kMqStages = 2;
 
 __device__ __forceinline__ int mq_clamp(int n, int hi) { return n < 0 ? 0 : (n > hi ? hi : n); }
 

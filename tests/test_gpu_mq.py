@@ -170,3 +170,40 @@ def test_mq_named_workload_in_the_bench_configuration():
     torch.cuda.synchronize()
     P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), res["O"], res["out_lse"], w.kv_dtype,
                       "oracle union")
+
+
+def test_mq_graph_replay_equals_eager():
+    """The whole several-query step captured once replays bit for bit, with eager work between replays,
+    and follows new queries written into the same buffer."""
+    w = MQ_SMALL["t4"]
+    inp, d, st = run_case(w)
+    eager = [t.clone() for t in (st.out, st.out_lse, st.page_list, st.page_mask, st.list_len)]
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        st.run(stream.cuda_stream)
+    stream.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        st.run(stream.cuda_stream)
+    for _ in range(3):
+        st.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, (st.out, st.out_lse, st.page_list, st.page_mask, st.list_len)):
+            assert torch.equal(a, b)
+    # new queries in the same buffer: the replay follows them
+    inp.q[:] = inp.q[:, ::-1]
+    d.q.copy_(torch.from_numpy(np.ascontiguousarray(inp.q)))
+    g.replay()
+    torch.cuda.synchronize()
+    res = O.mq_decode_step(inp)
+    gpu_lists = st.token_lists()
+    G = w.group
+    out, lse = st.out.cpu().numpy(), st.out_lse.cpu().numpy()
+    for t in range(w.num_queries):
+        for (b, h), lst in res["lists_by_token"][t].items():
+            if gpu_lists[t][(b, h)] == lst:
+                sl = slice(h * G, (h + 1) * G)
+                P.check_attention(out[b, t, sl], lse[b, t, sl], res["O"][b, t, sl], res["out_lse"][b, t, sl],
+                                  w.kv_dtype, f"replay token {t} row {b},{h}")
