@@ -27,6 +27,7 @@ namespace spd {
 constexpr int kMqG = 4;      // query heads per KV head
 constexpr int kMqRows = 16;  // 4 query tokens x G = 4 heads
 constexpr int kUnionThreads = 1024;
+constexpr int kUnionRounds = 2;  // list entries per thread read up front (4 tokens x 512 entries)
 // Pages of a wave in flight: one computed while the next one loads (three or four were measured
 // slower: the kernel is bound by its per-page instructions, not by load latency).
 constexpr int kMqStages = 2;
@@ -40,17 +41,36 @@ __global__ __launch_bounds__(kUnionThreads) void page_list_union_kernel(UnionArg
   __shared__ uint32_t wsum[kUnionThreads / kWave];
   const int row = blockIdx.x;
   const int b = row / a.num_kv_heads, h = row % a.num_kv_heads;
+  // Thread k reads entry k of the tokens' lists laid end to end (token k / token_max_list) and that
+  // token's length at the same time -- entries past a length are read from inside the list row and
+  // dropped -- while the byte map is cleared; longer lists take further rounds.
+  const int total = a.num_tokens * a.token_max_list;
+  int ent[kUnionRounds], len_of[kUnionRounds];
+#pragma unroll
+  for (int k = 0; k < kUnionRounds; ++k) {
+    const int e = (int)threadIdx.x + k * kUnionThreads;
+    ent[k] = -1;
+    len_of[k] = 0;
+    if (e < total) {
+      const size_t trow = ((size_t)b * a.num_tokens + e / a.token_max_list) * a.num_kv_heads + h;
+      ent[k] = a.token_list[trow * a.token_max_list + e % a.token_max_list];
+      len_of[k] = a.token_len[trow];
+    }
+  }
   const int n = row_pages(a.seq_lens[b], a.max_pages);
   for (int i = threadIdx.x; i < (n + 3) / 4; i += kUnionThreads) bits[i] = 0u;
   __syncthreads();
-  for (int t = 0; t < a.num_tokens; ++t) {
+  for (int k = 0; k < kUnionRounds; ++k) {
+    const int e = (int)threadIdx.x + k * kUnionThreads;
+    const int p = ent[k];
+    if (e < total && e % a.token_max_list < mq_clamp(len_of[k], a.token_max_list) && p >= 0 && p < n)
+      atomicOr(&bits[p >> 2], 1u << ((p & 3) * 8 + e / a.token_max_list));
+  }
+  for (int e = (int)threadIdx.x + kUnionRounds * kUnionThreads; e < total; e += kUnionThreads) {
+    const int t = e / a.token_max_list, i = e % a.token_max_list;
     const size_t trow = ((size_t)b * a.num_tokens + t) * a.num_kv_heads + h;
-    const int len = mq_clamp(a.token_len[trow], a.token_max_list);
-    const int32_t* lst = a.token_list + trow * a.token_max_list;
-    for (int i = threadIdx.x; i < len; i += kUnionThreads) {
-      const int p = lst[i];
-      if (p >= 0 && p < n) atomicOr(&bits[p >> 2], 1u << ((p & 3) * 8 + t));
-    }
+    const int p = i < mq_clamp(a.token_len[trow], a.token_max_list) ? a.token_list[trow * a.token_max_list + i] : -1;
+    if (p >= 0 && p < n) atomicOr(&bits[p >> 2], 1u << ((p & 3) * 8 + t));
   }
   __syncthreads();
   // thread k owns pages [k per, (k + 1) per): count, block scan, write in page order
