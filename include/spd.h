@@ -97,7 +97,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 8
+#define SPD_ABI_VERSION 9
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
@@ -351,7 +351,7 @@ int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float
  * queries, request b's block-table row, seq_lens L - T + 1 + t, key statistics covering all L
  * keys), then merges them with spd_page_list_union and attends with spd_sparse_paged_decode_mq
  * and spd_lse_merge_mq.  Supported: page_size 16, max_pages_per_seq <= SPD_MQ_MAX_PAGES; decode
- * and merge need f16 queries and pools, head_dim 128 and the per-row plan (balanced = 0). */
+ * and merge need f16 queries, f16 or fp8 pools, head_dim 128 and the per-row plan (balanced = 0). */
 #define SPD_MQ_MAX_TOKENS 4
 #define SPD_MQ_ROWS 16          /* chunk-state rows per (request, KV head): 4 tokens x G = 4 */
 #define SPD_MQ_MAX_PAGES 32768
@@ -371,7 +371,8 @@ int spd_page_list_union(const spd_desc* desc, int32_t num_tokens, int32_t token_
                         uint32_t* page_mask, int32_t* list_len, void* stream);
 
 /* Decode attention of the T query tokens of every row over the union list: q (device,
- * [B, T, Hq, d] f16), out (device, [B, T, Hq, d] f32), out_lse (device, [B, T, Hq] f32).  Each
+ * [B, T, Hq, d] f16), out (device, [B, T, Hq, d] f32), out_lse (device, [B, T, Hq] f32);
+ * k_scale / v_scale (device) are required for fp8 pools and ignored otherwise.  Each
  * union page is read once for all T x G query rows; row (t, g) keeps the page only when bit t of
  * its mask is set, and only positions < L - T + 1 + t.  Split as spd_sparse_paged_decode's per-row
  * plan over the union lengths; rows with more than one chunk write part_o (device,
@@ -380,6 +381,7 @@ int spd_page_list_union(const spd_desc* desc, int32_t num_tokens, int32_t token_
  * out_lse = -inf.  page_phys may be NULL (then block_table is read). */
 int spd_sparse_paged_decode_mq(const spd_desc* desc, int32_t num_tokens, const spd_plan_params* plan,
                                const void* q, const void* k_pool, const void* v_pool,
+                               const uint16_t* k_scale, const uint16_t* v_scale,
                                const int32_t* block_table, const int32_t* seq_lens,
                                const int32_t* page_list, const int32_t* page_phys,
                                const uint32_t* page_mask, const int32_t* list_len, float sm_scale,

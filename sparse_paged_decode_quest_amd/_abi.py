@@ -80,7 +80,8 @@ def lib():
         L.spd_sparse_paged_decode.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v]
         L.spd_lse_merge.argtypes = [D, P, v, v, v, v, v, v]
         L.spd_page_list_union.argtypes = [D, c_int32, c_int32, v, v, v, v, v, v, v, v, v]
-        L.spd_sparse_paged_decode_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v]
+        L.spd_sparse_paged_decode_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v,
+                                                 v]
         L.spd_lse_merge_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v]
         L.spd_plan_grid.argtypes = [D, P, POINTER(c_int32)]
         L.spd_plan_chunks.argtypes = [c_int32, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32)]
@@ -200,10 +201,12 @@ def spd_page_list_union(desc, num_tokens, token_max_list, token_list, token_len,
            "spd_page_list_union")
 
 
-def spd_sparse_paged_decode_mq(desc, num_tokens, plan, q, k_pool, v_pool, block_table, seq_lens, page_list,
-                               page_phys, page_mask, list_len, sm_scale, out, out_lse, part_o, part_lse, stream=None):
+def spd_sparse_paged_decode_mq(desc, num_tokens, plan, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
+                               page_list, page_phys, page_mask, list_len, sm_scale, out, out_lse, part_o, part_lse,
+                               stream=None):
     _check(lib().spd_sparse_paged_decode_mq(ctypes.byref(desc), int(num_tokens), ctypes.byref(plan), _ptr(q),
-                                            _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                                            _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                            _ptr(block_table), _ptr(seq_lens),
                                             _ptr(page_list), _ptr(page_phys), _ptr(page_mask), _ptr(list_len),
                                             float(sm_scale), _ptr(out), _ptr(out_lse), _ptr(part_o), _ptr(part_lse),
                                             _stream(stream)), "spd_sparse_paged_decode_mq")

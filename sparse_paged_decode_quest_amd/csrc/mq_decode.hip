@@ -116,28 +116,51 @@ struct MqPage {
 };
 
 // One page's K operand (lane: key l % 16, channels 32 (l / 16) .. + 31) and V rows (lane: channels
-// 2 l, 2 l + 1 of every key).
+// 2 l, 2 l + 1 of every key), as fp16 bits; fp8 pools hold their codes' values times 2^-8 here
+// (exact), with the key's scales times 256 beside them.
 struct MqKV {
   uint4 k[4];
   uint32_t v[kPage];
+  float ks, vs;  // fp8: this lane's key (l % 16) K and V scales times 256
 };
 
-template <int D>
+template <int D, int KVD>
 __device__ __forceinline__ void mq_load(const MqDecodeArgs& a, const MqPage& r, int h, MqKV& kv) {
   if (r.page < 0) return;
   const int lane = threadIdx.x % kWave;
   const size_t head_page = (size_t)r.phys * a.num_kv_heads + h;
-  const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.k_pool) +
-                                                   (head_page * kPage + (lane & 15)) * D + 32 * (lane >> 4));
+  if constexpr (KVD == SPD_DTYPE_F16) {
+    const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.k_pool) +
+                                                     (head_page * kPage + (lane & 15)) * D + 32 * (lane >> 4));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) kv.k[i] = ld_stream(kp + i);
-  const uint32_t* vp = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(a.v_pool) +
-                                                         head_page * kPage * D) + lane;
+    for (int i = 0; i < 4; ++i) kv.k[i] = ld_stream(kp + i);
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(a.v_pool) +
+                                                           head_page * kPage * D) + lane;
 #pragma unroll
-  for (int t = 0; t < kPage; ++t) kv.v[t] = ld_stream(vp + t * (D / 2));
+    for (int t = 0; t < kPage; ++t) kv.v[t] = ld_stream(vp + t * (D / 2));
+  } else {  // E4M3FN codes: 32 of the key's channels, two of every key's
+    const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.k_pool) +
+                                                     (head_page * kPage + (lane & 15)) * D + 32 * (lane >> 4));
+    const uint4 c0 = ld_stream(kp), c1 = ld_stream(kp + 1);
+    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    uint32_t hk[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      hk[2 * i] = fp8x2_to_half2_scaled(w[i] & 0xffffu);
+      hk[2 * i + 1] = fp8x2_to_half2_scaled(w[i] >> 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kv.k[i] = make_uint4(hk[4 * i], hk[4 * i + 1], hk[4 * i + 2], hk[4 * i + 3]);
+    const uint16_t* vp = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.v_pool) +
+                                                           head_page * kPage * D) + lane;
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) kv.v[t] = fp8x2_to_half2_scaled(ld_stream(vp + t * (D / 2)));
+    kv.ks = half_bits_to_float(a.k_scale[head_page * kPage + (lane & 15)]) * 256.f;
+    kv.vs = half_bits_to_float(a.v_scale[head_page * kPage + (lane & 15)]) * 256.f;
+  }
 }
 
-template <int D>
+template <int D, int KVD>
 __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
   static_assert(D == 128, "the logit tile covers 128 channels: 4 lane groups x 32");
   __shared__ _Float16 p16[4][kMqRows][kPage];  // P of the wave's page, [row][key]
@@ -213,10 +236,15 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
                                                 __builtin_bit_cast(mq_half4, make_uint2(kv.k[i].z, kv.k[i].w)), s, 0, 0, 0);
     }
     const bool ok = q4 < T && ((r.mask >> q4) & 1u) && r.page * kPage + tok < lim && tok < r.valid;
+    // fp8: key tok's K scale on its logit column; its V scale on its probabilities (P times the scale
+    // is what V's fp16 values times 2^8 are weighted with).  Slots past the request's end (scales may
+    // be NaN) are masked before either is used.
+    const float kscale = KVD == SPD_DTYPE_F16 ? a.sm_scale_log2 : a.sm_scale_log2 * (ok ? kv.ks : 0.f);
+    const float vscale = KVD == SPD_DTYPE_F16 ? 1.f : (ok ? kv.vs : 0.f);
     float p[4], alpha[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const float x = ok ? s[jj] * a.sm_scale_log2 : -INFINITY;
+      const float x = ok ? s[jj] * kscale : -INFINITY;
       const float m_new = fmaxf(m_run[jj], row_max(x));
       alpha[jj] = m_new == -INFINITY ? 1.f : exp2f(m_run[jj] - m_new);
       p[jj] = m_new == -INFINITY ? 0.f : exp2f(x - m_new);
@@ -224,7 +252,7 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
       m_run[jj] = m_new;
     }
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) p16[wave][4 * q4 + jj][tok] = (_Float16)p[jj];
+    for (int jj = 0; jj < 4; ++jj) p16[wave][4 * q4 + jj][tok] = (_Float16)(p[jj] * vscale);
     if (tok == 0) *reinterpret_cast<float4*>(&al_lds[wave][4 * q4]) = make_float4(alpha[0], alpha[1], alpha[2], alpha[3]);
     // V^T: this lane's channels 2 l (low halves) and 2 l + 1 (high halves) of the 16 keys, keys past
     // the request's end zeroed (their slots may hold NaN, and 0 x NaN would reach every row)
@@ -287,7 +315,7 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < kMqStages - 1; ++k) {  // the first kMqStages - 1 pages' loads go out at once
       rp[k] = k < cnt ? page_at(lp, lph, lm, k) : MqPage{-1, 0, 0u, 0};
-      mq_load<D>(a, rp[k], h, kv[k]);
+      mq_load<D, KVD>(a, rp[k], h, kv[k]);
     }
     for (int u0 = 0; u0 < cnt; u0 += kMqStages) {
 #pragma unroll
@@ -297,7 +325,7 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
         const int un = u + kMqStages - 1;
         MqPage& rn = rp[(k + kMqStages - 1) % kMqStages];
         rn = un < cnt ? page_at(lp, lph, lm, un) : MqPage{-1, 0, 0u, 0};
-        mq_load<D>(a, rn, h, kv[(k + kMqStages - 1) % kMqStages]);
+        mq_load<D, KVD>(a, rn, h, kv[(k + kMqStages - 1) % kMqStages]);
         process(rp[k], kv[k]);
       }
     }
@@ -354,10 +382,13 @@ int launch_page_list_union(const UnionArgs& a, hipStream_t stream) {
   return 0;
 }
 
-int launch_mq_decode(const MqDecodeArgs& a, int head_dim, hipStream_t stream) {
+int launch_mq_decode(const MqDecodeArgs& a, int head_dim, int kv_dtype, hipStream_t stream) {
   if (head_dim != 128) return SPD_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(mq_decode_kernel<128>, dim3((unsigned)(a.batch * a.num_kv_heads * a.blocks_per_row)), dim3(256),
-                     0, stream, a);
+  const dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.blocks_per_row)), block(256);
+  if (kv_dtype == SPD_DTYPE_F16) hipLaunchKernelGGL((mq_decode_kernel<128, SPD_DTYPE_F16>), grid, block, 0, stream, a);
+  else if (kv_dtype == SPD_DTYPE_FP8_E4M3FN)
+    hipLaunchKernelGGL((mq_decode_kernel<128, SPD_DTYPE_FP8_E4M3FN>), grid, block, 0, stream, a);
+  else return SPD_ERR_UNSUPPORTED;
   return 0;
 }
 

@@ -588,7 +588,8 @@ int spd_page_list_union(const spd_desc* desc, int32_t num_tokens, int32_t token_
 }
 
 int spd_sparse_paged_decode_mq(const spd_desc* desc, int32_t num_tokens, const spd_plan_params* plan, const void* q,
-                               const void* k_pool, const void* v_pool, const int32_t* block_table,
+                               const void* k_pool, const void* v_pool, const uint16_t* k_scale,
+                               const uint16_t* v_scale, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* page_list, const int32_t* page_phys,
                                const uint32_t* page_mask, const int32_t* list_len, float sm_scale, float* out,
                                float* out_lse, float* part_o, float* part_lse, void* stream) {
@@ -597,16 +598,19 @@ int spd_sparse_paged_decode_mq(const spd_desc* desc, int32_t num_tokens, const s
   int32_t J;
   if ((rc = plan_j(desc, plan, J))) return rc;
   if (plan->balanced) return SPD_ERR_UNSUPPORTED;
-  if (desc->kv_dtype != SPD_DTYPE_F16 || desc->head_dim != 128) return SPD_ERR_UNSUPPORTED;
+  if (desc->q_dtype != SPD_DTYPE_F16 || desc->head_dim != 128) return SPD_ERR_UNSUPPORTED;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return SPD_ERR_INVALID_ARG;
   if (desc->batch == 0) return SPD_OK;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !page_list || !page_mask || !list_len || !out ||
       !out_lse || !part_o || !part_lse)
     return SPD_ERR_INVALID_ARG;
+  if (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && (!k_scale || !v_scale)) return SPD_ERR_INVALID_ARG;
   spd::MqDecodeArgs a{};
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.page_list = page_list;
@@ -627,7 +631,7 @@ int spd_sparse_paged_decode_mq(const spd_desc* desc, int32_t num_tokens, const s
   a.blocks_per_row = J;
   a.min_chunk = plan->min_chunk;
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
-  return launched(spd::launch_mq_decode(a, desc->head_dim, (hipStream_t)stream));
+  return launched(spd::launch_mq_decode(a, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
 }
 
 int spd_lse_merge_mq(const spd_desc* desc, int32_t num_tokens, const spd_plan_params* plan, const float* part_o,

@@ -168,6 +168,8 @@ struct MqDecodeArgs {
   const void* q;              // [B, T, Hq, d]
   const void* k_pool;
   const void* v_pool;
+  const uint16_t* k_scale;    // fp8 pools
+  const uint16_t* v_scale;
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* page_list;
@@ -182,7 +184,7 @@ struct MqDecodeArgs {
   int blocks_per_row, min_chunk;
   float sm_scale_log2;
 };
-int launch_mq_decode(const MqDecodeArgs& a, int head_dim, hipStream_t stream);
+int launch_mq_decode(const MqDecodeArgs& a, int head_dim, int kv_dtype, hipStream_t stream);
 
 // Moira Eq. 4: chunk size and count of a row of n listed pages.
 __host__ __device__ inline void plan_chunks(int n, int J, int C, int& c, int& m) {

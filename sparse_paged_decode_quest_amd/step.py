@@ -359,7 +359,8 @@ class MQDecodeStep:
 
     def attend(self, stream=None):
         d = self.d
-        A.spd_sparse_paged_decode_mq(self.desc, self.T, self.pp, d.q, d.k_pool, d.v_pool, d.block_table, d.seq_lens,
+        A.spd_sparse_paged_decode_mq(self.desc, self.T, self.pp, d.q, d.k_pool, d.v_pool, d.k_scale, d.v_scale,
+                                     d.block_table, d.seq_lens,
                                      self.page_list, self.page_phys, self.page_mask, self.list_len, self.w.sm_scale,
                                      self.out, self.out_lse, self.part_o, self.part_lse, stream)
         A.spd_lse_merge_mq(self.desc, self.T, self.pp, self.part_o, self.part_lse, self.list_len, self.out,

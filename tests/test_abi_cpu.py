@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 8
+    assert A.abi_version() == 9
 
 
 def test_error_strings(lib):
@@ -338,9 +338,10 @@ def test_several_query_tokens_argument_checks(lib):
                                      p["pm"], p["ll"], 0)
 
     def dec_rc(desc, T=4, pl=plan, **null):
-        p = {k: FAKE for k in ("q", "k", "v", "bt", "sl", "pl", "pp", "pm", "ll", "o", "lse", "po", "pls")}
+        p = {k: FAKE for k in ("q", "k", "v", "ks", "vs", "bt", "sl", "pl", "pp", "pm", "ll", "o", "lse", "po", "pls")}
         p.update(null)
-        return L.spd_sparse_paged_decode_mq(ctypes.byref(desc), T, ctypes.byref(pl), p["q"], p["k"], p["v"], p["bt"],
+        return L.spd_sparse_paged_decode_mq(ctypes.byref(desc), T, ctypes.byref(pl), p["q"], p["k"], p["v"], p["ks"],
+                                            p["vs"], p["bt"],
                                             p["sl"], p["pl"], p["pp"], p["pm"], p["ll"], ctypes.c_float(0.1), p["o"],
                                             p["lse"], p["po"], p["pls"], 0)
 
@@ -355,7 +356,8 @@ def test_several_query_tokens_argument_checks(lib):
     assert union_rc(desc_for(w, max_list=24, max_pages_per_seq=40000)) == A.SPD_ERR_UNSUPPORTED
     assert dec_rc(d, pl=A.PlanParams(4, 16, 512, 1)) == A.SPD_ERR_UNSUPPORTED  # per-row plan only
     assert dec_rc(desc_for(W.small(num_queries=4, d=64), max_list=24)) == A.SPD_ERR_UNSUPPORTED
-    assert dec_rc(desc_for(W.small(num_queries=4, kv="fp8"), max_list=24)) == A.SPD_ERR_UNSUPPORTED
+    assert dec_rc(desc_for(W.small(num_queries=4, kv="f32", q="f32"), max_list=24)) == A.SPD_ERR_UNSUPPORTED
+    assert dec_rc(desc_for(W.small(num_queries=4, kv="fp8"), max_list=24), ks=None) == A.SPD_ERR_INVALID_ARG
     assert dec_rc(d, pm=None) == A.SPD_ERR_INVALID_ARG
     rc = L.spd_lse_merge_mq(ctypes.byref(d), 4, ctypes.byref(plan), FAKE, None, FAKE, FAKE, FAKE, 0)
     assert rc == A.SPD_ERR_INVALID_ARG

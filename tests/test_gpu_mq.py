@@ -38,6 +38,8 @@ MQ_SMALL = {
     "t2": W.small("mq_t2", num_queries=2, seq_lens=(513, 300, 2, 129), budget=9, n_local=3),
     "t3_planted": W.small("mq_t3", num_queries=3, seq_lens=(1500, 250, 31), budget=16, planted=("fixed", 8),
                           delta=3.0),
+    "t4_fp8": W.small("mq_fp8", num_queries=4, kv="fp8", seq_lens=(1500, 250, 31, 3), budget=16,
+                      streaming=(0,), n_sink_stream=1, n_local_stream=2),
 }
 
 
