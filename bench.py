@@ -420,20 +420,26 @@ def bench_mq(args, w, inp, base, plan, gen_s):
     token_len = probe.token_len.cpu().numpy()
     # algorithmic bytes: every token scans the dynamic rows' key boxes; the union pages' K / V are read
     # once for the T tokens; queries, outputs, block-table rows; the rebuilt last two pages
+    kvb = {"f16": 2, "fp8": 1}[w.kv_dtype]
+    page_kv = 16 * d * kvb * 2 + (16 * 2 * 2 if w.kv_dtype == "fp8" else 0)  # K and V (+ fp16 scales)
     meta = T * int(w.n_pages.sum()) * dyn * 2 * d * 2
-    kv = int(union_len.sum()) * 16 * d * 2 * 2
-    per_token_kv = int(token_len.sum()) * 16 * d * 2 * 2  # what T independent decodes would read
+    kv = int(union_len.sum()) * page_kv
+    per_token_kv = int(token_len.sum()) * page_kv  # what T independent decodes would read
     q = w.batch * T * w.num_q_heads * d * 2
     o = w.batch * T * w.num_q_heads * (d + 1) * 4
     tables = T * int(w.n_pages.sum()) * 4
-    tail = w.batch * w.num_kv_heads * 2 * (16 * d * 2 + 2 * d * 2)
+    tail = w.batch * w.num_kv_heads * 2 * (16 * d * kvb + (32 if w.kv_dtype == "fp8" else 0) + 2 * d * 2)
     ab = {"meta": meta, "kv": kv, "q": q, "o": o, "tables": tables, "tail": tail,
           "total": meta + kv + q + o + tables + tail}
     layer_bytes = sum(t.numel() * t.element_size() for t in (base.k_pool, base.v_pool, base.page_meta))
     R = args.layers or int(min(64, max(4, math.ceil((1 << 30) / ab["total"]))))
     R = max(1, min(R, int(100e9 // max(layer_bytes, 1))))
+    def clone(t):
+        return None if t is None else t.clone()
+
     layers = [base] + [S.DeviceInputs(q=base.q.clone(), k_pool=base.k_pool.clone(), v_pool=base.v_pool.clone(),
-                                      k_scale=None, v_scale=None, block_table=base.block_table.clone(),
+                                      k_scale=clone(base.k_scale), v_scale=clone(base.v_scale),
+                                      block_table=base.block_table.clone(),
                                       seq_lens=base.seq_lens.clone(), head_kind=base.head_kind.copy(),
                                       page_meta=base.page_meta.clone()) for _ in range(R - 1)]
     steps = [probe] + [S.MQDecodeStep(w, x, plan=plan) for x in layers[1:]]

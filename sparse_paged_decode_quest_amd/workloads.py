@@ -217,6 +217,11 @@ def named(name: str, seed_offset: int = 0) -> Workload:
                         n_sink=1, n_local=2, n_sink_stream=4, n_local_stream=16,
                         streaming_heads=(0, 1, 2, 3), planted=("fixed", 64), delta=2.0,
                         seed=BASE_SEED + 8 + seed_offset)
+    if name == "mtp4_b1_512k_fp8":
+        # the 512k fp8 layer verifying 4 draft tokens: each token's 256 pages over 32768
+        return Workload(name=name, seq_lens=(524288,), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        kv_dtype="fp8", q_dtype="f16", mode="topk", budget_pages=256, num_queries=4,
+                        n_sink=1, n_local=2, planted=("fixed", 512), delta=2.0, seed=BASE_SEED + 9 + seed_offset)
     if name == "llama3_8b_b1_128k_f16_hier64":
         # the 128k layer with 64-token physical pages scored through 16-token logical pages (LServe,
         # "Hierarchical Paging", N_P = 64, N_L = 16): token budget 4096 = 64 physical pages
@@ -232,7 +237,7 @@ def named(name: str, seed_offset: int = 0) -> Workload:
 
 NAMED = ("tiny_b1_hq8_d64_4k_f32", "llama3_8b_b1_128k_f16", "mixed_b8_bimodal_f16",
          "mixed_b8_powerlaw_f16", "coverage_b4_128k_f16", "fp8_b1_512k", "llama3_8b_b1_128k_f16_dense",
-         "coverage_mvar_b4_128k_f16", "llama3_8b_b1_128k_f16_hier64", "mtp4_b1_128k_f16")
+         "coverage_mvar_b4_128k_f16", "llama3_8b_b1_128k_f16_hier64", "mtp4_b1_128k_f16", "mtp4_b1_512k_fp8")
 
 
 # --------------------------------------------------------------------------------------

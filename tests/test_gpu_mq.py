@@ -155,8 +155,9 @@ def test_mq_every_page_listed_is_dense_causal_attention():
     assert np.all(out[4, :2] == 0)  # two keys, four draft tokens: the first two tokens see no key
 
 
-def test_mq_named_workload_in_the_bench_configuration():
-    w = W.named("mtp4_b1_128k_f16")
+@pytest.mark.parametrize("name", [n for n in W.NAMED if W.named(n).num_queries > 1])
+def test_mq_named_workload_in_the_bench_configuration(name):
+    w = W.named(name)
     inp, d, st = run_case(w)
     meta_ref = O.page_meta_build(inp)
     gpu_lists, ref_lists = check_token_lists(inp, st, meta_ref)
