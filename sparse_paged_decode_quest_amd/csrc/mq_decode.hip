@@ -73,13 +73,21 @@ __global__ __launch_bounds__(kUnionThreads) void page_list_union_kernel(UnionArg
     if (p >= 0 && p < n) atomicOr(&bits[p >> 2], 1u << ((p & 3) * 8 + t));
   }
   __syncthreads();
-  // thread k owns pages [k per, (k + 1) per): count, block scan, write in page order
-  const int per = (n + kUnionThreads - 1) / kUnionThreads;
-  const int p0 = (int)threadIdx.x * per;
+  // thread k owns the words [k per, (k + 1) per) of the byte map (4 pages each; bytes past page n
+  // are zero): count its listed pages, block scan, write them in page order
+  const int words = (n + 3) / 4;
+  const int per = (words + kUnionThreads - 1) / kUnionThreads;
+  const int w0 = (int)threadIdx.x * per;
   uint32_t cnt = 0;
   for (int i = 0; i < per; ++i) {
-    const int p = p0 + i;
-    if (p < n && ((bits[p >> 2] >> ((p & 3) * 8)) & 0xffu)) ++cnt;
+    const int wi = w0 + i;
+    if (wi < words) {
+      uint32_t x = bits[wi];
+      x |= x >> 4;
+      x |= x >> 2;
+      x |= x >> 1;
+      cnt += __popc(x & 0x01010101u);  // bytes that hold any token's bit
+    }
   }
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const uint32_t incl = wave_incl_scan(cnt);
@@ -91,16 +99,22 @@ __global__ __launch_bounds__(kUnionThreads) void page_list_union_kernel(UnionArg
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
   const size_t out_row = (size_t)row * a.max_list;
   for (int i = 0; i < per; ++i) {
-    const int p = p0 + i;
-    if (p >= n) break;
-    const uint32_t m = (bits[p >> 2] >> ((p & 3) * 8)) & 0xffu;
-    if (!m) continue;
-    if (pos < (uint32_t)a.max_list) {
-      a.page_list[out_row + pos] = p;
-      a.page_mask[out_row + pos] = m;
-      if (a.page_phys) a.page_phys[out_row + pos] = bt_row[p];
+    const int wi = w0 + i;
+    if (wi >= words) break;
+    const uint32_t x = bits[wi];
+    if (!x) continue;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t m = (x >> (8 * k)) & 0xffu;
+      if (!m) continue;
+      const int p = 4 * wi + k;
+      if (pos < (uint32_t)a.max_list) {
+        a.page_list[out_row + pos] = p;
+        a.page_mask[out_row + pos] = m;
+        if (a.page_phys) a.page_phys[out_row + pos] = bt_row[p];
+      }
+      ++pos;
     }
-    ++pos;
   }
   if (threadIdx.x == kUnionThreads - 1) a.list_len[row] = (int)min(base + incl, (uint32_t)a.max_list);
 }
