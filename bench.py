@@ -168,6 +168,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--fused", action="store_true", help="scorer and selector in one launch")
+    ap.add_argument("--merged", action="store_true", help="decode and merge in one launch (last-block merge)")
     ap.add_argument("--plan", default=None,
                     help="self-planning constants C,N_J,N_T[,balanced] (default: the step's for the workload)")
     ap.add_argument("--phase-only", default=None,
@@ -214,7 +215,7 @@ def main():
         plan = S.Plan(*v[:3], balanced=bool(v[3]) if len(v) > 3 else False)
     if w.num_queries > 1:
         return bench_mq(args, w, inp, base, plan, gen_s)
-    probe = S.DecodeStep(w, base, plan=plan, fused=args.fused)
+    probe = S.DecodeStep(w, base, plan=plan, fused=args.fused, merged=args.merged)
     probe.run()
     torch.cuda.synchronize()
     ab0 = algorithmic_bytes(w, probe.list_len.cpu().numpy(), inp.head_kind)
@@ -230,7 +231,7 @@ def main():
                                       block_table=clone(base.block_table), seq_lens=clone(base.seq_lens),
                                       head_kind=base.head_kind.copy(), page_meta=clone(base.page_meta))
                        for _ in range(R - 1)]
-    steps = [probe] + [S.DecodeStep(w, d, plan=plan, fused=args.fused) for d in layers[1:]]
+    steps = [probe] + [S.DecodeStep(w, d, plan=plan, fused=args.fused, merged=args.merged) for d in layers[1:]]
     for st in steps:
         st.run()
     torch.cuda.synchronize()
@@ -238,7 +239,8 @@ def main():
     for st in (steps[1 % R], steps[-1]):
         assert st.lists() == ref_lists and torch.equal(st.out, steps[0].out), "layer copies disagree"
 
-    phases = {"decode": lambda st, s: st.decode(s), "merge": lambda st, s: st.merge(s)}
+    phases = ({"decode_merged": lambda st, s: st.attend(s)} if args.merged else
+              {"decode": lambda st, s: st.decode(s), "merge": lambda st, s: st.merge(s)})
     if probe.tail in ("side", "serial"):
         phases["tail"] = lambda st, s: st.refresh_tail(s)
     if not args.fused:
@@ -315,7 +317,7 @@ def main():
     reuse = None
     if w.mode == "topk" and not args.fused and args.reuse > 1:
         C = args.reuse
-        rsteps = [S.DecodeStep(w, d, plan=plan, reuse=C) for d in layers]
+        rsteps = [S.DecodeStep(w, d, plan=plan, reuse=C, merged=args.merged) for d in layers]
         for d in layers:
             d.seq_lens.sub_(C - 1)
         torch.cuda.synchronize()
@@ -388,7 +390,7 @@ def main():
                    "head_dim": w.head_dim, "page": w.page_size, "logical_page": 16, "kv_dtype": w.kv_dtype, "mode": w.mode,
                    "estimator": w.estimator,
                    "budget_pages": w.budget_pages, "gamma": w.gamma, "streaming_kv_heads": len(w.streaming_heads),
-                   "layers_rotated": R, "graph": True, "fused_select": args.fused,
+                   "layers_rotated": R, "graph": True, "fused_select": args.fused, "merged_decode": args.merged,
                    "plan": [probe.plan.min_chunk, probe.plan.min_blocks_per_row, probe.plan.min_grid_blocks,
                             int(probe.plan.balanced)]},
         "step_us": round(step_us, 3), "step_us_spread": spread, "tokens_per_s": round(w.batch / step_s, 1),

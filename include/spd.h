@@ -97,7 +97,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 9
+#define SPD_ABI_VERSION 10
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
@@ -331,6 +331,21 @@ int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, c
                             const int32_t* page_phys, const int32_t* list_len, float sm_scale,
                             float* out, float* out_lse, float* part_o, float* part_lse,
                             void* stream);
+
+/* spd_sparse_paged_decode with the merge in the same launch (a fused decode + merge): each block
+ * of a row with more than one chunk writes its chunk state, makes it visible device-wide and takes
+ * a ticket on its row in counters (device, [B, Hkv] uint32); the block that takes the row's last
+ * ticket merges the row's chunk states exactly (as spd_lse_merge) into out / out_lse and sets the
+ * ticket back to 0.  No block waits for another.  counters must be zero-filled before the first
+ * call and is left zero by every call; calls that share counters must not overlap.  part_o /
+ * part_lse are still needed (the chunk states pass through them).  No spd_lse_merge follows. */
+int spd_sparse_paged_decode_merged(const spd_desc* desc, const spd_plan_params* plan, const void* q,
+                                   const void* k_pool, const void* v_pool, const uint16_t* k_scale,
+                                   const uint16_t* v_scale, const int32_t* block_table,
+                                   const int32_t* seq_lens, const int32_t* page_list,
+                                   const int32_t* page_phys, const int32_t* list_len, float sm_scale,
+                                   float* out, float* out_lse, float* part_o, float* part_lse,
+                                   uint32_t* counters, void* stream);
 
 /* Exact merge of the chunk states of every row with more than one chunk:
  * out_lse = log sum_j exp(lse_j), out = sum_j exp(lse_j - out_lse) * o_j.  Rows with at

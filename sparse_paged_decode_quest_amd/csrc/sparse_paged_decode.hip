@@ -300,7 +300,57 @@ __device__ __forceinline__ PageRef batch_page(int lp, int lph, int i, int n_b, i
   return r;
 }
 
-template <int D, int QD, int KVD>
+// Fused merge (the last-block variant of decode + merge): after writing its chunk state, a block
+// makes it visible device-wide and takes a ticket on its row; the block that takes the last ticket
+// reads every chunk state of the row, merges them exactly (PersistentKV, section 3.3) and leaves the
+// ticket at zero for the next call.  No block waits for another.
+template <int D>
+__device__ __forceinline__ void merge_row_in_block(const DecodeArgs& a, int row, int m, size_t slot_row, size_t qrow) {
+  __shared__ int last;
+  __shared__ float w_s[kMaxChunks][kGq];  // chunk weights exp(lse_j - M_g); m <= kMaxChunks in both plans
+  __shared__ float mg[kGq], sg[kGq];
+  __threadfence();  // release this block's chunk state (agent scope)
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(&a.counters[row], 1u) == (unsigned)(m - 1);
+  __syncthreads();
+  if (!last) return;
+  __threadfence();  // acquire the other blocks' chunk states
+  // every chunk log-sum-exp at once; wave g folds head g's max and weight sum
+  for (int e = threadIdx.x; e < m * kGq; e += blockDim.x) w_s[e / kGq][e % kGq] = a.part_lse[slot_row * kGq + e];
+  __syncthreads();
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;  // 4 waves, one per head
+  {
+    float M = -INFINITY;
+    for (int jj = lane; jj < m; jj += kWave) M = fmaxf(M, w_s[jj][wave]);
+    M = wave_max_f(M);
+    float S = 0.f;
+    for (int jj = lane; jj < m; jj += kWave) {
+      const float w = M == -INFINITY ? 0.f : expf(w_s[jj][wave] - M);
+      w_s[jj][wave] = w;
+      S += w;
+    }
+    S = wave_sum_f(S);
+    if (lane == 0) {
+      mg[wave] = M;
+      sg[wave] = S;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < kGq * D; e += blockDim.x) {
+    const int g = e / D, ch = e % D;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int jj = 0; jj < m; ++jj) acc = fmaf(w_s[jj][g], a.part_o[((slot_row + jj) * kGq + g) * D + ch], acc);
+    const bool empty = mg[g] == -INFINITY;
+    a.out[(qrow + g) * D + ch] = empty ? 0.f : acc / sg[g];
+    if (ch == 0) a.out_lse[qrow + g] = empty ? -INFINITY : mg[g] + logf(sg[g]);
+  }
+  if (threadIdx.x == 0) a.counters[row] = 0u;
+}
+
+// MERGE: the row's chunk states are merged by the last of its blocks to finish (a ticket per row in
+// a.counters), in the same launch; see merge_row_in_block.
+template <int D, int QD, int KVD, bool MERGE = false>
 __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) {
   using T = DecTraits<D, QD, KVD>;
   constexpr int CPL = T::CPL;
@@ -540,6 +590,9 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
       if (ch == 0) a.part_lse[slot] = lse;
     }
   }
+  if constexpr (MERGE) {
+    if (m > 1) merge_row_in_block<D>(a, row, m, slot_row, qrow);
+  }
 }
 
 // Exact merge of a row's chunk states (PersistentKV, section 3.3; states are stored
@@ -651,10 +704,11 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
 int launch_sparse_paged_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype, hipStream_t stream) {
   // per-row plan: rows x J blocks; balanced plan: blocks_per_row holds the whole grid N_T + rows
   dim3 grid((unsigned)(a.balanced ? a.blocks_per_row : a.batch * a.num_kv_heads * a.blocks_per_row)), block(256);
-#define SPD_DEC_CASE(D, QD, KVD)                                                                 \
-  if (head_dim == D && q_dtype == QD && kv_dtype == KVD) {                                       \
-    hipLaunchKernelGGL((sparse_paged_decode_kernel<D, QD, KVD>), grid, block, 0, stream, a);     \
-    return 0;                                                                                    \
+#define SPD_DEC_CASE(D, QD, KVD)                                                                      \
+  if (head_dim == D && q_dtype == QD && kv_dtype == KVD) {                                            \
+    if (a.counters) hipLaunchKernelGGL((sparse_paged_decode_kernel<D, QD, KVD, true>), grid, block, 0, stream, a); \
+    else hipLaunchKernelGGL((sparse_paged_decode_kernel<D, QD, KVD, false>), grid, block, 0, stream, a);           \
+    return 0;                                                                                         \
   }
   SPD_DEC_CASE(64, SPD_DTYPE_F32, SPD_DTYPE_F32)
   SPD_DEC_CASE(128, SPD_DTYPE_F32, SPD_DTYPE_F32)

@@ -472,11 +472,11 @@ int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, co
   return launched(spd::launch_page_score_select(f, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
 }
 
-int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, const void* q, const void* k_pool,
-                            const void* v_pool, const uint16_t* k_scale, const uint16_t* v_scale,
-                            const int32_t* block_table, const int32_t* seq_lens, const int32_t* page_list,
-                            const int32_t* page_phys, const int32_t* list_len, float sm_scale, float* out,
-                            float* out_lse, float* part_o, float* part_lse, void* stream) {
+static int decode_impl(const spd_desc* desc, const spd_plan_params* plan, const void* q, const void* k_pool,
+                       const void* v_pool, const uint16_t* k_scale, const uint16_t* v_scale,
+                       const int32_t* block_table, const int32_t* seq_lens, const int32_t* page_list,
+                       const int32_t* page_phys, const int32_t* list_len, float sm_scale, float* out,
+                       float* out_lse, float* part_o, float* part_lse, uint32_t* counters, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   int32_t J;
@@ -514,8 +514,29 @@ int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, c
   a.grid_target = plan->min_grid_blocks;
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   a.lgs = lgs_of(desc);
+  a.counters = counters;
   return launched(spd::launch_sparse_paged_decode(a, desc->head_dim, desc->q_dtype, desc->kv_dtype,
                                                   (hipStream_t)stream));
+}
+
+int spd_sparse_paged_decode(const spd_desc* desc, const spd_plan_params* plan, const void* q, const void* k_pool,
+                            const void* v_pool, const uint16_t* k_scale, const uint16_t* v_scale,
+                            const int32_t* block_table, const int32_t* seq_lens, const int32_t* page_list,
+                            const int32_t* page_phys, const int32_t* list_len, float sm_scale, float* out,
+                            float* out_lse, float* part_o, float* part_lse, void* stream) {
+  return decode_impl(desc, plan, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, page_list, page_phys,
+                     list_len, sm_scale, out, out_lse, part_o, part_lse, nullptr, stream);
+}
+
+int spd_sparse_paged_decode_merged(const spd_desc* desc, const spd_plan_params* plan, const void* q,
+                                   const void* k_pool, const void* v_pool, const uint16_t* k_scale,
+                                   const uint16_t* v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* page_list, const int32_t* page_phys, const int32_t* list_len,
+                                   float sm_scale, float* out, float* out_lse, float* part_o, float* part_lse,
+                                   uint32_t* counters, void* stream) {
+  if (!counters && desc && desc->batch > 0) return SPD_ERR_INVALID_ARG;
+  return decode_impl(desc, plan, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, page_list, page_phys,
+                     list_len, sm_scale, out, out_lse, part_o, part_lse, counters, stream);
 }
 
 int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float* part_o, const float* part_lse,

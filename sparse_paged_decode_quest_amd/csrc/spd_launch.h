@@ -132,6 +132,7 @@ struct DecodeArgs {
   int balanced, grid_target;  // step-wide split over grid_target (N_T) + rows blocks
   float sm_scale_log2;  // softmax scale times log2(e)
   int lgs;              // log2 of logical pages per physical page: each list entry is 2^lgs work units
+  unsigned int* counters;  // [B, Hkv] row tickets (zero between calls): set = merge in the same launch
 };
 int launch_sparse_paged_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype,
                                hipStream_t stream);

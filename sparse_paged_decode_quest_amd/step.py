@@ -141,7 +141,8 @@ class DecodeStep:
     """
 
     def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, fused: bool = False,
-                 tail: str = "auto", phys_lists: bool = True, keep_sel_scores: bool = False, reuse: int = 1):
+                 tail: str = "auto", phys_lists: bool = True, keep_sel_scores: bool = False, reuse: int = 1,
+                 merged: bool = False):
         if tail not in TAILS:
             raise ValueError(f"tail must be one of {TAILS}")
         skippable = w.mode == "topk" and w.n_local >= 1
@@ -186,6 +187,9 @@ class DecodeStep:
         op = A.OP_PAGE_SCORE_SELECT if self.fused else A.OP_PAGE_SCORE
         self.ws_bytes = A.spd_workspace_bytes(self.desc, self.sel, op)
         self.workspace = torch.zeros(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+        # merged: decode and merge in one launch (row tickets, zero between calls)
+        self.merged = merged
+        self.counters = torch.zeros((B, Hkv), **i32) if merged else None
 
     def refresh_tail(self, stream=None):
         """Summary of the page the newest token is in (one page per request, all heads)."""
@@ -233,6 +237,13 @@ class DecodeStep:
                         stream)
 
     def attend(self, stream=None):
+        if self.merged:
+            d = self.d
+            A.spd_sparse_paged_decode_merged(self.desc, self.pp, d.q, d.k_pool, d.v_pool, d.k_scale, d.v_scale,
+                                             d.block_table, d.seq_lens, self.page_list, self.page_phys, self.list_len,
+                                             self.w.sm_scale, self.out, self.out_lse, self.part_o, self.part_lse,
+                                             self.counters, stream)
+            return
         self.decode(stream)
         self.merge(stream)
 
