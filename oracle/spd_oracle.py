@@ -584,13 +584,51 @@ def hier_row_shares(inp, meta: np.ndarray, b: int, h: int):
     return np.array([pi_log[j * g:(j + 1) * g].sum() for j in range(hier_n_physical(L, NP))]), lse
 
 
+def hier_stats_build(inp, stats: np.ndarray | None = None, first_page=None) -> np.ndarray:
+    """Moira's page summaries per 16-token logical page (mean and variance of its valid keys, stored in
+    bf16), kept with the physical page that holds it: layout [num_pool_pages, Hkv, g, 2, d] float64
+    holding bf16 values; entries not visited are NaN, or keep their values in ``stats``."""
+    Npool, Hkv, NP, d = inp.k_pool.shape
+    g = NP // PAGE
+    out = np.full((Npool, Hkv, g, 2, d), np.nan) if stats is None else np.array(stats, dtype=np.float64)
+    for b in range(len(inp.seq_lens)):
+        start = 0 if first_page is None else max(0, int(first_page[b]))
+        for lp in range(start, n_pages(inp.seq_lens[b])):
+            phys = int(inp.block_table[b, lp // g])
+            for h in range(Hkv):
+                keys = hier_logical_keys(inp, b, h, lp)
+                mu, var = page_mean_var(keys, len(keys))
+                out[phys, h, lp % g, 0], out[phys, h, lp % g, 1] = round_bf16(mu), round_bf16(var)
+    return out
+
+
+def hier_row_shares_mvar(inp, stats: np.ndarray, b: int, h: int):
+    """Coverage shares of the physical pages of dynamic row (b, h) under the mvar estimate: Eq. 2 for every
+    logical page from its summary, the row's first and current logical pages computed exactly, the group-
+    mean share of each logical page, summed over the logical pages of each physical page."""
+    w = inp.workload
+    G = w.group
+    NP = physical_page_tokens(inp)
+    g = NP // PAGE
+    L = int(inp.seq_lens[b])
+    n_log = n_pages(L)
+    lps = np.arange(n_log)
+    st = stats[inp.block_table[b, lps // g].astype(np.int64), h, lps % g]
+    q = inp.q[b, h * G:(h + 1) * G].astype(np.float64)
+    valid = np.array([valid_tokens(L, p) for p in lps], dtype=np.float64)
+    ell = mvar_logmass(q, st[:, 0], st[:, 1], valid, w.sm_scale)
+    for p in sorted({0, n_log - 1}):
+        ell[:, p] = exact_logmass(q, hier_logical_keys(inp, b, h, p), w.sm_scale)
+    pi_log, lse = shares_from_logmass(ell)
+    return np.array([pi_log[j * g:(j + 1) * g].sum() for j in range(hier_n_physical(L, NP))]), lse
+
+
 def hier_page_select(inp, meta: np.ndarray):
     """Lists of physical pages for every row: streaming rows keep their sink + local physical
     pages; dynamic rows the forced physical pages plus the best others under the physical page
     budget (top-K by (score desc, page asc)), or the coverage rule over physical shares.  Same
     dict as page_select."""
     w = inp.workload
-    assert w.estimator == "bound", "hierarchical paging scores pages from their key boxes"
     NP = physical_page_tokens(inp)
     out = {"lists": {}, "scores": {}, "S": {}, "lse": {}}
     for b in range(len(inp.seq_lens)):
@@ -608,7 +646,7 @@ def hier_page_select(inp, meta: np.ndarray):
             elif n == 0:
                 out["scores"][(b, h)], out["lse"][(b, h)], out["lists"][(b, h)] = np.zeros(0), np.full(w.group, -np.inf), []
             else:
-                pi, lse = hier_row_shares(inp, meta, b, h)
+                pi, lse = (hier_row_shares_mvar if w.estimator == "mvar" else hier_row_shares)(inp, meta, b, h)
                 out["scores"][(b, h)], out["lse"][(b, h)] = pi, lse
                 out["lists"][(b, h)] = select_coverage(pi, n, w.gamma, forced)
     return out
@@ -655,7 +693,7 @@ def decode_step(inp, meta: np.ndarray | None = None):
     """Metadata (if not given) -> scores -> lists -> attention, as the method orders them."""
     if physical_page_tokens(inp) != PAGE:  # hierarchical paging
         if meta is None:
-            meta = hier_meta_build(inp)
+            meta = hier_stats_build(inp) if inp.workload.estimator == "mvar" else hier_meta_build(inp)
         sel = hier_page_select(inp, meta)
         O, lse = hier_sparse_paged_decode(inp, sel["lists"], inp.workload.sm_scale)
         return {"meta": meta, **sel, "O": O, "out_lse": lse}

@@ -227,3 +227,31 @@ def test_coverage_gamma_one_lists_every_physical_page_and_equals_dense():
             for g in range(G):
                 o_ref, lse_ref = _sdpa(inp.q[b, h * G + g].astype(np.float64), K, V, w.sm_scale)
                 assert np.allclose(res["O"][b, h * G + g], o_ref, rtol=0, atol=1e-12)
+
+
+def test_mvar_shares_are_the_flat_mvar_logical_shares_summed_per_physical_page():
+    w = _hier(mode="coverage", estimator="mvar", gamma=0.9, n_local=1, planted=("fixed", 5), delta=("nats", 6.0))
+    inp = W.generate(w)
+    flat = _flat_relayout(inp)
+    st_h = O.hier_stats_build(inp)
+    st_f = O.page_stats_build(flat)
+    for b, L in enumerate(w.seq_lens):
+        for h in range(w.num_kv_heads):
+            pi, lse = O.hier_row_shares_mvar(inp, st_h, b, h)
+            pi_f, lse_f = O.shares_from_logmass(O.row_logmass_mvar(flat, st_f, b, h))
+            assert np.array_equal(lse, lse_f)
+            assert np.allclose(pi, [pi_f[4 * j:4 * j + 4].sum() for j in range(-(-L // NP))], rtol=0, atol=1e-15)
+
+
+def test_mvar_gamma_one_lists_every_physical_page_and_equals_dense():
+    w = _hier(mode="coverage", estimator="mvar", gamma=1.0, n_local=1, seq_lens=(333, 64, 17))
+    inp = W.generate(w)
+    res = O.decode_step(inp)
+    G = w.group
+    for b, L in enumerate(w.seq_lens):
+        for h in range(w.num_kv_heads):
+            assert res["lists"][(b, h)] == list(range(-(-L // NP)))
+            K, V = _dense_unpaged(inp, b, h)
+            for g in range(G):
+                o_ref, _ = _sdpa(inp.q[b, h * G + g].astype(np.float64), K, V, w.sm_scale)
+                assert np.allclose(res["O"][b, h * G + g], o_ref, rtol=0, atol=1e-12)
