@@ -156,8 +156,8 @@ typedef enum spd_op {
 
 /* Shapes of one step.  Supported: page_size 16 or 64; head_dim 64 or 128; Hq / Hkv = 4;
  * (q_dtype, kv_dtype) in {(f32, f32), (f16, f16), (f16, fp8)}.  page_size 64 (hierarchical
- * paging) supports both rules with the BOUND estimator, tail modes NONE and SKIP, and the
- * unfused entry points; f32 pools need head_dim 64 there.  Others return SPD_ERR_UNSUPPORTED so
+ * paging) supports both rules and both estimators (summaries and estimates per 16-token logical
+ * page), tail modes NONE and SKIP, and the unfused entry points; f32 pools need head_dim 64 there.  Others return SPD_ERR_UNSUPPORTED so
  * a caller can route them elsewhere. */
 typedef struct spd_desc {
   int32_t batch;              /* B >= 0 */

@@ -150,7 +150,7 @@ __device__ __forceinline__ void mvar_block_ell(const ScoreArgs& a, const int (&r
   typename T::M m[ITERS];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it)
-    if (ok[it]) T::load_m(m[it], a.meta, ((size_t)raw[it] * a.num_kv_heads + h) * 2 * D, c0);
+    if (ok[it]) T::load_m(m[it], a.meta, head_unit(raw[it], a.num_kv_heads, h, a.lgs, pg[it] & ((1 << a.lgs) - 1)) * 2 * D, c0);
   const size_t row = (size_t)b * a.num_kv_heads + h;
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
@@ -164,7 +164,7 @@ __device__ __forceinline__ void mvar_block_ell(const ScoreArgs& a, const int (&r
     for (int g = 0; g < kG; ++g) s[g] = group_sum<LPP>(s[g]);
     if (sub == 0 && pg[it] >= 1 && pg[it] < n_est) {
       const float lv = ln_tokens(valid_in_page(len, pg[it]));
-      a.ell[row * a.max_pages + pg[it]] =
+      a.ell[row * ell_stride(a) + pg[it]] =
           ok[it] ? make_float4(s[0] + lv, s[1] + lv, s[2] + lv, s[3] + lv)
                  : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);  // page outside the pool
     }
@@ -182,7 +182,7 @@ __device__ __forceinline__ void mvar_exact_pages(const ScoreArgs& a, const int32
   static_assert(kPage * LPT <= kScoreWaves * kWave, "one token row per LPT threads");
   __shared__ float red_m[kScoreWaves][kG], red_s[kScoreWaves][kG];
   const int len = a.seq_lens[b];
-  const int n = row_pages(len, a.max_pages);
+  const int n = row_logical_pages(len, a.max_pages, a.lgs);  // 16-token pages (hierarchical paging too)
   if (n <= 0) return;  // uniform
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int t = threadIdx.x / LPT, sub = threadIdx.x % LPT;
@@ -193,12 +193,12 @@ __device__ __forceinline__ void mvar_exact_pages(const ScoreArgs& a, const int32
   const int pages = n > 1 ? 2 : 1;
   for (int k = 0; k < pages; ++k) {
     const int p = k == 0 ? 0 : n - 1;
-    const int phys = bt_row[p];
+    const int phys = bt_row[p >> a.lgs];
     const bool tok = phys >= 0 && phys < a.num_pool_pages && t < valid_in_page(len, p);
     float x[kG];
     if (tok) {
       float kv[T::CW];
-      T::load_key(kv, a.k_pool, a.k_scale, (size_t)phys * a.num_kv_heads + h, t, c0);
+      T::load_key(kv, a.k_pool, a.k_scale, head_unit(phys, a.num_kv_heads, h, a.lgs, p & ((1 << a.lgs) - 1)), t, c0);
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
         float acc = 0.f;
@@ -230,7 +230,7 @@ __device__ __forceinline__ void mvar_exact_pages(const ScoreArgs& a, const int32
         for (int w = 0; w < kScoreWaves; ++w) lse_combine(m, s, red_m[w][g], red_s[w][g]);
         lg[g] = m == -INFINITY ? -INFINITY : m + logf(s);
       }
-      a.ell[row * a.max_pages + p] = make_float4(lg[0], lg[1], lg[2], lg[3]);
+      a.ell[row * ell_stride(a) + p] = make_float4(lg[0], lg[1], lg[2], lg[3]);
     }
     __syncthreads();
   }
@@ -244,6 +244,7 @@ __device__ __forceinline__ void mvar_exact_pages(const ScoreArgs& a, const int32
     m.num_kv_heads = a.num_kv_heads;
     m.max_pages = a.max_pages;
     m.num_pool_pages = a.num_pool_pages;
+    m.lgs = a.lgs;
     build_page_stats<D, KVD>(m, b, n - 1, h, len);
   }
 }
@@ -268,9 +269,9 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_mvar_kernel(Sc
   int raw[ITERS];  // block-table entries, read before the request's length (clamped into the row)
 #pragma unroll
   for (int it = 0; it < ITERS; ++it)
-    raw[it] = bt_row[min(p_begin + (it * kScoreWaves + wave) * T::PPI + lane / T::LPP, a.max_pages - 1)];
+    raw[it] = bt_row[min((p_begin + (it * kScoreWaves + wave) * T::PPI + lane / T::LPP) >> a.lgs, a.max_pages - 1)];
   const int len = a.seq_lens[b];
-  const int n = row_pages(len, a.max_pages);
+  const int n = row_logical_pages(len, a.max_pages, a.lgs);
   if (p_begin >= n - 1) return;  // uniform: nothing to estimate here
   mvar_block_ell<D, KVD, ITERS>(a, raw, n - 1, len, b, h, p_begin);
 }
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_mvar_kernel(Sc
 int launch_page_score_mvar(const ScoreArgs& a, int head_dim, int kv_dtype, hipStream_t stream) {
   const unsigned rows = (unsigned)(a.batch * a.dyn.count);
   const dim3 grid(rows * (unsigned)(a.blocks_per_row + 1)), block(kScoreWaves * kWave);
-  const bool long_scan = score_iters((long long)rows * a.max_pages) == kScoreItersLong;
+  const bool long_scan = score_iters((long long)rows * ((long long)a.max_pages << a.lgs)) == kScoreItersLong;
 #define SPD_MVAR_CASE(D, KVD)                                                                                        \
   if (head_dim == D && kv_dtype == KVD) {                                                                            \
     if (long_scan) hipLaunchKernelGGL((page_score_mvar_kernel<D, KVD, kScoreItersLong>), grid, block, 0, stream, a);  \

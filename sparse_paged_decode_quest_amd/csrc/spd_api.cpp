@@ -78,7 +78,6 @@ int check_sel(const spd_desc* d, const spd_select_params* s) {
   }
   if (s->estimator != SPD_ESTIMATOR_BOUND && s->estimator != SPD_ESTIMATOR_MVAR) return SPD_ERR_INVALID_ARG;
   if (s->estimator == SPD_ESTIMATOR_MVAR && s->mode != SPD_SELECT_COVERAGE) return SPD_ERR_INVALID_ARG;
-  if (is_hier(d) && is_mvar(s)) return SPD_ERR_UNSUPPORTED;  // 64-token pages: key-box estimates only
   return SPD_OK;
 }
 
@@ -255,7 +254,6 @@ int build_summaries(const spd_desc* desc, const void* k_pool, const uint16_t* k_
   if (!k_pool || !block_table || !seq_lens || !out) return SPD_ERR_INVALID_ARG;
   if (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale) return SPD_ERR_INVALID_ARG;
   if ((first_page && span_pages < 1) || span_pages < 0) return SPD_ERR_INVALID_ARG;
-  if (stats && is_hier(desc)) return SPD_ERR_UNSUPPORTED;
   spd::MetaArgs a = meta_args(desc, k_pool, k_scale, block_table, seq_lens, out);
   a.first_page = first_page;
   a.stats = stats;

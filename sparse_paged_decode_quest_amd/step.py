@@ -149,7 +149,8 @@ class DecodeStep:
         if fused and w.estimator == "mvar":
             raise ValueError("the fused score + select launch has no mvar estimator")
         if tail == "auto":
-            tail = ("rebuild" if fused else "select") if skippable else "rebuild" if w.estimator == "mvar" else "serial"
+            tail = (("rebuild" if fused else "select") if skippable else
+                    "rebuild" if w.estimator == "mvar" and w.page_size == 16 else "serial")
         if tail in ("select", "side") and not skippable:
             raise ValueError(f"tail={tail!r} skips the last page: top-K with a local window only")
         if tail == "select" and fused:

@@ -299,12 +299,14 @@ def test_plan_grid_formula(lib):
 
 
 def test_hierarchical_paging_argument_checks(lib):
-    """64-token physical pages (LServe, "Hierarchical Paging"): both rules with the key-box bound,
-    the unfused entry points and tail modes NONE / SKIP; everything else is reported unsupported."""
+    """64-token physical pages (LServe, "Hierarchical Paging"): both rules, both estimators, the
+    unfused entry points and tail modes NONE / SKIP; everything else is reported unsupported."""
     w = W.small(page_size=64, budget=6, n_local=1)
     d = desc_for(w, page_size=64)
     cov = sel_for(w, mode=A.SELECT_COVERAGE, gamma=0.9)
-    assert score_rc(d, sel_for(w, mode=A.SELECT_COVERAGE, gamma=0.9, estimator=A.ESTIMATOR_MVAR)) == A.SPD_ERR_UNSUPPORTED
+    mv = sel_for(w, mode=A.SELECT_COVERAGE, gamma=0.9, estimator=A.ESTIMATOR_MVAR)
+    assert score_rc(d, mv, tail=A.TAIL_REBUILD) == A.SPD_ERR_UNSUPPORTED  # the in-scorer rebuild: 16-token pages
+    assert score_rc(d, mv, k_pool=None) == A.SPD_ERR_INVALID_ARG          # exact first / current pages need keys
     assert select_rc(desc_for(w, page_size=64, max_list=w.pages_per_seq - 1), cov) == A.SPD_ERR_INVALID_ARG
     assert score_rc(d, cov, ws_bytes=A.spd_workspace_bytes(d, cov, A.OP_PAGE_SCORE) - 1) == A.SPD_ERR_WORKSPACE
     # the coverage log-masses are kept per logical page: four times the 16-token layout's workspace
@@ -314,8 +316,8 @@ def test_hierarchical_paging_argument_checks(lib):
     assert fused_rc(d, sel_for(w)) == A.SPD_ERR_UNSUPPORTED
     assert A.lib().spd_workspace_bytes(ctypes.byref(d), ctypes.byref(sel_for(w)), A.OP_PAGE_SCORE_SELECT) == \
         ctypes.c_size_t(-1).value
-    rc = A.lib().spd_page_stats_build(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 0)
-    assert rc == A.SPD_ERR_UNSUPPORTED
+    rc = A.lib().spd_page_stats_build(ctypes.byref(d), None, FAKE, FAKE, FAKE, None, 0, FAKE, 0)
+    assert rc == A.SPD_ERR_INVALID_ARG
     # f32 pools at d = 128: a logical page's key box spans 32 lanes, more than hierarchical scoring folds
     w32 = W.small(page_size=64, kv="f32", q="f32", d=128, budget=6, n_local=1)
     assert score_rc(desc_for(w32, page_size=64), sel_for(w32)) == A.SPD_ERR_UNSUPPORTED

@@ -272,3 +272,39 @@ def test_hier_named_workload_in_the_bench_configuration():
     for (b, h) in oracle_lists:
         sl = slice(h * G, (h + 1) * G)
         P.check_attention(out[b, sl], out_lse[b, sl], o_ref[b, sl], lse_ref[b, sl], w.kv_dtype, f"lists {b},{h}")
+
+
+@pytest.mark.parametrize("seq", [(1200, 333, 64, 1), (20000, 5000)], ids=["ragged", "long"])
+def test_hier_mvar_summaries_shares_lists_attention(seq):
+    """Moira's mvar estimate over 64-token pages: bf16 summaries per 16-token logical page, Eq. 2 per
+    logical page (the first and current logical pages exact), page share = the sum of its logical
+    pages' shares."""
+    w = W.small("h_mvar", page_size=NP, mode="coverage", estimator="mvar", gamma=0.95, n_local=1, seq_lens=seq,
+                planted=("fixed", 12), delta=("nats", 6.0))
+    inp, d, st = run_case(w)
+    assert st.tail == "serial"
+    stats_ref = O.hier_stats_build(inp)
+    got = d.page_meta.float().cpu().numpy()
+    built = np.isfinite(stats_ref)
+    assert np.array_equal(got[built], stats_ref[built]), "page summaries differ"
+    scores = st.scores.cpu().numpy()
+    lists = st.lists()
+    oracle_lists = {}
+    for b, L in enumerate(w.seq_lens):
+        n = O.hier_n_physical(L, NP)
+        for h in range(w.num_kv_heads):
+            forced = O.forced_pages(n, w.n_sink, w.n_local)
+            if n == 0:
+                oracle_lists[(b, h)] = []
+                continue
+            pi, _ = O.hier_row_shares_mvar(inp, stats_ref, b, h)
+            P.check_coverage_shares(scores[b, h, :n], pi)
+            P.check_coverage_list(lists[(b, h)], pi, n, w.gamma, forced)
+            oracle_lists[(b, h)] = O.select_coverage(pi, n, w.gamma, forced)
+    o_ref, lse_ref = O.hier_sparse_paged_decode(inp, oracle_lists, w.sm_scale)
+    set_lists(st, oracle_lists)
+    st.out.fill_(float("nan"))
+    st.out_lse.fill_(float("nan"))
+    st.attend()
+    torch.cuda.synchronize()
+    P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), o_ref, lse_ref, w.kv_dtype, "mvar lists")
