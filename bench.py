@@ -58,9 +58,12 @@ def algorithmic_bytes(w, list_len: np.ndarray, head_kind: np.ndarray) -> dict:
     meta_bytes = 4 if w.kv_dtype == "f32" else 2
     n_pages = w.n_pages  # physical pages (block-table slots)
     dyn_heads = int((head_kind == 0).sum())
-    meta = int(w.n_logical.sum()) * dyn_heads * 2 * d * meta_bytes  # one key box per 16-token logical page
+    # one key box per 16-token logical page, except the newest one of each request: its statistics are
+    # rebuilt from its keys (the tail term), so its stored box need not be read
+    rebuilt_rows = int((w.n_logical > 0).sum()) * dyn_heads
+    meta = (int(w.n_logical.sum()) * dyn_heads - rebuilt_rows) * 2 * d * meta_bytes
     key_page = 16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0)
-    tail = w.batch * dyn_heads * (key_page + 2 * d * meta_bytes)
+    tail = rebuilt_rows * (key_page + 2 * d * meta_bytes)
     if w.estimator == "mvar":  # bf16 summaries; the first and current pages read as keys, one summary written
         meta = int(np.maximum(n_pages - 2, 0).sum()) * dyn_heads * 2 * d * 2
         tail = dyn_heads * int(np.minimum(n_pages, 2).sum()) * key_page + w.batch * dyn_heads * 2 * d * 2
@@ -100,12 +103,14 @@ def scorer_bytes(w, head_kind: np.ndarray, tail: str) -> int:
         skip = 1 if tail in ("side", "select") else 0
         logical = sum(min(int(nl), g * max(int(npg) - skip, 0)) for nl, npg in zip(w.n_logical, w.n_pages))
         return dyn_heads * (logical * 2 * d * meta_bytes + int(w.n_pages.sum()) * 8) + q
+    # every scanned (page, dynamic head) pair reads its block-table entry and writes its score; the meta
+    # row of each row's last page is not read when the scorer skips that page or rebuilds it from its keys
     rows = int((w.n_pages > 0).sum()) * dyn_heads
-    scanned = int(w.n_pages.sum()) * dyn_heads - (rows if tail in ("side", "rebuild") else 0)
-    per_page_head = 2 * d * meta_bytes + 4 + 4  # meta row + block-table entry + score
-    rebuilt = rows * (16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0) + 2 * d * meta_bytes + 4 + 4) \
+    pairs = int(w.n_pages.sum()) * dyn_heads
+    meta_rows = pairs - (rows if tail in ("side", "select", "rebuild") else 0)
+    rebuilt = rows * (16 * d * kv_bytes + (32 if w.kv_dtype == "fp8" else 0) + 2 * d * meta_bytes) \
         if tail == "rebuild" else 0
-    return scanned * per_page_head + q + rebuilt
+    return pairs * (4 + 4) + meta_rows * 2 * d * meta_bytes + q + rebuilt
 
 
 def copy_bandwidth(stream, mib: int = 1024, reps: int = 10) -> float:
