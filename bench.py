@@ -425,16 +425,17 @@ def bench_mq(args, w, inp, base, plan, gen_s):
     dyn = int((inp.head_kind == 0).sum())
     union_len = probe.list_len.cpu().numpy()
     token_len = probe.token_len.cpu().numpy()
-    # algorithmic bytes: every token scans the dynamic rows' key boxes; the union pages' K / V are read
-    # once for the T tokens; queries, outputs, block-table rows; the rebuilt last two pages
+    # algorithmic bytes: the dynamic rows' key boxes, read once for the T tokens (one scan scores every
+    # token row); the union pages' K / V, read once for the T tokens; queries, outputs, block-table rows;
+    # the rebuilt last two pages
     kvb = {"f16": 2, "fp8": 1}[w.kv_dtype]
     page_kv = 16 * d * kvb * 2 + (16 * 2 * 2 if w.kv_dtype == "fp8" else 0)  # K and V (+ fp16 scales)
-    meta = T * int(w.n_pages.sum()) * dyn * 2 * d * 2
+    meta = int(w.n_pages.sum()) * dyn * 2 * d * 2
     kv = int(union_len.sum()) * page_kv
     per_token_kv = int(token_len.sum()) * page_kv  # what T independent decodes would read
     q = w.batch * T * w.num_q_heads * d * 2
     o = w.batch * T * w.num_q_heads * (d + 1) * 4
-    tables = T * int(w.n_pages.sum()) * 4
+    tables = int(w.n_pages.sum()) * 4
     tail = w.batch * w.num_kv_heads * 2 * (16 * d * kvb + (32 if w.kv_dtype == "fp8" else 0) + 2 * d * 2)
     ab = {"meta": meta, "kv": kv, "q": q, "o": o, "tables": tables, "tail": tail,
           "total": meta + kv + q + o + tables + tail}
@@ -507,8 +508,9 @@ def bench_mq(args, w, inp, base, plan, gen_s):
                "sample": f"{n} whole steps of {w.name} ({T} query tokens: last-page statistics, each token's "
                          f"scores and selection, attention; fp64 numpy, 1 thread) in {el:.1f} s",
                "step_ms": round(el / n * 1e3, 2)}
-    # the scan of T token rows is the kernel that moves the most bytes
-    sc_bytes = meta + tables + q + T * int(w.n_pages.sum()) * dyn * 4
+    # the scan of the T token rows is the kernel that moves the most bytes: key boxes and block-table
+    # entries of every (page, dynamic head), the queries, T scores per (page, dynamic head)
+    sc_bytes = meta + int(w.n_pages.sum()) * dyn * (4 + 4 * T) + w.batch * T * dyn * w.group * d * 2
     line = {
         "metric": METRIC, "value": round(ab["total"] / step_s / 1e12, 4), "unit": "TB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 6), "higher_is_better": True,
@@ -522,7 +524,7 @@ def bench_mq(args, w, inp, base, plan, gen_s):
         "bytes_per_step": ab, "kv_bytes_without_union": per_token_kv, "frac_of_peak": round(ab["total"] / step_s / 1e12 / PEAK_HBM_TBS, 4),
         "beta_copy_TBs": round(beta, 3), "phase_us": {k: round(v, 3) for k, v in phase_us.items()},
         "union_len": {"min": int(union_len.min()), "median": int(np.median(union_len)), "max": int(union_len.max())},
-        "roofline": {"bound": "hbm", "kernel": "page_score_kernel (B x T token rows)",
+        "roofline": {"bound": "hbm", "kernel": "mq_page_score_kernel (T token rows per scan)",
                      "achieved": round(sc_bytes / (phase_us["score"] * 1e-6) / 1e9, 1), "peak": PEAK_HBM_TBS * 1000,
                      "unit": "GB/s", "frac": round(sc_bytes / (phase_us["score"] * 1e-6) / 1e9 / (PEAK_HBM_TBS * 1000), 4),
                      "traffic": None, "algorithmic_bytes_per_launch": sc_bytes, "avg_launch_us": round(phase_us["score"], 3)},

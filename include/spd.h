@@ -97,7 +97,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 10
+#define SPD_ABI_VERSION 11
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
@@ -361,15 +361,31 @@ int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float
  * speculative decoding verifies at once -- with their page lists shared as one scan (LiteTopK,
  * section 3.4, LiteDSA: "Candidate Union and Membership Masks", "Grouped Sparse Attention").
  * Request b's cache holds seq_lens[b] = L keys, the draft tokens' included; query token t sits at
- * position L - T + t and attends to positions < L - T + 1 + t.  The caller selects each token's
- * pages with spd_page_score / spd_page_select on a descriptor of B * T rows (row b T + t: token t's
- * queries, request b's block-table row, seq_lens L - T + 1 + t, key statistics covering all L
- * keys), then merges them with spd_page_list_union and attends with spd_sparse_paged_decode_mq
+ * position L - T + t and attends to positions < L - T + 1 + t.  The caller scores every token's
+ * pages in one scan with spd_page_score_mq (or with spd_page_score on a descriptor of B * T rows)
+ * and selects them with spd_page_select on the B * T rows (row b T + t: token t's queries,
+ * request b's block-table row, seq_lens L - T + 1 + t, key statistics covering all L keys), then
+ * merges them with spd_page_list_union and attends with spd_sparse_paged_decode_mq
  * and spd_lse_merge_mq.  Supported: page_size 16, max_pages_per_seq <= SPD_MQ_MAX_PAGES; decode
  * and merge need f16 queries, f16 or fp8 pools, head_dim 128 and the per-row plan (balanced = 0). */
 #define SPD_MQ_MAX_TOKENS 4
 #define SPD_MQ_ROWS 16          /* chunk-state rows per (request, KV head): 4 tokens x G = 4 */
 #define SPD_MQ_MAX_PAGES 32768
+
+/* Page scores of the T token rows of every request in one scan (top-K, bound estimator): each
+ * (page, KV head) key box is read once and bounded against the T query groups (LServe summary,
+ * "Hierarchical Paging", page importance; LiteTopK, section 3.4, one candidate list per query
+ * token).  desc describes the B requests; seq_lens (device, [B]) holds L; q (device, [B, T, Hq, d],
+ * the query dtype of desc); page_meta and block_table as for spd_page_score; head_kind (host, [Hkv])
+ * as for spd_page_score: streaming heads are not scored.  Writes scores (device,
+ * [B * T, Hkv, max_pages_per_seq] f32; row b T + t) for the pages of token t's length
+ * L - T + 1 + t, bit for bit what spd_page_score with SPD_TAIL_NONE writes on a descriptor of B * T
+ * rows; later entries are not written.  The statistics of the pages the draft tokens are in must be
+ * current (spd_page_meta_build over the last pages first).  sel must be top-K with the bound
+ * estimator (else SPD_ERR_UNSUPPORTED); errors otherwise as spd_page_score and spd_page_list_union. */
+int spd_page_score_mq(const spd_desc* desc, int32_t num_tokens, const spd_select_params* sel, const void* q,
+                      const void* page_meta, const int32_t* block_table, const int32_t* seq_lens,
+                      const uint8_t* head_kind, float* scores, void* stream);
 
 /* Union of the T token lists of every (request, KV head) row (LiteDSA's candidate union).
  * desc describes the B requests (max_list: the union's capacity, at least

@@ -30,7 +30,8 @@ ESTIMATOR_BOUND, ESTIMATOR_MVAR = 0, 1
 EXPORTS = ("spd_page_meta_build", "spd_page_stats_build", "spd_page_score", "spd_page_select", "spd_page_score_select",
            "spd_sparse_paged_decode", "spd_lse_merge", "spd_plan_grid", "spd_plan_chunks", "spd_page_list_refresh",
            "spd_partials_size", "spd_workspace_bytes", "spd_error_string", "spd_abi_version",
-           "spd_page_list_union", "spd_sparse_paged_decode_mq", "spd_lse_merge_mq", "spd_sparse_paged_decode_merged")
+           "spd_page_list_union", "spd_sparse_paged_decode_mq", "spd_lse_merge_mq", "spd_sparse_paged_decode_merged",
+           "spd_page_score_mq")
 MQ_ROWS = 16  # chunk-state rows per (request, KV head) of the several-query decode
 
 
@@ -81,6 +82,7 @@ def lib():
         L.spd_lse_merge.argtypes = [D, P, v, v, v, v, v, v]
         L.spd_sparse_paged_decode_merged.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v, v]
         L.spd_page_list_union.argtypes = [D, c_int32, c_int32, v, v, v, v, v, v, v, v, v]
+        L.spd_page_score_mq.argtypes = [D, c_int32, S, v, v, v, v, POINTER(c_uint8), v, v]
         L.spd_sparse_paged_decode_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v,
                                                  v]
         L.spd_lse_merge_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v]
@@ -203,6 +205,13 @@ def spd_sparse_paged_decode_merged(desc, plan, q, k_pool, v_pool, k_scale, v_sca
 def spd_lse_merge(desc, plan, part_o, part_lse, list_len, out, out_lse, stream=None):
     _check(lib().spd_lse_merge(ctypes.byref(desc), ctypes.byref(plan), _ptr(part_o), _ptr(part_lse),
                                _ptr(list_len), _ptr(out), _ptr(out_lse), _stream(stream)), "spd_lse_merge")
+
+
+def spd_page_score_mq(desc, num_tokens, sel, q, page_meta, block_table, seq_lens, head_kind, scores, stream=None):
+    _check(lib().spd_page_score_mq(ctypes.byref(desc), int(num_tokens), ctypes.byref(sel), _ptr(q), _ptr(page_meta),
+                                   _ptr(block_table), _ptr(seq_lens), _heads(head_kind), _ptr(scores),
+                                   _stream(stream)),
+           "spd_page_score_mq")
 
 
 def spd_page_list_union(desc, num_tokens, token_max_list, token_list, token_len, block_table, seq_lens, page_list,

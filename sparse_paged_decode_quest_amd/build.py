@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libspd.so")
 ARCH = os.environ.get("SPD_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["spd_api.cpp", "page_meta_build.hip", "page_score.hip", "page_select.hip",
-           "page_score_select.hip", "page_score_mvar.hip", "sparse_paged_decode.hip", "mq_decode.hip"]
+           "page_score_select.hip", "page_score_mvar.hip", "sparse_paged_decode.hip", "mq_decode.hip", "mq_score.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,0 +1,98 @@
+// Page scores of T query tokens per request in one scan (several query tokens, top-K over 16-token
+// pages).  LiteTopK, section 3.4 (LiteDSA): every draft token keeps its own candidate list, so each
+// token row needs its own page scores; the tokens of a request share the cache and its key boxes,
+// so the scan reads each (page, KV head) meta row once and bounds it against the T query groups
+// (LServe summary, "Hierarchical Paging": S_j = sum_i max(q_i kmax_i, q_i kmin_i), then the max over
+// the group).  The arithmetic per (page, token) is the single-query scorer's, so a token row's scores
+// are bit for bit those of the scorer run on that row alone.
+//
+// Work layout: the single-query scorer's (score_common.h) over the pages of the longest token row
+// (the last token, length L); lanes hold the T query groups in registers.  Token t (length
+// L - T + 1 + t) gets the scores of its own pages only.  Every wave reads its query groups from L2;
+// staging them through LDS once per workgroup (one copy, one barrier) measured slower.
+#include "mq_score.h"
+#include "score_common.h"
+
+namespace spd {
+
+template <int D, int KVD, int ITERS>
+__global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(ScoreArgs a, int num_tokens) {
+  using T = ScoreTraits<D, KVD>;
+  constexpr int LPP = T::LPP;
+  const int row_dyn = blockIdx.x / a.blocks_per_row;
+  const int blk = blockIdx.x % a.blocks_per_row;
+  const int b = row_dyn / a.dyn.count;
+  const int h = a.dyn.head[row_dyn % a.dyn.count];
+  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+  const int p_begin = blk * a.pages_per_block;
+  int raw[ITERS];
+  load_block_table<D, KVD, kScoreWaves, ITERS>(bt_row, a.max_pages, p_begin, raw);
+
+  const int len = a.seq_lens[b];
+  const int n = row_pages(len, a.max_pages);  // pages of the last token's row
+  if (p_begin >= n) return;                   // uniform over the block
+
+  const int lane = threadIdx.x % kWave;
+  const int sub = lane % LPP;
+  const int c0 = sub * T::CW;
+  int pg[ITERS];
+  bool ok[ITERS];
+  typename T::M m[ITERS];
+  // every block-table entry is tested before the first key-box load is issued: a test after a
+  // conditional load would make the compiler wait for that load too
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    pg[it] = score_page<D, KVD, kScoreWaves>(p_begin, it);
+    ok[it] = pg[it] < n && raw[it] >= 0 && raw[it] < a.num_pool_pages;
+  }
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it)
+    if (ok[it]) T::load_m(m[it], a.meta, head_unit(raw[it], a.num_kv_heads, h, 0, 0) * 2 * D, c0);
+  // the query groups after the key boxes, unconditionally (token indices clamped to the last token),
+  // so that no wait for them comes between the block-table entries and the key-box loads
+  typename T::Q qr[kMqScoreMaxTokens];
+#pragma unroll
+  for (int t = 0; t < kMqScoreMaxTokens; ++t) {
+    const int tt = min(t, num_tokens - 1);
+    T::load_q(qr[t], a.q, (((size_t)b * num_tokens + tt) * a.num_q_heads + (size_t)h * kG) * D, c0);
+  }
+#pragma unroll
+  for (int t = 0; t < kMqScoreMaxTokens; ++t) {
+    if (t >= num_tokens) break;
+    const int n_t = row_pages(len - num_tokens + 1 + t, a.max_pages);
+    float* sc_row = a.scores + (((size_t)b * num_tokens + t) * a.num_kv_heads + h) * a.max_pages;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      float s[kG];
+      if (ok[it]) T::bound(qr[t], m[it], s);
+      else {
+#pragma unroll
+        for (int g = 0; g < kG; ++g) s[g] = 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < kG; ++g) s[g] = group_sum<LPP>(s[g]);
+      if (sub == 0 && pg[it] < n_t) sc_row[pg[it]] = ok[it] ? topk_score(s) : -INFINITY;
+    }
+  }
+}
+
+int launch_mq_page_score(const ScoreArgs& a, int num_tokens, int head_dim, int kv_dtype, hipStream_t stream) {
+  const unsigned rows = (unsigned)(a.batch * a.dyn.count);
+  const dim3 grid(rows * (unsigned)a.blocks_per_row), block(kScoreWaves * kWave);
+  const bool long_scan = score_iters((long long)rows * a.max_pages) == kScoreItersLong;
+#define SPD_MQ_SCORE_CASE(D, KVD)                                                                                     \
+  if (head_dim == D && kv_dtype == KVD) {                                                                             \
+    if (long_scan) hipLaunchKernelGGL((mq_page_score_kernel<D, KVD, kScoreItersLong>), grid, block, 0, stream, a, num_tokens); \
+    else hipLaunchKernelGGL((mq_page_score_kernel<D, KVD, kScoreItersShort>), grid, block, 0, stream, a, num_tokens);  \
+    return 0;                                                                                                         \
+  }
+  SPD_MQ_SCORE_CASE(64, SPD_DTYPE_F16)
+  SPD_MQ_SCORE_CASE(128, SPD_DTYPE_F16)
+  SPD_MQ_SCORE_CASE(128, SPD_DTYPE_FP8_E4M3FN)
+  SPD_MQ_SCORE_CASE(64, SPD_DTYPE_F32)
+  SPD_MQ_SCORE_CASE(128, SPD_DTYPE_F32)
+#undef SPD_MQ_SCORE_CASE
+  return SPD_ERR_UNSUPPORTED;
+}
+
+}  // namespace spd

@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "../../include/spd.h"
+#include "mq_score.h"
 #include "score_common.h"
 #include "spd_launch.h"
 
@@ -573,6 +574,24 @@ static int check_mq(const spd_desc* d, int32_t num_tokens) {
   if (num_tokens < 1 || num_tokens > SPD_MQ_MAX_TOKENS) return SPD_ERR_INVALID_ARG;
   if (is_hier(d) || d->max_pages_per_seq > SPD_MQ_MAX_PAGES) return SPD_ERR_UNSUPPORTED;
   return SPD_OK;
+}
+
+int spd_page_score_mq(const spd_desc* desc, int32_t num_tokens, const spd_select_params* sel, const void* q,
+                      const void* page_meta, const int32_t* block_table, const int32_t* seq_lens,
+                      const uint8_t* head_kind, float* scores, void* stream) {
+  int rc = check_mq(desc, num_tokens);
+  if (rc) return rc;
+  if ((rc = check_sel(desc, sel))) return rc;
+  if (sel->mode != SPD_SELECT_TOPK || is_mvar(sel)) return SPD_ERR_UNSUPPORTED;
+  spd::HeadList dyn, strm;
+  uint64_t mask;
+  if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
+  if (desc->batch == 0 || dyn.count == 0) return SPD_OK;
+  if (!q || !page_meta || !block_table || !seq_lens || !scores) return SPD_ERR_INVALID_ARG;
+  spd::ScoreArgs a = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, score_ppb(desc, sel, dyn.count));
+  a.scores = scores;
+  a.tail_mode = SPD_TAIL_NONE;
+  return launched(spd::launch_mq_page_score(a, num_tokens, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
 }
 
 int spd_page_list_union(const spd_desc* desc, int32_t num_tokens, int32_t token_max_list, const int32_t* token_list,

@@ -349,7 +349,14 @@ class MQDecodeStep:
                               self.d.page_meta, stream)
 
     def score(self, stream=None):
-        """Page scores of every token row (statistics over all cached keys)."""
+        """Page scores of every token row (statistics over all cached keys): one scan that reads each
+        key box once for the T tokens."""
+        d = self.d
+        A.spd_page_score_mq(self.desc, self.T, self.sel, d.q, d.page_meta, d.block_table, d.seq_lens, d.head_kind,
+                            self.scores, stream)
+
+    def score_per_token(self, stream=None):
+        """The same scores from the single-query scorer over the B * T token rows (one scan per token)."""
         d = self.d
         A.spd_page_score(self.desc_x, self.sel, self.q_x, d.page_meta, d.k_pool, d.k_scale, A.TAIL_NONE, self.bt_x,
                          self.seq_x, d.head_kind, self.scores, self.head_lse, self.workspace, self.ws_bytes, stream)

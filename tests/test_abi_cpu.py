@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 10
+    assert A.abi_version() == 11
 
 
 def test_error_strings(lib):
@@ -363,3 +363,20 @@ def test_several_query_tokens_argument_checks(lib):
     assert dec_rc(d, pm=None) == A.SPD_ERR_INVALID_ARG
     rc = L.spd_lse_merge_mq(ctypes.byref(d), 4, ctypes.byref(plan), FAKE, None, FAKE, FAKE, FAKE, 0)
     assert rc == A.SPD_ERR_INVALID_ARG
+
+    def score_rc(desc, T=4, sel=None, **null):
+        p = {k: FAKE for k in ("q", "meta", "bt", "sl", "sc")}
+        p.update(null)
+        heads = (ctypes.c_uint8 * desc.num_kv_heads)(*([0] * desc.num_kv_heads))
+        s = sel if sel is not None else sel_for(w)
+        return L.spd_page_score_mq(ctypes.byref(desc), T, ctypes.byref(s), p["q"], p["meta"], p["bt"], p["sl"], heads,
+                                   p["sc"], 0)
+
+    for T in (0, 5):
+        assert score_rc(d, T=T) == A.SPD_ERR_INVALID_ARG
+    for k in ("q", "meta", "bt", "sl", "sc"):
+        assert score_rc(d, **{k: None}) == A.SPD_ERR_INVALID_ARG, k
+    assert score_rc(d, sel=sel_for(w, mode=A.SELECT_COVERAGE)) == A.SPD_ERR_UNSUPPORTED
+    assert score_rc(d, sel=sel_for(w, mode=A.SELECT_COVERAGE, estimator=A.ESTIMATOR_MVAR)) == A.SPD_ERR_UNSUPPORTED
+    assert score_rc(desc_for(w, max_list=24, page_size=64)) == A.SPD_ERR_UNSUPPORTED
+    assert score_rc(desc_for(w, max_list=24, batch=0)) == A.SPD_OK

@@ -131,6 +131,45 @@ def test_mq_lists_union_attention(name):
                       "oracle union")
 
 
+SCORE_ONLY = {
+    "d64_f16": W.small("mq_s64", num_queries=3, d=64, seq_lens=(513, 300, 2, 129, 4000), budget=9, Hkv=3, Hq=12,
+                       streaming=(2,)),
+    "d128_f32": W.small("mq_s32", num_queries=4, kv="f32", q="f32", seq_lens=(1500, 250, 31, 3), budget=16),
+    "dense_short": W.small("mq_dense", num_queries=4, seq_lens=(333, 48, 17, 5, 2), budget=1000, Hkv=2, Hq=8),
+}
+
+
+@pytest.mark.parametrize("name", list(MQ_SMALL) + list(SCORE_ONLY))
+def test_mq_one_scan_scores_equal_the_per_token_scorer(name):
+    """The one-scan scorer of the T token rows writes, for every token's pages, bit for bit what the
+    single-query scorer writes on that token's row alone; streaming heads are left untouched."""
+    w = MQ_SMALL.get(name) or SCORE_ONLY[name]
+    say(f"[case] {name} T={w.num_queries} d={w.head_dim} kv={w.kv_dtype} seq={w.seq_lens[:8]}")
+    inp = W.generate(w)
+    d = S.upload(inp)
+    S.build_meta(w, d)
+    st = S.MQDecodeStep(w, d)
+    st.refresh_tail()
+    got = []
+    for fn in (st.score, st.score_per_token):
+        st.scores.fill_(float("nan"))
+        fn()
+        torch.cuda.synchronize()
+        got.append(st.scores.clone())
+    one, per = got
+    T = w.num_queries
+    for b, L in enumerate(w.seq_lens):
+        for t in range(T):
+            n_t = -(-max(L - T + 1 + t, 0) // 16)
+            for h in range(w.num_kv_heads):
+                r = b * T + t
+                if inp.head_kind[h]:
+                    assert torch.isnan(one[r, h]).all()
+                    continue
+                assert torch.equal(one[r, h, :n_t], per[r, h, :n_t]), (b, t, h)
+                assert not torch.isnan(one[r, h, :n_t]).any()
+
+
 @pytest.mark.parametrize("plan", [S.Plan(1, 1, 0), S.Plan(2, 3, 0), S.Plan(4, 16, 512), S.Plan(1000, 1, 0)])
 def test_mq_plan_invariance(plan):
     w = MQ_SMALL["t4"].replace(budget_pages=40)
