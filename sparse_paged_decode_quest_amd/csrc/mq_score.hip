@@ -22,7 +22,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(Scor
   const int row_dyn = blockIdx.x / a.blocks_per_row;
   const int blk = blockIdx.x % a.blocks_per_row;
   const int b = row_dyn / a.dyn.count;
-  const int h = a.dyn.head[row_dyn % a.dyn.count];
+  const int h = a.dyn.at(row_dyn % a.dyn.count);
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
   const int p_begin = blk * a.pages_per_block;
   int raw[ITERS];

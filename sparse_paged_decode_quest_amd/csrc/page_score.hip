@@ -29,7 +29,7 @@ __device__ __forceinline__ RowRole row_role(const ScoreArgs& a) {
   RowRole r;
   r.blk = blockIdx.x % per_row;
   r.b = row_dyn / a.dyn.count;
-  r.h = a.dyn.head[row_dyn % a.dyn.count];
+  r.h = a.dyn.at(row_dyn % a.dyn.count);
   r.tail = r.blk == a.blocks_per_row;
   return r;
 }
@@ -115,7 +115,7 @@ __device__ __forceinline__ ShareRole share_role(const ScoreArgs& a) {
   ShareRole r;
   r.part = blockIdx.x % bpr;
   r.b = row_dyn / a.dyn.count;
-  r.h = a.dyn.head[row_dyn % a.dyn.count];
+  r.h = a.dyn.at(row_dyn % a.dyn.count);
   r.n = row_logical_pages(a.seq_lens[r.b], a.max_pages, a.lgs);
   r.row = (size_t)r.b * a.num_kv_heads + r.h;
   return r;

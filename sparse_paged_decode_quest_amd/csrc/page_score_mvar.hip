@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_mvar_kernel(Sc
   const int row_dyn = blockIdx.x / per_row;
   const int blk = blockIdx.x % per_row;
   const int b = row_dyn / a.dyn.count;
-  const int h = a.dyn.head[row_dyn % a.dyn.count];
+  const int h = a.dyn.at(row_dyn % a.dyn.count);
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
   if (blk == a.blocks_per_row) {
     mvar_exact_pages<D, KVD>(a, bt_row, b, h);

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(NW * kWave) void page_score_select_kernel(FusedArgs
   if ((int)blockIdx.x >= dyn_blocks) {
     const int k = blockIdx.x - dyn_blocks;
     const int b = k / f.stream_heads.count;
-    const int h = f.stream_heads.head[k % f.stream_heads.count];
+    const int h = f.stream_heads.at(k % f.stream_heads.count);
     const size_t row = (size_t)b * a.num_kv_heads + h;
     select_streaming_row(f.sel, row_pages(a.seq_lens[b], a.max_pages), row, a.block_table + (size_t)b * a.max_pages);
     return;
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(NW * kWave) void page_score_select_kernel(FusedArgs
   const int blk = blockIdx.x % per_row;
   const bool tail_block = blk == a.blocks_per_row;
   const int b = row_dyn / a.dyn.count;
-  const int h = a.dyn.head[row_dyn % a.dyn.count];
+  const int h = a.dyn.at(row_dyn % a.dyn.count);
   const size_t row = (size_t)b * a.num_kv_heads + h;
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
   const int p_begin = blk * a.pages_per_block;

@@ -108,12 +108,14 @@ int check_list_capacity(const spd_desc* d, const spd_select_params* s) {
 int head_lists(const spd_desc* d, const uint8_t* head_kind, spd::HeadList& dyn, spd::HeadList& strm, uint64_t& mask) {
   if (!head_kind) return SPD_ERR_INVALID_ARG;
   dyn.count = strm.count = 0;
+  dyn.mask = strm.mask = 0;
   mask = 0;
   for (int h = 0; h < d->num_kv_heads; ++h) {
-    if (head_kind[h] == SPD_HEAD_DYNAMIC) dyn.head[dyn.count++] = (uint8_t)h;
+    if (head_kind[h] == SPD_HEAD_DYNAMIC) { dyn.head[dyn.count++] = (uint8_t)h; dyn.mask |= 1ull << h; }
     else if (head_kind[h] == SPD_HEAD_STREAMING) { strm.head[strm.count++] = (uint8_t)h; mask |= 1ull << h; }
     else return SPD_ERR_INVALID_ARG;
   }
+  strm.mask = mask;
   return SPD_OK;
 }
 

@@ -53,8 +53,16 @@ int launch_page_meta_build(const MetaArgs& a, int head_dim, int kv_dtype, hipStr
 
 // KV heads of one kind, listed in ascending order (dynamic heads for the scorer).
 struct HeadList {
-  uint8_t head[SPD_MAX_KV_HEADS];
+  uint8_t head[SPD_MAX_KV_HEADS];  // ascending
   int count;
+  uint64_t mask;  // bit h set for every listed head
+  // head[k] from the mask alone (k-th set bit): a kernel finds its head with bit operations instead of
+  // a dependent read of the argument block before its first loads
+  __device__ __forceinline__ int at(int k) const {
+    uint64_t m = mask;
+    for (int i = 0; i < k; ++i) m &= m - 1;
+    return __builtin_ctzll(m);
+  }
 };
 
 struct ScoreArgs {
