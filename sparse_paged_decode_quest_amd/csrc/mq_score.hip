@@ -15,29 +15,6 @@
 
 namespace spd {
 
-// The page bound of one query group against one key box, for fp16 queries and boxes: per channel pair,
-// the box bound whose product is larger (kmax where the query half is >= 0, kmin where its sign bit is
-// set) goes into a dot2.  The selection mask is the query halves shifted right arithmetically by 15
-// (all ones where the sign bit is set), so a pair costs a packed shift, a bit-field select and the dot2;
-// the operands and the dot2 chain are the single-query scorer's, so the sums are bit for bit the same.
-template <typename Q, typename M>
-__device__ __forceinline__ void mq_bound_f16(const Q& qr, const M& m, float (&s)[kG]) {
-  const uint32_t lo[4] = {m.mn.x, m.mn.y, m.mn.z, m.mn.w};
-  const uint32_t hi[4] = {m.mx.x, m.mx.y, m.mx.z, m.mx.w};
-#pragma unroll
-  for (int g = 0; g < kG; ++g) {
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t neg;  // 0xffff in each half whose sign bit is set (a packed arithmetic shift; no memory access)
-      asm("v_pk_ashrrev_i16 %0, %1, %2" : "=v"(neg) : "s"(0x000f000fu), "v"(qr.h[g][i]));  // 15 in each half
-      const uint32_t sel = (lo[i] & neg) | (hi[i] & ~neg);
-      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, sel), __builtin_bit_cast(h2_t, qr.h[g][i]), acc, false);
-    }
-    s[g] = acc;
-  }
-}
-
 template <int D, int KVD, int ITERS>
 __global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(ScoreArgs a, int num_tokens) {
   using T = ScoreTraits<D, KVD>;
@@ -87,10 +64,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(Scor
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       float s[kG];
-      if (ok[it]) {
-        if constexpr (KVD == SPD_DTYPE_F32) T::bound(qr[t], m[it], s);
-        else mq_bound_f16(qr[t], m[it], s);
-      }
+      if (ok[it]) T::bound(qr[t], m[it], s);
       else {
 #pragma unroll
         for (int g = 0; g < kG; ++g) s[g] = 0.f;

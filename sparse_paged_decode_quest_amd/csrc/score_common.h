@@ -66,10 +66,11 @@ struct ScoreTraitsF16 {
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // per half: 0xffff where the query is >= 0 (sign bit clear), from the sign bits
-        const uint32_t neg = (qr.h[g][i] >> 15) & 0x00010001u;
-        const uint32_t pos = (neg ^ 0x00010001u) * 0xffffu;
-        const uint32_t sel = (hi[i] & pos) | (lo[i] & ~pos);
+        // per half: 0xffff where the query's sign bit is set (a packed arithmetic shift by 15), so kmin
+        // is taken there and kmax elsewhere
+        uint32_t neg;
+        asm("v_pk_ashrrev_i16 %0, %1, %2" : "=v"(neg) : "s"(0x000f000fu), "v"(qr.h[g][i]));
+        const uint32_t sel = (lo[i] & neg) | (hi[i] & ~neg);
         acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, sel), __builtin_bit_cast(h2_t, qr.h[g][i]), acc, false);
       }
       s[g] = acc;
