@@ -56,6 +56,53 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(Scor
     const int tt = min(t, num_tokens - 1);
     T::load_q(qr[t], a.q, (((size_t)b * num_tokens + tt) * a.num_q_heads + (size_t)h * kG) * D, c0);
   }
+  if constexpr (LPP == 16 && kMqScoreMaxTokens == 4) {
+    // The 16 sums (token t, head g) of a page live spread over its 16 lanes.  A reduce-scatter hands
+    // lane l the whole sum of k = l = 4 t + g: at each level (lane bit 1, 2, 4, 8) a lane keeps the half
+    // of its partial sums whose index bit equals its lane bit and adds the partner's partials of that
+    // half.  The pairs added are the butterfly's (group_sum), so the sums are bit for bit the same.
+    const bool b0 = sub & 1, b1 = sub & 2, b2 = sub & 4, b3 = sub & 8;
+    const int t_l = sub >> 2;
+    const int n_tl = row_pages(len - num_tokens + 1 + t_l, a.max_pages);
+    float* sc_l = a.scores + (((size_t)b * num_tokens + min(t_l, num_tokens - 1)) * a.num_kv_heads + h) * a.max_pages;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      float v[16];
+#pragma unroll
+      for (int t = 0; t < kMqScoreMaxTokens; ++t) {
+        float st[kG];
+        if (ok[it]) T::bound(qr[t], m[it], st);
+        else {
+#pragma unroll
+          for (int g = 0; g < kG; ++g) st[g] = 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < kG; ++g) v[t * kG + g] = st[g];
+      }
+      float u[8], w[4], x[2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float keep = b0 ? v[2 * j + 1] : v[2 * j], send = b0 ? v[2 * j] : v[2 * j + 1];
+        u[j] = keep + __uint_as_float(dpp<0xb1>(__float_as_uint(send)));  // lane ^ 1
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float keep = b1 ? u[2 * j + 1] : u[2 * j], send = b1 ? u[2 * j] : u[2 * j + 1];
+        w[j] = keep + __uint_as_float(dpp<0x4e>(__float_as_uint(send)));  // lane ^ 2
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float keep = b2 ? w[2 * j + 1] : w[2 * j], send = b2 ? w[2 * j] : w[2 * j + 1];
+        x[j] = keep + __shfl_xor(send, 4, kWave);
+      }
+      const float y = (b3 ? x[1] : x[0]) + __shfl_xor(b3 ? x[0] : x[1], 8, kWave);
+      // largest over the group: the four lanes of token t_l
+      float mx = fmaxf(y, __uint_as_float(dpp<0xb1>(__float_as_uint(y))));
+      mx = fmaxf(mx, __uint_as_float(dpp<0x4e>(__float_as_uint(mx))));
+      if ((sub & 3) == 0 && t_l < num_tokens && pg[it] < n_tl) sc_l[pg[it]] = ok[it] ? mx : -INFINITY;
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < kMqScoreMaxTokens; ++t) {
     if (t >= num_tokens) break;
