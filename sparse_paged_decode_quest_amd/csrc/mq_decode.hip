@@ -28,6 +28,7 @@ constexpr int kMqG = 4;      // query heads per KV head
 constexpr int kMqRows = 16;  // 4 query tokens x G = 4 heads
 constexpr int kUnionThreads = 1024;
 constexpr int kUnionRounds = 2;  // list entries per thread read up front (4 tokens x 512 entries)
+constexpr int kUnionRankMinPages = 16384;  // block tables this wide merge sorted lists by rank
 // Pages of a wave in flight: one computed while the next one loads (three or four were measured
 // slower: the kernel is bound by its per-page instructions, not by load latency).
 constexpr int kMqStages = 2;
@@ -36,6 +37,7 @@ __device__ __forceinline__ int mq_clamp(int n, int hi) { return n < 0 ? 0 : (n >
 
 // One workgroup per (request, KV head): a byte per page of the request in LDS collects the
 // tokens' bits (atomicOr on the word holding it), then an ordered compaction writes the union.
+template <bool RANK>
 __global__ __launch_bounds__(kUnionThreads) void page_list_union_kernel(UnionArgs a) {
   extern __shared__ uint32_t bits[];  // ceil(max_pages / 4) words
   __shared__ uint32_t wsum[kUnionThreads / kWave];
@@ -58,6 +60,70 @@ __global__ __launch_bounds__(kUnionThreads) void page_list_union_kernel(UnionArg
     }
   }
   const int n = row_pages(a.seq_lens[b], a.max_pages);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+  const size_t out_row = (size_t)row * a.max_list;
+
+  if (RANK && total <= kUnionThreads) {  // uniform over the block
+    // Sorted lists (as the selector writes them) are merged by rank, with no pass over the request's
+    // pages: entry e of list t goes to position sum_t' |{x in list t' : x < p}| + |{t' < t : p in list
+    // t'}| of the merged sequence (ties by token), and the first of each run of equal pages collects
+    // the run's token bits.  Lists that are not strictly ascending take the byte map below.  The merge
+    // costs about the same at any length (7-8 us measured), the byte map grows with the request's pages
+    // (5.2 us at 8192 pages, 11.9 us at 32768), so the merge is compiled in for tables of at least
+    // kUnionRankMinPages pages.
+    __shared__ int32_t skey[kUnionThreads];
+    __shared__ int32_t merged[kUnionThreads];
+    __shared__ uint8_t mtok[kUnionThreads];
+    const int e = (int)threadIdx.x;
+    const int cap = a.token_max_list;
+    const int t = e / cap, j = e % cap;
+    const bool valid = e < total && j < mq_clamp(len_of[0], cap) && ent[0] >= 0 && ent[0] < n;
+    constexpr int kNone = 0x7fffffff;  // sorts after every page
+    const int key = valid ? ent[0] : kNone;
+    if (e < total) skey[e] = key;
+    __syncthreads();
+    const bool in_order = e >= total || j + 1 >= cap || skey[e + 1] == kNone || key < skey[e + 1];
+    if (__syncthreads_and(in_order)) {
+      const int m_total = __syncthreads_count(valid);
+      if (valid) {
+        int rank = 0;
+        for (int u = 0; u < a.num_tokens; ++u) {
+          const int32_t* lst = skey + u * cap;
+          int lo = 0, hi = cap;  // first index whose key is >= key
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (lst[mid] < key) lo = mid + 1;
+            else hi = mid;
+          }
+          rank += lo + ((u < t && lo < cap && lst[lo] == key) ? 1 : 0);
+        }
+        merged[rank] = key;
+        mtok[rank] = (uint8_t)t;
+      }
+      __syncthreads();
+      const int r = e;
+      const bool first = r < m_total && (r == 0 || merged[r - 1] != merged[r]);
+      const uint32_t f = first ? 1u : 0u;
+      const uint32_t incl = wave_incl_scan(f);
+      if (lane == kWave - 1) wsum[wave] = incl;
+      __syncthreads();
+      uint32_t base = 0;
+      for (int w = 0; w < wave; ++w) base += wsum[w];
+      const uint32_t pos = base + incl - f;
+      if (first && pos < (uint32_t)a.max_list) {
+        const int pg = merged[r];
+        uint32_t mask = 0;
+        for (int k = r; k < m_total && merged[k] == pg; ++k) mask |= 1u << mtok[k];
+        a.page_list[out_row + pos] = pg;
+        a.page_mask[out_row + pos] = mask;
+        if (a.page_phys) a.page_phys[out_row + pos] = bt_row[pg];
+      }
+      if (threadIdx.x == kUnionThreads - 1) a.list_len[row] = (int)min(base + incl, (uint32_t)a.max_list);
+      return;
+    }
+  }
+
   for (int i = threadIdx.x; i < (n + 3) / 4; i += kUnionThreads) bits[i] = 0u;
   __syncthreads();
   for (int k = 0; k < kUnionRounds; ++k) {
@@ -89,15 +155,12 @@ __global__ __launch_bounds__(kUnionThreads) void page_list_union_kernel(UnionArg
       cnt += __popc(x & 0x01010101u);  // bytes that hold any token's bit
     }
   }
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const uint32_t incl = wave_incl_scan(cnt);
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
   uint32_t base = 0;
   for (int w = 0; w < wave; ++w) base += wsum[w];
   uint32_t pos = base + incl - cnt;
-  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
-  const size_t out_row = (size_t)row * a.max_list;
   for (int i = 0; i < per; ++i) {
     const int wi = w0 + i;
     if (wi >= words) break;
@@ -391,8 +454,9 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
 
 int launch_page_list_union(const UnionArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)((a.max_pages + 3) / 4) * sizeof(uint32_t);
-  hipLaunchKernelGGL(page_list_union_kernel, dim3((unsigned)(a.batch * a.num_kv_heads)), dim3(kUnionThreads), lds,
-                     stream, a);
+  const dim3 grid((unsigned)(a.batch * a.num_kv_heads)), block(kUnionThreads);
+  if (a.max_pages >= kUnionRankMinPages) hipLaunchKernelGGL(page_list_union_kernel<true>, grid, block, lds, stream, a);
+  else hipLaunchKernelGGL(page_list_union_kernel<false>, grid, block, lds, stream, a);
   return 0;
 }
 

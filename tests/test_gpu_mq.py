@@ -95,9 +95,11 @@ def set_union(st, union):
         dst.copy_(src)
 
 
+@pytest.mark.parametrize("wide", [False, True], ids=["bytemap_union", "rank_union"])
 @pytest.mark.parametrize("name", list(MQ_SMALL))
-def test_mq_lists_union_attention(name):
-    w = MQ_SMALL[name]
+def test_mq_lists_union_attention(name, wide):
+    # block tables of 16384 pages take the union kernel's rank merge of the sorted token lists
+    w = MQ_SMALL[name].replace(max_pages_per_seq=16384) if wide else MQ_SMALL[name]
     inp, d, st = run_case(w)
     meta_ref = O.page_meta_build(inp)
     assert np.array_equal(d.page_meta.cpu().numpy()[np.unique(inp.block_table)], meta_ref[np.unique(inp.block_table)])
