@@ -97,7 +97,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 11
+#define SPD_ABI_VERSION 12
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
@@ -362,10 +362,9 @@ int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float
  * section 3.4, LiteDSA: "Candidate Union and Membership Masks", "Grouped Sparse Attention").
  * Request b's cache holds seq_lens[b] = L keys, the draft tokens' included; query token t sits at
  * position L - T + t and attends to positions < L - T + 1 + t.  The caller scores every token's
- * pages in one scan with spd_page_score_mq (or with spd_page_score on a descriptor of B * T rows)
- * and selects them with spd_page_select on the B * T rows (row b T + t: token t's queries,
- * request b's block-table row, seq_lens L - T + 1 + t, key statistics covering all L keys), then
- * merges them with spd_page_list_union and attends with spd_sparse_paged_decode_mq
+ * pages in one scan with spd_page_score_mq and selects them with spd_page_select_mq (row b T + t:
+ * token t's queries, request b's block-table row, length L - T + 1 + t derived on the device, key
+ * statistics covering all L keys), then merges them with spd_page_list_union and attends with spd_sparse_paged_decode_mq
  * and spd_lse_merge_mq.  Supported: page_size 16, max_pages_per_seq <= SPD_MQ_MAX_PAGES; decode
  * and merge need f16 queries, f16 or fp8 pools, head_dim 128 and the per-row plan (balanced = 0). */
 #define SPD_MQ_MAX_TOKENS 4
@@ -386,6 +385,24 @@ int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float
 int spd_page_score_mq(const spd_desc* desc, int32_t num_tokens, const spd_select_params* sel, const void* q,
                       const void* page_meta, const int32_t* block_table, const int32_t* seq_lens,
                       const uint8_t* head_kind, float* scores, void* stream);
+
+/* Page lists of the T token rows of every request (top-K, bound estimator): row (b T + t, h) is
+ * token t of request b, selected as a single query of length L - T + 1 + t would be (forced sink and
+ * local pages of that length, then the best pages by (score desc, page asc) under the budget; LServe,
+ * "Token budget and physical page selection"), where L = seq_lens[b] is read on the device, so a
+ * captured call follows lengths that change between replays.  desc describes the B requests
+ * (block_table [B, max_pages_per_seq] is request b's row for all of its tokens); scores (device,
+ * [B * T, Hkv, max_pages_per_seq] f32) as spd_page_score_mq writes them; token_list (device,
+ * [B * T, Hkv, token_max_list]) and token_len (device, [B * T, Hkv]) receive the lists, ascending;
+ * token_phys (device, same shape as token_list, may be NULL) the physical page of each entry, read
+ * from block_table (then required).  head_kind (host): streaming heads get their static table for
+ * the token's length.  Returns SPD_ERR_INVALID_ARG when token_max_list cannot hold the longest list
+ * (as spd_page_select's max_list), SPD_ERR_UNSUPPORTED for COVERAGE or MVAR; otherwise errors as
+ * spd_page_select. */
+int spd_page_select_mq(const spd_desc* desc, int32_t num_tokens, int32_t token_max_list,
+                       const spd_select_params* sel, const float* scores, const int32_t* seq_lens,
+                       const uint8_t* head_kind, const int32_t* block_table, int32_t* token_list,
+                       int32_t* token_phys, int32_t* token_len, void* stream);
 
 /* Union of the T token lists of every (request, KV head) row (LiteDSA's candidate union).
  * desc describes the B requests (max_list: the union's capacity, at least

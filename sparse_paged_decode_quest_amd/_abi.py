@@ -31,7 +31,7 @@ EXPORTS = ("spd_page_meta_build", "spd_page_stats_build", "spd_page_score", "spd
            "spd_sparse_paged_decode", "spd_lse_merge", "spd_plan_grid", "spd_plan_chunks", "spd_page_list_refresh",
            "spd_partials_size", "spd_workspace_bytes", "spd_error_string", "spd_abi_version",
            "spd_page_list_union", "spd_sparse_paged_decode_mq", "spd_lse_merge_mq", "spd_sparse_paged_decode_merged",
-           "spd_page_score_mq")
+           "spd_page_score_mq", "spd_page_select_mq")
 MQ_ROWS = 16  # chunk-state rows per (request, KV head) of the several-query decode
 
 
@@ -83,6 +83,7 @@ def lib():
         L.spd_sparse_paged_decode_merged.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v, v]
         L.spd_page_list_union.argtypes = [D, c_int32, c_int32, v, v, v, v, v, v, v, v, v]
         L.spd_page_score_mq.argtypes = [D, c_int32, S, v, v, v, v, POINTER(c_uint8), v, v]
+        L.spd_page_select_mq.argtypes = [D, c_int32, c_int32, S, v, v, POINTER(c_uint8), v, v, v, v, v]
         L.spd_sparse_paged_decode_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v,
                                                  v]
         L.spd_lse_merge_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v]
@@ -212,6 +213,14 @@ def spd_page_score_mq(desc, num_tokens, sel, q, page_meta, block_table, seq_lens
                                    _ptr(block_table), _ptr(seq_lens), _heads(head_kind), _ptr(scores),
                                    _stream(stream)),
            "spd_page_score_mq")
+
+
+def spd_page_select_mq(desc, num_tokens, token_max_list, sel, scores, seq_lens, head_kind, block_table, token_list,
+                       token_phys, token_len, stream=None):
+    _check(lib().spd_page_select_mq(ctypes.byref(desc), int(num_tokens), int(token_max_list), ctypes.byref(sel),
+                                    _ptr(scores), _ptr(seq_lens), _heads(head_kind), _ptr(block_table),
+                                    _ptr(token_list), _ptr(token_phys), _ptr(token_len), _stream(stream)),
+           "spd_page_select_mq")
 
 
 def spd_page_list_union(desc, num_tokens, token_max_list, token_list, token_len, block_table, seq_lens, page_list,

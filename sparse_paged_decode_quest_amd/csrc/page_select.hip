@@ -35,18 +35,30 @@ __device__ __forceinline__ void rebuild_tail_pages(const SelectArgs& a, int k) {
   if (n > 0) build_page_meta_rt(a.tail, b, n - 1, h, len);
 }
 
+// Row blockIdx.x = (b T + t) Hkv + h of a step with T = a.num_tokens query tokens per request: token t of
+// request b sees the first seq_lens[b] - T + 1 + t keys (T = 1: the request's own length) and reads
+// request b's block-table row.  Returns the token row's length; b is the request.
+__device__ __forceinline__ int token_row_length(const SelectArgs& a, int token_row, int& b) {
+  const int T = a.num_tokens;
+  b = token_row / T;
+  const int len = a.seq_lens[b] - (T - 1 - token_row % T);
+  return len > 0 ? len : 0;
+}
+
 template <int NW, int KPL, bool COV>
 __global__ __launch_bounds__(NW * kWave) void page_select_kernel(SelectArgs a) {
   __shared__ SelectSmem<NW, KPL, COV> sm;
-  const int rows = a.batch * a.num_kv_heads;
+  const int rows = a.batch * a.num_tokens * a.num_kv_heads;
   if ((int)blockIdx.x >= rows) {
     rebuild_tail_pages<NW>(a, blockIdx.x - rows);
     return;
   }
-  const int b = blockIdx.x / a.num_kv_heads;
+  const int token_row = blockIdx.x / a.num_kv_heads;
   const int h = blockIdx.x % a.num_kv_heads;
-  const size_t row = (size_t)b * a.num_kv_heads + h;
-  const int n = row_phys_pages(a.seq_lens[b], a.max_pages, a.lgs);  // physical pages (hierarchical paging)
+  const size_t row = (size_t)token_row * a.num_kv_heads + h;
+  int b;
+  const int len = token_row_length(a, token_row, b);
+  const int n = row_phys_pages(len, a.max_pages, a.lgs);  // physical pages (hierarchical paging)
   const int32_t* bt_row = a.page_phys ? a.block_table + (size_t)b * a.max_pages : nullptr;
   if ((a.streaming_mask >> h) & 1ull) {
     select_streaming_row(a, n, row, bt_row);
@@ -111,8 +123,8 @@ int launch_page_list_refresh(const SelectArgs& a, hipStream_t stream) {
 int launch_page_select(const SelectArgs& a, hipStream_t stream) {
   SelectGeometry g;
   if (!select_geometry(a.max_pages, g)) return SPD_ERR_UNSUPPORTED;
-  const int rows = a.batch * a.num_kv_heads;
-  const int tail_blocks = a.tail.meta ? (rows + g.nw - 1) / g.nw : 0;
+  const int rows = a.batch * a.num_tokens * a.num_kv_heads;
+  const int tail_blocks = a.tail.meta ? (a.batch * a.num_kv_heads + g.nw - 1) / g.nw : 0;
   const dim3 grid((unsigned)(rows + tail_blocks)), block(g.nw * kWave);
   const bool cov = a.mode == SPD_SELECT_COVERAGE;
 #define SPD_SEL_CASE(NW, KPL)                                                                          \

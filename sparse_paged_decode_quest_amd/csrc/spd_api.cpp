@@ -226,6 +226,7 @@ spd::SelectArgs select_args(const spd_desc* d, const spd_select_params* s, const
   a.n_sink_stream = s->n_sink_stream;
   a.n_local_stream = s->n_local_stream;
   a.lgs = lgs_of(d);
+  a.num_tokens = 1;
   return a;
 }
 
@@ -594,6 +595,33 @@ int spd_page_score_mq(const spd_desc* desc, int32_t num_tokens, const spd_select
   a.scores = scores;
   a.tail_mode = SPD_TAIL_NONE;
   return launched(spd::launch_mq_page_score(a, num_tokens, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
+}
+
+int spd_page_select_mq(const spd_desc* desc, int32_t num_tokens, int32_t token_max_list,
+                       const spd_select_params* sel, const float* scores, const int32_t* seq_lens,
+                       const uint8_t* head_kind, const int32_t* block_table, int32_t* token_list,
+                       int32_t* token_phys, int32_t* token_len, void* stream) {
+  int rc = check_mq(desc, num_tokens);
+  if (rc) return rc;
+  if (token_max_list < 1) return SPD_ERR_INVALID_ARG;
+  if ((rc = check_sel(desc, sel))) return rc;
+  if (sel->mode != SPD_SELECT_TOPK || is_mvar(sel)) return SPD_ERR_UNSUPPORTED;
+  // the token lists' capacity must hold the longest list the rule can produce
+  spd_desc tok = *desc;
+  tok.max_list = token_max_list;
+  if ((rc = check_list_capacity(&tok, sel))) return rc;
+  spd::SelectGeometry g;
+  if (!spd::select_geometry(desc->max_pages_per_seq, g)) return SPD_ERR_UNSUPPORTED;
+  spd::HeadList dyn, strm;
+  uint64_t mask;
+  if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
+  if (desc->batch == 0) return SPD_OK;
+  if (!seq_lens || !token_list || !token_len || (dyn.count > 0 && !scores)) return SPD_ERR_INVALID_ARG;
+  if (token_phys && !block_table) return SPD_ERR_INVALID_ARG;
+  spd::SelectArgs a = select_args(&tok, sel, seq_lens, block_table, token_list, token_phys, token_len, nullptr, mask);
+  a.scores = scores;
+  a.num_tokens = num_tokens;
+  return launched(spd::launch_page_select(a, (hipStream_t)stream));
 }
 
 int spd_page_list_union(const spd_desc* desc, int32_t num_tokens, int32_t token_max_list, const int32_t* token_list,

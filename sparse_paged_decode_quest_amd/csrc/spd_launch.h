@@ -106,6 +106,8 @@ struct SelectArgs {
   unsigned long long gamma_fx;  // gamma in 2^-40 fixed point
   int n_sink, n_local, n_sink_stream, n_local_stream;
   int lgs;                  // log2 of logical pages per physical page: rows, lists and budget count physical pages
+  int num_tokens;           // query tokens per request (>= 1): rows are (b T + t, h); token t of request b sees
+                            // seq_lens[b] - T + 1 + t keys and request b's block-table row
   MetaArgs tail;            // tail.meta set: also rebuild each request's last logical page, all KV heads
 };
 int launch_page_select(const SelectArgs& a, hipStream_t stream);

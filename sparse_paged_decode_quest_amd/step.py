@@ -314,16 +314,10 @@ class MQDecodeStep:
         self.token_cap = w.list_capacity
         self.union_cap = min(T * self.token_cap, w.pages_per_seq)
         self.desc = make_desc(w, d.num_pool_pages, self.union_cap)                 # the B requests
-        self.desc_x = make_desc(w.replace(seq_lens=tuple(w.seq_lens) * T), d.num_pool_pages, self.token_cap)
         self.sel = make_select(w)
-        # the B * T token rows: queries, block-table rows and causal lengths
-        self.q_x = d.q.view(B * T, Hq, D)
-        self.bt_x = d.block_table.repeat_interleave(T, dim=0).contiguous()
-        self.seq_x = torch.zeros(B * T, **i32)
-        self.steps_t = torch.arange(T, dtype=torch.int32, device=dev)
-        self.set_lengths()
+        # the B * T token rows (row b T + t) share their request's block-table row and length; the
+        # library derives each token's causal length from d.seq_lens on every call
         self.scores = torch.zeros((B * T, Hkv, w.pages_per_seq), **f32)
-        self.head_lse = torch.zeros((B * T, Hq), **f32)
         self.token_list = torch.zeros((B * T, Hkv, self.token_cap), **i32)
         self.token_len = torch.zeros((B * T, Hkv), **i32)
         self.page_list = torch.zeros((B, Hkv, self.union_cap), **i32)
@@ -335,13 +329,6 @@ class MQDecodeStep:
         self.J = A.spd_plan_grid(self.desc, self.pp)
         self.part_o = torch.zeros(B * Hkv * self.J * A.MQ_ROWS * D, **f32)
         self.part_lse = torch.zeros(B * Hkv * self.J * A.MQ_ROWS, **f32)
-        self.ws_bytes = A.spd_workspace_bytes(self.desc_x, self.sel, A.OP_PAGE_SCORE)
-        self.workspace = torch.zeros(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
-
-    def set_lengths(self):
-        """Causal length of every token row from the requests' lengths (a device op, capturable)."""
-        L = self.d.seq_lens.to(torch.int32)
-        self.seq_x.copy_((L[:, None] - self.T + 1 + self.steps_t[None, :]).reshape(-1))
 
     def refresh_tail(self, stream=None):
         """Key statistics of the pages the draft tokens are in (the last two pages of each request)."""
@@ -355,17 +342,11 @@ class MQDecodeStep:
         A.spd_page_score_mq(self.desc, self.T, self.sel, d.q, d.page_meta, d.block_table, d.seq_lens, d.head_kind,
                             self.scores, stream)
 
-    def score_per_token(self, stream=None):
-        """The same scores from the single-query scorer over the B * T token rows (one scan per token)."""
-        d = self.d
-        A.spd_page_score(self.desc_x, self.sel, self.q_x, d.page_meta, d.k_pool, d.k_scale, A.TAIL_NONE, self.bt_x,
-                         self.seq_x, d.head_kind, self.scores, self.head_lse, self.workspace, self.ws_bytes, stream)
-
     def select_only(self, stream=None):
-        """Each token row's page list from its scores."""
+        """Each token row's page list from its scores (lengths read on the device)."""
         d = self.d
-        A.spd_page_select(self.desc_x, self.sel, self.scores, self.seq_x, d.head_kind, self.bt_x, None, None, None,
-                          self.token_list, None, self.token_len, None, stream)
+        A.spd_page_select_mq(self.desc, self.T, self.token_cap, self.sel, self.scores, d.seq_lens, d.head_kind,
+                             d.block_table, self.token_list, None, self.token_len, stream)
 
     def select(self, stream=None):
         self.score(stream)

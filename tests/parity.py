@@ -95,7 +95,8 @@ def check_coverage_list(lst, pi, n, gamma, forced):
         assert mass - min(float(pi[p]) for p in chosen) < t + TIE_RTOL, "not minimal"
     # threshold set up to the band
     lo = min(float(pi[p]) for p in chosen)
-    unchosen = [p for p in free if p not in set(chosen)]
+    chosen_set = set(chosen)
+    unchosen = [p for p in free if p not in chosen_set]
     if unchosen:
         hi = max(float(pi[p]) for p in unchosen)
         assert hi <= lo * (1 + TIE_RTOL) + 1e-12, (hi, lo)

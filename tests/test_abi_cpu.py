@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 11
+    assert A.abi_version() == 12
 
 
 def test_error_strings(lib):
@@ -380,3 +380,30 @@ def test_several_query_tokens_argument_checks(lib):
     assert score_rc(d, sel=sel_for(w, mode=A.SELECT_COVERAGE, estimator=A.ESTIMATOR_MVAR)) == A.SPD_ERR_UNSUPPORTED
     assert score_rc(desc_for(w, max_list=24, page_size=64)) == A.SPD_ERR_UNSUPPORTED
     assert score_rc(desc_for(w, max_list=24, batch=0)) == A.SPD_OK
+
+
+def test_several_query_token_selection_argument_checks(lib):
+    """spd_page_select_mq: token counts, the token lists' capacity, the rule, null pointers."""
+    w = W.small(num_queries=4, budget=6, n_sink_stream=2, n_local_stream=3)
+    d = desc_for(w, max_list=24)
+    L = A.lib()
+
+    def sel_rc(desc, T=4, tml=6, sel=None, **null):
+        p = {k: FAKE for k in ("sc", "sl", "bt", "tl", "tp", "tn")}
+        p.update(null)
+        heads = (ctypes.c_uint8 * desc.num_kv_heads)(*([0] * desc.num_kv_heads))
+        s = sel if sel is not None else sel_for(w)
+        return L.spd_page_select_mq(ctypes.byref(desc), T, tml, ctypes.byref(s), p["sc"], p["sl"], heads, p["bt"],
+                                    p["tl"], p["tp"], p["tn"], 0)
+
+    for T in (0, 5):
+        assert sel_rc(d, T=T) == A.SPD_ERR_INVALID_ARG
+    assert sel_rc(d, tml=0) == A.SPD_ERR_INVALID_ARG
+    assert sel_rc(d, tml=5) == A.SPD_ERR_INVALID_ARG             # cannot hold a budget of 6 pages
+    for k in ("sc", "sl", "tl", "tn"):
+        assert sel_rc(d, **{k: None}) == A.SPD_ERR_INVALID_ARG, k
+    assert sel_rc(d, bt=None) == A.SPD_ERR_INVALID_ARG           # physical pages wanted
+    assert sel_rc(d, sel=sel_for(w, mode=A.SELECT_COVERAGE)) == A.SPD_ERR_UNSUPPORTED
+    assert sel_rc(desc_for(w, max_list=24, page_size=64)) == A.SPD_ERR_UNSUPPORTED
+    assert sel_rc(desc_for(w, max_list=24, max_pages_per_seq=40000)) == A.SPD_ERR_UNSUPPORTED
+    assert sel_rc(desc_for(w, max_list=24, batch=0)) == A.SPD_OK

@@ -198,6 +198,48 @@ def test_all_heads_tail_rebuild_updates_only_last_pages():
     assert np.array_equal(got, ref)
 
 
+LONG_ROWS = {  # rows long enough for every selector geometry (2, 8, 32 and 64 key slots per lane)
+    "f16_8192_pages": dict(seq_lens=(8192 * 16, 3000), budget=256),
+    "f16_8193_pages": dict(seq_lens=(8193 * 16 - 7, 2049 * 16), budget=256),
+    "fp8_32768_pages": dict(kv="fp8", seq_lens=(32768 * 16,), budget=256, planted=("fixed", 64)),
+    "f16_40000_pages": dict(seq_lens=(40000 * 16 - 3, 5), budget=300),
+    "cov_8193_pages": dict(mode="coverage", gamma=0.99, n_local=1, seq_lens=(8193 * 16 - 1, 700),
+                           planted=("fixed", 40), delta=("nats", 10.0)),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_ROWS))
+def test_fused_score_select_on_long_rows(name):
+    """The fused score + select launch on rows of 8,192 to 40,000 pages (the workgroup geometries that
+    long contexts take), against the oracle: every dynamic row's scores, its list by the tie rule, and
+    attention over the GPU's lists; the unfused step must give the same lists."""
+    kw = dict(LONG_ROWS[name])
+    w = W.small("long_" + name, Hkv=2, Hq=8, streaming=(1,), n_sink_stream=2, n_local_stream=4, **kw)
+    inp, d, st = run_case(w, fused=True, tail="auto")
+    meta_ref = O.page_meta_build(inp)
+    scores = st.scores.cpu().numpy()
+    lists = st.lists()
+    for b in range(w.batch):
+        n = O.n_pages(inp.seq_lens[b])
+        h = 0  # the dynamic head
+        ref, lst, forced, _ = oracle_row(inp, meta_ref, b, h)
+        say(f"  row b={b} n={n} gpu_len={len(lists[(b, h)])} oracle_len={len(lst)} same={lists[(b, h)] == lst}")
+        if w.mode == "topk":
+            scale = P.bound_scale(inp, meta_ref, b, h)
+            P.check_topk_scores(scores[b, h, :n], ref, scale)
+            P.check_topk_list(lists[(b, h)], ref, n, w.budget_pages, forced, scale)
+        else:
+            P.check_coverage_shares(scores[b, h, :n], ref)
+            P.check_coverage_list(lists[(b, h)], ref, n, w.gamma, forced)
+        assert lists[(b, 1)] == O.forced_pages(n, w.n_sink_stream, w.n_local_stream)
+    o_ref, lse_ref = O.sparse_paged_decode(inp, lists, w.sm_scale)
+    P.check_attention(st.out.cpu().numpy(), st.out_lse.cpu().numpy(), o_ref, lse_ref, w.kv_dtype, name)
+    unfused = S.DecodeStep(w, d, fused=False, tail="none")
+    unfused.run()
+    torch.cuda.synchronize()
+    assert unfused.lists() == lists
+
+
 @pytest.mark.parametrize("mode", ["topk", "coverage"])
 def test_fused_select_equals_unfused(mode):
     kw = dict(budget=40) if mode == "topk" else dict(mode="coverage", gamma=0.9, n_local=1, planted=("fixed", 6),
