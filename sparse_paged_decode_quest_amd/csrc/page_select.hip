@@ -11,16 +11,26 @@
 namespace spd {
 
 // Keys (and physical pages, when the list of physical pages is wanted) of the row's pages in
-// the slot layout of select_row_keys.  `sc` holds top-K scores or coverage shares.
+// the slot layout of select_row_keys.  `sc` holds top-K scores or coverage shares.  The loads cover
+// the whole row stride (max_pages) so they are issued before the request's length arrives; slots
+// at or past the row's n pages are then cleared.
 template <int NW, int KPL, bool COV>
-__device__ __forceinline__ void load_row_keys(const float* sc, int n, uint32_t (&key)[KPL], SlotPhys<KPL>& phys) {
+__device__ __forceinline__ void load_row_keys(const float* sc, const int32_t* len_ptr, int max_pages, int lgs,
+                                              uint32_t (&key)[KPL], SlotPhys<KPL>& phys, int& n) {
   const int wbase = (int)(threadIdx.x / kWave) * kWave * KPL + (int)(threadIdx.x % kWave);
+  const __amdgpu_buffer_rsrc_t sc_r = make_rsrc(sc, (uint32_t)max_pages * 4u);  // slots past the row read 0
+  float v[KPL];
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int p = wbase + i * kWave;
-    const float v = p < n ? sc[p] : 0.f;
-    key[i] = COV ? coverage_key(v) : score_key(v);
-    phys.load(i, p, n);
+    v[i] = buf_load_f32(sc_r, (uint32_t)p * 4u);
+    phys.load(i, p, max_pages);
+  }
+  n = row_phys_pages(*len_ptr, max_pages, lgs);
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int p = wbase + i * kWave;
+    key[i] = p < n ? (COV ? coverage_key(v[i]) : score_key(v[i])) : 0u;
   }
 }
 
@@ -56,18 +66,27 @@ __global__ __launch_bounds__(NW * kWave) void page_select_kernel(SelectArgs a) {
   const int token_row = blockIdx.x / a.num_kv_heads;
   const int h = blockIdx.x % a.num_kv_heads;
   const size_t row = (size_t)token_row * a.num_kv_heads + h;
-  int b;
-  const int len = token_row_length(a, token_row, b);
-  const int n = row_phys_pages(len, a.max_pages, a.lgs);  // physical pages (hierarchical paging)
+  const int T = a.num_tokens;
+  const int b = token_row / T;
   const int32_t* bt_row = a.page_phys ? a.block_table + (size_t)b * a.max_pages : nullptr;
   if ((a.streaming_mask >> h) & 1ull) {
-    select_streaming_row(a, n, row, bt_row);
+    int b_;
+    select_streaming_row(a, row_phys_pages(token_row_length(a, token_row, b_), a.max_pages, a.lgs), row, bt_row);
     return;
   }
   uint32_t key[KPL];
   SlotPhys<KPL> phys;
   phys.bt_row = bt_row;
-  load_row_keys<NW, KPL, COV>(a.scores + row * a.max_pages, n, key, phys);
+  // token t of request b sees seq_lens[b] - (T - 1 - t) keys (T = 1: the request's length)
+  const int len_off = T - 1 - token_row % T;
+  int n;
+  if (len_off == 0) {
+    load_row_keys<NW, KPL, COV>(a.scores + row * a.max_pages, a.seq_lens + b, a.max_pages, a.lgs, key, phys, n);
+  } else {
+    int b_;
+    const int len = token_row_length(a, token_row, b_);
+    load_row_keys<NW, KPL, COV>(a.scores + row * a.max_pages, &len, a.max_pages, a.lgs, key, phys, n);
+  }
   select_row_keys<NW, KPL, COV>(a, key, phys, row_shape(n, a.n_sink, a.n_local), row, sm);
 }
 

@@ -287,20 +287,20 @@ __device__ __forceinline__ void score_block(const ScoreArgs& a, const int (&raw)
   typename T::Q qr;
   T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0);
   typename T::M m[ITERS];
+  // Every group's meta row is loaded, with no branch around the load: a page past the scan or outside
+  // the pool reads the row of pool page 0 instead, and its bound is discarded.
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
-    if (ok) T::load_m(m[it], a.meta, head_unit(phys[it], a.num_kv_heads, h, a.lgs, pg[it] & ((1 << a.lgs) - 1)) * 2 * D, c0);
+    T::load_m(m[it], a.meta, head_unit(ok ? phys[it] : 0, a.num_kv_heads, h, a.lgs, pg[it] & ((1 << a.lgs) - 1)) * 2 * D, c0);
   }
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
     float s[kG];
-    if (ok) T::bound(qr, m[it], s);
-    else {
+    T::bound(qr, m[it], s);
 #pragma unroll
-      for (int g = 0; g < kG; ++g) s[g] = 0.f;
-    }
+    for (int g = 0; g < kG; ++g) s[g] = ok ? s[g] : 0.f;
 #pragma unroll
     for (int g = 0; g < kG; ++g) s[g] = group_sum<LPP>(s[g]);
     if (sub == 0) fn(pg[it], ok && pg[it] < n, s);
@@ -375,20 +375,20 @@ __device__ __forceinline__ void score_block_topk_hier(const ScoreArgs& a, const 
   typename T::Q qr;
   T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0);
   typename T::M m[ITERS];
+  // Every group's meta row is loaded, with no branch around the load: a page past the scan or outside
+  // the pool reads the row of pool page 0 instead, and its bound is discarded.
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
-    if (ok) T::load_m(m[it], a.meta, head_unit(phys[it], a.num_kv_heads, h, a.lgs, pg[it] & ((1 << a.lgs) - 1)) * 2 * D, c0);
+    T::load_m(m[it], a.meta, head_unit(ok ? phys[it] : 0, a.num_kv_heads, h, a.lgs, pg[it] & ((1 << a.lgs) - 1)) * 2 * D, c0);
   }
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
     float s[kG];
-    if (ok) T::bound(qr, m[it], s);
-    else {
+    T::bound(qr, m[it], s);
 #pragma unroll
-      for (int g = 0; g < kG; ++g) s[g] = 0.f;
-    }
+    for (int g = 0; g < kG; ++g) s[g] = ok ? s[g] : 0.f;
 #pragma unroll
     for (int g = 0; g < kG; ++g) s[g] = group_sum<LPP>(s[g]);  // every lane of the group holds the sums
     float v = ok ? topk_score(s) : -INFINITY;

@@ -99,8 +99,10 @@ struct SlotPhys {
   static constexpr bool kInRegs = KPL <= 8;
   int32_t v[kInRegs ? KPL : 1];
   const int32_t* bt_row;  // nullable: no list of physical pages wanted
+  // slot i (page p) of a row of n block-table entries, read without a branch (past n, or with no
+  // table, it reads 0)
   __device__ __forceinline__ void load(int i, int p, int n) {
-    if constexpr (kInRegs) v[i] = (bt_row && p < n) ? bt_row[p] : 0;
+    if constexpr (kInRegs) v[i] = buf_load_i32(make_rsrc(bt_row, bt_row ? (uint32_t)n * 4u : 0u), (uint32_t)p * 4u);
   }
   __device__ __forceinline__ int32_t at(int i, int p) const {
     if constexpr (kInRegs) return v[i];

@@ -398,12 +398,15 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   // J * min_chunk pages, where the chunk size is the minimum; otherwise they are read again.
   const int spec_i0 = a.balanced ? -1 : j * a.min_chunk;
   int spec_lp = -1, spec_lph = -1;  // list entry (physical page slot when lgs > 0) and physical page of the unit
+  // the row's list and physical pages through range-checked loads: entries past max_list read 0, with
+  // no branch around each read
+  const __amdgpu_buffer_rsrc_t list_r = make_rsrc(list, (uint32_t)a.max_list * 4u);
+  const __amdgpu_buffer_rsrc_t plist_r = make_rsrc(plist, plist ? (uint32_t)a.max_list * 4u : 0u);
   if (!a.balanced) {
     const int e = (spec_i0 + wave + 4 * lane) >> a.lgs;
-    if (e < a.max_list) {
-      spec_lp = list[e];
-      if (plist) spec_lph = plist[e];
-    }
+    spec_lp = buf_load_i32(list_r, (uint32_t)e * 4u);
+    spec_lph = buf_load_i32(plist_r, (uint32_t)e * 4u);
+    if (e >= a.max_list) spec_lp = -1;
   }
   typename T::Q q;
   T::load_q(q, a.q, qrow * D, quarter);
@@ -526,9 +529,10 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
         lp = spec_lp;
         lph = spec_lph;
       }
-    } else if (lane < cnt) {
-      lp = list[idx >> a.lgs];
-      if (plist) lph = plist[idx >> a.lgs];
+    } else {
+      lp = buf_load_i32(list_r, (uint32_t)(idx >> a.lgs) * 4u);
+      lph = buf_load_i32(plist_r, (uint32_t)(idx >> a.lgs) * 4u);
+      lp = lane < cnt ? lp : -1;
     }
     // unit idx of entry lp is its logical page (lp << lgs) + (idx mod 2^lgs); entries outside the
     // request are not usable (checked before the shift, so no entry can wrap into range)
@@ -596,21 +600,28 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
 }
 
 // Exact merge of a row's chunk states (PersistentKV, section 3.3; states are stored
-// normalised: o_j = a_j / l_j and lse_j = m_j + ln l_j).  One 1024-thread block per (row,
-// query head).  The row's list length, the chunk log-sum-exps and the first kPre chunk outputs
-// of every thread are all requested at once -- entries past the row's chunk count are read
-// (they lie inside the partial buffers) and never used -- so the merge costs one memory round
-// trip.  Chunk weights exp(lse_j - lse) go through LDS; D channels x (1024 / D) chunk
-// partitions accumulate in parallel and the partitions are summed in a fixed order.
-constexpr int kMergeThreads = 1024;
+// normalised: o_j = a_j / l_j and lse_j = m_j + ln l_j): lse = log sum_j exp(lse_j) and
+// o = sum_j exp(lse_j - lse) o_j.  One 256-thread block per (row, chunk-state row r), with no
+// workgroup barrier: every wave reads all the row's chunk log-sum-exps (lane i holds chunks i,
+// i + 64, ...) and takes their max and weight sum with DPP reductions -- the same bits in every
+// wave -- while its lanes split the channels and the chunks: lane l of wave w owns channel
+// w * D/4 + l mod (D/4) and the chunks of class l / (D/4) (chunk j belongs to class j mod CL, CL =
+// 256 / D).  The classes' partial sums are combined with lane swaps.  The list length, the chunk
+// log-sum-exps and the first chunk outputs are all requested at once (entries past the row's chunk
+// count lie inside the partial buffers and are not used), so a row of up to 64 chunks is merged in one
+// memory round trip: the first global access of a kernel costs about a microsecond, and every
+// dependent one after it about half that.
+constexpr int kMergeThreads = 256;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
-  constexpr int PARTS = kMergeThreads / D;
-  constexpr int kPre = 8;  // chunk outputs per thread loaded up front (J <= kPre * PARTS needs no more)
-  __shared__ float w_s[kMaxChunks];
-  __shared__ float red[kMergeThreads / kWave];
-  __shared__ float part_s[PARTS][D];
+  constexpr int CL = kMergeThreads / D;   // chunk classes: 2 (d = 128) or 4 (d = 64)
+  constexpr int CPW = kWave / CL;          // channels per wave
+  constexpr int kSlots = kMaxChunks / kWave;
+  constexpr int kPre = kWave / CL;         // chunk outputs per lane requested with the log-sum-exps: the
+                                           // first 64 chunks (later ones cost one more round trip per 8)
+  static_assert(CPW * (kMergeThreads / kWave) == D, "every channel has one lane per class");
+  __shared__ float w_lds[kMergeThreads / kWave][kMaxChunks];  // one copy of the weights per wave
   // block (row, r): chunk-state row r of (request, KV head) row `row`; with several query tokens per
   // request r = t G + g (token t, head g of the group) and the output is [B, T, Hq, d]
   const int R = a.rows_per_head;
@@ -621,11 +632,12 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
   if (r >= a.num_tokens * kGq) return;  // rows of absent query tokens (uniform over the block)
   const int J = a.blocks_per_row;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int ch = threadIdx.x % D, part = threadIdx.x / D;
+  const int cls = lane / CPW;
+  const int ch = wave * CPW + lane % CPW;
   // Balanced plan: the row's chunk count and first chunk number come from every row's list length
   // (one more dependent read before the chunk states).
   int c, m, first = 0;
-  int n = a.list_len[row];
+  const int n = a.list_len[row];
   if (a.balanced) {
     const int rows = a.batch * a.num_kv_heads;
     c = balanced_chunk(a.list_len, rows, a.max_list, a.min_chunk, a.grid_target, a.lgs);
@@ -633,72 +645,62 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(MergeArgs a) {
   }
   const size_t slot0 = (a.balanced ? (size_t)first : (size_t)row * J) * R + r;  // + j * R
   const int J_read = a.balanced ? m : J;  // chunk slots of the row that may be read
-
-  // speculative loads (per-row plan: before the row's chunk count is known): chunk lse values,
-  // first chunk outputs
-  float lse_j[(kMaxChunks + kMergeThreads - 1) / kMergeThreads];
+  // range-checked loads over the row's chunk slots: chunks past J_read read as 0, with no branch
+  const __amdgpu_buffer_rsrc_t lse_r = make_rsrc(a.part_lse + slot0, (uint32_t)(J_read * R) * 4u);
+  const __amdgpu_buffer_rsrc_t o_r = make_rsrc(a.part_o + slot0 * D, (uint32_t)(J_read * R) * D * 4u);
+  float lse_s[kSlots], pre[kPre];
 #pragma unroll
-  for (int k = 0; k < (kMaxChunks + kMergeThreads - 1) / kMergeThreads; ++k) {
-    const int jj = (int)threadIdx.x + k * kMergeThreads;
-    lse_j[k] = jj < J_read ? a.part_lse[slot0 + (size_t)jj * R] : -INFINITY;
-  }
-  float pre[kPre];
+  for (int k = 0; k < kSlots; ++k) lse_s[k] = buf_load_f32(lse_r, (uint32_t)((lane + k * kWave) * R) * 4u);
 #pragma unroll
-  for (int u = 0; u < kPre; ++u) {
-    const int jj = part + u * PARTS;
-    pre[u] = jj < J_read ? a.part_o[(slot0 + (size_t)jj * R) * D + ch] : 0.f;
-  }
+  for (int i = 0; i < kPre; ++i) pre[i] = buf_load_f32(o_r, ((uint32_t)((cls + CL * i) * R * D) + (uint32_t)ch) * 4u);
   if (!a.balanced) plan_chunks(clamp_len(n, a.max_list) << a.lgs, J, a.min_chunk, c, m);
-  if (m <= 1) return;
+  if (m <= 1) return;  // written by the decode itself
 
-  float mx = -INFINITY;
+  float M = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < (kMaxChunks + kMergeThreads - 1) / kMergeThreads; ++k) {
-    const int jj = (int)threadIdx.x + k * kMergeThreads;
-    if (jj < m) {
-      w_s[jj] = lse_j[k];
-      mx = fmaxf(mx, lse_j[k]);
-    }
-  }
-  mx = wave_max_f(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  const float M = wave_max_f(lane < kMergeThreads / kWave ? red[lane] : -INFINITY);  // one read per lane
-  __syncthreads();
+  for (int k = 0; k < kSlots; ++k) M = fmaxf(M, lane + k * kWave < m ? lse_s[k] : -INFINITY);
+  M = wave_max_f(M);
   const size_t qrow = ((size_t)b * a.num_tokens + r / kGq) * a.num_q_heads + (size_t)h * kGq + r % kGq;
-  if (M == -INFINITY) {
-    for (int e = threadIdx.x; e < D; e += kMergeThreads) a.out[qrow * D + e] = 0.f;
+  if (M == -INFINITY) {  // no chunk holds a key
+    if (cls == 0) a.out[qrow * D + ch] = 0.f;
     if (threadIdx.x == 0) a.out_lse[qrow] = -INFINITY;
     return;
   }
-  float sum = 0.f;
-  for (int jj = threadIdx.x; jj < m; jj += kMergeThreads) {
-    const float wj = expf(w_s[jj] - M);
-    w_s[jj] = wj;
-    sum += wj;
+  // chunk weights exp(lse_j - M), chunk j in lane j mod 64 of slot j / 64 (0 past the row's chunks)
+  float w_s[kSlots];
+  float S = 0.f;
+#pragma unroll
+  for (int k = 0; k < kSlots; ++k) {
+    w_s[k] = lane + k * kWave < m ? expf(lse_s[k] - M) : 0.f;
+    S += w_s[k];
   }
-  sum = wave_sum_f(sum);
-  if (lane == 0) red[wave] = sum;
-  __syncthreads();
-  const float S = wave_sum_f(lane < kMergeThreads / kWave ? red[lane] : 0.f);
-
+  S = wave_sum_f(S);
+  // the first 64 chunks: each class takes its chunk's weight from lane cls + CL i of slot 0
   float acc = 0.f;
 #pragma unroll
-  for (int u = 0; u < kPre; ++u) {
-    const int jj = part + u * PARTS;
-    if (jj < m) acc = fmaf(w_s[jj], pre[u], acc);
-  }
-  for (int jj = part + kPre * PARTS; jj < m; jj += PARTS)
-    acc = fmaf(w_s[jj], a.part_o[(slot0 + (size_t)jj * R) * D + ch], acc);
-  part_s[part][ch] = acc;
-  __syncthreads();
-  if (threadIdx.x < D) {
-    float o = 0.f;
+  for (int i = 0; i < kPre; ++i) {
+    float wv = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < PARTS; ++pp) o += part_s[pp][threadIdx.x];
-    a.out[qrow * D + threadIdx.x] = o / S;
-    if (threadIdx.x == 0) a.out_lse[qrow] = M + logf(S);
+    for (int q = 0; q < CL; ++q) {
+      const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_s[0]), CL * i + q));
+      wv = cls == q ? x : wv;
+    }
+    acc = fmaf(wv, cls + CL * i < m ? pre[i] : 0.f, acc);  // stale partials past the row may hold NaN
   }
+  if (m > kWave) {  // longer rows: the remaining weights through LDS (one copy per wave)
+#pragma unroll
+    for (int k = 1; k < kSlots; ++k)
+      if (lane + k * kWave < m) w_lds[wave][lane + k * kWave] = w_s[k];
+    wave_fence();
+#pragma unroll 8
+    for (int jj = cls + kWave; jj < m; jj += CL)
+      acc = fmaf(w_lds[wave][jj], a.part_o[(slot0 + (size_t)jj * R) * D + ch], acc);
+  }
+  // classes: lanes CPW apart hold the same channel
+  if constexpr (CL == 4) acc += xor16(acc);
+  acc += xor32(acc);
+  if (cls == 0) a.out[qrow * D + ch] = acc / S;
+  if (threadIdx.x == 0) a.out_lse[qrow] = M + logf(S);
 }
 
 int launch_sparse_paged_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype, hipStream_t stream) {

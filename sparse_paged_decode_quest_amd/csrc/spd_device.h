@@ -99,6 +99,24 @@ __device__ __forceinline__ T ld_stream(const T* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// ------------------------------------------------------------------ range-checked loads
+
+// Buffer resource over [p, p + bytes), bytes < 2^31: a buffer load at a byte offset outside the
+// range returns 0 and touches no memory.  Loads whose need depends on a bound (list entries past a
+// list's length, chunks past a row's chunk count) are issued through it without a branch per load --
+// a conditional global load compiles to an exec-masked branch around every load, which costs more
+// than the load's issue.  The third descriptor word selects 32-bit raw data (gfx9 buffer format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// (the builtin returns the 32 loaded bits as an unsigned integer: reinterpret, do not convert)
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
+}
+__device__ __forceinline__ int32_t buf_load_i32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
+}
+
 // ------------------------------------------------------------------ wave reductions
 
 template <int WIDTH>
