@@ -44,8 +44,9 @@
  *    enqueued; results are ready when the stream reaches the enqueued work.
  *  - Every call returns SPD_OK (0) or a negative spd_status.  Argument checks happen on the
  *    host before anything is enqueued; on an error nothing is launched.  SPD_ERR_LAUNCH
- *    reports a HIP launch failure.  No exceptions cross the ABI and there is no global
- *    mutable state, so calls from several host threads are safe.
+ *    reports a HIP launch failure.  No exceptions cross the ABI and, apart from the per-device
+ *    address of spd_sparse_paged_decode_noalloc's array, there is no global mutable state, so calls
+ *    from several host threads are safe.
  *  - Layouts are dense row-major C arrays:
  *      q            [B, Hq, d]                 f32 or f16 (spd_desc.q_dtype)
  *    P = spd_desc.page_size (tokens of a physical page), g = P / 16 (logical pages per
@@ -97,7 +98,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 12
+#define SPD_ABI_VERSION 13
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
@@ -354,6 +355,25 @@ int spd_sparse_paged_decode_merged(const spd_desc* desc, const spd_plan_params* 
 int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float* part_o,
                   const float* part_lse, const int32_t* list_len, float* out, float* out_lse,
                   void* stream);
+
+/* spd_sparse_paged_decode followed by spd_lse_merge, for callers that cannot allocate memory (code
+ * under graph capture, tight serving loops, harnesses that forbid allocation): the chunk partials
+ * live in a device array inside the library, SPD_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held
+ * until the process ends; the caller passes only inputs and outputs, with the meaning, layouts and
+ * results of spd_sparse_paged_decode + spd_lse_merge.  Nothing is allocated or freed.  The first call
+ * on a device looks the array's address up for that device (not a stream operation; make that call
+ * before capturing the entry point into a graph).  Returns SPD_ERR_WORKSPACE when the partials of
+ * the descriptor and plan (spd_partials_size: part_o elements, then part_lse elements after rounding
+ * up to 256 bytes, 4 bytes each) exceed SPD_NOALLOC_SCRATCH_BYTES, SPD_ERR_LAUNCH when the device or
+ * the array's address cannot be found; other errors as spd_sparse_paged_decode.  Every call on a GPU
+ * uses that GPU's one array: calls that overlap on one GPU (other streams, other host threads) race
+ * and must be serialised by the caller. */
+#define SPD_NOALLOC_SCRATCH_BYTES (32u << 20)
+int spd_sparse_paged_decode_noalloc(const spd_desc* desc, const spd_plan_params* plan, const void* q,
+                                    const void* k_pool, const void* v_pool, const uint16_t* k_scale,
+                                    const uint16_t* v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* page_list, const int32_t* page_phys, const int32_t* list_len,
+                                    float sm_scale, float* out, float* out_lse, void* stream);
 
 /* ------------------------------------------------------------------ several query tokens per request
  *

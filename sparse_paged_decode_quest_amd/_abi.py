@@ -31,7 +31,7 @@ EXPORTS = ("spd_page_meta_build", "spd_page_stats_build", "spd_page_score", "spd
            "spd_sparse_paged_decode", "spd_lse_merge", "spd_plan_grid", "spd_plan_chunks", "spd_page_list_refresh",
            "spd_partials_size", "spd_workspace_bytes", "spd_error_string", "spd_abi_version",
            "spd_page_list_union", "spd_sparse_paged_decode_mq", "spd_lse_merge_mq", "spd_sparse_paged_decode_merged",
-           "spd_page_score_mq", "spd_page_select_mq")
+           "spd_page_score_mq", "spd_page_select_mq", "spd_sparse_paged_decode_noalloc")
 MQ_ROWS = 16  # chunk-state rows per (request, KV head) of the several-query decode
 
 
@@ -80,6 +80,7 @@ def lib():
                                             c_size_t, v]
         L.spd_sparse_paged_decode.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v]
         L.spd_lse_merge.argtypes = [D, P, v, v, v, v, v, v]
+        L.spd_sparse_paged_decode_noalloc.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v]
         L.spd_sparse_paged_decode_merged.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v, v]
         L.spd_page_list_union.argtypes = [D, c_int32, c_int32, v, v, v, v, v, v, v, v, v]
         L.spd_page_score_mq.argtypes = [D, c_int32, S, v, v, v, v, POINTER(c_uint8), v, v]
@@ -201,6 +202,15 @@ def spd_sparse_paged_decode_merged(desc, plan, q, k_pool, v_pool, k_scale, v_sca
                                                 float(sm_scale), _ptr(out), _ptr(out_lse), _ptr(part_o),
                                                 _ptr(part_lse), _ptr(counters), _stream(stream)),
            "spd_sparse_paged_decode_merged")
+
+
+def spd_sparse_paged_decode_noalloc(desc, plan, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
+                                    page_list, page_phys, list_len, sm_scale, out, out_lse, stream=None):
+    _check(lib().spd_sparse_paged_decode_noalloc(ctypes.byref(desc), ctypes.byref(plan), _ptr(q), _ptr(k_pool),
+                                                 _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                                                 _ptr(seq_lens), _ptr(page_list), _ptr(page_phys), _ptr(list_len),
+                                                 float(sm_scale), _ptr(out), _ptr(out_lse), _stream(stream)),
+           "spd_sparse_paged_decode_noalloc")
 
 
 def spd_lse_merge(desc, plan, part_o, part_lse, list_len, out, out_lse, stream=None):

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -567,6 +568,51 @@ int spd_lse_merge(const spd_desc* desc, const spd_plan_params* plan, const float
   a.rows_per_head = desc->num_q_heads / desc->num_kv_heads;
   a.num_tokens = 1;
   return launched(spd::launch_lse_merge(a, desc->head_dim, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ decode without allocation
+
+// Chunk partials of spd_sparse_paged_decode_noalloc: a file-scope array in device memory, one copy per
+// GPU, held until the process ends.  In host code `scratch` only names the symbol; kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[SPD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];  // per device, resolved on its first call
+
+// The current device's address of `scratch` (looked up once per device, with that device current).
+static int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPD_ERR_LAUNCH;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPD_ERR_LAUNCH;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SPD_OK;
+}
+
+int spd_sparse_paged_decode_noalloc(const spd_desc* desc, const spd_plan_params* plan, const void* q,
+                                    const void* k_pool, const void* v_pool, const uint16_t* k_scale,
+                                    const uint16_t* v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* page_list, const int32_t* page_phys, const int32_t* list_len,
+                                    float sm_scale, float* out, float* out_lse, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  size_t n_po, n_pl;
+  if ((rc = spd_partials_size(desc, plan, &n_po, &n_pl))) return rc;
+  const size_t lse_off = align_up(n_po * sizeof(float));
+  if (lse_off + n_pl * sizeof(float) > (size_t)SPD_NOALLOC_SCRATCH_BYTES) return SPD_ERR_WORKSPACE;
+  if (desc->batch == 0) return SPD_OK;
+  void* base = nullptr;
+  if ((rc = scratch_address(&base))) return rc;
+  float* part_o = static_cast<float*>(base);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(base) + lse_off);
+  if ((rc = decode_impl(desc, plan, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, page_list,
+                        page_phys, list_len, sm_scale, out, out_lse, part_o, part_lse, nullptr, stream)))
+    return rc;
+  return spd_lse_merge(desc, plan, part_o, part_lse, list_len, out, out_lse, stream);
 }
 
 // ------------------------------------------------------------------ several query tokens per request

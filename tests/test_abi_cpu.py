@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 12
+    assert A.abi_version() == 13
 
 
 def test_error_strings(lib):
@@ -407,3 +407,20 @@ def test_several_query_token_selection_argument_checks(lib):
     assert sel_rc(desc_for(w, max_list=24, page_size=64)) == A.SPD_ERR_UNSUPPORTED
     assert sel_rc(desc_for(w, max_list=24, max_pages_per_seq=40000)) == A.SPD_ERR_UNSUPPORTED
     assert sel_rc(desc_for(w, max_list=24, batch=0)) == A.SPD_OK
+
+
+def test_noalloc_decode_rejects_partials_beyond_its_array(lib):
+    """spd_sparse_paged_decode_noalloc refuses a descriptor and plan whose chunk partials exceed its
+    array, before touching the device; invalid descriptors and plans are refused as elsewhere."""
+    w = W.small("noalloc_huge", seq_lens=(100,) * 64, Hkv=64, Hq=256)
+    L = A.lib()
+
+    def rc(desc, plan):
+        return L.spd_sparse_paged_decode_noalloc(ctypes.byref(desc), ctypes.byref(plan), FAKE, FAKE, FAKE, None, None,
+                                                 FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE, 0)
+
+    d = desc_for(w)
+    assert rc(d, A.PlanParams(4, 1024, 0, 0)) == A.SPD_ERR_WORKSPACE     # 4096 rows x 1024 chunks
+    assert rc(d, A.PlanParams(0, 16, 512, 0)) == A.SPD_ERR_INVALID_ARG   # min_chunk < 1
+    assert rc(desc_for(w, head_dim=96), A.PlanParams(4, 16, 512, 0)) == A.SPD_ERR_UNSUPPORTED
+    assert rc(desc_for(w, batch=0), A.PlanParams(4, 16, 512, 0)) == A.SPD_OK
