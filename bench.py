@@ -40,6 +40,8 @@ PEAK_HBM_TBS = 8.0
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SOURCES = ["score_common.h", "page_score.hip", "spd_device.h", "spd_launch.h"]  # what page_score_kernel is built from
 MVAR_SOURCES = KERNEL_SOURCES + ["page_score_mvar.hip", "meta_build.h"]  # page_score_mvar_kernel
+DECODE_SOURCES = ["sparse_paged_decode.hip", "spd_device.h", "spd_launch.h"]  # sparse_paged_decode_kernel
+HELD_OUT = (100, 101, 102, 103, 104)  # timing seeds beside the calibration seed (offsets from each workload's seed)
 
 
 def kernel_hash(files=KERNEL_SOURCES) -> str:
@@ -132,8 +134,8 @@ def copy_bandwidth(stream, mib: int = 1024, reps: int = 10) -> float:
     return 2 * (mib << 20) / sec / 1e12
 
 
-def cpu_baseline(w, inp, seconds: float) -> dict:
-    """The fp64 oracle (untuned) on the host: whole decode steps of this workload."""
+def _oracle_steps(w, inp, seconds: float) -> dict:
+    """Whole decode steps of the fp64 oracle (untuned), one thread, for about `seconds`."""
     from threadpoolctl import threadpool_limits
 
     from oracle import spd_oracle as O
@@ -163,6 +165,101 @@ def cpu_baseline(w, inp, seconds: float) -> dict:
     return {"steps": steps, "seconds": el, "step_s": el / steps}
 
 
+def cpu_baseline(w, inp, seconds: float) -> dict:
+    """The fp64 oracle on the host: whole decode steps of this workload on one thread."""
+    return _oracle_steps(w, inp, seconds)
+
+
+_ARRAYS = ("q", "k_pool", "v_pool", "k_scale", "v_scale", "block_table", "seq_lens", "head_kind")
+
+
+def _oracle_worker(job):
+    """A host process running whole oracle steps over inputs held in shared memory (it imports no GPU code)."""
+    from multiprocessing import shared_memory
+
+    from sparse_paged_decode_quest_amd import workloads as W
+
+    w, specs, seconds = job
+    shms, arrs = [], {}
+    for name, spec in specs.items():
+        if spec is None:
+            arrs[name] = None
+            continue
+        shm_name, shape, dtype = spec
+        shm = shared_memory.SharedMemory(name=shm_name)
+        shms.append(shm)
+        arrs[name] = np.ndarray(shape, dtype=np.dtype(dtype), buffer=shm.buf)
+    try:
+        inp = W.Inputs(workload=w, **arrs)
+        return _oracle_steps(w, inp, seconds)
+    finally:
+        for shm in shms:
+            shm.close()
+
+
+def host_cpu() -> dict:
+    """The host's CPU model and the cores this process may use (read at run time)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return {"model": model, "cores_available": cores}
+
+
+def cpu_baseline_parallel(w, inp, seconds: float, procs: int) -> dict:
+    """The same oracle steps in `procs` host processes at once (one thread each), over shared copies of the
+    inputs: the host's whole-step throughput with that many cores."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+
+    shms, specs = [], {}
+    try:
+        for name in _ARRAYS:
+            a = getattr(inp, name)
+            if a is None:
+                specs[name] = None
+                continue
+            a = np.ascontiguousarray(a)
+            shm = shared_memory.SharedMemory(create=True, size=max(1, a.nbytes))
+            shms.append(shm)
+            np.ndarray(a.shape, dtype=a.dtype, buffer=shm.buf)[...] = a
+            specs[name] = (shm.name, a.shape, a.dtype.str)
+        from concurrent.futures import ProcessPoolExecutor
+
+        # a worker that cannot start raises here (BrokenProcessPool) instead of being respawned, and the
+        # wait is bounded
+        with ProcessPoolExecutor(max_workers=procs, mp_context=mp.get_context("spawn")) as ex:
+            futs = [ex.submit(_oracle_worker, (w, specs, seconds)) for _ in range(procs)]
+            res = [f.result(timeout=4 * seconds + 300) for f in futs]
+    finally:
+        for shm in shms:
+            shm.close()
+            shm.unlink()
+    steps = sum(r["steps"] for r in res)
+    el = max(r["seconds"] for r in res)
+    return {"steps": steps, "seconds": el, "step_s": el / steps, "procs": procs}
+
+
+def traffic_record(w_name: str, kernel: str, sources) -> dict | None:
+    """The committed counter record of `kernel` on workload `w_name`, if its sources still hash to the value
+    the counters were taken at."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    with open(PMC_FILE) as f:
+        pmc = json.load(f)
+    h = kernel_hash(sources)
+    for rec in pmc.get("records", []):
+        if rec["workload"] == w_name and rec["kernel"] == kernel and rec["kernel_hash"] == h:
+            return rec
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +268,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--layers", type=int, default=0, help="independent input copies rotated per step (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-procs", type=int, default=16,
+                    help="host processes of the all-cores CPU baseline (capped at the cores this process may use)")
+    ap.add_argument("--held-out-steps", type=int, default=420,
+                    help="timed steps on each held-out seed (0: skip)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--fused", action="store_true", help="scorer and selector in one launch")
     ap.add_argument("--merged", action="store_true", help="decode and merge in one launch (last-block merge)")
@@ -352,6 +453,36 @@ def main():
     ab = algorithmic_bytes(w, list_len, inp.head_kind)
     tbs = ab["total"] / step_s / 1e12
 
+    # Held-out seeds: the same workload drawn from the timing seeds (the calibration seed above chose the
+    # plan constants), each with its own rotated layer copies; step time and achieved bandwidth per seed.
+    held = None
+    if args.held_out_steps > 0:
+        per_seed = {}
+        for off in HELD_OUT:
+            ws = W.named(w.name, seed_offset=off)
+            inp_s = W.generate(ws)
+            d0 = S.upload(inp_s)
+            S.build_meta(ws, d0)
+            ds = [d0] + [S.DeviceInputs(q=clone(d0.q), k_pool=clone(d0.k_pool), v_pool=clone(d0.v_pool),
+                                        k_scale=clone(d0.k_scale), v_scale=clone(d0.v_scale),
+                                        block_table=clone(d0.block_table), seq_lens=clone(d0.seq_lens),
+                                        head_kind=d0.head_kind.copy(), page_meta=clone(d0.page_meta))
+                         for _ in range(R - 1)]
+            st_s = [S.DecodeStep(ws, d, plan=plan, fused=args.fused, merged=args.merged) for d in ds]
+            saved = steps[:]
+            steps[:] = st_s  # `timed` replays the layers in `steps`
+            timed(whole, R, R)
+            sec = timed(whole, args.held_out_steps, R) / args.held_out_steps
+            ab_s = algorithmic_bytes(ws, st_s[0].list_len.cpu().numpy(), inp_s.head_kind)
+            steps[:] = saved
+            per_seed[str(ws.seed)] = {"step_us": round(sec * 1e6, 3), "TBs": round(ab_s["total"] / sec / 1e12, 4)}
+            del ds, st_s, d0, inp_s
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        us = [v["step_us"] for v in per_seed.values()]
+        held = {"seeds": per_seed, "median_step_us": round(float(np.median(us)), 3),
+                "steps_each": args.held_out_steps, "calibration_seed": w.seed}
+
     dom_name = "select" if args.fused else "score"
     mvar = w.estimator == "mvar"
     dom_kernel = "page_score_select_kernel" if args.fused else "page_score_mvar_kernel" if mvar else "page_score_kernel"
@@ -359,25 +490,31 @@ def main():
     dom_bytes = scorer_bytes(w, inp.head_kind, probe.tail)
     dom_us = phase_us[dom_name]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic = None
-    if os.path.exists(PMC_FILE):
-        with open(PMC_FILE) as f:
-            pmc = json.load(f)
-        rec = pmc.get(w.name, {})
-        if rec.get("kernel_hash") == dom_hash and rec.get("kernel") == dom_kernel:
-            traffic = rec.get("hbm_bytes_per_launch")
+    rec = traffic_record(w.name, dom_kernel, MVAR_SOURCES if mvar else KERNEL_SOURCES)
+    traffic = rec["hbm_bytes_per_launch"] if rec else None
+    dec_rec = traffic_record(w.name, "sparse_paged_decode_kernel", DECODE_SOURCES)
     roofline = {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_TBS * 1000, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4),
                 "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3),
                 "frac_of_beta_copy": round(achieved / (beta * 1000), 4)}
 
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu:
+        host = host_cpu()
         cb = cpu_baseline(w, inp, args.cpu_seconds)
         cpu = {"value": round(ab["total"] / cb["step_s"] / 1e12, 8), "unit": "TB/s", "cores": 1, "kind": "oracle",
                "sample": f"{cb['steps']} whole decode steps of {w.name} (tail meta refresh, scores, selection, "
                          f"attention; fp64 numpy, 1 thread) in {cb['seconds']:.1f} s",
-               "step_ms": round(cb["step_s"] * 1e3, 2)}
+               "step_ms": round(cb["step_s"] * 1e3, 2), "cpu_model": host["model"]}
+        procs = max(1, min(args.cpu_procs, host["cores_available"]))
+        if procs > 1:
+            cp = cpu_baseline_parallel(w, inp, args.cpu_seconds, procs)
+            cpu_all = {"value": round(ab["total"] / cp["step_s"] / 1e12, 8), "unit": "TB/s", "cores": procs,
+                       "kind": "oracle",
+                       "sample": f"{cp['steps']} whole decode steps of {w.name} in {procs} host processes at once "
+                                 f"(one thread each, inputs shared) in {cp['seconds']:.1f} s",
+                       "step_ms": round(cp["step_s"] * 1e3, 3), "cpu_model": host["model"],
+                       "cores_available": host["cores_available"]}
 
     step_us = step_s * 1e6
     if not args.fused:
@@ -404,7 +541,11 @@ def main():
         "phase_us": {k: round(v, 3) for k, v in phase_us.items()},
         "selection_overhead": sel_over, "reuse": reuse,
         "list_len": {"min": int(list_len.min()), "median": int(np.median(list_len)), "max": int(list_len.max())},
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "cpu_baseline_all_cores": cpu_all,
+        "decode_traffic": None if dec_rec is None else {
+            "hbm_bytes_per_launch": dec_rec["hbm_bytes_per_launch"], "listed_kv_bytes": dec_rec["reference_bytes"],
+            "ratio": round(dec_rec["hbm_bytes_per_launch"] / dec_rec["reference_bytes"], 4)},
+        "held_out_seeds": held,
         "setup_s": round(gen_s, 1), "kernel_hash": dom_hash,
     }
     print(json.dumps(line))
