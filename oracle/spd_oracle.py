@@ -365,6 +365,27 @@ def select_coverage(pi: np.ndarray, n: int, gamma: float, forced: list) -> list:
     return list(range(n))
 
 
+def reuse_lists(inp, lists: dict) -> dict:
+    """Lists for a later step of a reuse chunk (LServe, "Reusable Page Selection": the pages selected
+    on the chunk's first step serve its remaining steps), at the current lengths inp.seq_lens.
+
+    Reading of the pages: a dynamic row keeps its selected pages and gains the pages of the current
+    forced set (sink and local window) that lie past its last entry, appended in ascending order --
+    a query must attend to its own newest page, and every rule here keeps the sink and local pages;
+    pages that were local when the chunk selected stay listed.  A streaming row takes its static sink
+    + local table for the current length."""
+    w = inp.workload
+    out = {}
+    for (b, h), lst in lists.items():
+        n = n_pages(inp.seq_lens[b])
+        if inp.head_kind[h]:
+            out[(b, h)] = forced_pages(n, w.n_sink_stream, w.n_local_stream)
+            continue
+        last = lst[-1] if lst else -1
+        out[(b, h)] = list(lst) + [p for p in forced_pages(n, w.n_sink, w.n_local) if p > last]
+    return out
+
+
 def page_select(inp, meta: np.ndarray, stats: np.ndarray | None = None):
     """Scores and lists for every (request, KV head) row.
 

@@ -317,7 +317,15 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
     // is what V's fp16 values times 2^8 are weighted with).  Slots past the request's end (scales may
     // be NaN) are masked before either is used.
     const float kscale = KVD == SPD_DTYPE_F16 ? a.sm_scale_log2 : a.sm_scale_log2 * (ok ? kv.ks : 0.f);
-    const float vscale = KVD == SPD_DTYPE_F16 ? 1.f : (ok ? kv.vs : 0.f);
+    // fp8: the probabilities carry each key's V scale relative to the page's largest (at most 1, so the
+    // fp16 operand neither overflows nor loses precision to small scales); that largest scale multiplies
+    // the page's PV product in fp32 below
+    float vmax = 1.f;
+    if constexpr (KVD != SPD_DTYPE_F16) {
+      vmax = row_max(tok < r.valid ? kv.vs : 0.f);  // the page's 16 tokens, one per lane of the row
+      vmax = vmax > 0.f ? vmax : 1.f;
+    }
+    const float vscale = KVD == SPD_DTYPE_F16 ? 1.f : (ok ? kv.vs / vmax : 0.f);
     float p[4], alpha[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -350,10 +358,13 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
     // B = P^T: row l % 16, keys 4 q4 .. 4 q4 + 3; A = V^T tile s: channel 16 s + l % 16, the same keys
     const mq_half4 pb = *reinterpret_cast<const mq_half4*>(&p16[wave][tok][4 * q4]);
     const float al = al_lds[wave][tok];
+    // fp8: acc = vmax (acc al / vmax + V^T P'^T), the page's contribution scaled in fp32
+    const float pre = KVD == SPD_DTYPE_F16 ? al : al / vmax;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
       const uint2 va = reinterpret_cast<const uint2*>(&vt[wave][16 * t + tok][0])[q4];
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(mq_half4, va), pb, acc[t] * al, 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(mq_half4, va), pb, acc[t] * pre, 0, 0, 0);
+      if constexpr (KVD != SPD_DTYPE_F16) acc[t] = acc[t] * vmax;
     }
     wave_fence();
   };

@@ -40,6 +40,8 @@ MQ_SMALL = {
                           delta=3.0),
     "t4_fp8": W.small("mq_fp8", num_queries=4, kv="fp8", seq_lens=(1500, 250, 31, 3), budget=16,
                       streaming=(0,), n_sink_stream=1, n_local_stream=2),
+    # four token lists of 256 entries: the union's capacity is exactly 1024 entries (the rank merge's limit)
+    "t4_cap1024": W.small("mq_cap", num_queries=4, seq_lens=(9000, 4100, 700), budget=256, Hkv=2, Hq=8),
 }
 
 
@@ -276,3 +278,33 @@ def test_mq_graph_replay_equals_eager():
                 sl = slice(h * G, (h + 1) * G)
                 P.check_attention(out[b, t, sl], lse[b, t, sl], res["O"][b, t, sl], res["out_lse"][b, t, sl],
                                   w.kv_dtype, f"replay token {t} row {b},{h}")
+
+
+@pytest.mark.parametrize("factor", [1e5, 1e-3], ids=["large_v", "small_v"])
+def test_mq_fp8_value_scales_at_both_ends(factor):
+    """fp8 V scales far above and below the usual (V amax about 3e5 and 3e-3): the decode's fp16
+    probability operand carries each scale relative to its page's largest, so neither overflows to inf
+    nor loses precision in fp16 subnormals.  Attention is linear in V, so outputs are compared after
+    dividing by the factor."""
+    w = MQ_SMALL["t4_fp8"]
+    inp = W.generate(w)
+    vs = inp.v_scale.astype(np.float64) * factor
+    assert np.isfinite(vs[np.isfinite(inp.v_scale)]).all() and vs[np.isfinite(vs)].max() < 65504
+    inp.v_scale = vs.astype(np.float16)
+    say(f"[case] v_scale x {factor}: stored scales {np.nanmin(inp.v_scale):.3g} .. {np.nanmax(inp.v_scale):.3g}")
+    d = S.upload(inp)
+    S.build_meta(w, d)
+    st = S.MQDecodeStep(w, d)
+    st.run()
+    torch.cuda.synchronize()
+    res = O.mq_decode_step(inp)
+    gpu_lists = st.token_lists()
+    out, lse = st.out.cpu().numpy(), st.out_lse.cpu().numpy()
+    assert np.isfinite(out).all()
+    G = w.group
+    for t in range(w.num_queries):
+        for (b, h), lst in res["lists_by_token"][t].items():
+            if gpu_lists[t][(b, h)] == lst:
+                sl = slice(h * G, (h + 1) * G)
+                P.check_attention(out[b, t, sl] / factor, lse[b, t, sl], res["O"][b, t, sl] / factor,
+                                  res["out_lse"][b, t, sl], w.kv_dtype, f"x{factor} token {t} row {b},{h}")

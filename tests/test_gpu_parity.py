@@ -403,13 +403,9 @@ def test_reusable_selection_serves_a_chunk_of_growing_steps(reuse):
         poison_outputs(st)
         st.reuse_step()
         torch.cuda.synchronize()
-        for (b, h), lst in expect.items():
-            n = O.n_pages(int(L[b]))
-            if inp.head_kind[h]:
-                expect[(b, h)] = O.forced_pages(n, w.n_sink_stream, w.n_local_stream)
-            else:
-                last = lst[-1] if lst else -1
-                expect[(b, h)] = lst + [p for p in O.forced_pages(n, w.n_sink, w.n_local) if p > last]
+        at = copy.copy(inp)
+        at.seq_lens = L.astype(inp.seq_lens.dtype)
+        expect = O.reuse_lists(at, expect)
         got = st.lists()
         assert got == expect, i
         pp = st.page_phys.cpu().numpy()

@@ -469,3 +469,62 @@ def test_tiny_workload_selects_its_planted_pages():
         # deviations of its spread over N(0, 1) pages, so most (not all) planted pages rank high
         hit = len(set(inp.planted[(0, h)].tolist()) & set(lst))
         assert hit >= 5, hit
+
+
+# ---------------------------------------------------------------------------------- reuse rule
+
+def _reuse_inputs(seq_lens, streaming=(1,)):
+    w = W.small("reuse_pin", seq_lens=seq_lens, budget=6, n_sink=1, n_local=2, streaming=streaming,
+                n_sink_stream=2, n_local_stream=2, Hkv=2, Hq=8)
+    return W.generate(w)
+
+
+def test_reuse_rule_worked_example():
+    """Hand-worked: a top-K list selected at 12 pages, reused one token later (13 pages): the newly
+    opened page 12 is appended; page 10, local when selected, stays; the streaming row follows the length."""
+    import copy
+
+    inp = _reuse_inputs((16 * 12,))
+    sel = {(0, 0): [0, 5, 9, 10, 11], (0, 1): [0, 1, 10, 11]}
+    later = copy.copy(inp)
+    later.seq_lens = np.array([16 * 12 + 1], dtype=inp.seq_lens.dtype)
+    got = O.reuse_lists(later, sel)
+    assert got[(0, 0)] == [0, 5, 9, 10, 11, 12]
+    assert got[(0, 1)] == [0, 1, 11, 12]
+
+
+def test_reuse_rule_is_the_selection_when_lengths_do_not_change():
+    """At the chunk's first step's own lengths the reused lists are the selected lists: every forced page
+    is already listed (a selection always holds the sink and the local window)."""
+    inp = _reuse_inputs((700, 37, 2050, 16, 17))
+    sel = O.page_select(inp, O.page_meta_build(inp))["lists"]
+    assert O.reuse_lists(inp, sel) == sel
+
+
+@pytest.mark.parametrize("grow", [1, 15, 16, 17, 40])
+def test_reuse_rule_keeps_the_chunk_and_the_current_forced_pages(grow):
+    """After growth every reused dynamic list is ascending without repeats, holds the chunk's selection
+    and the current sink and local pages, adds only pages that did not exist or were past the old last
+    entry, and is at most the chunk's list plus the pages opened since."""
+    import copy
+
+    full = np.array([700, 37, 2050, 16, 17]) + 40
+    inp = _reuse_inputs(tuple(int(x) for x in full))
+    first = copy.copy(inp)
+    first.seq_lens = (full - 40).astype(inp.seq_lens.dtype)
+    sel = O.page_select(first, O.page_meta_build(first))["lists"]
+    later = copy.copy(inp)
+    later.seq_lens = (full - 40 + grow).astype(inp.seq_lens.dtype)
+    got = O.reuse_lists(later, sel)
+    w = inp.workload
+    for (b, h), lst in got.items():
+        n_old, n_new = O.n_pages(first.seq_lens[b]), O.n_pages(later.seq_lens[b])
+        if inp.head_kind[h]:
+            assert lst == list(range(min(2, n_new))) + [p for p in range(max(2, n_new - 2), n_new)]
+            continue
+        assert lst == sorted(set(lst))
+        assert set(sel[(b, h)]) <= set(lst)
+        assert set(O.forced_pages(n_new, w.n_sink, w.n_local)) <= set(lst)
+        added = [p for p in lst if p not in set(sel[(b, h)])]
+        assert all(p > max(sel[(b, h)]) for p in added)
+        assert len(lst) <= len(sel[(b, h)]) + (n_new - n_old)
