@@ -98,7 +98,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 13
+#define SPD_ABI_VERSION 14
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
@@ -191,6 +191,18 @@ typedef struct spd_select_params {
   int32_t n_sink_stream;
   int32_t n_local_stream;
   int32_t estimator;          /* spd_estimator; MVAR needs COVERAGE */
+  void* topk_state;           /* (device, nullable) TOPK with the BOUND estimator and page_size 16 only: the
+                               * LiteTopK gate state of every (token) row, spd_topk_state_bytes(rows)
+                               * bytes, zero-filled before its first use and then left to the library.
+                               * When set, spd_page_select / spd_page_select_mq predict each row's gate
+                               * from its previous selection (LiteTopK, section 3.3 "Predictive Gating":
+                               * the lower edge where 1.5 K' free pages are reached) and, on the next call,
+                               * rank only the free pages scoring at or above it when they number at
+                               * least the K' = budget - |forced| pages the rule takes and at most 2048
+                               * (then they hold the top K' and every page tied with the K'-th; LiteTopK,
+                               * section 3.2 "Top-k Selection"), else the whole row.  Lists are those of
+                               * the ungated selection exactly.  Calls on one state must not overlap.
+                               * Ignored by the scorers and spd_page_list_refresh. */
 } spd_select_params;
 
 /* Self-planned split (Moira, section 3.3, Eq. 4): J = max(min_blocks_per_row,
@@ -478,6 +490,13 @@ int spd_partials_size(const spd_desc* desc, const spd_plan_params* plan, size_t*
 /* Workspace bytes an op needs (0 when it needs none); (size_t)-1 on invalid arguments or an
  * op that the arguments do not support. */
 size_t spd_workspace_bytes(const spd_desc* desc, const spd_select_params* sel, int32_t op);
+
+/* Bytes of a LiteTopK gate state (spd_select_params.topk_state) for `rows` rows: B * Hkv for a
+ * single-query step, B * T * Hkv for spd_page_select_mq.  Per row 32 bytes: {float gate, float largest
+ * free score of the last selection, uint32 valid, uint32 path of the last selection (1: from the
+ * candidates, 0: whole row), uint32 candidates it counted, 3 x uint32 reserved}.  (size_t)-1 for
+ * rows < 0. */
+size_t spd_topk_state_bytes(int32_t rows);
 
 /* Static description of a status code. */
 const char* spd_error_string(int status);

@@ -31,7 +31,7 @@ EXPORTS = ("spd_page_meta_build", "spd_page_stats_build", "spd_page_score", "spd
            "spd_sparse_paged_decode", "spd_lse_merge", "spd_plan_grid", "spd_plan_chunks", "spd_page_list_refresh",
            "spd_partials_size", "spd_workspace_bytes", "spd_error_string", "spd_abi_version",
            "spd_page_list_union", "spd_sparse_paged_decode_mq", "spd_lse_merge_mq", "spd_sparse_paged_decode_merged",
-           "spd_page_score_mq", "spd_page_select_mq", "spd_sparse_paged_decode_noalloc")
+           "spd_page_score_mq", "spd_page_select_mq", "spd_sparse_paged_decode_noalloc", "spd_topk_state_bytes")
 MQ_ROWS = 16  # chunk-state rows per (request, KV head) of the several-query decode
 
 
@@ -51,7 +51,7 @@ class Desc(ctypes.Structure):
 class SelectParams(ctypes.Structure):
     _fields_ = [("mode", c_int32), ("budget_pages", c_int32), ("gamma", c_float), ("sm_scale", c_float),
                 ("n_sink", c_int32), ("n_local", c_int32), ("n_sink_stream", c_int32),
-                ("n_local_stream", c_int32), ("estimator", c_int32)]
+                ("n_local_stream", c_int32), ("estimator", c_int32), ("topk_state", c_void_p)]
 
 
 class PlanParams(ctypes.Structure):
@@ -93,11 +93,13 @@ def lib():
         L.spd_partials_size.argtypes = [D, P, POINTER(c_size_t), POINTER(c_size_t)]
         L.spd_workspace_bytes.argtypes = [D, S, c_int32]
         L.spd_workspace_bytes.restype = c_size_t
+        L.spd_topk_state_bytes.argtypes = [c_int32]
+        L.spd_topk_state_bytes.restype = c_size_t
         L.spd_error_string.argtypes = [c_int32]
         L.spd_error_string.restype = ctypes.c_char_p
         L.spd_abi_version.argtypes = []
         for name in EXPORTS:
-            if name not in ("spd_workspace_bytes", "spd_error_string"):
+            if name not in ("spd_workspace_bytes", "spd_error_string", "spd_topk_state_bytes"):
                 getattr(L, name).restype = c_int32
         _lib = L
     return _lib
@@ -283,3 +285,14 @@ def spd_workspace_bytes(desc, sel, op) -> int:
     if n == ctypes.c_size_t(-1).value:
         raise SpdError(SPD_ERR_INVALID_ARG, "spd_workspace_bytes")
     return n
+
+
+def spd_topk_state_bytes(rows: int) -> int:
+    n = lib().spd_topk_state_bytes(int(rows))
+    if n == ctypes.c_size_t(-1).value:
+        raise SpdError(SPD_ERR_INVALID_ARG, "spd_topk_state_bytes")
+    return n
+
+
+# gate state of one row (spd_topk_state_bytes): float gate, float top, uint32 valid, path, seen, 3 x reserved
+GATE_ROW_BYTES = 32

@@ -74,6 +74,11 @@ __global__ __launch_bounds__(NW * kWave) void page_select_kernel(SelectArgs a) {
     select_streaming_row(a, row_phys_pages(token_row_length(a, token_row, b_), a.max_pages, a.lgs), row, bt_row);
     return;
   }
+  // LiteTopK gate of the row (requested with the scores)
+  TopkGateRow gr{};
+  if constexpr (!COV) {
+    if (a.gate.rows) gr = a.gate.rows[row];
+  }
   uint32_t key[KPL];
   SlotPhys<KPL> phys;
   phys.bt_row = bt_row;
@@ -87,7 +92,12 @@ __global__ __launch_bounds__(NW * kWave) void page_select_kernel(SelectArgs a) {
     const int len = token_row_length(a, token_row, b_);
     load_row_keys<NW, KPL, COV>(a.scores + row * a.max_pages, &len, a.max_pages, a.lgs, key, phys, n);
   }
-  select_row_keys<NW, KPL, COV>(a, key, phys, row_shape(n, a.n_sink, a.n_local), row, sm);
+  if constexpr (COV) {
+    select_row_keys<NW, KPL, COV>(a, key, phys, row_shape(n, a.n_sink, a.n_local), row, sm);
+  } else {
+    __shared__ GateSmem gs;
+    select_row_keys<NW, KPL, COV>(a, key, phys, row_shape(n, a.n_sink, a.n_local), row, sm, &gr, &gs);
+  }
 }
 
 // Reusable page selection (LServe, "Reusable Page Selection"): between two selections the lists

@@ -62,7 +62,15 @@ struct SelectSmem {
     H above, inbin;  // count / mass above the bin and inside it
     uint32_t kc;     // top-K cut key found by ranking the crossing bin's keys
     int need_eq;     // keys equal to kc still to take
+    int gate_bin;    // top-K, first digit: lowest bin of the group where 1.5 K' keys are reached (-1: fewer)
   } cross;
+};
+
+// The candidate path of the gated top-K selector (LiteTopK): the free keys at or above the gate, in page order.
+struct GateSmem {
+  uint32_t key[kGateCap];
+  int32_t page[kGateCap];
+  int32_t phys[kGateCap];
 };
 
 __device__ __forceinline__ unsigned long long share_fx(float pi) {
@@ -110,27 +118,41 @@ struct SlotPhys {
   }
 };
 
-// Select the pages of one dynamic row from its keys (top-K: score_key of the scores;
-// coverage: coverage_key of the shares).  phys gives the physical page of each slot (written
-// to a.page_phys when that is set).  Every thread of the workgroup must call this.
-template <int NW, int KPL, bool COV>
-__device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint32_t (&key)[KPL],
-                                                const SlotPhys<KPL>& phys, const RowShape r, const size_t row,
-                                                SelectSmem<NW, KPL, COV>& sm) {
-  using H = typename SelectSmem<NW, KPL, COV>::H;
+// The next call's gate of row `row` (LiteTopK, section 3.3, predictive gating from the previous token's
+// selection): candidates will be the free pages scoring at least the score of gate_key; with no key
+// (gate_key = 0) the gate is `fallback` (-inf: every free page).  Rows that took every free page or none
+// keep no gate.
+__device__ __forceinline__ void gate_store(const TopkGate& g, size_t row, int dec, uint32_t gate_key, uint32_t top_key,
+                                           float fallback, uint32_t path, uint32_t seen) {
+  TopkGateRow v;
+  v.lo = gate_key ? key_to_score(gate_key) : fallback;
+  v.top = top_key ? key_to_score(top_key) : -INFINITY;
+  v.valid = dec == 2 ? 1u : 0u;
+  v.path = path;  // how this selection ran: 1 from the candidates, 0 over the whole row
+  v.seen = seen;  // free pages at or above the gate it counted
+  v.pad[0] = v.pad[1] = v.pad[2] = 0u;
+  g.rows[row] = v;
+}
+
+// The cut of one row's keys: the decision dec (0: forced pages only, 1: every free page, 2: cut at key kc --
+// keys above kc are taken, keys equal to kc while fewer than need_eq were taken, in page order), found by the
+// radix walk described at the top of this file.  free_at / forced_at say which key slots are free or forced
+// pages, page_of gives the page order of a slot (ties are taken in that order); n_free / n_forced count them.
+// Top-K also returns top_key, the largest free key, and gate_key, the lower edge of the first digit's group
+// where 1.5 K' free keys are reached (0 when there are fewer, or no walk ran): the next call's predicted gate.
+// Every thread of the workgroup must call this.
+template <int NW, int KPL, bool COV, typename SM, typename FreeAt, typename ForcedAt, typename PageOf>
+__device__ __forceinline__ void row_cut(const SelectArgs& a, const uint32_t (&key)[KPL], FreeAt free_at,
+                                        ForcedAt forced_at, PageOf page_of, const int n_free, const int n_forced,
+                                        SM& sm, int& dec, uint32_t& kc, int& need_eq, uint32_t& gate_key,
+                                        uint32_t& top_key) {
+  using H = typename SM::H;
   constexpr int STRIDE = NW * kWave;
   constexpr int PER = SelectDigit<COV>::kBins / kWave;  // histogram bins summed by one lane
   constexpr int kBits = SelectDigit<COV>::kBits;
   constexpr int kBins = SelectDigit<COV>::kBins;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int n_free = r.local_begin - r.sink_end;
-  const int n_forced = r.n - n_free;
-  const int wbase = wave * kWave * KPL + lane;
-  auto page_of = [&](int i) { return wbase + i * kWave; };
-  auto free_at = [&](int i) { return (unsigned)(page_of(i) - r.sink_end) < (unsigned)n_free; };
-  auto forced_at = [&](int i) { const int p = page_of(i); return p < r.n && !free_at(i); };
   auto mass_of = [&](uint32_t k) { return share_fx(__uint_as_float(k)); };
-
   // ---- range of the free keys, forced mass (coverage); clear two histogram buffers
   uint32_t mn = 0xffffffffu, mx = 0u;
   unsigned long long fmass = 0;
@@ -157,11 +179,12 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
   // lane w < NW reads wave w's entries; DPP reductions give every lane the workgroup's values
   mn = wave_min(lane < NW ? sm.wmin[lane] : 0xffffffffu);
   mx = wave_max(lane < NW ? sm.wmax[lane] : 0u);
+  top_key = mx;
+  gate_key = 0u;
   if (COV) fmass = wave_sum(lane < NW ? sm.wsum[lane] : 0ull);
 
   // ---- decision: 0 = forced pages only, 1 = every page, 2 = cut at key kc: keys above kc are
   // kept, keys equal to kc are kept in page order while fewer than need_eq of them were taken.
-  int dec;
   unsigned long long need;  // count (top-K) or mass (coverage) still to cover
   if (!COV) {
     const int kp = a.budget - n_forced;
@@ -171,8 +194,8 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
     dec = (n_free == 0 || fmass >= a.gamma_fx) ? 0 : 2;
     need = dec == 2 ? a.gamma_fx - fmass : 0ull;
   }
-  uint32_t kc = 0;
-  int need_eq = kNoLimit;
+  kc = 0;
+  need_eq = kNoLimit;
   if (dec == 2) {
     if (mn == mx) {
       // every free key is equal: top-K takes them in page order; coverage keeps them all (they
@@ -211,6 +234,15 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
           for (int j = 0; j < PER; ++j) s += h[lane * PER + ((j + lane) % PER)];
           const H incl = wave_incl_scan(s);
           const H excl = incl - s;
+          if constexpr (!COV) {
+            // the next call's gate (LiteTopK, section 3.3): the lowest bin of the group where the count from
+            // the top reaches 1.5 K' (the margin of a predicted filter)
+            if (pass == 0) {
+              const H need2 = need + need / 2;
+              const unsigned long long hit2 = __ballot(excl < need2 && incl >= need2);
+              if (lane == 0) sm.cross.gate_bin = hit2 ? kBins - 1 - ((__ffsll((long long)hit2) - 1) * PER + PER - 1) : -1;
+            }
+          }
           const unsigned long long hit = __ballot(excl < need && incl >= need);
           if (hit == 0ull) {  // coverage only: the free pages cannot reach t -- keep every page
             if (lane == 0) sm.cross.bin = -1;
@@ -238,6 +270,7 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
           break;
         }
         const H above = sm.cross.above, inbin = sm.cross.inbin;
+        if (!COV && pass == 0 && sm.cross.gate_bin >= 0) gate_key = prefix | ((uint32_t)sm.cross.gate_bin << shift);
         need -= above;
         prefix |= (uint32_t)bin << shift;
         pmask |= (uint32_t)(nb - 1) << shift;
@@ -298,6 +331,164 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
       }
     }
   }
+
+}
+
+// The gated top-K path (LiteTopK, section 3.2 "Sampling" and "Top-k Selection"; section 3.3 "Predictive
+// Gating").  The row's gate was predicted from its previous selection.  The free pages scoring at or above
+// it are the candidates; when they number at least K' they hold the top K' free pages and every page tied
+// with the K'-th, so the row's cut is the cut among the candidates.  They are gathered in page order (the
+// slot layout is page order: wave, slot, lane) with one ballot per slot, cut by the radix walk over their
+// scores' bit patterns (section 3.2, "Extension to Decoding"), and written between the row's sink and local
+// pages; the next gate is stored.  Returns false, with nothing written or stored, when the gate is absent
+// or the candidates number fewer than K' or more than kGateCap: the caller then cuts the whole row.
+// `seen` receives the candidate count (0 without a gate).  Every thread of the workgroup must call this.
+template <int NW, int KPL>
+__device__ __forceinline__ bool select_row_gated(const SelectArgs& a, const uint32_t (&key)[KPL],
+                                                 const SlotPhys<KPL>& phys, const RowShape r, const size_t row,
+                                                 const TopkGateRow& gr, SelectSmem<NW, KPL, false>& sm, GateSmem& gs,
+                                                 uint32_t& seen) {
+  constexpr int CS = kGateCap / (NW * kWave);  // candidate slots per lane in the cut
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int n_free = r.local_begin - r.sink_end;
+  const int n_forced = r.n - n_free;
+  const int kp = a.budget - n_forced;
+  seen = 0u;
+  if (!gr.valid || kp <= 0 || n_free <= kp) return false;  // uniform: nothing to rank, or no prediction
+  const int wbase = wave * kWave * KPL + lane;
+  auto page_of = [&](int i) { return wbase + i * kWave; };
+  const uint32_t gate_key = score_key(gr.lo);
+  auto cand = [&](int i) { return (unsigned)(page_of(i) - r.sink_end) < (unsigned)n_free && key[i] >= gate_key; };
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) c += cand(i) ? 1u : 0u;
+  const uint32_t cw = wave_sum(c);
+  if (lane == 0) sm.wsure[wave] = cw;
+  __syncthreads();
+  const uint32_t wl = lane < NW ? sm.wsure[lane] : 0u;
+  const uint32_t wincl = wave_incl_scan(wl);
+  const uint32_t count = lane_u32(wincl, NW - 1);
+  seen = count;
+  if (count < (uint32_t)kp || count > (uint32_t)kGateCap) return false;  // uniform
+  // gather in page order
+  uint32_t pos = lane_u32(wincl - wl, wave);
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const bool ci = cand(i);
+    const unsigned long long m = __ballot(ci);
+    if (ci) {
+      const uint32_t q = pos + lanes_below(m);
+      gs.key[q] = key[i];
+      gs.page[q] = page_of(i);
+      if constexpr (SlotPhys<KPL>::kInRegs) gs.phys[q] = phys.v[i];
+    }
+    pos += (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  // the cut among the candidates: slot i of a lane holds candidate wave * 64 CS + 64 i + lane (page order)
+  const int cbase = wave * kWave * CS + lane;
+  uint32_t ck[CS];
+#pragma unroll
+  for (int i = 0; i < CS; ++i) ck[i] = cbase + i * kWave < (int)count ? gs.key[cbase + i * kWave] : 0u;
+  auto order_of = [&](int i) { return cbase + i * kWave; };
+  auto free_c = [&](int i) { return order_of(i) < (int)count; };
+  auto forced_c = [&](int) { return false; };
+  int dec;
+  uint32_t kc, next_key, top_key;
+  int need_eq;
+  row_cut<NW, CS, false>(a, ck, free_c, forced_c, order_of, (int)count, n_forced, sm, dec, kc, need_eq, next_key,
+                         top_key);
+  if (dec == 1) {  // exactly K' candidates: all taken
+    kc = 0u;
+    need_eq = kNoLimit;
+  }
+  // compaction: the chosen candidates after the sink pages
+  auto take_sure = [&](int i) { return free_c(i) && ck[i] > kc; };
+  auto take_eq = [&](int i) { return free_c(i) && ck[i] == kc; };
+  uint32_t sure_l = 0, eq_l = 0;
+#pragma unroll
+  for (int i = 0; i < CS; ++i) {
+    sure_l += take_sure(i) ? 1u : 0u;
+    eq_l += take_eq(i) ? 1u : 0u;
+  }
+  const uint32_t sure_w = wave_sum(sure_l), eq_w = wave_sum(eq_l);
+  if (lane == 0) {
+    sm.wsure[wave] = sure_w;
+    sm.weq[wave] = eq_w;
+  }
+  __syncthreads();
+  const uint32_t sw_l = lane < NW ? sm.wsure[lane] : 0u, ew_l = lane < NW ? sm.weq[lane] : 0u;
+  const uint32_t sw_incl = wave_incl_scan(sw_l), ew_incl = wave_incl_scan(ew_l);
+  const uint32_t sure_before = lane_u32(sw_incl - sw_l, wave), eq_before = lane_u32(ew_incl - ew_l, wave);
+  const uint32_t ne = (uint32_t)need_eq;
+  const uint32_t chosen = lane_u32(sw_incl, NW - 1) + min(lane_u32(ew_incl, NW - 1), ne);
+  uint32_t q0 = (uint32_t)r.sink_end + sure_before + min(eq_before, ne);
+  int eq_left = eq_before < ne ? (int)(ne - eq_before) : 0;
+  int32_t* out = a.page_list + row * a.max_list;
+  int32_t* out_phys = a.page_phys ? a.page_phys + row * a.max_list : nullptr;
+  float* out_sc = a.sel_scores ? a.sel_scores + row * a.max_list : nullptr;
+#pragma unroll
+  for (int i = 0; i < CS; ++i) {
+    const unsigned long long eq_mask = __ballot(take_eq(i));
+    const bool take = take_sure(i) || (take_eq(i) && (int)lanes_below(eq_mask) < eq_left);
+    const unsigned long long take_mask = __ballot(take);
+    const uint32_t q = q0 + lanes_below(take_mask);
+    if (take && q < (uint32_t)a.max_list) {
+      const int pg = gs.page[order_of(i)];
+      out[q] = pg;
+      if (out_phys) out_phys[q] = SlotPhys<KPL>::kInRegs ? gs.phys[order_of(i)] : phys.bt_row[pg];
+      if (out_sc) out_sc[q] = key_to_score(ck[i]);
+    }
+    q0 += (uint32_t)__popcll(take_mask);
+    eq_left -= __popcll(eq_mask);
+  }
+  // the forced pages: sinks first, locals last (every free page lies between them)
+  const int n_local_pages = r.n - r.local_begin;
+  for (int i = threadIdx.x; i < r.sink_end + n_local_pages; i += NW * kWave) {
+    const bool sink = i < r.sink_end;
+    const int pg = sink ? i : r.local_begin + (i - r.sink_end);
+    const uint32_t q = sink ? (uint32_t)i : (uint32_t)r.sink_end + chosen + (uint32_t)(i - r.sink_end);
+    if (q < (uint32_t)a.max_list) {
+      out[q] = pg;
+      if (out_phys) out_phys[q] = phys.bt_row[pg];
+      if (out_sc) out_sc[q] = a.scores[row * a.max_pages + pg];
+    }
+  }
+  if (threadIdx.x == 0) {
+    a.list_len[row] = (int)min((uint32_t)r.sink_end + chosen + (uint32_t)n_local_pages, (uint32_t)a.max_list);
+    gate_store(a.gate, row, 2, next_key, top_key, gr.lo, 1u, count);  // fewer than 1.5 K' candidates: keep the gate
+  }
+  return true;
+}
+
+// Select the pages of one dynamic row from its keys (top-K: score_key of the scores;
+// coverage: coverage_key of the shares).  phys gives the physical page of each slot (written
+// to a.page_phys when that is set).  Top-K rows with a gate state also get the next call's predicted
+// gate.  Every thread of the workgroup must call this.
+template <int NW, int KPL, bool COV>
+__device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint32_t (&key)[KPL],
+                                                const SlotPhys<KPL>& phys, const RowShape r, const size_t row,
+                                                SelectSmem<NW, KPL, COV>& sm, const TopkGateRow* gr = nullptr,
+                                                GateSmem* gs = nullptr) {
+  uint32_t seen = 0u;
+  if constexpr (!COV && KPL <= 32) {  // (rows over 32,768 pages keep their registers for the whole-row cut)
+    if (a.gate.rows && gr && gs) {
+      if (select_row_gated<NW, KPL>(a, key, phys, r, row, *gr, sm, *gs, seen)) return;
+      __syncthreads();  // the whole-row cut below reuses the shared counts
+    }
+  }
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int n_free = r.local_begin - r.sink_end;
+  const int n_forced = r.n - n_free;
+  const int wbase = wave * kWave * KPL + lane;
+  auto page_of = [&](int i) { return wbase + i * kWave; };
+  auto free_at = [&](int i) { return (unsigned)(page_of(i) - r.sink_end) < (unsigned)n_free; };
+  auto forced_at = [&](int i) { const int p = page_of(i); return p < r.n && !free_at(i); };
+  int dec;
+  uint32_t kc, gate_key, top_key;
+  int need_eq;
+  row_cut<NW, KPL, COV>(a, key, free_at, forced_at, page_of, n_free, n_forced, sm, dec, kc, need_eq, gate_key, top_key);
+  if (!COV && a.gate.rows && threadIdx.x == 0) gate_store(a.gate, row, dec, gate_key, top_key, -INFINITY, 0u, seen);
 
   // ---- compaction in ascending page order.  Decisions 0 and 1 become cuts that no free key
   // passes (every key is below 0xffffffff) or that every free key passes.

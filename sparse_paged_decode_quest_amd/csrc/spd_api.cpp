@@ -80,7 +80,20 @@ int check_sel(const spd_desc* d, const spd_select_params* s) {
   }
   if (s->estimator != SPD_ESTIMATOR_BOUND && s->estimator != SPD_ESTIMATOR_MVAR) return SPD_ERR_INVALID_ARG;
   if (s->estimator == SPD_ESTIMATOR_MVAR && s->mode != SPD_SELECT_COVERAGE) return SPD_ERR_INVALID_ARG;
+  // the LiteTopK gate serves the top-K rule with the bound estimator over 16-token pages
+  if (s->topk_state && (s->mode != SPD_SELECT_TOPK || s->estimator != SPD_ESTIMATOR_BOUND)) return SPD_ERR_INVALID_ARG;
+  if (s->topk_state && d->page_size != SPD_PAGE_SIZE) return SPD_ERR_UNSUPPORTED;
   return SPD_OK;
+}
+
+// The LiteTopK gate state of `rows` rows in the caller's buffer (layout in spd.h).
+constexpr size_t kGateRowBytes = sizeof(spd::TopkGateRow);
+static_assert(kGateRowBytes == 32, "the gate header is 32 bytes");
+size_t gate_state_bytes(int64_t rows) { return (size_t)rows * kGateRowBytes; }
+spd::TopkGate gate_of(const spd_select_params* s, int64_t) {
+  spd::TopkGate g{};
+  g.rows = static_cast<spd::TopkGateRow*>(s->topk_state);
+  return g;
 }
 
 // Tail mode: a known value; a rebuild needs the K pool (and its scales for fp8); skipping the
@@ -228,6 +241,7 @@ spd::SelectArgs select_args(const spd_desc* d, const spd_select_params* s, const
   a.n_local_stream = s->n_local_stream;
   a.lgs = lgs_of(d);
   a.num_tokens = 1;
+  a.gate = gate_of(s, (int64_t)d->batch * d->num_kv_heads);
   return a;
 }
 
@@ -275,6 +289,8 @@ int build_summaries(const spd_desc* desc, const void* k_pool, const uint16_t* k_
 extern "C" {
 
 int spd_abi_version(void) { return SPD_ABI_VERSION; }
+
+size_t spd_topk_state_bytes(int32_t rows) { return rows < 0 ? (size_t)-1 : gate_state_bytes(rows); }
 
 const char* spd_error_string(int status) {
   switch (status) {
@@ -427,6 +443,7 @@ int spd_page_list_refresh(const spd_desc* desc, const spd_select_params* sel, co
   if (!seq_lens || !page_list || !list_len || !block_table) return SPD_ERR_INVALID_ARG;
   if (page_meta && (!k_pool || (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale))) return SPD_ERR_INVALID_ARG;
   spd::SelectArgs a = select_args(desc, sel, seq_lens, block_table, page_list, page_phys, list_len, nullptr, mask);
+  a.gate = spd::TopkGate{};  // the refresh selects nothing
   if (page_meta && !is_mvar(sel)) a.tail = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
   if ((rc = launched(spd::launch_page_list_refresh(a, (hipStream_t)stream)))) return rc;
   if (page_meta && is_mvar(sel))
@@ -444,7 +461,7 @@ int spd_page_score_select(const spd_desc* desc, const spd_select_params* sel, co
   if ((rc = check_sel(desc, sel))) return rc;
   if ((rc = check_list_capacity(desc, sel))) return rc;
   FusedWs w;
-  if (is_mvar(sel) || is_hier(desc) || !fused_ws(desc, sel, w)) return SPD_ERR_UNSUPPORTED;
+  if (is_mvar(sel) || is_hier(desc) || !fused_ws(desc, sel, w) || sel->topk_state) return SPD_ERR_UNSUPPORTED;
   spd::HeadList dyn, strm;
   uint64_t mask;
   if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
@@ -667,6 +684,7 @@ int spd_page_select_mq(const spd_desc* desc, int32_t num_tokens, int32_t token_m
   spd::SelectArgs a = select_args(&tok, sel, seq_lens, block_table, token_list, token_phys, token_len, nullptr, mask);
   a.scores = scores;
   a.num_tokens = num_tokens;
+  a.gate = gate_of(sel, (int64_t)desc->batch * num_tokens * desc->num_kv_heads);  // rows of the token rows
   return launched(spd::launch_page_select(a, (hipStream_t)stream));
 }
 

@@ -65,6 +65,22 @@ struct HeadList {
   }
 };
 
+// LiteTopK gate state of top-K rows (LiteTopK, section 3.2 "Sampling" and "Top-k Selection", section 3.3
+// "Predictive Gating"): per (token row, KV head) a gate predicted from the row's previous selection.  The
+// selector ranks only the free pages scoring at or above it when they hold the top K'.
+struct TopkGateRow {
+  float lo;        // gate: free pages scoring >= lo are candidates
+  float top;       // largest free score of the previous selection (range of the sample)
+  uint32_t valid;  // nonzero once a selection has predicted a gate
+  uint32_t path;   // how the last selection ran: 1 from the candidates, 0 over the whole row
+  uint32_t seen;   // candidates (free pages at or above the gate) the last selection counted
+  uint32_t pad[3];
+};
+constexpr int kGateCap = 2048;  // candidates the selector ranks; more send it to the whole row
+struct TopkGate {
+  TopkGateRow* rows;  // [B * T * Hkv]; null: no gate
+};
+
 struct ScoreArgs {
   const void* q;
   const void* meta;
@@ -108,6 +124,8 @@ struct SelectArgs {
   int lgs;                  // log2 of logical pages per physical page: rows, lists and budget count physical pages
   int num_tokens;           // query tokens per request (>= 1): rows are (b T + t, h); token t of request b sees
                             // seq_lens[b] - T + 1 + t keys and request b's block-table row
+  TopkGate gate;            // top-K: select from the scorer's gated candidates when they hold the top K'
+                            // pages, then predict the next gate (rows.null: no gate)
   MetaArgs tail;            // tail.meta set: also rebuild each request's last logical page, all KV heads
 };
 int launch_page_select(const SelectArgs& a, hipStream_t stream);

@@ -109,6 +109,17 @@ def build_meta(w: Workload, d: DeviceInputs, stream=None) -> None:
 TAILS = ("auto", "none", "select", "side", "serial", "rebuild")
 
 
+def gate_state(rows: int, device) -> torch.Tensor:
+    """A zeroed LiteTopK gate state for `rows` (token) rows (spd_select_params.topk_state)."""
+    return torch.zeros(A.spd_topk_state_bytes(rows), dtype=torch.uint8, device=device)
+
+
+def gate_paths(state: torch.Tensor, rows: int) -> np.ndarray:
+    """How each row's last selection ran (1: from the gated candidates, 0: whole row) and the candidates it saw."""
+    hdr = state[:rows * A.GATE_ROW_BYTES].view(torch.int32).view(rows, 8).cpu().numpy()
+    return hdr[:, 3:5]
+
+
 class DecodeStep:
     """Buffers for one decode step of workload ``w`` over device inputs ``d``.
 
@@ -142,7 +153,7 @@ class DecodeStep:
 
     def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, fused: bool = False,
                  tail: str = "auto", phys_lists: bool = True, keep_sel_scores: bool = False, reuse: int = 1,
-                 merged: bool = False):
+                 merged: bool = False, gated: bool | None = None):
         if tail not in TAILS:
             raise ValueError(f"tail must be one of {TAILS}")
         skippable = w.mode == "topk" and w.n_local >= 1
@@ -171,6 +182,14 @@ class DecodeStep:
         self.sel = make_select(w)
         self.pp = self.plan.params()
         B, Hq, Hkv, D = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+        # LiteTopK gate (top-K, bound estimator, 16-token pages, separate scorer and selector)
+        gate_ok = w.mode == "topk" and w.estimator == "bound" and w.page_size == 16 and not fused
+        self.gated = gate_ok if gated is None else bool(gated)
+        if self.gated and not gate_ok:
+            raise ValueError("the LiteTopK gate needs top-K, the bound estimator, 16-token pages and fused=False")
+        self.topk_state = gate_state(B * Hkv, d.q.device) if self.gated else None
+        if self.gated:
+            self.sel.topk_state = self.topk_state.data_ptr()
         f32 = dict(dtype=torch.float32, device=dev)
         i32 = dict(dtype=torch.int32, device=dev)
         self.scores = torch.zeros((B, Hkv, w.pages_per_seq), **f32)
@@ -300,7 +319,7 @@ class MQDecodeStep:
     [B, T, Hq, d]; ``out`` is [B, T, Hq, d] and ``out_lse`` [B, T, Hq].
     """
 
-    def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None):
+    def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, gated: bool = True):
         T = w.num_queries
         if T < 2 or w.mode != "topk" or w.page_size != 16:
             raise ValueError("several query tokens: top-K over 16-token pages, T >= 2")
@@ -315,6 +334,11 @@ class MQDecodeStep:
         self.union_cap = min(T * self.token_cap, w.pages_per_seq)
         self.desc = make_desc(w, d.num_pool_pages, self.union_cap)                 # the B requests
         self.sel = make_select(w)
+        # LiteTopK gate of the B * T token rows, each predicted from that row's previous selection
+        self.gated = gated
+        self.topk_state = gate_state(B * T * Hkv, dev) if gated else None
+        if gated:
+            self.sel.topk_state = self.topk_state.data_ptr()
         # the B * T token rows (row b T + t) share their request's block-table row and length; the
         # library derives each token's causal length from d.seq_lens on every call
         self.scores = torch.zeros((B * T, Hkv, w.pages_per_seq), **f32)
