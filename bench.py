@@ -449,6 +449,31 @@ def main():
         timed(fn, R, R)
         phase_us[name] = timed(fn, reps, R) / reps * 1e6
 
+    # LiteTopK's predicted gate (top-K with the bound estimator): how the last timed selection ran, and the
+    # same step and selection with the gate off.  Each layer repeats its own query, so every gate is the
+    # one its previous call predicted for the same scores: the served share is the best case, and a step
+    # whose gates all miss costs about the ungated step plus one count over the loaded keys.
+    gate = None
+    if probe.gated:
+        rows = w.batch * w.num_kv_heads
+        gp = S.gate_paths(probe.topk_state, rows)
+        dyn = [b * w.num_kv_heads + h for b in range(w.batch) for h in range(w.num_kv_heads) if not inp.head_kind[h]]
+        ung = {id(a): S.DecodeStep(w, d, plan=plan, merged=args.merged, gated=False) for a, d in zip(steps, layers)}
+        for st in ung.values():
+            st.run()
+        reps = max(R, args.steps // 4)
+        ug = {}
+        for name, fn in (("step_us", lambda st, s: ung[id(st)].run(s)),
+                         ("select_only_us", lambda st, s: ung[id(st)].select_only(s))):
+            timed(fn, R, R)
+            ug[name] = round(timed(fn, reps, R) / reps * 1e6, 3)
+        served = gp[dyn, 0]
+        gate = {"rows_from_candidates": int(served.sum()), "dynamic_rows": len(dyn),
+                "candidates_median": int(np.median(gp[dyn, 1][served == 1])) if served.any() else None,
+                "ungated": ug, "query": "repeated per layer (the gate predicted from the same scores)"}
+        del ung
+        torch.cuda.synchronize()
+
     list_len = steps[0].list_len.cpu().numpy()
     ab = algorithmic_bytes(w, list_len, inp.head_kind)
     tbs = ab["total"] / step_s / 1e12
@@ -539,7 +564,7 @@ def main():
         "bytes_per_step": ab, "frac_of_peak": round(tbs / PEAK_HBM_TBS, 4),
         "beta_copy_TBs": round(beta, 3), "frac_of_beta": round(tbs / beta, 4),
         "phase_us": {k: round(v, 3) for k, v in phase_us.items()},
-        "selection_overhead": sel_over, "reuse": reuse,
+        "selection_overhead": sel_over, "gate": gate, "reuse": reuse,
         "list_len": {"min": int(list_len.min()), "median": int(np.median(list_len)), "max": int(list_len.max())},
         "roofline": roofline, "cpu_baseline": cpu, "cpu_baseline_all_cores": cpu_all,
         "decode_traffic": None if dec_rec is None else {
@@ -628,6 +653,22 @@ def bench_mq(args, w, inp, base, plan, gen_s):
     for name, fn in phases.items():
         timed(fn, R)
         phase_us[name] = timed(fn, max(R, args.steps // 4)) * 1e6
+    gate = None
+    if probe.gated:  # the same step with the token rows' gates off (each layer repeats its queries)
+        rows = w.batch * T * w.num_kv_heads
+        gp = S.gate_paths(probe.topk_state, rows)
+        ung = {id(a): S.MQDecodeStep(w, x, plan=plan, gated=False) for a, x in zip(steps, layers)}
+        for st in ung.values():
+            st.run()
+        ug = {}
+        for name, fn in (("step_us", lambda st, s: ung[id(st)].run(s)),
+                         ("select_only_us", lambda st, s: ung[id(st)].select_only(s))):
+            timed(fn, R)
+            ug[name] = round(timed(fn, max(R, args.steps // 4)) * 1e6, 3)
+        gate = {"token_rows_from_candidates": int(gp[:, 0].sum()), "token_rows": rows, "ungated": ug,
+                "query": "repeated per layer (the gate predicted from the same scores)"}
+        del ung
+        torch.cuda.synchronize()
     beta = copy_bandwidth(stream)
     cpu = None
     if not args.no_cpu:
@@ -665,6 +706,7 @@ def bench_mq(args, w, inp, base, plan, gen_s):
         "bytes_per_step": ab, "kv_bytes_without_union": per_token_kv, "frac_of_peak": round(ab["total"] / step_s / 1e12 / PEAK_HBM_TBS, 4),
         "beta_copy_TBs": round(beta, 3), "phase_us": {k: round(v, 3) for k, v in phase_us.items()},
         "union_len": {"min": int(union_len.min()), "median": int(np.median(union_len)), "max": int(union_len.max())},
+        "gate": gate,
         "roofline": {"bound": "hbm", "kernel": "mq_page_score_kernel (T token rows per scan)",
                      "achieved": round(sc_bytes / (phase_us["score"] * 1e-6) / 1e9, 1), "peak": PEAK_HBM_TBS * 1000,
                      "unit": "GB/s", "frac": round(sc_bytes / (phase_us["score"] * 1e-6) / 1e9 / (PEAK_HBM_TBS * 1000), 4),

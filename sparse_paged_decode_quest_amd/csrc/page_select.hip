@@ -11,26 +11,40 @@
 namespace spd {
 
 // Keys (and physical pages, when the list of physical pages is wanted) of the row's pages in
-// the slot layout of select_row_keys.  `sc` holds top-K scores or coverage shares.  The loads cover
-// the whole row stride (max_pages) so they are issued before the request's length arrives; slots
-// at or past the row's n pages are then cleared.
+// the slot layout of select_row_keys.  `sc` holds top-K scores or coverage shares.  The row's length
+// (len_src[0] - len_off, at least 0), its scores over the whole row stride (max_pages: they need no
+// length) and its LiteTopK gate (gate_src, nullable) are requested together and waited for once; then
+// slots at or past the row's n pages are cleared (coverage), or every slot that is not a free page
+// (top-K: the sinks of n_sink and the window of n_local are taken without their keys).  A row with a
+// valid gate leaves the physical pages of its slots to the selection (phys_later): the gated cut
+// requests only its candidates'.
 template <int NW, int KPL, bool COV>
-__device__ __forceinline__ void load_row_keys(const float* sc, const int32_t* len_ptr, int max_pages, int lgs,
-                                              uint32_t (&key)[KPL], SlotPhys<KPL>& phys, int& n) {
+__device__ __forceinline__ void load_row_keys(const float* sc, const int32_t* len_src, int len_off, int max_pages,
+                                              int lgs, int n_sink, int n_local, const TopkGateRow* gate_src,
+                                              TopkGateRow& gr, uint32_t (&key)[KPL], SlotPhys<KPL>& phys, int& n,
+                                              bool& phys_later) {
   const int wbase = (int)(threadIdx.x / kWave) * kWave * KPL + (int)(threadIdx.x % kWave);
+  const int raw_len = *len_src;
+  // the gate's threshold and validity, read without a branch (no gate: both read 0)
+  const __amdgpu_buffer_rsrc_t gate_r = make_rsrc(gate_src, gate_src ? (uint32_t)sizeof(TopkGateRow) : 0u);
+  gr.lo = buf_load_f32(gate_r, (uint32_t)offsetof(TopkGateRow, lo));
+  gr.valid = (uint32_t)buf_load_i32(gate_r, (uint32_t)offsetof(TopkGateRow, valid));
   const __amdgpu_buffer_rsrc_t sc_r = make_rsrc(sc, (uint32_t)max_pages * 4u);  // slots past the row read 0
   float v[KPL];
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    const int p = wbase + i * kWave;
-    v[i] = buf_load_f32(sc_r, (uint32_t)p * 4u);
-    phys.load(i, p, max_pages);
+  for (int i = 0; i < KPL; ++i) v[i] = buf_load_f32(sc_r, (uint32_t)(wbase + i * kWave) * 4u);
+  n = row_phys_pages(max(raw_len - len_off, 0), max_pages, lgs);
+  phys_later = !COV && KPL <= 32 && gate_src && gr.valid;
+  if (!phys_later) {
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) phys.load(i, wbase + i * kWave, max_pages);
   }
-  n = row_phys_pages(*len_ptr, max_pages, lgs);
+  const RowShape r = row_shape(n, n_sink, n_local);
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int p = wbase + i * kWave;
-    key[i] = p < n ? (COV ? coverage_key(v[i]) : score_key(v[i])) : 0u;
+    if constexpr (COV) key[i] = p < n ? coverage_key(v[i]) : 0u;
+    else key[i] = (unsigned)(p - r.sink_end) < (unsigned)(r.local_begin - r.sink_end) ? score_key(v[i]) : 0u;
   }
 }
 
@@ -74,29 +88,21 @@ __global__ __launch_bounds__(NW * kWave) void page_select_kernel(SelectArgs a) {
     select_streaming_row(a, row_phys_pages(token_row_length(a, token_row, b_), a.max_pages, a.lgs), row, bt_row);
     return;
   }
-  // LiteTopK gate of the row (requested with the scores)
   TopkGateRow gr{};
-  if constexpr (!COV) {
-    if (a.gate.rows) gr = a.gate.rows[row];
-  }
   uint32_t key[KPL];
   SlotPhys<KPL> phys;
   phys.bt_row = bt_row;
   // token t of request b sees seq_lens[b] - (T - 1 - t) keys (T = 1: the request's length)
-  const int len_off = T - 1 - token_row % T;
   int n;
-  if (len_off == 0) {
-    load_row_keys<NW, KPL, COV>(a.scores + row * a.max_pages, a.seq_lens + b, a.max_pages, a.lgs, key, phys, n);
-  } else {
-    int b_;
-    const int len = token_row_length(a, token_row, b_);
-    load_row_keys<NW, KPL, COV>(a.scores + row * a.max_pages, &len, a.max_pages, a.lgs, key, phys, n);
-  }
+  bool phys_later;
+  load_row_keys<NW, KPL, COV>(a.scores + row * a.max_pages, a.seq_lens + b, T - 1 - token_row % T, a.max_pages, a.lgs,
+                              a.n_sink, a.n_local, COV ? nullptr : a.gate.rows ? a.gate.rows + row : nullptr, gr, key,
+                              phys, n, phys_later);
   if constexpr (COV) {
     select_row_keys<NW, KPL, COV>(a, key, phys, row_shape(n, a.n_sink, a.n_local), row, sm);
   } else {
     __shared__ GateSmem gs;
-    select_row_keys<NW, KPL, COV>(a, key, phys, row_shape(n, a.n_sink, a.n_local), row, sm, &gr, &gs);
+    select_row_keys<NW, KPL, COV>(a, key, phys, row_shape(n, a.n_sink, a.n_local), row, sm, &gr, &gs, phys_later);
   }
 }
 

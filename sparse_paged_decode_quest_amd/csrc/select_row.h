@@ -70,7 +70,6 @@ struct SelectSmem {
 struct GateSmem {
   uint32_t key[kGateCap];
   int32_t page[kGateCap];
-  int32_t phys[kGateCap];
 };
 
 __device__ __forceinline__ unsigned long long share_fx(float pi) {
@@ -140,48 +139,57 @@ __device__ __forceinline__ void gate_store(const TopkGate& g, size_t row, int de
 // pages, page_of gives the page order of a slot (ties are taken in that order); n_free / n_forced count them.
 // Top-K also returns top_key, the largest free key, and gate_key, the lower edge of the first digit's group
 // where 1.5 K' free keys are reached (0 when there are fewer, or no walk ran): the next call's predicted gate.
-// Every thread of the workgroup must call this.
-template <int NW, int KPL, bool COV, typename SM, typename FreeAt, typename ForcedAt, typename PageOf>
+// BITS is the digit width.  With PRE (top-K only) the caller has found the range -- pre_mn at or below every
+// free key, pre_mx the largest -- and has cleared the first two histogram buffers and the candidate count
+// before a barrier; the cut then starts with the first digit.  Every thread of the workgroup must call this.
+template <int NW, int KPL, bool COV, int BITS, bool PRE, typename SM, typename FreeAt, typename ForcedAt,
+          typename PageOf>
 __device__ __forceinline__ void row_cut(const SelectArgs& a, const uint32_t (&key)[KPL], FreeAt free_at,
                                         ForcedAt forced_at, PageOf page_of, const int n_free, const int n_forced,
                                         SM& sm, int& dec, uint32_t& kc, int& need_eq, uint32_t& gate_key,
-                                        uint32_t& top_key) {
+                                        uint32_t& top_key, uint32_t pre_mn = 0u, uint32_t pre_mx = 0u) {
   using H = typename SM::H;
   constexpr int STRIDE = NW * kWave;
-  constexpr int PER = SelectDigit<COV>::kBins / kWave;  // histogram bins summed by one lane
-  constexpr int kBits = SelectDigit<COV>::kBits;
-  constexpr int kBins = SelectDigit<COV>::kBins;
+  constexpr int kBits = BITS;
+  constexpr int kBins = 1 << BITS;
+  constexpr int PER = kBins / kWave;  // histogram bins summed by one lane
+  static_assert(kBins <= SelectDigit<COV>::kBins && PER >= 1, "digit width out of range");
+  static_assert(!(PRE && COV), "a given range is a top-K cut");
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   auto mass_of = [&](uint32_t k) { return share_fx(__uint_as_float(k)); };
-  // ---- range of the free keys, forced mass (coverage); clear two histogram buffers
-  uint32_t mn = 0xffffffffu, mx = 0u;
+  uint32_t mn = pre_mn, mx = pre_mx;
   unsigned long long fmass = 0;
+  if constexpr (!PRE) {
+    // ---- range of the free keys, forced mass (coverage); clear two histogram buffers
+    mn = 0xffffffffu;
+    mx = 0u;
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    if (free_at(i)) {
-      mn = min(mn, key[i]);
-      mx = max(mx, key[i]);
-    } else if (COV && forced_at(i)) {
-      fmass += mass_of(key[i]);
+    for (int i = 0; i < KPL; ++i) {
+      if (free_at(i)) {
+        mn = min(mn, key[i]);
+        mx = max(mx, key[i]);
+      } else if (COV && forced_at(i)) {
+        fmass += mass_of(key[i]);
+      }
     }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (COV) fmass = wave_sum(fmass);
+    if (lane == 0) {
+      sm.wmin[wave] = mn;
+      sm.wmax[wave] = mx;
+      sm.wsum[wave] = fmass;
+    }
+    for (int e = threadIdx.x; e < 2 * SelectDigit<COV>::kBins; e += STRIDE) (&sm.hist[0][0])[e] = 0;
+    if (threadIdx.x == 0) sm.cand_count = 0;
+    __syncthreads();
+    // lane w < NW reads wave w's entries; DPP reductions give every lane the workgroup's values
+    mn = wave_min(lane < NW ? sm.wmin[lane] : 0xffffffffu);
+    mx = wave_max(lane < NW ? sm.wmax[lane] : 0u);
+    if (COV) fmass = wave_sum(lane < NW ? sm.wsum[lane] : 0ull);
   }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
-  if (COV) fmass = wave_sum(fmass);
-  if (lane == 0) {
-    sm.wmin[wave] = mn;
-    sm.wmax[wave] = mx;
-    sm.wsum[wave] = fmass;
-  }
-  for (int e = threadIdx.x; e < 2 * kBins; e += STRIDE) (&sm.hist[0][0])[e] = 0;
-  if (threadIdx.x == 0) sm.cand_count = 0;
-  __syncthreads();
-  // lane w < NW reads wave w's entries; DPP reductions give every lane the workgroup's values
-  mn = wave_min(lane < NW ? sm.wmin[lane] : 0xffffffffu);
-  mx = wave_max(lane < NW ? sm.wmax[lane] : 0u);
   top_key = mx;
   gate_key = 0u;
-  if (COV) fmass = wave_sum(lane < NW ? sm.wsum[lane] : 0ull);
 
   // ---- decision: 0 = forced pages only, 1 = every page, 2 = cut at key kc: keys above kc are
   // kept, keys equal to kc are kept in page order while fewer than need_eq of them were taken.
@@ -337,67 +345,107 @@ __device__ __forceinline__ void row_cut(const SelectArgs& a, const uint32_t (&ke
 // The gated top-K path (LiteTopK, section 3.2 "Sampling" and "Top-k Selection"; section 3.3 "Predictive
 // Gating").  The row's gate was predicted from its previous selection.  The free pages scoring at or above
 // it are the candidates; when they number at least K' they hold the top K' free pages and every page tied
-// with the K'-th, so the row's cut is the cut among the candidates.  They are gathered in page order (the
-// slot layout is page order: wave, slot, lane) with one ballot per slot, cut by the radix walk over their
-// scores' bit patterns (section 3.2, "Extension to Decoding"), and written between the row's sink and local
-// pages; the next gate is stored.  Returns false, with nothing written or stored, when the gate is absent
-// or the candidates number fewer than K' or more than kGateCap: the caller then cuts the whole row.
-// `seen` receives the candidate count (0 without a gate).  Every thread of the workgroup must call this.
+// with the K'-th, so the row's cut is the cut among the candidates.
+//
+// The keys arrive with every slot that is not a free page set to 0 (below every gate).  One pass over them
+// finds the free keys' range and counts the candidates (one compare and a ballot per slot, summed on the
+// scalar unit), beside the clearing of the histograms: one barrier.  With between K' and kGateCap
+// candidates, they are gathered in page order (the slot layout is page order: wave, slot, lane) -- a slot
+// with no candidate in the wave costs its compare and one uniform branch -- and cut by the radix walk over
+// their bit patterns (section 3.2, "Extension to Decoding"), starting from the range the gate and the
+// largest key span; each candidate's physical page is requested as soon as it is gathered, and the forced
+// pages' before the first barrier.  The list is written between the sink and local pages and the next
+// gate is stored.
+//
+// Returns 1 when the row was selected; 0 when the candidates number fewer than K' or more than kGateCap:
+// nothing was written, and pre_mn / pre_mx hold the free keys' range for the whole-row cut (histograms
+// cleared, past a barrier); -1 when the gate is absent or there is nothing to rank (nothing done).  `seen`
+// receives the candidate count.  Every thread of the workgroup must call this.
 template <int NW, int KPL>
-__device__ __forceinline__ bool select_row_gated(const SelectArgs& a, const uint32_t (&key)[KPL],
-                                                 const SlotPhys<KPL>& phys, const RowShape r, const size_t row,
-                                                 const TopkGateRow& gr, SelectSmem<NW, KPL, false>& sm, GateSmem& gs,
-                                                 uint32_t& seen) {
-  constexpr int CS = kGateCap / (NW * kWave);  // candidate slots per lane in the cut
+__device__ __forceinline__ int select_row_gated(const SelectArgs& a, const uint32_t (&key)[KPL],
+                                                const SlotPhys<KPL>& phys, const RowShape r, const size_t row,
+                                                const TopkGateRow& gr, SelectSmem<NW, KPL, false>& sm, GateSmem& gs,
+                                                uint32_t& seen, uint32_t& pre_mn, uint32_t& pre_mx) {
+  constexpr int STRIDE = NW * kWave;
+  constexpr int CS = kGateCap / STRIDE;  // candidate slots per lane in the cut
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int n_free = r.local_begin - r.sink_end;
   const int n_forced = r.n - n_free;
   const int kp = a.budget - n_forced;
   seen = 0u;
-  if (!gr.valid || kp <= 0 || n_free <= kp) return false;  // uniform: nothing to rank, or no prediction
+  if (!gr.valid || kp <= 0 || n_free <= kp) return -1;  // uniform: nothing to rank, or no prediction
   const int wbase = wave * kWave * KPL + lane;
   auto page_of = [&](int i) { return wbase + i * kWave; };
-  const uint32_t gate_key = score_key(gr.lo);
-  auto cand = [&](int i) { return (unsigned)(page_of(i) - r.sink_end) < (unsigned)n_free && key[i] >= gate_key; };
-  uint32_t c = 0;
+  const uint32_t gate_key = max(score_key(gr.lo), 1u);  // above 0: the cleared slots are never candidates
+  const __amdgpu_buffer_rsrc_t bt_r = make_rsrc(phys.bt_row, phys.bt_row ? (uint32_t)r.n * 4u : 0u);
+  // forced page threadIdx.x (sinks, then locals): its physical page, requested now, written last
+  const int n_local_pages = r.n - r.local_begin;
+  const int n_fixed = r.sink_end + n_local_pages;
+  const int t = (int)threadIdx.x;
+  const int fpg = t < r.sink_end ? t : r.local_begin + (t - r.sink_end);
+  const int32_t fph = buf_load_i32(bt_r, (uint32_t)(t < n_fixed ? fpg : 0) * 4u);
+  // ---- range, candidate count; clear the first two histogram buffers
+  uint32_t mn = 0xffffffffu, mx = 0u, c = 0u;
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) c += cand(i) ? 1u : 0u;
-  const uint32_t cw = wave_sum(c);
-  if (lane == 0) sm.wsure[wave] = cw;
+  for (int i = 0; i < KPL; ++i) {
+    mx = max(mx, key[i]);
+    mn = min(mn, key[i] ? key[i] : 0xffffffffu);
+    c += (uint32_t)__popcll(__ballot(key[i] >= gate_key));  // wave-uniform
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (lane == 0) {
+    sm.wmin[wave] = mn;
+    sm.wmax[wave] = mx;
+    sm.wsure[wave] = c;
+  }
+  for (int e = threadIdx.x; e < 2 * SelectDigit<false>::kBins; e += STRIDE) (&sm.hist[0][0])[e] = 0;
+  if (threadIdx.x == 0) sm.cand_count = 0;
   __syncthreads();
+  mn = wave_min(lane < NW ? sm.wmin[lane] : 0xffffffffu);
+  mx = wave_max(lane < NW ? sm.wmax[lane] : 0u);
   const uint32_t wl = lane < NW ? sm.wsure[lane] : 0u;
   const uint32_t wincl = wave_incl_scan(wl);
   const uint32_t count = lane_u32(wincl, NW - 1);
   seen = count;
-  if (count < (uint32_t)kp || count > (uint32_t)kGateCap) return false;  // uniform
-  // gather in page order
+  pre_mn = mn;
+  pre_mx = mx;
+  if (count < (uint32_t)kp || count > (uint32_t)kGateCap) return 0;  // uniform
+  // ---- gather in page order
   uint32_t pos = lane_u32(wincl - wl, wave);
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
-    const bool ci = cand(i);
+    const bool ci = key[i] >= gate_key;
     const unsigned long long m = __ballot(ci);
-    if (ci) {
-      const uint32_t q = pos + lanes_below(m);
-      gs.key[q] = key[i];
-      gs.page[q] = page_of(i);
-      if constexpr (SlotPhys<KPL>::kInRegs) gs.phys[q] = phys.v[i];
+    if (m) {
+      if (ci) {
+        const uint32_t q = pos + lanes_below(m);
+        gs.key[q] = key[i];
+        gs.page[q] = page_of(i);
+      }
+      pos += (uint32_t)__popcll(m);
     }
-    pos += (uint32_t)__popcll(m);
   }
   __syncthreads();
   // the cut among the candidates: slot i of a lane holds candidate wave * 64 CS + 64 i + lane (page order)
   const int cbase = wave * kWave * CS + lane;
   uint32_t ck[CS];
+  int32_t cpg[CS], cph[CS];
 #pragma unroll
-  for (int i = 0; i < CS; ++i) ck[i] = cbase + i * kWave < (int)count ? gs.key[cbase + i * kWave] : 0u;
+  for (int i = 0; i < CS; ++i) {
+    const bool in = cbase + i * kWave < (int)count;
+    ck[i] = in ? gs.key[cbase + i * kWave] : 0u;
+    cpg[i] = in ? gs.page[cbase + i * kWave] : 0;
+    cph[i] = buf_load_i32(bt_r, (uint32_t)cpg[i] * 4u);
+  }
   auto order_of = [&](int i) { return cbase + i * kWave; };
   auto free_c = [&](int i) { return order_of(i) < (int)count; };
   auto forced_c = [&](int) { return false; };
   int dec;
   uint32_t kc, next_key, top_key;
   int need_eq;
-  row_cut<NW, CS, false>(a, ck, free_c, forced_c, order_of, (int)count, n_forced, sm, dec, kc, need_eq, next_key,
-                         top_key);
+  row_cut<NW, CS, false, SelectDigit<false>::kBits, true>(a, ck, free_c, forced_c, order_of, (int)count, n_forced, sm,
+                                                         dec, kc, need_eq, next_key, top_key, gate_key, mx);
   if (dec == 1) {  // exactly K' candidates: all taken
     kc = 0u;
     need_eq = kNoLimit;
@@ -434,23 +482,22 @@ __device__ __forceinline__ bool select_row_gated(const SelectArgs& a, const uint
     const unsigned long long take_mask = __ballot(take);
     const uint32_t q = q0 + lanes_below(take_mask);
     if (take && q < (uint32_t)a.max_list) {
-      const int pg = gs.page[order_of(i)];
-      out[q] = pg;
-      if (out_phys) out_phys[q] = SlotPhys<KPL>::kInRegs ? gs.phys[order_of(i)] : phys.bt_row[pg];
+      out[q] = cpg[i];
+      if (out_phys) out_phys[q] = cph[i];
       if (out_sc) out_sc[q] = key_to_score(ck[i]);
     }
     q0 += (uint32_t)__popcll(take_mask);
     eq_left -= __popcll(eq_mask);
   }
-  // the forced pages: sinks first, locals last (every free page lies between them)
-  const int n_local_pages = r.n - r.local_begin;
-  for (int i = threadIdx.x; i < r.sink_end + n_local_pages; i += NW * kWave) {
+  // the forced pages: sinks first, locals last (every free page lies between them); the first round's
+  // physical pages were requested at the start
+  for (int i = t; i < n_fixed; i += STRIDE) {
     const bool sink = i < r.sink_end;
     const int pg = sink ? i : r.local_begin + (i - r.sink_end);
     const uint32_t q = sink ? (uint32_t)i : (uint32_t)r.sink_end + chosen + (uint32_t)(i - r.sink_end);
     if (q < (uint32_t)a.max_list) {
       out[q] = pg;
-      if (out_phys) out_phys[q] = phys.bt_row[pg];
+      if (out_phys) out_phys[q] = i == t ? fph : phys.bt_row[pg];
       if (out_sc) out_sc[q] = a.scores[row * a.max_pages + pg];
     }
   }
@@ -458,24 +505,33 @@ __device__ __forceinline__ bool select_row_gated(const SelectArgs& a, const uint
     a.list_len[row] = (int)min((uint32_t)r.sink_end + chosen + (uint32_t)n_local_pages, (uint32_t)a.max_list);
     gate_store(a.gate, row, 2, next_key, top_key, gr.lo, 1u, count);  // fewer than 1.5 K' candidates: keep the gate
   }
-  return true;
+  return 1;
 }
 
 // Select the pages of one dynamic row from its keys (top-K: score_key of the scores;
 // coverage: coverage_key of the shares).  phys gives the physical page of each slot (written
-// to a.page_phys when that is set).  Top-K rows with a gate state also get the next call's predicted
-// gate.  Every thread of the workgroup must call this.
+// to a.page_phys when that is set); with phys_later its registers are requested here, once the gated
+// candidates have not served the row.  Top-K rows with a gate state (gr, gs) also get the next call's
+// predicted gate; their keys must be 0 in every slot that is not a free page.  Every thread of the
+// workgroup must call this.
 template <int NW, int KPL, bool COV>
 __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint32_t (&key)[KPL],
-                                                const SlotPhys<KPL>& phys, const RowShape r, const size_t row,
+                                                SlotPhys<KPL>& phys, const RowShape r, const size_t row,
                                                 SelectSmem<NW, KPL, COV>& sm, const TopkGateRow* gr = nullptr,
-                                                GateSmem* gs = nullptr) {
+                                                GateSmem* gs = nullptr, bool phys_later = false) {
   uint32_t seen = 0u;
+  int gated = -1;  // 1: selected from the candidates; 0: range found, cut the whole row; -1: no gate
+  uint32_t pre_mn = 0u, pre_mx = 0u;
   if constexpr (!COV && KPL <= 32) {  // (rows over 32,768 pages keep their registers for the whole-row cut)
     if (a.gate.rows && gr && gs) {
-      if (select_row_gated<NW, KPL>(a, key, phys, r, row, *gr, sm, *gs, seen)) return;
-      __syncthreads();  // the whole-row cut below reuses the shared counts
+      gated = select_row_gated<NW, KPL>(a, key, phys, r, row, *gr, sm, *gs, seen, pre_mn, pre_mx);
+      if (gated == 1) return;
     }
+  }
+  if (phys_later) {
+    const int wb = (int)(threadIdx.x / kWave) * kWave * KPL + (int)(threadIdx.x % kWave);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) phys.load(i, wb + i * kWave, a.max_pages);
   }
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int n_free = r.local_begin - r.sink_end;
@@ -487,7 +543,12 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
   int dec;
   uint32_t kc, gate_key, top_key;
   int need_eq;
-  row_cut<NW, KPL, COV>(a, key, free_at, forced_at, page_of, n_free, n_forced, sm, dec, kc, need_eq, gate_key, top_key);
+  if (!COV && gated == 0)  // uniform: the gated attempt found the range
+    row_cut<NW, KPL, false, SelectDigit<false>::kBits, true>(a, key, free_at, forced_at, page_of, n_free, n_forced,
+                                                             sm, dec, kc, need_eq, gate_key, top_key, pre_mn, pre_mx);
+  else
+    row_cut<NW, KPL, COV, SelectDigit<COV>::kBits, false>(a, key, free_at, forced_at, page_of, n_free, n_forced, sm,
+                                                          dec, kc, need_eq, gate_key, top_key);
   if (!COV && a.gate.rows && threadIdx.x == 0) gate_store(a.gate, row, dec, gate_key, top_key, -INFINITY, 0u, seen);
 
   // ---- compaction in ascending page order.  Decisions 0 and 1 become cuts that no free key
@@ -535,7 +596,8 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
     if (take && q < (uint32_t)a.max_list) {
       out[q] = page_of(i);
       if (SlotPhys<KPL>::kInRegs && out_phys) out_phys[q] = phys.at(i, page_of(i));
-      if (out_sc) out_sc[q] = COV ? __uint_as_float(key[i]) : key_to_score(key[i]);
+      // (a top-K slot with key 0 is a forced page of the separate selector: its score is read back below)
+      if (out_sc && (COV || key[i] != 0u)) out_sc[q] = COV ? __uint_as_float(key[i]) : key_to_score(key[i]);
     }
     pos += (uint32_t)__popcll(take_mask);
   };
@@ -567,6 +629,16 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       const uint32_t end = min(pos, (uint32_t)a.max_list);
       for (uint32_t q = pos0 + lane; q < end; q += kWave) out_phys[q] = phys.bt_row[out[q]];
+    }
+  }
+  if (!COV && out_sc && a.scores) {
+    // the forced pages' scores, read back (sinks lead the list, locals end it)
+    const int n_local_pages = r.n - r.local_begin;
+    for (int i = threadIdx.x; i < r.sink_end + n_local_pages; i += NW * kWave) {
+      const bool sink = i < r.sink_end;
+      const int pg = sink ? i : r.local_begin + (i - r.sink_end);
+      const uint32_t q = sink ? (uint32_t)i : total - (uint32_t)n_local_pages + (uint32_t)(i - r.sink_end);
+      if (q < (uint32_t)a.max_list) out_sc[q] = a.scores[row * a.max_pages + pg];
     }
   }
   if (threadIdx.x == 0) a.list_len[row] = (int)min(total, (uint32_t)a.max_list);
