@@ -275,6 +275,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--fused", action="store_true", help="scorer and selector in one launch")
     ap.add_argument("--merged", action="store_true", help="decode and merge in one launch (last-block merge)")
+    ap.add_argument("--no-gate", action="store_true", help="top-K selection without the LiteTopK gate")
     ap.add_argument("--plan", default=None,
                     help="self-planning constants C,N_J,N_T[,balanced] (default: the step's for the workload)")
     ap.add_argument("--phase-only", default=None,
@@ -321,7 +322,8 @@ def main():
         plan = S.Plan(*v[:3], balanced=bool(v[3]) if len(v) > 3 else False)
     if w.num_queries > 1:
         return bench_mq(args, w, inp, base, plan, gen_s)
-    probe = S.DecodeStep(w, base, plan=plan, fused=args.fused, merged=args.merged)
+    gated = False if args.no_gate else None
+    probe = S.DecodeStep(w, base, plan=plan, fused=args.fused, merged=args.merged, gated=gated)
     probe.run()
     torch.cuda.synchronize()
     ab0 = algorithmic_bytes(w, probe.list_len.cpu().numpy(), inp.head_kind)
@@ -337,7 +339,8 @@ def main():
                                       block_table=clone(base.block_table), seq_lens=clone(base.seq_lens),
                                       head_kind=base.head_kind.copy(), page_meta=clone(base.page_meta))
                        for _ in range(R - 1)]
-    steps = [probe] + [S.DecodeStep(w, d, plan=plan, fused=args.fused, merged=args.merged) for d in layers[1:]]
+    steps = [probe] + [S.DecodeStep(w, d, plan=plan, fused=args.fused, merged=args.merged, gated=gated)
+                       for d in layers[1:]]
     for st in steps:
         st.run()
     torch.cuda.synchronize()
@@ -493,7 +496,7 @@ def main():
                                         block_table=clone(d0.block_table), seq_lens=clone(d0.seq_lens),
                                         head_kind=d0.head_kind.copy(), page_meta=clone(d0.page_meta))
                          for _ in range(R - 1)]
-            st_s = [S.DecodeStep(ws, d, plan=plan, fused=args.fused, merged=args.merged) for d in ds]
+            st_s = [S.DecodeStep(ws, d, plan=plan, fused=args.fused, merged=args.merged, gated=gated) for d in ds]
             saved = steps[:]
             steps[:] = st_s  # `timed` replays the layers in `steps`
             timed(whole, R, R)
@@ -584,7 +587,7 @@ def bench_mq(args, w, inp, base, plan, gen_s):
     from sparse_paged_decode_quest_amd import step as S
 
     T = w.num_queries
-    probe = S.MQDecodeStep(w, base, plan=plan)
+    probe = S.MQDecodeStep(w, base, plan=plan, gated=not args.no_gate)
     probe.run()
     torch.cuda.synchronize()
     d = w.head_dim
@@ -616,7 +619,7 @@ def bench_mq(args, w, inp, base, plan, gen_s):
                                       block_table=base.block_table.clone(),
                                       seq_lens=base.seq_lens.clone(), head_kind=base.head_kind.copy(),
                                       page_meta=base.page_meta.clone()) for _ in range(R - 1)]
-    steps = [probe] + [S.MQDecodeStep(w, x, plan=plan) for x in layers[1:]]
+    steps = [probe] + [S.MQDecodeStep(w, x, plan=plan, gated=not args.no_gate) for x in layers[1:]]
     for st in steps:
         st.run()
     torch.cuda.synchronize()

@@ -23,8 +23,8 @@
 // found the crossing bin in it (three rotating histogram buffers let the next digit's
 // histogram start at once) -- 64 lane sums over skewed addresses (no LDS bank conflicts), a
 // scan, and a second scan inside the crossing lane's group of bins.  Top-K usually stops after
-// one digit: when at most kCandMax keys share the crossing bin, wave 0 ranks those candidates
-// directly.  Ties at the K'-th key are taken in page order.  Values every wave needs from the
+// one digit: when at most kCandMax keys share the crossing bin, wave 0 holds one each and counts
+// the keys above and equal to its own.  Ties at the K'-th key are taken in page order.  Values every wave needs from the
 // others (ranges, counts) are read one per lane and combined with DPP reductions and scans:
 // one LDS read per wave instead of one per wave entry, since sixteen waves reading the same
 // LDS words one by one were the bulk of the selection time.
@@ -53,8 +53,7 @@ struct SelectSmem {
   H hist[3][SelectDigit<COV>::kBins];
   unsigned long long wsum[NW];
   uint32_t wmin[NW], wmax[NW];
-  uint32_t cand_key[kCandMax];
-  int32_t cand_page[kCandMax];
+  alignas(16) uint32_t cand_key[kCandMax];
   uint32_t cand_count;
   uint32_t wsure[NW], weq[NW];  // per-wave counts of kept-for-sure keys and keys equal to the cut key
   struct {
@@ -62,7 +61,7 @@ struct SelectSmem {
     H above, inbin;  // count / mass above the bin and inside it
     uint32_t kc;     // top-K cut key found by ranking the crossing bin's keys
     int need_eq;     // keys equal to kc still to take
-    int gate_bin;    // top-K, first digit: lowest bin of the group where 1.5 K' keys are reached (-1: fewer)
+    int gate_bin;    // top-K, first digit: the bin where 1.5 K' keys are reached, from the top (-1: fewer)
   } cross;
 };
 
@@ -136,16 +135,15 @@ __device__ __forceinline__ void gate_store(const TopkGate& g, size_t row, int de
 // The cut of one row's keys: the decision dec (0: forced pages only, 1: every free page, 2: cut at key kc --
 // keys above kc are taken, keys equal to kc while fewer than need_eq were taken, in page order), found by the
 // radix walk described at the top of this file.  free_at / forced_at say which key slots are free or forced
-// pages, page_of gives the page order of a slot (ties are taken in that order); n_free / n_forced count them.
-// Top-K also returns top_key, the largest free key, and gate_key, the lower edge of the first digit's group
+// pages; n_free / n_forced count them.
+// Top-K also returns top_key, the largest free key, and gate_key, the lower edge of the first digit's bin
 // where 1.5 K' free keys are reached (0 when there are fewer, or no walk ran): the next call's predicted gate.
 // BITS is the digit width.  With PRE (top-K only) the caller has found the range -- pre_mn at or below every
 // free key, pre_mx the largest -- and has cleared the first two histogram buffers and the candidate count
 // before a barrier; the cut then starts with the first digit.  Every thread of the workgroup must call this.
-template <int NW, int KPL, bool COV, int BITS, bool PRE, typename SM, typename FreeAt, typename ForcedAt,
-          typename PageOf>
+template <int NW, int KPL, bool COV, int BITS, bool PRE, typename SM, typename FreeAt, typename ForcedAt>
 __device__ __forceinline__ void row_cut(const SelectArgs& a, const uint32_t (&key)[KPL], FreeAt free_at,
-                                        ForcedAt forced_at, PageOf page_of, const int n_free, const int n_forced,
+                                        ForcedAt forced_at, const int n_free, const int n_forced,
                                         SM& sm, int& dec, uint32_t& kc, int& need_eq, uint32_t& gate_key,
                                         uint32_t& top_key, uint32_t pre_mn = 0u, uint32_t pre_mx = 0u) {
   using H = typename SM::H;
@@ -243,12 +241,20 @@ __device__ __forceinline__ void row_cut(const SelectArgs& a, const uint32_t (&ke
           const H incl = wave_incl_scan(s);
           const H excl = incl - s;
           if constexpr (!COV) {
-            // the next call's gate (LiteTopK, section 3.3): the lowest bin of the group where the count from
-            // the top reaches 1.5 K' (the margin of a predicted filter)
+            // the next call's gate (LiteTopK, section 3.3): the bin where the count from the top reaches
+            // 1.5 K' (the margin of a predicted filter) -- its group first, then the bin inside it
             if (pass == 0) {
               const H need2 = need + need / 2;
               const unsigned long long hit2 = __ballot(excl < need2 && incl >= need2);
-              if (lane == 0) sm.cross.gate_bin = hit2 ? kBins - 1 - ((__ffsll((long long)hit2) - 1) * PER + PER - 1) : -1;
+              int gbin = -1;
+              if (hit2) {
+                const int g2 = __ffsll((long long)hit2) - 1;
+                const H v2 = lane < PER ? h[g2 * PER + lane] : (H)0;
+                const H incl3 = wave_incl_scan(v2) + lane_u32(excl, g2);
+                const unsigned long long hit3 = __ballot(lane < PER && incl3 - v2 < need2 && incl3 >= need2);
+                gbin = kBins - 1 - (g2 * PER + __ffsll((long long)hit3) - 1);
+              }
+              if (lane == 0) sm.cross.gate_bin = gbin;
             }
           }
           const unsigned long long hit = __ballot(excl < need && incl >= need);
@@ -294,8 +300,10 @@ __device__ __forceinline__ void row_cut(const SelectArgs& a, const uint32_t (&ke
           break;
         }
         if (!COV && inbin <= (H)kCandMax) {
-          // few keys left in the bin: gather them; wave 0 ranks them (one candidate per lane,
-          // compared against every other through lane reads) and publishes the cut
+          // few keys left in the bin: gather them (in any order); wave 0 holds one per lane, reads them all
+          // back from LDS four at a time and counts the keys above and equal to its own.  The cut key is the
+          // one with fewer than need keys above it and at least need at or above it; ties at the cut are
+          // settled in page order by the compaction.
           uint32_t c = 0;
 #pragma unroll
           for (int i = 0; i < KPL; ++i) c += (free_at(i) && (key[i] & pmask) == prefix) ? 1u : 0u;
@@ -306,29 +314,28 @@ __device__ __forceinline__ void row_cut(const SelectArgs& a, const uint32_t (&ke
           uint32_t pos = lane_u32(base, 0) + cincl - c;
 #pragma unroll
           for (int i = 0; i < KPL; ++i) {
-            if (free_at(i) && (key[i] & pmask) == prefix) {
-              sm.cand_key[pos] = key[i];
-              sm.cand_page[pos] = page_of(i);
-              ++pos;
-            }
+            if (free_at(i) && (key[i] & pmask) == prefix) sm.cand_key[pos++] = key[i];
           }
           __syncthreads();
           if (wave == 0) {
             const int m = (int)sm.cand_count;  // == inbin
             const uint32_t ck = lane < m ? sm.cand_key[lane] : 0u;
-            const int cp = lane < m ? sm.cand_page[lane] : 0x7fffffff;
-            int rank = 0;
-            for (int j = 0; j < m; ++j) {
-              const uint32_t kj = lane_u32(ck, j);
-              const int pj = (int)lane_u32((uint32_t)cp, j);
-              rank += (kj > ck || (kj == ck && pj < cp)) ? 1 : 0;
+            uint32_t above = 0, same = 0;
+            for (int j = 0; j < m; j += 4) {
+              const uint4 k4 = *reinterpret_cast<const uint4*>(&sm.cand_key[j]);  // past m: not counted
+              const uint32_t kj[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const bool in = j + u < m;
+                above += in && kj[u] > ck ? 1u : 0u;
+                same += in && kj[u] == ck ? 1u : 0u;
+              }
             }
-            const unsigned long long cut = __ballot(lane < m && rank == (int)need - 1);
-            const uint32_t kcut = lane_u32(ck, __ffsll((long long)cut) - 1);
-            const int above_cut = __popcll(__ballot(lane < m && ck > kcut));
-            if (lane == 0) {
-              sm.cross.kc = kcut;
-              sm.cross.need_eq = (int)need - above_cut;
+            const uint32_t nd = (uint32_t)need;
+            const unsigned long long cut = __ballot(lane < m && above < nd && above + same >= nd);
+            if (lane == __ffsll((long long)cut) - 1) {
+              sm.cross.kc = ck;
+              sm.cross.need_eq = (int)(nd - above);
             }
           }
           __syncthreads();
@@ -444,8 +451,8 @@ __device__ __forceinline__ int select_row_gated(const SelectArgs& a, const uint3
   int dec;
   uint32_t kc, next_key, top_key;
   int need_eq;
-  row_cut<NW, CS, false, SelectDigit<false>::kBits, true>(a, ck, free_c, forced_c, order_of, (int)count, n_forced, sm,
-                                                         dec, kc, need_eq, next_key, top_key, gate_key, mx);
+  row_cut<NW, CS, false, SelectDigit<false>::kBits, true>(a, ck, free_c, forced_c, (int)count, n_forced, sm, dec, kc,
+                                                         need_eq, next_key, top_key, gate_key, mx);
   if (dec == 1) {  // exactly K' candidates: all taken
     kc = 0u;
     need_eq = kNoLimit;
@@ -544,11 +551,11 @@ __device__ __forceinline__ void select_row_keys(const SelectArgs& a, const uint3
   uint32_t kc, gate_key, top_key;
   int need_eq;
   if (!COV && gated == 0)  // uniform: the gated attempt found the range
-    row_cut<NW, KPL, false, SelectDigit<false>::kBits, true>(a, key, free_at, forced_at, page_of, n_free, n_forced,
-                                                             sm, dec, kc, need_eq, gate_key, top_key, pre_mn, pre_mx);
+    row_cut<NW, KPL, false, SelectDigit<false>::kBits, true>(a, key, free_at, forced_at, n_free, n_forced, sm, dec,
+                                                             kc, need_eq, gate_key, top_key, pre_mn, pre_mx);
   else
-    row_cut<NW, KPL, COV, SelectDigit<COV>::kBits, false>(a, key, free_at, forced_at, page_of, n_free, n_forced, sm,
-                                                          dec, kc, need_eq, gate_key, top_key);
+    row_cut<NW, KPL, COV, SelectDigit<COV>::kBits, false>(a, key, free_at, forced_at, n_free, n_forced, sm, dec, kc,
+                                                          need_eq, gate_key, top_key);
   if (!COV && a.gate.rows && threadIdx.x == 0) gate_store(a.gate, row, dec, gate_key, top_key, -INFINITY, 0u, seen);
 
   // ---- compaction in ascending page order.  Decisions 0 and 1 become cuts that no free key
