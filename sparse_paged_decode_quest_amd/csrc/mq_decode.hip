@@ -183,6 +183,7 @@ __global__ __launch_bounds__(kUnionThreads) void page_list_union_kernel(UnionArg
 }
 
 typedef _Float16 mq_half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 mq_half8 __attribute__((ext_vector_type(8)));
 typedef float mq_float4 __attribute__((ext_vector_type(4)));
 
 struct MqPage {
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
 
   // A operand: query row l % 16 = (t_a, g_a), channels 32 q4 .. 32 q4 + 31
   const int t_a = tok >> 2, g_a = tok & 3;
-  mq_half4 qa[8];
+  mq_half8 qa[4];
   {
     uint4 w[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
     if (t_a < T) {
@@ -287,8 +288,7 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      qa[2 * i] = __builtin_bit_cast(mq_half4, make_uint2(w[i].x, w[i].y));
-      qa[2 * i + 1] = __builtin_bit_cast(mq_half4, make_uint2(w[i].z, w[i].w));
+      qa[i] = __builtin_bit_cast(mq_half8, w[i]);
     }
   }
 
@@ -301,31 +301,31 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
   }
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) acc[t] = mq_float4{0.f, 0.f, 0.f, 0.f};
+  // fp8: acc holds the PV sums in units of 2^e_acc, e_acc being the exponent bound of the last page's
+  // largest V scale (the same in every lane); f16 keeps e_acc = 0
+  int e_acc = 0;
 
   auto process = [&](const MqPage& r, const MqKV& kv) {
     if (r.page < 0) return;
     mq_float4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[2 * i], __builtin_bit_cast(mq_half4, make_uint2(kv.k[i].x, kv.k[i].y)),
-                                                s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[2 * i + 1],
-                                                __builtin_bit_cast(mq_half4, make_uint2(kv.k[i].z, kv.k[i].w)), s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[i], __builtin_bit_cast(mq_half8, kv.k[i]), s, 0, 0, 0);
     }
     const bool ok = q4 < T && ((r.mask >> q4) & 1u) && r.page * kPage + tok < lim && tok < r.valid;
     // fp8: key tok's K scale on its logit column; its V scale on its probabilities (P times the scale
     // is what V's fp16 values times 2^8 are weighted with).  Slots past the request's end (scales may
     // be NaN) are masked before either is used.
     const float kscale = KVD == SPD_DTYPE_F16 ? a.sm_scale_log2 : a.sm_scale_log2 * (ok ? kv.ks : 0.f);
-    // fp8: the probabilities carry each key's V scale relative to the page's largest (at most 1, so the
-    // fp16 operand neither overflows nor loses precision to small scales); that largest scale multiplies
-    // the page's PV product in fp32 below
-    float vmax = 1.f;
+    // fp8: the probabilities carry each key's V scale over 2^e_pg, the power of two just above the page's
+    // largest scale (so under 1: the fp16 operand neither overflows nor loses precision to small scales);
+    // the accumulator moves to units of 2^e_pg below, exactly, since every factor is a power of two
+    int e_pg = 0;
     if constexpr (KVD != SPD_DTYPE_F16) {
-      vmax = row_max(tok < r.valid ? kv.vs : 0.f);  // the page's 16 tokens, one per lane of the row
-      vmax = vmax > 0.f ? vmax : 1.f;
+      const float vmax = row_max(tok < r.valid ? kv.vs : 0.f);  // the page's 16 tokens, one per lane of the row
+      e_pg = vmax > 0.f ? __builtin_amdgcn_frexp_expf(vmax) : 0;  // vmax < 2^e_pg
     }
-    const float vscale = KVD == SPD_DTYPE_F16 ? 1.f : (ok ? kv.vs / vmax : 0.f);
+    const float vscale = KVD == SPD_DTYPE_F16 ? 1.f : (ok ? __builtin_amdgcn_ldexpf(kv.vs, -e_pg) : 0.f);
     float p[4], alpha[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -358,13 +358,13 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
     // B = P^T: row l % 16, keys 4 q4 .. 4 q4 + 3; A = V^T tile s: channel 16 s + l % 16, the same keys
     const mq_half4 pb = *reinterpret_cast<const mq_half4*>(&p16[wave][tok][4 * q4]);
     const float al = al_lds[wave][tok];
-    // fp8: acc = vmax (acc al / vmax + V^T P'^T), the page's contribution scaled in fp32
-    const float pre = KVD == SPD_DTYPE_F16 ? al : al / vmax;
+    // fp8: in units of 2^e_pg, acc = acc al 2^(e_acc - e_pg) + V^T P'^T
+    const float pre = KVD == SPD_DTYPE_F16 ? al : __builtin_amdgcn_ldexpf(al, e_acc - e_pg);
+    e_acc = e_pg;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
       const uint2 va = reinterpret_cast<const uint2*>(&vt[wave][16 * t + tok][0])[q4];
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(mq_half4, va), pb, acc[t] * pre, 0, 0, 0);
-      if constexpr (KVD != SPD_DTYPE_F16) acc[t] = acc[t] * vmax;
     }
     wave_fence();
   };
@@ -429,8 +429,14 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
     }
   }
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-    *reinterpret_cast<float4*>(&ws_acc[wave][tok][16 * t + 4 * q4]) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+  for (int t = 0; t < D / 16; ++t) {
+    mq_float4 o = acc[t];
+    if constexpr (KVD != SPD_DTYPE_F16) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = __builtin_amdgcn_ldexpf(o[c], e_acc);  // back from units of 2^e_acc
+    }
+    *reinterpret_cast<float4*>(&ws_acc[wave][tok][16 * t + 4 * q4]) = make_float4(o[0], o[1], o[2], o[3]);
+  }
   __syncthreads();
 
   // merge the four wave states (fixed order); write the chunk result of the rows of tokens < T
