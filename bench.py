@@ -284,6 +284,9 @@ def main():
                     help="also time chunks of this many steps that reuse one page selection (1: off)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--gate-drift", default=None,
+                    help="only measure LiteTopK's gate under drifting queries, for these comma-separated noise "
+                         "levels (one JSON line each)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -316,6 +319,8 @@ def main():
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
 
+    if args.gate_drift:
+        return gate_drift(args, w, inp, base)
     plan = None
     if args.plan:
         v = [int(x) for x in args.plan.split(",")]
@@ -577,6 +582,97 @@ def main():
         "setup_s": round(gen_s, 1), "kernel_hash": dom_hash,
     }
     print(json.dumps(line))
+
+
+def gate_drift(args, w, inp, base):
+    """LiteTopK's gate when consecutive queries differ.  Per layer copy, two steps read the same KV and page
+    statistics with queries q_a and q_b = (q_a + eps n) / sqrt(1 + eps^2) (n fresh Gaussian noise, eps relative to
+    q_a's standard deviation) and share one gate state; the calls alternate, so every gate was predicted from
+    the other query's scores.  Reports the rows served from candidates after each query's call, the share of a
+    row's list the two queries have in common, and the alternating step and selection times with the gate on
+    and off (graph replays over the rotated layers, HIP events on the replay stream)."""
+    import dataclasses
+
+    import torch
+
+    from sparse_paged_decode_quest_amd import step as S
+
+    if w.num_queries > 1 or not S.DecodeStep(w, base).gated:
+        print(json.dumps({"error": f"{w.name} has no LiteTopK gate (single-query top-K with the bound estimator "
+                                   "on 16-token pages only)"}))
+        sys.exit(2)
+    R = args.layers or (12 if max(w.seq_lens) > 262144 else 24)
+
+    def clone(t):
+        return None if t is None else t.clone()
+
+    layers = [base] + [S.DeviceInputs(q=clone(base.q), k_pool=clone(base.k_pool), v_pool=clone(base.v_pool),
+                                      k_scale=clone(base.k_scale), v_scale=clone(base.v_scale),
+                                      block_table=clone(base.block_table), seq_lens=clone(base.seq_lens),
+                                      head_kind=base.head_kind.copy(), page_meta=clone(base.page_meta))
+                       for _ in range(R - 1)]
+    rows = w.batch * w.num_kv_heads
+    dyn = [b * w.num_kv_heads + h for b in range(w.batch) for h in range(w.num_kv_heads) if not inp.head_kind[h]]
+    stream = torch.cuda.Stream()
+
+    def timed(fn, steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for i in range(2 * R):
+                fn(i, stream.cuda_stream)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(2 * R):
+                fn(i, stream.cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, steps // (2 * R))
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * 2 * R)
+
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)
+    for eps in [float(x) for x in args.gate_drift.split(",")]:
+        pairs, upairs = [], []
+        for d in layers:
+            n = torch.randn(d.q.shape, generator=gen, device="cuda", dtype=torch.float32)
+            qa = d.q.float()
+            db = dataclasses.replace(d, q=((qa + eps * qa.std() * n) / (1 + eps * eps) ** 0.5).to(d.q.dtype))
+            sa, sb = S.DecodeStep(w, d), S.DecodeStep(w, db)
+            sb.topk_state = sa.topk_state  # one gate state for both queries
+            sb.sel.topk_state = sa.topk_state.data_ptr()
+            pairs.append((sa, sb))
+            upairs.append((S.DecodeStep(w, d, gated=False), S.DecodeStep(w, db, gated=False)))
+        sa, sb = pairs[0]
+        served = []
+        for _ in range(2):
+            for st in (sa, sb):
+                st.run()
+                torch.cuda.synchronize()
+                served.append(int(S.gate_paths(sa.topk_state, rows)[dyn, 0].sum()))
+        la, lb = sa.lists(), sb.lists()
+        ua, ub = upairs[0]
+        ua.run()
+        ub.run()
+        torch.cuda.synchronize()
+        assert ua.lists() == la and ub.lists() == lb, "gated lists differ from the ungated selection's"
+        overlap = [len(set(la[k]) & set(lb[k])) / max(1, len(la[k])) for k in la if not inp.head_kind[k[1]]]
+        pick = lambda ps, i: ps[i % R][i // R % 2]  # R calls with q_a, then R with q_b
+        res = {"step_us_gated": timed(lambda i, s: pick(pairs, i).run(s), args.steps),
+               "step_us_ungated": timed(lambda i, s: pick(upairs, i).run(s), args.steps),
+               "select_us_gated": timed(lambda i, s: pick(pairs, i).select_only(s), args.steps),
+               "select_us_ungated": timed(lambda i, s: pick(upairs, i).select_only(s), args.steps)}
+        print(json.dumps({"gate_drift": w.name, "eps": eps, "dynamic_rows": len(dyn), "rows_from_candidates": served[2:],
+                          "list_overlap_mean": round(float(np.mean(overlap)), 4),
+                          "list_overlap_min": round(float(np.min(overlap)), 4), "layers_rotated": R,
+                          **{k: round(v, 3) for k, v in res.items()}}), flush=True)
+        del pairs, upairs
+        torch.cuda.synchronize()
 
 
 def bench_mq(args, w, inp, base, plan, gen_s):
