@@ -98,7 +98,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 14
+#define SPD_ABI_VERSION 15
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
@@ -443,12 +443,15 @@ int spd_page_select_mq(const spd_desc* desc, int32_t num_tokens, int32_t token_m
  * outside [0, n_b) of the request are ignored.  Writes page_list (device, [B, Hkv, max_list]) in
  * ascending page order, page_mask (device, same shape, uint32: bit t set when token t listed the
  * page), list_len (device, [B, Hkv]) and, when page_phys (device, may be NULL) is set, the
- * physical page of each entry from block_table.  Errors as elsewhere; num_tokens outside
- * [1, SPD_MQ_MAX_TOKENS] is SPD_ERR_INVALID_ARG. */
+ * physical page of each entry from block_table.  Two methods give the same union: block tables of
+ * at least 16,384 pages whose token lists are ascending and hold at most 1,024 entries in all merge
+ * the lists by rank, the others collect them in a byte map over the request's pages; union_path
+ * (device, may be NULL, [B, Hkv]) receives 1 for a row merged by rank and 0 for a byte-map row.
+ * Errors as elsewhere; num_tokens outside [1, SPD_MQ_MAX_TOKENS] is SPD_ERR_INVALID_ARG. */
 int spd_page_list_union(const spd_desc* desc, int32_t num_tokens, int32_t token_max_list,
                         const int32_t* token_list, const int32_t* token_len, const int32_t* block_table,
                         const int32_t* seq_lens, int32_t* page_list, int32_t* page_phys,
-                        uint32_t* page_mask, int32_t* list_len, void* stream);
+                        uint32_t* page_mask, int32_t* list_len, int32_t* union_path, void* stream);
 
 /* Decode attention of the T query tokens of every row over the union list: q (device,
  * [B, T, Hq, d] f16), out (device, [B, T, Hq, d] f32), out_lse (device, [B, T, Hq] f32);

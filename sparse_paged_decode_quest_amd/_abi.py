@@ -82,7 +82,7 @@ def lib():
         L.spd_lse_merge.argtypes = [D, P, v, v, v, v, v, v]
         L.spd_sparse_paged_decode_noalloc.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v]
         L.spd_sparse_paged_decode_merged.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v, v]
-        L.spd_page_list_union.argtypes = [D, c_int32, c_int32, v, v, v, v, v, v, v, v, v]
+        L.spd_page_list_union.argtypes = [D, c_int32, c_int32, v, v, v, v, v, v, v, v, v, v]
         L.spd_page_score_mq.argtypes = [D, c_int32, S, v, v, v, v, POINTER(c_uint8), v, v]
         L.spd_page_select_mq.argtypes = [D, c_int32, c_int32, S, v, v, POINTER(c_uint8), v, v, v, v, v]
         L.spd_sparse_paged_decode_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v,
@@ -236,10 +236,11 @@ def spd_page_select_mq(desc, num_tokens, token_max_list, sel, scores, seq_lens, 
 
 
 def spd_page_list_union(desc, num_tokens, token_max_list, token_list, token_len, block_table, seq_lens, page_list,
-                        page_phys, page_mask, list_len, stream=None):
+                        page_phys, page_mask, list_len, stream=None, union_path=None):
     _check(lib().spd_page_list_union(ctypes.byref(desc), int(num_tokens), int(token_max_list), _ptr(token_list),
                                      _ptr(token_len), _ptr(block_table), _ptr(seq_lens), _ptr(page_list),
-                                     _ptr(page_phys), _ptr(page_mask), _ptr(list_len), _stream(stream)),
+                                     _ptr(page_phys), _ptr(page_mask), _ptr(list_len), _ptr(union_path),
+                                     _stream(stream)),
            "spd_page_list_union")
 
 

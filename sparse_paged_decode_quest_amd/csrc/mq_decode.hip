@@ -119,7 +119,10 @@ __global__ __launch_bounds__(kUnionThreads) void page_list_union_kernel(UnionArg
         a.page_mask[out_row + pos] = mask;
         if (a.page_phys) a.page_phys[out_row + pos] = bt_row[pg];
       }
-      if (threadIdx.x == kUnionThreads - 1) a.list_len[row] = (int)min(base + incl, (uint32_t)a.max_list);
+      if (threadIdx.x == kUnionThreads - 1) {
+        a.list_len[row] = (int)min(base + incl, (uint32_t)a.max_list);
+        if (a.path) a.path[row] = 1;
+      }
       return;
     }
   }
@@ -179,7 +182,10 @@ __global__ __launch_bounds__(kUnionThreads) void page_list_union_kernel(UnionArg
       ++pos;
     }
   }
-  if (threadIdx.x == kUnionThreads - 1) a.list_len[row] = (int)min(base + incl, (uint32_t)a.max_list);
+  if (threadIdx.x == kUnionThreads - 1) {
+    a.list_len[row] = (int)min(base + incl, (uint32_t)a.max_list);
+    if (a.path) a.path[row] = 0;
+  }
 }
 
 typedef _Float16 mq_half4 __attribute__((ext_vector_type(4)));

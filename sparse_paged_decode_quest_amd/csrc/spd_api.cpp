@@ -691,7 +691,7 @@ int spd_page_select_mq(const spd_desc* desc, int32_t num_tokens, int32_t token_m
 int spd_page_list_union(const spd_desc* desc, int32_t num_tokens, int32_t token_max_list, const int32_t* token_list,
                         const int32_t* token_len, const int32_t* block_table, const int32_t* seq_lens,
                         int32_t* page_list, int32_t* page_phys, uint32_t* page_mask, int32_t* list_len,
-                        void* stream) {
+                        int32_t* union_path, void* stream) {
   int rc = check_mq(desc, num_tokens);
   if (rc) return rc;
   if (token_max_list < 1) return SPD_ERR_INVALID_ARG;
@@ -710,6 +710,7 @@ int spd_page_list_union(const spd_desc* desc, int32_t num_tokens, int32_t token_
   a.page_phys = page_phys;
   a.page_mask = page_mask;
   a.list_len = list_len;
+  a.path = union_path;
   a.batch = desc->batch;
   a.num_kv_heads = desc->num_kv_heads;
   a.max_pages = desc->max_pages_per_seq;

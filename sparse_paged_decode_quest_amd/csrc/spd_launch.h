@@ -189,6 +189,7 @@ struct UnionArgs {
   int32_t* page_phys;         // nullable
   uint32_t* page_mask;        // [B, Hkv, max_list]
   int32_t* list_len;          // [B, Hkv]
+  int32_t* path;              // nullable [B, Hkv]: 1 where the rank merge built the row's union, 0 the byte map
   int batch, num_kv_heads, max_pages, max_list, num_tokens, token_max_list;
 };
 int launch_page_list_union(const UnionArgs& a, hipStream_t stream);

@@ -376,10 +376,13 @@ class MQDecodeStep:
         self.score(stream)
         self.select_only(stream)
 
-    def union(self, stream=None):
+    def union(self, stream=None, path=None):
+        """The union of the token lists; `path` ([B, Hkv] int32, optional) receives 1 for rows merged by rank
+        and 0 for rows built in the byte map."""
         d = self.d
         A.spd_page_list_union(self.desc, self.T, self.token_cap, self.token_list, self.token_len, d.block_table,
-                              d.seq_lens, self.page_list, self.page_phys, self.page_mask, self.list_len, stream)
+                              d.seq_lens, self.page_list, self.page_phys, self.page_mask, self.list_len, stream,
+                              union_path=path)
 
     def attend(self, stream=None):
         d = self.d

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 14
+    assert A.abi_version() == 15
 
 
 def test_error_strings(lib):
@@ -337,7 +337,7 @@ def test_several_query_tokens_argument_checks(lib):
         p = {k: FAKE for k in ("tl", "tn", "bt", "sl", "pl", "pp", "pm", "ll")}
         p.update(null)
         return L.spd_page_list_union(ctypes.byref(desc), T, tml, p["tl"], p["tn"], p["bt"], p["sl"], p["pl"], p["pp"],
-                                     p["pm"], p["ll"], 0)
+                                     p["pm"], p["ll"], None, 0)
 
     def dec_rc(desc, T=4, pl=plan, **null):
         p = {k: FAKE for k in ("q", "k", "v", "ks", "vs", "bt", "sl", "pl", "pp", "pm", "ll", "o", "lse", "po", "pls")}

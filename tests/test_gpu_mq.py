@@ -113,6 +113,14 @@ def test_mq_lists_union_attention(name, wide):
     # the union is exact integer work: it must be the union of the GPU's own token lists
     union = st.union_lists()
     assert union == O.union_lists(gpu_lists)
+    # and it was built the intended way: ascending token lists of at most 1,024 entries on a 16,384-page
+    # table are merged by rank, every other row in the byte map
+    path = torch.full((w.batch, w.num_kv_heads), -1, dtype=torch.int32, device="cuda")
+    st.union(path=path)
+    torch.cuda.synchronize()
+    assert st.token_cap * w.num_queries <= 1024
+    assert (path.cpu().numpy() == (1 if wide else 0)).all(), path.cpu().numpy()
+    assert st.union_lists() == union
     pp = st.page_phys.cpu().numpy()
     for (b, h), (pages, _) in union.items():
         assert pp[b, h, :len(pages)].tolist() == inp.block_table[b, pages].tolist()
