@@ -54,11 +54,17 @@
  *      k_pool,v_pool [num_pool_pages, Hkv, P, d]  f32, f16 or fp8 E4M3FN bytes
  *      k_scale,v_scale [num_pool_pages, Hkv, P]  fp16 bits (fp8 pools only; value =
  *                                              E4M3FN(code) * scale)
- *      page_meta    [num_pool_pages, Hkv, g, 2, d] per logical page (sub-page i of the
- *                                              physical page): index 0 = channel min, 1 =
- *                                              channel max; f32 for f32 pools, f16 otherwise
- *                                              (for fp8 pools rounded outward: min down, max up)
- *      page_stats   [num_pool_pages, Hkv, 2, d] bf16 bits: index 0 = channel mean, 1 =
+ *      page_meta    [B, Hkv, max_pages_per_seq * g, 2, d] per request, in logical page
+ *                                              order: entry [b, h, p] is logical page p of
+ *                                              request b (tokens 16 p .. 16 p + 15); index 0 =
+ *                                              channel min, 1 = channel max; f32 for f32 pools,
+ *                                              f16 otherwise (for fp8 pools rounded outward:
+ *                                              min down, max up).  The key statistics are
+ *                                              request state, like the request's block-table
+ *                                              row: a caller that moves a request to another
+ *                                              batch position moves its rows with it
+ *      page_stats   [B, Hkv, max_pages_per_seq * g, 2, d] bf16 bits, per request in logical
+ *                                              page order as page_meta: index 0 = channel mean, 1 =
  *                                              channel variance (mean squared deviation) of
  *                                              the page's valid keys, each rounded to nearest
  *                                              even (Moira, section 3.1 "Page summaries and the
@@ -98,7 +104,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 15
+#define SPD_ABI_VERSION 16
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
@@ -227,14 +233,14 @@ typedef struct spd_plan_params {
 /* ------------------------------------------------------------------ entry points */
 
 /* Channel-wise min / max of the valid keys of logical pages p of each request, for every KV
- * head, written to page_meta at the logical page's place in its physical page.  first_page and
+ * head, read through the block table and written to page_meta at [b, h, p].  first_page and
  * span_pages count logical pages.  first_page (device, [B], may be
  * NULL): when set, pages first_page[b] .. min(n_b, first_page[b] + span_pages) - 1 are built
  * (span_pages >= 1).  When NULL, span_pages = 0 builds every page 0..n_b-1 (the bulk build at
  * prefill) and span_pages >= 1 builds the last span_pages pages of each request, read from
  * seq_lens on the device -- span_pages = 1 is the refresh of the page the newest token is in.
- * k_scale (device) is required for fp8 pools and ignored otherwise.  Other slots of page_meta
- * are not touched. */
+ * k_scale (device) is required for fp8 pools and ignored otherwise.  Other entries of page_meta,
+ * and those of pages whose block-table entry is outside [0, num_pool_pages), are not touched. */
 int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t* k_scale,
                         const int32_t* block_table, const int32_t* seq_lens,
                         const int32_t* first_page, int32_t span_pages, void* page_meta,
@@ -242,7 +248,7 @@ int spd_page_meta_build(const spd_desc* desc, const void* k_pool, const uint16_t
 
 /* Moira page summaries (section 3.1, "Page summaries and the mvar estimate"): channel mean and
  * variance of the valid keys of logical pages of each request, every KV head, written to
- * page_stats (bf16, layout above) at the page's physical slot.  Pages, arguments and errors as
+ * page_stats (bf16, layout above) at [b, h, p].  Pages, arguments and errors as
  * in spd_page_meta_build. */
 int spd_page_stats_build(const spd_desc* desc, const void* k_pool, const uint16_t* k_scale,
                          const int32_t* block_table, const int32_t* seq_lens,
@@ -258,6 +264,8 @@ int spd_page_stats_build(const spd_desc* desc, const void* k_pool, const uint16_
  * logical pages.  COVERAGE: l_{g,p} = sm_scale * S_{g,p} +
  * ln(valid tokens of p); head_lse[b, h*G+g] = logsumexp_p l_{g,p}; scores[b,h,p] =
  * (1/G) sum_g exp(l_{g,p} - head_lse) (Moira's group-mean share, section 3.2, Eq. 3).
+ * The key boxes are read from page_meta at [b, h, p] alone; block_table (device) only marks the
+ * pages whose entry lies outside [0, num_pool_pages): they score -inf (TOPK) or carry no mass.
  * tail_mode (spd_tail_mode) says how each dynamic row's last logical page is treated;
  * SPD_TAIL_REBUILD reads k_pool (and k_scale for fp8 pools) and writes that page's entries of
  * page_meta, which is otherwise only read; SPD_TAIL_SKIP is valid in TOPK mode only.  head_lse
@@ -411,7 +419,8 @@ int spd_sparse_paged_decode_noalloc(const spd_desc* desc, const spd_plan_params*
  * as for spd_page_score: streaming heads are not scored.  Writes scores (device,
  * [B * T, Hkv, max_pages_per_seq] f32; row b T + t) for the pages of token t's length
  * L - T + 1 + t, bit for bit what spd_page_score with SPD_TAIL_NONE writes on a descriptor of B * T
- * rows; later entries are not written.  The statistics of the pages the draft tokens are in must be
+ * rows whose block-table rows and page_meta rows repeat each request's T times; later entries are
+ * not written.  The statistics of the pages the draft tokens are in must be
  * current (spd_page_meta_build over the last pages first).  sel must be top-K with the bound
  * estimator (else SPD_ERR_UNSUPPORTED); errors otherwise as spd_page_score and spd_page_list_union. */
 int spd_page_score_mq(const spd_desc* desc, int32_t num_tokens, const spd_select_params* sel, const void* q,

@@ -65,9 +65,10 @@ template <int D> struct MetaTraits<D, SPD_DTYPE_FP8_E4M3FN> {
   }
 };
 
-// Statistics of logical page p of request b (len tokens), KV head h, by the calling wave, stored
-// with the physical page that holds it (sub-page p mod 2^lgs of block-table slot p >> lgs).
-// Pages whose block-table entry is outside the pool are left alone.
+// Statistics of logical page p of request b (len tokens), KV head h, by the calling wave, read from
+// the physical page that holds it (sub-page p mod 2^lgs of block-table slot p >> lgs) and stored at
+// the request's logical page (meta_unit).  Pages whose block-table entry is outside the pool are
+// left alone.
 template <int D, int KVD>
 __device__ __forceinline__ void build_page_meta(const MetaArgs& a, int b, int p, int h, int len) {
   using T = MetaTraits<D, KVD>;
@@ -99,7 +100,7 @@ __device__ __forceinline__ void build_page_meta(const MetaArgs& a, int b, int p,
       hi[c] = ok ? fmaxf(hi[c], v[t][c]) : hi[c];
     }
   }
-  T::store(a.meta, unit * 2 * D + c0, lo, hi, D);
+  T::store(a.meta, meta_unit(b, h, p, a.num_kv_heads, a.max_pages, a.lgs) * 2 * D + c0, lo, hi, D);
 }
 
 // Moira page summary ("Page summaries and the mvar estimate"): channel-wise mean and variance of
@@ -139,7 +140,7 @@ __device__ __forceinline__ void build_page_stats(const MetaArgs& a, int b, int p
     if (KVD == SPD_DTYPE_FP8_E4M3FN) scale = half_bits_to_float(a.k_scale[head_base + t]);
     T::load(a.k_pool, (head_base + t) * D + c0, v[t], scale);
   }
-  uint16_t* m = reinterpret_cast<uint16_t*>(a.meta) + unit * 2 * D + c0;
+  uint16_t* m = reinterpret_cast<uint16_t*>(a.meta) + meta_unit(b, h, p, a.num_kv_heads, a.max_pages, a.lgs) * 2 * D + c0;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     double sum = 0.0;

@@ -38,24 +38,20 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(Scor
   int pg[ITERS];
   bool ok[ITERS];
   typename T::M m[ITERS];
-  // every block-table entry is tested before the first key-box load is issued: a test after a
-  // conditional load would make the compiler wait for that load too
+  // the key boxes' addresses need no block-table entry: they are requested at once, and the entries
+  // only mark pages outside the pool afterwards
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    pg[it] = score_page<D, KVD, kScoreWaves>(p_begin, it);
-    ok[it] = pg[it] < n && raw[it] >= 0 && raw[it] < a.num_pool_pages;
-  }
-#pragma unroll
-  for (int it = 0; it < ITERS; ++it)
-    if (ok[it]) T::load_m(m[it], a.meta, head_unit(raw[it], a.num_kv_heads, h, 0, 0) * 2 * D, c0);
-  // the query groups after the key boxes, unconditionally (token indices clamped to the last token),
-  // so that no wait for them comes between the block-table entries and the key-box loads
+  for (int it = 0; it < ITERS; ++it) pg[it] = score_page<D, KVD, kScoreWaves>(p_begin, it);
+  load_boxes<D, KVD, ITERS>(a, b, h, pg, c0, m);
+  // the query groups after the key boxes, unconditionally (token indices clamped to the last token)
   typename T::Q qr[kMqScoreMaxTokens];
 #pragma unroll
   for (int t = 0; t < kMqScoreMaxTokens; ++t) {
     const int tt = min(t, num_tokens - 1);
     T::load_q(qr[t], a.q, (((size_t)b * num_tokens + tt) * a.num_q_heads + (size_t)h * kG) * D, c0);
   }
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) ok[it] = pg[it] < n && raw[it] >= 0 && raw[it] < a.num_pool_pages;
   if constexpr (LPP == 16 && kMqScoreMaxTokens == 4) {
     // The 16 sums (token t, head g) of a page live spread over its 16 lanes.  A reduce-scatter hands
     // lane l the whole sum of k = l = 4 t + g: at each level (lane bit 1, 2, 4, 8) a lane keeps the half

@@ -147,10 +147,13 @@ __device__ __forceinline__ void mvar_block_ell(const ScoreArgs& a, const int (&r
   }
   typename T::Q qr;
   T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0, a.sm_scale);
+  // the summaries' addresses need no block-table entry, so they are requested without waiting for it
+  // (a page past the row's summaries reads its last one, and its mass is discarded)
   typename T::M m[ITERS];
+  const size_t base = meta_unit(b, h, 0, a.num_kv_heads, a.max_pages, a.lgs);
+  const int last = (a.max_pages << a.lgs) - 1;
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it)
-    if (ok[it]) T::load_m(m[it], a.meta, head_unit(raw[it], a.num_kv_heads, h, a.lgs, pg[it] & ((1 << a.lgs) - 1)) * 2 * D, c0);
+  for (int it = 0; it < ITERS; ++it) T::load_m(m[it], a.meta, (base + min(pg[it], last)) * 2 * D, c0);
   const size_t row = (size_t)b * a.num_kv_heads + h;
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {

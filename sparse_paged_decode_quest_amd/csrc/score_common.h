@@ -265,8 +265,21 @@ __device__ __forceinline__ void load_block_table(const int32_t* bt_row, int max_
   for (int it = 0; it < ITERS; ++it) raw[it] = bt_row[min(score_page<D, KVD, NW>(p_begin, it) >> lgs, max_pages - 1)];
 }
 
+// Key boxes of the calling lane's page groups (logical pages pg) of request b, KV head h.  Their
+// addresses follow from the logical pages alone, so the loads are issued at once, beside the
+// block-table entries that only mark pages outside the pool; every group's box is loaded with no
+// branch around the load (a page past the row's boxes reads its last box, and its bound is discarded).
+template <int D, int KVD, int ITERS>
+__device__ __forceinline__ void load_boxes(const ScoreArgs& a, int b, int h, const int (&pg)[ITERS], int c0,
+                                           typename ScoreTraits<D, KVD>::M (&m)[ITERS]) {
+  const size_t base = meta_unit(b, h, 0, a.num_kv_heads, a.max_pages, a.lgs);
+  const int last = (a.max_pages << a.lgs) - 1;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) ScoreTraits<D, KVD>::load_m(m[it], a.meta, (base + min(pg[it], last)) * 2 * D, c0);
+}
+
 // Bounds S_{g,p} of the pages [p_begin, p_begin + NW * ITERS * PPI) owned by this workgroup.
-// Pages >= n are not loaded (n is the scan limit); raw holds load_block_table's entries.
+// Pages >= n do not count (n is the scan limit); raw holds load_block_table's entries.
 // For each of the ITERS page groups of the calling lane, `fn(p, ok, s)` is called on lanes
 // with sub == 0 after the LPP-lane reduction (p may be >= n: then ok is false and fn must
 // ignore it).  Pages whose block-table entry is outside the pool have ok = false.
@@ -278,25 +291,16 @@ __device__ __forceinline__ void score_block(const ScoreArgs& a, const int (&raw)
   const int lane = threadIdx.x % kWave;
   const int sub = lane % LPP;
   const int c0 = sub * T::CW;
-  int pg[ITERS], phys[ITERS];
+  int pg[ITERS];
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    pg[it] = score_page<D, KVD, NW>(p_begin, it);
-    phys[it] = pg[it] < n ? raw[it] : -1;
-  }
+  for (int it = 0; it < ITERS; ++it) pg[it] = score_page<D, KVD, NW>(p_begin, it);
   typename T::Q qr;
   T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0);
   typename T::M m[ITERS];
-  // Every group's meta row is loaded, with no branch around the load: a page past the scan or outside
-  // the pool reads the row of pool page 0 instead, and its bound is discarded.
+  load_boxes<D, KVD, ITERS>(a, b, h, pg, c0, m);
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
-    const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
-    T::load_m(m[it], a.meta, head_unit(ok ? phys[it] : 0, a.num_kv_heads, h, a.lgs, pg[it] & ((1 << a.lgs) - 1)) * 2 * D, c0);
-  }
-#pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
+    const bool ok = pg[it] < n && raw[it] >= 0 && raw[it] < a.num_pool_pages;
     float s[kG];
     T::bound(qr, m[it], s);
 #pragma unroll
@@ -323,7 +327,8 @@ __device__ __forceinline__ void score_tail_page(const ScoreArgs& a, const int32_
   if (phys < 0 || phys >= a.num_pool_pages) return;
   const size_t head_page = (size_t)phys * a.num_kv_heads + h;
   typename T::M m;
-  T::rebuild(m, a.k_pool, a.k_scale, head_page, valid_in_page(len, n - 1), c0, a.meta_out, head_page * 2 * D);
+  T::rebuild(m, a.k_pool, a.k_scale, head_page, valid_in_page(len, n - 1), c0, a.meta_out,
+             meta_unit(b, h, n - 1, a.num_kv_heads, a.max_pages, 0) * 2 * D);
   float s[kG];
   T::bound(qr, m, s);
 #pragma unroll
@@ -366,25 +371,16 @@ __device__ __forceinline__ void score_block_topk_hier(const ScoreArgs& a, const 
   const int sub = lane % LPP;
   const int c0 = sub * T::CW;
   const int span = LPP << a.lgs;  // lanes of one physical page
-  int pg[ITERS], phys[ITERS];
+  int pg[ITERS];
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    pg[it] = score_page<D, KVD, NW>(p_begin, it);
-    phys[it] = pg[it] < n ? raw[it] : -1;
-  }
+  for (int it = 0; it < ITERS; ++it) pg[it] = score_page<D, KVD, NW>(p_begin, it);
   typename T::Q qr;
   T::load_q(qr, a.q, ((size_t)b * a.num_q_heads + (size_t)h * kG) * D, c0);
   typename T::M m[ITERS];
-  // Every group's meta row is loaded, with no branch around the load: a page past the scan or outside
-  // the pool reads the row of pool page 0 instead, and its bound is discarded.
+  load_boxes<D, KVD, ITERS>(a, b, h, pg, c0, m);
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
-    const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
-    T::load_m(m[it], a.meta, head_unit(ok ? phys[it] : 0, a.num_kv_heads, h, a.lgs, pg[it] & ((1 << a.lgs) - 1)) * 2 * D, c0);
-  }
-#pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const bool ok = phys[it] >= 0 && phys[it] < a.num_pool_pages;
+    const bool ok = pg[it] < n && raw[it] >= 0 && raw[it] < a.num_pool_pages;
     float s[kG];
     T::bound(qr, m[it], s);
 #pragma unroll

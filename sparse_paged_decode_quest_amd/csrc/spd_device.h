@@ -312,10 +312,18 @@ __device__ __forceinline__ int row_phys_pages(int len, int max_pages, int lgs) {
 }
 
 // Index of the kPage-token unit holding sub-page `sub` of physical page `phys`, KV head h, in the
-// pools ([pages, Hkv, kPage << lgs, d]): its keys start at element unit * kPage * d, its scales at
-// unit * kPage, and its key statistics at unit * 2 * d of the page meta ([pages, Hkv, 2^lgs, 2, d]).
+// pools ([pages, Hkv, kPage << lgs, d]): its keys start at element unit * kPage * d and its scales
+// at unit * kPage.
 __device__ __forceinline__ size_t head_unit(int phys, int num_kv_heads, int h, int lgs, int sub) {
   return (((size_t)phys * num_kv_heads + h) << lgs) + (size_t)sub;
+}
+
+// Index of logical page p of request b, KV head h, in the key statistics ([B, Hkv, max_pages << lgs,
+// 2, d]): its box starts at element index * 2 * d.  The statistics are kept per request in logical
+// page order, head-major, so a scan over a row's pages reads one contiguous run and its addresses do
+// not wait for the block table.
+__device__ __forceinline__ size_t meta_unit(int b, int h, int p, int num_kv_heads, int max_pages, int lgs) {
+  return ((size_t)b * num_kv_heads + h) * ((size_t)max_pages << lgs) + (size_t)p;
 }
 
 }  // namespace spd

@@ -49,7 +49,7 @@ class DeviceInputs:
     block_table: torch.Tensor
     seq_lens: torch.Tensor
     head_kind: np.ndarray      # host
-    page_meta: torch.Tensor    # [Npool, Hkv, 2, d]: key min / max, or (mvar) key mean / variance in bf16
+    page_meta: torch.Tensor    # [B, Hkv, pages * g, 2, d]: key min / max, or (mvar) key mean / variance in bf16
 
     @property
     def num_pool_pages(self) -> int:
@@ -67,8 +67,8 @@ def upload(inp: Inputs, device="cuda") -> DeviceInputs:
     v_scale = None if inp.v_scale is None else t(inp.v_scale.view(np.int16))
     mdt = torch.bfloat16 if w.estimator == "mvar" else torch.float32 if w.kv_dtype == "f32" else torch.float16
     g = w.page_size // 16  # logical pages per physical page (hierarchical paging)
-    shape = (inp.num_pool_pages, w.num_kv_heads) + ((g,) if g > 1 else ()) + (2, w.head_dim)
-    meta = torch.zeros(shape, dtype=mdt, device=device)
+    # per request in logical page order, head-major: a row's scan reads one contiguous run
+    meta = torch.zeros((w.batch, w.num_kv_heads, w.pages_per_seq * g, 2, w.head_dim), dtype=mdt, device=device)
     return DeviceInputs(q=t(inp.q), k_pool=t(inp.k_pool), v_pool=t(inp.v_pool), k_scale=k_scale, v_scale=v_scale,
                         block_table=t(inp.block_table), seq_lens=t(inp.seq_lens), head_kind=inp.head_kind.copy(),
                         page_meta=meta)

@@ -26,6 +26,36 @@ TIE_RTOL = 1e-5
 ATTN_TOL = {"f32": 2e-3, "f16": 2e-3, "fp8": 2e-2}
 
 
+def pool_meta(meta, block_table, seq_lens, num_pool_pages, fill=0):
+    """The library's key statistics in the oracle's layout.
+
+    The library keeps them per request in logical page order ([B, Hkv, max_pages * g, 2, d], g
+    logical pages per physical page); the oracle keeps them with the physical page that holds each
+    logical page ([num_pool_pages, Hkv, 2, d], or [num_pool_pages, Hkv, g, 2, d] when g > 1).  The
+    result holds the entries of each request's first ceil(L / 16) logical pages at their physical
+    page; pool pages that hold none of them keep ``fill``."""
+    meta = np.asarray(meta)
+    bt = np.asarray(block_table)
+    B, H, LP = meta.shape[:3]
+    g = LP // bt.shape[1]
+    out = np.full((num_pool_pages, H, g) + meta.shape[3:], fill, dtype=meta.dtype)
+    for b in range(B):
+        n = min(O.n_pages(int(seq_lens[b])), LP)
+        lp = np.arange(n)
+        phys = bt[b, lp // g].astype(np.int64)
+        ok = (phys >= 0) & (phys < num_pool_pages)
+        out[phys[ok], :, (lp % g)[ok]] = meta[b][:, lp[ok]].swapaxes(0, 1)
+    return out[:, :, 0] if g == 1 else out
+
+
+def meta_past_rows(meta, seq_lens):
+    """The library's key-statistics entries past each request's logical pages (never written by a
+    build over the request's pages), flattened."""
+    meta = np.asarray(meta)
+    LP = meta.shape[2]
+    return np.concatenate([meta[b, :, min(O.n_pages(int(L)), LP):].ravel() for b, L in enumerate(seq_lens)])
+
+
 def bound_scale(inp, meta, b, h):
     """Per page: max over the group's heads of sum_c |q_c| max(|kmax_c|, |kmin_c|)."""
     w = inp.workload

@@ -141,7 +141,8 @@ def test_hier_small_meta_scores_lists_attention(name, tail):
         tail = "serial"  # coverage counts the forced pages' shares: their statistics are rebuilt first
     inp, d, st = run_case(w, tail=tail)
     meta_ref = O.hier_meta_build(inp)
-    assert np.array_equal(d.page_meta.cpu().numpy(), meta_ref), "logical page meta differs"
+    got = P.pool_meta(d.page_meta.cpu().numpy(), inp.block_table, inp.seq_lens, d.num_pool_pages)
+    assert np.array_equal(got, meta_ref), "logical page meta differs"
     rows = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
     oracle_lists = check_rows(inp, st, meta_ref, rows)
     lists = st.lists()
@@ -230,7 +231,7 @@ def test_hier_reuse_chunk_of_growing_steps():
     for b, x in enumerate(L):  # the newest logical page holds the statistics of its tokens at the final length
         lp = O.n_pages(int(x)) - 1
         phys = int(inp.block_table[b, lp // 4])
-        assert np.array_equal(got[phys, :, lp % 4], ref[phys, :, lp % 4]), b
+        assert np.array_equal(got[b, :, lp], ref[phys, :, lp % 4]), b
 
 
 def test_hier_named_workload_in_the_bench_configuration():
@@ -244,7 +245,7 @@ def test_hier_named_workload_in_the_bench_configuration():
     torch.cuda.synchronize()
     assert st.tail == "select"
     meta_ref = O.hier_meta_build(inp)
-    got = d.page_meta.cpu().numpy()
+    got = P.pool_meta(d.page_meta.cpu().numpy(), inp.block_table, inp.seq_lens, d.num_pool_pages)
     rng = np.random.default_rng(7)
     n = O.hier_n_physical(w.seq_lens[0], NP)
     for j in sorted(set(rng.choice(n, size=32, replace=False).tolist()) | {n - 1}):
@@ -284,7 +285,8 @@ def test_hier_mvar_summaries_shares_lists_attention(seq):
     inp, d, st = run_case(w)
     assert st.tail == "serial"
     stats_ref = O.hier_stats_build(inp)
-    got = d.page_meta.float().cpu().numpy()
+    got = P.pool_meta(d.page_meta.float().cpu().numpy(), inp.block_table, inp.seq_lens, d.num_pool_pages,
+                      fill=np.nan)
     built = np.isfinite(stats_ref)
     assert np.array_equal(got[built], stats_ref[built]), "page summaries differ"
     scores = st.scores.cpu().numpy()

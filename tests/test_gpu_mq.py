@@ -108,7 +108,8 @@ def test_mq_lists_union_attention(name, wide):
     w = MQ_SMALL[name].replace(max_pages_per_seq=16384) if wide else MQ_SMALL[name]
     inp, d, st = run_case(w)
     meta_ref = O.page_meta_build(inp)
-    assert np.array_equal(d.page_meta.cpu().numpy()[np.unique(inp.block_table)], meta_ref[np.unique(inp.block_table)])
+    assert np.array_equal(P.pool_meta(d.page_meta.cpu().numpy(), inp.block_table, inp.seq_lens, d.num_pool_pages),
+                          meta_ref)
     gpu_lists, ref_lists = check_token_lists(inp, st, meta_ref)
     # the union is exact integer work: it must be the union of the GPU's own token lists
     union = st.union_lists()
@@ -157,17 +158,18 @@ SCORE_ONLY = {
 
 def per_token_scores(w, d, st):
     """The token rows' scores from the single-query scorer: a descriptor of B * T rows whose block-table
-    rows repeat each request's row and whose lengths are the tokens' causal lengths (built here, in the
-    test, only to compare the two scorers)."""
+    rows and key statistics repeat each request's and whose lengths are the tokens' causal lengths (built
+    here, in the test, only to compare the two scorers)."""
     T = w.num_queries
     seq_x = torch.tensor([max(L - T + 1 + t, 0) for L in d.seq_lens.cpu().tolist() for t in range(T)],
                          dtype=torch.int32, device=d.q.device)
     bt_x = d.block_table.repeat_interleave(T, dim=0).contiguous()
+    meta_x = d.page_meta.repeat_interleave(T, dim=0).contiguous()
     desc_x = S.make_desc(w.replace(seq_lens=tuple(w.seq_lens) * T), d.num_pool_pages, st.token_cap)
     q_x = d.q.view(w.batch * T, w.num_q_heads, w.head_dim)
     out = torch.full_like(st.scores, float("nan"))
     head_lse = torch.zeros((w.batch * T, w.num_q_heads), dtype=torch.float32, device=d.q.device)
-    A.spd_page_score(desc_x, st.sel, q_x, d.page_meta, d.k_pool, d.k_scale, A.TAIL_NONE, bt_x, seq_x, d.head_kind,
+    A.spd_page_score(desc_x, st.sel, q_x, meta_x, d.k_pool, d.k_scale, A.TAIL_NONE, bt_x, seq_x, d.head_kind,
                      out, head_lse, None, 0)
     torch.cuda.synchronize()
     return out

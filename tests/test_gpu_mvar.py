@@ -46,8 +46,21 @@ def used_pages(inp):
     return np.unique(np.concatenate([inp.block_table[b, :O.n_pages(L)] for b, L in enumerate(inp.seq_lens)]))
 
 
-def stats_host(d):
-    return d.page_meta.float().cpu().numpy().astype(np.float64)
+def stats_host(d, inp):
+    """The device's page summaries in the oracle's layout (with their physical pages; others 0)."""
+    return P.pool_meta(d.page_meta.float().cpu().numpy().astype(np.float64), inp.block_table, inp.seq_lens,
+                       d.num_pool_pages)
+
+
+def last_pages(w):
+    """(request, logical page) of each non-empty request's newest page."""
+    return [(b, O.n_pages(L) - 1) for b, L in enumerate(w.seq_lens) if L > 0]
+
+
+def set_pages(d, pages, value):
+    """Overwrite the device's summaries of the given (request, logical page) pairs, every KV head."""
+    for b, p in pages:
+        d.page_meta[b, :, p] = value
 
 
 @pytest.mark.parametrize("name", list(MVAR))
@@ -60,14 +73,14 @@ def test_page_summaries_equal_the_rounded_statistics(name):
     S.build_meta(w, d)
     torch.cuda.synchronize()
     ref = O.page_stats_build(inp)
-    got = stats_host(d)
+    got = stats_host(d, inp)
     u = used_pages(inp)
     assert np.array_equal(got[u], ref[u]), f"{np.sum(got[u] != ref[u])} summary values differ"
     # the last page of each request only (span 1 from the end), over a zeroed buffer
     d.page_meta.zero_()
     S.build_summaries(w, d, None, 1)
     torch.cuda.synchronize()
-    got = stats_host(d)
+    got = stats_host(d, inp)
     last = [O.n_pages(L) - 1 for L in w.seq_lens]
     ref_last = O.page_stats_build(inp, first_page=last)
     for b, p in enumerate(last):
@@ -115,11 +128,11 @@ def test_mvar_step_scores_lists_attention(name):
     assert st.tail == "rebuild"
     # the scorer must rebuild the current pages' summaries: clear them first
     last_phys = [int(inp.block_table[b, O.n_pages(L) - 1]) for b, L in enumerate(w.seq_lens) if L > 0]
-    d.page_meta[last_phys] = 0
+    set_pages(d, last_pages(w), 0)
     st.run()
     torch.cuda.synchronize()
     stats_ref = O.page_stats_build(inp)
-    got = stats_host(d)
+    got = stats_host(d, inp)
     dyn = [h for h in range(w.num_kv_heads) if not inp.head_kind[h]]  # streaming heads keep no summaries
     assert np.array_equal(got[last_phys][:, dyn], stats_ref[last_phys][:, dyn]), "current-page summaries not rebuilt"
     oracle_lists = check_rows(inp, st, stats_ref)
@@ -144,11 +157,10 @@ def test_tail_none_scores_the_current_page_exactly_too():
     summary there changes nothing."""
     w = MVAR["f16_d128"]
     inp, d, st = run_mvar(w, tail="none")
-    last_phys = [int(inp.block_table[b, O.n_pages(L) - 1]) for b, L in enumerate(w.seq_lens) if L > 0]
-    d.page_meta[last_phys] = 7.0  # stale
+    set_pages(d, last_pages(w), 7.0)  # stale
     st.run()
     torch.cuda.synchronize()
-    assert torch.all(d.page_meta[last_phys] == 7.0)
+    assert all(torch.all(d.page_meta[b, :, p] == 7.0) for b, p in last_pages(w))
     check_rows(inp, st, O.page_stats_build(inp))
 
 
@@ -160,8 +172,7 @@ def test_first_and_current_pages_are_exact():
     st.run()
     torch.cuda.synchronize()
     before = st.scores.clone()
-    first_phys = [int(inp.block_table[b, 0]) for b in range(w.batch)]
-    d.page_meta[first_phys] = 1e30
+    set_pages(d, [(b, 0) for b in range(w.batch)], 1e30)
     st.run()
     torch.cuda.synchronize()
     assert torch.equal(st.scores, before)
@@ -183,7 +194,7 @@ def test_mvar_reuse_chunk_rebuilds_the_newest_summaries():
     torch.cuda.synchronize()
     st.reuse_step()
     torch.cuda.synchronize()
-    got = stats_host(d)
+    got = stats_host(d, inp)
     ref = O.page_stats_build(inp)
     last_phys = [int(inp.block_table[b, O.n_pages(L) - 1]) for b, L in enumerate(w.seq_lens) if L > 0]
     assert np.array_equal(got[last_phys], ref[last_phys])

@@ -74,7 +74,7 @@ def test_small_meta_scores_lists_attention(name, fused):
     w = SMALL[name]
     inp, d, st = run_case(w, fused=fused)
     meta_ref = O.page_meta_build(inp)
-    meta_gpu = d.page_meta.cpu().numpy()
+    meta_gpu = P.pool_meta(d.page_meta.cpu().numpy(), inp.block_table, inp.seq_lens, d.num_pool_pages)
     used = np.unique(np.concatenate([inp.block_table[b, :O.n_pages(L)] for b, L in enumerate(w.seq_lens)]))
     assert np.array_equal(meta_gpu[used], meta_ref[used]), "page meta differs"
 
@@ -192,10 +192,12 @@ def test_all_heads_tail_rebuild_updates_only_last_pages():
     d.page_meta.fill_(sentinel)
     st.refresh_tail()
     torch.cuda.synchronize()
-    got = d.page_meta.cpu().numpy()
+    raw = d.page_meta.cpu().numpy()
+    got = P.pool_meta(raw, inp.block_table, inp.seq_lens, d.num_pool_pages, fill=sentinel)
     first = [max(O.n_pages(L) - 1, 0) for L in w.seq_lens]
     ref = O.page_meta_build(inp, meta=np.full(got.shape, sentinel, dtype=got.dtype), first_page=first)
     assert np.array_equal(got, ref)
+    assert np.all(P.meta_past_rows(raw, w.seq_lens) == sentinel)  # entries past each request untouched
 
 
 LONG_ROWS = {  # rows long enough for every selector geometry (2, 8, 32 and 64 key slots per lane)
@@ -295,12 +297,12 @@ def test_step_tail_modes_rebuild_the_last_page(fused, tail):
         for b, L in enumerate(w.seq_lens):
             n = O.n_pages(L)
             for p in range(n):
-                phys = int(inp.block_table[b, p])
                 for h in range(w.num_kv_heads):
                     if p == n - 1 and (tail != "rebuild" or not inp.head_kind[h]):
-                        assert np.array_equal(got[phys, h], full[phys, h]), (kv, b, p, h)
+                        assert np.array_equal(got[b, h, p], full[b, h, p]), (kv, b, p, h)
                     else:
-                        assert np.all(got[phys, h] == 3.0), (kv, b, p, h)
+                        assert np.all(got[b, h, p] == 3.0), (kv, b, p, h)
+        assert np.all(P.meta_past_rows(got, w.seq_lens) == 3.0), kv
 
 
 @pytest.mark.parametrize("mode", ["topk", "coverage"])
@@ -423,7 +425,7 @@ def test_reusable_selection_serves_a_chunk_of_growing_steps(reuse):
     got = d.page_meta.cpu().numpy()
     for b, x in enumerate(L):
         phys = int(inp.block_table[b, last[b]])
-        assert np.array_equal(got[phys], ref[phys]), b
+        assert np.array_equal(got[b, :, last[b]], ref[phys]), b
 
 
 def test_deterministic_bitwise():

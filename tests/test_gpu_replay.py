@@ -61,7 +61,7 @@ def check_meta(at, d, heads=None):
     """Every page of every request holds the statistics of its keys at the current lengths (for the
     given KV heads; all by default)."""
     ref = O.page_meta_build(at)
-    got = d.page_meta.cpu().numpy()
+    got = P.pool_meta(d.page_meta.cpu().numpy(), at.block_table, at.seq_lens, d.num_pool_pages)
     hs = list(range(got.shape[1])) if heads is None else list(heads)
     for b, L in enumerate(at.seq_lens):
         phys = at.block_table[b, :O.n_pages(L)].astype(np.int64)

@@ -61,7 +61,7 @@ def check_named(name, fused):
                     lo, hi = O.round_bf16(mu), O.round_bf16(var)
                 else:
                     lo, hi = O.to_stored_meta(*O.page_key_minmax(keys, valid), w.kv_dtype)
-                assert np.array_equal(meta_gpu[phys, h, 0], lo) and np.array_equal(meta_gpu[phys, h, 1], hi), \
+                assert np.array_equal(meta_gpu[b, h, p, 0], lo) and np.array_equal(meta_gpu[b, h, p, 1], hi), \
                     (b, p, h)
 
     # 2. every row: scores, lists (tie rule), attention over the GPU's own lists
