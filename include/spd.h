@@ -217,10 +217,11 @@ typedef struct spd_select_params {
  * exits at once.  J is fixed by (B, Hkv) so a captured graph serves every list length.
  *
  * balanced != 0 plans the whole step at once instead (for skewed list lengths): with T the
- * total listed pages of all rows and n_max the longest list, every chunk holds
- * c = max(min_chunk, ceil(T / N_T), ceil(n_max / 1024)) pages, row r has m_r = ceil(n_r / c)
+ * total listed pages of all rows, n_max the longest list and z the number of rows with a
+ * non-empty list, every chunk holds c = max(min_chunk, ceil(T / N'), ceil(n_max / 1024))
+ * pages, where N' = N_T - z when N_T > z and N' = N_T otherwise; row r has m_r = ceil(n_r / c)
  * chunks, chunks are numbered row by row, and block k of the N_T + B * Hkv blocks processes
- * chunk k (sum m_r <= N_T + B * Hkv).  Every block derives the plan from the list lengths on
+ * chunk k (sum m_r < N_T when N_T > z, and sum m_r <= N_T + B * Hkv always).  Every block derives the plan from the list lengths on
  * the device, so a captured graph still serves every list length.  min_blocks_per_row is
  * not used; N_T >= 1. */
 typedef struct spd_plan_params {

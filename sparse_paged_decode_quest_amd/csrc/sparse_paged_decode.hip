@@ -214,17 +214,23 @@ __device__ __forceinline__ int row_units(const int32_t* list_len, int r, int max
 __device__ __forceinline__ int balanced_chunk(const int32_t* list_len, int rows, int max_list, int C, int NT, int lgs) {
   const int lane = threadIdx.x % kWave;
   unsigned long long tot = 0;
-  uint32_t nmax = 0;
+  uint32_t nmax = 0, nz = 0;
   for (int r0 = 0; r0 < rows; r0 += kWave) {
     const int r = r0 + lane;
     const int n = r < rows ? row_units(list_len, r, max_list, lgs) : 0;
     tot += (unsigned long long)n;
     nmax = max(nmax, (uint32_t)n);
+    nz += n > 0 ? 1u : 0u;
   }
   tot = wave_sum(tot);
   nmax = wave_max(nmax);
+  nz = (uint32_t)wave_sum((unsigned long long)nz);
+  // each of the nz non-empty rows rounds its chunk count up by less than one, so with
+  // c >= T / (N_T - nz) the chunks number fewer than T / c + nz <= N_T: the plan fills the N_T
+  // blocks meant to be resident at once and no chunk waits for a second round
+  const unsigned long long slots = (unsigned long long)NT > nz ? (unsigned long long)NT - nz : (unsigned long long)NT;
   unsigned long long c = (unsigned long long)C;
-  c = max(c, (tot + (unsigned long long)NT - 1) / (unsigned long long)NT);
+  c = max(c, (tot + slots - 1) / slots);
   c = max(c, (unsigned long long)((nmax + kMaxChunks - 1) / kMaxChunks));
   return (int)c;
 }

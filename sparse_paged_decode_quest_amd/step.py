@@ -27,11 +27,13 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "fp8": torch.uint8}
 @dataclasses.dataclass
 class Plan:
     """Self-planned split constants (Moira, section 3.3, Eq. 4), re-chosen for 16-token pages
-    and 256 compute units: a chunk of at least 4 pages (one per wave of a block) and at least
-    512 blocks over the grid.  ``balanced`` splits the step's total listed pages evenly instead
-    of each row into J chunks (for skewed list lengths; see spd_plan_params)."""
+    and 256 compute units: a chunk of at least 4 pages (one per wave of a block), at least 8
+    blocks per row and at least 512 blocks over the grid -- the blocks that two waves per SIMD
+    keep resident at once, so rows of a batch of 8 requests are not split into a second round of
+    blocks.  ``balanced`` splits the step's total listed pages evenly instead of each row into J
+    chunks (for skewed list lengths; see spd_plan_params)."""
     min_chunk: int = 4
-    min_blocks_per_row: int = 16
+    min_blocks_per_row: int = 8
     min_grid_blocks: int = 512
     balanced: bool = False
 
@@ -168,7 +170,7 @@ class DecodeStep:
             raise ValueError("tail='select' needs the separate selector (fused=False)")
         self.w, self.d = w, d
         # coverage lists range from the forced pages to the whole row: split the step evenly
-        self.plan = plan or (Plan(balanced=True, min_grid_blocks=1024) if w.mode == "coverage" else Plan())
+        self.plan = plan or (Plan(balanced=True) if w.mode == "coverage" else Plan())
         self.fused = fused
         self.tail = tail
         self.tail_mode = {"none": A.TAIL_NONE, "select": A.TAIL_SKIP, "side": A.TAIL_SKIP, "serial": A.TAIL_NONE,

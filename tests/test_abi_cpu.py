@@ -283,10 +283,13 @@ def test_plan_grid_formula(lib):
     for _ in range(300):
         rows, NT, C = int(rng.integers(1, 200)), int(rng.integers(1, 5000)), int(rng.integers(1, 40))
         n = rng.integers(0, 70000, size=rows) * (rng.random(rows) < 0.8)
-        T, nmax = int(n.sum()), int(n.max())
-        c = max(C, -(-T // NT), -(-nmax // 1024))
+        T, nmax, z = int(n.sum()), int(n.max()), int((n > 0).sum())
+        slots = NT - z if NT > z else NT
+        c = max(C, -(-T // slots), -(-nmax // 1024))
         m = -(-n // c)
         assert int(m.sum()) <= NT + rows and int(m.max()) <= 1024
+        if NT > z:
+            assert int(m.sum()) < NT  # one round of the N_T blocks
     # chunk sizes: every chunk holds at least C pages, at most J chunks, all pages covered once
     rng = np.random.default_rng(0)
     for _ in range(500):
