@@ -276,6 +276,8 @@ def main():
     ap.add_argument("--fused", action="store_true", help="scorer and selector in one launch")
     ap.add_argument("--merged", action="store_true", help="decode and merge in one launch (last-block merge)")
     ap.add_argument("--no-gate", action="store_true", help="top-K selection without the LiteTopK gate")
+    ap.add_argument("--tail", default="auto", choices=("auto", "none", "select", "side", "serial", "rebuild"),
+                    help="how the newest page's key statistics are rebuilt (DecodeStep's tail)")
     ap.add_argument("--plan", default=None,
                     help="self-planning constants C,N_J,N_T[,balanced] (default: the step's for the workload)")
     ap.add_argument("--phase-only", default=None,
@@ -328,7 +330,8 @@ def main():
     if w.num_queries > 1:
         return bench_mq(args, w, inp, base, plan, gen_s)
     gated = False if args.no_gate else None
-    probe = S.DecodeStep(w, base, plan=plan, fused=args.fused, merged=args.merged, gated=gated)
+    probe = S.DecodeStep(w, base, plan=plan, fused=args.fused, merged=args.merged, gated=gated,
+                             tail=args.tail)
     probe.run()
     torch.cuda.synchronize()
     ab0 = algorithmic_bytes(w, probe.list_len.cpu().numpy(), inp.head_kind)
@@ -344,7 +347,8 @@ def main():
                                       block_table=clone(base.block_table), seq_lens=clone(base.seq_lens),
                                       head_kind=base.head_kind.copy(), page_meta=clone(base.page_meta))
                        for _ in range(R - 1)]
-    steps = [probe] + [S.DecodeStep(w, d, plan=plan, fused=args.fused, merged=args.merged, gated=gated)
+    steps = [probe] + [S.DecodeStep(w, d, plan=plan, fused=args.fused, merged=args.merged, gated=gated,
+                             tail=args.tail)
                        for d in layers[1:]]
     for st in steps:
         st.run()
@@ -501,7 +505,8 @@ def main():
                                         block_table=clone(d0.block_table), seq_lens=clone(d0.seq_lens),
                                         head_kind=d0.head_kind.copy(), page_meta=clone(d0.page_meta))
                          for _ in range(R - 1)]
-            st_s = [S.DecodeStep(ws, d, plan=plan, fused=args.fused, merged=args.merged, gated=gated) for d in ds]
+            st_s = [S.DecodeStep(ws, d, plan=plan, fused=args.fused, merged=args.merged, gated=gated,
+                             tail=args.tail) for d in ds]
             saved = steps[:]
             steps[:] = st_s  # `timed` replays the layers in `steps`
             timed(whole, R, R)

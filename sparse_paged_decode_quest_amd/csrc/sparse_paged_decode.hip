@@ -396,6 +396,9 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   const int b = row / a.num_kv_heads;
   const int h = row % a.num_kv_heads;
   const size_t qrow = (size_t)b * a.num_q_heads + (size_t)h * kGq;  // first query head of the group
+  // the request's length, requested as soon as the row is known (per-row plan: with the list length
+  // and the list entries, so no round trip of its own comes before the first K / V loads)
+  const int len = a.seq_lens[b];
 
   const int32_t* list = a.page_list + (size_t)row * a.max_list;
   const int32_t* plist = a.page_phys ? a.page_phys + (size_t)row * a.max_list : nullptr;
@@ -408,11 +411,13 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   // no branch around each read
   const __amdgpu_buffer_rsrc_t list_r = make_rsrc(list, (uint32_t)a.max_list * 4u);
   const __amdgpu_buffer_rsrc_t plist_r = make_rsrc(plist, plist ? (uint32_t)a.max_list * 4u : 0u);
+  // Nothing here waits for these loads: the queries and the list length are requested behind them.
+  // Only lanes below the batch's page count use their entry, and those pages lie below the list
+  // length, so their entries are inside the list.
   if (!a.balanced) {
     const int e = (spec_i0 + wave + 4 * lane) >> a.lgs;
     spec_lp = buf_load_i32(list_r, (uint32_t)e * 4u);
     spec_lph = buf_load_i32(plist_r, (uint32_t)e * 4u);
-    if (e >= a.max_list) spec_lp = -1;
   }
   typename T::Q q;
   T::load_q(q, a.q, qrow * D, quarter);
@@ -430,7 +435,6 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   }
   const int i0 = j * c;
   const int i1 = min(n, i0 + c);
-  const int len = a.seq_lens[b];
   const int n_b = row_logical_pages(len, a.max_pages, a.lgs);   // 16-token pages of the request
   const int n_phys = row_phys_pages(len, a.max_pages, a.lgs);   // list entries must be below this
   const int sub_mask = (1 << a.lgs) - 1;
