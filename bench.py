@@ -688,7 +688,9 @@ def bench_mq(args, w, inp, base, plan, gen_s):
     from sparse_paged_decode_quest_amd import step as S
 
     T = w.num_queries
-    probe = S.MQDecodeStep(w, base, plan=plan, gated=not args.no_gate)
+    if args.tail not in ("auto", "select", "serial"):
+        raise SystemExit("several query tokens: --tail must be auto, select or serial")
+    probe = S.MQDecodeStep(w, base, plan=plan, gated=not args.no_gate, tail=args.tail)
     probe.run()
     torch.cuda.synchronize()
     d = w.head_dim
@@ -697,10 +699,11 @@ def bench_mq(args, w, inp, base, plan, gen_s):
     token_len = probe.token_len.cpu().numpy()
     # algorithmic bytes: the dynamic rows' key boxes, read once for the T tokens (one scan scores every
     # token row); the union pages' K / V, read once for the T tokens; queries, outputs, block-table rows;
-    # the rebuilt last two pages
+    # the rebuilt last two pages (not scanned when the scorer skips them: the "select" tail)
     kvb = {"f16": 2, "fp8": 1}[w.kv_dtype]
     page_kv = 16 * d * kvb * 2 + (16 * 2 * 2 if w.kv_dtype == "fp8" else 0)  # K and V (+ fp16 scales)
-    meta = int(w.n_pages.sum()) * dyn * 2 * d * 2
+    skipped = int(np.minimum(w.n_pages, 2).sum()) if probe.tail == "select" else 0
+    meta = (int(w.n_pages.sum()) - skipped) * dyn * 2 * d * 2
     kv = int(union_len.sum()) * page_kv
     per_token_kv = int(token_len.sum()) * page_kv  # what T independent decodes would read
     q = w.batch * T * w.num_q_heads * d * 2
@@ -720,7 +723,7 @@ def bench_mq(args, w, inp, base, plan, gen_s):
                                       block_table=base.block_table.clone(),
                                       seq_lens=base.seq_lens.clone(), head_kind=base.head_kind.copy(),
                                       page_meta=base.page_meta.clone()) for _ in range(R - 1)]
-    steps = [probe] + [S.MQDecodeStep(w, x, plan=plan, gated=not args.no_gate) for x in layers[1:]]
+    steps = [probe] + [S.MQDecodeStep(w, x, plan=plan, gated=not args.no_gate, tail=args.tail) for x in layers[1:]]
     for st in steps:
         st.run()
     torch.cuda.synchronize()
@@ -750,9 +753,10 @@ def bench_mq(args, w, inp, base, plan, gen_s):
     whole = (lambda st, s: st.run(s))
     timed(whole, max(args.warmup, R))
     step_s = timed(whole, args.steps)
-    phases = {"tail": lambda st, s: st.refresh_tail(s), "score": lambda st, s: st.score(s),
-              "select_only": lambda st, s: st.select_only(s), "union": lambda st, s: st.union(s),
-              "attend": lambda st, s: st.attend(s)}
+    phases = {"score": lambda st, s: st.score(s), "select_only": lambda st, s: st.select_only(s),
+              "union": lambda st, s: st.union(s), "attend": lambda st, s: st.attend(s)}
+    if probe.tail == "serial":
+        phases = {"tail": lambda st, s: st.refresh_tail(s), **phases}
     phase_us = {}
     for name, fn in phases.items():
         timed(fn, R)
@@ -761,7 +765,7 @@ def bench_mq(args, w, inp, base, plan, gen_s):
     if probe.gated:  # the same step with the token rows' gates off (each layer repeats its queries)
         rows = w.batch * T * w.num_kv_heads
         gp = S.gate_paths(probe.topk_state, rows)
-        ung = {id(a): S.MQDecodeStep(w, x, plan=plan, gated=False) for a, x in zip(steps, layers)}
+        ung = {id(a): S.MQDecodeStep(w, x, plan=plan, gated=False, tail=args.tail) for a, x in zip(steps, layers)}
         for st in ung.values():
             st.run()
         ug = {}
@@ -805,7 +809,8 @@ def bench_mq(args, w, inp, base, plan, gen_s):
                    "heads": f"Hq{w.num_q_heads}/Hkv{w.num_kv_heads}", "head_dim": d, "page": w.page_size,
                    "kv_dtype": w.kv_dtype, "mode": w.mode, "budget_pages": w.budget_pages,
                    "streaming_kv_heads": len(w.streaming_heads), "layers_rotated": R, "graph": True,
-                   "plan": [probe.plan.min_chunk, probe.plan.min_blocks_per_row, probe.plan.min_grid_blocks, 0]},
+                   "plan": [probe.plan.min_chunk, probe.plan.min_blocks_per_row, probe.plan.min_grid_blocks, 0],
+                   "tail": probe.tail},
         "step_us": round(step_s * 1e6, 3), "tokens_per_s": round(w.batch * T / step_s, 1),
         "bytes_per_step": ab, "kv_bytes_without_union": per_token_kv, "frac_of_peak": round(ab["total"] / step_s / 1e12 / PEAK_HBM_TBS, 4),
         "beta_copy_TBs": round(beta, 3), "phase_us": {k: round(v, 3) for k, v in phase_us.items()},

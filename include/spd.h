@@ -104,7 +104,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 16
+#define SPD_ABI_VERSION 17
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
@@ -421,12 +421,18 @@ int spd_sparse_paged_decode_noalloc(const spd_desc* desc, const spd_plan_params*
  * [B * T, Hkv, max_pages_per_seq] f32; row b T + t) for the pages of token t's length
  * L - T + 1 + t, bit for bit what spd_page_score with SPD_TAIL_NONE writes on a descriptor of B * T
  * rows whose block-table rows and page_meta rows repeat each request's T times; later entries are
- * not written.  The statistics of the pages the draft tokens are in must be
- * current (spd_page_meta_build over the last pages first).  sel must be top-K with the bound
- * estimator (else SPD_ERR_UNSUPPORTED); errors otherwise as spd_page_score and spd_page_list_union. */
+ * not written.  tail_mode SPD_TAIL_NONE scores every page: the statistics of the pages the draft
+ * tokens are in must then be current (spd_page_meta_build over the last pages first).
+ * SPD_TAIL_SKIP (needs sel->n_local >= 2, else SPD_ERR_INVALID_ARG) reads no statistics of the
+ * request's last two pages and writes -inf for them in every token row that holds them: with at
+ * most 4 draft tokens each token's last page is one of the two, so both are in every token's local
+ * window or past its length, and the selection takes them without their scores; their statistics
+ * may then be rebuilt beside the selection (spd_page_select_mq with page_meta).  Other tail modes
+ * return SPD_ERR_INVALID_ARG.  sel must be top-K with the bound estimator (else
+ * SPD_ERR_UNSUPPORTED); errors otherwise as spd_page_score and spd_page_list_union. */
 int spd_page_score_mq(const spd_desc* desc, int32_t num_tokens, const spd_select_params* sel, const void* q,
-                      const void* page_meta, const int32_t* block_table, const int32_t* seq_lens,
-                      const uint8_t* head_kind, float* scores, void* stream);
+                      const void* page_meta, int32_t tail_mode, const int32_t* block_table,
+                      const int32_t* seq_lens, const uint8_t* head_kind, float* scores, void* stream);
 
 /* Page lists of the T token rows of every request (top-K, bound estimator): row (b T + t, h) is
  * token t of request b, selected as a single query of length L - T + 1 + t would be (forced sink and
@@ -438,13 +444,19 @@ int spd_page_score_mq(const spd_desc* desc, int32_t num_tokens, const spd_select
  * [B * T, Hkv, token_max_list]) and token_len (device, [B * T, Hkv]) receive the lists, ascending;
  * token_phys (device, same shape as token_list, may be NULL) the physical page of each entry, read
  * from block_table (then required).  head_kind (host): streaming heads get their static table for
- * the token's length.  Returns SPD_ERR_INVALID_ARG when token_max_list cannot hold the longest list
+ * the token's length.  When page_meta (device, may be NULL) is set, workgroups beside the selection
+ * rebuild the key min / max of each request's last two logical pages (the ones the draft tokens are
+ * in), every KV head, from k_pool (and k_scale for fp8 pools) into page_meta -- what
+ * spd_page_meta_build does with span 2 (LServe, "Key statistics storage and updating"); block_table
+ * is then required, and the scores must not depend on those statistics (spd_page_score_mq with
+ * SPD_TAIL_SKIP).  Returns SPD_ERR_INVALID_ARG when token_max_list cannot hold the longest list
  * (as spd_page_select's max_list), SPD_ERR_UNSUPPORTED for COVERAGE or MVAR; otherwise errors as
  * spd_page_select. */
 int spd_page_select_mq(const spd_desc* desc, int32_t num_tokens, int32_t token_max_list,
                        const spd_select_params* sel, const float* scores, const int32_t* seq_lens,
-                       const uint8_t* head_kind, const int32_t* block_table, int32_t* token_list,
-                       int32_t* token_phys, int32_t* token_len, void* stream);
+                       const uint8_t* head_kind, const int32_t* block_table, const void* k_pool,
+                       const uint16_t* k_scale, void* page_meta, int32_t* token_list, int32_t* token_phys,
+                       int32_t* token_len, void* stream);
 
 /* Union of the T token lists of every (request, KV head) row (LiteDSA's candidate union).
  * desc describes the B requests (max_list: the union's capacity, at least

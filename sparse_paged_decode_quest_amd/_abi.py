@@ -83,8 +83,8 @@ def lib():
         L.spd_sparse_paged_decode_noalloc.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v]
         L.spd_sparse_paged_decode_merged.argtypes = [D, P, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v, v, v]
         L.spd_page_list_union.argtypes = [D, c_int32, c_int32, v, v, v, v, v, v, v, v, v, v]
-        L.spd_page_score_mq.argtypes = [D, c_int32, S, v, v, v, v, POINTER(c_uint8), v, v]
-        L.spd_page_select_mq.argtypes = [D, c_int32, c_int32, S, v, v, POINTER(c_uint8), v, v, v, v, v]
+        L.spd_page_score_mq.argtypes = [D, c_int32, S, v, v, c_int32, v, v, POINTER(c_uint8), v, v]
+        L.spd_page_select_mq.argtypes = [D, c_int32, c_int32, S, v, v, POINTER(c_uint8), v, v, v, v, v, v, v, v]
         L.spd_sparse_paged_decode_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v, v, v, v, v, v, c_float, v, v, v, v,
                                                  v]
         L.spd_lse_merge_mq.argtypes = [D, c_int32, P, v, v, v, v, v, v]
@@ -220,18 +220,20 @@ def spd_lse_merge(desc, plan, part_o, part_lse, list_len, out, out_lse, stream=N
                                _ptr(list_len), _ptr(out), _ptr(out_lse), _stream(stream)), "spd_lse_merge")
 
 
-def spd_page_score_mq(desc, num_tokens, sel, q, page_meta, block_table, seq_lens, head_kind, scores, stream=None):
+def spd_page_score_mq(desc, num_tokens, sel, q, page_meta, tail_mode, block_table, seq_lens, head_kind, scores,
+                      stream=None):
     _check(lib().spd_page_score_mq(ctypes.byref(desc), int(num_tokens), ctypes.byref(sel), _ptr(q), _ptr(page_meta),
-                                   _ptr(block_table), _ptr(seq_lens), _heads(head_kind), _ptr(scores),
-                                   _stream(stream)),
+                                   int(tail_mode), _ptr(block_table), _ptr(seq_lens), _heads(head_kind),
+                                   _ptr(scores), _stream(stream)),
            "spd_page_score_mq")
 
 
-def spd_page_select_mq(desc, num_tokens, token_max_list, sel, scores, seq_lens, head_kind, block_table, token_list,
-                       token_phys, token_len, stream=None):
+def spd_page_select_mq(desc, num_tokens, token_max_list, sel, scores, seq_lens, head_kind, block_table, k_pool,
+                       k_scale, page_meta, token_list, token_phys, token_len, stream=None):
     _check(lib().spd_page_select_mq(ctypes.byref(desc), int(num_tokens), int(token_max_list), ctypes.byref(sel),
                                     _ptr(scores), _ptr(seq_lens), _heads(head_kind), _ptr(block_table),
-                                    _ptr(token_list), _ptr(token_phys), _ptr(token_len), _stream(stream)),
+                                    _ptr(k_pool), _ptr(k_scale), _ptr(page_meta), _ptr(token_list),
+                                    _ptr(token_phys), _ptr(token_len), _stream(stream)),
            "spd_page_select_mq")
 
 

@@ -30,7 +30,16 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(Scor
 
   const int len = a.seq_lens[b];
   const int n = row_pages(len, a.max_pages);  // pages of the last token's row
-  if (p_begin >= n) return;                   // uniform over the block
+  // SPD_TAIL_SKIP: the request's last two pages are not scored.  Each token row's last page is one of
+  // them (T <= 4 draft tokens lie within 16 positions), so both are in every token's local window of at
+  // least two pages or past the token's length: block 0 writes -inf for them where a token sees them.
+  const int n_scan = a.tail_mode == SPD_TAIL_SKIP ? max(n - 2, 0) : n;
+  if (n_scan < n && blk == 0 && (int)threadIdx.x < 2 * num_tokens) {
+    const int t = (int)threadIdx.x >> 1, p = n_scan + ((int)threadIdx.x & 1);
+    if (p < row_pages(len - num_tokens + 1 + t, a.max_pages))
+      a.scores[(((size_t)b * num_tokens + t) * a.num_kv_heads + h) * a.max_pages + p] = -INFINITY;
+  }
+  if (p_begin >= n_scan) return;  // uniform over the block
 
   const int lane = threadIdx.x % kWave;
   const int sub = lane % LPP;
@@ -51,7 +60,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(Scor
     T::load_q(qr[t], a.q, (((size_t)b * num_tokens + tt) * a.num_q_heads + (size_t)h * kG) * D, c0);
   }
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) ok[it] = pg[it] < n && raw[it] >= 0 && raw[it] < a.num_pool_pages;
+  for (int it = 0; it < ITERS; ++it) ok[it] = pg[it] < n_scan && raw[it] >= 0 && raw[it] < a.num_pool_pages;
   if constexpr (LPP == 16 && kMqScoreMaxTokens == 4) {
     // The 16 sums (token t, head g) of a page live spread over its 16 lanes.  A reduce-scatter hands
     // lane l the whole sum of k = l = 4 t + g: at each level (lane bit 1, 2, 4, 8) a lane keeps the half
@@ -59,7 +68,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(Scor
     // half.  The pairs added are the butterfly's (group_sum), so the sums are bit for bit the same.
     const bool b0 = sub & 1, b1 = sub & 2, b2 = sub & 4, b3 = sub & 8;
     const int t_l = sub >> 2;
-    const int n_tl = row_pages(len - num_tokens + 1 + t_l, a.max_pages);
+    const int n_tl = min(row_pages(len - num_tokens + 1 + t_l, a.max_pages), n_scan);
     float* sc_l = a.scores + (((size_t)b * num_tokens + min(t_l, num_tokens - 1)) * a.num_kv_heads + h) * a.max_pages;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
@@ -102,7 +111,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(Scor
 #pragma unroll
   for (int t = 0; t < kMqScoreMaxTokens; ++t) {
     if (t >= num_tokens) break;
-    const int n_t = row_pages(len - num_tokens + 1 + t, a.max_pages);
+    const int n_t = min(row_pages(len - num_tokens + 1 + t, a.max_pages), n_scan);
     float* sc_row = a.scores + (((size_t)b * num_tokens + t) * a.num_kv_heads + h) * a.max_pages;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {

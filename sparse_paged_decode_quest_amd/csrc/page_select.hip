@@ -48,15 +48,20 @@ __device__ __forceinline__ void load_row_keys(const float* sc, const int32_t* le
   }
 }
 
-// Tail workgroup k: wave w rebuilds (request, KV head) item k * NW + w.
+// Tail workgroup k: wave w rebuilds (request, KV head, page) item k * NW + w: the request's last
+// logical page, or its last tail.span pages when span > 1 (several query tokens per step).
+__device__ __forceinline__ int tail_span(const SelectArgs& a) { return a.tail.span > 1 ? a.tail.span : 1; }
+
 template <int NW>
 __device__ __forceinline__ void rebuild_tail_pages(const SelectArgs& a, int k) {
+  const int span = tail_span(a);
   const int item = k * NW + (int)(threadIdx.x / kWave);
-  if (item >= a.batch * a.num_kv_heads) return;
-  const int b = item / a.num_kv_heads, h = item % a.num_kv_heads;
+  if (item >= a.batch * a.num_kv_heads * span) return;
+  const int s = item % span, bh = item / span;
+  const int b = bh / a.num_kv_heads, h = bh % a.num_kv_heads;
   const int len = a.seq_lens[b];
   const int n = row_logical_pages(len, a.max_pages, a.tail.lgs);  // the newest token's logical page
-  if (n > 0) build_page_meta_rt(a.tail, b, n - 1, h, len);
+  if (n - 1 - s >= 0) build_page_meta_rt(a.tail, b, n - 1 - s, h, len);
 }
 
 // Row blockIdx.x = (b T + t) Hkv + h of a step with T = a.num_tokens query tokens per request: token t of
@@ -159,7 +164,7 @@ int launch_page_select(const SelectArgs& a, hipStream_t stream) {
   SelectGeometry g;
   if (!select_geometry(a.max_pages, g)) return SPD_ERR_UNSUPPORTED;
   const int rows = a.batch * a.num_tokens * a.num_kv_heads;
-  const int tail_blocks = a.tail.meta ? (a.batch * a.num_kv_heads + g.nw - 1) / g.nw : 0;
+  const int tail_blocks = a.tail.meta ? (a.batch * a.num_kv_heads * (a.tail.span > 1 ? a.tail.span : 1) + g.nw - 1) / g.nw : 0;
   const dim3 grid((unsigned)(rows + tail_blocks)), block(g.nw * kWave);
   const bool cov = a.mode == SPD_SELECT_COVERAGE;
 #define SPD_SEL_CASE(NW, KPL)                                                                          \

@@ -643,12 +643,14 @@ static int check_mq(const spd_desc* d, int32_t num_tokens) {
 }
 
 int spd_page_score_mq(const spd_desc* desc, int32_t num_tokens, const spd_select_params* sel, const void* q,
-                      const void* page_meta, const int32_t* block_table, const int32_t* seq_lens,
+                      const void* page_meta, int32_t tail_mode, const int32_t* block_table, const int32_t* seq_lens,
                       const uint8_t* head_kind, float* scores, void* stream) {
   int rc = check_mq(desc, num_tokens);
   if (rc) return rc;
   if ((rc = check_sel(desc, sel))) return rc;
   if (sel->mode != SPD_SELECT_TOPK || is_mvar(sel)) return SPD_ERR_UNSUPPORTED;
+  // skipping the last two pages needs them forced for every token: a local window of two pages
+  if (tail_mode != SPD_TAIL_NONE && (tail_mode != SPD_TAIL_SKIP || sel->n_local < 2)) return SPD_ERR_INVALID_ARG;
   spd::HeadList dyn, strm;
   uint64_t mask;
   if ((rc = head_lists(desc, head_kind, dyn, strm, mask))) return rc;
@@ -656,14 +658,15 @@ int spd_page_score_mq(const spd_desc* desc, int32_t num_tokens, const spd_select
   if (!q || !page_meta || !block_table || !seq_lens || !scores) return SPD_ERR_INVALID_ARG;
   spd::ScoreArgs a = score_args(desc, sel, q, page_meta, block_table, seq_lens, dyn, score_ppb(desc, sel, dyn.count));
   a.scores = scores;
-  a.tail_mode = SPD_TAIL_NONE;
+  a.tail_mode = tail_mode;
   return launched(spd::launch_mq_page_score(a, num_tokens, desc->head_dim, desc->kv_dtype, (hipStream_t)stream));
 }
 
 int spd_page_select_mq(const spd_desc* desc, int32_t num_tokens, int32_t token_max_list,
                        const spd_select_params* sel, const float* scores, const int32_t* seq_lens,
-                       const uint8_t* head_kind, const int32_t* block_table, int32_t* token_list,
-                       int32_t* token_phys, int32_t* token_len, void* stream) {
+                       const uint8_t* head_kind, const int32_t* block_table, const void* k_pool,
+                       const uint16_t* k_scale, void* page_meta, int32_t* token_list, int32_t* token_phys,
+                       int32_t* token_len, void* stream) {
   int rc = check_mq(desc, num_tokens);
   if (rc) return rc;
   if (token_max_list < 1) return SPD_ERR_INVALID_ARG;
@@ -681,9 +684,15 @@ int spd_page_select_mq(const spd_desc* desc, int32_t num_tokens, int32_t token_m
   if (desc->batch == 0) return SPD_OK;
   if (!seq_lens || !token_list || !token_len || (dyn.count > 0 && !scores)) return SPD_ERR_INVALID_ARG;
   if (token_phys && !block_table) return SPD_ERR_INVALID_ARG;
+  if (page_meta && (!block_table || !k_pool || (desc->kv_dtype == SPD_DTYPE_FP8_E4M3FN && !k_scale)))
+    return SPD_ERR_INVALID_ARG;
   spd::SelectArgs a = select_args(&tok, sel, seq_lens, block_table, token_list, token_phys, token_len, nullptr, mask);
   a.scores = scores;
   a.num_tokens = num_tokens;
+  if (page_meta) {  // the last two pages of every request, all KV heads, beside the selection
+    a.tail = meta_args(desc, k_pool, k_scale, block_table, seq_lens, page_meta);
+    a.tail.span = 2;
+  }
   a.gate = gate_of(sel, (int64_t)desc->batch * num_tokens * desc->num_kv_heads);  // rows of the token rows
   return launched(spd::launch_page_select(a, (hipStream_t)stream));
 }

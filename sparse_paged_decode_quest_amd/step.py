@@ -321,10 +321,22 @@ class MQDecodeStep:
     [B, T, Hq, d]; ``out`` is [B, T, Hq, d] and ``out_lse`` [B, T, Hq].
     """
 
-    def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, gated: bool = True):
+    def __init__(self, w: Workload, d: DeviceInputs, plan: Plan | None = None, gated: bool = True,
+                 tail: str = "auto"):
         T = w.num_queries
         if T < 2 or w.mode != "topk" or w.page_size != 16:
             raise ValueError("several query tokens: top-K over 16-token pages, T >= 2")
+        # "select": the scorer skips each request's last two pages (in every token's local window of
+        # at least two pages) and the selector's spare workgroups rebuild their statistics; "serial":
+        # a rebuild launch before a scorer that reads them; "auto" picks "select" where it applies
+        skippable = w.n_local >= 2
+        if tail == "auto":
+            tail = "select" if skippable else "serial"
+        if tail not in ("select", "serial"):
+            raise ValueError("tail must be 'auto', 'select' or 'serial'")
+        if tail == "select" and not skippable:
+            raise ValueError("tail='select' needs a local window of at least two pages")
+        self.tail = tail
         self.w, self.d, self.T = w, d, T
         self.plan = plan or Plan()
         self.pp = self.plan.params()
@@ -361,18 +373,22 @@ class MQDecodeStep:
         A.spd_page_meta_build(self.desc, self.d.k_pool, self.d.k_scale, self.d.block_table, self.d.seq_lens, None, 2,
                               self.d.page_meta, stream)
 
-    def score(self, stream=None):
-        """Page scores of every token row (statistics over all cached keys): one scan that reads each
-        key box once for the T tokens."""
+    def score(self, stream=None, tail_mode=None):
+        """Page scores of every token row: one scan that reads each key box once for the T tokens (with
+        the "select" tail, the request's last two pages are not scored)."""
         d = self.d
-        A.spd_page_score_mq(self.desc, self.T, self.sel, d.q, d.page_meta, d.block_table, d.seq_lens, d.head_kind,
-                            self.scores, stream)
+        tm = (A.TAIL_SKIP if self.tail == "select" else A.TAIL_NONE) if tail_mode is None else tail_mode
+        A.spd_page_score_mq(self.desc, self.T, self.sel, d.q, d.page_meta, tm, d.block_table, d.seq_lens,
+                            d.head_kind, self.scores, stream)
 
     def select_only(self, stream=None):
-        """Each token row's page list from its scores (lengths read on the device)."""
+        """Each token row's page list from its scores (lengths read on the device); with the "select"
+        tail, spare workgroups rebuild the statistics of each request's last two pages."""
         d = self.d
+        meta = d.page_meta if self.tail == "select" else None
         A.spd_page_select_mq(self.desc, self.T, self.token_cap, self.sel, self.scores, d.seq_lens, d.head_kind,
-                             d.block_table, self.token_list, None, self.token_len, stream)
+                             d.block_table, d.k_pool, d.k_scale, meta, self.token_list, None, self.token_len,
+                             stream)
 
     def select(self, stream=None):
         self.score(stream)
@@ -396,7 +412,8 @@ class MQDecodeStep:
                            self.out_lse, stream)
 
     def run(self, stream=None):
-        self.refresh_tail(stream)
+        if self.tail == "serial":
+            self.refresh_tail(stream)
         self.select(stream)
         self.union(stream)
         self.attend(stream)

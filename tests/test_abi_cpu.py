@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(A.EXPORTS)
-    assert A.abi_version() == 16
+    assert A.abi_version() == 17
 
 
 def test_error_strings(lib):
@@ -367,13 +367,13 @@ def test_several_query_tokens_argument_checks(lib):
     rc = L.spd_lse_merge_mq(ctypes.byref(d), 4, ctypes.byref(plan), FAKE, None, FAKE, FAKE, FAKE, 0)
     assert rc == A.SPD_ERR_INVALID_ARG
 
-    def score_rc(desc, T=4, sel=None, **null):
+    def score_rc(desc, T=4, sel=None, tail=A.TAIL_NONE, **null):
         p = {k: FAKE for k in ("q", "meta", "bt", "sl", "sc")}
         p.update(null)
         heads = (ctypes.c_uint8 * desc.num_kv_heads)(*([0] * desc.num_kv_heads))
         s = sel if sel is not None else sel_for(w)
-        return L.spd_page_score_mq(ctypes.byref(desc), T, ctypes.byref(s), p["q"], p["meta"], p["bt"], p["sl"], heads,
-                                   p["sc"], 0)
+        return L.spd_page_score_mq(ctypes.byref(desc), T, ctypes.byref(s), p["q"], p["meta"], tail, p["bt"], p["sl"],
+                                   heads, p["sc"], 0)
 
     for T in (0, 5):
         assert score_rc(d, T=T) == A.SPD_ERR_INVALID_ARG
@@ -383,6 +383,10 @@ def test_several_query_tokens_argument_checks(lib):
     assert score_rc(d, sel=sel_for(w, mode=A.SELECT_COVERAGE, estimator=A.ESTIMATOR_MVAR)) == A.SPD_ERR_UNSUPPORTED
     assert score_rc(desc_for(w, max_list=24, page_size=64)) == A.SPD_ERR_UNSUPPORTED
     assert score_rc(desc_for(w, max_list=24, batch=0)) == A.SPD_OK
+    # skipping the last two pages needs them in every token's local window (n_local >= 2)
+    assert score_rc(d, sel=sel_for(w, n_local=1), tail=A.TAIL_SKIP) == A.SPD_ERR_INVALID_ARG
+    assert score_rc(d, tail=A.TAIL_REBUILD) == A.SPD_ERR_INVALID_ARG
+    assert score_rc(d, tail=7) == A.SPD_ERR_INVALID_ARG
 
 
 def test_several_query_token_selection_argument_checks(lib):
@@ -393,11 +397,12 @@ def test_several_query_token_selection_argument_checks(lib):
 
     def sel_rc(desc, T=4, tml=6, sel=None, **null):
         p = {k: FAKE for k in ("sc", "sl", "bt", "tl", "tp", "tn")}
+        p.update({"kp": None, "ks": None, "pm": None})
         p.update(null)
         heads = (ctypes.c_uint8 * desc.num_kv_heads)(*([0] * desc.num_kv_heads))
         s = sel if sel is not None else sel_for(w)
         return L.spd_page_select_mq(ctypes.byref(desc), T, tml, ctypes.byref(s), p["sc"], p["sl"], heads, p["bt"],
-                                    p["tl"], p["tp"], p["tn"], 0)
+                                    p["kp"], p["ks"], p["pm"], p["tl"], p["tp"], p["tn"], 0)
 
     for T in (0, 5):
         assert sel_rc(d, T=T) == A.SPD_ERR_INVALID_ARG
@@ -410,6 +415,11 @@ def test_several_query_token_selection_argument_checks(lib):
     assert sel_rc(desc_for(w, max_list=24, page_size=64)) == A.SPD_ERR_UNSUPPORTED
     assert sel_rc(desc_for(w, max_list=24, max_pages_per_seq=40000)) == A.SPD_ERR_UNSUPPORTED
     assert sel_rc(desc_for(w, max_list=24, batch=0)) == A.SPD_OK
+    # the rebuild of the last two pages needs the K pool and the block table
+    assert sel_rc(d, pm=FAKE) == A.SPD_ERR_INVALID_ARG
+    assert sel_rc(d, pm=FAKE, kp=FAKE, bt=None, tp=None) == A.SPD_ERR_INVALID_ARG
+    dq = desc_for(W.small(num_queries=4, budget=6, n_sink_stream=2, n_local_stream=3, kv="fp8"), max_list=24)
+    assert sel_rc(dq, pm=FAKE, kp=FAKE) == A.SPD_ERR_INVALID_ARG  # fp8 pools need k_scale
 
 
 def test_noalloc_decode_rejects_partials_beyond_its_array(lib):

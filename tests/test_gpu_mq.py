@@ -58,7 +58,8 @@ def run_case(w, plan=None):
 
 def check_token_lists(inp, st, meta_ref):
     """Each token's page scores (tolerance of parity.py) and lists (tie rule) against the oracle's, on
-    every token row; returns the GPU's and the oracle's lists."""
+    every token row; returns the GPU's and the oracle's lists.  A step whose scan skips each request's
+    last two pages (the "select" tail) holds -inf there, and the lists take those pages as forced."""
     w = inp.workload
     T = w.num_queries
     gpu = st.token_lists()
@@ -77,7 +78,9 @@ def check_token_lists(inp, st, meta_ref):
                 S_ = O.row_bounds(one, meta_ref, b, h)
                 sc = O.topk_scores(S_)
                 scale = P.bound_scale(one, meta_ref, b, h)
-                P.check_topk_scores(scores[b * T + t, h, :n], sc, scale)
+                k = max(O.n_pages(inp.seq_lens[b]) - 2, 0) if st.tail == "select" else n
+                P.check_topk_scores(scores[b * T + t, h, :min(k, n)], sc[:min(k, n)], scale[:min(k, n)])
+                assert np.all(scores[b * T + t, h, k:n] == -np.inf), (t, b, h)
                 forced = O.forced_pages(n, w.n_sink, w.n_local)
                 P.check_topk_list(gpu[t][(b, h)], sc, n, w.budget_pages, forced, scale)
                 ref[(b, h)] = O.select_topk(sc, n, w.budget_pages, forced)
@@ -188,9 +191,14 @@ def test_mq_one_scan_scores_match_the_oracle(name):
     st = S.MQDecodeStep(w, d)
     st.refresh_tail()
     st.scores.fill_(float("nan"))
-    st.score()
+    st.score(tail_mode=A.TAIL_NONE)
     torch.cuda.synchronize()
     one = st.scores.clone()
+    # skipping the last two pages: the same scores elsewhere, -inf on those pages where a token sees them
+    st.scores.fill_(float("nan"))
+    st.score(tail_mode=A.TAIL_SKIP)
+    torch.cuda.synchronize()
+    skip = st.scores.clone()
     per = per_token_scores(w, d, st)
     meta_ref = O.page_meta_build(inp)
     got = one.cpu().numpy()
@@ -207,6 +215,46 @@ def test_mq_one_scan_scores_match_the_oracle(name):
                 ref = O.topk_scores(O.row_bounds(tok, meta_ref, b, h))
                 P.check_topk_scores(got[r, h, :n_t], ref, P.bound_scale(tok, meta_ref, b, h))
                 assert torch.equal(one[r, h, :n_t], per[r, h, :n_t]), (b, t, h)
+                k = max(O.n_pages(inp.seq_lens[b]) - 2, 0)
+                assert torch.equal(skip[r, h, :min(k, n_t)], one[r, h, :min(k, n_t)]), (b, t, h)
+                assert torch.all(skip[r, h, k:n_t] == float("-inf")), (b, t, h)
+                assert torch.isnan(skip[r, h, n_t:]).all(), (b, t, h)
+
+
+@pytest.mark.parametrize("name", ["t4", "t4_fp8", "t2"])
+def test_mq_last_pages_rebuilt_beside_the_selection(name):
+    """The default step skips each request's last two pages in the scan and rebuilds their statistics in
+    the selector's spare workgroups: exactly those pages' statistics are written (all KV heads, equal to
+    the oracle's), the other entries are left alone, and the lists, unions and outputs are those of the
+    step that rebuilds the pages before a scan over every page."""
+    w = MQ_SMALL[name]
+    inp = W.generate(w)
+    d = S.upload(inp)
+    S.build_meta(w, d)
+    serial = S.MQDecodeStep(w, d, tail="serial")
+    sel = S.MQDecodeStep(w, d, gated=False)
+    assert sel.tail == "select"
+    serial.run()
+    torch.cuda.synchronize()
+    sentinel = 3.0
+    full = d.page_meta.clone()
+    d.page_meta.fill_(sentinel)
+    sel.select()
+    torch.cuda.synchronize()
+    got = d.page_meta.cpu().numpy()
+    ref = full.cpu().numpy()
+    for b, L in enumerate(w.seq_lens):
+        n = O.n_pages(L)
+        for p in range(got.shape[2]):
+            want = ref[b, :, p] if n - 2 <= p < n else np.full_like(got[b, :, p], sentinel)
+            assert np.array_equal(got[b, :, p], want), (name, b, p)
+    d.page_meta.copy_(full)
+    sel.run()
+    torch.cuda.synchronize()
+    assert sel.token_lists() == serial.token_lists()
+    assert sel.union_lists() == serial.union_lists()
+    assert torch.equal(sel.out, serial.out) and torch.equal(sel.out_lse, serial.out_lse)
+    assert torch.equal(d.page_meta, full)
 
 
 @pytest.mark.parametrize("plan", [S.Plan(1, 1, 0), S.Plan(2, 3, 0), S.Plan(4, 16, 512), S.Plan(1000, 1, 0)])
