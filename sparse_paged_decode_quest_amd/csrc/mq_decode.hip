@@ -29,8 +29,9 @@ constexpr int kMqRows = 16;  // 4 query tokens x G = 4 heads
 constexpr int kUnionThreads = 1024;
 constexpr int kUnionRounds = 2;  // list entries per thread read up front (4 tokens x 512 entries)
 constexpr int kUnionRankMinPages = 16384;  // block tables this wide merge sorted lists by rank
-// Pages of a wave in flight: one computed while the next one loads (three or four were measured
-// slower: the kernel is bound by its per-page instructions, not by load latency).
+// Pages of a wave in flight: the next page's loads go out before the current page is computed (two
+// register stages; the page's loads are scalar-addressed buffer loads and fp8 codes are decoded when
+// the page is processed, so nothing waits for the next page early).
 constexpr int kMqStages = 2;
 
 __device__ __forceinline__ int mq_clamp(int n, int hi) { return n < 0 ? 0 : (n > hi ? hi : n); }
@@ -202,31 +203,85 @@ struct MqPage {
 // One page's K operand (lane: key l % 16, channels 32 (l / 16) .. + 31) and V rows (lane: channels
 // 2 l, 2 l + 1 of every key), as fp16 bits; fp8 pools hold their codes' values times 2^-8 here
 // (exact), with the key's scales times 256 beside them.
-struct MqKV {
+// One page's K and V as loaded (fp16 values, or E4M3FN codes for fp8 pools): lane l holds key l % 16's
+// channels 32 (l / 16) .. + 31, and channels 2 l, 2 l + 1 of every key.  fp8 codes are decoded when the
+// page is processed, not when it is loaded, so nothing waits for a page's loads before the next page's
+// loads are issued.
+template <int KVD> struct MqKV;
+template <> struct MqKV<SPD_DTYPE_F16> {
   uint4 k[4];
   uint32_t v[kPage];
-  float ks, vs;  // fp8: this lane's key (l % 16) K and V scales times 256
+};
+template <> struct MqKV<SPD_DTYPE_FP8_E4M3FN> {
+  uint4 k[2];         // 32 codes
+  uint32_t v[kPage];  // two codes per key (low 16 bits)
+  uint32_t ks, vs;    // this lane's key (l % 16) K and V scales, fp16 bits (low 16 bits)
 };
 
+// A page's loads are issued with no branch around them: an entry that is not a usable page
+// (r.page < 0) reads pool page 0 of head h instead, and its values are never used.  The page's addresses are wave-uniform:
+// each load is a buffer load from a resource over the page (scalar registers) at this lane's constant
+// offset, so issuing a page needs no vector registers beyond the ones it loads into.  A load under a
+// branch, or vector address registers reused from a pending load's destination, made the compiler wait
+// for the other page's loads first, and only one page was ever in flight.
+struct MqLaneOff {
+  uint32_t k, v;  // byte offsets of this lane's K channels and V channel pair in a page (key 0)
+};
 template <int D, int KVD>
-__device__ __forceinline__ void mq_load(const MqDecodeArgs& a, const MqPage& r, int h, MqKV& kv) {
-  if (r.page < 0) return;
+__device__ __forceinline__ MqLaneOff mq_lane_offsets() {
   const int lane = threadIdx.x % kWave;
-  const size_t head_page = (size_t)r.phys * a.num_kv_heads + h;
+  constexpr uint32_t eb = KVD == SPD_DTYPE_F16 ? 2u : 1u;
+  return MqLaneOff{(uint32_t)(((lane & 15) * D + 32 * (lane >> 4)) * eb), (uint32_t)(lane * 2 * eb)};
+}
+
+template <int D, int KVD>
+__device__ __forceinline__ void mq_load(const MqDecodeArgs& a, const MqPage& r, int h, const MqLaneOff& off,
+                                        MqKV<KVD>& kv) {
+  const int lane = threadIdx.x % kWave;
+  constexpr uint32_t eb = KVD == SPD_DTYPE_F16 ? 2u : 1u;
+  constexpr uint32_t page_bytes = kPage * D * eb;
+  const size_t head_page = (size_t)(r.page < 0 ? 0 : r.phys) * a.num_kv_heads + h;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const uint8_t*>(a.k_pool) + head_page * page_bytes, page_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const uint8_t*>(a.v_pool) + head_page * page_bytes, page_bytes);
   if constexpr (KVD == SPD_DTYPE_F16) {
-    const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.k_pool) +
-                                                     (head_page * kPage + (lane & 15)) * D + 32 * (lane >> 4));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kv.k[i] = ld_stream(kp + i);
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(a.v_pool) +
-                                                           head_page * kPage * D) + lane;
+    for (int i = 0; i < 4; ++i) kv.k[i] = buf_load_u32x4_nt(kr, off.k + 16u * i);
 #pragma unroll
-    for (int t = 0; t < kPage; ++t) kv.v[t] = ld_stream(vp + t * (D / 2));
+    for (int t = 0; t < kPage; ++t) kv.v[t] = buf_load_u32_nt(vr, off.v + (uint32_t)t * D * eb);
   } else {  // E4M3FN codes: 32 of the key's channels, two of every key's
-    const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.k_pool) +
-                                                     (head_page * kPage + (lane & 15)) * D + 32 * (lane >> 4));
-    const uint4 c0 = ld_stream(kp), c1 = ld_stream(kp + 1);
-    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    kv.k[0] = buf_load_u32x4_nt(kr, off.k);
+    kv.k[1] = buf_load_u32x4_nt(kr, off.k + 16u);
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) kv.v[t] = buf_load_u16_nt(vr, off.v + (uint32_t)t * D * eb);
+    const __amdgpu_buffer_rsrc_t kscr = make_rsrc(a.k_scale + head_page * kPage, kPage * 2u);
+    const __amdgpu_buffer_rsrc_t vscr = make_rsrc(a.v_scale + head_page * kPage, kPage * 2u);
+    kv.ks = buf_load_u16_nt(kscr, (uint32_t)(lane & 15) * 2u);
+    kv.vs = buf_load_u16_nt(vscr, (uint32_t)(lane & 15) * 2u);
+  }
+}
+
+// This lane's key scales times 256 (fp8 pools; 1 for fp16 pools, whose scales are not used), decoded
+// when the page is processed.
+template <int KVD> __device__ __forceinline__ float mq_kscale(const MqKV<KVD>& kv) {
+  if constexpr (KVD == SPD_DTYPE_F16) return 1.f;
+  else return half_bits_to_float((uint16_t)kv.ks) * 256.f;
+}
+template <int KVD> __device__ __forceinline__ float mq_vscale(const MqKV<KVD>& kv) {
+  if constexpr (KVD == SPD_DTYPE_F16) return 1.f;
+  else return half_bits_to_float((uint16_t)kv.vs) * 256.f;
+}
+
+// The page's K operand (fp16, 32 channels) and V values (two fp16 channels per key) of this lane: the
+// loaded values, or fp8 codes decoded exactly to fp16 (value times 2^-8; the scales come later).
+template <int KVD>
+__device__ __forceinline__ void mq_unpack(const MqKV<KVD>& kv, uint4 (&k)[4], uint32_t (&v)[kPage]) {
+  if constexpr (KVD == SPD_DTYPE_F16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = kv.k[i];
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) v[t] = kv.v[t];
+  } else {
+    const uint32_t w[8] = {kv.k[0].x, kv.k[0].y, kv.k[0].z, kv.k[0].w, kv.k[1].x, kv.k[1].y, kv.k[1].z, kv.k[1].w};
     uint32_t hk[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -234,13 +289,9 @@ __device__ __forceinline__ void mq_load(const MqDecodeArgs& a, const MqPage& r, 
       hk[2 * i + 1] = fp8x2_to_half2_scaled(w[i] >> 16);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kv.k[i] = make_uint4(hk[4 * i], hk[4 * i + 1], hk[4 * i + 2], hk[4 * i + 3]);
-    const uint16_t* vp = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.v_pool) +
-                                                           head_page * kPage * D) + lane;
+    for (int i = 0; i < 4; ++i) k[i] = make_uint4(hk[4 * i], hk[4 * i + 1], hk[4 * i + 2], hk[4 * i + 3]);
 #pragma unroll
-    for (int t = 0; t < kPage; ++t) kv.v[t] = fp8x2_to_half2_scaled(ld_stream(vp + t * (D / 2)));
-    kv.ks = half_bits_to_float(a.k_scale[head_page * kPage + (lane & 15)]) * 256.f;
-    kv.vs = half_bits_to_float(a.v_scale[head_page * kPage + (lane & 15)]) * 256.f;
+    for (int t = 0; t < kPage; ++t) v[t] = fp8x2_to_half2_scaled(kv.v[t] & 0xffffu);
   }
 }
 
@@ -311,27 +362,30 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
   // largest V scale (the same in every lane); f16 keeps e_acc = 0
   int e_acc = 0;
 
-  auto process = [&](const MqPage& r, const MqKV& kv) {
+  auto process = [&](const MqPage& r, const MqKV<KVD>& kv) {
     if (r.page < 0) return;
+    uint4 kk[4];
+    uint32_t vv[kPage];
+    mq_unpack<KVD>(kv, kk, vv);
     mq_float4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[i], __builtin_bit_cast(mq_half8, kv.k[i]), s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[i], __builtin_bit_cast(mq_half8, kk[i]), s, 0, 0, 0);
     }
     const bool ok = q4 < T && ((r.mask >> q4) & 1u) && r.page * kPage + tok < lim && tok < r.valid;
     // fp8: key tok's K scale on its logit column; its V scale on its probabilities (P times the scale
     // is what V's fp16 values times 2^8 are weighted with).  Slots past the request's end (scales may
     // be NaN) are masked before either is used.
-    const float kscale = KVD == SPD_DTYPE_F16 ? a.sm_scale_log2 : a.sm_scale_log2 * (ok ? kv.ks : 0.f);
+    const float kscale = KVD == SPD_DTYPE_F16 ? a.sm_scale_log2 : a.sm_scale_log2 * (ok ? mq_kscale<KVD>(kv) : 0.f);
     // fp8: the probabilities carry each key's V scale over 2^e_pg, the power of two just above the page's
     // largest scale (so under 1: the fp16 operand neither overflows nor loses precision to small scales);
     // the accumulator moves to units of 2^e_pg below, exactly, since every factor is a power of two
     int e_pg = 0;
     if constexpr (KVD != SPD_DTYPE_F16) {
-      const float vmax = row_max(tok < r.valid ? kv.vs : 0.f);  // the page's 16 tokens, one per lane of the row
+      const float vmax = row_max(tok < r.valid ? mq_vscale<KVD>(kv) : 0.f);  // the page's 16 tokens, one per lane of the row
       e_pg = vmax > 0.f ? __builtin_amdgcn_frexp_expf(vmax) : 0;  // vmax < 2^e_pg
     }
-    const float vscale = KVD == SPD_DTYPE_F16 ? 1.f : (ok ? __builtin_amdgcn_ldexpf(kv.vs, -e_pg) : 0.f);
+    const float vscale = KVD == SPD_DTYPE_F16 ? 1.f : (ok ? __builtin_amdgcn_ldexpf(mq_vscale<KVD>(kv), -e_pg) : 0.f);
     float p[4], alpha[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -349,7 +403,7 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
     // the request's end zeroed (their slots may hold NaN, and 0 x NaN would reach every row)
     uint32_t v[kPage];
 #pragma unroll
-    for (int t = 0; t < kPage; ++t) v[t] = t < r.valid ? kv.v[t] : 0u;
+    for (int t = 0; t < kPage; ++t) v[t] = t < r.valid ? vv[t] : 0u;
     uint32_t lo[kPage / 2], hi[kPage / 2];
 #pragma unroll
     for (int i = 0; i < kPage / 2; ++i) {
@@ -393,7 +447,8 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
     r.valid = valid_in_page(len, p);
     return r;
   };
-  MqKV kv[kMqStages];  // ring of page buffers: page u lives in slot u mod kMqStages
+  MqKV<KVD> kv[kMqStages];  // ring of page buffers: page u lives in slot u mod kMqStages
+  const MqLaneOff off = mq_lane_offsets<D, KVD>();
   MqPage rp[kMqStages];
   for (int bb = 0; bb < my_pages; bb += kWave) {
     const int cnt = min(kWave, my_pages - bb);
@@ -406,22 +461,28 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
       if (plist) lph = plist[idx];
       else if (lp >= 0 && lp < n_b) lph = a.block_table[(size_t)b * a.max_pages + lp];
     }
-#pragma unroll
-    for (int k = 0; k < kMqStages - 1; ++k) {  // the first kMqStages - 1 pages' loads go out at once
-      rp[k] = k < cnt ? page_at(lp, lph, lm, k) : MqPage{-1, 0, 0u, 0};
-      mq_load<D, KVD>(a, rp[k], h, kv[k]);
+    // Page u + 1's loads are issued before page u is processed.  Inside the loop every load is a real
+    // page of the batch, so no wave reads a page it does not use; the last page (or the last two) is
+    // processed after the loop with no load behind it.
+    static_assert(kMqStages == 2, "the ring below alternates two slots");
+    rp[0] = page_at(lp, lph, lm, 0);
+    mq_load<D, KVD>(a, rp[0], h, off, kv[0]);
+    int u = 0;
+    for (; u + 2 < cnt; u += 2) {
+      rp[1] = page_at(lp, lph, lm, u + 1);
+      mq_load<D, KVD>(a, rp[1], h, off, kv[1]);
+      process(rp[0], kv[0]);
+      rp[0] = page_at(lp, lph, lm, u + 2);
+      mq_load<D, KVD>(a, rp[0], h, off, kv[0]);
+      process(rp[1], kv[1]);
     }
-    for (int u0 = 0; u0 < cnt; u0 += kMqStages) {
-#pragma unroll
-      for (int k = 0; k < kMqStages; ++k) {
-        const int u = u0 + k;
-        if (u >= cnt) break;  // uniform over the wave
-        const int un = u + kMqStages - 1;
-        MqPage& rn = rp[(k + kMqStages - 1) % kMqStages];
-        rn = un < cnt ? page_at(lp, lph, lm, un) : MqPage{-1, 0, 0u, 0};
-        mq_load<D, KVD>(a, rn, h, kv[(k + kMqStages - 1) % kMqStages]);
-        process(rp[k], kv[k]);
-      }
+    if (u + 1 < cnt) {  // two pages left: the second's loads go out before the first is processed
+      rp[1] = page_at(lp, lph, lm, u + 1);
+      mq_load<D, KVD>(a, rp[1], h, off, kv[1]);
+      process(rp[0], kv[0]);
+      process(rp[1], kv[1]);
+    } else {
+      process(rp[0], kv[0]);
     }
   }
 

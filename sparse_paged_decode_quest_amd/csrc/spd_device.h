@@ -116,6 +116,18 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
 __device__ __forceinline__ int32_t buf_load_i32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
 }
+// Streamed (non-temporal, cache policy bit 1) buffer loads of 16, 4 and 2 bytes.
+constexpr int kBufNt = 2;
+__device__ __forceinline__ uint4 buf_load_u32x4_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kBufNt);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t buf_load_u32_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kBufNt);
+}
+__device__ __forceinline__ uint32_t buf_load_u16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)byte_off, 0, kBufNt);
+}
 
 // ------------------------------------------------------------------ wave reductions
 
