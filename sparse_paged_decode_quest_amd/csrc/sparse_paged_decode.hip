@@ -53,15 +53,20 @@ struct DecTraits<D, SPD_DTYPE_F16, SPD_DTYPE_F16> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) q.h[g][s * 4 + i] = p[(g * D + s * 32 + quarter * 8) / 2 + i];
   }
-  __device__ static void load_k(KF& f, const void* pool, size_t tok_base, int quarter) {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(pool) + tok_base;
+  static constexpr uint32_t EB = 2;  // bytes per element
+  // byte offsets in a 16-token page of this lane's K chunk 0 (token tok) and V channels (token 0)
+  __device__ static uint32_t k_off(int tok, int quarter) { return (uint32_t)(tok * D + quarter * 8) * EB; }
+  __device__ static uint32_t v_off(int lane) { return (uint32_t)(lane * CPL) * EB; }
+  __device__ static void load_k(KF& f, __amdgpu_buffer_rsrc_t r, uint32_t off) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) f.k[s] = ld_stream(reinterpret_cast<const uint4*>(p + s * 32 + quarter * 8));
+    for (int s = 0; s < NS; ++s) f.k[s] = buf_load_u32x4_nt(r, off + (uint32_t)s * 32 * EB);
   }
-  __device__ static void load_v(VF& f, const void* pool, size_t page_base, int lane) {
-    const VW* p = reinterpret_cast<const VW*>(reinterpret_cast<const uint16_t*>(pool) + page_base + lane * CPL);
+  __device__ static void load_v(VF& f, __amdgpu_buffer_rsrc_t r, uint32_t off) {
 #pragma unroll
-    for (int t = 0; t < kPage; ++t) f.v[t] = ld_stream(p + t * (D / CPL));
+    for (int t = 0; t < kPage; ++t) {
+      if constexpr (CPL == 2) f.v[t] = buf_load_u32_nt(r, off + (uint32_t)t * D * EB);
+      else f.v[t] = (uint16_t)buf_load_u16_nt(r, off + (uint32_t)t * D * EB);
+    }
   }
   __device__ static void dots(const Q& q, const KF& f, float (&part)[kGq]) {
 #pragma unroll
@@ -108,15 +113,16 @@ struct DecTraits<D, SPD_DTYPE_F16, SPD_DTYPE_FP8_E4M3FN> {
 #pragma unroll
         for (int i = 0; i < 8; ++i) q.h[g][s * 8 + i] = p[(g * D + s * 64 + quarter * 16) / 2 + i];
   }
-  __device__ static void load_k(KF& f, const void* pool, size_t tok_base, int quarter) {
-    const uint8_t* p = reinterpret_cast<const uint8_t*>(pool) + tok_base;
+  static constexpr uint32_t EB = 1;
+  __device__ static uint32_t k_off(int tok, int quarter) { return (uint32_t)(tok * D + quarter * 16); }
+  __device__ static uint32_t v_off(int lane) { return (uint32_t)(lane * CPL); }
+  __device__ static void load_k(KF& f, __amdgpu_buffer_rsrc_t r, uint32_t off) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) f.k[s] = ld_stream(reinterpret_cast<const uint4*>(p + s * 64 + quarter * 16));
+    for (int s = 0; s < NS; ++s) f.k[s] = buf_load_u32x4_nt(r, off + (uint32_t)s * 64);
   }
-  __device__ static void load_v(VF& f, const void* pool, size_t page_base, int lane) {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(pool) + page_base + lane * CPL);
+  __device__ static void load_v(VF& f, __amdgpu_buffer_rsrc_t r, uint32_t off) {
 #pragma unroll
-    for (int t = 0; t < kPage; ++t) f.v[t] = ld_stream(p + t * (D / 2));
+    for (int t = 0; t < kPage; ++t) f.v[t] = (uint16_t)buf_load_u16_nt(r, off + (uint32_t)t * D);
   }
   // dot products of the codes' values times 2^-8 (the token scale and 2^8 are applied later)
   __device__ static void dots(const Q& q, const KF& f, float (&part)[kGq]) {
@@ -165,17 +171,21 @@ struct DecTraits<D, SPD_DTYPE_F32, SPD_DTYPE_F32> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) q.f[g][s * 4 + i] = p[g * D + s * 16 + quarter * 4 + i];
   }
-  __device__ static void load_k(KF& f, const void* pool, size_t tok_base, int quarter) {
-    const float* p = reinterpret_cast<const float*>(pool) + tok_base;
+  static constexpr uint32_t EB = 4;
+  __device__ static uint32_t k_off(int tok, int quarter) { return (uint32_t)(tok * D + quarter * 4) * EB; }
+  __device__ static uint32_t v_off(int lane) { return (uint32_t)(lane * CPL) * EB; }
+  __device__ static void load_k(KF& f, __amdgpu_buffer_rsrc_t r, uint32_t off) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) f.k[s] = ld_stream(reinterpret_cast<const float4*>(p + s * 16 + quarter * 4));
+    for (int s = 0; s < NS; ++s) {
+      const uint4 w = buf_load_u32x4_nt(r, off + (uint32_t)s * 16 * EB);
+      f.k[s] = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
+    }
   }
-  __device__ static void load_v(VF& f, const void* pool, size_t page_base, int lane) {
-    const float* p = reinterpret_cast<const float*>(pool) + page_base + lane * CPL;
+  __device__ static void load_v(VF& f, __amdgpu_buffer_rsrc_t r, uint32_t off) {
 #pragma unroll
     for (int t = 0; t < kPage; ++t)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) f.v[t][c] = ld_stream(p + t * D + c);
+      for (int c = 0; c < CPL; ++c) f.v[t][c] = __uint_as_float(buf_load_u32_nt(r, off + (uint32_t)(t * D + c) * EB));
   }
   __device__ static void dots(const Q& q, const KF& f, float (&part)[kGq]) {
 #pragma unroll
@@ -209,8 +219,9 @@ __device__ __forceinline__ int row_units(const int32_t* list_len, int r, int max
   return clamp_len(list_len[r], max_list) << lgs;
 }
 
-// Chunk size of the balanced plan, c = max(C, ceil(T / N_T), ceil(n_max / kMaxChunks)), from
-// every row's list length (computed by the calling wave; every lane receives it).
+// Chunk size of the balanced plan, c = max(C, ceil(T / N'), ceil(n_max / kMaxChunks)) with N' = N_T - z
+// (z rows with a non-empty list) when N_T > z, else N_T, from every row's list length (computed by the
+// calling wave; every lane receives it).
 __device__ __forceinline__ int balanced_chunk(const int32_t* list_len, int rows, int max_list, int C, int NT, int lgs) {
   const int lane = threadIdx.x % kWave;
   unsigned long long tot = 0;
@@ -448,18 +459,28 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
 
   // Pages of this wave alternate between two register stages, so the next page's K / V
   // loads are in flight while the current page is computed.
-  auto load = [&](const PageRef& r, typename T::KF& kd, typename T::VF& vd, float& ksd, float& vsd) {
-    if (r.page < 0) return;
-    const size_t head_page = head_unit(r.phys, a.num_kv_heads, h, a.lgs, r.page & sub_mask);
-    T::load_k(kd, a.k_pool, (head_page * kPage + tok) * D, quarter);
-    T::load_v(vd, a.v_pool, head_page * kPage * D, lane);
-    if (T::kScaled) {
-      ksd = half_bits_to_float(a.k_scale[head_page * kPage + tok]) * 256.f;
-      vsd = half_bits_to_float(a.v_scale[head_page * kPage + tok]) * 256.f;
+  // A page's loads are issued with no branch around them (an entry that is not a usable page reads
+  // pool unit 0 instead; its values are never used), as buffer loads from a resource over the 16-token
+  // unit -- built in scalar registers from the wave-uniform page -- at this lane's constant offsets, and
+  // fp8 scales stay fp16 bits until the page is processed.  A load under a branch, vector address
+  // registers reused from a pending load's destination, or a decode right after the load made the
+  // compiler wait for every outstanding load before the next page's, so one page was in flight.
+  constexpr uint32_t unit_bytes = kPage * D * T::EB;
+  const uint32_t k_lane = T::k_off(tok, quarter), v_lane = T::v_off(lane);
+  auto load = [&](const PageRef& r, typename T::KF& kd, typename T::VF& vd, uint32_t& ksd, uint32_t& vsd) {
+    const size_t head_page = head_unit(r.page < 0 ? 0 : r.phys, a.num_kv_heads, h, a.lgs, r.page < 0 ? 0 : r.page & sub_mask);
+    T::load_k(kd, make_rsrc(reinterpret_cast<const uint8_t*>(a.k_pool) + head_page * unit_bytes, unit_bytes), k_lane);
+    T::load_v(vd, make_rsrc(reinterpret_cast<const uint8_t*>(a.v_pool) + head_page * unit_bytes, unit_bytes), v_lane);
+    if constexpr (T::kScaled) {
+      ksd = buf_load_u16_nt(make_rsrc(a.k_scale + head_page * kPage, kPage * 2u), (uint32_t)tok * 2u);
+      vsd = buf_load_u16_nt(make_rsrc(a.v_scale + head_page * kPage, kPage * 2u), (uint32_t)tok * 2u);
     }
   };
-  auto process = [&](const PageRef& r, const typename T::KF& kf, const typename T::VF& vf, float ks, float vs) {
+  auto process = [&](const PageRef& r, const typename T::KF& kf, const typename T::VF& vf, uint32_t ks_bits,
+                     uint32_t vs_bits) {
     if (r.page < 0) return;
+    const float ks = T::kScaled ? half_bits_to_float((uint16_t)ks_bits) * 256.f : 1.f;
+    const float vs = T::kScaled ? half_bits_to_float((uint16_t)vs_bits) * 256.f : 1.f;
     // logits: partial dots over this lane's channel quarter, reduce-scattered over the quad
     float part[kGq];
     T::dots(q, kf, part);
@@ -529,7 +550,7 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   const int my_pages = i1 - i0 > wave ? (i1 - i0 - wave + 3) / 4 : 0;
   typename T::KF ka, kb;
   typename T::VF va, vb;
-  float ksa = 1.f, vsa = 1.f, ksb = 1.f, vsb = 1.f;
+  uint32_t ksa = 0, vsa = 0, ksb = 0, vsb = 0;
   for (int bb = 0; bb < my_pages; bb += kWave) {
     const int cnt = min(kWave, my_pages - bb);
     const int idx = i0 + wave + 4 * (bb + lane);
@@ -548,20 +569,26 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
     // request are not usable (checked before the shift, so no entry can wrap into range)
     if (lane < cnt) lp = (lp >= 0 && lp < n_phys) ? (lp << a.lgs) | (idx & sub_mask) : -1;
     if (!plist && lane < cnt && lp >= 0 && lp < n_b) lph = a.block_table[(size_t)b * a.max_pages + (lp >> a.lgs)];
+    // page u + 1's loads go out before page u is processed; inside the loop every load is a page of the
+    // batch, and the last page (or the last two) is processed after it with no load behind it
     PageRef ra = batch_page(lp, lph, 0, n_b, len, a.num_pool_pages), rb;
     load(ra, ka, va, ksa, vsa);
-    for (int u = 0; u < cnt; u += 2) {
-      if (u + 1 < cnt) {
-        rb = batch_page(lp, lph, u + 1, n_b, len, a.num_pool_pages);
-        load(rb, kb, vb, ksb, vsb);
-      }
+    int u = 0;
+    for (; u + 2 < cnt; u += 2) {
+      rb = batch_page(lp, lph, u + 1, n_b, len, a.num_pool_pages);
+      load(rb, kb, vb, ksb, vsb);
       process(ra, ka, va, ksa, vsa);
-      if (u + 1 >= cnt) break;
-      if (u + 2 < cnt) {
-        ra = batch_page(lp, lph, u + 2, n_b, len, a.num_pool_pages);
-        load(ra, ka, va, ksa, vsa);
-      }
+      ra = batch_page(lp, lph, u + 2, n_b, len, a.num_pool_pages);
+      load(ra, ka, va, ksa, vsa);
       process(rb, kb, vb, ksb, vsb);
+    }
+    if (u + 1 < cnt) {
+      rb = batch_page(lp, lph, u + 1, n_b, len, a.num_pool_pages);
+      load(rb, kb, vb, ksb, vsb);
+      process(ra, ka, va, ksa, vsa);
+      process(rb, kb, vb, ksb, vsb);
+    } else {
+      process(ra, ka, va, ksa, vsa);
     }
   }
 
