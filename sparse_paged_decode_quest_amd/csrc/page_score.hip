@@ -15,23 +15,99 @@
 
 namespace spd {
 
-// A dynamic row's workgroups: blk < blocks_per_row scan pages; with SPD_TAIL_REBUILD one more,
-// blk == blocks_per_row, rebuilds and scores the row's last page.  Unless the mode is
-// SPD_TAIL_NONE the scan stops before that page.
-struct RowRole {
-  int b, h, blk;
-  bool tail;
+// Scan work items: the blocks of pages_per_block pages that hold pages of a dynamic row's scan,
+// numbered request-major as (request b, dynamic head, block); the heads of a request need the same
+// number of blocks.  Scanning workgroup k takes item k, and workgroups past the last item exit, so a
+// batch of short and long requests has its working workgroups dispatched first instead of scattered
+// among the blocks past each short row's end.  With SPD_TAIL_REBUILD, workgroup scan_grid + r
+// rebuilds and scores the last page of dynamic row r.  Unless the mode is SPD_TAIL_NONE the scan
+// stops before that page.
+
+// Pages a row's scan covers for a request of `len` tokens, in the units the workgroups step over
+// (logical pages for coverage and hierarchical paging).
+template <bool COV, bool HIER>
+__device__ __forceinline__ int scan_limit(const ScoreArgs& a, int len) {
+  if constexpr (HIER) {
+    const int n_phys = row_phys_pages(len, a.max_pages, a.lgs);
+    const int phys_scan = a.tail_mode == SPD_TAIL_SKIP && n_phys > 0 ? n_phys - 1 : n_phys;
+    return min(row_logical_pages(len, a.max_pages, a.lgs), phys_scan << a.lgs);
+  } else {
+    return scan_pages(a, COV ? row_logical_pages(len, a.max_pages, a.lgs) : row_pages(len, a.max_pages));
+  }
+}
+
+// Scan work items of one row of a request of `len` tokens: its blocks of PPB pages.
+template <bool COV, bool HIER, int PPB>
+__device__ __forceinline__ int scan_blocks(const ScoreArgs& a, int len) {
+  return (scan_limit<COV, HIER>(a, len) + PPB - 1) / PPB;
+}
+
+// One wave's view of 64 requests of the numbering: lane i holds request b0 + i's length and the
+// inclusive count of the items of requests b0 .. b0 + i; `total` is the 64 requests' item count.
+struct ScanChunk {
+  int len, incl, total;
 };
 
-__device__ __forceinline__ RowRole row_role(const ScoreArgs& a) {
-  const int per_row = a.blocks_per_row + tail_blocks(a);
-  const int row_dyn = blockIdx.x / per_row;
-  RowRole r;
-  r.blk = blockIdx.x % per_row;
-  r.b = row_dyn / a.dyn.count;
-  r.h = a.dyn.at(row_dyn % a.dyn.count);
-  r.tail = r.blk == a.blocks_per_row;
-  return r;
+template <bool COV, bool HIER, int PPB>
+__device__ __forceinline__ ScanChunk scan_chunk(const ScoreArgs& a, int b0) {
+  const int b = b0 + (int)threadIdx.x % kWave;
+  ScanChunk c;
+  c.len = b < a.batch ? a.seq_lens[b] : 0;
+  const int items = b < a.batch ? scan_blocks<COV, HIER, PPB>(a, c.len) * a.dyn.count : 0;
+  c.incl = (int)wave_incl_scan((uint32_t)items);
+  c.total = (int)lane_u32((uint32_t)c.incl, kWave - 1);
+  return c;
+}
+
+struct ScanItem {
+  int b, h, blk, n_scan, len;
+};
+
+// Item `rel` of a chunk starting at request b0 (rel < c.total).  Every result is wave-uniform.
+template <bool COV, bool HIER, int PPB>
+__device__ __forceinline__ ScanItem chunk_item(const ScoreArgs& a, const ScanChunk& c, int b0, int rel) {
+  const int i = __popcll(__ballot(c.incl <= rel));  // the first lane whose inclusive count passes rel
+  ScanItem it;
+  it.b = b0 + i;
+  it.len = (int)lane_u32((uint32_t)c.len, i);
+  it.n_scan = scan_limit<COV, HIER>(a, it.len);
+  const int nb = (it.n_scan + PPB - 1) / PPB;
+  const int r = rel - ((int)lane_u32((uint32_t)c.incl, i) - nb * a.dyn.count);
+  const int hi = r / nb;
+  it.h = a.dyn.at(hi);
+  it.blk = r - hi * nb;
+  return it;
+}
+
+// Item k of a batch of one request, on the scalar unit: the length is one scalar load (read through
+// the constant address space, which the kernel never writes, so the compiler issues it as one).
+// Returns false past the last item.
+typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+template <bool COV, bool HIER, int PPB>
+__device__ __forceinline__ bool single_request_item(const ScoreArgs& a, int k, ScanItem& it) {
+  it.len = ((ConstI32Ptr)a.seq_lens)[0];
+  it.n_scan = scan_limit<COV, HIER>(a, it.len);
+  const int nb = (it.n_scan + PPB - 1) / PPB;
+  if (k >= nb * a.dyn.count) return false;
+  const int hi = k / nb;
+  it.b = 0;
+  it.h = a.dyn.at(hi);
+  it.blk = k - hi * nb;
+  return true;
+}
+
+// Item k of any batch, 64 requests per pass on the vector unit.  Returns false past the last item.
+template <bool COV, bool HIER, int PPB>
+__device__ __forceinline__ bool batch_item(const ScoreArgs& a, int k, ScanItem& it) {
+  for (int off = 0, b0 = 0; b0 < a.batch; b0 += kWave) {
+    const ScanChunk c = scan_chunk<COV, HIER, PPB>(a, b0);
+    if (k - off < c.total) {
+      it = chunk_item<COV, HIER, PPB>(a, c, b0, k - off);
+      return true;
+    }
+    off += c.total;
+  }
+  return false;
 }
 
 // HIER: top-K over physical pages of 2^lgs logical pages (hierarchical paging): the workgroups scan
@@ -39,33 +115,42 @@ __device__ __forceinline__ RowRole row_role(const ScoreArgs& a) {
 // physical page (the local window keeps it).
 template <int D, int KVD, bool COV, int ITERS, bool HIER>
 __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreArgs a) {
-  const RowRole r = row_role(a);
-  const int32_t* bt_row = a.block_table + (size_t)r.b * a.max_pages;
-  const int len = a.seq_lens[r.b];
-  if (r.tail) {
+  if ((int)blockIdx.x >= a.scan_grid) {  // tail workgroup of dynamic row blockIdx.x - scan_grid
+    const int row = (int)blockIdx.x - a.scan_grid;
+    const int b = row / a.dyn.count, h = a.dyn.at(row % a.dyn.count);
+    const int len = a.seq_lens[b];
     const int n = row_pages(len, a.max_pages);
-    if (n > 0) score_tail<D, KVD, COV>(a, bt_row, n, len, r.b, r.h, -1);
+    if (n > 0) score_tail<D, KVD, COV>(a, a.block_table + (size_t)b * a.max_pages, n, len, b, h, -1);
     return;
   }
-  const int p_begin = r.blk * a.pages_per_block;
-  int raw[ITERS];
-  load_block_table<D, KVD, kScoreWaves, ITERS>(bt_row, a.max_pages, p_begin, raw, HIER || COV ? a.lgs : 0);
-  float* sc_row = a.scores + ((size_t)r.b * a.num_kv_heads + r.h) * a.max_pages;
-  if constexpr (HIER) {
-    const int n_phys = row_phys_pages(len, a.max_pages, a.lgs);
-    const int phys_scan = a.tail_mode == SPD_TAIL_SKIP && n_phys > 0 ? n_phys - 1 : n_phys;
-    const int n_scan = min(row_logical_pages(len, a.max_pages, a.lgs), phys_scan << a.lgs);
-    if (a.tail_mode == SPD_TAIL_SKIP && r.blk == 0 && n_phys > 0 && threadIdx.x == 0) sc_row[n_phys - 1] = -INFINITY;
-    if (p_begin >= n_scan) return;  // uniform over the block
-    score_block_topk_hier<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, phys_scan, r.b, r.h, p_begin, sc_row);
-  } else {
-    // coverage over 64-token pages scans logical pages too (their shares are summed per page later)
-    const int n = COV ? row_logical_pages(len, a.max_pages, a.lgs) : row_pages(len, a.max_pages);
-    const int n_scan = scan_pages(a, n);
-    if (!COV && a.tail_mode == SPD_TAIL_SKIP && r.blk == 0 && n > 0 && threadIdx.x == 0) sc_row[n - 1] = -INFINITY;
-    if (p_begin >= n_scan) return;  // uniform over the block
-    if constexpr (COV) score_block_ell<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, len, r.b, r.h, p_begin);
-    else score_block_topk<D, KVD, kScoreWaves, ITERS>(a, raw, n_scan, r.b, r.h, p_begin, sc_row);
+  constexpr int PPB = ITERS * kScoreWaves * (kWave / ScoreTraits<D, KVD>::LPP);  // = a.pages_per_block
+  const int k = (int)blockIdx.x;
+  ScanItem it;
+  const bool found = a.batch == 1 ? single_request_item<COV, HIER, PPB>(a, k, it) : batch_item<COV, HIER, PPB>(a, k, it);
+  if (found) {
+    const int32_t* bt_row = a.block_table + (size_t)it.b * a.max_pages;
+    const int p_begin = it.blk * PPB;
+    int raw[ITERS];
+    load_block_table<D, KVD, kScoreWaves, ITERS>(bt_row, a.max_pages, p_begin, raw, HIER || COV ? a.lgs : 0);
+    float* sc_row = a.scores + ((size_t)it.b * a.num_kv_heads + it.h) * a.max_pages;
+    if constexpr (HIER) {
+      const int n_phys = row_phys_pages(it.len, a.max_pages, a.lgs);
+      const int phys_scan = a.tail_mode == SPD_TAIL_SKIP && n_phys > 0 ? n_phys - 1 : n_phys;
+      score_block_topk_hier<D, KVD, kScoreWaves, ITERS>(a, raw, it.n_scan, phys_scan, it.b, it.h, p_begin, sc_row);
+    } else if constexpr (COV) {
+      score_block_ell<D, KVD, kScoreWaves, ITERS>(a, raw, it.n_scan, it.len, it.b, it.h, p_begin);
+    } else {
+      score_block_topk<D, KVD, kScoreWaves, ITERS>(a, raw, it.n_scan, it.b, it.h, p_begin, sc_row);
+    }
+  }
+  // SPD_TAIL_SKIP: workgroup r < rows writes -inf for dynamic row r's skipped last page (after its
+  // own scan, so the write adds no round trip before the loads)
+  const int rows = a.batch * a.dyn.count;
+  if (!COV && a.tail_mode == SPD_TAIL_SKIP && k < rows) {
+    const int b = k / a.dyn.count, h = a.dyn.at(k % a.dyn.count);
+    const int len = a.seq_lens[b];
+    const int n = HIER ? row_phys_pages(len, a.max_pages, a.lgs) : row_pages(len, a.max_pages);
+    if (n > 0 && threadIdx.x == 0) a.scores[((size_t)b * a.num_kv_heads + h) * a.max_pages + n - 1] = -INFINITY;
   }
 }
 
@@ -202,25 +287,34 @@ void launch_coverage_shares(const ScoreArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(coverage_share_kernel, share_grid, share_block, 0, stream, a);
 }
 
+template <int D, int KVD, bool COV, int ITERS, bool HIER>
+int launch_scan(const ScoreArgs& a0, hipStream_t stream) {
+  const unsigned rows = (unsigned)(a0.batch * a0.dyn.count);
+  ScoreArgs a = a0;
+  a.scan_grid = (int)(rows * (unsigned)a.blocks_per_row);
+  const dim3 grid(rows * (unsigned)(a.blocks_per_row + tail_blocks(a))), block(kScoreWaves * kWave);
+  hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, ITERS, HIER>), grid, block, 0, stream, a);
+  return 0;
+}
+
 int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool coverage, hipStream_t stream) {
   const unsigned rows = (unsigned)(a.batch * a.dyn.count);
-  const dim3 grid(rows * (unsigned)(a.blocks_per_row + tail_blocks(a))), block(kScoreWaves * kWave);
   const bool long_scan = score_iters((long long)rows * ((long long)a.max_pages << a.lgs)) == kScoreItersLong;
-#define SPD_SCORE_LAUNCH(D, KVD, COV)                                                                                       \
-  if (long_scan) hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, kScoreItersLong, false>), grid, block, 0, stream, a);   \
-  else hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, kScoreItersShort, false>), grid, block, 0, stream, a);
-#define SPD_SCORE_LAUNCH_HIER(D, KVD)                                                                                       \
-  if (long_scan) hipLaunchKernelGGL((page_score_kernel<D, KVD, false, kScoreItersLong, true>), grid, block, 0, stream, a);  \
-  else hipLaunchKernelGGL((page_score_kernel<D, KVD, false, kScoreItersShort, true>), grid, block, 0, stream, a);
+#define SPD_SCORE_LAUNCH(D, KVD, COV, HIER)                                                           \
+  {                                                                                                   \
+    const int rc = long_scan ? launch_scan<D, KVD, COV, kScoreItersLong, HIER>(a, stream)             \
+                             : launch_scan<D, KVD, COV, kScoreItersShort, HIER>(a, stream);           \
+    if (rc != 0) return rc;                                                                           \
+  }
 #define SPD_SCORE_CASE(D, KVD)                                                                  \
   if (head_dim == D && kv_dtype == KVD) {                                                       \
     if (coverage) {                                                                             \
-      SPD_SCORE_LAUNCH(D, KVD, true)                                                            \
+      SPD_SCORE_LAUNCH(D, KVD, true, false)                                                     \
       launch_coverage_shares(a, stream);                                                        \
     } else if (a.lgs > 0) {                                                                     \
-      SPD_SCORE_LAUNCH_HIER(D, KVD)                                                             \
+      SPD_SCORE_LAUNCH(D, KVD, false, true)                                                     \
     } else {                                                                                    \
-      SPD_SCORE_LAUNCH(D, KVD, false)                                                           \
+      SPD_SCORE_LAUNCH(D, KVD, false, false)                                                    \
     }                                                                                           \
     return 0;                                                                                   \
   }
@@ -231,7 +325,6 @@ int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool cover
   SPD_SCORE_CASE(128, SPD_DTYPE_F32)
 #undef SPD_SCORE_CASE
 #undef SPD_SCORE_LAUNCH
-#undef SPD_SCORE_LAUNCH_HIER
   return SPD_ERR_UNSUPPORTED;
 }
 

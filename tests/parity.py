@@ -111,6 +111,9 @@ def check_coverage_list(lst, pi, n, gamma, forced):
     t = gamma - sum(float(pi[p]) for p in forced)
     chosen = [p for p in lst if p not in fset]
     free = [p for p in range(n) if p not in fset]
+    if not free:  # nothing to choose from: an empty row, or every page forced
+        assert not chosen
+        return
     if t <= TIE_RTOL:
         assert len(chosen) == 0 or t > -TIE_RTOL
         return

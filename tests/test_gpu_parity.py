@@ -52,6 +52,11 @@ SMALL = {
                        planted=("fixed", 6), delta=("nats", 6.0)),
     "cov_f32": W.small("cov_f32", kv="f32", q="f32", d=64, mode="coverage", gamma=0.95, n_local=1,
                        seq_lens=(900, 77), streaming=(0,)),
+    # more than 64 requests (the scorer numbers its work 64 requests at a time), empty ones among them
+    "f16_b70": W.small("f16_b70", seq_lens=tuple((i * 977) % 3100 for i in range(70)), budget=12),
+    "cov_b66": W.small("cov_b66", mode="coverage", gamma=0.9, n_local=1,
+                       seq_lens=tuple((i * 613) % 2900 for i in range(66)), planted=("fixed", 3),
+                       delta=("nats", 6.0)),
 }
 
 
