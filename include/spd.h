@@ -268,8 +268,10 @@ int spd_page_stats_build(const spd_desc* desc, const void* k_pool, const uint16_
  * The key boxes are read from page_meta at [b, h, p] alone; block_table (device) only marks the
  * pages whose entry lies outside [0, num_pool_pages): they score -inf (TOPK) or carry no mass.
  * tail_mode (spd_tail_mode) says how each dynamic row's last logical page is treated;
- * SPD_TAIL_REBUILD reads k_pool (and k_scale for fp8 pools) and writes that page's entries of
- * page_meta, which is otherwise only read; SPD_TAIL_SKIP is valid in TOPK mode only.  head_lse
+ * SPD_TAIL_REBUILD reads k_pool (and k_scale for fp8 pools) and writes the entries of page_meta
+ * of each request's last page for every KV head, streaming heads included (what
+ * spd_page_meta_build does for that page), which page_meta is otherwise only read for;
+ * SPD_TAIL_SKIP is valid in TOPK mode only.  head_lse
  * (device, [B, Hq]) may be NULL in TOPK mode.  workspace (device) of spd_workspace_bytes(desc,
  * sel, SPD_OP_PAGE_SCORE) bytes (0 in TOPK mode).
  * With the MVAR estimator page_meta holds page_stats; k_pool (and k_scale for fp8 pools) is

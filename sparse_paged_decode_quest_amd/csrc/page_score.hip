@@ -19,9 +19,10 @@ namespace spd {
 // numbered request-major as (request b, dynamic head, block); the heads of a request need the same
 // number of blocks.  Scanning workgroup k takes item k, and workgroups past the last item exit, so a
 // batch of short and long requests has its working workgroups dispatched first instead of scattered
-// among the blocks past each short row's end.  With SPD_TAIL_REBUILD, workgroup scan_grid + r
-// rebuilds and scores the last page of dynamic row r.  Unless the mode is SPD_TAIL_NONE the scan
-// stops before that page.
+// among the blocks past each short row's end.  With SPD_TAIL_REBUILD the grid starts with one
+// workgroup per (request, KV head), which rebuilds the key statistics of the request's last page
+// and, for a dynamic head, scores it; being first, they run beside the scan instead of after it.
+// Unless the mode is SPD_TAIL_NONE the scan stops before that page.
 
 // Pages a row's scan covers for a request of `len` tokens, in the units the workgroups step over
 // (logical pages for coverage and hierarchical paging).
@@ -115,16 +116,18 @@ __device__ __forceinline__ bool batch_item(const ScoreArgs& a, int k, ScanItem& 
 // physical page (the local window keeps it).
 template <int D, int KVD, bool COV, int ITERS, bool HIER>
 __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreArgs a) {
-  if ((int)blockIdx.x >= a.scan_grid) {  // tail workgroup of dynamic row blockIdx.x - scan_grid
-    const int row = (int)blockIdx.x - a.scan_grid;
-    const int b = row / a.dyn.count, h = a.dyn.at(row % a.dyn.count);
+  const int tails = a.tail_mode == SPD_TAIL_REBUILD ? a.batch * a.num_kv_heads : 0;
+  if ((int)blockIdx.x < tails) {  // the last page of (request, KV head) blockIdx.x
+    const int b = (int)blockIdx.x / a.num_kv_heads, h = (int)blockIdx.x % a.num_kv_heads;
     const int len = a.seq_lens[b];
     const int n = row_pages(len, a.max_pages);
-    if (n > 0) score_tail<D, KVD, COV>(a, a.block_table + (size_t)b * a.max_pages, n, len, b, h, -1);
+    const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+    if (n > 0 && ((a.dyn.mask >> h) & 1)) score_tail<D, KVD, COV>(a, bt_row, n, len, b, h, -1);
+    else if (n > 0) rebuild_tail_page<D, KVD>(a, bt_row, n, len, b, h);
     return;
   }
   constexpr int PPB = ITERS * kScoreWaves * (kWave / ScoreTraits<D, KVD>::LPP);  // = a.pages_per_block
-  const int k = (int)blockIdx.x;
+  const int k = (int)blockIdx.x - tails;
   ScanItem it;
   const bool found = a.batch == 1 ? single_request_item<COV, HIER, PPB>(a, k, it) : batch_item<COV, HIER, PPB>(a, k, it);
   if (found) {
@@ -288,24 +291,18 @@ void launch_coverage_shares(const ScoreArgs& a, hipStream_t stream) {
 }
 
 template <int D, int KVD, bool COV, int ITERS, bool HIER>
-int launch_scan(const ScoreArgs& a0, hipStream_t stream) {
-  const unsigned rows = (unsigned)(a0.batch * a0.dyn.count);
-  ScoreArgs a = a0;
-  a.scan_grid = (int)(rows * (unsigned)a.blocks_per_row);
-  const dim3 grid(rows * (unsigned)(a.blocks_per_row + tail_blocks(a))), block(kScoreWaves * kWave);
+void launch_scan(const ScoreArgs& a, hipStream_t stream) {
+  const unsigned tails = a.tail_mode == SPD_TAIL_REBUILD ? (unsigned)(a.batch * a.num_kv_heads) : 0u;
+  const dim3 grid(tails + (unsigned)(a.batch * a.dyn.count) * (unsigned)a.blocks_per_row), block(kScoreWaves * kWave);
   hipLaunchKernelGGL((page_score_kernel<D, KVD, COV, ITERS, HIER>), grid, block, 0, stream, a);
-  return 0;
 }
 
 int launch_page_score(const ScoreArgs& a, int head_dim, int kv_dtype, bool coverage, hipStream_t stream) {
   const unsigned rows = (unsigned)(a.batch * a.dyn.count);
   const bool long_scan = score_iters((long long)rows * ((long long)a.max_pages << a.lgs)) == kScoreItersLong;
 #define SPD_SCORE_LAUNCH(D, KVD, COV, HIER)                                                           \
-  {                                                                                                   \
-    const int rc = long_scan ? launch_scan<D, KVD, COV, kScoreItersLong, HIER>(a, stream)             \
-                             : launch_scan<D, KVD, COV, kScoreItersShort, HIER>(a, stream);           \
-    if (rc != 0) return rc;                                                                           \
-  }
+  if (long_scan) launch_scan<D, KVD, COV, kScoreItersLong, HIER>(a, stream);                          \
+  else launch_scan<D, KVD, COV, kScoreItersShort, HIER>(a, stream);
 #define SPD_SCORE_CASE(D, KVD)                                                                  \
   if (head_dim == D && kv_dtype == KVD) {                                                       \
     if (coverage) {                                                                             \

@@ -30,7 +30,11 @@ __global__ __launch_bounds__(NW * kWave) void page_score_select_kernel(FusedArgs
     const int b = k / f.stream_heads.count;
     const int h = f.stream_heads.at(k % f.stream_heads.count);
     const size_t row = (size_t)b * a.num_kv_heads + h;
-    select_streaming_row(f.sel, row_pages(a.seq_lens[b], a.max_pages), row, a.block_table + (size_t)b * a.max_pages);
+    const int len = a.seq_lens[b];
+    const int n = row_pages(len, a.max_pages);
+    const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+    select_streaming_row(f.sel, n, row, bt_row);
+    if (a.tail_mode == SPD_TAIL_REBUILD && n > 0) rebuild_tail_page<D, KVD>(a, bt_row, n, len, b, h);
     return;
   }
   const int row_dyn = blockIdx.x / per_row;

@@ -336,6 +336,20 @@ __device__ __forceinline__ void score_tail_page(const ScoreArgs& a, const int32_
   if (threadIdx.x == 0) fn(s);
 }
 
+// The last page's key statistics of a head whose row is not scored (a streaming head): lanes
+// 0..LPP-1 of wave 0 rebuild them from the K pool and store them, as score_tail_page does.
+template <int D, int KVD>
+__device__ __forceinline__ void rebuild_tail_page(const ScoreArgs& a, const int32_t* bt_row, int n, int len, int b,
+                                                  int h) {
+  using T = ScoreTraits<D, KVD>;
+  if (threadIdx.x >= T::LPP) return;
+  const int phys = bt_row[n - 1];
+  if (phys < 0 || phys >= a.num_pool_pages) return;
+  typename T::M m;
+  T::rebuild(m, a.k_pool, a.k_scale, (size_t)phys * a.num_kv_heads + h, valid_in_page(len, n - 1),
+             (int)threadIdx.x * T::CW, a.meta_out, meta_unit(b, h, n - 1, a.num_kv_heads, a.max_pages, 0) * 2 * D);
+}
+
 // Top-K keys of the workgroup's pages: score_p = max_g S_{g,p} (the group combine keeps the
 // score an upper bound for every query head of the group); pages whose block-table entry is
 // outside the pool score -inf.

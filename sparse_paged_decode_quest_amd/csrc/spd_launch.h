@@ -98,7 +98,6 @@ struct ScoreArgs {
   int blocks_per_row;        // page-scanning workgroups per (request, dynamic head)
   int partial_stride;        // partial slots per row: blocks_per_row + 1 (the tail workgroup's)
   int pages_per_block;
-  int scan_grid;             // standalone scorer: page-scanning workgroups of the launch (set by its launcher)
   float sm_scale;
   int tail_mode;             // spd_tail_mode: last page of each dynamic row scored / rebuilt / skipped
   int lgs;                   // log2 of logical pages per physical page; > 0: scores are per physical page

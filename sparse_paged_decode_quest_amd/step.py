@@ -135,9 +135,11 @@ class DecodeStep:
     * ``"side"``: the all-heads rebuild (``refresh_tail``) on a second stream, concurrent with a
       scorer that skips that page (top-K with a local window);
     * ``"serial"``: the all-heads rebuild, then a scorer that reads the rebuilt statistics;
-    * ``"rebuild"``: inside the scorer, by one extra workgroup per dynamic row;
-    * ``"auto"`` (default): ``"select"`` where it applies, ``"rebuild"`` for a fused top-K step
-      and for the mvar estimator (whose scorer reads that page's keys anyway), else ``"serial"``.
+    * ``"rebuild"``: inside the scorer, by workgroups at the front of its grid (one per request
+      and KV head: the bound estimator), which run beside the scan;
+    * ``"auto"`` (default): ``"select"`` where it applies, else ``"rebuild"`` on 16-token pages
+      (a fused top-K step, coverage, top-K without a local window, and the mvar estimator, whose
+      scorer reads that page's keys anyway), else ``"serial"``.
 
     With the mvar estimator (Moira, section 3.1) ``d.page_meta`` holds the bf16 page summaries
     and the scorer computes each row's first and current pages exactly; scoring and selection are
@@ -163,7 +165,7 @@ class DecodeStep:
             raise ValueError("the fused score + select launch has no mvar estimator")
         if tail == "auto":
             tail = (("rebuild" if fused else "select") if skippable else
-                    "rebuild" if w.estimator == "mvar" and w.page_size == 16 else "serial")
+                    "rebuild" if w.page_size == 16 else "serial")
         if tail in ("select", "side") and not skippable:
             raise ValueError(f"tail={tail!r} skips the last page: top-K with a local window only")
         if tail == "select" and fused:

@@ -282,9 +282,9 @@ def test_fused_select_equals_unfused(mode):
 @pytest.mark.parametrize("fused,tail", [(True, "rebuild"), (True, "side"), (True, "serial"), (False, "rebuild"),
                                         (False, "side"), (False, "serial"), (False, "select")])
 def test_step_tail_modes_rebuild_the_last_page(fused, tail):
-    """A step rebuilds the statistics of each request's last page and of no other page: in the
-    scorer ("rebuild": dynamic heads only), or for all heads by the meta-build kernel ("side",
-    "serial") or the selector's spare workgroups ("select")."""
+    """A step rebuilds the statistics of each request's last page, for every KV head, and of no
+    other page: in the scorer ("rebuild"), by the meta-build kernel ("side", "serial") or by the
+    selector's spare workgroups ("select")."""
     for kv in ("f16", "fp8", "f32"):
         w = W.small("tail_" + kv, kv=kv, q="f32" if kv == "f32" else "f16", d=64 if kv == "f32" else 128,
                     seq_lens=(333, 48, 1, 0), budget=10, streaming=(1,), Hkv=2, Hq=8)
@@ -303,7 +303,7 @@ def test_step_tail_modes_rebuild_the_last_page(fused, tail):
             n = O.n_pages(L)
             for p in range(n):
                 for h in range(w.num_kv_heads):
-                    if p == n - 1 and (tail != "rebuild" or not inp.head_kind[h]):
+                    if p == n - 1:
                         assert np.array_equal(got[b, h, p], full[b, h, p]), (kv, b, p, h)
                     else:
                         assert np.all(got[b, h, p] == 3.0), (kv, b, p, h)
