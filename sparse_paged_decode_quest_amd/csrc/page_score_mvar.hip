@@ -252,18 +252,21 @@ __device__ __forceinline__ void mvar_exact_pages(const ScoreArgs& a, const int32
   }
 }
 
-// Workgroups of a dynamic row: blk < blocks_per_row estimate pages [1, n - 1); blk ==
-// blocks_per_row is the exact workgroup.
+// The grid starts with the exact workgroups, one per dynamic row, so their dependent reads (length,
+// block table, keys) run beside the estimate instead of after it; then blocks_per_row workgroups per
+// dynamic row estimate pages [1, n - 1).
 template <int D, int KVD, int ITERS>
 __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_mvar_kernel(ScoreArgs a) {
   using T = MvarTraits<D, KVD>;
-  const int per_row = a.blocks_per_row + 1;
-  const int row_dyn = blockIdx.x / per_row;
-  const int blk = blockIdx.x % per_row;
+  const int rows = a.batch * a.dyn.count;
+  const bool exact = (int)blockIdx.x < rows;
+  const int k = exact ? (int)blockIdx.x : (int)blockIdx.x - rows;
+  const int row_dyn = exact ? k : k / a.blocks_per_row;
+  const int blk = exact ? 0 : k % a.blocks_per_row;
   const int b = row_dyn / a.dyn.count;
   const int h = a.dyn.at(row_dyn % a.dyn.count);
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
-  if (blk == a.blocks_per_row) {
+  if (exact) {
     mvar_exact_pages<D, KVD>(a, bt_row, b, h);
     return;
   }
