@@ -15,31 +15,24 @@
 
 namespace spd {
 
+// Pages the scan covers in a request of `len` tokens: its last token's row, less the request's last
+// two pages with SPD_TAIL_SKIP.  Each token row's last page is one of those two (T <= 4 draft tokens
+// lie within 16 positions), so both are in every token's local window of at least two pages or past
+// the token's length; the kernel writes -inf for them where a token sees them.
+__device__ __forceinline__ int mq_scan_pages(const ScoreArgs& a, int len) {
+  const int n = row_pages(len, a.max_pages);
+  return a.tail_mode == SPD_TAIL_SKIP ? max(n - 2, 0) : n;
+}
+
+// The pages [p_begin, p_begin + PPB) of work item `item` (score_common.h's numbering) for every token row.
 template <int D, int KVD, int ITERS>
-__global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(ScoreArgs a, int num_tokens) {
+__device__ __forceinline__ void mq_score_item(const ScoreArgs& a, int num_tokens, const ScanItem& item, int p_begin) {
   using T = ScoreTraits<D, KVD>;
   constexpr int LPP = T::LPP;
-  const int row_dyn = blockIdx.x / a.blocks_per_row;
-  const int blk = blockIdx.x % a.blocks_per_row;
-  const int b = row_dyn / a.dyn.count;
-  const int h = a.dyn.at(row_dyn % a.dyn.count);
+  const int b = item.b, h = item.h, len = item.len, n_scan = item.n_scan;
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
-  const int p_begin = blk * a.pages_per_block;
   int raw[ITERS];
   load_block_table<D, KVD, kScoreWaves, ITERS>(bt_row, a.max_pages, p_begin, raw);
-
-  const int len = a.seq_lens[b];
-  const int n = row_pages(len, a.max_pages);  // pages of the last token's row
-  // SPD_TAIL_SKIP: the request's last two pages are not scored.  Each token row's last page is one of
-  // them (T <= 4 draft tokens lie within 16 positions), so both are in every token's local window of at
-  // least two pages or past the token's length: block 0 writes -inf for them where a token sees them.
-  const int n_scan = a.tail_mode == SPD_TAIL_SKIP ? max(n - 2, 0) : n;
-  if (n_scan < n && blk == 0 && (int)threadIdx.x < 2 * num_tokens) {
-    const int t = (int)threadIdx.x >> 1, p = n_scan + ((int)threadIdx.x & 1);
-    if (p < row_pages(len - num_tokens + 1 + t, a.max_pages))
-      a.scores[(((size_t)b * num_tokens + t) * a.num_kv_heads + h) * a.max_pages + p] = -INFINITY;
-  }
-  if (p_begin >= n_scan) return;  // uniform over the block
 
   const int lane = threadIdx.x % kWave;
   const int sub = lane % LPP;
@@ -125,6 +118,24 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(Scor
       for (int g = 0; g < kG; ++g) s[g] = group_sum<LPP>(s[g]);
       if (sub == 0 && pg[it] < n_t) sc_row[pg[it]] = ok[it] ? topk_score(s) : -INFINITY;
     }
+  }
+}
+
+template <int D, int KVD, int ITERS>
+__global__ __launch_bounds__(kScoreWaves * kWave) void mq_page_score_kernel(ScoreArgs a, int num_tokens) {
+  constexpr int PPB = ITERS * kScoreWaves * (kWave / ScoreTraits<D, KVD>::LPP);  // = a.pages_per_block
+  const int k = (int)blockIdx.x;
+  ScanItem it;
+  if (scan_item<PPB>(a, k, it, [&](int len) { return mq_scan_pages(a, len); }))
+    mq_score_item<D, KVD, ITERS>(a, num_tokens, it, it.blk * PPB);
+  // SPD_TAIL_SKIP: workgroup r < rows writes -inf for dynamic row r's skipped pages, where a token sees
+  // them (after its own scan, so the writes add no round trip before the loads)
+  if (a.tail_mode == SPD_TAIL_SKIP && k < a.batch * a.dyn.count && (int)threadIdx.x < 2 * num_tokens) {
+    const int b = k / a.dyn.count, h = a.dyn.at(k % a.dyn.count);
+    const int len = a.seq_lens[b];
+    const int t = (int)threadIdx.x >> 1, p = mq_scan_pages(a, len) + ((int)threadIdx.x & 1);
+    if (p < row_pages(len - num_tokens + 1 + t, a.max_pages))
+      a.scores[(((size_t)b * num_tokens + t) * a.num_kv_heads + h) * a.max_pages + p] = -INFINITY;
   }
 }
 

@@ -15,14 +15,12 @@
 
 namespace spd {
 
-// Scan work items: the blocks of pages_per_block pages that hold pages of a dynamic row's scan,
-// numbered request-major as (request b, dynamic head, block); the heads of a request need the same
-// number of blocks.  Scanning workgroup k takes item k, and workgroups past the last item exit, so a
-// batch of short and long requests has its working workgroups dispatched first instead of scattered
-// among the blocks past each short row's end.  With SPD_TAIL_REBUILD the grid starts with one
-// workgroup per (request, KV head), which rebuilds the key statistics of the request's last page
-// and, for a dynamic head, scores it; being first, they run beside the scan instead of after it.
-// Unless the mode is SPD_TAIL_NONE the scan stops before that page.
+// The scanning workgroups take the numbered work items of score_common.h (scan_item), so a batch of
+// short and long requests has no workgroups past its rows' ends among the working ones.  With
+// SPD_TAIL_REBUILD the grid starts with one workgroup per (request, KV head), which rebuilds the key
+// statistics of the request's last page and, for a dynamic head, scores it; being first, they run
+// beside the scan instead of after it.  Unless the mode is SPD_TAIL_NONE the scan stops before that
+// page.
 
 // Pages a row's scan covers for a request of `len` tokens, in the units the workgroups step over
 // (logical pages for coverage and hierarchical paging).
@@ -35,80 +33,6 @@ __device__ __forceinline__ int scan_limit(const ScoreArgs& a, int len) {
   } else {
     return scan_pages(a, COV ? row_logical_pages(len, a.max_pages, a.lgs) : row_pages(len, a.max_pages));
   }
-}
-
-// Scan work items of one row of a request of `len` tokens: its blocks of PPB pages.
-template <bool COV, bool HIER, int PPB>
-__device__ __forceinline__ int scan_blocks(const ScoreArgs& a, int len) {
-  return (scan_limit<COV, HIER>(a, len) + PPB - 1) / PPB;
-}
-
-// One wave's view of 64 requests of the numbering: lane i holds request b0 + i's length and the
-// inclusive count of the items of requests b0 .. b0 + i; `total` is the 64 requests' item count.
-struct ScanChunk {
-  int len, incl, total;
-};
-
-template <bool COV, bool HIER, int PPB>
-__device__ __forceinline__ ScanChunk scan_chunk(const ScoreArgs& a, int b0) {
-  const int b = b0 + (int)threadIdx.x % kWave;
-  ScanChunk c;
-  c.len = b < a.batch ? a.seq_lens[b] : 0;
-  const int items = b < a.batch ? scan_blocks<COV, HIER, PPB>(a, c.len) * a.dyn.count : 0;
-  c.incl = (int)wave_incl_scan((uint32_t)items);
-  c.total = (int)lane_u32((uint32_t)c.incl, kWave - 1);
-  return c;
-}
-
-struct ScanItem {
-  int b, h, blk, n_scan, len;
-};
-
-// Item `rel` of a chunk starting at request b0 (rel < c.total).  Every result is wave-uniform.
-template <bool COV, bool HIER, int PPB>
-__device__ __forceinline__ ScanItem chunk_item(const ScoreArgs& a, const ScanChunk& c, int b0, int rel) {
-  const int i = __popcll(__ballot(c.incl <= rel));  // the first lane whose inclusive count passes rel
-  ScanItem it;
-  it.b = b0 + i;
-  it.len = (int)lane_u32((uint32_t)c.len, i);
-  it.n_scan = scan_limit<COV, HIER>(a, it.len);
-  const int nb = (it.n_scan + PPB - 1) / PPB;
-  const int r = rel - ((int)lane_u32((uint32_t)c.incl, i) - nb * a.dyn.count);
-  const int hi = r / nb;
-  it.h = a.dyn.at(hi);
-  it.blk = r - hi * nb;
-  return it;
-}
-
-// Item k of a batch of one request, on the scalar unit: the length is one scalar load (read through
-// the constant address space, which the kernel never writes, so the compiler issues it as one).
-// Returns false past the last item.
-typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
-template <bool COV, bool HIER, int PPB>
-__device__ __forceinline__ bool single_request_item(const ScoreArgs& a, int k, ScanItem& it) {
-  it.len = ((ConstI32Ptr)a.seq_lens)[0];
-  it.n_scan = scan_limit<COV, HIER>(a, it.len);
-  const int nb = (it.n_scan + PPB - 1) / PPB;
-  if (k >= nb * a.dyn.count) return false;
-  const int hi = k / nb;
-  it.b = 0;
-  it.h = a.dyn.at(hi);
-  it.blk = k - hi * nb;
-  return true;
-}
-
-// Item k of any batch, 64 requests per pass on the vector unit.  Returns false past the last item.
-template <bool COV, bool HIER, int PPB>
-__device__ __forceinline__ bool batch_item(const ScoreArgs& a, int k, ScanItem& it) {
-  for (int off = 0, b0 = 0; b0 < a.batch; b0 += kWave) {
-    const ScanChunk c = scan_chunk<COV, HIER, PPB>(a, b0);
-    if (k - off < c.total) {
-      it = chunk_item<COV, HIER, PPB>(a, c, b0, k - off);
-      return true;
-    }
-    off += c.total;
-  }
-  return false;
 }
 
 // HIER: top-K over physical pages of 2^lgs logical pages (hierarchical paging): the workgroups scan
@@ -129,7 +53,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_kernel(ScoreAr
   constexpr int PPB = ITERS * kScoreWaves * (kWave / ScoreTraits<D, KVD>::LPP);  // = a.pages_per_block
   const int k = (int)blockIdx.x - tails;
   ScanItem it;
-  const bool found = a.batch == 1 ? single_request_item<COV, HIER, PPB>(a, k, it) : batch_item<COV, HIER, PPB>(a, k, it);
+  const bool found = scan_item<PPB>(a, k, it, [&](int len) { return scan_limit<COV, HIER>(a, len); });
   if (found) {
     const int32_t* bt_row = a.block_table + (size_t)it.b * a.max_pages;
     const int p_begin = it.blk * PPB;

@@ -253,33 +253,32 @@ __device__ __forceinline__ void mvar_exact_pages(const ScoreArgs& a, const int32
 }
 
 // The grid starts with the exact workgroups, one per dynamic row, so their dependent reads (length,
-// block table, keys) run beside the estimate instead of after it; then blocks_per_row workgroups per
-// dynamic row estimate pages [1, n - 1).
+// block table, keys) run beside the estimate instead of after it; the estimate workgroups then take the
+// numbered work items of score_common.h (scan_item) over each row's pages [0, n - 1) (page 0, the
+// exact sink, is left out inside).
 template <int D, int KVD, int ITERS>
 __global__ __launch_bounds__(kScoreWaves * kWave) void page_score_mvar_kernel(ScoreArgs a) {
   using T = MvarTraits<D, KVD>;
+  constexpr int PPB = ITERS * kScoreWaves * T::PPI;  // = a.pages_per_block
   const int rows = a.batch * a.dyn.count;
-  const bool exact = (int)blockIdx.x < rows;
-  const int k = exact ? (int)blockIdx.x : (int)blockIdx.x - rows;
-  const int row_dyn = exact ? k : k / a.blocks_per_row;
-  const int blk = exact ? 0 : k % a.blocks_per_row;
-  const int b = row_dyn / a.dyn.count;
-  const int h = a.dyn.at(row_dyn % a.dyn.count);
-  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
-  if (exact) {
-    mvar_exact_pages<D, KVD>(a, bt_row, b, h);
+  if ((int)blockIdx.x < rows) {
+    const int b = (int)blockIdx.x / a.dyn.count;
+    const int h = a.dyn.at((int)blockIdx.x % a.dyn.count);
+    mvar_exact_pages<D, KVD>(a, a.block_table + (size_t)b * a.max_pages, b, h);
     return;
   }
-  const int p_begin = blk * a.pages_per_block;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  int raw[ITERS];  // block-table entries, read before the request's length (clamped into the row)
+  ScanItem it;
+  if (!scan_item<PPB>(a, (int)blockIdx.x - rows, it,
+                      [&](int len) { return max(row_logical_pages(len, a.max_pages, a.lgs) - 1, 0); }))
+    return;
+  const int32_t* bt_row = a.block_table + (size_t)it.b * a.max_pages;
+  const int p_begin = it.blk * PPB;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  int raw[ITERS];  // block-table entries (clamped into the row)
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it)
-    raw[it] = bt_row[min((p_begin + (it * kScoreWaves + wave) * T::PPI + lane / T::LPP) >> a.lgs, a.max_pages - 1)];
-  const int len = a.seq_lens[b];
-  const int n = row_logical_pages(len, a.max_pages, a.lgs);
-  if (p_begin >= n - 1) return;  // uniform: nothing to estimate here
-  mvar_block_ell<D, KVD, ITERS>(a, raw, n - 1, len, b, h, p_begin);
+  for (int i = 0; i < ITERS; ++i)
+    raw[i] = bt_row[min((p_begin + (i * kScoreWaves + wave) * T::PPI + lane / T::LPP) >> a.lgs, a.max_pages - 1)];
+  mvar_block_ell<D, KVD, ITERS>(a, raw, it.n_scan, it.len, it.b, it.h, p_begin);
 }
 
 int launch_page_score_mvar(const ScoreArgs& a, int head_dim, int kv_dtype, hipStream_t stream) {

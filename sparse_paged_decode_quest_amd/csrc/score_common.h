@@ -219,6 +219,99 @@ __device__ __forceinline__ int scan_pages(const ScoreArgs& a, int n) {
   return a.tail_mode != SPD_TAIL_NONE && n > 0 ? n - 1 : n;
 }
 
+// Scan work numbering shared by the scorers: the blocks of PPB pages that hold pages of a dynamic row's
+// scan, numbered request-major as (request b, dynamic head, block) -- the heads of a request need the
+// same number of blocks -- from the requests' lengths on the device.  `n_scan(len)` gives the pages a
+// row's scan covers for a request of len tokens.  A workgroup takes one item; those past the last item
+// exit, so a batch of short and long requests has its working workgroups dispatched first instead of
+// scattered among the blocks past each short row's end.
+struct ScanItem {
+  int b, h, blk, n_scan, len;
+};
+
+// One wave's view of 64 requests: lane i holds request b0 + i's length and the inclusive count of the
+// items of requests b0 .. b0 + i; `total` is the 64 requests' item count.
+struct ScanChunk {
+  int len, incl, total;
+};
+
+template <int PPB, typename NScan>
+__device__ __forceinline__ ScanChunk scan_chunk(const ScoreArgs& a, int b0, NScan n_scan) {
+  const int b = b0 + (int)threadIdx.x % kWave;
+  ScanChunk c;
+  c.len = b < a.batch ? a.seq_lens[b] : 0;
+  const int items = b < a.batch ? (n_scan(c.len) + PPB - 1) / PPB * a.dyn.count : 0;
+  c.incl = (int)wave_incl_scan((uint32_t)items);
+  c.total = (int)lane_u32((uint32_t)c.incl, kWave - 1);
+  return c;
+}
+
+// Item `rel` of a chunk starting at request b0 (rel < c.total).  Every result is wave-uniform.
+template <int PPB, typename NScan>
+__device__ __forceinline__ ScanItem chunk_item(const ScoreArgs& a, const ScanChunk& c, int b0, int rel, NScan n_scan) {
+  const int i = __popcll(__ballot(c.incl <= rel));  // the first lane whose inclusive count passes rel
+  ScanItem it;
+  it.b = b0 + i;
+  it.len = (int)lane_u32((uint32_t)c.len, i);
+  it.n_scan = n_scan(it.len);
+  const int nb = (it.n_scan + PPB - 1) / PPB;
+  const int r = rel - ((int)lane_u32((uint32_t)c.incl, i) - nb * a.dyn.count);
+  const int hi = r / nb;
+  it.h = a.dyn.at(hi);
+  it.blk = r - hi * nb;
+  return it;
+}
+
+// Item k of the numbering; false past the last item.  A batch of up to kSmallBatch requests reads its
+// lengths as scalar loads (through the constant address space, which the kernels never write, so the
+// compiler issues them as such; indices clamped into the batch), all requested before the first is
+// used, and finds its request by a running count on the scalar unit; larger batches read 64 lengths per
+// wave with one vector load and a DPP prefix sum.  Each length is one scalar-cache request per
+// workgroup: on batches of 8 with thousands of workgroups past short rows the vector load was faster
+// (scorer 11.5 against 9.4 us), on full rows of 4 requests the scalar loads (35.7 against 36.7 us).
+typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+constexpr int kSmallBatch = 4;
+template <int PPB, typename NScan>
+__device__ __forceinline__ bool scan_item(const ScoreArgs& a, int k, ScanItem& it, NScan n_scan) {
+  if (a.batch <= kSmallBatch) {
+    const ConstI32Ptr lens_c = (ConstI32Ptr)a.seq_lens;
+    int lens[kSmallBatch];
+#pragma unroll
+    for (int i = 0; i < kSmallBatch; ++i) lens[i] = lens_c[min(i, a.batch - 1)];
+    // every length in a scalar register here: the loads are issued together and waited for once
+    static_assert(kSmallBatch == 4, "one operand per length below");
+    asm volatile("" ::"s"(lens[0]), "s"(lens[1]), "s"(lens[2]), "s"(lens[3]));
+    int off = 0;
+#pragma unroll
+    for (int i = 0; i < kSmallBatch; ++i) {
+      if (i >= a.batch) break;
+      const int ns = n_scan(lens[i]);
+      const int nb = (ns + PPB - 1) / PPB;
+      const int cnt = nb * a.dyn.count;
+      if (k - off < cnt) {
+        const int hi = (k - off) / nb;
+        it.b = i;
+        it.len = lens[i];
+        it.n_scan = ns;
+        it.h = a.dyn.at(hi);
+        it.blk = k - off - hi * nb;
+        return true;
+      }
+      off += cnt;
+    }
+    return false;
+  }
+  for (int off = 0, b0 = 0; b0 < a.batch; b0 += kWave) {
+    const ScanChunk c = scan_chunk<PPB>(a, b0, n_scan);
+    if (k - off < c.total) {
+      it = chunk_item<PPB>(a, c, b0, k - off, n_scan);
+      return true;
+    }
+    off += c.total;
+  }
+  return false;
+}
+
 // Pages per workgroup of NW waves with ITERS page groups each.
 __host__ __device__ constexpr int score_pages_per_block(int d, int meta_bytes, int nw, int iters) {
   return iters * nw * (kWave / (d * meta_bytes / 16));

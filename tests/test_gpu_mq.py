@@ -42,6 +42,8 @@ MQ_SMALL = {
                       streaming=(0,), n_sink_stream=1, n_local_stream=2),
     # four token lists of 256 entries: the union's capacity is exactly 1024 entries (the rank merge's limit)
     "t4_cap1024": W.small("mq_cap", num_queries=4, seq_lens=(9000, 4100, 700), budget=256, Hkv=2, Hq=8),
+    # more than 64 requests: the scan's work is numbered 64 requests at a time
+    "t2_b66": W.small("mq_b66", num_queries=2, seq_lens=tuple((i * 733) % 2600 + 4 for i in range(66)), budget=9),
 }
 
 

@@ -39,6 +39,10 @@ MVAR = {
                         seq_lens=(1500, 250, 2), planted=("fixed", 4), delta=("nats", 5.0), seed=W.BASE_SEED + 62),
     "f16_d64": W.small("mvar_f16_d64", d=64, mode="coverage", estimator="mvar", gamma=0.8, n_sink=2, n_local=0,
                        seq_lens=(513, 300, 32), seed=W.BASE_SEED + 63),
+    # more than 64 requests: the scan's work is numbered 64 requests at a time
+    "f16_b67": W.small("mvar_f16_b67", mode="coverage", estimator="mvar", gamma=0.9, n_local=1,
+                       seq_lens=tuple((i * 541) % 2300 + 1 for i in range(67)), planted=("fixed", 3),
+                       delta=("nats", 6.0), seed=W.BASE_SEED + 64),
 }
 
 
