@@ -104,7 +104,7 @@
 extern "C" {
 #endif
 
-#define SPD_ABI_VERSION 17
+#define SPD_ABI_VERSION 18
 #define SPD_PAGE_SIZE 16       /* logical page, and the plain physical page */
 #define SPD_HIER_PAGE_SIZE 64  /* physical page of hierarchical paging (4 logical pages) */
 #define SPD_MAX_KV_HEADS 64
