@@ -506,33 +506,35 @@ __global__ __launch_bounds__(256) void mq_decode_kernel(MqDecodeArgs a) {
   }
   __syncthreads();
 
-  // merge the four wave states (fixed order); write the chunk result of the rows of tokens < T
-  for (int e = threadIdx.x; e < T * kMqG * D; e += blockDim.x) {
-    const int rr = e / D, ch = e % D;
-    float M = ws_m[0][rr];
+  // merge the four wave states.  Each wave first takes the 64 (row, wave) weights in its own lanes --
+  // lane l holds row l / 4 and wave state l % 4: the row's largest log-sum, the state's weight
+  // exp2(m_w - M) / L and the row's log-sum-exp -- so the per-channel pass below is four fused
+  // multiply-adds with the weights read from those lanes.
+  const int fr = lane >> 2, fw = lane & 3;
+  const float mw = ws_m[fw][fr];
+  float M = fmaxf(mw, __uint_as_float(dpp<0xb1>(__float_as_uint(mw))));  // lane ^ 1
+  M = fmaxf(M, __uint_as_float(dpp<0x4e>(__float_as_uint(M))));          // lane ^ 2
+  const float sc = M == -INFINITY ? 0.f : exp2f(mw - M);
+  float L = ws_l[fw][fr] * sc;
+  L += __uint_as_float(dpp<0xb1>(__float_as_uint(L)));
+  L += __uint_as_float(dpp<0x4e>(__float_as_uint(L)));
+  const float fac = M == -INFINITY ? 0.f : sc / L;
+  const int rows_out = T * kMqG;
+  if (wave == 0 && fw == 0 && fr < rows_out) {
+    const float lse = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
+    if (m == 1) a.out_lse[out_row(fr / kMqG, fr % kMqG)] = lse;
+    else a.part_lse[((size_t)row * a.blocks_per_row + j) * kMqRows + fr] = lse;
+  }
+  // this thread: channel threadIdx.x % D of rows 2 i + wave / 2 (uniform over the wave)
+  const int ch = (int)threadIdx.x % D;
+  const int half = __builtin_amdgcn_readfirstlane(wave >> 1);
+  for (int rr = half; rr < rows_out; rr += 2) {
+    float o = 0.f;
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, ws_m[w][rr]);
-    float o = 0.f, lse = -INFINITY;
-    if (M != -INFINITY) {
-      float L = 0.f, A = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float sc = exp2f(ws_m[w][rr] - M);
-        L = fmaf(ws_l[w][rr], sc, L);
-        A = fmaf(ws_acc[w][rr][ch], sc, A);
-      }
-      o = A / L;
-      lse = (M + log2f(L)) * kLn2;
-    }
-    if (m == 1) {
-      const size_t orow = out_row(rr / kMqG, rr % kMqG);
-      a.out[orow * D + ch] = o;
-      if (ch == 0) a.out_lse[orow] = lse;
-    } else {
-      const size_t slot = ((size_t)row * a.blocks_per_row + j) * kMqRows + rr;
-      a.part_o[slot * D + ch] = o;
-      if (ch == 0) a.part_lse[slot] = lse;
-    }
+    for (int w = 0; w < 4; ++w)
+      o = fmaf(ws_acc[w][rr][ch], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fac), 4 * rr + w)), o);
+    if (m == 1) a.out[out_row(rr / kMqG, rr % kMqG) * D + ch] = o;
+    else a.part_o[(((size_t)row * a.blocks_per_row + j) * kMqRows + rr) * D + ch] = o;
   }
 }
 

@@ -604,31 +604,33 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
     for (int cc = 0; cc < CPL; ++cc) ws_acc[wave][g][lane * CPL + cc] = acc[g][cc];
   __syncthreads();
 
-  // merge the four wave states (fixed order) and write the chunk result
-  for (int e = threadIdx.x; e < kGq * D; e += blockDim.x) {
-    const int g = e / D, ch = e % D;
-    float M = ws_m[0][g];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, ws_m[w][g]);
-    float o = 0.f, lse = -INFINITY;
-    if (M != -INFINITY) {
-      float L = 0.f, A = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float sc = exp2f(ws_m[w][g] - M);
-        L = fmaf(ws_l[w][g], sc, L);
-        A = fmaf(ws_acc[w][g][ch], sc, A);
-      }
-      o = A / L;
-      lse = (M + log2f(L)) * kLn2;
+  // merge the four wave states.  Each wave first takes the kGq x 4 (row, wave) weights in its lanes --
+  // lane l holds row (l / 4) mod kGq and wave state l % 4: the row's largest log-sum, the state's
+  // weight exp2(m_w - M) / L and the row's log-sum-exp -- so the per-channel pass below is four fused
+  // multiply-adds with the weights read from those lanes.
+  {
+    const int fg = (lane >> 2) & (kGq - 1), fw = lane & 3;
+    const float mw = ws_m[fw][fg];
+    float M = fmaxf(mw, __uint_as_float(dpp<0xb1>(__float_as_uint(mw))));  // lane ^ 1
+    M = fmaxf(M, __uint_as_float(dpp<0x4e>(__float_as_uint(M))));          // lane ^ 2
+    const float sc = M == -INFINITY ? 0.f : exp2f(mw - M);
+    float L = ws_l[fw][fg] * sc;
+    L += __uint_as_float(dpp<0xb1>(__float_as_uint(L)));
+    L += __uint_as_float(dpp<0x4e>(__float_as_uint(L)));
+    const float fac = M == -INFINITY ? 0.f : sc / L;
+    if (threadIdx.x < 4 * kGq && fw == 0) {
+      const float lse = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
+      if (m == 1) a.out_lse[qrow + fg] = lse;
+      else a.part_lse[(slot_row + j) * kGq + fg] = lse;
     }
-    if (m == 1) {
-      a.out[(qrow + g) * D + ch] = o;
-      if (ch == 0) a.out_lse[qrow + g] = lse;
-    } else {
-      const size_t slot = (slot_row + j) * kGq + g;
-      a.part_o[slot * D + ch] = o;
-      if (ch == 0) a.part_lse[slot] = lse;
+    for (int e = threadIdx.x; e < kGq * D; e += blockDim.x) {
+      const int g = __builtin_amdgcn_readfirstlane(e / D), ch = e % D;  // the row is uniform over a wave
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        o = fmaf(ws_acc[w][g][ch], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fac), 4 * g + w)), o);
+      if (m == 1) a.out[(qrow + g) * D + ch] = o;
+      else a.part_o[((slot_row + j) * kGq + g) * D + ch] = o;
     }
   }
   if constexpr (MERGE) {
