@@ -269,7 +269,6 @@ __device__ __forceinline__ ScanItem chunk_item(const ScoreArgs& a, const ScanChu
 // wave with one vector load and a DPP prefix sum.  Each length is one scalar-cache request per
 // workgroup: on batches of 8 with thousands of workgroups past short rows the vector load was faster
 // (scorer 11.5 against 9.4 us), on full rows of 4 requests the scalar loads (35.7 against 36.7 us).
-typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
 constexpr int kSmallBatch = 4;
 template <int PPB, typename NScan>
 __device__ __forceinline__ bool scan_item(const ScoreArgs& a, int k, ScanItem& it, NScan n_scan) {

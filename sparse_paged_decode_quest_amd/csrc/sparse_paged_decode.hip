@@ -403,13 +403,19 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
     row = blockIdx.x / a.blocks_per_row;
     j = blockIdx.x % a.blocks_per_row;
     slot_row = (size_t)row * a.blocks_per_row;
+    // The argument block's pointers this prologue uses are held here, so their loads are waited for
+    // once, now; the row's list length is requested right after.  (A scalar-load wait covers every
+    // scalar load in flight, so an argument fetched after the length would wait for the length too,
+    // and the query loads behind it.)
+    asm volatile("" ::"s"(a.q), "s"(a.page_list), "s"(a.page_phys), "s"(a.seq_lens), "s"(a.list_len));
+    n = ((ConstI32Ptr)a.list_len)[row];
   }
   const int b = row / a.num_kv_heads;
   const int h = row % a.num_kv_heads;
   const size_t qrow = (size_t)b * a.num_q_heads + (size_t)h * kGq;  // first query head of the group
   // the request's length, requested as soon as the row is known (per-row plan: with the list length
   // and the list entries, so no round trip of its own comes before the first K / V loads)
-  const int len = a.seq_lens[b];
+  const int len = ((ConstI32Ptr)a.seq_lens)[b];
 
   const int32_t* list = a.page_list + (size_t)row * a.max_list;
   const int32_t* plist = a.page_phys ? a.page_phys + (size_t)row * a.max_list : nullptr;
@@ -433,7 +439,7 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   typename T::Q q;
   T::load_q(q, a.q, qrow * D, quarter);
   if (!a.balanced) {
-    n = row_units(a.list_len, row, a.max_list, a.lgs);
+    n = clamp_len(n, a.max_list) << a.lgs;  // the row's work units (row_units)
     if (n == 0) {
       if (j == 0) {
         for (int e = threadIdx.x; e < kGq * D; e += blockDim.x) a.out[qrow * D + e] = 0.f;

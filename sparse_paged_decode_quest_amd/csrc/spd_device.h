@@ -138,6 +138,10 @@ __device__ __forceinline__ float xor_sum(float v) {
   return v;
 }
 
+// An int32 array read through the constant address space: the compiler issues wave-uniform reads of it
+// as scalar loads.  Only for memory the reading kernel never writes.
+typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+
 // Cross-lane moves through DPP (data-parallel primitives of the gfx9 vector ALU): a lane reads
 // another lane's register in the same instruction, without the LDS crossbar that __shfl uses.
 // Lanes whose source is out of range, or that the row / bank masks leave unwritten, get 0.
