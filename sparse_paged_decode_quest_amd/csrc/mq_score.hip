@@ -65,15 +65,13 @@ __device__ __forceinline__ void mq_score_item(const ScoreArgs& a, int num_tokens
     float* sc_l = a.scores + (((size_t)b * num_tokens + min(t_l, num_tokens - 1)) * a.num_kv_heads + h) * a.max_pages;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
+      // a page outside the row or the pool is bounded all the same (its box is read in bounds) and its
+      // sums stay within its own 16 lanes; its result is replaced by -inf below
       float v[16];
 #pragma unroll
       for (int t = 0; t < kMqScoreMaxTokens; ++t) {
         float st[kG];
-        if (ok[it]) T::bound(qr[t], m[it], st);
-        else {
-#pragma unroll
-          for (int g = 0; g < kG; ++g) st[g] = 0.f;
-        }
+        T::bound(qr[t], m[it], st);
 #pragma unroll
         for (int g = 0; g < kG; ++g) v[t * kG + g] = st[g];
       }
