@@ -420,9 +420,10 @@ __global__ __launch_bounds__(256) void sparse_paged_decode_kernel(DecodeArgs a) 
   const int32_t* list = a.page_list + (size_t)row * a.max_list;
   const int32_t* plist = a.page_phys ? a.page_phys + (size_t)row * a.max_list : nullptr;
   // Per-row plan: the list entries of this wave's first 64 pages are requested together with the
-  // row's list length, assuming the chunk starts at j * min_chunk -- true whenever the row fits in
-  // J * min_chunk pages, where the chunk size is the minimum; otherwise they are read again.
-  const int spec_i0 = a.balanced ? -1 : j * a.min_chunk;
+  // row's list length, assuming the row's list is full (max_list entries: a top-K row holding its
+  // budget), so the chunk is the plan's for that length (taken on the host) -- the minimum chunk
+  // whenever max_list fits in J * min_chunk; otherwise they are read again.
+  const int spec_i0 = a.balanced ? -1 : j * a.spec_chunk;
   int spec_lp = -1, spec_lph = -1;  // list entry (physical page slot when lgs > 0) and physical page of the unit
   // the row's list and physical pages through range-checked loads: entries past max_list read 0, with
   // no branch around each read

@@ -530,6 +530,11 @@ static int decode_impl(const spd_desc* desc, const spd_plan_params* plan, const 
   a.max_list = desc->max_list;
   a.blocks_per_row = J;
   a.min_chunk = plan->min_chunk;
+  {  // the chunk the decode guesses its list reads from: the plan's for a full list
+    int sc = 0, sm = 0;
+    spd::plan_chunks(desc->max_list << lgs_of(desc), J, plan->min_chunk, sc, sm);
+    a.spec_chunk = sc;
+  }
   a.balanced = plan->balanced;
   a.grid_target = plan->min_grid_blocks;
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;

@@ -157,6 +157,7 @@ struct DecodeArgs {
   float* part_lse;
   int batch, num_q_heads, num_kv_heads, max_pages, num_pool_pages, max_list;
   int blocks_per_row, min_chunk;
+  int spec_chunk;  // per-row plan: the chunk of a full list (max_list entries), where the list reads are guessed
   int balanced, grid_target;  // step-wide split over grid_target (N_T) + rows blocks
   float sm_scale_log2;  // softmax scale times log2(e)
   int lgs;              // log2 of logical pages per physical page: each list entry is 2^lgs work units
